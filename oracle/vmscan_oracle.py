@@ -1,0 +1,223 @@
+"""fp64 reference ("oracle") for the selective scan path.
+
+TEST INFRASTRUCTURE: plain, slow and written to be checked by eye against the pages.  Only
+``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline`` leg may use it; the
+HIP library never imports it and it never imports the HIP library.
+
+Pages cited (short keys used throughout this repository):
+
+* [P1] "状态空间模型如何重塑视觉序列处理 Vision Mamba的技术突破与应用价值",
+  sumeiyu.com/news/203653.  Section "选择性扫描机制的计算效率优势" states the linear
+  recurrence h_t = A h_{t-1} + B x_t, y_t = C h_t + D x_t.
+* [P3] "Vision Mamba的双向SSM 计算机视觉模型架构的下一代突破", aitangshan.cn/news/1404048.
+  §2.1 (A/A_b initialisation, v1/v2 parameter sets), §2.2 (backward scan runs on the reversed
+  sequence and is reversed back; fusion by averaging), §4.3 (v2 fast path averages the two
+  directions).
+* [P4] "VMamba的SS2D模块 状态空间模型在视觉领域的革新设计", lpnh.cn/news/670717.
+  §2.1 (forward: x, z split; y * act(z)), §2.2 (the four cross-scan orders X_s), §3.1 (Δ is
+  softplus of a projection; per-direction projections), §3.2 (A = -exp(A_log); fp32 for the
+  critical parts).
+* [P5] "Vision Mamba实战 双向SSM Encoder核心代码解析与实现", lpnh.cn/news/710454.
+  §1 table (shapes: A/A_b [d_inner, d_state], B/C [batch, d_state, seq_len], D/D_b [d_inner]),
+  §2.1 (A_log = log(arange(1..d_state)), D = 1), §2.2 (bidirectional scan = forward scan plus
+  the reversed scan of the reversed input), §4 (delta = softplus(dt_proj(.))).
+
+Readings where the pages are silent or garbled (each is also listed in the design notes):
+
+* Discretisation: zero-order hold for A (a = exp(Δ·A)) and Euler for B (b = Δ·B·u).  The pages
+  say only that the state equation is discretised ([P4] §3.2); the cumsum formula printed there
+  has no decay term and is not followed.
+* Initial state h_{-1} = 0 for every direction.
+* Vim backward direction shares u, Δ_raw, z and the Δ bias with the forward direction and has
+  its own A_b_log, B_b, C_b, D_b; B_b and C_b are stored in ORIGINAL token order.
+* Fusion is the average (y_f + y_b) / 2 ([P3] §2.2, §4.3), each direction gated by silu(z)
+  with z reversed together with x ([P3] §2.2 flips ``xz`` as one tensor).
+* SS2D: per-direction Δ_raw, B, C are stored in that direction's scan order; the four outputs
+  are mapped back to row-major pixel order and summed with no scale; the gate silu(z) is
+  applied to the sum only when z is given.
+"""
+import numpy as np
+from scipy.special import expit
+
+
+def softplus(x):
+    """softplus(x) = log(1 + exp(x)), evaluated without overflow ([P5] §4, [P4] §3.1)."""
+    return np.logaddexp(0.0, np.asarray(x, dtype=np.float64))
+
+
+def silu(v):
+    """silu(v) = v * sigmoid(v), the activation applied to the gate z ([P4] §2.1)."""
+    v = np.asarray(v, dtype=np.float64)
+    return v * expit(v)
+
+
+def scan_1d(u, delta_raw, A_log, B, C, D, delta_bias):
+    """One direction of the selective scan, ungated.
+
+    Shapes: u, delta_raw [batch, dim, L]; A_log [dim, N]; B, C [batch, N, L]; D, delta_bias [dim].
+    Returns s[batch, dim, L] with, per (b, d):
+
+        A_n   = -exp(A_log[d, n])                            [P4] §3.2
+        Δ_t   = softplus(delta_raw[b, d, t] + delta_bias[d])  [P4] §3.1, [P5] §4
+        h_t,n = exp(Δ_t A_n) h_{t-1},n + Δ_t B[b, n, t] u[b, d, t],  h_{-1} = 0   [P1]
+        s_t   = Σ_n C[b, n, t] h_t,n + D[d] u[b, d, t]        [P1]
+
+    The loop over t is the recurrence as written; batch, channel and state are vectorised.
+    """
+    u = np.asarray(u, dtype=np.float64)
+    delta_raw = np.asarray(delta_raw, dtype=np.float64)
+    A = -np.exp(np.asarray(A_log, dtype=np.float64))            # [dim, N]
+    B = np.asarray(B, dtype=np.float64)
+    C = np.asarray(C, dtype=np.float64)
+    D = np.asarray(D, dtype=np.float64)
+    bias = np.asarray(delta_bias, dtype=np.float64)
+    nb, nd, L = u.shape
+    N = A.shape[1]
+    delta = softplus(delta_raw + bias[None, :, None])           # [batch, dim, L]
+    h = np.zeros((nb, nd, N), dtype=np.float64)
+    s = np.empty((nb, nd, L), dtype=np.float64)
+    for t in range(L):
+        dt = delta[:, :, t][:, :, None]                          # [batch, dim, 1]
+        a = np.exp(dt * A[None, :, :])                           # [batch, dim, N]
+        b = dt * B[:, None, :, t] * u[:, :, t][:, :, None]       # [batch, dim, N]
+        h = a * h + b
+        s[:, :, t] = np.sum(h * C[:, None, :, t], axis=2) + D[None, :] * u[:, :, t]
+    return s
+
+
+def scan_1d_semiseparable(u, delta_raw, A_log, B, C, D, delta_bias, reverse=False):
+    """The same scan written as a dense L x L matrix (brute force, small L only).
+
+    Unrolling the recurrence gives s = (M + diag(D)) u per (b, d) with
+        forward:  M[t, s] = Δ_s Σ_n C_t,n B_s,n exp(A_n Σ_{r=s+1..t} Δ_r)    for s <= t
+        backward: M[t, s] = Δ_s Σ_n C_t,n B_s,n exp(A_n Σ_{r=t..s-1} Δ_r)    for s >= t
+    i.e. the decay covers the receiving token and excludes the source token.  The backward form
+    is the reversed scan of [P3] §2.2 written directly in original token order.  This uses sums
+    of Δ inside one exponential instead of a running product, so it is an independent check.
+    """
+    u = np.asarray(u, dtype=np.float64)
+    A = -np.exp(np.asarray(A_log, dtype=np.float64))
+    B = np.asarray(B, dtype=np.float64)
+    C = np.asarray(C, dtype=np.float64)
+    D = np.asarray(D, dtype=np.float64)
+    delta = softplus(np.asarray(delta_raw, dtype=np.float64) + np.asarray(delta_bias, dtype=np.float64)[None, :, None])
+    nb, nd, L = u.shape
+    out = np.empty((nb, nd, L), dtype=np.float64)
+    for b in range(nb):
+        for d in range(nd):
+            dl = delta[b, d]
+            M = np.zeros((L, L), dtype=np.float64)
+            for t in range(L):
+                srange = range(0, t + 1) if not reverse else range(t, L)
+                for s in srange:
+                    if not reverse:
+                        seg = dl[s + 1:t + 1].sum()
+                    else:
+                        seg = dl[t:s].sum()
+                    M[t, s] = dl[s] * np.sum(C[b, :, t] * B[b, :, s] * np.exp(A[d] * seg))
+            out[b, d] = M @ u[b, d] + D[d] * u[b, d]
+    return out
+
+
+def vim_bidir(u, delta_raw, z, A_log, A_b_log, B, C, B_b, C_b, D, D_b, delta_bias):
+    """Vision Mamba bidirectional (v2 scan inputs) selective scan with the silu(z) gate.
+
+        y_f = scan(u, Δ_raw; A_log, B, C, D) * silu(z)
+        y_b = flip( scan(flip u, flip Δ_raw; A_b_log, flip B_b, flip C_b, D_b) * silu(flip z) )
+        out = (y_f + y_b) / 2
+
+    [P3] §2.2 (reverse, scan, reverse back; average fusion), [P3] §4.3 and [P5] §2.2 (the
+    backward branch is the forward branch applied to the flipped tensors).  Shapes as in
+    ``scan_1d``; A_log, A_b_log [dim, N]; B, C, B_b, C_b [batch, N, L] in original order.
+    """
+    f = lambda x: np.flip(np.asarray(x, dtype=np.float64), axis=-1)
+    g = silu(z)
+    y_f = scan_1d(u, delta_raw, A_log, B, C, D, delta_bias) * g
+    y_b_rev = scan_1d(f(u), f(delta_raw), A_b_log, f(B_b), f(C_b), D_b, delta_bias) * silu(f(z))
+    y_b = f(y_b_rev)
+    return (y_f + y_b) / 2.0
+
+
+def ss2d_orders(x):
+    """The four cross-scan sequences of [P4] §2.2 for x[batch, dim, H, W]:
+    row-major flatten, column-major flatten (transpose then flatten), and each reversed."""
+    x = np.asarray(x, dtype=np.float64)
+    nb, nd, H, W = x.shape
+    row = x.reshape(nb, nd, H * W)
+    col = np.swapaxes(x, 2, 3).reshape(nb, nd, H * W)
+    return [row, col, np.flip(row, axis=-1), np.flip(col, axis=-1)]
+
+
+def ss2d_cross_scan(x, delta_raw, A_log, B, C, D, delta_bias, z=None):
+    """VMamba SS2D cross-scan + cross-merge ([P4] §2.1, §2.2, §3.1).
+
+    x [batch, dim, H, W]; delta_raw [batch, 4, dim, H*W] and B, C [batch, 4, N, H*W], each in
+    its own direction's scan order; A_log [4, dim, N]; D, delta_bias [4, dim]; z optional
+    [batch, dim, H, W].  For k = 0..3 the ungated scan of the k-th sequence is mapped back to
+    row-major pixel order and the four are summed; silu(z) multiplies the sum when z is given.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    nb, nd, H, W = x.shape
+    L = H * W
+    seqs = ss2d_orders(x)
+    ys = [scan_1d(seqs[k], np.asarray(delta_raw)[:, k], np.asarray(A_log)[k], np.asarray(B)[:, k],
+                  np.asarray(C)[:, k], np.asarray(D)[k], np.asarray(delta_bias)[k]) for k in range(4)]
+    # inverse maps: row order is already row-major; column order is transposed back;
+    # reversed orders are flipped back first.
+    col_back = lambda y: np.swapaxes(y.reshape(nb, nd, W, H), 2, 3).reshape(nb, nd, L)
+    out = ys[0] + col_back(ys[1]) + np.flip(ys[2], axis=-1) + col_back(np.flip(ys[3], axis=-1))
+    out = out.reshape(nb, nd, H, W)
+    if z is not None:
+        out = out * silu(z)
+    return out
+
+
+def ss2d_cross_scan_pathwalk(x, delta_raw, A_log, B, C, D, delta_bias, z=None):
+    """SS2D by walking each direction's path pixel by pixel with explicit (h, w) coordinates
+    (pure Python loops; tiny inputs only).  Independent of the reshape/transpose/flip code in
+    ``ss2d_cross_scan``: direction 0 visits (i div W, i mod W), direction 1 visits
+    (i mod H, i div H), directions 2 and 3 visit the same paths from the other end."""
+    x = np.asarray(x, dtype=np.float64)
+    nb, nd, H, W = x.shape
+    L = H * W
+    A = -np.exp(np.asarray(A_log, dtype=np.float64))
+    out = np.zeros((nb, nd, H, W), dtype=np.float64)
+
+    def pixel(k, i):
+        if k == 0:
+            return divmod(i, W)
+        if k == 1:
+            return (i % H, i // H)
+        if k == 2:
+            return divmod(L - 1 - i, W)
+        j = L - 1 - i
+        return (j % H, j // H)
+
+    for b in range(nb):
+        for d in range(nd):
+            for k in range(4):
+                h = np.zeros(A.shape[2])
+                for i in range(L):
+                    ph, pw = pixel(k, i)
+                    xv = x[b, d, ph, pw]
+                    dl = float(softplus(float(delta_raw[b, k, d, i]) + float(delta_bias[k, d])))
+                    h = np.exp(dl * A[k, d]) * h + dl * np.asarray(B[b, k, :, i], dtype=np.float64) * xv
+                    out[b, d, ph, pw] += float(np.dot(np.asarray(C[b, k, :, i], dtype=np.float64), h)) + float(D[k, d]) * xv
+    if z is not None:
+        out = out * silu(z)
+    return out
+
+
+def rel_err(y, r):
+    """Parity error: max_i |y_i - r_i| / max(|r_i|, rms(r)).
+
+    A plain elementwise relative error is undefined where r_i ~ 0 (silu(z) ~ 0 or C.h cancelling
+    D.u), so each element is normalised by max(|r_i|, rms over the whole output)."""
+    y = np.asarray(y, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    if r.size == 0:
+        return 0.0
+    rms = float(np.sqrt(np.mean(r * r)))
+    denom = np.maximum(np.abs(r), rms)
+    denom = np.where(denom > 0, denom, 1.0)
+    return float(np.max(np.abs(y - r) / denom))

@@ -1,0 +1,330 @@
+"""Pins for the fp64 oracle: each ``pin_*`` takes an implementation namespace (with
+``scan_1d``, ``vim_bidir``, ``ss2d_cross_scan``) and returns the list of failure messages
+(empty = pass).  They check the oracle against facts fixed by the mathematics, not against the
+oracle itself: hand-derived closed forms, brute force on tiny inputs, linearity, the flip
+identity, limits and the SS2D reductions.  ``test_oracle_pins`` runs them on the oracle;
+``test_oracle_mutants`` runs them on copies of the oracle with a planted mistake and requires
+that every mistake is caught by at least one pin."""
+import math
+import os
+
+import numpy as np
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def rich_vim(rng, nb=2, nd=3, L=7, N=4, bias_lo=-2.0, bias_hi=0.5):
+    """Random small inputs with non-trivial A, A_b, D, D_b (so swapped or dropped parameters show)."""
+    r = rng
+    return dict(
+        u=r.standard_normal((nb, nd, L)),
+        delta_raw=r.standard_normal((nb, nd, L)),
+        z=r.standard_normal((nb, nd, L)),
+        A_log=r.uniform(-1.0, 1.5, (nd, N)),
+        A_b_log=r.uniform(-1.0, 1.5, (nd, N)),
+        B=r.standard_normal((nb, N, L)),
+        C=r.standard_normal((nb, N, L)),
+        B_b=r.standard_normal((nb, N, L)),
+        C_b=r.standard_normal((nb, N, L)),
+        D=r.uniform(0.5, 1.5, nd),
+        D_b=r.uniform(-1.5, -0.5, nd),
+        delta_bias=r.uniform(bias_lo, bias_hi, nd),
+    )
+
+
+def rich_ss2d(rng, nb=2, nd=2, H=3, W=4, N=3):
+    r = rng
+    L = H * W
+    return dict(
+        x=r.standard_normal((nb, nd, H, W)),
+        delta_raw=r.standard_normal((nb, 4, nd, L)),
+        A_log=r.uniform(-1.0, 1.5, (4, nd, N)),
+        B=r.standard_normal((nb, 4, N, L)),
+        C=r.standard_normal((nb, 4, N, L)),
+        D=r.uniform(-1.5, 1.5, (4, nd)),
+        delta_bias=r.uniform(-2.0, 0.5, (4, nd)),
+    )
+
+
+def _vim(impl, p, **over):
+    q = dict(p)
+    q.update(over)
+    return impl.vim_bidir(q["u"], q["delta_raw"], q["z"], q["A_log"], q["A_b_log"], q["B"], q["C"],
+                          q["B_b"], q["C_b"], q["D"], q["D_b"], q["delta_bias"])
+
+
+def _ss2d(impl, p, **over):
+    q = dict(p)
+    q.update(over)
+    return impl.ss2d_cross_scan(q["x"], q["delta_raw"], q["A_log"], q["B"], q["C"], q["D"], q["delta_bias"], q.get("z"))
+
+
+def _check(msgs, name, err, tol):
+    if not (err <= tol):
+        msgs.append(f"{name}: err {err:.3e} > {tol:.1e}")
+
+
+def pin_softplus_silu(impl):
+    """softplus and silu against math.log1p/math.exp evaluated one value at a time."""
+    msgs = []
+    xs = [-40.0, -20.0, -6.9, -3.0, -1e-3, 0.0, 1e-3, 0.7, 3.0, 19.0, 25.0, 60.0]
+    for x in xs:
+        ref = x + math.log1p(math.exp(-x)) if x > 0 else math.log1p(math.exp(x))
+        _check(msgs, f"softplus({x})", abs(float(impl.softplus(x)) - ref) / max(abs(ref), 1e-300), 1e-14)
+        sref = x / (1.0 + math.exp(-x)) if x > -700 else 0.0
+        _check(msgs, f"silu({x})", abs(float(impl.silu(x)) - sref) / max(abs(sref), 1e-300), 1e-14)
+    return msgs
+
+
+def pin_golden_single_token(impl):
+    """Hand-derived L = 1 cases stored in tests/golden/closed_forms.txt."""
+    msgs = []
+    env = {"log": math.log, "exp": math.exp, "log1p": math.log1p}
+    with open(os.path.join(GOLDEN, "closed_forms.txt")) as f:
+        for ln in f:
+            ln = ln.strip()
+            if not ln or ln.startswith("#"):
+                continue
+            lhs, rhs = ln.split("|")
+            v = [float(t) for t in lhs.split()]
+            u, dr, bias, B0, B1, C0, C1, D, Bb0, Bb1, Cb0, Cb1, Db, z = v
+            expect = eval(rhs, {"__builtins__": {}}, env)
+            a = lambda x: np.array(x, dtype=np.float64)
+            got = impl.vim_bidir(a([[[u]]]), a([[[dr]]]), a([[[z]]]), a([[0.3, 0.9]]), a([[-0.2, 0.1]]),
+                                 a([[[B0], [B1]]]), a([[[C0], [C1]]]), a([[[Bb0], [Bb1]]]), a([[[Cb0], [Cb1]]]),
+                                 a([D]), a([Db]), a([bias]))
+            err = abs(float(got[0, 0, 0]) - expect) / max(abs(expect), 1.0)
+            _check(msgs, f"golden[{ln[:30]}...]", err, 1e-13)
+    return msgs
+
+
+def pin_single_token_closed_form(impl, seed=0):
+    """L = 1: s_0 = u (Δ Σ_n B_n C_n + D) for each direction; both directions see the one token."""
+    msgs = []
+    rng = np.random.default_rng(seed)
+    p = rich_vim(rng, nb=3, nd=4, L=1, N=5)
+    dl = np.logaddexp(0.0, p["delta_raw"][:, :, 0] + p["delta_bias"][None, :])
+    bc_f = np.einsum("bn,bn->b", p["B"][:, :, 0], p["C"][:, :, 0])[:, None]
+    bc_b = np.einsum("bn,bn->b", p["B_b"][:, :, 0], p["C_b"][:, :, 0])[:, None]
+    u = p["u"][:, :, 0]
+    zz = p["z"][:, :, 0]
+    g = zz / (1.0 + np.exp(-zz))
+    expect = 0.5 * (u * (dl * bc_f + p["D"][None]) + u * (dl * bc_b + p["D_b"][None])) * g
+    _check(msgs, "L=1 closed form", O.rel_err(_vim(impl, p)[:, :, 0], expect), 1e-13)
+    return msgs
+
+
+def pin_geometric_series(impl):
+    """Constant Δ=δ, B=β, C=γ, u=υ, z over t: with a_n = exp(δ A_n) the forward state is
+    h_t,n = δ β_n υ (1 - a_n^{t+1}) / (1 - a_n) and the backward state at original position t has
+    absorbed L - t tokens: h^b_t,n = δ β^b_n υ (1 - (a^b_n)^{L-t}) / (1 - a^b_n)."""
+    msgs = []
+    rng = np.random.default_rng(1)
+    nb, nd, L, N = 1, 3, 23, 4
+    p = rich_vim(rng, nb=nb, nd=nd, L=L, N=N)
+    dr = rng.standard_normal(nd)
+    ups = rng.standard_normal(nd)
+    zc = rng.standard_normal(nd)
+    beta, gamma = rng.standard_normal(N), rng.standard_normal(N)
+    beta_b, gamma_b = rng.standard_normal(N), rng.standard_normal(N)
+    p["u"] = np.broadcast_to(ups[None, :, None], (nb, nd, L)).copy()
+    p["delta_raw"] = np.broadcast_to(dr[None, :, None], (nb, nd, L)).copy()
+    p["z"] = np.broadcast_to(zc[None, :, None], (nb, nd, L)).copy()
+    p["B"] = np.broadcast_to(beta[None, :, None], (nb, N, L)).copy()
+    p["C"] = np.broadcast_to(gamma[None, :, None], (nb, N, L)).copy()
+    p["B_b"] = np.broadcast_to(beta_b[None, :, None], (nb, N, L)).copy()
+    p["C_b"] = np.broadcast_to(gamma_b[None, :, None], (nb, N, L)).copy()
+    delta = np.logaddexp(0.0, dr + p["delta_bias"])            # [nd]
+    A = -np.exp(p["A_log"])
+    Ab = -np.exp(p["A_b_log"])
+    t = np.arange(L)
+    expect = np.empty((nd, L))
+    for d in range(nd):
+        a = np.exp(delta[d] * A[d])
+        ab = np.exp(delta[d] * Ab[d])
+        hf = delta[d] * beta[None, :] * ups[d] * (1 - a[None, :] ** (t[:, None] + 1)) / (1 - a[None, :])
+        hb = delta[d] * beta_b[None, :] * ups[d] * (1 - ab[None, :] ** (L - t[:, None])) / (1 - ab[None, :])
+        sf = hf @ gamma + p["D"][d] * ups[d]
+        sb = hb @ gamma_b + p["D_b"][d] * ups[d]
+        expect[d] = 0.5 * (sf + sb) * zc[d] / (1 + np.exp(-zc[d]))
+    _check(msgs, "geometric series", O.rel_err(_vim(impl, p)[0], expect), 1e-12)
+    return msgs
+
+
+def pin_semiseparable(impl):
+    """Brute force: out = silu(z) * ((M_f + diag D) u + (M_b + diag D_b) u) / 2 with the L x L
+    matrices built from exponentials of partial sums of Δ (oracle.scan_1d_semiseparable)."""
+    msgs = []
+    rng = np.random.default_rng(2)
+    for L in (1, 2, 5, 12):
+        p = rich_vim(rng, nb=2, nd=2, L=L, N=3)
+        sf = O.scan_1d_semiseparable(p["u"], p["delta_raw"], p["A_log"], p["B"], p["C"], p["D"], p["delta_bias"])
+        sb = O.scan_1d_semiseparable(p["u"], p["delta_raw"], p["A_b_log"], p["B_b"], p["C_b"], p["D_b"], p["delta_bias"], reverse=True)
+        g = p["z"] / (1 + np.exp(-p["z"]))
+        expect = 0.5 * (sf + sb) * g
+        _check(msgs, f"semiseparable L={L}", O.rel_err(_vim(impl, p), expect), 1e-12)
+        # the forward direction alone through scan_1d
+        s1 = impl.scan_1d(p["u"], p["delta_raw"], p["A_log"], p["B"], p["C"], p["D"], p["delta_bias"])
+        _check(msgs, f"semiseparable scan_1d L={L}", O.rel_err(s1, sf), 1e-12)
+    return msgs
+
+
+def pin_semiseparable_closed(impl):
+    """The brute-force matrices themselves, at L = 1 and for constant inputs (geometric sums)."""
+    msgs = []
+    rng = np.random.default_rng(3)
+    p = rich_vim(rng, nb=1, nd=2, L=6, N=3)
+    for k in ("u", "delta_raw"):
+        p[k] = np.broadcast_to(p[k][:, :, :1], p[k].shape).copy()
+    for k in ("B", "C"):
+        p[k] = np.broadcast_to(p[k][:, :, :1], p[k].shape).copy()
+    sf = O.scan_1d_semiseparable(p["u"], p["delta_raw"], p["A_log"], p["B"], p["C"], p["D"], p["delta_bias"])
+    sb = O.scan_1d_semiseparable(p["u"], p["delta_raw"], p["A_log"], p["B"], p["C"], p["D"], p["delta_bias"], reverse=True)
+    L = 6
+    t = np.arange(L)
+    for d in range(2):
+        dl = float(np.logaddexp(0.0, p["delta_raw"][0, d, 0] + p["delta_bias"][d]))
+        a = np.exp(dl * -np.exp(p["A_log"][d]))
+        bc = p["B"][0, :, 0] * p["C"][0, :, 0]
+        uu = p["u"][0, d, 0]
+        ef = ((dl * uu * (1 - a[None] ** (t[:, None] + 1)) / (1 - a[None])) @ bc) + p["D"][d] * uu
+        eb = ((dl * uu * (1 - a[None] ** (L - t[:, None])) / (1 - a[None])) @ bc) + p["D"][d] * uu
+        _check(msgs, "semiseparable fwd closed", O.rel_err(sf[0, d], ef), 1e-12)
+        _check(msgs, "semiseparable bwd closed", O.rel_err(sb[0, d], eb), 1e-12)
+    return msgs
+
+
+def pin_linearity(impl):
+    """out is linear in u for fixed Δ_raw, B, C, z."""
+    msgs = []
+    rng = np.random.default_rng(4)
+    p = rich_vim(rng, nb=2, nd=3, L=9, N=4)
+    u2 = rng.standard_normal(p["u"].shape)
+    al, be = 0.7, -1.3
+    lhs = _vim(impl, p, u=al * p["u"] + be * u2)
+    rhs = al * _vim(impl, p) + be * _vim(impl, p, u=u2)
+    _check(msgs, "linearity in u", O.rel_err(lhs, rhs), 1e-12)
+    return msgs
+
+
+def pin_flip_identity(impl):
+    """Running the bidirectional scan on reversed inputs with the forward and backward parameter
+    sets exchanged gives the reversed output ([P3] §2.2: the backward scan is the forward scan of
+    the reversed sequence)."""
+    msgs = []
+    rng = np.random.default_rng(5)
+    p = rich_vim(rng, nb=2, nd=3, L=11, N=4)
+    f = lambda a: np.flip(a, axis=-1)
+    lhs = _vim(impl, p, u=f(p["u"]), delta_raw=f(p["delta_raw"]), z=f(p["z"]), A_log=p["A_b_log"], A_b_log=p["A_log"],
+               B=f(p["B_b"]), C=f(p["C_b"]), B_b=f(p["B"]), C_b=f(p["C"]), D=p["D_b"], D_b=p["D"])
+    _check(msgs, "flip identity", O.rel_err(lhs, f(_vim(impl, p))), 1e-12)
+    return msgs
+
+
+def pin_limits(impl):
+    """Δ -> 0 (bias -40): out -> (D + D_b) u silu(z) / 2.  Δ|A| large (bias +30, A_n <= -1):
+    memoryless, s_t = u_t (Δ_t Σ_n B C + D).  z = 0: out = 0."""
+    msgs = []
+    rng = np.random.default_rng(6)
+    p = rich_vim(rng, nb=2, nd=3, L=8, N=4)
+    g = p["z"] / (1 + np.exp(-p["z"]))
+    small = _vim(impl, p, delta_bias=np.full(3, -40.0))
+    expect = 0.5 * (p["D"][None, :, None] + p["D_b"][None, :, None]) * p["u"] * g
+    _check(msgs, "delta->0", O.rel_err(small, expect), 1e-12)
+    q = dict(p)
+    q["A_log"] = np.abs(p["A_log"])
+    q["A_b_log"] = np.abs(p["A_b_log"])
+    q["delta_raw"] = 0.1 * p["delta_raw"]
+    big = _vim(impl, q, delta_bias=np.full(3, 30.0))
+    dl = np.logaddexp(0.0, q["delta_raw"] + 30.0)
+    bcf = np.einsum("bnt,bnt->bt", q["B"], q["C"])[:, None, :]
+    bcb = np.einsum("bnt,bnt->bt", q["B_b"], q["C_b"])[:, None, :]
+    expect = 0.5 * (q["u"] * (dl * bcf + q["D"][None, :, None]) + q["u"] * (dl * bcb + q["D_b"][None, :, None])) * g
+    _check(msgs, "memoryless", O.rel_err(big, expect), 1e-9)
+    zero = _vim(impl, p, z=np.zeros_like(p["z"]))
+    if np.max(np.abs(zero)) != 0.0:
+        msgs.append("z=0 does not give 0")
+    return msgs
+
+
+def pin_ss2d_pathwalk(impl):
+    """SS2D against the pixel-by-pixel path walk (explicit coordinates, no reshape/flip)."""
+    msgs = []
+    rng = np.random.default_rng(7)
+    for (H, W) in ((1, 1), (2, 3), (3, 2), (4, 4)):
+        p = rich_ss2d(rng, nb=2, nd=2, H=H, W=W, N=3)
+        walk = O.ss2d_cross_scan_pathwalk(p["x"], p["delta_raw"], p["A_log"], p["B"], p["C"], p["D"], p["delta_bias"])
+        _check(msgs, f"ss2d pathwalk {H}x{W}", O.rel_err(_ss2d(impl, p), walk), 1e-12)
+    p = rich_ss2d(rng, nb=1, nd=2, H=3, W=2, N=3)
+    z = rng.standard_normal(p["x"].shape)
+    walk = O.ss2d_cross_scan_pathwalk(p["x"], p["delta_raw"], p["A_log"], p["B"], p["C"], p["D"], p["delta_bias"], z)
+    _check(msgs, "ss2d pathwalk gated", O.rel_err(_ss2d(impl, p, z=z), walk), 1e-12)
+    return msgs
+
+
+def pin_ss2d_single_pixel(impl):
+    """H = W = 1: out = x Σ_k (Δ_k Σ_n B_k,n C_k,n + D_k)."""
+    msgs = []
+    rng = np.random.default_rng(8)
+    p = rich_ss2d(rng, nb=3, nd=2, H=1, W=1, N=4)
+    dl = np.logaddexp(0.0, p["delta_raw"][:, :, :, 0] + p["delta_bias"][None])      # [nb, 4, nd]
+    bc = np.einsum("bkn,bkn->bk", p["B"][..., 0], p["C"][..., 0])                 # [nb, 4]
+    expect = p["x"][:, :, 0, 0] * np.sum(dl * bc[:, :, None] + p["D"][None], axis=1)
+    _check(msgs, "ss2d 1x1", O.rel_err(_ss2d(impl, p)[:, :, 0, 0], expect), 1e-13)
+    return msgs
+
+
+def pin_ss2d_one_row(impl):
+    """H = 1: column order equals row order, so with direction 1 = direction 0 and direction 3 =
+    direction 2, and direction 2 set up as the Vim backward branch (its scan-order Δ_raw = flip Δ_raw,
+    B = flip B_b, C = flip C_b), SS2D = 2 (s_f + s_b) = 4 vim_bidir / silu(z) (ungated Vim sum)."""
+    msgs = []
+    rng = np.random.default_rng(9)
+    W = 9
+    p = rich_vim(rng, nb=2, nd=3, L=W, N=4)
+    p["z"] = np.full(p["z"].shape, 3.0)
+    f = lambda a: np.flip(a, axis=-1)
+    vim = _vim(impl, p)
+    g = 3.0 / (1 + math.exp(-3.0))
+    q = dict(
+        x=p["u"][:, :, None, :],
+        delta_raw=np.stack([p["delta_raw"], p["delta_raw"], f(p["delta_raw"]), f(p["delta_raw"])], axis=1),
+        A_log=np.stack([p["A_log"], p["A_log"], p["A_b_log"], p["A_b_log"]]),
+        B=np.stack([p["B"], p["B"], f(p["B_b"]), f(p["B_b"])], axis=1),
+        C=np.stack([p["C"], p["C"], f(p["C_b"]), f(p["C_b"])], axis=1),
+        D=np.stack([p["D"], p["D"], p["D_b"], p["D_b"]]),
+        delta_bias=np.stack([p["delta_bias"]] * 4),
+    )
+    _check(msgs, "ss2d one row = 2 x bidir", O.rel_err(_ss2d(impl, q)[:, :, 0, :], 4.0 * vim / g), 1e-12)
+    return msgs
+
+
+def pin_ss2d_transpose(impl):
+    """ss2d(x^T, directions 0<->1 and 2<->3 exchanged) = ss2d(x)^T."""
+    msgs = []
+    rng = np.random.default_rng(10)
+    p = rich_ss2d(rng, nb=2, nd=2, H=3, W=5, N=3)
+    perm = [1, 0, 3, 2]
+    q = dict(x=np.swapaxes(p["x"], 2, 3), delta_raw=p["delta_raw"][:, perm], A_log=p["A_log"][perm],
+             B=p["B"][:, perm], C=p["C"][:, perm], D=p["D"][perm], delta_bias=p["delta_bias"][perm])
+    _check(msgs, "ss2d transpose", O.rel_err(_ss2d(impl, q), np.swapaxes(_ss2d(impl, p), 2, 3)), 1e-12)
+    return msgs
+
+
+ALL_PINS = [
+    pin_softplus_silu,
+    pin_golden_single_token,
+    pin_single_token_closed_form,
+    pin_geometric_series,
+    pin_semiseparable,
+    pin_semiseparable_closed,
+    pin_linearity,
+    pin_flip_identity,
+    pin_limits,
+    pin_ss2d_pathwalk,
+    pin_ss2d_single_pixel,
+    pin_ss2d_one_row,
+    pin_ss2d_transpose,
+]

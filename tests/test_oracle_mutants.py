@@ -1,0 +1,155 @@
+"""Plant one plausible mistake at a time in a copy of the oracle (on the CPU) and require that
+at least one pin in ``oracle_pins`` catches it.  This shows the pins constrain every step:
+softplus, the decay, the input term, the readout, the skip term, the flip handling, the fusion,
+the gate and the SS2D index maps."""
+import types
+
+import numpy as np
+import pytest
+
+import oracle as O
+from oracle_pins import ALL_PINS
+
+
+def _scan(u, delta_raw, A_log, B, C, D, bias, bug=None):
+    u = np.asarray(u, dtype=np.float64)
+    A = -np.exp(np.asarray(A_log, dtype=np.float64))
+    if bug == "A_not_exp":
+        A = np.asarray(A_log, dtype=np.float64)
+    if bug == "A_sign":
+        A = np.exp(np.asarray(A_log, dtype=np.float64))
+    B = np.asarray(B, dtype=np.float64)
+    C = np.asarray(C, dtype=np.float64)
+    if bug == "swap_BC":
+        B, C = C, B
+    D = np.asarray(D, dtype=np.float64)
+    x = np.asarray(delta_raw, dtype=np.float64) + np.asarray(bias, dtype=np.float64)[None, :, None]
+    delta = x if bug == "no_softplus" else np.logaddexp(0.0, x)
+    if bug == "exp_not_softplus":
+        delta = np.exp(x)
+    nb, nd, L = u.shape
+    h = np.zeros((nb, nd, A.shape[1]))
+    s = np.empty((nb, nd, L))
+    for t in range(L):
+        dt = delta[:, :, t][:, :, None]
+        dprev = delta[:, :, max(t - 1, 0)][:, :, None]
+        a = np.exp((dprev if bug == "decay_prev_delta" else dt) * A[None])
+        if bug == "euler_A":
+            a = 1.0 + dt * A[None]
+        uu = u[:, :, max(t - 1, 0)] if bug == "input_prev_u" else u[:, :, t]
+        b = (1.0 if bug == "no_delta_in_b" else dt) * B[:, None, :, t] * uu[:, :, None]
+        if bug == "readout_before_update":
+            s[:, :, t] = np.sum(h * C[:, None, :, t], axis=2) + D[None, :] * u[:, :, t]
+            h = a * h + b
+            continue
+        h = a * h + b
+        y = np.sum(h * C[:, None, :, t], axis=2)
+        if bug != "drop_D":
+            y = y + D[None, :] * u[:, :, t]
+        s[:, :, t] = y
+    return s
+
+
+def _vim(u, dr, z, Al, Abl, B, C, Bb, Cb, D, Db, bias, bug=None, scan_bug=None):
+    f = lambda a: np.flip(np.asarray(a, dtype=np.float64), axis=-1)
+    sc = lambda *a: _scan(*a, bug=scan_bug)
+    g = O.silu(z)
+    yf = sc(u, dr, Al, B, C, D, bias) * g
+    if bug == "bwd_uses_fwd_BC":
+        rev = sc(f(u), f(dr), Abl, f(B), f(C), Db, bias)
+    elif bug == "bwd_uses_fwd_A":
+        rev = sc(f(u), f(dr), Al, f(Bb), f(Cb), Db, bias)
+    elif bug == "bwd_BC_not_flipped":
+        rev = sc(f(u), f(dr), Abl, Bb, Cb, Db, bias)
+    elif bug == "bwd_delta_not_flipped":
+        rev = sc(f(u), dr, Abl, f(Bb), f(Cb), Db, bias)
+    elif bug == "bwd_D_is_fwd_D":
+        rev = sc(f(u), f(dr), Abl, f(Bb), f(Cb), D, bias)
+    else:
+        rev = sc(f(u), f(dr), Abl, f(Bb), f(Cb), Db, bias)
+    if bug == "gate_not_flipped":
+        yb = f(rev * O.silu(z))
+    else:
+        yb = f(rev * O.silu(f(z)))
+    if bug == "no_flip_back":
+        yb = rev * O.silu(z)
+    if bug == "sum_not_avg":
+        return yf + yb
+    if bug == "gate_silu_is_sigmoid":
+        g2 = 1.0 / (1.0 + np.exp(-np.asarray(z, dtype=np.float64)))
+        return 0.5 * (yf / np.where(g == 0, 1, g) * g2 + yb / np.where(g == 0, 1, g) * g2)
+    return 0.5 * (yf + yb)
+
+
+def _ss2d(x, dr, Al, B, C, D, bias, z=None, bug=None, scan_bug=None):
+    x = np.asarray(x, dtype=np.float64)
+    nb, nd, H, W = x.shape
+    L = H * W
+    row = x.reshape(nb, nd, L)
+    col = np.swapaxes(x, 2, 3).reshape(nb, nd, L)
+    if bug == "col_as_reshape":
+        col = x.reshape(nb, nd, W, H).reshape(nb, nd, L)
+    seqs = [row, col, np.flip(row, -1), np.flip(col, -1)]
+    dr = np.asarray(dr)
+    ys = [_scan(seqs[k], dr[:, k], np.asarray(Al)[k], np.asarray(B)[:, k], np.asarray(C)[:, k],
+                np.asarray(D)[k], np.asarray(bias)[k], bug=scan_bug) for k in range(4)]
+    back = lambda y: np.swapaxes(y.reshape(nb, nd, W, H), 2, 3).reshape(nb, nd, L)
+    if bug == "col_not_transposed_back":
+        back = lambda y: y
+    flipk = (lambda y: y) if bug == "rev_not_flipped_back" else (lambda y: np.flip(y, -1))
+    out = ys[0] + back(ys[1]) + flipk(ys[2]) + back(flipk(ys[3]))
+    if bug == "avg4":
+        out = out / 4.0
+    out = out.reshape(nb, nd, H, W)
+    if z is not None:
+        out = out * O.silu(z)
+    return out
+
+
+def _impl(scan_bug=None, vim_bug=None, ss2d_bug=None):
+    return types.SimpleNamespace(
+        softplus=O.softplus,
+        silu=O.silu,
+        scan_1d=lambda *a: _scan(*a, bug=scan_bug),
+        vim_bidir=lambda *a: _vim(*a, bug=vim_bug, scan_bug=scan_bug),
+        ss2d_cross_scan=lambda x, dr, Al, B, C, D, bias, z=None: _ss2d(x, dr, Al, B, C, D, bias, z, bug=ss2d_bug, scan_bug=scan_bug),
+    )
+
+
+SCAN_BUGS = ["A_not_exp", "A_sign", "swap_BC", "no_softplus", "exp_not_softplus", "decay_prev_delta", "euler_A",
+             "input_prev_u", "no_delta_in_b", "readout_before_update", "drop_D"]
+VIM_BUGS = ["bwd_uses_fwd_BC", "bwd_uses_fwd_A", "bwd_BC_not_flipped", "bwd_delta_not_flipped", "bwd_D_is_fwd_D",
+            "gate_not_flipped", "no_flip_back", "sum_not_avg", "gate_silu_is_sigmoid"]
+SS2D_BUGS = ["col_as_reshape", "col_not_transposed_back", "rev_not_flipped_back", "avg4"]
+
+
+def _caught(impl):
+    failures = []
+    for pin in ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                msgs = pin(impl)
+        except Exception as e:  # a crash or NaN check also counts as caught
+            msgs = [f"{pin.__name__} raised {type(e).__name__}"]
+        if msgs:
+            failures.append(pin.__name__)
+    return failures
+
+
+def test_unmutated_copy_passes():
+    assert _caught(_impl()) == []
+
+
+@pytest.mark.parametrize("bug", SCAN_BUGS)
+def test_scan_mutant_caught(bug):
+    assert _caught(_impl(scan_bug=bug)), f"planted mistake {bug} passes every pin"
+
+
+@pytest.mark.parametrize("bug", VIM_BUGS)
+def test_vim_mutant_caught(bug):
+    assert _caught(_impl(vim_bug=bug)), f"planted mistake {bug} passes every pin"
+
+
+@pytest.mark.parametrize("bug", SS2D_BUGS)
+def test_ss2d_mutant_caught(bug):
+    assert _caught(_impl(ss2d_bug=bug)), f"planted mistake {bug} passes every pin"
