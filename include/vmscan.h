@@ -1,0 +1,154 @@
+/*
+ * vmscan: Vision Mamba bidirectional selective scan and VMamba SS2D cross-scan for MI355X
+ * (gfx950).  C ABI: plain pointers and sizes; no C++ or framework types cross this boundary.
+ *
+ * Pages cited (short keys):
+ *   [P1] "状态空间模型如何重塑视觉序列处理 Vision Mamba的技术突破与应用价值" (sumeiyu.com/news/203653),
+ *        section "选择性扫描机制的计算效率优势": h_t = A h_{t-1} + B x_t, y_t = C h_t + D x_t.
+ *   [P3] "Vision Mamba的双向SSM 计算机视觉模型架构的下一代突破" (aitangshan.cn/news/1404048),
+ *        §2.1 (A/A_b, v1/v2 parameter sets), §2.2 (reverse, scan, reverse back; average fusion),
+ *        §4.3 (v2 fast path: (out + out_b.flip) / 2).
+ *   [P4] "VMamba的SS2D模块 状态空间模型在视觉领域的革新设计" (lpnh.cn/news/670717),
+ *        §2.1 (y * act(z) after the core), §2.2 (four cross-scan orders), §3.1 (Δ = softplus of a
+ *        projection; per-direction projections), §3.2 (A = -exp(A_log)).
+ *   [P5] "Vision Mamba实战 双向SSM Encoder核心代码解析与实现" (lpnh.cn/news/710454),
+ *        §1 table (A/A_b [d_inner, d_state], B/C [batch, d_state, seq_len], D/D_b [d_inner]),
+ *        §2.2 (bidirectional scan = forward scan + reversed scan of the reversed input),
+ *        §4 (delta = softplus(.)).
+ *
+ * Per direction and per (batch b, channel d) both entry points compute, in fp32:
+ *   Δ_t   = softplus(Δ_raw[t] + delta_bias[d])                     [P4] §3.1, [P5] §4
+ *   a_t,n = exp(Δ_t A_n),  A_n = -exp(A_log[d, n])                  [P4] §3.2 (zero-order hold)
+ *   h_t,n = a_t,n h_{t-1},n + Δ_t B_t,n u_t,  h_{-1} = 0           [P1]
+ *   y_t   = Σ_n C_t,n h_t,n + D[d] u_t                              [P1]
+ *
+ * Conventions shared by every entry point:
+ *   - Ownership: every pointer is caller-owned DEVICE memory (except `stream`).  The library never
+ *     allocates or frees memory and keeps no state other than a thread-local last HIP error.
+ *   - Layout: all tensors are dense, row-major, with the shapes stated per argument.  Every
+ *     pointer must be 16-byte aligned (else VMSCAN_ERR_ALIGN).  `out` must not alias an input.
+ *   - Activation dtype: VMSCAN_F32 (float) or VMSCAN_BF16 (bfloat16 bit patterns, 2 bytes) for
+ *     u/x, delta_raw, z, B, C and out.  A_log, D and delta_bias are always float32.  The state
+ *     and all arithmetic are float32; bf16 outputs are rounded to nearest even once, at the store.
+ *   - d_state must be 16 (else VMSCAN_ERR_UNSUPPORTED).
+ *   - Errors: arguments are validated synchronously and a status is returned before anything is
+ *     enqueued; on success the kernels are enqueued on `stream` (NULL = the default stream) and the
+ *     call returns without waiting.  A failed launch returns VMSCAN_ERR_HIP and the hipError_t
+ *     is kept for vmscan_last_hip_error().  No entry point throws or aborts.
+ *   - Workspace: caller-provided device scratch of at least the queried size (0 means none is
+ *     needed and `workspace` may be NULL).  Its contents on entry are ignored.
+ */
+#ifndef VMSCAN_H
+#define VMSCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  VMSCAN_OK = 0,
+  VMSCAN_ERR_NULL = 1,        /* a required pointer is NULL                                  */
+  VMSCAN_ERR_SHAPE = 2,       /* a size is < 1, or too large for the index types               */
+  VMSCAN_ERR_UNSUPPORTED = 3, /* d_state or dtype not supported                                */
+  VMSCAN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                              */
+  VMSCAN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the queried size               */
+  VMSCAN_ERR_HIP = 6          /* a HIP call failed; see vmscan_last_hip_error()                */
+} vmscan_status;
+
+typedef enum { VMSCAN_F32 = 0, VMSCAN_BF16 = 1 } vmscan_dtype;
+
+/* Human-readable name of a status (static string, never NULL). */
+const char *vmscan_status_string(vmscan_status s);
+
+/* hipError_t (as int) behind the last VMSCAN_ERR_HIP returned on the calling thread; 0 if none. */
+int vmscan_last_hip_error(void);
+
+/* Chunk length (tokens) the library uses for a bidirectional scan of this shape when
+ * chunk_len = 0 is passed to the _ex entry points; a value >= seqlen means one chunk. */
+int64_t vmscan_fwd_bidir_chunk_len(int64_t batch, int64_t dim, int64_t seqlen, int d_state);
+
+/* Workspace bytes for vmscan_fwd_bidir / vmscan_fwd_bidir_ex (chunk_len 0 = library choice).
+ * Returns 0 for invalid arguments. */
+size_t vmscan_fwd_bidir_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen, int d_state,
+                                        vmscan_dtype dtype);
+size_t vmscan_fwd_bidir_workspace_bytes_ex(int64_t batch, int64_t dim, int64_t seqlen, int d_state,
+                                           vmscan_dtype dtype, int64_t chunk_len);
+
+/*
+ * Vision Mamba bidirectional (v2 scan inputs) selective scan, fused with the SiLU gate.
+ *   out = ( y_f + flip(y_b') ) / 2 * silu(z)                       [P3] §2.2, §4.3; [P5] §2.2
+ * where y_f is the scan above over t = 0..L-1 with (A_log, B, C, D) and y_b' is the same scan of
+ * the reversed sequence (reversed u, Δ_raw) with (A_b_log, reversed B_b, reversed C_b, D_b).
+ * The backward direction shares u, delta_raw, z and delta_bias with the forward one; B_b and C_b
+ * are given in ORIGINAL token order.  No reversed copy is materialised.  The v1 variant of [P3]
+ * §2.1 is obtained by passing B_b = B, C_b = C and D_b = D.
+ *
+ *   u, delta_raw, z : [batch, dim, seqlen]     activation dtype
+ *   A_log, A_b_log  : [dim, d_state]           float32
+ *   B, C, B_b, C_b  : [batch, d_state, seqlen] activation dtype, original token order
+ *   D, D_b          : [dim]                    float32
+ *   delta_bias      : [dim]                    float32 (shared by both directions)
+ *   out             : [batch, dim, seqlen]     activation dtype
+ * Long sequences are split into chunks whose boundary states are carried across workgroups
+ * (chunk_len 0 = library choice; otherwise the given length, clamped to [1, seqlen]).
+ */
+vmscan_status vmscan_fwd_bidir(const void *u, const void *delta_raw, const void *z,
+                               const float *A_log, const float *A_b_log,
+                               const void *B, const void *C, const void *B_b, const void *C_b,
+                               const float *D, const float *D_b, const float *delta_bias,
+                               void *out, int64_t batch, int64_t dim, int64_t seqlen, int d_state,
+                               vmscan_dtype dtype, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+vmscan_status vmscan_fwd_bidir_ex(const void *u, const void *delta_raw, const void *z,
+                                  const float *A_log, const float *A_b_log,
+                                  const void *B, const void *C, const void *B_b, const void *C_b,
+                                  const float *D, const float *D_b, const float *delta_bias,
+                                  void *out, int64_t batch, int64_t dim, int64_t seqlen, int d_state,
+                                  vmscan_dtype dtype, void *workspace, size_t workspace_bytes,
+                                  int64_t chunk_len, hipStream_t stream);
+
+/* Workspace bytes for ss2d_cross_scan_fwd / _ex (chunk_len 0 = library choice); 0 if invalid. */
+size_t ss2d_cross_scan_workspace_bytes(int64_t batch, int64_t dim, int64_t H, int64_t W, int d_state,
+                                       vmscan_dtype dtype);
+size_t ss2d_cross_scan_workspace_bytes_ex(int64_t batch, int64_t dim, int64_t H, int64_t W,
+                                          int d_state, vmscan_dtype dtype, int64_t chunk_len);
+
+/*
+ * VMamba SS2D cross-scan and cross-merge ([P4] §2.2, §3.1).  Direction k scans x in order
+ *   k=0 row-major, k=1 column-major, k=2 reversed row-major, k=3 reversed column-major,
+ * each with its own delta_raw[:,k], B[:,k], C[:,k] (stored in THAT direction's scan order),
+ * A_log[k], D[k] and delta_bias[k], without a gate.  The four outputs are mapped back to
+ * row-major pixels and summed in fp32:  out = Σ_k y_k  (times silu(z) when z is not NULL).
+ *
+ *   x          : [batch, dim, H, W]          activation dtype
+ *   delta_raw  : [batch, 4, dim, H*W]        activation dtype, scan order of each direction
+ *   A_log      : [4, dim, d_state]           float32
+ *   B, C       : [batch, 4, d_state, H*W]    activation dtype, scan order of each direction
+ *   D          : [4, dim]                    float32
+ *   delta_bias : [4, dim]                    float32
+ *   z          : [batch, dim, H, W] or NULL  activation dtype
+ *   out        : [batch, dim, H, W]          activation dtype
+ * H*W must be < 2^31.
+ */
+vmscan_status ss2d_cross_scan_fwd(const void *x, const void *delta_raw, const float *A_log,
+                                  const void *B, const void *C, const float *D,
+                                  const float *delta_bias, const void *z, void *out,
+                                  int64_t batch, int64_t dim, int64_t H, int64_t W, int d_state,
+                                  vmscan_dtype dtype, void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+vmscan_status ss2d_cross_scan_fwd_ex(const void *x, const void *delta_raw, const float *A_log,
+                                     const void *B, const void *C, const float *D,
+                                     const float *delta_bias, const void *z, void *out,
+                                     int64_t batch, int64_t dim, int64_t H, int64_t W, int d_state,
+                                     vmscan_dtype dtype, void *workspace, size_t workspace_bytes,
+                                     int64_t chunk_len, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VMSCAN_H */

@@ -1,0 +1,174 @@
+"""vmscan: MI355X (gfx950) Vision Mamba bidirectional selective scan and VMamba SS2D cross-scan.
+
+Thin ctypes binding over ``libvmscan.so`` (C ABI in ``include/vmscan.h``).  The functions below
+only check and marshal arguments (torch tensors -> device pointers, the current HIP stream, a
+workspace from torch's allocator); every step of the scan runs in the library's HIP kernels.
+There is no fallback: if the library is missing or cannot be loaded, importing the binding
+raises.
+"""
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libvmscan.so")
+
+VMSCAN_F32 = 0
+VMSCAN_BF16 = 1
+D_STATE = 16
+
+_c_void_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m selective_state_space_41_amd.build` "
+                          "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.vmscan_status_string.restype = ctypes.c_char_p
+    lib.vmscan_status_string.argtypes = [ctypes.c_int]
+    lib.vmscan_last_hip_error.restype = ctypes.c_int
+    lib.vmscan_last_hip_error.argtypes = []
+    lib.vmscan_fwd_bidir_chunk_len.restype = _i64
+    lib.vmscan_fwd_bidir_chunk_len.argtypes = [_i64, _i64, _i64, ctypes.c_int]
+    lib.vmscan_fwd_bidir_workspace_bytes.restype = ctypes.c_size_t
+    lib.vmscan_fwd_bidir_workspace_bytes.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int]
+    lib.vmscan_fwd_bidir_workspace_bytes_ex.restype = ctypes.c_size_t
+    lib.vmscan_fwd_bidir_workspace_bytes_ex.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _i64]
+    fwd_args = [_c_void_p] * 13 + [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _c_void_p, ctypes.c_size_t]
+    lib.vmscan_fwd_bidir.restype = ctypes.c_int
+    lib.vmscan_fwd_bidir.argtypes = fwd_args + [_c_void_p]
+    lib.vmscan_fwd_bidir_ex.restype = ctypes.c_int
+    lib.vmscan_fwd_bidir_ex.argtypes = fwd_args + [_i64, _c_void_p]
+    lib.ss2d_cross_scan_workspace_bytes.restype = ctypes.c_size_t
+    lib.ss2d_cross_scan_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int]
+    lib.ss2d_cross_scan_workspace_bytes_ex.restype = ctypes.c_size_t
+    lib.ss2d_cross_scan_workspace_bytes_ex.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _i64]
+    ss_args = [_c_void_p] * 9 + [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _c_void_p, ctypes.c_size_t]
+    lib.ss2d_cross_scan_fwd.restype = ctypes.c_int
+    lib.ss2d_cross_scan_fwd.argtypes = ss_args + [_c_void_p]
+    lib.ss2d_cross_scan_fwd_ex.restype = ctypes.c_int
+    lib.ss2d_cross_scan_fwd_ex.argtypes = ss_args + [_i64, _c_void_p]
+    return lib
+
+
+lib = _load()
+
+
+def status_string(code):
+    return lib.vmscan_status_string(int(code)).decode()
+
+
+def _check(code):
+    if code != 0:
+        msg = status_string(code)
+        if code == 6:
+            msg += f" (hipError_t {lib.vmscan_last_hip_error()})"
+        raise RuntimeError(msg)
+
+
+def _act_dtype(t):
+    if t.dtype == torch.float32:
+        return VMSCAN_F32
+    if t.dtype == torch.bfloat16:
+        return VMSCAN_BF16
+    raise TypeError(f"activation dtype must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need(t, name, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(stream, device):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def vmscan_fwd_bidir(u, delta_raw, z, A_log, A_b_log, B, C, B_b, C_b, D, D_b, delta_bias,
+                     out=None, chunk_len=0, workspace=None, stream=None):
+    """Bidirectional selective scan with the silu(z) gate; returns ``out`` [batch, dim, L].
+
+    u, delta_raw, z: [batch, dim, L]; A_log, A_b_log: [dim, 16] float32; B, C, B_b, C_b:
+    [batch, 16, L] (original token order); D, D_b, delta_bias: [dim] float32.  Activations are
+    float32 or bfloat16 (all the same).  ``chunk_len`` 0 lets the library choose."""
+    if u.dim() != 3:
+        raise ValueError("u must be [batch, dim, L]")
+    nb, nd, L = u.shape
+    dev = u.device
+    adt = u.dtype
+    dt = _act_dtype(u)
+    for name, t in (("u", u), ("delta_raw", delta_raw), ("z", z)):
+        _need(t, name, (nb, nd, L), adt, dev)
+    for name, t in (("B", B), ("C", C), ("B_b", B_b), ("C_b", C_b)):
+        _need(t, name, (nb, D_STATE, L), adt, dev)
+    for name, t in (("A_log", A_log), ("A_b_log", A_b_log)):
+        _need(t, name, (nd, D_STATE), torch.float32, dev)
+    for name, t in (("D", D), ("D_b", D_b), ("delta_bias", delta_bias)):
+        _need(t, name, (nd,), torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(u)
+    else:
+        _need(out, "out", (nb, nd, L), adt, dev)
+    wsb = lib.vmscan_fwd_bidir_workspace_bytes_ex(nb, nd, L, D_STATE, dt, int(chunk_len))
+    if workspace is None or workspace.numel() < wsb:
+        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    _check(lib.vmscan_fwd_bidir_ex(
+        _ptr(u), _ptr(delta_raw), _ptr(z), _ptr(A_log), _ptr(A_b_log), _ptr(B), _ptr(C), _ptr(B_b), _ptr(C_b),
+        _ptr(D), _ptr(D_b), _ptr(delta_bias), _ptr(out), nb, nd, L, D_STATE, dt,
+        _ptr(workspace), workspace.numel(), int(chunk_len), _stream(stream, dev)))
+    return out
+
+
+def ss2d_cross_scan_fwd(x, delta_raw, A_log, B, C, D, delta_bias, z=None, out=None, chunk_len=0,
+                        workspace=None, stream=None):
+    """SS2D four-direction cross-scan with cross-merge; returns ``out`` [batch, dim, H, W].
+
+    x: [batch, dim, H, W]; delta_raw: [batch, 4, dim, H*W]; A_log: [4, dim, 16] float32;
+    B, C: [batch, 4, 16, H*W] (each direction's scan order); D, delta_bias: [4, dim] float32;
+    z: optional [batch, dim, H, W] gate."""
+    if x.dim() != 4:
+        raise ValueError("x must be [batch, dim, H, W]")
+    nb, nd, H, W = x.shape
+    L = H * W
+    dev = x.device
+    adt = x.dtype
+    dt = _act_dtype(x)
+    _need(x, "x", (nb, nd, H, W), adt, dev)
+    _need(delta_raw, "delta_raw", (nb, 4, nd, L), adt, dev)
+    _need(B, "B", (nb, 4, D_STATE, L), adt, dev)
+    _need(C, "C", (nb, 4, D_STATE, L), adt, dev)
+    _need(A_log, "A_log", (4, nd, D_STATE), torch.float32, dev)
+    _need(D, "D", (4, nd), torch.float32, dev)
+    _need(delta_bias, "delta_bias", (4, nd), torch.float32, dev)
+    if z is not None:
+        _need(z, "z", (nb, nd, H, W), adt, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _need(out, "out", (nb, nd, H, W), adt, dev)
+    wsb = lib.ss2d_cross_scan_workspace_bytes_ex(nb, nd, H, W, D_STATE, dt, int(chunk_len))
+    if workspace is None or workspace.numel() < wsb:
+        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    _check(lib.ss2d_cross_scan_fwd_ex(
+        _ptr(x), _ptr(delta_raw), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(delta_bias), _ptr(z), _ptr(out),
+        nb, nd, H, W, D_STATE, dt, _ptr(workspace), workspace.numel(), int(chunk_len), _stream(stream, dev)))
+    return out
+
+
+def fwd_bidir_chunk_len(batch, dim, seqlen):
+    return int(lib.vmscan_fwd_bidir_chunk_len(batch, dim, seqlen, D_STATE))

@@ -1,0 +1,54 @@
+"""Compile the HIP library in-tree for gfx950.
+
+``python -m selective_state_space_41_amd.build`` (or ``build()``) runs hipcc on
+``csrc/vmscan.hip`` and writes ``libvmscan.so`` next to this file; it always recompiles.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+LIB = os.path.join(PKG, "libvmscan.so")
+PROBE = os.path.join(PKG, "vmscan_probe")
+
+# Packed fp32 VALU forms are kept out of every gfx950 code object.
+HIP_FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def _hipcc():
+    h = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(h):
+        raise RuntimeError("hipcc not found: the ROCm toolchain is required to build vmscan")
+    return h
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    # hipcc's host pass does not know the packed-fp32 feature name; that warning is harmless
+    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"build failed ({r.returncode}): {' '.join(cmd)}\n{out}")
+    return out
+
+
+def build(verbose=False):
+    """Compile libvmscan.so and the throughput probe executable."""
+    hipcc = _hipcc()
+    tmp = LIB + ".tmp"
+    out = _run([hipcc, *HIP_FLAGS, "-shared", "-I", os.path.join(ROOT, "include"),
+                "-o", tmp, os.path.join(PKG, "csrc", "vmscan.hip")])
+    os.replace(tmp, LIB)
+    probe_src = os.path.join(PKG, "csrc", "probe.hip")
+    if os.path.exists(probe_src):
+        out += _run([hipcc, *HIP_FLAGS, "-o", PROBE + ".tmp", probe_src])
+        os.replace(PROBE + ".tmp", PROBE)
+    if verbose and out.strip():
+        print(out)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))
