@@ -4,30 +4,36 @@
 // What is computed is stated in that header with the page citations; this file holds the
 // kernels and the host-side validation and dispatch.
 //
-// Design (gfx950, wave64, 160 KB LDS per CU, fp32 VALU + transcendental unit):
-//  * One workgroup = one wavefront = 16 channels x 2 directions x 2 state halves.  Each lane
-//    keeps 8 of the 16 fp32 states of one (batch, channel, direction) in VGPRs; the two halves
-//    of a state vector sit in adjacent lanes and their readout partial sums are combined with
-//    one DPP quad_perm swap.  The path is not a dense contraction, so there is no MFMA.
-//  * Both directions run in lockstep inside the wavefront: at step i the forward lanes are at
-//    chunk position i and the backward lanes at position Kc-1-i.  The first half of the steps
-//    writes each direction's y into an fp32 LDS row per channel ("meet in the middle"); the
-//    second half adds the other direction's y to it, so every output is complete when both
-//    directions have passed it.  No reversed copy of any tensor is made.
-//  * Inputs are staged per tile of kTS steps: Δ = softplus(Δ_raw + bias) and Δ·u are computed
-//    once per (token, channel, direction) into LDS, and B/C (shared by all channels of a batch)
-//    are converted to fp32 in LDS and broadcast to the lanes.  The decay uses the hardware
-//    exp2 with A pre-scaled by log2(e).
-//  * Long sequences are split into chunks of K tokens.  A first kernel computes each chunk's
-//    local end state from zero and its Σ Δ; the main kernel folds the preceding chunks'
-//    (Σ Δ, end state) pairs into its initial state (exp(A Σ Δ) is the chunk's total decay)
-//    before scanning, so the carry crosses workgroups without recomputing the scan.
-//  * SS2D runs as two such bidirectional pairs: (row-major, reversed row-major) and
-//    (column-major, reversed column-major).  The first pair writes its fp32 sum to a workspace
-//    image; the second adds its own sum and stores the output.
-//  * Block ids are remapped so that the workgroups an XCD receives (hardware dispatch is
-//    round-robin over the 8 XCDs) are consecutive tiles of the same batch and chunk, which share
-//    their B/C reads in that XCD's L2.
+// Design (gfx950: wave64, 160 KB LDS per CU, fp32 VALU with a transcendental rate of about a
+// third of the FMA rate, so this path is bound by VALU issue, not by HBM; no dense
+// contraction, so no MFMA):
+//  * A workgroup is two wavefronts over the same 64 channels of one batch row: wave 0 runs the
+//    forward direction, wave 1 the backward direction.  Lane = channel; the lane keeps all 16
+//    fp32 states of its (batch, channel, direction) in VGPRs.  Per state and token the VALU
+//    work is exp2(Δ·A') (A' = A·log2 e), h·a, h + (Δu)·B, y + C·h.
+//  * B and C are the same for every channel of a batch row, so each wave reads them as
+//    wave-uniform scalars (s_load) from an fp32 [batch][direction][position][B 0..15, C 0..15]
+//    copy that a small transpose kernel writes first (per position the wave needs 128
+//    contiguous bytes).  No VALU instruction is spent on B/C.
+//  * u, Δ_raw (and z) are read per lane in windows of 8 consecutive tokens (16-byte loads;
+//    the hardware accepts the 2-byte-aligned rows of odd-length bf16 sequences), one window
+//    ahead of use.  Δ = softplus(Δ_raw + bias) is computed once per (token, channel,
+//    direction) with a compensated log1p: log(1+e) = ln2·log2(s) + (e - (s - 1)), s = 1 + e.
+//  * Both directions advance in lockstep: at step i the forward wave is at chunk position i,
+//    the backward wave at Kc-1-i.  In the first half of the steps each direction stores its y
+//    (including its D·u term) in an fp32 LDS row per channel; after a barrier, in the second
+//    half, each direction adds the other's stored y at the positions it reaches and writes the
+//    finished output (gate applied once, bf16 rounded once) straight to HBM in 8-token
+//    windows.  No reversed copy of any tensor is made and no epilogue pass is needed.
+//  * Sequences longer than one LDS row are split into chunks.  A first kernel computes each
+//    chunk's end state from a zero start and its Σ Δ; the main kernel folds the preceding
+//    chunks' pairs (Σ Δ, end state) into its initial state, exp(A Σ Δ) being a chunk's total
+//    decay, so the carry crosses workgroups without re-running the recurrence.
+//  * SS2D runs as two such bidirectional pairs over the image: (row-major, reversed row-major)
+//    writes an fp32 image, then (column-major, reversed column-major) adds its sum and stores.
+//  * Workgroup ids are remapped so that the workgroups one XCD receives (the hardware deals
+//    them round-robin over 8 XCDs) are consecutive tiles of the same batch row, which then
+//    share their B/C reads in that XCD's L2.
 
 #include <hip/hip_runtime.h>
 
@@ -38,18 +44,22 @@
 
 namespace {
 
-constexpr int kN = 16;                       // d_state
-constexpr int kCH = 16;                      // channels per workgroup
-constexpr int kTS = 16;                      // steps per staged tile
-constexpr int kThreads = 64;                 // one wavefront
-constexpr int kBCStride = kTS * 32 + 16;     // floats per direction in the B/C tile (+pad vs bank conflicts)
-constexpr int kKMax = 512;                   // longest chunk whose y row fits the LDS budget
-constexpr int kMinChunk = 64;                // shortest chunk the planner picks
-constexpr int kTargetBlocks = 4096;          // planner: workgroups wanted to fill 256 CUs
-constexpr int kAggStride = kN + 1;           // per chunk: 16 end states + Σ Δ
+constexpr int kN = 16;                 // d_state
+constexpr int kW = 64;                 // channels per workgroup = lanes per wave
+constexpr int kThreads = 2 * kW;       // wave 0 forward, wave 1 backward
+constexpr int kWin = 8;                // tokens per register window
+constexpr int kBC = 2 * kN;            // floats per position in the B/C copy
+constexpr int kKMax = 206;             // longest LDS row: 3 workgroups of 64 x 207 floats per CU
+constexpr int kMinChunk = 32;          // shortest chunk the planner picks
+constexpr int kTargetBlocks = 768;     // planner: enough workgroups for one full round
+constexpr int kAggStride = kN + 1;     // per chunk: 16 end states + Σ Δ
+constexpr int kTransThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 thread_local int g_last_hip_error = 0;
+
+typedef __attribute__((address_space(4))) const float* scalar_fp;  // read-only: uniform loads -> s_load
 
 // ---------------------------------------------------------------------------------------------
 // device helpers
@@ -68,18 +78,85 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 __device__ __forceinline__ void st_act(float* p, int64_t i, float v) { p[i] = v; }
 __device__ __forceinline__ void st_act(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16_rne(v); }
 
-// softplus(x) = log(1 + e^x).  log1pf keeps full relative accuracy for the small e^x (~1e-3)
-// that the Δ bias range produces; above 20 the correction term is below fp32 resolution.
-__device__ __forceinline__ float softplus_f(float x) { return x > 20.0f ? x : log1pf(expf(x)); }
-
-__device__ __forceinline__ float silu_f(float v) { return v / (1.0f + expf(-v)); }
-
-// Adjacent-lane swap (lanes 2k <-> 2k+1) through DPP quad_perm [1,0,3,2].
-__device__ __forceinline__ float swap_pair(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+// 8 consecutive elements starting at p (any element alignment).
+__device__ __forceinline__ void load8(const uint16_t* p, float (&t)[kWin]) {
+  uint4 r;
+  __builtin_memcpy(&r, p, sizeof(r));
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    t[2 * k] = __uint_as_float(w[k] << 16);
+    t[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float (&t)[kWin]) {
+  float4 r0, r1;
+  __builtin_memcpy(&r0, p, sizeof(r0));
+  __builtin_memcpy(&r1, p + 4, sizeof(r1));
+  t[0] = r0.x; t[1] = r0.y; t[2] = r0.z; t[3] = r0.w;
+  t[4] = r1.x; t[5] = r1.y; t[6] = r1.z; t[7] = r1.w;
+}
+__device__ __forceinline__ void store8(uint16_t* p, const float (&t)[kWin]) {
+  uint32_t w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    w[k] = static_cast<uint32_t>(f32_to_bf16_rne(t[2 * k])) | (static_cast<uint32_t>(f32_to_bf16_rne(t[2 * k + 1])) << 16);
+  const uint4 r = make_uint4(w[0], w[1], w[2], w[3]);
+  __builtin_memcpy(p, &r, sizeof(r));
+}
+__device__ __forceinline__ void store8(float* p, const float (&t)[kWin]) {
+  const float4 r0 = make_float4(t[0], t[1], t[2], t[3]);
+  const float4 r1 = make_float4(t[4], t[5], t[6], t[7]);
+  __builtin_memcpy(p, &r0, sizeof(r0));
+  __builtin_memcpy(p + 4, &r1, sizeof(r1));
 }
 
-// Hardware dispatch sends workgroup i to XCD i % 8.  Return the logical tile id so that the
+// v[j] = base[i0 + sgn*j] for j < nw (nw <= kWin); sgn is wave-uniform.  Full windows are one
+// vector load of the 8-element run; short windows read only their valid elements.
+template <typename T>
+__device__ __forceinline__ void load_run(const T* base, int64_t i0, int sgn, int nw, float (&v)[kWin]) {
+  if (nw == kWin) {
+    float t[kWin];
+    load8(base + (sgn > 0 ? i0 : i0 - (kWin - 1)), t);
+#pragma unroll
+    for (int j = 0; j < kWin; ++j) v[j] = sgn > 0 ? t[j] : t[kWin - 1 - j];
+  } else {
+#pragma unroll
+    for (int j = 0; j < kWin; ++j) v[j] = j < nw ? ld_act(base, i0 + sgn * j) : 0.0f;
+  }
+}
+template <typename T>
+__device__ __forceinline__ void store_run(T* base, int64_t i0, int sgn, int nw, const float (&v)[kWin]) {
+  if (nw == kWin) {
+    float t[kWin];
+#pragma unroll
+    for (int j = 0; j < kWin; ++j) t[j] = sgn > 0 ? v[j] : v[kWin - 1 - j];
+    store8(base + (sgn > 0 ? i0 : i0 - (kWin - 1)), t);
+  } else {
+#pragma unroll
+    for (int j = 0; j < kWin; ++j)
+      if (j < nw) st_act(base, i0 + sgn * j, v[j]);
+  }
+}
+
+// softplus(x) = log(1 + e^x).  With e = e^x and s = fl(1 + e), e - (s - 1) is exactly the
+// rounding error of s (for e <= 1; for e > 1 it is below the result's resolution), and
+// log(1 + e) = log(s) + log(1 + c/s) ~= ln2 * log2(s) + c.  This keeps full fp32 relative
+// accuracy for the e ~ 1e-3 that the Δ bias range produces, where a plain log(1 + e) loses
+// about three digits.  Above 20 the correction to x is below fp32 resolution.
+__device__ __forceinline__ float softplus_f(float x) {
+  const float e = __builtin_amdgcn_exp2f(x * kLog2e);
+  const float s = 1.0f + e;
+  const float c = e - (s - 1.0f);
+  const float r = __builtin_fmaf(__builtin_amdgcn_logf(s), kLn2, c);
+  return x > 20.0f ? x : r;
+}
+
+__device__ __forceinline__ float silu_f(float v) {
+  return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-v * kLog2e));
+}
+
+// Hardware dispatch deals workgroup i to XCD i % 8.  Return the logical tile id so that the
 // tiles one XCD runs are contiguous in logical order.
 __device__ __forceinline__ int logical_block(int bid, int nblocks) {
   const int xcd = bid & 7, local = bid >> 3;
@@ -88,303 +165,452 @@ __device__ __forceinline__ int logical_block(int bid, int nblocks) {
 }
 
 struct DirArgs {
-  const void* draw;  // Δ_raw of this direction; element (b, d, idx) at b*draw_bs + d*L + idx
+  const void* draw;    // Δ_raw; element (b, d, idx) at b*draw_bs + d*L + idx
   int64_t draw_bs;
-  const void* B;     // (b, n, idx) at b*bc_bs + n*L + idx
+  const void* B;       // (b, n, idx) at b*bc_bs + n*L + idx
   const void* C;
   int64_t bc_bs;
   const float* A_log;  // [dim][16]
   const float* Dp;     // [dim]
   const float* bias;   // [dim]
-  int rev;             // 1: this direction's tensors are stored in reversed pair order
+  int rev;             // 1: this direction's Δ_raw/B/C are stored in reversed position order
 };
 
 struct ScanArgs {
-  const void* u;   // [batch][dim][L] (element index via the order map)
+  const void* u;   // [batch][dim][L] (element of position s via the order map)
   int64_t u_bs;    // batch stride of u, z, out, wsy
   const void* z;   // gate, same layout as u, or null
   void* out;
   float* wsy;      // fp32 image of the first SS2D pair
+  float* bct;      // [batch][2][L][kBC] fp32 B/C copy in position order
   float* agg;      // [batch][dim][2][nch][kAggStride]
   DirArgs d0, d1;  // forward and backward direction of the pair
   int64_t L;
   int dim, batch, K, nch, ngroups;
   int order;       // 0: position s -> element s; 1: column-major position -> row-major pixel
   int H, W;
-  int mode;        // 0: Vim gated average; 1: SS2D first pair -> wsy; 2: SS2D second pair -> out
 };
+
+enum { kModeVim = 0, kModeFirstPair = 1, kModeSecondPair = 2 };
 
 __device__ __forceinline__ int64_t elem_of(const ScanArgs& a, int64_t s) {
   return a.order == 0 ? s : static_cast<int64_t>(s % a.H) * a.W + s / a.H;
 }
 
-// Shared-memory tiles of one workgroup.
-struct Tiles {
-  float2* tD;   // [2][kTS][kCH]   (Δ, Δ·u)
-  float* tBC;   // [2][kBCStride]  per step: B[0..15], C[0..15]
-};
+// ---------------------------------------------------------------------------------------------
+// B/C transpose: bct[b][dir][s][0..15] = B_dir[b][:, si(s)], bct[b][dir][s][16..31] = C_dir[...]
 
-// Stage steps [i0, i0+ns) of both directions: Δ and Δ·u per (direction, step, channel), and the
-// fp32 B/C of each (direction, step).  In the first phase of the main kernel (INIT_Y) the skip
-// terms (D_f + D_b)·u are also written into the y rows of the positions first visited here.
-template <typename T, bool INIT_Y>
-__device__ __forceinline__ void produce_tile(const ScanArgs& a, int b, int d0, int64_t s_lo, int Kc,
-                                             int i0, int ns, Tiles t, float* ybuf, int ybs) {
-  const int lane = threadIdx.x;
-  const T* ub = static_cast<const T*>(a.u) + static_cast<int64_t>(b) * a.u_bs;
+template <typename T>
+__global__ __launch_bounds__(kTransThreads) void bc_transpose_kernel(ScanArgs a) {
+  const int64_t ntile = (a.L + kTransThreads - 1) / kTransThreads;
+  const int64_t blk = blockIdx.x;
+  const int64_t tile = blk % ntile;
+  const int dir = static_cast<int>((blk / ntile) & 1);
+  const int b = static_cast<int>(blk / (2 * ntile));
+  const int64_t s = tile * kTransThreads + threadIdx.x;
+  if (s >= a.L) return;
+  const DirArgs& da = dir == 0 ? a.d0 : a.d1;
+  const int64_t si = da.rev ? a.L - 1 - s : s;
+  const T* bb = static_cast<const T*>(da.B) + static_cast<int64_t>(b) * da.bc_bs + si;
+  const T* cb = static_cast<const T*>(da.C) + static_cast<int64_t>(b) * da.bc_bs + si;
+  float v[kBC];
 #pragma unroll
-  for (int dir = 0; dir < 2; ++dir) {
-    const DirArgs& da = dir == 0 ? a.d0 : a.d1;
-    const T* draw = static_cast<const T*>(da.draw) + static_cast<int64_t>(b) * da.draw_bs;
-    // Δ entries of this direction: kTS steps x kCH channels; consecutive lanes take consecutive
-    // steps of one channel row, so the loads are contiguous along positions.
-#pragma unroll 2
-    for (int k = 0; k < (kTS * kCH) / kThreads; ++k) {
-      const int e = k * kThreads + lane;
-      const int ch = e / kTS;
-      const int jj = e % kTS;
-      const int d = d0 + ch;
-      if (jj < ns) {
-        const int i = i0 + jj;
-        const int pos = dir == 0 ? i : Kc - 1 - i;
-        const int64_t s = s_lo + pos;
-        float2 v = make_float2(0.0f, 0.0f);
-        if (d < a.dim) {
-          const int64_t si = da.rev ? a.L - 1 - s : s;
-          const float uu = ld_act(ub + static_cast<int64_t>(d) * a.L, elem_of(a, s));
-          const float x = ld_act(draw + static_cast<int64_t>(d) * a.L, si) + da.bias[d];
-          const float dl = softplus_f(x);
-          v = make_float2(dl, dl * uu);
-          if (INIT_Y) ybuf[ch * ybs + pos] = (a.d0.Dp[d] + a.d1.Dp[d]) * uu;
-        }
-        t.tD[(dir * kTS + jj) * kCH + ch] = v;
-      }
-    }
-    // B/C entries of this direction: kTS steps x 32 (B then C).
-    const T* bb = static_cast<const T*>(da.B) + static_cast<int64_t>(b) * da.bc_bs;
-    const T* cb = static_cast<const T*>(da.C) + static_cast<int64_t>(b) * da.bc_bs;
-#pragma unroll 2
-    for (int k = 0; k < (kTS * 32) / kThreads; ++k) {
-      const int e = k * kThreads + lane;
-      const int q = e / kTS;
-      const int jj = e % kTS;
-      if (jj < ns) {
-        const int i = i0 + jj;
-        const int pos = dir == 0 ? i : Kc - 1 - i;
-        const int64_t s = s_lo + pos;
-        const int64_t si = da.rev ? a.L - 1 - s : s;
-        const T* src = (q < kN ? bb : cb) + static_cast<int64_t>(q & (kN - 1)) * a.L;
-        t.tBC[dir * kBCStride + jj * 32 + q] = ld_act(src, si);
-      }
-    }
+  for (int n = 0; n < kN; ++n) {
+    v[n] = ld_act(bb, static_cast<int64_t>(n) * a.L);
+    v[kN + n] = ld_act(cb, static_cast<int64_t>(n) * a.L);
   }
+  float4* dst = reinterpret_cast<float4*>(a.bct + ((static_cast<int64_t>(b) * 2 + dir) * a.L + s) * kBC);
+#pragma unroll
+  for (int q = 0; q < kBC / 4; ++q) dst[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
 }
 
-struct LaneInfo {
-  int dir, ch, half;
+// ---------------------------------------------------------------------------------------------
+// Scan kernels.  Everything that differs between the forward and backward wave, the Vim and the
+// SS2D pairs and the two scan orders is a template parameter, so the token loop has no
+// data-dependent branches:
+//   DIR   0: step i visits chunk position i; 1: position Kc-1-i
+//   MODE  kModeVim / kModeFirstPair / kModeSecondPair (output handling; SS2D backward tensors are
+//         stored in reversed position order)
+//   ORDER 0: u element = position; 1: column-major position -> row-major pixel
+
+struct Lane {
+  int b, c, lane, d, dd;  // dd: channel clamped into range for the loads of inactive lanes
+  bool valid;
+  int64_t s_lo;
+  int Kc;
 };
 
-__device__ __forceinline__ LaneInfo lane_info() {
-  const int lane = threadIdx.x;
-  return LaneInfo{lane >> 5, (lane >> 1) & (kCH - 1), lane & 1};
-}
-
-// Decode the logical tile into (batch, chunk, channel group).
-__device__ __forceinline__ void tile_coords(const ScanArgs& a, int& b, int& c, int& g) {
+__device__ __forceinline__ Lane lane_ctx(const ScanArgs& a) {
+  Lane l;
   const int nblocks = a.batch * a.nch * a.ngroups;
   const int tile = logical_block(static_cast<int>(blockIdx.x), nblocks);
-  g = tile % a.ngroups;
+  const int g = tile % a.ngroups;
   const int rest = tile / a.ngroups;
-  c = rest % a.nch;
-  b = rest / a.nch;
+  l.c = rest % a.nch;
+  l.b = rest / a.nch;
+  l.lane = threadIdx.x & (kW - 1);
+  l.d = g * kW + l.lane;
+  l.valid = l.d < a.dim;
+  l.dd = l.valid ? l.d : a.dim - 1;
+  l.s_lo = static_cast<int64_t>(l.c) * a.K;
+  l.Kc = static_cast<int>(a.L - l.s_lo < a.K ? a.L - l.s_lo : a.K);
+  return l;
 }
 
-__device__ __forceinline__ void load_a2(const ScanArgs& a, const LaneInfo& li, int d, float (&A2)[8]) {
-  const float* al = li.dir == 0 ? a.d0.A_log : a.d1.A_log;
+template <int MODE, int DIR>
+struct Dir {
+  static constexpr bool kRev = MODE != kModeVim && DIR == 1;  // storage order reversed
+  // global position of step i
+  static __device__ __forceinline__ int64_t pos(const Lane& l, int i) {
+    return DIR == 0 ? l.s_lo + i : l.s_lo + l.Kc - 1 - i;
+  }
+  // Δ_raw / B / C storage index of step i
+  static __device__ __forceinline__ int64_t sidx(const ScanArgs& a, const Lane& l, int i) {
+    return kRev ? a.L - 1 - pos(l, i) : pos(l, i);
+  }
+  static constexpr int kPosSgn = DIR == 0 ? 1 : -1;
+  static constexpr int kSidxSgn = kRev ? -kPosSgn : kPosSgn;
+};
+
+template <int ORDER>
+__device__ __forceinline__ int64_t elem(const ScanArgs& a, int64_t s) {
+  return ORDER == 0 ? s : static_cast<int64_t>(s % a.H) * a.W + s / a.H;
+}
+
+// v[j] = base[i0 + SGN*j]; FULL: j < kWin as one vector load of the 8-element run; else j < nw.
+template <int SGN, bool FULL, typename T>
+__device__ __forceinline__ void load_seq(const T* base, int64_t i0, int nw, float (&v)[kWin]) {
+  if (FULL) {
+    float t[kWin];
+    load8(base + (SGN > 0 ? i0 : i0 - (kWin - 1)), t);
 #pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    // A = -exp(A_log) ([P4] §3.2), pre-scaled by log2(e) so that exp(Δ A) = exp2(Δ A2)
-    A2[n] = d < a.dim ? -expf(al[static_cast<int64_t>(d) * kN + li.half * 8 + n]) * kLog2e : 0.0f;
+    for (int j = 0; j < kWin; ++j) v[j] = SGN > 0 ? t[j] : t[kWin - 1 - j];
+  } else {
+#pragma unroll
+    for (int j = 0; j < kWin; ++j) v[j] = j < nw ? ld_act(base, i0 + SGN * j) : 0.0f;
+  }
+}
+template <int SGN, bool FULL, typename T>
+__device__ __forceinline__ void store_seq(T* base, int64_t i0, int nw, const float (&v)[kWin]) {
+  if (FULL) {
+    float t[kWin];
+#pragma unroll
+    for (int j = 0; j < kWin; ++j) t[j] = SGN > 0 ? v[j] : v[kWin - 1 - j];
+    store8(base + (SGN > 0 ? i0 : i0 - (kWin - 1)), t);
+  } else {
+#pragma unroll
+    for (int j = 0; j < kWin; ++j)
+      if (j < nw) st_act(base, i0 + SGN * j, v[j]);
   }
 }
 
-// One scan step of 8 states: a = exp(Δ A), h = a h + Δ u B, partial readout Σ C h.
-__device__ __forceinline__ float scan_step(float dl, float du, const float (&A2)[8], float (&h)[8],
-                                           const float4& b0, const float4& b1, const float4& c0,
-                                           const float4& c1) {
-  const float Bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-  const float Cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+// Raw u and Δ_raw of steps [i0, i0+nw) of one direction.
+template <typename T, int MODE, int ORDER, int DIR, bool FULL>
+__device__ __forceinline__ void load_window(const ScanArgs& a, const Lane& l, const DirArgs& da, int i0, int nw,
+                                            float (&uu)[kWin], float (&xr)[kWin]) {
+  using Dr = Dir<MODE, DIR>;
+  const T* ub = static_cast<const T*>(a.u) + static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(l.dd) * a.L;
+  const T* db = static_cast<const T*>(da.draw) + static_cast<int64_t>(l.b) * da.draw_bs + static_cast<int64_t>(l.dd) * a.L;
+  if (ORDER == 0) {
+    load_seq<Dr::kPosSgn, FULL>(ub, Dr::pos(l, i0), nw, uu);
+  } else {
+#pragma unroll
+    for (int j = 0; j < kWin; ++j) uu[j] = (FULL || j < nw) ? ld_act(ub, elem<ORDER>(a, Dr::pos(l, i0 + j))) : 0.0f;
+  }
+  load_seq<Dr::kSidxSgn, FULL>(db, Dr::sidx(a, l, i0), nw, xr);
+}
+
+__device__ __forceinline__ void load_a2(const DirArgs& da, int dd, float (&A2)[kN]) {
+#pragma unroll
+  for (int n = 0; n < kN; ++n) A2[n] = -__expf(da.A_log[static_cast<int64_t>(dd) * kN + n]) * kLog2e;  // A = -exp(A_log)
+}
+
+// B/C of one position: 16 + 16 wave-uniform floats (two s_load_dwordx16).
+__device__ __forceinline__ void load_bc(scalar_fp p, float (&bc)[kBC]) {
+#pragma unroll
+  for (int q = 0; q < kBC; ++q) bc[q] = p[q];
+}
+
+// One token for 16 states, h = exp2(Δ A') h + (Δu) B; returns Σ C h.  The B/C of the next
+// token (nxt) is requested right after the first use of this token's B/C (cur): scalar loads may
+// return out of order, so a wait for cur waits for every scalar load in flight, and issuing nxt
+// only after that wait leaves it a whole token of VALU work to arrive.
+__device__ __forceinline__ float scan_token(float dl, float du, const float (&A2)[kN], float (&h)[kN],
+                                           const float (&cur)[kBC], float (&nxt)[kBC], scalar_fp nxt_p) {
+  float an[kN];
+#pragma unroll
+  for (int n = 0; n < kN; ++n) an[n] = __builtin_amdgcn_exp2f(dl * A2[n]);
+#pragma unroll
+  for (int n = 0; n < kN; ++n) h[n] = h[n] * an[n];
+  h[0] = __builtin_fmaf(du, cur[0], h[0]);
+  __builtin_amdgcn_sched_barrier(0);
+  load_bc(nxt_p, nxt);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int n = 1; n < kN; ++n) h[n] = __builtin_fmaf(du, cur[n], h[n]);
   float y0 = 0.0f, y1 = 0.0f;
 #pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    const float an = __builtin_amdgcn_exp2f(dl * A2[n]);
-    h[n] = __builtin_fmaf(an, h[n], du * Bv[n]);
-    if (n & 1) y1 = __builtin_fmaf(Cv[n], h[n], y1);
-    else y0 = __builtin_fmaf(Cv[n], h[n], y0);
+  for (int n = 0; n < kN; n += 2) {
+    y0 = __builtin_fmaf(cur[kN + n], h[n], y0);
+    y1 = __builtin_fmaf(cur[kN + n + 1], h[n + 1], y1);
   }
   return y0 + y1;
 }
 
-__device__ __forceinline__ size_t smem_tiles_bytes() {
-  return sizeof(float2) * 2 * kTS * kCH + sizeof(float) * 2 * kBCStride;
+// Steps [i0, i0 + kWin) of one direction.  On entry bcA holds the B/C of step i0; on exit bcA
+// holds the B/C of step i0 + kWin.  The buffers alternate between the steps, so no register
+// copies are needed.  The one-past-the-end prefetch of a direction's last step stays inside the
+// B/C copy: the forward row is followed by the backward row of the same batch, and the backward
+// direction runs towards the forward row.
+template <int MODE, int DIR>
+__device__ __forceinline__ void run_steps(const Lane& l, int i0, const float (&dl)[kWin], const float (&du)[kWin],
+                                          const float (&A2)[kN], float (&h)[kN], float (&bcA)[kBC],
+                                          float (&bcB)[kBC], scalar_fp bct, float (&y)[kWin]) {
+  using Dr = Dir<MODE, DIR>;
+  // Address of step i0 + k as a window base plus an immediate offset.
+  const int64_t p0 = Dr::pos(l, i0);
+  scalar_fp base = DIR == 0 ? bct + p0 * kBC : bct + (p0 - kWin) * kBC;
+#pragma unroll
+  for (int j = 0; j < kWin; j += 2) {
+    y[j] = scan_token(dl[j], du[j], A2, h, bcA, bcB, base + (DIR == 0 ? j + 1 : kWin - j - 1) * kBC);
+    y[j + 1] = scan_token(dl[j + 1], du[j + 1], A2, h, bcB, bcA, base + (DIR == 0 ? j + 2 : kWin - j - 2) * kBC);
+  }
+}
+
+// One step i of one direction outside the full windows (chunk tails): raw loads, Δ, the token
+// update and the B/C prefetch of step i + 1 into bcA.  Returns y + D·u; *u_out = u.
+template <typename T, int MODE, int ORDER, int DIR>
+__device__ __forceinline__ float single_step(const ScanArgs& a, const Lane& l, const DirArgs& da, float bias, float Dv,
+                                             int i, const float (&A2)[kN], float (&h)[kN], scalar_fp bct,
+                                             float (&bcA)[kBC], float* dl_out) {
+  using Dr = Dir<MODE, DIR>;
+  const T* ub = static_cast<const T*>(a.u) + static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(l.dd) * a.L;
+  const T* db = static_cast<const T*>(da.draw) + static_cast<int64_t>(l.b) * da.draw_bs + static_cast<int64_t>(l.dd) * a.L;
+  const float uu = ld_act(ub, elem<ORDER>(a, Dr::pos(l, i)));
+  const float dl = softplus_f(ld_act(db, Dr::sidx(a, l, i)) + bias);
+  float bcB[kBC];
+  const float y = scan_token(dl, dl * uu, A2, h, bcA, bcB, bct + Dr::pos(l, i + 1) * kBC);
+#pragma unroll
+  for (int q = 0; q < kBC; ++q) bcA[q] = bcB[q];
+  *dl_out = dl;
+  return y + Dv * uu;
+}
+
+// Δ and Δ·u of a window from its raw u and Δ_raw.
+__device__ __forceinline__ void prep_window(const float (&uu)[kWin], const float (&xr)[kWin], float bias,
+                                            float (&dl)[kWin], float (&du)[kWin]) {
+#pragma unroll
+  for (int j = 0; j < kWin; ++j) {
+    dl[j] = softplus_f(xr[j] + bias);
+    du[j] = dl[j] * uu[j];
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
 // Pass A: per chunk and direction, the end state of the chunk scanned from a zero state, and Σ Δ.
 
-template <typename T>
-__global__ __launch_bounds__(kThreads, 2) void chunk_state_kernel(ScanArgs a) {
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  Tiles t{reinterpret_cast<float2*>(smem_raw),
-          reinterpret_cast<float*>(smem_raw + sizeof(float2) * 2 * kTS * kCH)};
-  int b, c, g;
-  tile_coords(a, b, c, g);
-  const LaneInfo li = lane_info();
-  const int d0 = g * kCH;
-  const int d = d0 + li.ch;
-  const int64_t s_lo = static_cast<int64_t>(c) * a.K;
-  const int Kc = static_cast<int>(a.L - s_lo < a.K ? a.L - s_lo : a.K);
-  float A2[8];
-  load_a2(a, li, d, A2);
-  float h[8];
+template <typename T, int MODE, int ORDER, int DIR>
+__device__ __forceinline__ void state_window(const ScanArgs& a, const Lane& l, const DirArgs& da, float bias, int i0,
+                                             int i_full_end, const float (&A2)[kN], float (&h)[kN], float& S,
+                                             float (&uu)[kWin], float (&xr)[kWin], scalar_fp bct,
+                                             float (&bcA)[kBC], float (&bcB)[kBC]) {
+  float dl[kWin], du[kWin], y[kWin];
+  prep_window(uu, xr, bias, dl, du);
+  if (i0 + kWin < i_full_end) load_window<T, MODE, ORDER, DIR, true>(a, l, da, i0 + kWin, kWin, uu, xr);
 #pragma unroll
-  for (int n = 0; n < 8; ++n) h[n] = 0.0f;
+  for (int j = 0; j < kWin; ++j) S += dl[j];
+  run_steps<MODE, DIR>(l, i0, dl, du, A2, h, bcA, bcB, bct, y);
+}
+
+template <typename T, int MODE, int ORDER, int DIR>
+__device__ __forceinline__ void chunk_state_dir(const ScanArgs& a, const Lane& l) {
+  using Dr = Dir<MODE, DIR>;
+  const DirArgs& da = DIR == 0 ? a.d0 : a.d1;
+  float A2[kN], h[kN];
+  load_a2(da, l.dd, A2);
+#pragma unroll
+  for (int n = 0; n < kN; ++n) h[n] = 0.0f;
+  const float bias = da.bias[l.dd];
+  scalar_fp bct = (scalar_fp)(a.bct) + ((static_cast<int64_t>(l.b) * 2 + DIR) * a.L) * kBC;
   float S = 0.0f;
-  const float2* myD = t.tD + li.dir * kTS * kCH + li.ch;
-  const float* myBC = t.tBC + li.dir * kBCStride + li.half * 8;
-  for (int i0 = 0; i0 < Kc; i0 += kTS) {
-    const int ns = Kc - i0 < kTS ? Kc - i0 : kTS;
-    __syncthreads();
-    produce_tile<T, false>(a, b, d0, s_lo, Kc, i0, ns, t, nullptr, 0);
-    __syncthreads();
-    for (int jj = 0; jj < ns; ++jj) {
-      const float2 dv = myD[jj * kCH];
-      const float* p = myBC + jj * 32;
-      const float4 b0 = *reinterpret_cast<const float4*>(p);
-      const float4 b1 = *reinterpret_cast<const float4*>(p + 4);
-      S += dv.x;
-      const float Bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-#pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        const float an = __builtin_amdgcn_exp2f(dv.x * A2[n]);
-        h[n] = __builtin_fmaf(an, h[n], dv.y * Bv[n]);
-      }
-    }
+  float uu[kWin], xr[kWin], bcA[kBC], bcB[kBC];
+  const int full_end = (l.Kc / kWin) * kWin;
+  load_bc(bct + Dr::pos(l, 0) * kBC, bcA);
+  if (full_end > 0) load_window<T, MODE, ORDER, DIR, true>(a, l, da, 0, kWin, uu, xr);
+  for (int i0 = 0; i0 < full_end; i0 += kWin)
+    state_window<T, MODE, ORDER, DIR>(a, l, da, bias, i0, full_end, A2, h, S, uu, xr, bct, bcA, bcB);
+  for (int i = full_end; i < l.Kc; ++i) {
+    float dl;
+    single_step<T, MODE, ORDER, DIR>(a, l, da, bias, 0.0f, i, A2, h, bct, bcA, &dl);
+    S += dl;
   }
-  if (d < a.dim) {
-    float* ag = a.agg + ((((static_cast<int64_t>(b) * a.dim + d) * 2 + li.dir) * a.nch) + c) * kAggStride;
+  if (l.valid) {
+    float* ag = a.agg + ((((static_cast<int64_t>(l.b) * a.dim + l.d) * 2 + DIR) * a.nch) + l.c) * kAggStride;
 #pragma unroll
-    for (int n = 0; n < 8; ++n) ag[li.half * 8 + n] = h[n];
-    if (li.half == 0) ag[kN] = S;
+    for (int n = 0; n < kN; ++n) ag[n] = h[n];
+    ag[kN] = S;
   }
+}
+
+template <typename T, int MODE, int ORDER>
+__global__ __launch_bounds__(kThreads) void chunk_state_kernel(ScanArgs a) {
+  const Lane l = lane_ctx(a);
+  if (threadIdx.x < kW) chunk_state_dir<T, MODE, ORDER, 0>(a, l);
+  else chunk_state_dir<T, MODE, ORDER, 1>(a, l);
 }
 
 // ---------------------------------------------------------------------------------------------
 // Main pass: fused bidirectional scan of one chunk with meet-in-the-middle combination.
 
-template <typename T>
-__global__ __launch_bounds__(kThreads, 2) void scan_pair_kernel(ScanArgs a) {
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  Tiles t{reinterpret_cast<float2*>(smem_raw),
-          reinterpret_cast<float*>(smem_raw + sizeof(float2) * 2 * kTS * kCH)};
-  float* ybuf = reinterpret_cast<float*>(smem_raw + smem_tiles_bytes());
-  const int ybs = (a.K + 1) | 1;  // odd row stride: the 16 channel rows fall in distinct banks
+// Finished outputs of steps [i0, i0+nw) of one direction (second phase).
+template <typename T, int MODE, int ORDER, int DIR, bool FULL>
+__device__ __forceinline__ void finish_window(const ScanArgs& a, const Lane& l, int i0, int nw, const float (&yo)[kWin]) {
+  using Dr = Dir<MODE, DIR>;
+  const int64_t rowb = static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(l.d) * a.L;
+  T* ob = static_cast<T*>(a.out) + rowb;
+  const int64_t p0 = Dr::pos(l, i0);
+  if (MODE == kModeVim) {
+    // out = (y_f + y_b) / 2 * silu(z): the gate is applied once to the fused sum
+    float zz[kWin], o[kWin];
+    load_seq<Dr::kPosSgn, FULL>(static_cast<const T*>(a.z) + rowb, p0, nw, zz);
+#pragma unroll
+    for (int j = 0; j < kWin; ++j) o[j] = 0.5f * yo[j] * silu_f(zz[j]);
+    store_seq<Dr::kPosSgn, FULL>(ob, p0, nw, o);
+  } else if (MODE == kModeFirstPair) {
+    if (ORDER == 0) {
+      store_seq<Dr::kPosSgn, FULL>(a.wsy + rowb, p0, nw, yo);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kWin; ++j)
+        if (FULL || j < nw) a.wsy[rowb + elem<ORDER>(a, p0 + Dr::kPosSgn * j)] = yo[j];
+    }
+  } else {
+    const T* zb = a.z ? static_cast<const T*>(a.z) + rowb : nullptr;
+#pragma unroll
+    for (int j = 0; j < kWin; ++j) {
+      if (FULL || j < nw) {
+        const int64_t e = elem<ORDER>(a, p0 + Dr::kPosSgn * j);
+        float w = yo[j] + a.wsy[rowb + e];
+        if (zb) w *= silu_f(ld_act(zb, e));
+        st_act(ob, e, w);
+      }
+    }
+  }
+}
 
-  int b, c, g;
-  tile_coords(a, b, c, g);
-  const LaneInfo li = lane_info();
-  const int d0 = g * kCH;
-  const int d = d0 + li.ch;
-  const bool valid = d < a.dim;
-  const int64_t s_lo = static_cast<int64_t>(c) * a.K;
-  const int Kc = static_cast<int>(a.L - s_lo < a.K ? a.L - s_lo : a.K);
+// Output of one finished position of one direction (second phase), element by element.
+template <typename T, int MODE, int ORDER, int DIR>
+__device__ __forceinline__ void finish_one(const ScanArgs& a, const Lane& l, int i, float yo) {
+  float v[kWin];
+  v[0] = yo;
+#pragma unroll
+  for (int j = 1; j < kWin; ++j) v[j] = 0.0f;
+  finish_window<T, MODE, ORDER, DIR, false>(a, l, i, 1, v);
+}
+
+// One full window of the main pass.  PHASE 0 stores y (with its D·u term) in the channel's LDS
+// row at the chunk positions; PHASE 1 adds the other direction's stored y and finishes the
+// outputs.
+template <typename T, int MODE, int ORDER, int DIR, int PHASE>
+__device__ __forceinline__ void pair_window(const ScanArgs& a, const Lane& l, const DirArgs& da, float bias, float Dv,
+                                            int i0, int i_full_end, const float (&A2)[kN], float (&h)[kN],
+                                            float (&uu)[kWin], float (&xr)[kWin], scalar_fp bct, float (&bcA)[kBC],
+                                            float (&bcB)[kBC], float* myY) {
+  float dl[kWin], du[kWin], dv[kWin], y[kWin];
+  prep_window(uu, xr, bias, dl, du);
+#pragma unroll
+  for (int j = 0; j < kWin; ++j) dv[j] = Dv * uu[j];
+  // Prefetch the next full window of this phase while this one is computed.
+  if (i0 + kWin < i_full_end) load_window<T, MODE, ORDER, DIR, true>(a, l, da, i0 + kWin, kWin, uu, xr);
+  run_steps<MODE, DIR>(l, i0, dl, du, A2, h, bcA, bcB, bct, y);
+  const int p0 = DIR == 0 ? i0 : l.Kc - 1 - i0;  // chunk position of step i0
+  if (PHASE == 0) {
+#pragma unroll
+    for (int j = 0; j < kWin; ++j) myY[p0 + (DIR == 0 ? j : -j)] = y[j] + dv[j];
+  } else {
+    float yo[kWin];
+#pragma unroll
+    for (int j = 0; j < kWin; ++j) yo[j] = myY[p0 + (DIR == 0 ? j : -j)] + y[j] + dv[j];
+    if (l.valid) finish_window<T, MODE, ORDER, DIR, true>(a, l, i0, kWin, yo);
+  }
+}
+
+// Steps [i_begin, i_end) of one phase: full windows, then the remaining steps one at a time.
+template <typename T, int MODE, int ORDER, int DIR, int PHASE>
+__device__ __forceinline__ void run_phase(const ScanArgs& a, const Lane& l, const DirArgs& da, float bias, float Dv,
+                                          int i_begin, int i_end, const float (&A2)[kN], float (&h)[kN],
+                                          scalar_fp bct, float (&bcA)[kBC], float (&bcB)[kBC], float* myY) {
+  float uu[kWin], xr[kWin];
+  const int full_end = i_begin + ((i_end - i_begin) / kWin) * kWin;
+  if (full_end > i_begin) load_window<T, MODE, ORDER, DIR, true>(a, l, da, i_begin, kWin, uu, xr);
+  for (int i0 = i_begin; i0 < full_end; i0 += kWin)
+    pair_window<T, MODE, ORDER, DIR, PHASE>(a, l, da, bias, Dv, i0, full_end, A2, h, uu, xr, bct, bcA, bcB, myY);
+  for (int i = full_end; i < i_end; ++i) {
+    float dl;
+    const float y = single_step<T, MODE, ORDER, DIR>(a, l, da, bias, Dv, i, A2, h, bct, bcA, &dl);
+    const int pos = DIR == 0 ? i : l.Kc - 1 - i;
+    if (PHASE == 0) myY[pos] = y;
+    else if (l.valid) finish_one<T, MODE, ORDER, DIR>(a, l, i, myY[pos] + y);
+  }
+}
+
+template <typename T, int MODE, int ORDER, int DIR>
+__device__ __forceinline__ void scan_pair_dir(const ScanArgs& a, const Lane& l, float* ybuf, int ybs) {
+  using Dr = Dir<MODE, DIR>;
+  const DirArgs& da = DIR == 0 ? a.d0 : a.d1;
+  const int Kc = l.Kc;
   const int M = (Kc + 1) >> 1;  // steps of the first phase
 
-  float A2[8];
-  load_a2(a, li, d, A2);
-  float h[8];
+  float A2[kN], h[kN];
+  load_a2(da, l.dd, A2);
 #pragma unroll
-  for (int n = 0; n < 8; ++n) h[n] = 0.0f;
+  for (int n = 0; n < kN; ++n) h[n] = 0.0f;
+  const float bias = da.bias[l.dd];
+  const float Dv = da.Dp[l.dd];
 
   // Carry-in: fold the preceding chunks' (Σ Δ, end state) pairs in scan order.
-  if (a.nch > 1 && valid) {
-    const float* ag = a.agg + ((static_cast<int64_t>(b) * a.dim + d) * 2 + li.dir) * a.nch * kAggStride;
-    const int j_begin = li.dir == 0 ? 0 : a.nch - 1;
-    const int j_count = li.dir == 0 ? c : a.nch - 1 - c;
-    const int j_step = li.dir == 0 ? 1 : -1;
-    for (int k = 0; k < j_count; ++k) {
-      const float* e = ag + (j_begin + k * j_step) * kAggStride;
+  if (a.nch > 1) {
+    const float* ag = a.agg + ((static_cast<int64_t>(l.b) * a.dim + l.dd) * 2 + DIR) * a.nch * kAggStride;
+    const int cnt = DIR == 0 ? l.c : a.nch - 1 - l.c;
+    for (int k = 0; k < cnt; ++k) {
+      const float* e = ag + (DIR == 0 ? k : a.nch - 1 - k) * kAggStride;
       const float S = e[kN];
 #pragma unroll
-      for (int n = 0; n < 8; ++n)
-        h[n] = __builtin_fmaf(__builtin_amdgcn_exp2f(A2[n] * S), h[n], e[li.half * 8 + n]);
+      for (int n = 0; n < kN; ++n) h[n] = __builtin_fmaf(__builtin_amdgcn_exp2f(A2[n] * S), h[n], e[n]);
     }
   }
 
-  const float2* myD = t.tD + li.dir * kTS * kCH + li.ch;
-  const float* myBC = t.tBC + li.dir * kBCStride + li.half * 8;
-  float* myY = ybuf + li.ch * ybs;
-  const bool writer = valid && li.half == 0;
+  scalar_fp bct = (scalar_fp)(a.bct) + ((static_cast<int64_t>(l.b) * 2 + DIR) * a.L) * kBC;
+  float* myY = ybuf + l.lane * ybs;
+  float bcA[kBC], bcB[kBC];
+  load_bc(bct + Dr::pos(l, 0) * kBC, bcA);
 
-  for (int phase = 0; phase < 2; ++phase) {
-    const int i_begin = phase == 0 ? 0 : M;
-    const int i_end = phase == 0 ? M : Kc;
-    for (int i0 = i_begin; i0 < i_end; i0 += kTS) {
-      const int ns = i_end - i0 < kTS ? i_end - i0 : kTS;
-      __syncthreads();
-      if (phase == 0)
-        produce_tile<T, true>(a, b, d0, s_lo, Kc, i0, ns, t, ybuf, ybs);
-      else
-        produce_tile<T, false>(a, b, d0, s_lo, Kc, i0, ns, t, ybuf, ybs);
-      __syncthreads();
-      for (int jj = 0; jj < ns; ++jj) {
-        const float2 dv = myD[jj * kCH];
-        const float* p = myBC + jj * 32;
-        const float4 b0 = *reinterpret_cast<const float4*>(p);
-        const float4 b1 = *reinterpret_cast<const float4*>(p + 4);
-        const float4 c0 = *reinterpret_cast<const float4*>(p + 16);
-        const float4 c1 = *reinterpret_cast<const float4*>(p + 20);
-        float yp = scan_step(dv.x, dv.y, A2, h, b0, b1, c0, c1);
-        yp += swap_pair(yp);
-        const int i = i0 + jj;
-        const int pos = li.dir == 0 ? i : Kc - 1 - i;
-        if (writer) {
-          // The middle token of an odd chunk is visited by both directions in the same step:
-          // the backward contribution goes to the spare slot at index Kc.
-          if (phase == 0 && li.dir == 1 && (Kc & 1) && i == M - 1)
-            myY[Kc] = yp;
-          else
-            myY[pos] += yp;
-        }
-      }
-    }
-    __syncthreads();
+  // Phase 0: steps [0, M).  For an odd chunk the backward direction reaches the middle token at
+  // its last phase-0 step, together with the forward direction; its value goes to spare slot Kc.
+  const int p0_end = (DIR == 1 && (Kc & 1)) ? M - 1 : M;
+  run_phase<T, MODE, ORDER, DIR, 0>(a, l, da, bias, Dv, 0, p0_end, A2, h, bct, bcA, bcB, myY);
+  if (p0_end < M) {
+    float dl;
+    myY[Kc] = single_step<T, MODE, ORDER, DIR>(a, l, da, bias, Dv, M - 1, A2, h, bct, bcA, &dl);
   }
+  __syncthreads();
+  // Phase 1: steps [M, Kc).
+  run_phase<T, MODE, ORDER, DIR, 1>(a, l, da, bias, Dv, M, Kc, A2, h, bct, bcA, bcB, myY);
+}
 
-  // Epilogue: combined rows -> output (coalesced along positions).
-  const int lane = threadIdx.x;
-  const T* zb = a.z ? static_cast<const T*>(a.z) + static_cast<int64_t>(b) * a.u_bs : nullptr;
-  T* ob = static_cast<T*>(a.out) + static_cast<int64_t>(b) * a.u_bs;
-  float* wb = a.wsy ? a.wsy + static_cast<int64_t>(b) * a.u_bs : nullptr;
-  for (int ch = 0; ch < kCH; ++ch) {
-    const int dd = d0 + ch;
-    if (dd >= a.dim) break;
-    const float* row = ybuf + ch * ybs;
-    const int64_t rbase = static_cast<int64_t>(dd) * a.L;
-    for (int pos = lane; pos < Kc; pos += kThreads) {
-      float v = row[pos];
-      if ((Kc & 1) && pos == M - 1) v += row[Kc];
-      const int64_t gi = rbase + elem_of(a, s_lo + pos);
-      if (a.mode == 0) {
-        st_act(ob, gi, 0.5f * v * silu_f(ld_act(zb, gi)));
-      } else if (a.mode == 1) {
-        wb[gi] = v;
-      } else {
-        float w = v + wb[gi];
-        if (zb) w *= silu_f(ld_act(zb, gi));
-        st_act(ob, gi, w);
-      }
-    }
+template <typename T, int MODE, int ORDER>
+__global__ __launch_bounds__(kThreads) void scan_pair_kernel(ScanArgs a) {
+  extern __shared__ float ybuf[];  // [kW][ybs]: y of the first direction to reach a position
+  const int ybs = (a.K + 1) | 1;   // odd row stride spreads the 64 lanes over the banks
+  const Lane l = lane_ctx(a);
+  if (threadIdx.x < kW) scan_pair_dir<T, MODE, ORDER, 0>(a, l, ybuf, ybs);
+  else scan_pair_dir<T, MODE, ORDER, 1>(a, l, ybuf, ybs);
+  __syncthreads();
+  // The middle position of an odd chunk: both directions stored their value in the first phase.
+  if ((l.Kc & 1) && threadIdx.x < kW && l.valid) {
+    const float* myY = ybuf + l.lane * ybs;
+    const int M = (l.Kc + 1) >> 1;
+    finish_one<T, MODE, ORDER, 0>(a, l, M - 1, myY[M - 1] + myY[l.Kc]);
   }
 }
 
@@ -396,11 +622,11 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Chunk length for a pair scan over L tokens with `base` = batch * channel-groups workgroups per
-// chunk.  One chunk when the y rows fit in LDS and there is enough parallelism; otherwise enough
-// chunks to reach kTargetBlocks workgroups, each no longer than kKMax.
+// chunk: one chunk when it fits an LDS row and there are enough workgroups, else enough chunks
+// of at most kKMax tokens to reach kTargetBlocks workgroups.
 int64_t plan_chunk(int64_t base, int64_t L, int64_t forced) {
-  if (forced > 0) return forced < L ? forced : L;
-  if (L <= kKMax && (base >= 1024 || L <= kMinChunk)) return L;
+  if (forced > 0) return forced < kKMax ? (forced < L ? forced : L) : (kKMax < L ? kKMax : L);
+  if (L <= kKMax && (base >= kTargetBlocks / 2 || L <= kMinChunk)) return L;
   int64_t nch = ceil_div(L, kKMax);
   const int64_t want = ceil_div(kTargetBlocks, base);
   if (want > nch) nch = want;
@@ -409,13 +635,15 @@ int64_t plan_chunk(int64_t base, int64_t L, int64_t forced) {
   return K;
 }
 
+size_t round256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+size_t bct_bytes(int64_t batch, int64_t L) { return round256(static_cast<size_t>(batch) * 2 * L * kBC * sizeof(float)); }
+
 size_t agg_bytes(int64_t batch, int64_t dim, int64_t L, int64_t K) {
   const int64_t nch = ceil_div(L, K);
   if (nch <= 1) return 0;
-  return static_cast<size_t>(batch) * dim * 2 * nch * kAggStride * sizeof(float);
+  return round256(static_cast<size_t>(batch) * dim * 2 * nch * kAggStride * sizeof(float));
 }
-
-size_t round256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 bool shape_ok(int64_t batch, int64_t dim, int64_t L) {
   if (batch < 1 || dim < 1 || L < 1) return false;
@@ -429,27 +657,31 @@ vmscan_status launch_failed(hipError_t e) {
   return VMSCAN_ERR_HIP;
 }
 
-template <typename T>
-vmscan_status run_pair(ScanArgs a, hipStream_t stream) {
+template <typename T, int MODE, int ORDER>
+vmscan_status run_pair(const ScanArgs& a, hipStream_t stream) {
   const int64_t nblocks = static_cast<int64_t>(a.batch) * a.nch * a.ngroups;
-  if (nblocks >= (int64_t{1} << 31)) return VMSCAN_ERR_SHAPE;
-  const size_t tiles = sizeof(float2) * 2 * kTS * kCH + sizeof(float) * 2 * kBCStride;
+  const int64_t tblocks = static_cast<int64_t>(a.batch) * 2 * ceil_div(a.L, kTransThreads);
+  if (nblocks >= (int64_t{1} << 31) || tblocks >= (int64_t{1} << 31)) return VMSCAN_ERR_SHAPE;
+  hipLaunchKernelGGL(bc_transpose_kernel<T>, dim3(static_cast<unsigned>(tblocks)), dim3(kTransThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return launch_failed(e);
   if (a.nch > 1) {
-    hipLaunchKernelGGL(chunk_state_kernel<T>, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), tiles,
+    hipLaunchKernelGGL((chunk_state_kernel<T, MODE, ORDER>), dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0,
                        stream, a);
-    const hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess) return launch_failed(e);
   }
-  const size_t ybs = static_cast<size_t>((a.K + 1) | 1);
-  const size_t smem = tiles + sizeof(float) * kCH * ybs;
-  hipLaunchKernelGGL(scan_pair_kernel<T>, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), smem, stream, a);
-  const hipError_t e = hipGetLastError();
+  const size_t smem = sizeof(float) * kW * static_cast<size_t>((a.K + 1) | 1);
+  hipLaunchKernelGGL((scan_pair_kernel<T, MODE, ORDER>), dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), smem,
+                     stream, a);
+  e = hipGetLastError();
   if (e != hipSuccess) return launch_failed(e);
   return VMSCAN_OK;
 }
 
+template <int MODE, int ORDER>
 vmscan_status run_pair_dtype(const ScanArgs& a, vmscan_dtype dtype, hipStream_t stream) {
-  return dtype == VMSCAN_F32 ? run_pair<float>(a, stream) : run_pair<uint16_t>(a, stream);
+  return dtype == VMSCAN_F32 ? run_pair<float, MODE, ORDER>(a, stream) : run_pair<uint16_t, MODE, ORDER>(a, stream);
 }
 
 }  // namespace
@@ -476,7 +708,7 @@ int vmscan_last_hip_error(void) { return g_last_hip_error; }
 
 int64_t vmscan_fwd_bidir_chunk_len(int64_t batch, int64_t dim, int64_t seqlen, int d_state) {
   if (!shape_ok(batch, dim, seqlen) || d_state != kN) return 0;
-  return plan_chunk(batch * ceil_div(dim, kCH), seqlen, 0);
+  return plan_chunk(batch * ceil_div(dim, kW), seqlen, 0);
 }
 
 size_t vmscan_fwd_bidir_workspace_bytes_ex(int64_t batch, int64_t dim, int64_t seqlen, int d_state,
@@ -484,8 +716,8 @@ size_t vmscan_fwd_bidir_workspace_bytes_ex(int64_t batch, int64_t dim, int64_t s
   if (!shape_ok(batch, dim, seqlen) || d_state != kN || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16) ||
       chunk_len < 0)
     return 0;
-  const int64_t K = plan_chunk(batch * ceil_div(dim, kCH), seqlen, chunk_len);
-  return agg_bytes(batch, dim, seqlen, K);
+  const int64_t K = plan_chunk(batch * ceil_div(dim, kW), seqlen, chunk_len);
+  return bct_bytes(batch, seqlen) + agg_bytes(batch, dim, seqlen, K);
 }
 
 size_t vmscan_fwd_bidir_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen, int d_state,
@@ -506,10 +738,10 @@ vmscan_status vmscan_fwd_bidir_ex(const void* u, const void* delta_raw, const vo
   if (d_state != kN || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16)) return VMSCAN_ERR_UNSUPPORTED;
   for (const void* p : ptrs)
     if (!aligned16(p)) return VMSCAN_ERR_ALIGN;
-  const int64_t K = plan_chunk(batch * ceil_div(dim, kCH), seqlen, chunk_len);
-  const size_t need = agg_bytes(batch, dim, seqlen, K);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return VMSCAN_ERR_WORKSPACE;
-  if (need > 0 && !aligned16(workspace)) return VMSCAN_ERR_ALIGN;
+  const int64_t K = plan_chunk(batch * ceil_div(dim, kW), seqlen, chunk_len);
+  const size_t need = vmscan_fwd_bidir_workspace_bytes_ex(batch, dim, seqlen, d_state, dtype, chunk_len);
+  if (!workspace || workspace_bytes < need) return VMSCAN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return VMSCAN_ERR_ALIGN;
 
   ScanArgs a{};
   a.u = u;
@@ -517,7 +749,8 @@ vmscan_status vmscan_fwd_bidir_ex(const void* u, const void* delta_raw, const vo
   a.z = z;
   a.out = out;
   a.wsy = nullptr;
-  a.agg = static_cast<float*>(workspace);
+  a.bct = static_cast<float*>(workspace);
+  a.agg = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + bct_bytes(batch, seqlen));
   a.d0 = DirArgs{delta_raw, dim * seqlen, B, C, kN * seqlen, A_log, D, delta_bias, 0};
   a.d1 = DirArgs{delta_raw, dim * seqlen, B_b, C_b, kN * seqlen, A_b_log, D_b, delta_bias, 0};
   a.L = seqlen;
@@ -525,12 +758,11 @@ vmscan_status vmscan_fwd_bidir_ex(const void* u, const void* delta_raw, const vo
   a.batch = static_cast<int>(batch);
   a.K = static_cast<int>(K);
   a.nch = static_cast<int>(ceil_div(seqlen, K));
-  a.ngroups = static_cast<int>(ceil_div(dim, kCH));
+  a.ngroups = static_cast<int>(ceil_div(dim, kW));
   a.order = 0;
   a.H = 1;
   a.W = static_cast<int>(seqlen);
-  a.mode = 0;
-  return run_pair_dtype(a, dtype, stream);
+  return run_pair_dtype<kModeVim, 0>(a, dtype, stream);
 }
 
 vmscan_status vmscan_fwd_bidir(const void* u, const void* delta_raw, const void* z, const float* A_log,
@@ -549,9 +781,9 @@ size_t ss2d_cross_scan_workspace_bytes_ex(int64_t batch, int64_t dim, int64_t H,
   const int64_t L = H * W;
   if (!shape_ok(batch, dim, L) || d_state != kN || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16) || chunk_len < 0)
     return 0;
-  const int64_t K = plan_chunk(batch * ceil_div(dim, kCH), L, chunk_len);
+  const int64_t K = plan_chunk(batch * ceil_div(dim, kW), L, chunk_len);
   const size_t img = round256(static_cast<size_t>(batch) * dim * L * sizeof(float));
-  return img + 2 * round256(agg_bytes(batch, dim, L, K));
+  return img + bct_bytes(batch, L) + agg_bytes(batch, dim, L, K);
 }
 
 size_t ss2d_cross_scan_workspace_bytes(int64_t batch, int64_t dim, int64_t H, int64_t W, int d_state,
@@ -578,12 +810,9 @@ vmscan_status ss2d_cross_scan_fwd_ex(const void* x, const void* delta_raw, const
   if (!workspace || workspace_bytes < need) return VMSCAN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return VMSCAN_ERR_ALIGN;
 
-  const int64_t K = plan_chunk(batch * ceil_div(dim, kCH), L, chunk_len);
+  const int64_t K = plan_chunk(batch * ceil_div(dim, kW), L, chunk_len);
   const size_t img = round256(static_cast<size_t>(batch) * dim * L * sizeof(float));
-  const size_t aggb = round256(agg_bytes(batch, dim, L, K));
-  float* wsy = static_cast<float*>(workspace);
-  float* agg0 = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + img);
-  float* agg1 = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + img + aggb);
+  unsigned char* wsp = static_cast<unsigned char*>(workspace);
 
   const size_t esz = dtype == VMSCAN_F32 ? 4 : 2;
   auto off = [&](const void* p, int64_t elems) {
@@ -600,13 +829,15 @@ vmscan_status ss2d_cross_scan_fwd_ex(const void* x, const void* delta_raw, const
   a.u_bs = dim * L;
   a.z = z;
   a.out = out;
-  a.wsy = wsy;
+  a.wsy = reinterpret_cast<float*>(wsp);
+  a.bct = reinterpret_cast<float*>(wsp + img);
+  a.agg = reinterpret_cast<float*>(wsp + img + bct_bytes(batch, L));
   a.L = L;
   a.dim = static_cast<int>(dim);
   a.batch = static_cast<int>(batch);
   a.K = static_cast<int>(K);
   a.nch = static_cast<int>(ceil_div(L, K));
-  a.ngroups = static_cast<int>(ceil_div(dim, kCH));
+  a.ngroups = static_cast<int>(ceil_div(dim, kW));
   a.H = static_cast<int>(H);
   a.W = static_cast<int>(W);
 
@@ -614,17 +845,14 @@ vmscan_status ss2d_cross_scan_fwd_ex(const void* x, const void* delta_raw, const
   a.d0 = dir_args(0, 0);
   a.d1 = dir_args(2, 1);
   a.order = 0;
-  a.mode = 1;
-  a.agg = agg0;
-  vmscan_status st = run_pair_dtype(a, dtype, stream);
+  vmscan_status st = run_pair_dtype<kModeFirstPair, 0>(a, dtype, stream);
   if (st != VMSCAN_OK) return st;
   // Pair 2: column-major order (direction 1) and its reverse (direction 3) -> + image -> out.
+  // Its transpose and chunk-state kernels reuse the B/C and carry regions after pair 1 (same stream).
   a.d0 = dir_args(1, 0);
   a.d1 = dir_args(3, 1);
   a.order = 1;
-  a.mode = 2;
-  a.agg = agg1;
-  return run_pair_dtype(a, dtype, stream);
+  return run_pair_dtype<kModeSecondPair, 1>(a, dtype, stream);
 }
 
 vmscan_status ss2d_cross_scan_fwd(const void* x, const void* delta_raw, const float* A_log, const void* B,

@@ -96,22 +96,37 @@ def test_fwd_misaligned(lib):
         assert _fwd(lib, p) == ERR_ALIGN, i
 
 
+def r256(x):
+    return (x + 255) // 256 * 256
+
+
+def bct_bytes(nb, L):
+    return r256(nb * 2 * L * 32 * 4)
+
+
+def agg_bytes(nb, nd, L, K):
+    nch = -(-L // K)
+    return 0 if nch <= 1 else r256(nb * nd * 2 * nch * 17 * 4)
+
+
 def test_fwd_workspace(lib):
-    # a chunked plan needs a workspace; a too-small or missing one is rejected
+    # the workspace holds the fp32 B/C copy and, for chunked plans, the chunk carries
     need = lib.vmscan_fwd_bidir_workspace_bytes_ex(I64(2), I64(16), I64(100), 16, 1, I64(16))
-    assert need == 2 * 16 * 2 * 7 * 17 * 4
+    assert need == bct_bytes(2, 100) + agg_bytes(2, 16, 100, 16)
+    assert _fwd(lib, _good_ptrs(), L=100, chunk=16) == ERR_WORKSPACE
     assert _fwd(lib, _good_ptrs(), L=100, chunk=16) == ERR_WORKSPACE
     assert _fwd(lib, _good_ptrs(), L=100, chunk=16, ws=0x80000, wsb=need - 1) == ERR_WORKSPACE
     assert _fwd(lib, _good_ptrs(), L=100, chunk=16, ws=0x80008, wsb=need) == ERR_ALIGN
 
 
 def test_workspace_queries(lib):
-    assert lib.vmscan_fwd_bidir_workspace_bytes(I64(128), I64(384), I64(197), 16, 1) == 0
+    assert lib.vmscan_fwd_bidir_chunk_len(I64(128), I64(384), I64(197), 16) == 197
+    assert lib.vmscan_fwd_bidir_workspace_bytes(I64(128), I64(384), I64(197), 16, 1) == bct_bytes(128, 197)
     assert lib.vmscan_fwd_bidir_workspace_bytes(I64(0), I64(384), I64(197), 16, 1) == 0
     K = lib.vmscan_fwd_bidir_chunk_len(I64(8), I64(384), I64(6085), 16)
-    assert 64 <= K <= 512
-    nch = -(-6085 // K)
-    assert lib.vmscan_fwd_bidir_workspace_bytes(I64(8), I64(384), I64(6085), 16, 1) == 8 * 384 * 2 * nch * 17 * 4
+    assert 32 <= K <= 206
+    assert lib.vmscan_fwd_bidir_workspace_bytes(I64(8), I64(384), I64(6085), 16, 1) == \
+        bct_bytes(8, 6085) + agg_bytes(8, 384, 6085, K)
     img = 32 * 512 * 3136 * 4
     assert lib.ss2d_cross_scan_workspace_bytes(I64(32), I64(512), I64(56), I64(56), 16, 1) >= img
     assert lib.ss2d_cross_scan_workspace_bytes(I64(32), I64(512), I64(0), I64(56), 16, 1) == 0
