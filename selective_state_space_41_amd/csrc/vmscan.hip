@@ -69,78 +69,51 @@ __device__ __forceinline__ float ld_act(const uint16_t* p, int64_t i) {
   return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
 }
 
+// Round to bfloat16, nearest-even (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t x = __float_as_uint(f);
-  if ((x & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((x >> 16) | 0x40u);  // quiet NaN
-  x += 0x7fffu + ((x >> 16) & 1u);
-  return static_cast<uint16_t>(x >> 16);
+  const __bf16 v = static_cast<__bf16>(f);
+  uint16_t r;
+  __builtin_memcpy(&r, &v, sizeof(r));
+  return r;
 }
 __device__ __forceinline__ void st_act(float* p, int64_t i, float v) { p[i] = v; }
 __device__ __forceinline__ void st_act(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16_rne(v); }
 
-// 8 consecutive elements starting at p (any element alignment).
-__device__ __forceinline__ void load8(const uint16_t* p, float (&t)[kWin]) {
+// Eight consecutive elements (any element alignment), kept as loaded until unpacked so that a
+// prefetch is not waited for before its values are used.
+template <typename T>
+struct Run8;
+template <>
+struct Run8<uint16_t> {
   uint4 r;
-  __builtin_memcpy(&r, p, sizeof(r));
-  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+  __device__ __forceinline__ void load(const uint16_t* p) { __builtin_memcpy(&r, p, sizeof(r)); }
+  template <bool REV>
+  __device__ __forceinline__ void unpack(float (&v)[kWin]) const {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    t[2 * k] = __uint_as_float(w[k] << 16);
-    t[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+    for (int k = 0; k < 4; ++k) {
+      v[REV ? kWin - 1 - 2 * k : 2 * k] = __uint_as_float(w[k] << 16);
+      v[REV ? kWin - 2 - 2 * k : 2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+    }
   }
-}
-__device__ __forceinline__ void load8(const float* p, float (&t)[kWin]) {
+};
+template <>
+struct Run8<float> {
   float4 r0, r1;
-  __builtin_memcpy(&r0, p, sizeof(r0));
-  __builtin_memcpy(&r1, p + 4, sizeof(r1));
-  t[0] = r0.x; t[1] = r0.y; t[2] = r0.z; t[3] = r0.w;
-  t[4] = r1.x; t[5] = r1.y; t[6] = r1.z; t[7] = r1.w;
-}
-__device__ __forceinline__ void store8(uint16_t* p, const float (&t)[kWin]) {
-  uint32_t w[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k)
-    w[k] = static_cast<uint32_t>(f32_to_bf16_rne(t[2 * k])) | (static_cast<uint32_t>(f32_to_bf16_rne(t[2 * k + 1])) << 16);
-  const uint4 r = make_uint4(w[0], w[1], w[2], w[3]);
-  __builtin_memcpy(p, &r, sizeof(r));
-}
-__device__ __forceinline__ void store8(float* p, const float (&t)[kWin]) {
-  const float4 r0 = make_float4(t[0], t[1], t[2], t[3]);
-  const float4 r1 = make_float4(t[4], t[5], t[6], t[7]);
-  __builtin_memcpy(p, &r0, sizeof(r0));
-  __builtin_memcpy(p + 4, &r1, sizeof(r1));
-}
-
-// v[j] = base[i0 + sgn*j] for j < nw (nw <= kWin); sgn is wave-uniform.  Full windows are one
-// vector load of the 8-element run; short windows read only their valid elements.
-template <typename T>
-__device__ __forceinline__ void load_run(const T* base, int64_t i0, int sgn, int nw, float (&v)[kWin]) {
-  if (nw == kWin) {
-    float t[kWin];
-    load8(base + (sgn > 0 ? i0 : i0 - (kWin - 1)), t);
-#pragma unroll
-    for (int j = 0; j < kWin; ++j) v[j] = sgn > 0 ? t[j] : t[kWin - 1 - j];
-  } else {
-#pragma unroll
-    for (int j = 0; j < kWin; ++j) v[j] = j < nw ? ld_act(base, i0 + sgn * j) : 0.0f;
+  __device__ __forceinline__ void load(const float* p) {
+    __builtin_memcpy(&r0, p, sizeof(r0));
+    __builtin_memcpy(&r1, p + 4, sizeof(r1));
   }
-}
-template <typename T>
-__device__ __forceinline__ void store_run(T* base, int64_t i0, int sgn, int nw, const float (&v)[kWin]) {
-  if (nw == kWin) {
-    float t[kWin];
+  template <bool REV>
+  __device__ __forceinline__ void unpack(float (&v)[kWin]) const {
+    const float t[kWin] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
-    for (int j = 0; j < kWin; ++j) t[j] = sgn > 0 ? v[j] : v[kWin - 1 - j];
-    store8(base + (sgn > 0 ? i0 : i0 - (kWin - 1)), t);
-  } else {
-#pragma unroll
-    for (int j = 0; j < kWin; ++j)
-      if (j < nw) st_act(base, i0 + sgn * j, v[j]);
+    for (int j = 0; j < kWin; ++j) v[j] = t[REV ? kWin - 1 - j : j];
   }
-}
+};
 
-// softplus(x) = log(1 + e^x).  With e = e^x and s = fl(1 + e), e - (s - 1) is exactly the
-// rounding error of s (for e <= 1; for e > 1 it is below the result's resolution), and
+// softplus(x) = log(1 + e^x).  With e = e^x and s = fl(1 + e), c = e - (s - 1) is the rounding
+// error of s (exactly for e <= 1; for e > 1 it is below the result's resolution), and
 // log(1 + e) = log(s) + log(1 + c/s) ~= ln2 * log2(s) + c.  This keeps full fp32 relative
 // accuracy for the e ~ 1e-3 that the Δ bias range produces, where a plain log(1 + e) loses
 // about three digits.  Above 20 the correction to x is below fp32 resolution.
@@ -187,15 +160,10 @@ struct ScanArgs {
   DirArgs d0, d1;  // forward and backward direction of the pair
   int64_t L;
   int dim, batch, K, nch, ngroups;
-  int order;       // 0: position s -> element s; 1: column-major position -> row-major pixel
-  int H, W;
+  int H, W;        // image shape for the column order (SS2D); H = 1 otherwise
 };
 
 enum { kModeVim = 0, kModeFirstPair = 1, kModeSecondPair = 2 };
-
-__device__ __forceinline__ int64_t elem_of(const ScanArgs& a, int64_t s) {
-  return a.order == 0 ? s : static_cast<int64_t>(s % a.H) * a.W + s / a.H;
-}
 
 // ---------------------------------------------------------------------------------------------
 // B/C transpose: bct[b][dir][s][0..15] = B_dir[b][:, si(s)], bct[b][dir][s][16..31] = C_dir[...]
@@ -225,12 +193,11 @@ __global__ __launch_bounds__(kTransThreads) void bc_transpose_kernel(ScanArgs a)
 }
 
 // ---------------------------------------------------------------------------------------------
-// Scan kernels.  Everything that differs between the forward and backward wave, the Vim and the
-// SS2D pairs and the two scan orders is a template parameter, so the token loop has no
-// data-dependent branches:
+// Scan kernels.  What differs between the forward and backward wave, the Vim and SS2D pairs and
+// the two scan orders is a template parameter, so the token loop has no data-dependent branches:
 //   DIR   0: step i visits chunk position i; 1: position Kc-1-i
-//   MODE  kModeVim / kModeFirstPair / kModeSecondPair (output handling; SS2D backward tensors are
-//         stored in reversed position order)
+//   MODE  kModeVim / kModeFirstPair / kModeSecondPair (SS2D backward tensors are stored in
+//         reversed position order; the modes differ in the epilogue)
 //   ORDER 0: u element = position; 1: column-major position -> row-major pixel
 
 struct Lane {
@@ -260,6 +227,8 @@ __device__ __forceinline__ Lane lane_ctx(const ScanArgs& a) {
 template <int MODE, int DIR>
 struct Dir {
   static constexpr bool kRev = MODE != kModeVim && DIR == 1;  // storage order reversed
+  static constexpr int kPosSgn = DIR == 0 ? 1 : -1;
+  static constexpr int kSidxSgn = kRev ? -kPosSgn : kPosSgn;
   // global position of step i
   static __device__ __forceinline__ int64_t pos(const Lane& l, int i) {
     return DIR == 0 ? l.s_lo + i : l.s_lo + l.Kc - 1 - i;
@@ -268,57 +237,64 @@ struct Dir {
   static __device__ __forceinline__ int64_t sidx(const ScanArgs& a, const Lane& l, int i) {
     return kRev ? a.L - 1 - pos(l, i) : pos(l, i);
   }
-  static constexpr int kPosSgn = DIR == 0 ? 1 : -1;
-  static constexpr int kSidxSgn = kRev ? -kPosSgn : kPosSgn;
 };
 
-template <int ORDER>
-__device__ __forceinline__ int64_t elem(const ScanArgs& a, int64_t s) {
-  return ORDER == 0 ? s : static_cast<int64_t>(s % a.H) * a.W + s / a.H;
-}
-
-// v[j] = base[i0 + SGN*j]; FULL: j < kWin as one vector load of the 8-element run; else j < nw.
-template <int SGN, bool FULL, typename T>
-__device__ __forceinline__ void load_seq(const T* base, int64_t i0, int nw, float (&v)[kWin]) {
-  if (FULL) {
-    float t[kWin];
-    load8(base + (SGN > 0 ? i0 : i0 - (kWin - 1)), t);
-#pragma unroll
-    for (int j = 0; j < kWin; ++j) v[j] = SGN > 0 ? t[j] : t[kWin - 1 - j];
-  } else {
-#pragma unroll
-    for (int j = 0; j < kWin; ++j) v[j] = j < nw ? ld_act(base, i0 + SGN * j) : 0.0f;
+// Row-major pixel of a column-major position, advanced one position at a time (SS2D column
+// order: position p is pixel (p mod H, p div H)).  L < 2^31 for SS2D, so int32 suffices.
+struct ColPix {
+  int h, w, H, W;
+  __device__ __forceinline__ void init(int p, int H_, int W_) {
+    H = H_;
+    W = W_;
+    w = p / H;
+    h = p - w * H;
   }
-}
-template <int SGN, bool FULL, typename T>
-__device__ __forceinline__ void store_seq(T* base, int64_t i0, int nw, const float (&v)[kWin]) {
-  if (FULL) {
-    float t[kWin];
-#pragma unroll
-    for (int j = 0; j < kWin; ++j) t[j] = SGN > 0 ? v[j] : v[kWin - 1 - j];
-    store8(base + (SGN > 0 ? i0 : i0 - (kWin - 1)), t);
-  } else {
-#pragma unroll
-    for (int j = 0; j < kWin; ++j)
-      if (j < nw) st_act(base, i0 + SGN * j, v[j]);
+  __device__ __forceinline__ int pix() const { return h * W + w; }
+  template <int SGN>
+  __device__ __forceinline__ void step() {
+    if (SGN > 0) {
+      if (++h == H) { h = 0; ++w; }
+    } else {
+      if (--h < 0) { h = H - 1; --w; }
+    }
   }
-}
+};
 
-// Raw u and Δ_raw of steps [i0, i0+nw) of one direction.
-template <typename T, int MODE, int ORDER, int DIR, bool FULL>
-__device__ __forceinline__ void load_window(const ScanArgs& a, const Lane& l, const DirArgs& da, int i0, int nw,
-                                            float (&uu)[kWin], float (&xr)[kWin]) {
+// Raw u and Δ_raw of a full window of 8 steps of one direction, kept as loaded until unpacked.
+template <typename T, int MODE, int ORDER, int DIR>
+struct Window {
   using Dr = Dir<MODE, DIR>;
-  const T* ub = static_cast<const T*>(a.u) + static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(l.dd) * a.L;
-  const T* db = static_cast<const T*>(da.draw) + static_cast<int64_t>(l.b) * da.draw_bs + static_cast<int64_t>(l.dd) * a.L;
-  if (ORDER == 0) {
-    load_seq<Dr::kPosSgn, FULL>(ub, Dr::pos(l, i0), nw, uu);
-  } else {
+  Run8<T> u;      // ORDER 0
+  T ug[kWin];     // ORDER 1 (gathered)
+  Run8<T> x;
+  __device__ __forceinline__ void load(const ScanArgs& a, const Lane& l, const DirArgs& da, int i0) {
+    const T* ub = static_cast<const T*>(a.u) + static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(l.dd) * a.L;
+    const T* db = static_cast<const T*>(da.draw) + static_cast<int64_t>(l.b) * da.draw_bs + static_cast<int64_t>(l.dd) * a.L;
+    const int64_t p = Dr::pos(l, i0);
+    if (ORDER == 0) {
+      u.load(ub + (Dr::kPosSgn > 0 ? p : p - (kWin - 1)));
+    } else {
+      ColPix cp;
+      cp.init(static_cast<int>(p), a.H, a.W);
 #pragma unroll
-    for (int j = 0; j < kWin; ++j) uu[j] = (FULL || j < nw) ? ld_act(ub, elem<ORDER>(a, Dr::pos(l, i0 + j))) : 0.0f;
+      for (int j = 0; j < kWin; ++j) {
+        ug[j] = ub[cp.pix()];
+        cp.template step<Dr::kPosSgn>();
+      }
+    }
+    const int64_t si = Dr::sidx(a, l, i0);
+    x.load(db + (Dr::kSidxSgn > 0 ? si : si - (kWin - 1)));
   }
-  load_seq<Dr::kSidxSgn, FULL>(db, Dr::sidx(a, l, i0), nw, xr);
-}
+  __device__ __forceinline__ void unpack(float (&uu)[kWin], float (&xr)[kWin]) const {
+    if (ORDER == 0) {
+      u.template unpack<(Dr::kPosSgn < 0)>(uu);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kWin; ++j) uu[j] = ld_act(ug, j);
+    }
+    x.template unpack<(Dr::kSidxSgn < 0)>(xr);
+  }
+};
 
 __device__ __forceinline__ void load_a2(const DirArgs& da, int dd, float (&A2)[kN]) {
 #pragma unroll
@@ -331,23 +307,38 @@ __device__ __forceinline__ void load_bc(scalar_fp p, float (&bc)[kBC]) {
   for (int q = 0; q < kBC; ++q) bc[q] = p[q];
 }
 
+// Bring the B/C lines of steps [i, i + kWin) of one direction into L2 ahead of their scalar
+// loads.  The scalar cache misses on nearly every position, and a scalar load can only be
+// waited for together with all others in flight, so its latency is hidden only if it hits L2.
+// Lane k < kWin touches the line of step i + k through the vector path, whose loads complete in
+// order and are waited for with the window data anyway.  Positions are clamped into the row.
+template <int MODE, int DIR>
+__device__ __forceinline__ uint32_t touch_bc(const ScanArgs& a, const Lane& l, int i) {
+  using Dr = Dir<MODE, DIR>;
+  int64_t p = Dr::pos(l, i + (l.lane & (kWin - 1)));
+  p = p < 0 ? 0 : (p >= a.L ? a.L - 1 : p);
+  const uint32_t* row = reinterpret_cast<const uint32_t*>(a.bct) + ((static_cast<int64_t>(l.b) * 2 + DIR) * a.L) * kBC;
+  return row[p * kBC];
+}
+
 // One token for 16 states, h = exp2(Δ A') h + (Δu) B; returns Σ C h.  The B/C of the next
-// token (nxt) is requested right after the first use of this token's B/C (cur): scalar loads may
-// return out of order, so a wait for cur waits for every scalar load in flight, and issuing nxt
-// only after that wait leaves it a whole token of VALU work to arrive.
+// token (nxt) is requested once this token's B values are dead (after the h updates), so at most
+// 48 SGPRs hold B/C.  Scalar loads may return out of order, so the wait for this token's B/C
+// (at its first use) covers every scalar load in flight; issuing nxt after that point leaves it
+// the readout plus the next token's decays to arrive.
 __device__ __forceinline__ float scan_token(float dl, float du, const float (&A2)[kN], float (&h)[kN],
                                            const float (&cur)[kBC], float (&nxt)[kBC], scalar_fp nxt_p) {
   float an[kN];
 #pragma unroll
   for (int n = 0; n < kN; ++n) an[n] = __builtin_amdgcn_exp2f(dl * A2[n]);
 #pragma unroll
-  for (int n = 0; n < kN; ++n) h[n] = h[n] * an[n];
-  h[0] = __builtin_fmaf(du, cur[0], h[0]);
+  for (int n = 0; n < kN; ++n) {
+    h[n] = h[n] * an[n];
+    h[n] = __builtin_fmaf(du, cur[n], h[n]);
+  }
   __builtin_amdgcn_sched_barrier(0);
   load_bc(nxt_p, nxt);
   __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int n = 1; n < kN; ++n) h[n] = __builtin_fmaf(du, cur[n], h[n]);
   float y0 = 0.0f, y1 = 0.0f;
 #pragma unroll
   for (int n = 0; n < kN; n += 2) {
@@ -377,25 +368,6 @@ __device__ __forceinline__ void run_steps(const Lane& l, int i0, const float (&d
   }
 }
 
-// One step i of one direction outside the full windows (chunk tails): raw loads, Δ, the token
-// update and the B/C prefetch of step i + 1 into bcA.  Returns y + D·u; *u_out = u.
-template <typename T, int MODE, int ORDER, int DIR>
-__device__ __forceinline__ float single_step(const ScanArgs& a, const Lane& l, const DirArgs& da, float bias, float Dv,
-                                             int i, const float (&A2)[kN], float (&h)[kN], scalar_fp bct,
-                                             float (&bcA)[kBC], float* dl_out) {
-  using Dr = Dir<MODE, DIR>;
-  const T* ub = static_cast<const T*>(a.u) + static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(l.dd) * a.L;
-  const T* db = static_cast<const T*>(da.draw) + static_cast<int64_t>(l.b) * da.draw_bs + static_cast<int64_t>(l.dd) * a.L;
-  const float uu = ld_act(ub, elem<ORDER>(a, Dr::pos(l, i)));
-  const float dl = softplus_f(ld_act(db, Dr::sidx(a, l, i)) + bias);
-  float bcB[kBC];
-  const float y = scan_token(dl, dl * uu, A2, h, bcA, bcB, bct + Dr::pos(l, i + 1) * kBC);
-#pragma unroll
-  for (int q = 0; q < kBC; ++q) bcA[q] = bcB[q];
-  *dl_out = dl;
-  return y + Dv * uu;
-}
-
 // Δ and Δ·u of a window from its raw u and Δ_raw.
 __device__ __forceinline__ void prep_window(const float (&uu)[kWin], const float (&xr)[kWin], float bias,
                                             float (&dl)[kWin], float (&du)[kWin]) {
@@ -406,21 +378,34 @@ __device__ __forceinline__ void prep_window(const float (&uu)[kWin], const float
   }
 }
 
+// One step i outside the full windows (chunk tails): raw loads, Δ, the token update and the B/C
+// prefetch of step i + 1 into bcA.  Returns y + D·u and sets *dl_out = Δ.
+template <typename T, int MODE, int ORDER, int DIR>
+__device__ __forceinline__ float single_step(const ScanArgs& a, const Lane& l, const DirArgs& da, float bias, float Dv,
+                                             int i, const float (&A2)[kN], float (&h)[kN], scalar_fp bct,
+                                             float (&bcA)[kBC], float* dl_out) {
+  using Dr = Dir<MODE, DIR>;
+  const T* ub = static_cast<const T*>(a.u) + static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(l.dd) * a.L;
+  const T* db = static_cast<const T*>(da.draw) + static_cast<int64_t>(l.b) * da.draw_bs + static_cast<int64_t>(l.dd) * a.L;
+  const int64_t p = Dr::pos(l, i);
+  int64_t e = p;
+  if (ORDER == 1) {
+    ColPix cp;
+    cp.init(static_cast<int>(p), a.H, a.W);
+    e = cp.pix();
+  }
+  const float uu = ld_act(ub, e);
+  const float dl = softplus_f(ld_act(db, Dr::sidx(a, l, i)) + bias);
+  float bcB[kBC];
+  const float y = scan_token(dl, dl * uu, A2, h, bcA, bcB, bct + Dr::pos(l, i + 1) * kBC);
+#pragma unroll
+  for (int q = 0; q < kBC; ++q) bcA[q] = bcB[q];
+  *dl_out = dl;
+  return y + Dv * uu;
+}
+
 // ---------------------------------------------------------------------------------------------
 // Pass A: per chunk and direction, the end state of the chunk scanned from a zero state, and Σ Δ.
-
-template <typename T, int MODE, int ORDER, int DIR>
-__device__ __forceinline__ void state_window(const ScanArgs& a, const Lane& l, const DirArgs& da, float bias, int i0,
-                                             int i_full_end, const float (&A2)[kN], float (&h)[kN], float& S,
-                                             float (&uu)[kWin], float (&xr)[kWin], scalar_fp bct,
-                                             float (&bcA)[kBC], float (&bcB)[kBC]) {
-  float dl[kWin], du[kWin], y[kWin];
-  prep_window(uu, xr, bias, dl, du);
-  if (i0 + kWin < i_full_end) load_window<T, MODE, ORDER, DIR, true>(a, l, da, i0 + kWin, kWin, uu, xr);
-#pragma unroll
-  for (int j = 0; j < kWin; ++j) S += dl[j];
-  run_steps<MODE, DIR>(l, i0, dl, du, A2, h, bcA, bcB, bct, y);
-}
 
 template <typename T, int MODE, int ORDER, int DIR>
 __device__ __forceinline__ void chunk_state_dir(const ScanArgs& a, const Lane& l) {
@@ -433,17 +418,34 @@ __device__ __forceinline__ void chunk_state_dir(const ScanArgs& a, const Lane& l
   const float bias = da.bias[l.dd];
   scalar_fp bct = (scalar_fp)(a.bct) + ((static_cast<int64_t>(l.b) * 2 + DIR) * a.L) * kBC;
   float S = 0.0f;
-  float uu[kWin], xr[kWin], bcA[kBC], bcB[kBC];
+  float bcA[kBC], bcB[kBC];
+  Window<T, MODE, ORDER, DIR> win;
   const int full_end = (l.Kc / kWin) * kWin;
+  uint32_t sink = touch_bc<MODE, DIR>(a, l, 0), touch = 0;
   load_bc(bct + Dr::pos(l, 0) * kBC, bcA);
-  if (full_end > 0) load_window<T, MODE, ORDER, DIR, true>(a, l, da, 0, kWin, uu, xr);
-  for (int i0 = 0; i0 < full_end; i0 += kWin)
-    state_window<T, MODE, ORDER, DIR>(a, l, da, bias, i0, full_end, A2, h, S, uu, xr, bct, bcA, bcB);
+  if (full_end > 0) win.load(a, l, da, 0);
+  for (int i0 = 0; i0 < full_end; i0 += kWin) {
+    float uu[kWin], xr[kWin], dl[kWin], du[kWin], y[kWin];
+    win.unpack(uu, xr);
+    sink ^= touch;
+    // The prefetch must not be hoisted above the unpack: the window registers are loop-carried,
+    // and a load into other registers would need a copy (and so a wait) at the loop back edge.
+    // It is unconditional for the same reason (the last window reloads itself).
+    __builtin_amdgcn_sched_barrier(0);
+    win.load(a, l, da, i0 + kWin < full_end ? i0 + kWin : i0);
+    touch = touch_bc<MODE, DIR>(a, l, i0 + kWin);
+    prep_window(uu, xr, bias, dl, du);
+#pragma unroll
+    for (int j = 0; j < kWin; ++j) S += dl[j];
+    run_steps<MODE, DIR>(l, i0, dl, du, A2, h, bcA, bcB, bct, y);
+  }
   for (int i = full_end; i < l.Kc; ++i) {
     float dl;
     single_step<T, MODE, ORDER, DIR>(a, l, da, bias, 0.0f, i, A2, h, bct, bcA, &dl);
     S += dl;
   }
+  sink ^= touch;
+  if (sink == 0x7fc00001u && a.dim < 0) a.agg[0] = 0.0f;  // keeps the touch loads; never true
   if (l.valid) {
     float* ag = a.agg + ((((static_cast<int64_t>(l.b) * a.dim + l.d) * 2 + DIR) * a.nch) + l.c) * kAggStride;
 #pragma unroll
@@ -461,97 +463,47 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(ScanArgs a) {
 
 // ---------------------------------------------------------------------------------------------
 // Main pass: fused bidirectional scan of one chunk with meet-in-the-middle combination.
+// Phase 0 (steps [0, M)) stores each direction's y, including its D·u term, in the channel's LDS
+// row at the chunk positions; phase 1 (steps [M, Kc)) adds it to the other direction's stored
+// value.  After both phases every row holds y_f + y_b, and the epilogue writes the outputs.
 
-// Finished outputs of steps [i0, i0+nw) of one direction (second phase).
-template <typename T, int MODE, int ORDER, int DIR, bool FULL>
-__device__ __forceinline__ void finish_window(const ScanArgs& a, const Lane& l, int i0, int nw, const float (&yo)[kWin]) {
-  using Dr = Dir<MODE, DIR>;
-  const int64_t rowb = static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(l.d) * a.L;
-  T* ob = static_cast<T*>(a.out) + rowb;
-  const int64_t p0 = Dr::pos(l, i0);
-  if (MODE == kModeVim) {
-    // out = (y_f + y_b) / 2 * silu(z): the gate is applied once to the fused sum
-    float zz[kWin], o[kWin];
-    load_seq<Dr::kPosSgn, FULL>(static_cast<const T*>(a.z) + rowb, p0, nw, zz);
-#pragma unroll
-    for (int j = 0; j < kWin; ++j) o[j] = 0.5f * yo[j] * silu_f(zz[j]);
-    store_seq<Dr::kPosSgn, FULL>(ob, p0, nw, o);
-  } else if (MODE == kModeFirstPair) {
-    if (ORDER == 0) {
-      store_seq<Dr::kPosSgn, FULL>(a.wsy + rowb, p0, nw, yo);
-    } else {
-#pragma unroll
-      for (int j = 0; j < kWin; ++j)
-        if (FULL || j < nw) a.wsy[rowb + elem<ORDER>(a, p0 + Dr::kPosSgn * j)] = yo[j];
-    }
-  } else {
-    const T* zb = a.z ? static_cast<const T*>(a.z) + rowb : nullptr;
-#pragma unroll
-    for (int j = 0; j < kWin; ++j) {
-      if (FULL || j < nw) {
-        const int64_t e = elem<ORDER>(a, p0 + Dr::kPosSgn * j);
-        float w = yo[j] + a.wsy[rowb + e];
-        if (zb) w *= silu_f(ld_act(zb, e));
-        st_act(ob, e, w);
-      }
-    }
-  }
-}
-
-// Output of one finished position of one direction (second phase), element by element.
-template <typename T, int MODE, int ORDER, int DIR>
-__device__ __forceinline__ void finish_one(const ScanArgs& a, const Lane& l, int i, float yo) {
-  float v[kWin];
-  v[0] = yo;
-#pragma unroll
-  for (int j = 1; j < kWin; ++j) v[j] = 0.0f;
-  finish_window<T, MODE, ORDER, DIR, false>(a, l, i, 1, v);
-}
-
-// One full window of the main pass.  PHASE 0 stores y (with its D·u term) in the channel's LDS
-// row at the chunk positions; PHASE 1 adds the other direction's stored y and finishes the
-// outputs.
-template <typename T, int MODE, int ORDER, int DIR, int PHASE>
-__device__ __forceinline__ void pair_window(const ScanArgs& a, const Lane& l, const DirArgs& da, float bias, float Dv,
-                                            int i0, int i_full_end, const float (&A2)[kN], float (&h)[kN],
-                                            float (&uu)[kWin], float (&xr)[kWin], scalar_fp bct, float (&bcA)[kBC],
-                                            float (&bcB)[kBC], float* myY) {
-  float dl[kWin], du[kWin], dv[kWin], y[kWin];
-  prep_window(uu, xr, bias, dl, du);
-#pragma unroll
-  for (int j = 0; j < kWin; ++j) dv[j] = Dv * uu[j];
-  // Prefetch the next full window of this phase while this one is computed.
-  if (i0 + kWin < i_full_end) load_window<T, MODE, ORDER, DIR, true>(a, l, da, i0 + kWin, kWin, uu, xr);
-  run_steps<MODE, DIR>(l, i0, dl, du, A2, h, bcA, bcB, bct, y);
-  const int p0 = DIR == 0 ? i0 : l.Kc - 1 - i0;  // chunk position of step i0
-  if (PHASE == 0) {
-#pragma unroll
-    for (int j = 0; j < kWin; ++j) myY[p0 + (DIR == 0 ? j : -j)] = y[j] + dv[j];
-  } else {
-    float yo[kWin];
-#pragma unroll
-    for (int j = 0; j < kWin; ++j) yo[j] = myY[p0 + (DIR == 0 ? j : -j)] + y[j] + dv[j];
-    if (l.valid) finish_window<T, MODE, ORDER, DIR, true>(a, l, i0, kWin, yo);
-  }
-}
-
-// Steps [i_begin, i_end) of one phase: full windows, then the remaining steps one at a time.
 template <typename T, int MODE, int ORDER, int DIR, int PHASE>
 __device__ __forceinline__ void run_phase(const ScanArgs& a, const Lane& l, const DirArgs& da, float bias, float Dv,
                                           int i_begin, int i_end, const float (&A2)[kN], float (&h)[kN],
                                           scalar_fp bct, float (&bcA)[kBC], float (&bcB)[kBC], float* myY) {
-  float uu[kWin], xr[kWin];
+  Window<T, MODE, ORDER, DIR> win;
   const int full_end = i_begin + ((i_end - i_begin) / kWin) * kWin;
-  if (full_end > i_begin) load_window<T, MODE, ORDER, DIR, true>(a, l, da, i_begin, kWin, uu, xr);
-  for (int i0 = i_begin; i0 < full_end; i0 += kWin)
-    pair_window<T, MODE, ORDER, DIR, PHASE>(a, l, da, bias, Dv, i0, full_end, A2, h, uu, xr, bct, bcA, bcB, myY);
+  uint32_t sink = touch_bc<MODE, DIR>(a, l, i_begin), touch = 0;
+  if (full_end > i_begin) win.load(a, l, da, i_begin);
+  for (int i0 = i_begin; i0 < full_end; i0 += kWin) {
+    float uu[kWin], xr[kWin], dl[kWin], du[kWin], y[kWin];
+    win.unpack(uu, xr);
+    sink ^= touch;
+    __builtin_amdgcn_sched_barrier(0);  // see chunk_state_dir
+    win.load(a, l, da, i0 + kWin < full_end ? i0 + kWin : i0);
+    touch = touch_bc<MODE, DIR>(a, l, i0 + kWin);
+    prep_window(uu, xr, bias, dl, du);
+    const int p0 = DIR == 0 ? i0 : l.Kc - 1 - i0;  // chunk position of step i0
+    float prev[kWin];
+    if (PHASE == 1) {
+#pragma unroll
+      for (int j = 0; j < kWin; ++j) prev[j] = myY[p0 + (DIR == 0 ? j : -j)];
+    }
+    run_steps<MODE, DIR>(l, i0, dl, du, A2, h, bcA, bcB, bct, y);
+#pragma unroll
+    for (int j = 0; j < kWin; ++j) {
+      const float v = __builtin_fmaf(Dv, uu[j], y[j]);
+      myY[p0 + (DIR == 0 ? j : -j)] = PHASE == 1 ? prev[j] + v : v;
+    }
+  }
   for (int i = full_end; i < i_end; ++i) {
     float dl;
-    const float y = single_step<T, MODE, ORDER, DIR>(a, l, da, bias, Dv, i, A2, h, bct, bcA, &dl);
+    const float v = single_step<T, MODE, ORDER, DIR>(a, l, da, bias, Dv, i, A2, h, bct, bcA, &dl);
     const int pos = DIR == 0 ? i : l.Kc - 1 - i;
-    if (PHASE == 0) myY[pos] = y;
-    else if (l.valid) finish_one<T, MODE, ORDER, DIR>(a, l, i, myY[pos] + y);
+    myY[pos] = PHASE == 1 ? myY[pos] + v : v;
   }
+  sink ^= touch;
+  if (sink == 0x7fc00001u && a.dim < 0) a.agg[0] = 0.0f;  // keeps the touch loads; never true
 }
 
 template <typename T, int MODE, int ORDER, int DIR>
@@ -585,8 +537,8 @@ __device__ __forceinline__ void scan_pair_dir(const ScanArgs& a, const Lane& l, 
   float bcA[kBC], bcB[kBC];
   load_bc(bct + Dr::pos(l, 0) * kBC, bcA);
 
-  // Phase 0: steps [0, M).  For an odd chunk the backward direction reaches the middle token at
-  // its last phase-0 step, together with the forward direction; its value goes to spare slot Kc.
+  // For an odd chunk both directions reach the middle token at their last phase-0 step; the
+  // backward value of that step goes to the spare slot Kc.
   const int p0_end = (DIR == 1 && (Kc & 1)) ? M - 1 : M;
   run_phase<T, MODE, ORDER, DIR, 0>(a, l, da, bias, Dv, 0, p0_end, A2, h, bct, bcA, bcB, myY);
   if (p0_end < M) {
@@ -594,24 +546,141 @@ __device__ __forceinline__ void scan_pair_dir(const ScanArgs& a, const Lane& l, 
     myY[Kc] = single_step<T, MODE, ORDER, DIR>(a, l, da, bias, Dv, M - 1, A2, h, bct, bcA, &dl);
   }
   __syncthreads();
-  // Phase 1: steps [M, Kc).
   run_phase<T, MODE, ORDER, DIR, 1>(a, l, da, bias, Dv, M, Kc, A2, h, bct, bcA, bcB, myY);
+}
+
+// Combined value of chunk position q of LDS row c (adds the spare slot at the middle token).
+__device__ __forceinline__ float row_val(const float* ybuf, int ybs, int c, int q, int Kc, int M) {
+  float v = ybuf[c * ybs + q];
+  if ((Kc & 1) && q == M - 1) v += ybuf[c * ybs + Kc];
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const float (&v)[kWin]);
+template <>
+__device__ __forceinline__ void store8(uint16_t* p, const float (&v)[kWin]) {
+  uint32_t w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    w[k] = static_cast<uint32_t>(f32_to_bf16_rne(v[2 * k])) | (static_cast<uint32_t>(f32_to_bf16_rne(v[2 * k + 1])) << 16);
+  const uint4 r = make_uint4(w[0], w[1], w[2], w[3]);
+  __builtin_memcpy(p, &r, sizeof(r));
+}
+template <>
+__device__ __forceinline__ void store8(float* p, const float (&v)[kWin]) {
+  const float4 r0 = make_float4(v[0], v[1], v[2], v[3]), r1 = make_float4(v[4], v[5], v[6], v[7]);
+  __builtin_memcpy(p, &r0, sizeof(r0));
+  __builtin_memcpy(p + 4, &r1, sizeof(r1));
+}
+
+// Outputs of one chunk from the combined LDS rows.  Row-major order: the chunk's part of each
+// channel row is cut into groups of 8 positions; the 128 threads take groups in turn (consecutive
+// threads on consecutive groups of a row, so the 16-byte loads and stores are contiguous), and
+// each thread issues the gate loads of kEpiBatch groups before using any of them.  Column order
+// (second SS2D pair): position by position, pixel index advanced incrementally.
+constexpr int kEpiBatch = 4;
+
+template <typename T, int MODE, int ORDER>
+__device__ __forceinline__ void pair_epilogue(const ScanArgs& a, const Lane& l, const float* ybuf, int ybs) {
+  const int g_d0 = l.d - l.lane;  // first channel of the group
+  const int Kc = l.Kc, M = (Kc + 1) >> 1;
+  const int tid = threadIdx.x;
+  const int nch_here = a.dim - g_d0 < kW ? a.dim - g_d0 : kW;
+  const T* zb = static_cast<const T*>(a.z);
+  T* ob = static_cast<T*>(a.out);
+  const int64_t base = static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(g_d0) * a.L + l.s_lo;
+  if (ORDER == 0) {
+    const int ngr = Kc / kWin;            // full groups per row
+    const int items = nch_here * ngr;
+    for (int it0 = tid; it0 < items; it0 += kThreads * kEpiBatch) {
+      Run8<T> zr[kEpiBatch];
+      int cc[kEpiBatch], qq[kEpiBatch];
+#pragma unroll
+      for (int k = 0; k < kEpiBatch; ++k) {
+        const int it = it0 + k * kThreads;
+        const int itc = it < items ? it : items - 1;  // clamped: loads stay in range
+        cc[k] = itc / ngr;
+        qq[k] = (itc - cc[k] * ngr) * kWin;
+        if (MODE == kModeVim || (MODE == kModeSecondPair && zb)) zr[k].load(zb + base + static_cast<int64_t>(cc[k]) * a.L + qq[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < kEpiBatch; ++k) {
+        if (it0 + k * kThreads >= items) break;
+        const int64_t gi = base + static_cast<int64_t>(cc[k]) * a.L + qq[k];
+        float v[kWin], zz[kWin];
+#pragma unroll
+        for (int j = 0; j < kWin; ++j) v[j] = row_val(ybuf, ybs, cc[k], qq[k] + j, Kc, M);
+        if (MODE == kModeVim) {
+          zr[k].template unpack<false>(zz);
+#pragma unroll
+          for (int j = 0; j < kWin; ++j) v[j] = 0.5f * v[j] * silu_f(zz[j]);  // (y_f + y_b) / 2 * silu(z)
+          store8(ob + gi, v);
+        } else if (MODE == kModeFirstPair) {
+          store8(a.wsy + gi, v);
+        } else {
+          float w[kWin];
+          Run8<float> wr;
+          wr.load(a.wsy + gi);
+          wr.template unpack<false>(w);
+          if (zb) zr[k].template unpack<false>(zz);
+#pragma unroll
+          for (int j = 0; j < kWin; ++j) v[j] = zb ? (v[j] + w[j]) * silu_f(zz[j]) : v[j] + w[j];
+          store8(ob + gi, v);
+        }
+      }
+    }
+    // positions past the last full group of each row
+    const int rem = Kc - ngr * kWin;
+    for (int it = tid; it < nch_here * rem; it += kThreads) {
+      const int c = it / rem, q = ngr * kWin + (it - (it / rem) * rem);
+      const int64_t gi = base + static_cast<int64_t>(c) * a.L + q;
+      const float v = row_val(ybuf, ybs, c, q, Kc, M);
+      if (MODE == kModeVim) {
+        st_act(ob, gi, 0.5f * v * silu_f(ld_act(zb, gi)));
+      } else if (MODE == kModeFirstPair) {
+        a.wsy[gi] = v;
+      } else {
+        float w = v + a.wsy[gi];
+        if (zb) w *= silu_f(ld_act(zb, gi));
+        st_act(ob, gi, w);
+      }
+    }
+  } else {
+    // pixel of position s_lo + tid, advanced by kThreads positions per iteration
+    ColPix cp;
+    cp.init(static_cast<int>(l.s_lo) + tid, a.H, a.W);
+    const int dw = kThreads / a.H, dh = kThreads - dw * a.H;
+    const int64_t rbase = static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(g_d0) * a.L;
+    for (int q = tid; q < Kc; q += kThreads) {
+      const int64_t e = cp.pix();
+      for (int c = 0; c < nch_here; ++c) {
+        const int64_t gi = rbase + static_cast<int64_t>(c) * a.L + e;
+        const float v = row_val(ybuf, ybs, c, q, Kc, M);
+        if (MODE == kModeFirstPair) {
+          a.wsy[gi] = v;
+        } else {
+          float w = v + a.wsy[gi];
+          if (zb) w *= silu_f(ld_act(zb, gi));
+          st_act(ob, gi, w);
+        }
+      }
+      cp.h += dh;
+      cp.w += dw;
+      if (cp.h >= cp.H) { cp.h -= cp.H; ++cp.w; }
+    }
+  }
 }
 
 template <typename T, int MODE, int ORDER>
 __global__ __launch_bounds__(kThreads) void scan_pair_kernel(ScanArgs a) {
-  extern __shared__ float ybuf[];  // [kW][ybs]: y of the first direction to reach a position
+  extern __shared__ float ybuf[];  // [kW][ybs]: combined y of the chunk
   const int ybs = (a.K + 1) | 1;   // odd row stride spreads the 64 lanes over the banks
   const Lane l = lane_ctx(a);
   if (threadIdx.x < kW) scan_pair_dir<T, MODE, ORDER, 0>(a, l, ybuf, ybs);
   else scan_pair_dir<T, MODE, ORDER, 1>(a, l, ybuf, ybs);
   __syncthreads();
-  // The middle position of an odd chunk: both directions stored their value in the first phase.
-  if ((l.Kc & 1) && threadIdx.x < kW && l.valid) {
-    const float* myY = ybuf + l.lane * ybs;
-    const int M = (l.Kc + 1) >> 1;
-    finish_one<T, MODE, ORDER, 0>(a, l, M - 1, myY[M - 1] + myY[l.Kc]);
-  }
+  pair_epilogue<T, MODE, ORDER>(a, l, ybuf, ybs);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -759,7 +828,6 @@ vmscan_status vmscan_fwd_bidir_ex(const void* u, const void* delta_raw, const vo
   a.K = static_cast<int>(K);
   a.nch = static_cast<int>(ceil_div(seqlen, K));
   a.ngroups = static_cast<int>(ceil_div(dim, kW));
-  a.order = 0;
   a.H = 1;
   a.W = static_cast<int>(seqlen);
   return run_pair_dtype<kModeVim, 0>(a, dtype, stream);
@@ -844,14 +912,12 @@ vmscan_status ss2d_cross_scan_fwd_ex(const void* x, const void* delta_raw, const
   // Pair 1: row-major order (direction 0) and its reverse (direction 2) -> fp32 image.
   a.d0 = dir_args(0, 0);
   a.d1 = dir_args(2, 1);
-  a.order = 0;
   vmscan_status st = run_pair_dtype<kModeFirstPair, 0>(a, dtype, stream);
   if (st != VMSCAN_OK) return st;
   // Pair 2: column-major order (direction 1) and its reverse (direction 3) -> + image -> out.
   // Its transpose and chunk-state kernels reuse the B/C and carry regions after pair 1 (same stream).
   a.d0 = dir_args(1, 0);
   a.d1 = dir_args(3, 1);
-  a.order = 1;
   return run_pair_dtype<kModeSecondPair, 1>(a, dtype, stream);
 }
 
