@@ -21,6 +21,13 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# ALU roofline of the recurrence.  One state update (token, channel, direction, state) needs one
+# exp2 and four fp32 VALU ops (Δ·A', h·a, h + Δu·B, y + C·h).  MI355X: 256 CUs at 2.4 GHz; fp32
+# vector peak 157.3 TFLOP/s = 128 FMA lanes per CU per clock; transcendentals issue at a quarter of
+# that, 32 lanes per CU per clock.  So one update costs at least 4/128 + 1/32 = 1/16 CU-clock and
+# the peak is 256 * 2.4e9 * 16 = 9.83e12 updates/s.
+CUS, CLOCK_HZ = 256, 2.4e9
+ALU_PEAK_UPD_S = CUS * CLOCK_HZ / (4.0 / 128 + 1.0 / 32)
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SRC = os.path.join(ROOT, "selective_state_space_41_amd", "csrc", "vmscan.hip")
 
@@ -46,6 +53,13 @@ def algorithmic_bytes(cfg):
     return act + dr + bc + par, nb * nd * L
 
 
+def state_updates(cfg):
+    """Recurrence state updates per call: tokens * channels * directions * d_state."""
+    dirs = 2 if cfg["kind"] == "vim" else 4
+    seq = cfg["seqlen"] if cfg["kind"] == "vim" else cfg["H"] * cfg["W"]
+    return cfg["batch"] * cfg["dim"] * seq * dirs * cfg["d_state"]
+
+
 def source_digest():
     with open(KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -64,34 +78,119 @@ def traffic_record(workload):
     return rec.get("traffic_bytes_per_launch")
 
 
+def _db_rows(path, sql):
+    import glob
+    import sqlite3
+    rows = []
+    for f in sorted(glob.glob(os.path.join(path, "**", "*.db"), recursive=True)):
+        con = sqlite3.connect(f)
+        rows += con.execute(sql).fetchall()
+        con.close()
+    if not rows:
+        raise SystemExit(f"no rocprofv3 results under {path}")
+    return rows
+
+
+def _counter_kib(path, counter, like):
+    """Mean of a counter per dispatch (KiB for FETCH_SIZE/WRITE_SIZE) over the dispatches of the
+    kernels whose name contains ``like``, from a rocprofv3 --pmc result database."""
+    rows = _db_rows(path, "select kernel_name, counter_name, value from counters_collection")
+    vals = [v for k, c, v in rows if c == counter and like in k]
+    if not vals:
+        raise SystemExit(f"{counter}: no dispatch of a kernel matching {like!r} under {path}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def summarize_kernels(path, command, out_txt):
+    """Per-kernel duration table (rocprofv3 --kernel-trace result database) written as text."""
+    rows = _db_rows(path, "select name, count(*), avg(duration), min(duration), max(duration), sum(duration) "
+                          "from kernels group by name")
+    rows.sort(key=lambda r: -r[5])
+    lines = [f"command: {command}", "", f"{'calls':>6} {'avg us':>10} {'min us':>10} {'max us':>10}  kernel"]
+    for name, n, avg, mn, mx, _ in rows:
+        lines.append(f"{n:6d} {avg / 1e3:10.2f} {mn / 1e3:10.2f} {mx / 1e3:10.2f}  {name[:140]}")
+    with open(out_txt, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_counters(out_txt, like, runs):
+    """Mean per dispatch of every counter in rocprofv3 --pmc runs, for the kernel matching
+    ``like``; ``runs`` is a list of (result_dir, command)."""
+    lines = [f"kernel: dispatches whose name contains {like!r}; values are means per dispatch", ""]
+    for path, command in runs:
+        rows = _db_rows(path, "select kernel_name, counter_name, value from counters_collection")
+        acc = {}
+        for k, c, v in rows:
+            if like in k:
+                acc.setdefault(c, []).append(v)
+        lines.append(f"command: {command}")
+        for c in sorted(acc):
+            lines.append(f"  {c:28s} {sum(acc[c]) / len(acc[c]):16.6g}   (n={len(acc[c])})")
+        lines.append("")
+    with open(out_txt, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def summarize_traffic(workload, like, dirs, commands):
+    """HBM bytes per launch of the kernel matching ``like``: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for a plain 1 GiB device copy."""
+    f_kib, nf = _counter_kib(dirs["fetch"], "FETCH_SIZE", like)
+    w_kib, nw = _counter_kib(dirs["write"], "WRITE_SIZE", like)
+    cf_kib, _ = _counter_kib(dirs["copy_fetch"], "FETCH_SIZE", "copy")
+    cw_kib, _ = _counter_kib(dirs["copy_write"], "WRITE_SIZE", "copy")
+    gib = float(1 << 30)
+    rs, ws = gib / (cf_kib * 1024), gib / (cw_kib * 1024)
+    rd, wr = f_kib * 1024 * rs, w_kib * 1024 * ws
+    rec = {"workload": workload, "kernel_match": like, "source_sha256_16": source_digest(),
+           "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib, "dispatches": [nf, nw],
+           "copy_fetch_kib_per_GiB": cf_kib, "copy_write_kib_per_GiB": cw_kib,
+           "read_scale": rs, "write_scale": ws, "read_bytes": rd, "write_bytes": wr,
+           "traffic_bytes_per_launch": int(round(rd + wr)), "commands": commands}
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, f"traffic_{workload}.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec, indent=1))
+
+
 def _cpu_worker(args):
-    cfg_id, bsel = args
-    import numpy as np  # noqa: F401
+    cfg_id, bsel, min_s = args
     import oracle as O
     import synth
     p = synth.make_vim_inputs(cfg_id)
     sl = slice(bsel[0], bsel[1])
-    t0 = time.perf_counter()
-    O.vim_bidir(p["u"][sl], p["delta_raw"][sl], p["z"][sl], p["A_log"], p["A_b_log"], p["B"][sl], p["C"][sl],
-                p["B_b"][sl], p["C_b"][sl], p["D"], p["D_b"], p["delta_bias"])
-    return time.perf_counter() - t0
+    reps, t0 = 0, time.perf_counter()
+    while True:   # repeat the slice until this worker has computed for at least min_s seconds
+        O.vim_bidir(p["u"][sl], p["delta_raw"][sl], p["z"][sl], p["A_log"], p["A_b_log"], p["B"][sl], p["C"][sl],
+                    p["B_b"][sl], p["C_b"][sl], p["D"], p["D_b"], p["delta_bias"])
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_s:
+            return reps, dt
 
 
-def cpu_baseline(cfg_id, cfg):
-    """The fp64 oracle on the same workload (all batches of the Vim-Ti scan), batch slices spread
-    over a process pool.  Throughput = tokens·channels / slowest worker's compute time."""
+def cpu_baseline(cfg_id, cfg, min_s=1.0):
+    """The fp64 oracle on the same workload: the batches of the Vim-Ti scan are split into
+    slices over a process pool (one process per host core, at most 16) and each process repeats
+    its slice for at least ``min_s`` seconds.  Throughput = tokens·channels computed / slowest
+    worker's compute time (input generation excluded)."""
     import multiprocessing as mp
     workers = max(1, min(16, os.cpu_count() or 1))
     nb = cfg["batch"]
     per = math.ceil(nb / workers)
-    slices = [(cfg_id, (i, min(nb, i + per))) for i in range(0, nb, per)]
+    slices = [(cfg_id, (i, min(nb, i + per)), min_s) for i in range(0, nb, per)]
     ctx = mp.get_context("spawn")
     with ctx.Pool(len(slices)) as pool:
-        times = pool.map(_cpu_worker, slices)
-    toks = nb * cfg["dim"] * cfg["seqlen"]
-    return {"value": toks / max(times), "unit": "tokens·channels/s", "cores": len(slices), "kind": "oracle",
-            "sample": f"{cfg['name']}: all {nb} batches (fp64 numpy oracle), {len(slices)} processes, "
-                      f"{sum(times):.1f} CPU-s, slowest worker {max(times):.2f} s"}
+        res = pool.map(_cpu_worker, slices)
+    tpb = cfg["dim"] * cfg["seqlen"]
+    work = sum(r * (b[1][1] - b[1][0]) * tpb for (r, _), b in zip(res, slices))
+    wall = max(t for _, t in res)
+    return {"value": work / wall, "unit": "tokens·channels/s", "cores": len(slices), "kind": "oracle",
+            "sample": f"{cfg['name']}: batch slices of {per} (all {nb} batches), each repeated for >= {min_s:.0f} s "
+                      f"in its own process (fp64 numpy oracle); {sum(t for _, t in res):.1f} CPU-s in total, "
+                      f"slowest worker {wall:.2f} s"}
 
 
 def make_sets(cfg_id, cfg, nsets, torch):
@@ -158,11 +257,12 @@ def bench_config(cfg_id, steps, warmup, with_cpu, torch, V):
         wsb = V.lib.ss2d_cross_scan_workspace_bytes(cfg["batch"], cfg["dim"], cfg["H"], cfg["W"], 16, 1 if cfg["dtype"] == "bf16" else 0)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
 
-    def call(i):
+    def call(i, stage=3):
         act, par = sets[i % len(sets)]
         if cfg["kind"] == "vim":
             V.vmscan_fwd_bidir(act["u"], act["delta_raw"], act["z"], par["A_log"], par["A_b_log"], act["B"], act["C"],
-                               act["B_b"], act["C_b"], par["D"], par["D_b"], par["delta_bias"], out=act["out"], workspace=ws)
+                               act["B_b"], act["C_b"], par["D"], par["D_b"], par["delta_bias"], out=act["out"], workspace=ws,
+                               stage=stage)
         else:
             V.ss2d_cross_scan_fwd(act["x"], act["delta_raw"], par["A_log"], act["B"], act["C"], par["D"],
                                   par["delta_bias"], out=act["out"], workspace=ws)
@@ -171,29 +271,43 @@ def bench_config(cfg_id, steps, warmup, with_cpu, torch, V):
         call(i)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)   # the binding launches on this stream
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    # per-launch events for the spread (the first/last pair brackets the whole timed region)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    split = cfg["kind"] == "vim"              # Vim: time the scan stage (dominant kernel) on its own
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    e_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    e0.record(stream)
-    ev[0].record(stream)
     for i in range(steps):
-        call(warmup + i)
-        ev[i + 1].record(stream)
-    e1.record(stream)
+        ev[i][0].record(stream)
+        if split:
+            call(warmup + i, stage=1)
+            ev[i][1].record(stream)
+            call(warmup + i, stage=2)
+        else:
+            call(warmup + i)
+            ev[i][1].record(stream)
+    e_end.record(stream)
     torch.cuda.synchronize()
-    total_ms = e0.elapsed_time(e1)
-    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    total_ms = ev[0][0].elapsed_time(e_end)
+    step_ms = sorted(ev[i][0].elapsed_time(ev[i + 1][0] if i + 1 < steps else e_end) for i in range(steps))
+    if split:
+        scan_ms = [ev[i][1].elapsed_time(ev[i + 1][0] if i + 1 < steps else e_end) for i in range(steps)]
+    else:
+        scan_ms = [ev[i][0].elapsed_time(ev[i + 1][0] if i + 1 < steps else e_end) for i in range(steps)]
+    kern_ms = sum(scan_ms) / steps
     ms = total_ms / steps
     value = toks / (ms * 1e-3)
     gbs = nbytes / (ms * 1e-3) / 1e9
+    upd = state_updates(cfg)
+    alu = upd / (kern_ms * 1e-3)
     dtype = "f32"  # arithmetic and state are fp32; activations are stored as cfg["dtype"]
     is_default = cfg_id == 1
-    roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_record(cfg["name"]),
-            "algorithmic_bytes_per_launch": nbytes,
-            "kernel": "scan_pair_kernel<bf16>" if cfg["kind"] == "vim" else "scan_pair_kernel<bf16> x2 pairs (+chunk_state_kernel)"}
+    roof = {"bound": "alu", "achieved": round(alu / 1e9, 1), "peak": round(ALU_PEAK_UPD_S / 1e9, 1), "unit": "Gupd/s",
+            "frac": round(alu / ALU_PEAK_UPD_S, 4), "traffic": traffic_record(cfg["name"]),
+            "kernel": ("scan_pair_kernel<bf16, vim> (scan stage of vmscan_fwd_bidir)" if split else
+                       "all kernels of the call (transpose, chunk states, both SS2D pairs)"),
+            "kernel_avg_us": round(kern_ms * 1000, 2),
+            "updates_per_launch": upd,
+            "hbm": {"achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                    "algorithmic_bytes_per_step": nbytes}}
     rec = {
         "metric": METRIC,
         "value": value,
@@ -210,7 +324,8 @@ def bench_config(cfg_id, steps, warmup, with_cpu, torch, V):
         "config": {"workload": cfg["name"], "batch": cfg["batch"], "dim": cfg["dim"],
                    "seqlen": cfg.get("seqlen", cfg.get("H", 0) * cfg.get("W", 0)), "d_state": cfg["d_state"],
                    "io_dtype": cfg["dtype"], "rotation_sets": len(sets),
-                   "step_ms_p10_p50_p90": [per[len(per) // 10], per[len(per) // 2], per[(9 * len(per)) // 10]]},
+                   "step_ms_p10_p50_p90": [step_ms[len(step_ms) // 10], step_ms[len(step_ms) // 2],
+                                           step_ms[(9 * len(step_ms)) // 10]]},
         "roofline": roof,
     }
     if cfg["kind"] == "ss2d":
@@ -229,7 +344,28 @@ def main():
     ap.add_argument("--config", type=int, default=1)
     ap.add_argument("--all", action="store_true", help="one line per workload (configs 0-4)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain 1 GiB device-to-device copy (counter calibration for FETCH_SIZE/WRITE_SIZE)")
+    ap.add_argument("--summarize-kernels", nargs=3, metavar=("RESULT_DIR", "COMMAND", "OUT_TXT"),
+                    help="write the per-kernel table of a rocprofv3 --kernel-trace run (no GPU needed)")
+    ap.add_argument("--summarize-traffic", nargs=7,
+                    metavar=("WORKLOAD", "KERNEL_MATCH", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR",
+                             "COMMANDS_JSON"),
+                    help="write profiles/traffic_<workload>.json from four rocprofv3 --pmc runs (no GPU needed)")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="ARG",
+                    help="OUT_TXT KERNEL_MATCH then pairs RESULT_DIR COMMAND of rocprofv3 --pmc runs (no GPU needed)")
     args = ap.parse_args()
+    if args.summarize_counters:
+        a = args.summarize_counters
+        summarize_counters(a[0], a[1], list(zip(a[2::2], a[3::2])))
+        return
+    if args.summarize_kernels:
+        summarize_kernels(*args.summarize_kernels)
+        return
+    if args.summarize_traffic:
+        w, like, fd, wd, cfd, cwd, cmds = args.summarize_traffic
+        summarize_traffic(w, like, {"fetch": fd, "write": wd, "copy_fetch": cfd, "copy_write": cwd}, json.loads(cmds))
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the path shards over "
               "batch/channels with no communication, see the design notes.", file=sys.stderr)
@@ -238,6 +374,18 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        # A plain copy of a known size: its FETCH_SIZE/WRITE_SIZE per dispatch give the scale that
+        # turns the same counters of the scan kernels into bytes.
+        n = (1 << 30) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy", "bytes_read_per_dispatch": n * 4, "bytes_written_per_dispatch": n * 4,
+                          "dispatches": max(1, args.steps)}), flush=True)
+        return
     import selective_state_space_41_amd as V
     cfgs = [0, 1, 2, 3, 4] if args.all else [args.config]
     for c in cfgs:

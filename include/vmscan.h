@@ -94,7 +94,9 @@ size_t vmscan_fwd_bidir_workspace_bytes_ex(int64_t batch, int64_t dim, int64_t s
  *   delta_bias      : [dim]                    float32 (shared by both directions)
  *   out             : [batch, dim, seqlen]     activation dtype
  * Long sequences are split into chunks whose boundary states are carried across workgroups
- * (chunk_len 0 = library choice; otherwise the given length, clamped to [1, seqlen]).
+ * (chunk_len 0 = library choice; otherwise the given length, clamped to [1, min(seqlen, 206)]).
+ * The workspace (size from vmscan_fwd_bidir_workspace_bytes[_ex]) holds a float32 copy of
+ * B/C/B_b/C_b and, for split sequences, the chunk end states.
  */
 vmscan_status vmscan_fwd_bidir(const void *u, const void *delta_raw, const void *z,
                                const float *A_log, const float *A_b_log,
@@ -110,6 +112,24 @@ vmscan_status vmscan_fwd_bidir_ex(const void *u, const void *delta_raw, const vo
                                   void *out, int64_t batch, int64_t dim, int64_t seqlen, int d_state,
                                   vmscan_dtype dtype, void *workspace, size_t workspace_bytes,
                                   int64_t chunk_len, hipStream_t stream);
+
+/*
+ * The two stages of vmscan_fwd_bidir_ex, for callers that time or overlap them separately:
+ *   stage 1: write the float32 copy of B/C/B_b/C_b (position-major) into the workspace;
+ *   stage 2: run the scan from that copy (chunk states if the sequence is split, then the fused
+ *            bidirectional scan); requires a completed stage 1 with the same B/C pointers, shapes
+ *            and workspace, else the output is unspecified;
+ *   stage 3: both (= vmscan_fwd_bidir_ex).
+ * Other stage values return VMSCAN_ERR_UNSUPPORTED.  Arguments as for vmscan_fwd_bidir_ex.
+ */
+vmscan_status vmscan_fwd_bidir_stage(const void *u, const void *delta_raw, const void *z,
+                                     const float *A_log, const float *A_b_log,
+                                     const void *B, const void *C, const void *B_b, const void *C_b,
+                                     const float *D, const float *D_b, const float *delta_bias,
+                                     void *out, int64_t batch, int64_t dim, int64_t seqlen,
+                                     int d_state, vmscan_dtype dtype, void *workspace,
+                                     size_t workspace_bytes, int64_t chunk_len, int stage,
+                                     hipStream_t stream);
 
 /* Workspace bytes for ss2d_cross_scan_fwd / _ex (chunk_len 0 = library choice); 0 if invalid. */
 size_t ss2d_cross_scan_workspace_bytes(int64_t batch, int64_t dim, int64_t H, int64_t W, int d_state,

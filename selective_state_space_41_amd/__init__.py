@@ -3,8 +3,8 @@
 Thin ctypes binding over ``libvmscan.so`` (C ABI in ``include/vmscan.h``).  The functions below
 only check and marshal arguments (torch tensors -> device pointers, the current HIP stream, a
 workspace from torch's allocator); every step of the scan runs in the library's HIP kernels.
-There is no fallback: if the library is missing or cannot be loaded, importing the binding
-raises.
+There is no fallback: the library is loaded on first use (``load()``), and if it is missing or
+cannot be loaded that raises.
 """
 import ctypes
 import os
@@ -42,6 +42,8 @@ def _load():
     lib.vmscan_fwd_bidir.argtypes = fwd_args + [_c_void_p]
     lib.vmscan_fwd_bidir_ex.restype = ctypes.c_int
     lib.vmscan_fwd_bidir_ex.argtypes = fwd_args + [_i64, _c_void_p]
+    lib.vmscan_fwd_bidir_stage.restype = ctypes.c_int
+    lib.vmscan_fwd_bidir_stage.argtypes = fwd_args + [_i64, ctypes.c_int, _c_void_p]
     lib.ss2d_cross_scan_workspace_bytes.restype = ctypes.c_size_t
     lib.ss2d_cross_scan_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int]
     lib.ss2d_cross_scan_workspace_bytes_ex.restype = ctypes.c_size_t
@@ -54,18 +56,32 @@ def _load():
     return lib
 
 
-lib = _load()
+_LIB = None
+
+
+def load():
+    """Load libvmscan.so (once) and return the ctypes handle; raises if it is not built."""
+    global _LIB
+    if _LIB is None:
+        _LIB = _load()
+    return _LIB
+
+
+def __getattr__(name):
+    if name == "lib":
+        return load()
+    raise AttributeError(name)
 
 
 def status_string(code):
-    return lib.vmscan_status_string(int(code)).decode()
+    return load().vmscan_status_string(int(code)).decode()
 
 
 def _check(code):
     if code != 0:
         msg = status_string(code)
         if code == 6:
-            msg += f" (hipError_t {lib.vmscan_last_hip_error()})"
+            msg += f" (hipError_t {load().vmscan_last_hip_error()})"
         raise RuntimeError(msg)
 
 
@@ -99,13 +115,27 @@ def _stream(stream, device):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _workspace(ws, nbytes, dev):
+    """The caller's workspace if it is a large enough uint8 device tensor, else a new one when
+    none was given.  A workspace that is given but too small is an error, not silently replaced:
+    the stages of one call must see the same buffer."""
+    if ws is None:
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    if ws.dtype != torch.uint8 or ws.device != dev or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
+    if ws.numel() < nbytes:
+        raise ValueError(f"workspace holds {ws.numel()} bytes, {nbytes} needed")
+    return ws
+
+
 def vmscan_fwd_bidir(u, delta_raw, z, A_log, A_b_log, B, C, B_b, C_b, D, D_b, delta_bias,
-                     out=None, chunk_len=0, workspace=None, stream=None):
+                     out=None, chunk_len=0, workspace=None, stream=None, stage=3):
     """Bidirectional selective scan with the silu(z) gate; returns ``out`` [batch, dim, L].
 
     u, delta_raw, z: [batch, dim, L]; A_log, A_b_log: [dim, 16] float32; B, C, B_b, C_b:
     [batch, 16, L] (original token order); D, D_b, delta_bias: [dim] float32.  Activations are
-    float32 or bfloat16 (all the same).  ``chunk_len`` 0 lets the library choose."""
+    float32 or bfloat16 (all the same).  ``chunk_len`` 0 lets the library choose.  ``stage``
+    1 / 2 runs only the B/C preparation / the scan (vmscan_fwd_bidir_stage); 3 runs both."""
     if u.dim() != 3:
         raise ValueError("u must be [batch, dim, L]")
     nb, nd, L = u.shape
@@ -124,13 +154,13 @@ def vmscan_fwd_bidir(u, delta_raw, z, A_log, A_b_log, B, C, B_b, C_b, D, D_b, de
         out = torch.empty_like(u)
     else:
         _need(out, "out", (nb, nd, L), adt, dev)
+    lib = load()
     wsb = lib.vmscan_fwd_bidir_workspace_bytes_ex(nb, nd, L, D_STATE, dt, int(chunk_len))
-    if workspace is None or workspace.numel() < wsb:
-        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
-    _check(lib.vmscan_fwd_bidir_ex(
+    workspace = _workspace(workspace, wsb, dev)
+    _check(lib.vmscan_fwd_bidir_stage(
         _ptr(u), _ptr(delta_raw), _ptr(z), _ptr(A_log), _ptr(A_b_log), _ptr(B), _ptr(C), _ptr(B_b), _ptr(C_b),
         _ptr(D), _ptr(D_b), _ptr(delta_bias), _ptr(out), nb, nd, L, D_STATE, dt,
-        _ptr(workspace), workspace.numel(), int(chunk_len), _stream(stream, dev)))
+        _ptr(workspace), workspace.numel(), int(chunk_len), int(stage), _stream(stream, dev)))
     return out
 
 
@@ -161,9 +191,9 @@ def ss2d_cross_scan_fwd(x, delta_raw, A_log, B, C, D, delta_bias, z=None, out=No
         out = torch.empty_like(x)
     else:
         _need(out, "out", (nb, nd, H, W), adt, dev)
+    lib = load()
     wsb = lib.ss2d_cross_scan_workspace_bytes_ex(nb, nd, H, W, D_STATE, dt, int(chunk_len))
-    if workspace is None or workspace.numel() < wsb:
-        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, wsb, dev)
     _check(lib.ss2d_cross_scan_fwd_ex(
         _ptr(x), _ptr(delta_raw), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(delta_bias), _ptr(z), _ptr(out),
         nb, nd, H, W, D_STATE, dt, _ptr(workspace), workspace.numel(), int(chunk_len), _stream(stream, dev)))
@@ -171,4 +201,4 @@ def ss2d_cross_scan_fwd(x, delta_raw, A_log, B, C, D, delta_bias, z=None, out=No
 
 
 def fwd_bidir_chunk_len(batch, dim, seqlen):
-    return int(lib.vmscan_fwd_bidir_chunk_len(batch, dim, seqlen, D_STATE))
+    return int(load().vmscan_fwd_bidir_chunk_len(batch, dim, seqlen, D_STATE))

@@ -726,14 +726,22 @@ vmscan_status launch_failed(hipError_t e) {
   return VMSCAN_ERR_HIP;
 }
 
+enum { kStagePrepare = 1, kStageScan = 2, kStageAll = 3 };
+
+// Stage kStagePrepare writes the fp32 B/C copy; stage kStageScan runs the chunk-state and the
+// main kernels from it.
 template <typename T, int MODE, int ORDER>
-vmscan_status run_pair(const ScanArgs& a, hipStream_t stream) {
+vmscan_status run_pair(const ScanArgs& a, hipStream_t stream, int stages) {
   const int64_t nblocks = static_cast<int64_t>(a.batch) * a.nch * a.ngroups;
   const int64_t tblocks = static_cast<int64_t>(a.batch) * 2 * ceil_div(a.L, kTransThreads);
   if (nblocks >= (int64_t{1} << 31) || tblocks >= (int64_t{1} << 31)) return VMSCAN_ERR_SHAPE;
-  hipLaunchKernelGGL(bc_transpose_kernel<T>, dim3(static_cast<unsigned>(tblocks)), dim3(kTransThreads), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return launch_failed(e);
+  hipError_t e;
+  if (stages & kStagePrepare) {
+    hipLaunchKernelGGL(bc_transpose_kernel<T>, dim3(static_cast<unsigned>(tblocks)), dim3(kTransThreads), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return launch_failed(e);
+  }
+  if (!(stages & kStageScan)) return VMSCAN_OK;
   if (a.nch > 1) {
     hipLaunchKernelGGL((chunk_state_kernel<T, MODE, ORDER>), dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0,
                        stream, a);
@@ -749,8 +757,52 @@ vmscan_status run_pair(const ScanArgs& a, hipStream_t stream) {
 }
 
 template <int MODE, int ORDER>
-vmscan_status run_pair_dtype(const ScanArgs& a, vmscan_dtype dtype, hipStream_t stream) {
-  return dtype == VMSCAN_F32 ? run_pair<float, MODE, ORDER>(a, stream) : run_pair<uint16_t, MODE, ORDER>(a, stream);
+vmscan_status run_pair_dtype(const ScanArgs& a, vmscan_dtype dtype, hipStream_t stream, int stages = kStageAll) {
+  return dtype == VMSCAN_F32 ? run_pair<float, MODE, ORDER>(a, stream, stages)
+                             : run_pair<uint16_t, MODE, ORDER>(a, stream, stages);
+}
+
+// Validation and kernel arguments of the bidirectional scan (shared by its entry points).
+vmscan_status vim_args(ScanArgs& a, const void* u, const void* delta_raw, const void* z, const float* A_log,
+                       const float* A_b_log, const void* B, const void* C, const void* B_b, const void* C_b,
+                       const float* D, const float* D_b, const float* delta_bias, void* out, int64_t batch,
+                       int64_t dim, int64_t seqlen, int d_state, vmscan_dtype dtype, void* workspace,
+                       size_t workspace_bytes, int64_t chunk_len);
+
+vmscan_status vim_args(ScanArgs& a, const void* u, const void* delta_raw, const void* z, const float* A_log,
+                       const float* A_b_log, const void* B, const void* C, const void* B_b, const void* C_b,
+                       const float* D, const float* D_b, const float* delta_bias, void* out, int64_t batch,
+                       int64_t dim, int64_t seqlen, int d_state, vmscan_dtype dtype, void* workspace,
+                       size_t workspace_bytes, int64_t chunk_len) {
+  const void* ptrs[] = {u, delta_raw, z, A_log, A_b_log, B, C, B_b, C_b, D, D_b, delta_bias, out};
+  for (const void* p : ptrs)
+    if (!p) return VMSCAN_ERR_NULL;
+  if (!shape_ok(batch, dim, seqlen) || chunk_len < 0) return VMSCAN_ERR_SHAPE;
+  if (d_state != kN || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16)) return VMSCAN_ERR_UNSUPPORTED;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return VMSCAN_ERR_ALIGN;
+  const int64_t K = plan_chunk(batch * ceil_div(dim, kW), seqlen, chunk_len);
+  const size_t need = bct_bytes(batch, seqlen) + agg_bytes(batch, dim, seqlen, K);
+  if (!workspace || workspace_bytes < need) return VMSCAN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return VMSCAN_ERR_ALIGN;
+  a.u = u;
+  a.u_bs = dim * seqlen;
+  a.z = z;
+  a.out = out;
+  a.wsy = nullptr;
+  a.bct = static_cast<float*>(workspace);
+  a.agg = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + bct_bytes(batch, seqlen));
+  a.d0 = DirArgs{delta_raw, dim * seqlen, B, C, kN * seqlen, A_log, D, delta_bias, 0};
+  a.d1 = DirArgs{delta_raw, dim * seqlen, B_b, C_b, kN * seqlen, A_b_log, D_b, delta_bias, 0};
+  a.L = seqlen;
+  a.dim = static_cast<int>(dim);
+  a.batch = static_cast<int>(batch);
+  a.K = static_cast<int>(K);
+  a.nch = static_cast<int>(ceil_div(seqlen, K));
+  a.ngroups = static_cast<int>(ceil_div(dim, kW));
+  a.H = 1;
+  a.W = static_cast<int>(seqlen);
+  return VMSCAN_OK;
 }
 
 }  // namespace
@@ -800,37 +852,22 @@ vmscan_status vmscan_fwd_bidir_ex(const void* u, const void* delta_raw, const vo
                                   void* out, int64_t batch, int64_t dim, int64_t seqlen, int d_state,
                                   vmscan_dtype dtype, void* workspace, size_t workspace_bytes,
                                   int64_t chunk_len, hipStream_t stream) {
-  const void* ptrs[] = {u, delta_raw, z, A_log, A_b_log, B, C, B_b, C_b, D, D_b, delta_bias, out};
-  for (const void* p : ptrs)
-    if (!p) return VMSCAN_ERR_NULL;
-  if (!shape_ok(batch, dim, seqlen) || chunk_len < 0) return VMSCAN_ERR_SHAPE;
-  if (d_state != kN || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16)) return VMSCAN_ERR_UNSUPPORTED;
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return VMSCAN_ERR_ALIGN;
-  const int64_t K = plan_chunk(batch * ceil_div(dim, kW), seqlen, chunk_len);
-  const size_t need = vmscan_fwd_bidir_workspace_bytes_ex(batch, dim, seqlen, d_state, dtype, chunk_len);
-  if (!workspace || workspace_bytes < need) return VMSCAN_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return VMSCAN_ERR_ALIGN;
+  return vmscan_fwd_bidir_stage(u, delta_raw, z, A_log, A_b_log, B, C, B_b, C_b, D, D_b, delta_bias, out, batch, dim,
+                                seqlen, d_state, dtype, workspace, workspace_bytes, chunk_len, 3, stream);
+}
 
+vmscan_status vmscan_fwd_bidir_stage(const void* u, const void* delta_raw, const void* z, const float* A_log,
+                                     const float* A_b_log, const void* B, const void* C, const void* B_b,
+                                     const void* C_b, const float* D, const float* D_b, const float* delta_bias,
+                                     void* out, int64_t batch, int64_t dim, int64_t seqlen, int d_state,
+                                     vmscan_dtype dtype, void* workspace, size_t workspace_bytes, int64_t chunk_len,
+                                     int stage, hipStream_t stream) {
+  if (stage < 1 || stage > 3) return VMSCAN_ERR_UNSUPPORTED;
   ScanArgs a{};
-  a.u = u;
-  a.u_bs = dim * seqlen;
-  a.z = z;
-  a.out = out;
-  a.wsy = nullptr;
-  a.bct = static_cast<float*>(workspace);
-  a.agg = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + bct_bytes(batch, seqlen));
-  a.d0 = DirArgs{delta_raw, dim * seqlen, B, C, kN * seqlen, A_log, D, delta_bias, 0};
-  a.d1 = DirArgs{delta_raw, dim * seqlen, B_b, C_b, kN * seqlen, A_b_log, D_b, delta_bias, 0};
-  a.L = seqlen;
-  a.dim = static_cast<int>(dim);
-  a.batch = static_cast<int>(batch);
-  a.K = static_cast<int>(K);
-  a.nch = static_cast<int>(ceil_div(seqlen, K));
-  a.ngroups = static_cast<int>(ceil_div(dim, kW));
-  a.H = 1;
-  a.W = static_cast<int>(seqlen);
-  return run_pair_dtype<kModeVim, 0>(a, dtype, stream);
+  const vmscan_status st = vim_args(a, u, delta_raw, z, A_log, A_b_log, B, C, B_b, C_b, D, D_b, delta_bias, out, batch,
+                                    dim, seqlen, d_state, dtype, workspace, workspace_bytes, chunk_len);
+  if (st != VMSCAN_OK) return st;
+  return run_pair_dtype<kModeVim, 0>(a, dtype, stream, stage);
 }
 
 vmscan_status vmscan_fwd_bidir(const void* u, const void* delta_raw, const void* z, const float* A_log,

@@ -154,3 +154,24 @@ def test_ss2d_errors(lib):
     assert _ss(lib, _good_ptrs(8), z=0x90002) == ERR_ALIGN
     assert _ss(lib, _good_ptrs(8), ws=0) == ERR_WORKSPACE
     assert _ss(lib, _good_ptrs(8), wsb=16) == ERR_WORKSPACE
+
+
+def _stage(lib, ptrs, stage, nb=2, nd=16, L=8, ds=16, dt=1, ws=0x100000, wsb=1 << 30, chunk=0):
+    args = [VP(p) for p in ptrs] + [I64(nb), I64(nd), I64(L), ctypes.c_int(ds), ctypes.c_int(dt),
+                                     VP(ws), ctypes.c_size_t(wsb), I64(chunk), ctypes.c_int(stage), VP(0)]
+    return lib.vmscan_fwd_bidir_stage(*args)
+
+
+def test_stage_errors(lib):
+    # an unknown stage is rejected before any other check
+    for st in (0, 4, -1, 99):
+        assert _stage(lib, _good_ptrs(), st) == ERR_UNSUPPORTED, st
+        assert _stage(lib, [0] * 13, st) == ERR_UNSUPPORTED, st
+    # valid stages validate like vmscan_fwd_bidir_ex
+    for st in (1, 2, 3):
+        p = _good_ptrs()
+        p[4] = 0
+        assert _stage(lib, p, st) == ERR_NULL
+        assert _stage(lib, _good_ptrs(), st, L=0) == ERR_SHAPE
+        assert _stage(lib, _good_ptrs(), st, ds=32) == ERR_UNSUPPORTED
+        assert _stage(lib, _good_ptrs(), st, ws=0) == ERR_WORKSPACE

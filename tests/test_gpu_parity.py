@@ -78,6 +78,25 @@ def test_vim_deterministic():
     assert np.array_equal(c, d)
 
 
+def test_vim_stages_compose():
+    """Stage 1 (B/C copy) then stage 2 (scan) gives exactly the one-call result, chunked or not."""
+    import torch
+    import gpu_common as G
+    import selective_state_space_41_amd as V
+    for L, K in ((197, 0), (300, 64)):
+        p = synth.make_vim_inputs(1, layer=5, batch=3, dim=96, seqlen=L)
+        act, par = G.vim_device(p)
+        args = (act["u"], act["delta_raw"], act["z"], par["A_log"], par["A_b_log"], act["B"], act["C"], act["B_b"],
+                act["C_b"], par["D"], par["D_b"], par["delta_bias"])
+        ws = torch.empty(V.lib.vmscan_fwd_bidir_workspace_bytes_ex(3, 96, L, 16, 1, K), dtype=torch.uint8, device="cuda")
+        ref = V.vmscan_fwd_bidir(*args, chunk_len=K, workspace=ws)
+        out = torch.empty_like(ref)
+        V.vmscan_fwd_bidir(*args, out=out, chunk_len=K, workspace=ws, stage=1)
+        V.vmscan_fwd_bidir(*args, out=out, chunk_len=K, workspace=ws, stage=2)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), (L, K)
+
+
 def test_config0_full():
     p = synth.make_vim_inputs(0)
     _report("config 0 (fp32 B1 D384 L197)", O.rel_err(run_vim(p), oracle_vim(p)), 1e-5)
