@@ -35,8 +35,9 @@
  *     enqueued; on success the kernels are enqueued on `stream` (NULL = the default stream) and the
  *     call returns without waiting.  A failed launch returns VMSCAN_ERR_HIP and the hipError_t
  *     is kept for vmscan_last_hip_error().  No entry point throws or aborts.
- *   - Workspace: caller-provided device scratch of at least the queried size (0 means none is
- *     needed and `workspace` may be NULL).  Its contents on entry are ignored.
+ *   - Workspace: caller-provided device scratch of at least the queried size.  When the query
+ *     returns 0 none is needed and `workspace` may be NULL (if given, it must still be 16-byte
+ *     aligned).  Its contents on entry are ignored.
  */
 #ifndef VMSCAN_H
 #define VMSCAN_H
@@ -96,7 +97,7 @@ size_t vmscan_fwd_bidir_workspace_bytes_ex(int64_t batch, int64_t dim, int64_t s
  * Long sequences are split into chunks whose boundary states are carried across workgroups
  * (chunk_len 0 = library choice; otherwise the given length, clamped to [1, min(seqlen, 206)]).
  * The workspace (size from vmscan_fwd_bidir_workspace_bytes[_ex]) holds a float32 copy of
- * B/C/B_b/C_b and, for split sequences, the chunk end states.
+ * B/C/B_b/C_b in position-major order and, for split sequences, the chunk end states.
  */
 vmscan_status vmscan_fwd_bidir(const void *u, const void *delta_raw, const void *z,
                                const float *A_log, const float *A_b_log,
@@ -115,10 +116,11 @@ vmscan_status vmscan_fwd_bidir_ex(const void *u, const void *delta_raw, const vo
 
 /*
  * The two stages of vmscan_fwd_bidir_ex, for callers that time or overlap them separately:
- *   stage 1: write the float32 copy of B/C/B_b/C_b (position-major) into the workspace;
- *   stage 2: run the scan from that copy (chunk states if the sequence is split, then the fused
- *            bidirectional scan); requires a completed stage 1 with the same B/C pointers, shapes
- *            and workspace, else the output is unspecified;
+ *   stage 1: preparation: the float32 position-major copy of B/C/B_b/C_b and, for a split
+ *            sequence, each chunk's end state (scanned from zero) and Δ sum, in the workspace;
+ *   stage 2: the fused bidirectional scan, which reads that copy and folds the carries into
+ *            each chunk's initial state; it requires a completed stage 1 with the same inputs,
+ *            shapes, chunk_len and workspace, else the output is unspecified;
  *   stage 3: both (= vmscan_fwd_bidir_ex).
  * Other stage values return VMSCAN_ERR_UNSUPPORTED.  Arguments as for vmscan_fwd_bidir_ex.
  */

@@ -116,16 +116,21 @@ def _stream(stream, device):
 
 
 def _workspace(ws, nbytes, dev):
-    """The caller's workspace if it is a large enough uint8 device tensor, else a new one when
-    none was given.  A workspace that is given but too small is an error, not silently replaced:
-    the stages of one call must see the same buffer."""
+    """The caller's workspace if it is a large enough uint8 device tensor; a new one when none
+    was given and the call needs one (None when it needs none).  A workspace that is given but
+    too small is an error, not silently replaced: the stages of one call must see the same
+    buffer."""
     if ws is None:
-        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        return torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes > 0 else None
     if ws.dtype != torch.uint8 or ws.device != dev or not ws.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
     if ws.numel() < nbytes:
         raise ValueError(f"workspace holds {ws.numel()} bytes, {nbytes} needed")
     return ws
+
+
+def _nbytes(t):
+    return t.numel() if t is not None else 0
 
 
 def vmscan_fwd_bidir(u, delta_raw, z, A_log, A_b_log, B, C, B_b, C_b, D, D_b, delta_bias,
@@ -135,7 +140,8 @@ def vmscan_fwd_bidir(u, delta_raw, z, A_log, A_b_log, B, C, B_b, C_b, D, D_b, de
     u, delta_raw, z: [batch, dim, L]; A_log, A_b_log: [dim, 16] float32; B, C, B_b, C_b:
     [batch, 16, L] (original token order); D, D_b, delta_bias: [dim] float32.  Activations are
     float32 or bfloat16 (all the same).  ``chunk_len`` 0 lets the library choose.  ``stage``
-    1 / 2 runs only the B/C preparation / the scan (vmscan_fwd_bidir_stage); 3 runs both."""
+    1 / 2 runs only the preparation (B/C copy, chunk carries) / the fused scan
+    (vmscan_fwd_bidir_stage); 3 runs both."""
     if u.dim() != 3:
         raise ValueError("u must be [batch, dim, L]")
     nb, nd, L = u.shape
@@ -160,7 +166,7 @@ def vmscan_fwd_bidir(u, delta_raw, z, A_log, A_b_log, B, C, B_b, C_b, D, D_b, de
     _check(lib.vmscan_fwd_bidir_stage(
         _ptr(u), _ptr(delta_raw), _ptr(z), _ptr(A_log), _ptr(A_b_log), _ptr(B), _ptr(C), _ptr(B_b), _ptr(C_b),
         _ptr(D), _ptr(D_b), _ptr(delta_bias), _ptr(out), nb, nd, L, D_STATE, dt,
-        _ptr(workspace), workspace.numel(), int(chunk_len), int(stage), _stream(stream, dev)))
+        _ptr(workspace), _nbytes(workspace), int(chunk_len), int(stage), _stream(stream, dev)))
     return out
 
 
@@ -196,7 +202,7 @@ def ss2d_cross_scan_fwd(x, delta_raw, A_log, B, C, D, delta_bias, z=None, out=No
     workspace = _workspace(workspace, wsb, dev)
     _check(lib.ss2d_cross_scan_fwd_ex(
         _ptr(x), _ptr(delta_raw), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(delta_bias), _ptr(z), _ptr(out),
-        nb, nd, H, W, D_STATE, dt, _ptr(workspace), workspace.numel(), int(chunk_len), _stream(stream, dev)))
+        nb, nd, H, W, D_STATE, dt, _ptr(workspace), _nbytes(workspace), int(chunk_len), _stream(stream, dev)))
     return out
 
 

@@ -4,27 +4,32 @@
 // What is computed is stated in that header with the page citations; this file holds the
 // kernels and the host-side validation and dispatch.
 //
-// Design (gfx950: wave64, 160 KB LDS per CU, fp32 VALU with a transcendental rate of about a
-// third of the FMA rate, so this path is bound by VALU issue, not by HBM; no dense
+// Design (gfx950: wave64, 4 SIMDs and 160 KB LDS per CU; fp32 VALU with a transcendental rate
+// of about a third of the FMA rate, so this path is bound by VALU issue, not by HBM; no dense
 // contraction, so no MFMA):
-//  * A workgroup is two wavefronts over the same 64 channels of one batch row: wave 0 runs the
-//    forward direction, wave 1 the backward direction.  Lane = channel; the lane keeps all 16
-//    fp32 states of its (batch, channel, direction) in VGPRs.  Per state and token the VALU
-//    work is exp2(Δ·A') (A' = A·log2 e), h·a, h + (Δu)·B, y + C·h.
-//  * B and C are the same for every channel of a batch row, so each wave reads them as
-//    wave-uniform scalars (s_load) from an fp32 [batch][direction][position][B 0..15, C 0..15]
-//    copy that a small transpose kernel writes first (per position the wave needs 128
-//    contiguous bytes).  No VALU instruction is spent on B/C.
+//  * One wave issues at most about one VALU instruction every 8 cycles, so a SIMD needs three
+//    or more resident waves to keep its VALU busy.  A workgroup is therefore four wavefronts
+//    over the same 64 channels (lane = channel) of one batch row: waves 0 and 2 run the forward
+//    direction, waves 1 and 3 the backward direction, and waves 0/1 keep states 0-7 of every
+//    channel, waves 2/3 states 8-15, in VGPRs.  At the Vim-Ti shape this is 3072 waves, three
+//    per SIMD.  Per state and token the VALU work is exp2(Δ·A') (A' = A·log2 e), h·a,
+//    h + (Δu)·B and y + C·h.
+//  * B and C are the same for every channel of a batch row, so each wave reads its 8 B and 8 C
+//    values per token as wave-uniform scalars (one s_load_dwordx16) from an fp32
+//    [batch][direction][half][position][16] copy that a small transpose kernel writes first.
+//    No VALU instruction is spent on B/C.
 //  * u, Δ_raw (and z) are read per lane in windows of 8 consecutive tokens (16-byte loads;
 //    the hardware accepts the 2-byte-aligned rows of odd-length bf16 sequences), one window
-//    ahead of use.  Δ = softplus(Δ_raw + bias) is computed once per (token, channel,
-//    direction) with a compensated log1p: log(1+e) = ln2·log2(s) + (e - (s - 1)), s = 1 + e.
-//  * Both directions advance in lockstep: at step i the forward wave is at chunk position i,
-//    the backward wave at Kc-1-i.  In the first half of the steps each direction stores its y
-//    (including its D·u term) in an fp32 LDS row per channel; after a barrier, in the second
-//    half, each direction adds the other's stored y at the positions it reaches and writes the
-//    finished output (gate applied once, bf16 rounded once) straight to HBM in 8-token
-//    windows.  No reversed copy of any tensor is made and no epilogue pass is needed.
+//    ahead of use.  Δ = softplus(Δ_raw + bias) is computed with a compensated log1p:
+//    log(1+e) = ln2·log2(s) + (e - (s - 1)), s = 1 + e.
+//  * All four waves advance in lockstep: at step i the forward waves are at chunk position i,
+//    the backward waves at Kc-1-i.  The channel's y at a position is the sum of four partial
+//    readouts (two directions x two state halves).  They meet in one fp32 LDS row per channel in
+//    a fixed order, so the result is deterministic: per window the lower-half wave of a direction
+//    stores (first half of the steps) or adds (second half) its partial y, including the D·u
+//    term; after a workgroup barrier the upper-half wave adds its own.  A cooperative epilogue
+//    then applies the gate once, rounds once, and writes 16-byte stores.  No reversed copy of
+//    any tensor is made.
 //  * Sequences longer than one LDS row are split into chunks.  A first kernel computes each
 //    chunk's end state from a zero start and its Σ Δ; the main kernel folds the preceding
 //    chunks' pairs (Σ Δ, end state) into its initial state, exp(A Σ Δ) being a chunk's total
@@ -45,10 +50,11 @@
 namespace {
 
 constexpr int kN = 16;                 // d_state
+constexpr int kH = 8;                  // states per wave: two waves per (channel, direction)
 constexpr int kW = 64;                 // channels per workgroup = lanes per wave
-constexpr int kThreads = 2 * kW;       // wave 0 forward, wave 1 backward
+constexpr int kThreads = 4 * kW;       // waves: (fwd, lo) (bwd, lo) (fwd, hi) (bwd, hi)
 constexpr int kWin = 8;                // tokens per register window
-constexpr int kBC = 2 * kN;            // floats per position in the B/C copy
+constexpr int kBC = 2 * kH;            // floats per (position, half) in the B/C copy: 8 B, 8 C
 constexpr int kKMax = 206;             // longest LDS row: 3 workgroups of 64 x 207 floats per CU
 constexpr int kMinChunk = 32;          // shortest chunk the planner picks
 constexpr int kTargetBlocks = 768;     // planner: enough workgroups for one full round
@@ -155,7 +161,7 @@ struct ScanArgs {
   const void* z;   // gate, same layout as u, or null
   void* out;
   float* wsy;      // fp32 image of the first SS2D pair
-  float* bct;      // [batch][2][L][kBC] fp32 B/C copy in position order
+  float* bct;      // [batch][2][2][L][kBC] fp32 B/C copy in position order
   float* agg;      // [batch][dim][2][nch][kAggStride]
   DirArgs d0, d1;  // forward and backward direction of the pair
   int64_t L;
@@ -166,7 +172,8 @@ struct ScanArgs {
 enum { kModeVim = 0, kModeFirstPair = 1, kModeSecondPair = 2 };
 
 // ---------------------------------------------------------------------------------------------
-// B/C transpose: bct[b][dir][s][0..15] = B_dir[b][:, si(s)], bct[b][dir][s][16..31] = C_dir[...]
+// B/C transpose: for half q, bct[b][dir][q][s][0..7] = B_dir[b][8q + 0..7, si(s)] and
+// bct[b][dir][q][s][8..15] = C_dir[b][8q + 0..7, si(s)].
 
 template <typename T>
 __global__ __launch_bounds__(kTransThreads) void bc_transpose_kernel(ScanArgs a) {
@@ -181,27 +188,31 @@ __global__ __launch_bounds__(kTransThreads) void bc_transpose_kernel(ScanArgs a)
   const int64_t si = da.rev ? a.L - 1 - s : s;
   const T* bb = static_cast<const T*>(da.B) + static_cast<int64_t>(b) * da.bc_bs + si;
   const T* cb = static_cast<const T*>(da.C) + static_cast<int64_t>(b) * da.bc_bs + si;
-  float v[kBC];
 #pragma unroll
-  for (int n = 0; n < kN; ++n) {
-    v[n] = ld_act(bb, static_cast<int64_t>(n) * a.L);
-    v[kN + n] = ld_act(cb, static_cast<int64_t>(n) * a.L);
+  for (int q = 0; q < 2; ++q) {
+    float v[kBC];
+#pragma unroll
+    for (int k = 0; k < kH; ++k) {
+      v[k] = ld_act(bb, static_cast<int64_t>(kH * q + k) * a.L);
+      v[kH + k] = ld_act(cb, static_cast<int64_t>(kH * q + k) * a.L);
+    }
+    float4* dst = reinterpret_cast<float4*>(a.bct + (((static_cast<int64_t>(b) * 2 + dir) * 2 + q) * a.L + s) * kBC);
+#pragma unroll
+    for (int k = 0; k < kBC / 4; ++k) dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
   }
-  float4* dst = reinterpret_cast<float4*>(a.bct + ((static_cast<int64_t>(b) * 2 + dir) * a.L + s) * kBC);
-#pragma unroll
-  for (int q = 0; q < kBC / 4; ++q) dst[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
 }
 
 // ---------------------------------------------------------------------------------------------
-// Scan kernels.  What differs between the forward and backward wave, the Vim and SS2D pairs and
+// Scan kernels.  What differs between the forward and backward waves, the Vim and SS2D pairs and
 // the two scan orders is a template parameter, so the token loop has no data-dependent branches:
 //   DIR   0: step i visits chunk position i; 1: position Kc-1-i
 //   MODE  kModeVim / kModeFirstPair / kModeSecondPair (SS2D backward tensors are stored in
 //         reversed position order; the modes differ in the epilogue)
 //   ORDER 0: u element = position; 1: column-major position -> row-major pixel
+// The state half of a wave is a wave-uniform run-time value (it only selects data).
 
 struct Lane {
-  int b, c, lane, d, dd;  // dd: channel clamped into range for the loads of inactive lanes
+  int b, c, lane, d, dd, half;  // dd: channel clamped into range for the loads of inactive lanes
   bool valid;
   int64_t s_lo;
   int Kc;
@@ -216,6 +227,7 @@ __device__ __forceinline__ Lane lane_ctx(const ScanArgs& a) {
   l.c = rest % a.nch;
   l.b = rest / a.nch;
   l.lane = threadIdx.x & (kW - 1);
+  l.half = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 7);
   l.d = g * kW + l.lane;
   l.valid = l.d < a.dim;
   l.dd = l.valid ? l.d : a.dim - 1;
@@ -296,93 +308,89 @@ struct Window {
   }
 };
 
-__device__ __forceinline__ void load_a2(const DirArgs& da, int dd, float (&A2)[kN]) {
+// A' = -exp(A_log) * log2 e for the wave's 8 states.
+__device__ __forceinline__ void load_a2(const DirArgs& da, const Lane& l, float (&A2)[kH]) {
 #pragma unroll
-  for (int n = 0; n < kN; ++n) A2[n] = -__expf(da.A_log[static_cast<int64_t>(dd) * kN + n]) * kLog2e;  // A = -exp(A_log)
+  for (int k = 0; k < kH; ++k)
+    A2[k] = -__expf(da.A_log[static_cast<int64_t>(l.dd) * kN + kH * l.half + k]) * kLog2e;
 }
 
-// B/C of one position: 16 + 16 wave-uniform floats (two s_load_dwordx16).
+// B/C of one position for the wave's half: 8 + 8 wave-uniform floats (one s_load_dwordx16).
 __device__ __forceinline__ void load_bc(scalar_fp p, float (&bc)[kBC]) {
 #pragma unroll
   for (int q = 0; q < kBC; ++q) bc[q] = p[q];
 }
 
-// Bring the B/C lines of steps [i, i + kWin) of one direction into L2 ahead of their scalar
-// loads.  The scalar cache misses on nearly every position, and a scalar load can only be
-// waited for together with all others in flight, so its latency is hidden only if it hits L2.
-// Lane k < kWin touches the line of step i + k through the vector path, whose loads complete in
-// order and are waited for with the window data anyway.  Positions are clamped into the row.
-template <int MODE, int DIR>
-__device__ __forceinline__ uint32_t touch_bc(const ScanArgs& a, const Lane& l, int i) {
-  using Dr = Dir<MODE, DIR>;
-  int64_t p = Dr::pos(l, i + (l.lane & (kWin - 1)));
-  p = p < 0 ? 0 : (p >= a.L ? a.L - 1 : p);
-  const uint32_t* row = reinterpret_cast<const uint32_t*>(a.bct) + ((static_cast<int64_t>(l.b) * 2 + DIR) * a.L) * kBC;
-  return row[p * kBC];
+// The wave's row of the B/C copy.
+template <int DIR>
+__device__ __forceinline__ scalar_fp bc_row(const ScanArgs& a, const Lane& l) {
+  return (scalar_fp)(a.bct) + (((static_cast<int64_t>(l.b) * 2 + DIR) * 2 + l.half) * a.L) * kBC;
 }
 
-// One token for 16 states, h = exp2(Δ A') h + (Δu) B; returns Σ C h.  The B/C of the next
-// token (nxt) is requested once this token's B values are dead (after the h updates), so at most
-// 48 SGPRs hold B/C.  Scalar loads may return out of order, so the wait for this token's B/C
-// (at its first use) covers every scalar load in flight; issuing nxt after that point leaves it
-// the readout plus the next token's decays to arrive.
-__device__ __forceinline__ float scan_token(float dl, float du, const float (&A2)[kN], float (&h)[kN],
+// One token for the wave's 8 states, h = exp2(Δ A') h + (Δu) B; returns yi + Σ C h.  The B/C of
+// the next token (nxt) is requested once this token's B values are dead (after the h updates),
+// so at most 32 SGPRs hold B/C.  Scalar loads may return out of order, so the wait for this
+// token's B/C (at its first use) covers every scalar load in flight; issuing nxt after that point
+// leaves it the readout plus the next token's decays to arrive.
+__device__ __forceinline__ float scan_token(float dl, float du, float yi, const float (&A2)[kH], float (&h)[kH],
                                            const float (&cur)[kBC], float (&nxt)[kBC], scalar_fp nxt_p) {
-  float an[kN];
+  float an[kH];
 #pragma unroll
-  for (int n = 0; n < kN; ++n) an[n] = __builtin_amdgcn_exp2f(dl * A2[n]);
+  for (int n = 0; n < kH; ++n) an[n] = __builtin_amdgcn_exp2f(dl * A2[n]);
 #pragma unroll
-  for (int n = 0; n < kN; ++n) {
+  for (int n = 0; n < kH; ++n) {
     h[n] = h[n] * an[n];
     h[n] = __builtin_fmaf(du, cur[n], h[n]);
   }
   __builtin_amdgcn_sched_barrier(0);
   load_bc(nxt_p, nxt);
   __builtin_amdgcn_sched_barrier(0);
-  float y0 = 0.0f, y1 = 0.0f;
+  float y0 = yi, y1 = 0.0f;
 #pragma unroll
-  for (int n = 0; n < kN; n += 2) {
-    y0 = __builtin_fmaf(cur[kN + n], h[n], y0);
-    y1 = __builtin_fmaf(cur[kN + n + 1], h[n + 1], y1);
+  for (int n = 0; n < kH; n += 2) {
+    y0 = __builtin_fmaf(cur[kH + n], h[n], y0);
+    y1 = __builtin_fmaf(cur[kH + n + 1], h[n + 1], y1);
   }
   return y0 + y1;
 }
 
 // Steps [i0, i0 + kWin) of one direction.  On entry bcA holds the B/C of step i0; on exit bcA
 // holds the B/C of step i0 + kWin.  The buffers alternate between the steps, so no register
-// copies are needed.  The one-past-the-end prefetch of a direction's last step stays inside the
-// B/C copy: the forward row is followed by the backward row of the same batch, and the backward
-// direction runs towards the forward row.
+// copies are needed.  The one-past-the-end prefetch of a row's last step stays inside the B/C
+// copy: forward rows are followed by another row, and backward rows follow another row.
 template <int MODE, int DIR>
 __device__ __forceinline__ void run_steps(const Lane& l, int i0, const float (&dl)[kWin], const float (&du)[kWin],
-                                          const float (&A2)[kN], float (&h)[kN], float (&bcA)[kBC],
-                                          float (&bcB)[kBC], scalar_fp bct, float (&y)[kWin]) {
+                                          const float (&yi)[kWin], const float (&A2)[kH], float (&h)[kH],
+                                          float (&bcA)[kBC], float (&bcB)[kBC], scalar_fp bct, float (&y)[kWin]) {
   using Dr = Dir<MODE, DIR>;
   // Address of step i0 + k as a window base plus an immediate offset.
   const int64_t p0 = Dr::pos(l, i0);
   scalar_fp base = DIR == 0 ? bct + p0 * kBC : bct + (p0 - kWin) * kBC;
 #pragma unroll
   for (int j = 0; j < kWin; j += 2) {
-    y[j] = scan_token(dl[j], du[j], A2, h, bcA, bcB, base + (DIR == 0 ? j + 1 : kWin - j - 1) * kBC);
-    y[j + 1] = scan_token(dl[j + 1], du[j + 1], A2, h, bcB, bcA, base + (DIR == 0 ? j + 2 : kWin - j - 2) * kBC);
+    y[j] = scan_token(dl[j], du[j], yi[j], A2, h, bcA, bcB, base + (DIR == 0 ? j + 1 : kWin - j - 1) * kBC);
+    y[j + 1] = scan_token(dl[j + 1], du[j + 1], yi[j + 1], A2, h, bcB, bcA,
+                          base + (DIR == 0 ? j + 2 : kWin - j - 2) * kBC);
   }
 }
 
-// Δ and Δ·u of a window from its raw u and Δ_raw.
-__device__ __forceinline__ void prep_window(const float (&uu)[kWin], const float (&xr)[kWin], float bias,
-                                            float (&dl)[kWin], float (&du)[kWin]) {
+// Δ and Δ·u of a window from its raw u and Δ_raw; yi = the lane's D·u share (lower half only).
+__device__ __forceinline__ void prep_window(const float (&uu)[kWin], const float (&xr)[kWin], float bias, float Dh,
+                                            float (&dl)[kWin], float (&du)[kWin], float (&yi)[kWin]) {
 #pragma unroll
   for (int j = 0; j < kWin; ++j) {
     dl[j] = softplus_f(xr[j] + bias);
     du[j] = dl[j] * uu[j];
+    yi[j] = Dh * uu[j];
   }
 }
 
 // One step i outside the full windows (chunk tails): raw loads, Δ, the token update and the B/C
-// prefetch of step i + 1 into bcA.  Returns y + D·u and sets *dl_out = Δ.
+// prefetch of step i + 1 into bcA.  Returns the wave's partial y (with its D·u share) and sets
+// *dl_out = Δ.
 template <typename T, int MODE, int ORDER, int DIR>
-__device__ __forceinline__ float single_step(const ScanArgs& a, const Lane& l, const DirArgs& da, float bias, float Dv,
-                                             int i, const float (&A2)[kN], float (&h)[kN], scalar_fp bct,
+__device__ __forceinline__ float single_step(const ScanArgs& a, const Lane& l, const DirArgs& da, float bias, float Dh,
+                                             int i, const float (&A2)[kH], float (&h)[kH], scalar_fp bct,
                                              float (&bcA)[kBC], float* dl_out) {
   using Dr = Dir<MODE, DIR>;
   const T* ub = static_cast<const T*>(a.u) + static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(l.dd) * a.L;
@@ -397,67 +405,62 @@ __device__ __forceinline__ float single_step(const ScanArgs& a, const Lane& l, c
   const float uu = ld_act(ub, e);
   const float dl = softplus_f(ld_act(db, Dr::sidx(a, l, i)) + bias);
   float bcB[kBC];
-  const float y = scan_token(dl, dl * uu, A2, h, bcA, bcB, bct + Dr::pos(l, i + 1) * kBC);
+  const float y = scan_token(dl, dl * uu, Dh * uu, A2, h, bcA, bcB, bct + Dr::pos(l, i + 1) * kBC);
 #pragma unroll
   for (int q = 0; q < kBC; ++q) bcA[q] = bcB[q];
   *dl_out = dl;
-  return y + Dv * uu;
+  return y;
 }
 
 // ---------------------------------------------------------------------------------------------
-// Pass A: per chunk and direction, the end state of the chunk scanned from a zero state, and Σ Δ.
+// Pass A: per chunk, direction and state half, the end states of the chunk scanned from a zero
+// state, and Σ Δ.
 
 template <typename T, int MODE, int ORDER, int DIR>
 __device__ __forceinline__ void chunk_state_dir(const ScanArgs& a, const Lane& l) {
-  using Dr = Dir<MODE, DIR>;
   const DirArgs& da = DIR == 0 ? a.d0 : a.d1;
-  float A2[kN], h[kN];
-  load_a2(da, l.dd, A2);
+  float A2[kH], h[kH];
+  load_a2(da, l, A2);
 #pragma unroll
-  for (int n = 0; n < kN; ++n) h[n] = 0.0f;
+  for (int n = 0; n < kH; ++n) h[n] = 0.0f;
   const float bias = da.bias[l.dd];
-  scalar_fp bct = (scalar_fp)(a.bct) + ((static_cast<int64_t>(l.b) * 2 + DIR) * a.L) * kBC;
+  const scalar_fp bct = bc_row<DIR>(a, l);
   float S = 0.0f;
   float bcA[kBC], bcB[kBC];
   Window<T, MODE, ORDER, DIR> win;
   const int full_end = (l.Kc / kWin) * kWin;
-  uint32_t sink = touch_bc<MODE, DIR>(a, l, 0), touch = 0;
-  load_bc(bct + Dr::pos(l, 0) * kBC, bcA);
+  load_bc(bct + Dir<MODE, DIR>::pos(l, 0) * kBC, bcA);
   if (full_end > 0) win.load(a, l, da, 0);
   for (int i0 = 0; i0 < full_end; i0 += kWin) {
-    float uu[kWin], xr[kWin], dl[kWin], du[kWin], y[kWin];
+    float uu[kWin], xr[kWin], dl[kWin], du[kWin], yi[kWin], y[kWin];
     win.unpack(uu, xr);
-    sink ^= touch;
     // The prefetch must not be hoisted above the unpack: the window registers are loop-carried,
     // and a load into other registers would need a copy (and so a wait) at the loop back edge.
     // It is unconditional for the same reason (the last window reloads itself).
     __builtin_amdgcn_sched_barrier(0);
     win.load(a, l, da, i0 + kWin < full_end ? i0 + kWin : i0);
-    touch = touch_bc<MODE, DIR>(a, l, i0 + kWin);
-    prep_window(uu, xr, bias, dl, du);
+    prep_window(uu, xr, bias, 0.0f, dl, du, yi);
 #pragma unroll
     for (int j = 0; j < kWin; ++j) S += dl[j];
-    run_steps<MODE, DIR>(l, i0, dl, du, A2, h, bcA, bcB, bct, y);
+    run_steps<MODE, DIR>(l, i0, dl, du, yi, A2, h, bcA, bcB, bct, y);
   }
   for (int i = full_end; i < l.Kc; ++i) {
     float dl;
     single_step<T, MODE, ORDER, DIR>(a, l, da, bias, 0.0f, i, A2, h, bct, bcA, &dl);
     S += dl;
   }
-  sink ^= touch;
-  if (sink == 0x7fc00001u && a.dim < 0) a.agg[0] = 0.0f;  // keeps the touch loads; never true
   if (l.valid) {
     float* ag = a.agg + ((((static_cast<int64_t>(l.b) * a.dim + l.d) * 2 + DIR) * a.nch) + l.c) * kAggStride;
 #pragma unroll
-    for (int n = 0; n < kN; ++n) ag[n] = h[n];
-    ag[kN] = S;
+    for (int n = 0; n < kH; ++n) ag[kH * l.half + n] = h[n];
+    if (l.half == 0) ag[kN] = S;
   }
 }
 
 template <typename T, int MODE, int ORDER>
 __global__ __launch_bounds__(kThreads) void chunk_state_kernel(ScanArgs a) {
   const Lane l = lane_ctx(a);
-  if (threadIdx.x < kW) chunk_state_dir<T, MODE, ORDER, 0>(a, l);
+  if ((__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6) & 1) == 0) chunk_state_dir<T, MODE, ORDER, 0>(a, l);
   else chunk_state_dir<T, MODE, ORDER, 1>(a, l);
 }
 
@@ -465,60 +468,74 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(ScanArgs a) {
 // Main pass: fused bidirectional scan of one chunk with meet-in-the-middle combination.
 // Phase 0 (steps [0, M)) stores each direction's y, including its D·u term, in the channel's LDS
 // row at the chunk positions; phase 1 (steps [M, Kc)) adds it to the other direction's stored
-// value.  After both phases every row holds y_f + y_b, and the epilogue writes the outputs.
+// value.  Within a direction the lower-half wave writes (phase 0) or adds (phase 1) first and,
+// after a workgroup barrier, the upper-half wave adds.  Both directions run the same sequence of
+// windows and single steps, so all four waves meet the same barriers.  For an odd chunk both
+// directions reach the middle token at their last phase-0 step; the backward value of that step
+// goes to the spare slot Kc.  After both phases every row holds y_f + y_b.
+
+// LDS update of one value: the lower half writes (PHASE 0) or adds (PHASE 1); then, after the
+// barrier that the caller places between them, the upper half adds.
+template <int PHASE>
+__device__ __forceinline__ void lds_first(float* slot, float v) {
+  *slot = PHASE == 1 ? *slot + v : v;
+}
 
 template <typename T, int MODE, int ORDER, int DIR, int PHASE>
-__device__ __forceinline__ void run_phase(const ScanArgs& a, const Lane& l, const DirArgs& da, float bias, float Dv,
-                                          int i_begin, int i_end, const float (&A2)[kN], float (&h)[kN],
-                                          scalar_fp bct, float (&bcA)[kBC], float (&bcB)[kBC], float* myY) {
+__device__ __forceinline__ void run_phase(const ScanArgs& a, const Lane& l, const DirArgs& da, float bias, float Dh,
+                                          int i_begin, int n_win, int i_end, int spare_step, const float (&A2)[kH],
+                                          float (&h)[kH], scalar_fp bct, float (&bcA)[kBC], float (&bcB)[kBC],
+                                          float* myY) {
   Window<T, MODE, ORDER, DIR> win;
-  const int full_end = i_begin + ((i_end - i_begin) / kWin) * kWin;
-  uint32_t sink = touch_bc<MODE, DIR>(a, l, i_begin), touch = 0;
+  const int full_end = i_begin + n_win * kWin;
   if (full_end > i_begin) win.load(a, l, da, i_begin);
   for (int i0 = i_begin; i0 < full_end; i0 += kWin) {
-    float uu[kWin], xr[kWin], dl[kWin], du[kWin], y[kWin];
+    float uu[kWin], xr[kWin], dl[kWin], du[kWin], yi[kWin], y[kWin];
     win.unpack(uu, xr);
-    sink ^= touch;
     __builtin_amdgcn_sched_barrier(0);  // see chunk_state_dir
     win.load(a, l, da, i0 + kWin < full_end ? i0 + kWin : i0);
-    touch = touch_bc<MODE, DIR>(a, l, i0 + kWin);
-    prep_window(uu, xr, bias, dl, du);
+    prep_window(uu, xr, bias, Dh, dl, du, yi);
+    run_steps<MODE, DIR>(l, i0, dl, du, yi, A2, h, bcA, bcB, bct, y);
     const int p0 = DIR == 0 ? i0 : l.Kc - 1 - i0;  // chunk position of step i0
-    float prev[kWin];
-    if (PHASE == 1) {
+    if (l.half == 0) {
 #pragma unroll
-      for (int j = 0; j < kWin; ++j) prev[j] = myY[p0 + (DIR == 0 ? j : -j)];
+      for (int j = 0; j < kWin; ++j) lds_first<PHASE>(myY + p0 + (DIR == 0 ? j : -j), y[j]);
     }
-    run_steps<MODE, DIR>(l, i0, dl, du, A2, h, bcA, bcB, bct, y);
+    __syncthreads();
+    if (l.half == 1) {
 #pragma unroll
-    for (int j = 0; j < kWin; ++j) {
-      const float v = __builtin_fmaf(Dv, uu[j], y[j]);
-      myY[p0 + (DIR == 0 ? j : -j)] = PHASE == 1 ? prev[j] + v : v;
+      for (int j = 0; j < kWin; ++j) myY[p0 + (DIR == 0 ? j : -j)] += y[j];
     }
   }
   for (int i = full_end; i < i_end; ++i) {
     float dl;
-    const float v = single_step<T, MODE, ORDER, DIR>(a, l, da, bias, Dv, i, A2, h, bct, bcA, &dl);
-    const int pos = DIR == 0 ? i : l.Kc - 1 - i;
-    myY[pos] = PHASE == 1 ? myY[pos] + v : v;
+    const float v = single_step<T, MODE, ORDER, DIR>(a, l, da, bias, Dh, i, A2, h, bct, bcA, &dl);
+    const int pos = i == spare_step ? l.Kc : (DIR == 0 ? i : l.Kc - 1 - i);
+    if (l.half == 0) lds_first<PHASE>(myY + pos, v);
+    __syncthreads();
+    if (l.half == 1) myY[pos] += v;
   }
-  sink ^= touch;
-  if (sink == 0x7fc00001u && a.dim < 0) a.agg[0] = 0.0f;  // keeps the touch loads; never true
 }
 
+template <typename T>
+struct EpiZ;
+template <typename T, int MODE, int ORDER>
+__device__ __forceinline__ void epi_prefetch(const ScanArgs& a, const Lane& l, EpiZ<T>& e);
+
 template <typename T, int MODE, int ORDER, int DIR>
-__device__ __forceinline__ void scan_pair_dir(const ScanArgs& a, const Lane& l, float* ybuf, int ybs) {
+__device__ __forceinline__ void scan_pair_dir(const ScanArgs& a, const Lane& l, float* ybuf, int ybs, EpiZ<T>& epi) {
   using Dr = Dir<MODE, DIR>;
   const DirArgs& da = DIR == 0 ? a.d0 : a.d1;
   const int Kc = l.Kc;
   const int M = (Kc + 1) >> 1;  // steps of the first phase
+  const bool odd = (Kc & 1) != 0;
 
-  float A2[kN], h[kN];
-  load_a2(da, l.dd, A2);
+  float A2[kH], h[kH];
+  load_a2(da, l, A2);
 #pragma unroll
-  for (int n = 0; n < kN; ++n) h[n] = 0.0f;
+  for (int n = 0; n < kH; ++n) h[n] = 0.0f;
   const float bias = da.bias[l.dd];
-  const float Dv = da.Dp[l.dd];
+  const float Dh = l.half == 0 ? da.Dp[l.dd] : 0.0f;  // the lower half adds the D·u term
 
   // Carry-in: fold the preceding chunks' (Σ Δ, end state) pairs in scan order.
   if (a.nch > 1) {
@@ -528,25 +545,23 @@ __device__ __forceinline__ void scan_pair_dir(const ScanArgs& a, const Lane& l, 
       const float* e = ag + (DIR == 0 ? k : a.nch - 1 - k) * kAggStride;
       const float S = e[kN];
 #pragma unroll
-      for (int n = 0; n < kN; ++n) h[n] = __builtin_fmaf(__builtin_amdgcn_exp2f(A2[n] * S), h[n], e[n]);
+      for (int n = 0; n < kH; ++n) h[n] = __builtin_fmaf(__builtin_amdgcn_exp2f(A2[n] * S), h[n], e[kH * l.half + n]);
     }
   }
 
-  scalar_fp bct = (scalar_fp)(a.bct) + ((static_cast<int64_t>(l.b) * 2 + DIR) * a.L) * kBC;
+  const scalar_fp bct = bc_row<DIR>(a, l);
   float* myY = ybuf + l.lane * ybs;
   float bcA[kBC], bcB[kBC];
   load_bc(bct + Dr::pos(l, 0) * kBC, bcA);
 
-  // For an odd chunk both directions reach the middle token at their last phase-0 step; the
-  // backward value of that step goes to the spare slot Kc.
-  const int p0_end = (DIR == 1 && (Kc & 1)) ? M - 1 : M;
-  run_phase<T, MODE, ORDER, DIR, 0>(a, l, da, bias, Dv, 0, p0_end, A2, h, bct, bcA, bcB, myY);
-  if (p0_end < M) {
-    float dl;
-    myY[Kc] = single_step<T, MODE, ORDER, DIR>(a, l, da, bias, Dv, M - 1, A2, h, bct, bcA, &dl);
-  }
+  // The same window/step structure for both directions: the windows of phase 0 stop before the
+  // middle token of an odd chunk, which is then a single step of both directions.
+  const int nw0 = (odd ? M - 1 : M) / kWin;
+  const int spare = (DIR == 1 && odd) ? M - 1 : -1;
+  run_phase<T, MODE, ORDER, DIR, 0>(a, l, da, bias, Dh, 0, nw0, M, spare, A2, h, bct, bcA, bcB, myY);
   __syncthreads();
-  run_phase<T, MODE, ORDER, DIR, 1>(a, l, da, bias, Dv, M, Kc, A2, h, bct, bcA, bcB, myY);
+  epi_prefetch<T, MODE, ORDER>(a, l, epi);
+  run_phase<T, MODE, ORDER, DIR, 1>(a, l, da, bias, Dh, M, (Kc - M) / kWin, Kc, -1, A2, h, bct, bcA, bcB, myY);
 }
 
 // Combined value of chunk position q of LDS row c (adds the spare slot at the middle token).
@@ -575,14 +590,89 @@ __device__ __forceinline__ void store8(float* p, const float (&v)[kWin]) {
 }
 
 // Outputs of one chunk from the combined LDS rows.  Row-major order: the chunk's part of each
-// channel row is cut into groups of 8 positions; the 128 threads take groups in turn (consecutive
+// channel row is cut into groups of 8 positions; the threads take groups in turn (consecutive
 // threads on consecutive groups of a row, so the 16-byte loads and stores are contiguous), and
 // each thread issues the gate loads of kEpiBatch groups before using any of them.  Column order
 // (second SS2D pair): position by position, pixel index advanced incrementally.
-constexpr int kEpiBatch = 4;
+constexpr int kEpiBatch = 8;  // kThreads * kEpiBatch >= 64 * (kKMax / 8): one batch per chunk
+
+// Gate values of the first epilogue batch, requested before the second phase so that they have
+// arrived when the epilogue starts.
+template <typename T>
+struct EpiZ {
+  Run8<T> zr[kEpiBatch];
+};
+
+// Row c and first position q of epilogue item it (items: groups of 8 positions, row-major).
+__device__ __forceinline__ void epi_item(int it, int items, int ngr, int& c, int& q) {
+  const int itc = it < items ? it : items - 1;  // clamped: loads stay in range
+  c = itc / ngr;
+  q = (itc - c * ngr) * kWin;
+}
+
+// Finish one batch of groups (first group it0, then every kThreads-th) with its gate values.
+template <typename T, int MODE>
+__device__ __forceinline__ void epi_batch(const ScanArgs& a, const float* ybuf, int ybs, int Kc, int M, int64_t base,
+                                          int items, int ngr, int it0, const Run8<T> (&zr)[kEpiBatch]) {
+  const T* zb = static_cast<const T*>(a.z);
+  T* ob = static_cast<T*>(a.out);
+#pragma unroll
+  for (int k = 0; k < kEpiBatch; ++k) {
+    if (it0 + k * kThreads >= items) break;
+    int c, q;
+    epi_item(it0 + k * kThreads, items, ngr, c, q);
+    const int64_t gi = base + static_cast<int64_t>(c) * a.L + q;
+    float v[kWin], zz[kWin];
+#pragma unroll
+    for (int j = 0; j < kWin; ++j) v[j] = row_val(ybuf, ybs, c, q + j, Kc, M);
+    if (MODE == kModeVim) {
+      zr[k].template unpack<false>(zz);
+#pragma unroll
+      for (int j = 0; j < kWin; ++j) v[j] = 0.5f * v[j] * silu_f(zz[j]);  // (y_f + y_b) / 2 * silu(z)
+      store8(ob + gi, v);
+    } else if (MODE == kModeFirstPair) {
+      store8(a.wsy + gi, v);
+    } else {
+      float w[kWin];
+      Run8<float> wr;
+      wr.load(a.wsy + gi);
+      wr.template unpack<false>(w);
+      if (zb) zr[k].template unpack<false>(zz);
+#pragma unroll
+      for (int j = 0; j < kWin; ++j) v[j] = zb ? (v[j] + w[j]) * silu_f(zz[j]) : v[j] + w[j];
+      store8(ob + gi, v);
+    }
+  }
+}
+
+template <typename T, int MODE>
+__device__ __forceinline__ void epi_load(const ScanArgs& a, int64_t base, int items, int ngr, int it0,
+                                         Run8<T> (&zr)[kEpiBatch]) {
+  const T* zb = static_cast<const T*>(a.z);
+  if (!(MODE == kModeVim || (MODE == kModeSecondPair && zb))) return;
+#pragma unroll
+  for (int k = 0; k < kEpiBatch; ++k) {
+    int c, q;
+    epi_item(it0 + k * kThreads, items, ngr, c, q);
+    zr[k].load(zb + base + static_cast<int64_t>(c) * a.L + q);
+  }
+}
 
 template <typename T, int MODE, int ORDER>
-__device__ __forceinline__ void pair_epilogue(const ScanArgs& a, const Lane& l, const float* ybuf, int ybs) {
+__device__ __forceinline__ void epi_prefetch(const ScanArgs& a, const Lane& l, EpiZ<T>& e) {
+  if (ORDER != 0 || MODE != kModeVim) return;
+  const int g_d0 = l.d - l.lane;
+  const int nch_here = a.dim - g_d0 < kW ? a.dim - g_d0 : kW;
+  const int ngr = l.Kc / kWin;
+  const int items = nch_here * ngr;
+  if (static_cast<int>(threadIdx.x) >= items) return;
+  const int64_t base = static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(g_d0) * a.L + l.s_lo;
+  epi_load<T, MODE>(a, base, items, ngr, static_cast<int>(threadIdx.x), e.zr);
+}
+
+template <typename T, int MODE, int ORDER>
+__device__ __forceinline__ void pair_epilogue(const ScanArgs& a, const Lane& l, const float* ybuf, int ybs,
+                                              const EpiZ<T>& pre) {
   const int g_d0 = l.d - l.lane;  // first channel of the group
   const int Kc = l.Kc, M = (Kc + 1) >> 1;
   const int tid = threadIdx.x;
@@ -593,42 +683,19 @@ __device__ __forceinline__ void pair_epilogue(const ScanArgs& a, const Lane& l, 
   if (ORDER == 0) {
     const int ngr = Kc / kWin;            // full groups per row
     const int items = nch_here * ngr;
-    for (int it0 = tid; it0 < items; it0 += kThreads * kEpiBatch) {
+    if (tid < items) {
+      if (MODE == kModeVim) {
+        epi_batch<T, MODE>(a, ybuf, ybs, Kc, M, base, items, ngr, tid, pre.zr);
+      } else {
+        Run8<T> zr[kEpiBatch];
+        epi_load<T, MODE>(a, base, items, ngr, tid, zr);
+        epi_batch<T, MODE>(a, ybuf, ybs, Kc, M, base, items, ngr, tid, zr);
+      }
+    }
+    for (int it0 = tid + kThreads * kEpiBatch; it0 < items; it0 += kThreads * kEpiBatch) {
       Run8<T> zr[kEpiBatch];
-      int cc[kEpiBatch], qq[kEpiBatch];
-#pragma unroll
-      for (int k = 0; k < kEpiBatch; ++k) {
-        const int it = it0 + k * kThreads;
-        const int itc = it < items ? it : items - 1;  // clamped: loads stay in range
-        cc[k] = itc / ngr;
-        qq[k] = (itc - cc[k] * ngr) * kWin;
-        if (MODE == kModeVim || (MODE == kModeSecondPair && zb)) zr[k].load(zb + base + static_cast<int64_t>(cc[k]) * a.L + qq[k]);
-      }
-#pragma unroll
-      for (int k = 0; k < kEpiBatch; ++k) {
-        if (it0 + k * kThreads >= items) break;
-        const int64_t gi = base + static_cast<int64_t>(cc[k]) * a.L + qq[k];
-        float v[kWin], zz[kWin];
-#pragma unroll
-        for (int j = 0; j < kWin; ++j) v[j] = row_val(ybuf, ybs, cc[k], qq[k] + j, Kc, M);
-        if (MODE == kModeVim) {
-          zr[k].template unpack<false>(zz);
-#pragma unroll
-          for (int j = 0; j < kWin; ++j) v[j] = 0.5f * v[j] * silu_f(zz[j]);  // (y_f + y_b) / 2 * silu(z)
-          store8(ob + gi, v);
-        } else if (MODE == kModeFirstPair) {
-          store8(a.wsy + gi, v);
-        } else {
-          float w[kWin];
-          Run8<float> wr;
-          wr.load(a.wsy + gi);
-          wr.template unpack<false>(w);
-          if (zb) zr[k].template unpack<false>(zz);
-#pragma unroll
-          for (int j = 0; j < kWin; ++j) v[j] = zb ? (v[j] + w[j]) * silu_f(zz[j]) : v[j] + w[j];
-          store8(ob + gi, v);
-        }
-      }
+      epi_load<T, MODE>(a, base, items, ngr, it0, zr);
+      epi_batch<T, MODE>(a, ybuf, ybs, Kc, M, base, items, ngr, it0, zr);
     }
     // positions past the last full group of each row
     const int rem = Kc - ngr * kWin;
@@ -667,7 +734,7 @@ __device__ __forceinline__ void pair_epilogue(const ScanArgs& a, const Lane& l, 
       }
       cp.h += dh;
       cp.w += dw;
-      if (cp.h >= cp.H) { cp.h -= cp.H; ++cp.w; }
+      while (cp.h >= cp.H) { cp.h -= cp.H; ++cp.w; }
     }
   }
 }
@@ -677,10 +744,13 @@ __global__ __launch_bounds__(kThreads) void scan_pair_kernel(ScanArgs a) {
   extern __shared__ float ybuf[];  // [kW][ybs]: combined y of the chunk
   const int ybs = (a.K + 1) | 1;   // odd row stride spreads the 64 lanes over the banks
   const Lane l = lane_ctx(a);
-  if (threadIdx.x < kW) scan_pair_dir<T, MODE, ORDER, 0>(a, l, ybuf, ybs);
-  else scan_pair_dir<T, MODE, ORDER, 1>(a, l, ybuf, ybs);
+  EpiZ<T> epi;
+  if ((__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6) & 1) == 0)
+    scan_pair_dir<T, MODE, ORDER, 0>(a, l, ybuf, ybs, epi);
+  else
+    scan_pair_dir<T, MODE, ORDER, 1>(a, l, ybuf, ybs, epi);
   __syncthreads();
-  pair_epilogue<T, MODE, ORDER>(a, l, ybuf, ybs);
+  pair_epilogue<T, MODE, ORDER>(a, l, ybuf, ybs, epi);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -704,9 +774,13 @@ int64_t plan_chunk(int64_t base, int64_t L, int64_t forced) {
   return K;
 }
 
+int64_t groups(int64_t dim) { return ceil_div(dim, kW); }
+
 size_t round256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-size_t bct_bytes(int64_t batch, int64_t L) { return round256(static_cast<size_t>(batch) * 2 * L * kBC * sizeof(float)); }
+size_t bct_bytes(int64_t batch, int64_t L) {
+  return round256(static_cast<size_t>(batch) * 2 * 2 * L * kBC * sizeof(float));
+}
 
 size_t agg_bytes(int64_t batch, int64_t dim, int64_t L, int64_t K) {
   const int64_t nch = ceil_div(L, K);
@@ -728,8 +802,8 @@ vmscan_status launch_failed(hipError_t e) {
 
 enum { kStagePrepare = 1, kStageScan = 2, kStageAll = 3 };
 
-// Stage kStagePrepare writes the fp32 B/C copy; stage kStageScan runs the chunk-state and the
-// main kernels from it.
+// Stage kStagePrepare writes the fp32 B/C copy and, for a split sequence, runs the chunk-state
+// kernel; stage kStageScan runs the main kernel.
 template <typename T, int MODE, int ORDER>
 vmscan_status run_pair(const ScanArgs& a, hipStream_t stream, int stages) {
   const int64_t nblocks = static_cast<int64_t>(a.batch) * a.nch * a.ngroups;
@@ -740,14 +814,14 @@ vmscan_status run_pair(const ScanArgs& a, hipStream_t stream, int stages) {
     hipLaunchKernelGGL(bc_transpose_kernel<T>, dim3(static_cast<unsigned>(tblocks)), dim3(kTransThreads), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return launch_failed(e);
+    if (a.nch > 1) {
+      hipLaunchKernelGGL((chunk_state_kernel<T, MODE, ORDER>), dim3(static_cast<unsigned>(nblocks)), dim3(kThreads),
+                         0, stream, a);
+      e = hipGetLastError();
+      if (e != hipSuccess) return launch_failed(e);
+    }
   }
   if (!(stages & kStageScan)) return VMSCAN_OK;
-  if (a.nch > 1) {
-    hipLaunchKernelGGL((chunk_state_kernel<T, MODE, ORDER>), dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0,
-                       stream, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return launch_failed(e);
-  }
   const size_t smem = sizeof(float) * kW * static_cast<size_t>((a.K + 1) | 1);
   hipLaunchKernelGGL((scan_pair_kernel<T, MODE, ORDER>), dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), smem,
                      stream, a);
@@ -762,13 +836,14 @@ vmscan_status run_pair_dtype(const ScanArgs& a, vmscan_dtype dtype, hipStream_t 
                              : run_pair<uint16_t, MODE, ORDER>(a, stream, stages);
 }
 
-// Validation and kernel arguments of the bidirectional scan (shared by its entry points).
-vmscan_status vim_args(ScanArgs& a, const void* u, const void* delta_raw, const void* z, const float* A_log,
-                       const float* A_b_log, const void* B, const void* C, const void* B_b, const void* C_b,
-                       const float* D, const float* D_b, const float* delta_bias, void* out, int64_t batch,
-                       int64_t dim, int64_t seqlen, int d_state, vmscan_dtype dtype, void* workspace,
-                       size_t workspace_bytes, int64_t chunk_len);
+// The workspace: may be absent when nothing is needed, else at least `need` bytes; 16-byte
+// aligned when given.
+vmscan_status check_workspace(const void* workspace, size_t workspace_bytes, size_t need) {
+  if (need > 0 && (!workspace || workspace_bytes < need)) return VMSCAN_ERR_WORKSPACE;
+  return workspace && !aligned16(workspace) ? VMSCAN_ERR_ALIGN : VMSCAN_OK;
+}
 
+// Validation and kernel arguments of the bidirectional scan (shared by its entry points).
 vmscan_status vim_args(ScanArgs& a, const void* u, const void* delta_raw, const void* z, const float* A_log,
                        const float* A_b_log, const void* B, const void* C, const void* B_b, const void* C_b,
                        const float* D, const float* D_b, const float* delta_bias, void* out, int64_t batch,
@@ -781,10 +856,10 @@ vmscan_status vim_args(ScanArgs& a, const void* u, const void* delta_raw, const 
   if (d_state != kN || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16)) return VMSCAN_ERR_UNSUPPORTED;
   for (const void* p : ptrs)
     if (!aligned16(p)) return VMSCAN_ERR_ALIGN;
-  const int64_t K = plan_chunk(batch * ceil_div(dim, kW), seqlen, chunk_len);
-  const size_t need = bct_bytes(batch, seqlen) + agg_bytes(batch, dim, seqlen, K);
-  if (!workspace || workspace_bytes < need) return VMSCAN_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return VMSCAN_ERR_ALIGN;
+  const int64_t K = plan_chunk(batch * groups(dim), seqlen, chunk_len);
+  const vmscan_status ws =
+      check_workspace(workspace, workspace_bytes, bct_bytes(batch, seqlen) + agg_bytes(batch, dim, seqlen, K));
+  if (ws != VMSCAN_OK) return ws;
   a.u = u;
   a.u_bs = dim * seqlen;
   a.z = z;
@@ -799,7 +874,7 @@ vmscan_status vim_args(ScanArgs& a, const void* u, const void* delta_raw, const 
   a.batch = static_cast<int>(batch);
   a.K = static_cast<int>(K);
   a.nch = static_cast<int>(ceil_div(seqlen, K));
-  a.ngroups = static_cast<int>(ceil_div(dim, kW));
+  a.ngroups = static_cast<int>(groups(dim));
   a.H = 1;
   a.W = static_cast<int>(seqlen);
   return VMSCAN_OK;
@@ -829,7 +904,7 @@ int vmscan_last_hip_error(void) { return g_last_hip_error; }
 
 int64_t vmscan_fwd_bidir_chunk_len(int64_t batch, int64_t dim, int64_t seqlen, int d_state) {
   if (!shape_ok(batch, dim, seqlen) || d_state != kN) return 0;
-  return plan_chunk(batch * ceil_div(dim, kW), seqlen, 0);
+  return plan_chunk(batch * groups(dim), seqlen, 0);
 }
 
 size_t vmscan_fwd_bidir_workspace_bytes_ex(int64_t batch, int64_t dim, int64_t seqlen, int d_state,
@@ -837,7 +912,7 @@ size_t vmscan_fwd_bidir_workspace_bytes_ex(int64_t batch, int64_t dim, int64_t s
   if (!shape_ok(batch, dim, seqlen) || d_state != kN || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16) ||
       chunk_len < 0)
     return 0;
-  const int64_t K = plan_chunk(batch * ceil_div(dim, kW), seqlen, chunk_len);
+  const int64_t K = plan_chunk(batch * groups(dim), seqlen, chunk_len);
   return bct_bytes(batch, seqlen) + agg_bytes(batch, dim, seqlen, K);
 }
 
@@ -886,7 +961,7 @@ size_t ss2d_cross_scan_workspace_bytes_ex(int64_t batch, int64_t dim, int64_t H,
   const int64_t L = H * W;
   if (!shape_ok(batch, dim, L) || d_state != kN || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16) || chunk_len < 0)
     return 0;
-  const int64_t K = plan_chunk(batch * ceil_div(dim, kW), L, chunk_len);
+  const int64_t K = plan_chunk(batch * groups(dim), L, chunk_len);
   const size_t img = round256(static_cast<size_t>(batch) * dim * L * sizeof(float));
   return img + bct_bytes(batch, L) + agg_bytes(batch, dim, L, K);
 }
@@ -912,10 +987,10 @@ vmscan_status ss2d_cross_scan_fwd_ex(const void* x, const void* delta_raw, const
     if (!aligned16(p)) return VMSCAN_ERR_ALIGN;
   if (z && !aligned16(z)) return VMSCAN_ERR_ALIGN;
   const size_t need = ss2d_cross_scan_workspace_bytes_ex(batch, dim, H, W, d_state, dtype, chunk_len);
-  if (!workspace || workspace_bytes < need) return VMSCAN_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return VMSCAN_ERR_ALIGN;
+  const vmscan_status ws = check_workspace(workspace, workspace_bytes, need);
+  if (ws != VMSCAN_OK) return ws;
 
-  const int64_t K = plan_chunk(batch * ceil_div(dim, kW), L, chunk_len);
+  const int64_t K = plan_chunk(batch * groups(dim), L, chunk_len);
   const size_t img = round256(static_cast<size_t>(batch) * dim * L * sizeof(float));
   unsigned char* wsp = static_cast<unsigned char*>(workspace);
 
@@ -942,7 +1017,7 @@ vmscan_status ss2d_cross_scan_fwd_ex(const void* x, const void* delta_raw, const
   a.batch = static_cast<int>(batch);
   a.K = static_cast<int>(K);
   a.nch = static_cast<int>(ceil_div(L, K));
-  a.ngroups = static_cast<int>(ceil_div(dim, kW));
+  a.ngroups = static_cast<int>(groups(dim));
   a.H = static_cast<int>(H);
   a.W = static_cast<int>(W);
 
@@ -952,7 +1027,8 @@ vmscan_status ss2d_cross_scan_fwd_ex(const void* x, const void* delta_raw, const
   vmscan_status st = run_pair_dtype<kModeFirstPair, 0>(a, dtype, stream);
   if (st != VMSCAN_OK) return st;
   // Pair 2: column-major order (direction 1) and its reverse (direction 3) -> + image -> out.
-  // Its transpose and chunk-state kernels reuse the B/C and carry regions after pair 1 (same stream).
+  // Its transpose and chunk-state kernels reuse the B/C and carry regions after pair 1 (same
+  // stream, so in order).
   a.d0 = dir_args(1, 0);
   a.d1 = dir_args(3, 1);
   return run_pair_dtype<kModeSecondPair, 1>(a, dtype, stream);

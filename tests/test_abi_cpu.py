@@ -113,6 +113,7 @@ def test_fwd_workspace(lib):
     # the workspace holds the fp32 B/C copy and, for chunked plans, the chunk carries
     need = lib.vmscan_fwd_bidir_workspace_bytes_ex(I64(2), I64(16), I64(100), 16, 1, I64(16))
     assert need == bct_bytes(2, 100) + agg_bytes(2, 16, 100, 16)
+    assert lib.vmscan_fwd_bidir_workspace_bytes_ex(I64(2), I64(16), I64(100), 16, 1, I64(100)) == bct_bytes(2, 100)
     assert _fwd(lib, _good_ptrs(), L=100, chunk=16) == ERR_WORKSPACE
     assert _fwd(lib, _good_ptrs(), L=100, chunk=16) == ERR_WORKSPACE
     assert _fwd(lib, _good_ptrs(), L=100, chunk=16, ws=0x80000, wsb=need - 1) == ERR_WORKSPACE
@@ -175,3 +176,4 @@ def test_stage_errors(lib):
         assert _stage(lib, _good_ptrs(), st, L=0) == ERR_SHAPE
         assert _stage(lib, _good_ptrs(), st, ds=32) == ERR_UNSUPPORTED
         assert _stage(lib, _good_ptrs(), st, ws=0) == ERR_WORKSPACE
+        assert _stage(lib, _good_ptrs(), st, ws=0x80008) == ERR_ALIGN
