@@ -34,8 +34,10 @@
 //    chunk's end state from a zero start and its Σ Δ; the main kernel folds the preceding
 //    chunks' pairs (Σ Δ, end state) into its initial state, exp(A Σ Δ) being a chunk's total
 //    decay, so the carry crosses workgroups without re-running the recurrence.
-//  * SS2D runs as two such bidirectional pairs over the image: (row-major, reversed row-major)
-//    writes an fp32 image, then (column-major, reversed column-major) adds its sum and stores.
+//  * SS2D runs as two such bidirectional pairs, both over contiguous rows: the column pair
+//    (column-major and its reverse) scans a transposed copy of x and writes an fp32 image in
+//    column-major order; that image is transposed, and the row pair (row-major and its reverse)
+//    adds it in its epilogue and stores.  Tiled transposes keep every access contiguous.
 //  * Workgroup ids are remapped so that the workgroups one XCD receives (the hardware deals
 //    them round-robin over 8 XCDs) are consecutive tiles of the same batch row, which then
 //    share their B/C reads in that XCD's L2.
@@ -166,7 +168,6 @@ struct ScanArgs {
   DirArgs d0, d1;  // forward and backward direction of the pair
   int64_t L;
   int dim, batch, K, nch, ngroups;
-  int H, W;        // image shape for the column order (SS2D); H = 1 otherwise
 };
 
 enum { kModeVim = 0, kModeFirstPair = 1, kModeSecondPair = 2 };
@@ -203,12 +204,40 @@ __global__ __launch_bounds__(kTransThreads) void bc_transpose_kernel(ScanArgs a)
 }
 
 // ---------------------------------------------------------------------------------------------
+// Batched 2-D transpose through an LDS tile: out[img][c][r] = in[img][r][c] for R x Cc images.
+// Reads and writes run along the contiguous dimension of their side.
+
+constexpr int kTile = 64;
+
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in, T* __restrict__ out, int R, int Cc,
+                                                        int tiles_r, int tiles_c) {
+  __shared__ T tile[kTile][kTile + 1];
+  const int64_t blk = blockIdx.x;
+  const int tc = static_cast<int>(blk % tiles_c);
+  const int tr = static_cast<int>((blk / tiles_c) % tiles_r);
+  const int64_t img = blk / (static_cast<int64_t>(tiles_c) * tiles_r);
+  const T* src = in + img * R * Cc;
+  T* dst = out + img * R * Cc;
+  const int r0 = tr * kTile, c0 = tc * kTile;
+  const int tx = threadIdx.x & (kTile - 1), ty = threadIdx.x >> 6;
+  for (int i = ty; i < kTile; i += 4) {
+    const int r = r0 + i, c = c0 + tx;
+    if (r < R && c < Cc) tile[i][tx] = src[static_cast<int64_t>(r) * Cc + c];
+  }
+  __syncthreads();
+  for (int i = ty; i < kTile; i += 4) {
+    const int c = c0 + i, r = r0 + tx;
+    if (c < Cc && r < R) dst[static_cast<int64_t>(c) * R + r] = tile[tx][i];
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // Scan kernels.  What differs between the forward and backward waves, the Vim and SS2D pairs and
 // the two scan orders is a template parameter, so the token loop has no data-dependent branches:
 //   DIR   0: step i visits chunk position i; 1: position Kc-1-i
 //   MODE  kModeVim / kModeFirstPair / kModeSecondPair (SS2D backward tensors are stored in
 //         reversed position order; the modes differ in the epilogue)
-//   ORDER 0: u element = position; 1: column-major position -> row-major pixel
 // The state half of a wave is a wave-uniform run-time value (it only selects data).
 
 struct Lane {
@@ -251,59 +280,21 @@ struct Dir {
   }
 };
 
-// Row-major pixel of a column-major position, advanced one position at a time (SS2D column
-// order: position p is pixel (p mod H, p div H)).  L < 2^31 for SS2D, so int32 suffices.
-struct ColPix {
-  int h, w, H, W;
-  __device__ __forceinline__ void init(int p, int H_, int W_) {
-    H = H_;
-    W = W_;
-    w = p / H;
-    h = p - w * H;
-  }
-  __device__ __forceinline__ int pix() const { return h * W + w; }
-  template <int SGN>
-  __device__ __forceinline__ void step() {
-    if (SGN > 0) {
-      if (++h == H) { h = 0; ++w; }
-    } else {
-      if (--h < 0) { h = H - 1; --w; }
-    }
-  }
-};
-
 // Raw u and Δ_raw of a full window of 8 steps of one direction, kept as loaded until unpacked.
-template <typename T, int MODE, int ORDER, int DIR>
+template <typename T, int MODE, int DIR>
 struct Window {
   using Dr = Dir<MODE, DIR>;
-  Run8<T> u;      // ORDER 0
-  T ug[kWin];     // ORDER 1 (gathered)
-  Run8<T> x;
+  Run8<T> u, x;
   __device__ __forceinline__ void load(const ScanArgs& a, const Lane& l, const DirArgs& da, int i0) {
     const T* ub = static_cast<const T*>(a.u) + static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(l.dd) * a.L;
     const T* db = static_cast<const T*>(da.draw) + static_cast<int64_t>(l.b) * da.draw_bs + static_cast<int64_t>(l.dd) * a.L;
     const int64_t p = Dr::pos(l, i0);
-    if (ORDER == 0) {
-      u.load(ub + (Dr::kPosSgn > 0 ? p : p - (kWin - 1)));
-    } else {
-      ColPix cp;
-      cp.init(static_cast<int>(p), a.H, a.W);
-#pragma unroll
-      for (int j = 0; j < kWin; ++j) {
-        ug[j] = ub[cp.pix()];
-        cp.template step<Dr::kPosSgn>();
-      }
-    }
+    u.load(ub + (Dr::kPosSgn > 0 ? p : p - (kWin - 1)));
     const int64_t si = Dr::sidx(a, l, i0);
     x.load(db + (Dr::kSidxSgn > 0 ? si : si - (kWin - 1)));
   }
   __device__ __forceinline__ void unpack(float (&uu)[kWin], float (&xr)[kWin]) const {
-    if (ORDER == 0) {
-      u.template unpack<(Dr::kPosSgn < 0)>(uu);
-    } else {
-#pragma unroll
-      for (int j = 0; j < kWin; ++j) uu[j] = ld_act(ug, j);
-    }
+    u.template unpack<(Dr::kPosSgn < 0)>(uu);
     x.template unpack<(Dr::kSidxSgn < 0)>(xr);
   }
 };
@@ -388,21 +379,14 @@ __device__ __forceinline__ void prep_window(const float (&uu)[kWin], const float
 // One step i outside the full windows (chunk tails): raw loads, Δ, the token update and the B/C
 // prefetch of step i + 1 into bcA.  Returns the wave's partial y (with its D·u share) and sets
 // *dl_out = Δ.
-template <typename T, int MODE, int ORDER, int DIR>
+template <typename T, int MODE, int DIR>
 __device__ __forceinline__ float single_step(const ScanArgs& a, const Lane& l, const DirArgs& da, float bias, float Dh,
                                              int i, const float (&A2)[kH], float (&h)[kH], scalar_fp bct,
                                              float (&bcA)[kBC], float* dl_out) {
   using Dr = Dir<MODE, DIR>;
   const T* ub = static_cast<const T*>(a.u) + static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(l.dd) * a.L;
   const T* db = static_cast<const T*>(da.draw) + static_cast<int64_t>(l.b) * da.draw_bs + static_cast<int64_t>(l.dd) * a.L;
-  const int64_t p = Dr::pos(l, i);
-  int64_t e = p;
-  if (ORDER == 1) {
-    ColPix cp;
-    cp.init(static_cast<int>(p), a.H, a.W);
-    e = cp.pix();
-  }
-  const float uu = ld_act(ub, e);
+  const float uu = ld_act(ub, Dr::pos(l, i));
   const float dl = softplus_f(ld_act(db, Dr::sidx(a, l, i)) + bias);
   float bcB[kBC];
   const float y = scan_token(dl, dl * uu, Dh * uu, A2, h, bcA, bcB, bct + Dr::pos(l, i + 1) * kBC);
@@ -416,7 +400,7 @@ __device__ __forceinline__ float single_step(const ScanArgs& a, const Lane& l, c
 // Pass A: per chunk, direction and state half, the end states of the chunk scanned from a zero
 // state, and Σ Δ.
 
-template <typename T, int MODE, int ORDER, int DIR>
+template <typename T, int MODE, int DIR>
 __device__ __forceinline__ void chunk_state_dir(const ScanArgs& a, const Lane& l) {
   const DirArgs& da = DIR == 0 ? a.d0 : a.d1;
   float A2[kH], h[kH];
@@ -427,7 +411,7 @@ __device__ __forceinline__ void chunk_state_dir(const ScanArgs& a, const Lane& l
   const scalar_fp bct = bc_row<DIR>(a, l);
   float S = 0.0f;
   float bcA[kBC], bcB[kBC];
-  Window<T, MODE, ORDER, DIR> win;
+  Window<T, MODE, DIR> win;
   const int full_end = (l.Kc / kWin) * kWin;
   load_bc(bct + Dir<MODE, DIR>::pos(l, 0) * kBC, bcA);
   if (full_end > 0) win.load(a, l, da, 0);
@@ -446,7 +430,7 @@ __device__ __forceinline__ void chunk_state_dir(const ScanArgs& a, const Lane& l
   }
   for (int i = full_end; i < l.Kc; ++i) {
     float dl;
-    single_step<T, MODE, ORDER, DIR>(a, l, da, bias, 0.0f, i, A2, h, bct, bcA, &dl);
+    single_step<T, MODE, DIR>(a, l, da, bias, 0.0f, i, A2, h, bct, bcA, &dl);
     S += dl;
   }
   if (l.valid) {
@@ -457,11 +441,11 @@ __device__ __forceinline__ void chunk_state_dir(const ScanArgs& a, const Lane& l
   }
 }
 
-template <typename T, int MODE, int ORDER>
+template <typename T, int MODE>
 __global__ __launch_bounds__(kThreads) void chunk_state_kernel(ScanArgs a) {
   const Lane l = lane_ctx(a);
-  if ((__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6) & 1) == 0) chunk_state_dir<T, MODE, ORDER, 0>(a, l);
-  else chunk_state_dir<T, MODE, ORDER, 1>(a, l);
+  if ((__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6) & 1) == 0) chunk_state_dir<T, MODE, 0>(a, l);
+  else chunk_state_dir<T, MODE, 1>(a, l);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -481,12 +465,12 @@ __device__ __forceinline__ void lds_first(float* slot, float v) {
   *slot = PHASE == 1 ? *slot + v : v;
 }
 
-template <typename T, int MODE, int ORDER, int DIR, int PHASE>
+template <typename T, int MODE, int DIR, int PHASE>
 __device__ __forceinline__ void run_phase(const ScanArgs& a, const Lane& l, const DirArgs& da, float bias, float Dh,
                                           int i_begin, int n_win, int i_end, int spare_step, const float (&A2)[kH],
                                           float (&h)[kH], scalar_fp bct, float (&bcA)[kBC], float (&bcB)[kBC],
                                           float* myY) {
-  Window<T, MODE, ORDER, DIR> win;
+  Window<T, MODE, DIR> win;
   const int full_end = i_begin + n_win * kWin;
   if (full_end > i_begin) win.load(a, l, da, i_begin);
   for (int i0 = i_begin; i0 < full_end; i0 += kWin) {
@@ -509,7 +493,7 @@ __device__ __forceinline__ void run_phase(const ScanArgs& a, const Lane& l, cons
   }
   for (int i = full_end; i < i_end; ++i) {
     float dl;
-    const float v = single_step<T, MODE, ORDER, DIR>(a, l, da, bias, Dh, i, A2, h, bct, bcA, &dl);
+    const float v = single_step<T, MODE, DIR>(a, l, da, bias, Dh, i, A2, h, bct, bcA, &dl);
     const int pos = i == spare_step ? l.Kc : (DIR == 0 ? i : l.Kc - 1 - i);
     if (l.half == 0) lds_first<PHASE>(myY + pos, v);
     __syncthreads();
@@ -519,10 +503,10 @@ __device__ __forceinline__ void run_phase(const ScanArgs& a, const Lane& l, cons
 
 template <typename T>
 struct EpiZ;
-template <typename T, int MODE, int ORDER>
+template <typename T, int MODE>
 __device__ __forceinline__ void epi_prefetch(const ScanArgs& a, const Lane& l, EpiZ<T>& e);
 
-template <typename T, int MODE, int ORDER, int DIR>
+template <typename T, int MODE, int DIR>
 __device__ __forceinline__ void scan_pair_dir(const ScanArgs& a, const Lane& l, float* ybuf, int ybs, EpiZ<T>& epi) {
   using Dr = Dir<MODE, DIR>;
   const DirArgs& da = DIR == 0 ? a.d0 : a.d1;
@@ -558,10 +542,10 @@ __device__ __forceinline__ void scan_pair_dir(const ScanArgs& a, const Lane& l, 
   // middle token of an odd chunk, which is then a single step of both directions.
   const int nw0 = (odd ? M - 1 : M) / kWin;
   const int spare = (DIR == 1 && odd) ? M - 1 : -1;
-  run_phase<T, MODE, ORDER, DIR, 0>(a, l, da, bias, Dh, 0, nw0, M, spare, A2, h, bct, bcA, bcB, myY);
+  run_phase<T, MODE, DIR, 0>(a, l, da, bias, Dh, 0, nw0, M, spare, A2, h, bct, bcA, bcB, myY);
   __syncthreads();
-  epi_prefetch<T, MODE, ORDER>(a, l, epi);
-  run_phase<T, MODE, ORDER, DIR, 1>(a, l, da, bias, Dh, M, (Kc - M) / kWin, Kc, -1, A2, h, bct, bcA, bcB, myY);
+  epi_prefetch<T, MODE>(a, l, epi);
+  run_phase<T, MODE, DIR, 1>(a, l, da, bias, Dh, M, (Kc - M) / kWin, Kc, -1, A2, h, bct, bcA, bcB, myY);
 }
 
 // Combined value of chunk position q of LDS row c (adds the spare slot at the middle token).
@@ -658,9 +642,9 @@ __device__ __forceinline__ void epi_load(const ScanArgs& a, int64_t base, int it
   }
 }
 
-template <typename T, int MODE, int ORDER>
+template <typename T, int MODE>
 __device__ __forceinline__ void epi_prefetch(const ScanArgs& a, const Lane& l, EpiZ<T>& e) {
-  if (ORDER != 0 || MODE != kModeVim) return;
+  if (MODE != kModeVim) return;
   const int g_d0 = l.d - l.lane;
   const int nch_here = a.dim - g_d0 < kW ? a.dim - g_d0 : kW;
   const int ngr = l.Kc / kWin;
@@ -670,7 +654,7 @@ __device__ __forceinline__ void epi_prefetch(const ScanArgs& a, const Lane& l, E
   epi_load<T, MODE>(a, base, items, ngr, static_cast<int>(threadIdx.x), e.zr);
 }
 
-template <typename T, int MODE, int ORDER>
+template <typename T, int MODE>
 __device__ __forceinline__ void pair_epilogue(const ScanArgs& a, const Lane& l, const float* ybuf, int ybs,
                                               const EpiZ<T>& pre) {
   const int g_d0 = l.d - l.lane;  // first channel of the group
@@ -680,7 +664,7 @@ __device__ __forceinline__ void pair_epilogue(const ScanArgs& a, const Lane& l, 
   const T* zb = static_cast<const T*>(a.z);
   T* ob = static_cast<T*>(a.out);
   const int64_t base = static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(g_d0) * a.L + l.s_lo;
-  if (ORDER == 0) {
+  {
     const int ngr = Kc / kWin;            // full groups per row
     const int items = nch_here * ngr;
     if (tid < items) {
@@ -713,44 +697,21 @@ __device__ __forceinline__ void pair_epilogue(const ScanArgs& a, const Lane& l, 
         st_act(ob, gi, w);
       }
     }
-  } else {
-    // pixel of position s_lo + tid, advanced by kThreads positions per iteration
-    ColPix cp;
-    cp.init(static_cast<int>(l.s_lo) + tid, a.H, a.W);
-    const int dw = kThreads / a.H, dh = kThreads - dw * a.H;
-    const int64_t rbase = static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(g_d0) * a.L;
-    for (int q = tid; q < Kc; q += kThreads) {
-      const int64_t e = cp.pix();
-      for (int c = 0; c < nch_here; ++c) {
-        const int64_t gi = rbase + static_cast<int64_t>(c) * a.L + e;
-        const float v = row_val(ybuf, ybs, c, q, Kc, M);
-        if (MODE == kModeFirstPair) {
-          a.wsy[gi] = v;
-        } else {
-          float w = v + a.wsy[gi];
-          if (zb) w *= silu_f(ld_act(zb, gi));
-          st_act(ob, gi, w);
-        }
-      }
-      cp.h += dh;
-      cp.w += dw;
-      while (cp.h >= cp.H) { cp.h -= cp.H; ++cp.w; }
-    }
   }
 }
 
-template <typename T, int MODE, int ORDER>
+template <typename T, int MODE>
 __global__ __launch_bounds__(kThreads) void scan_pair_kernel(ScanArgs a) {
   extern __shared__ float ybuf[];  // [kW][ybs]: combined y of the chunk
   const int ybs = (a.K + 1) | 1;   // odd row stride spreads the 64 lanes over the banks
   const Lane l = lane_ctx(a);
   EpiZ<T> epi;
   if ((__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6) & 1) == 0)
-    scan_pair_dir<T, MODE, ORDER, 0>(a, l, ybuf, ybs, epi);
+    scan_pair_dir<T, MODE, 0>(a, l, ybuf, ybs, epi);
   else
-    scan_pair_dir<T, MODE, ORDER, 1>(a, l, ybuf, ybs, epi);
+    scan_pair_dir<T, MODE, 1>(a, l, ybuf, ybs, epi);
   __syncthreads();
-  pair_epilogue<T, MODE, ORDER>(a, l, ybuf, ybs, epi);
+  pair_epilogue<T, MODE>(a, l, ybuf, ybs, epi);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -804,7 +765,7 @@ enum { kStagePrepare = 1, kStageScan = 2, kStageAll = 3 };
 
 // Stage kStagePrepare writes the fp32 B/C copy and, for a split sequence, runs the chunk-state
 // kernel; stage kStageScan runs the main kernel.
-template <typename T, int MODE, int ORDER>
+template <typename T, int MODE>
 vmscan_status run_pair(const ScanArgs& a, hipStream_t stream, int stages) {
   const int64_t nblocks = static_cast<int64_t>(a.batch) * a.nch * a.ngroups;
   const int64_t tblocks = static_cast<int64_t>(a.batch) * 2 * ceil_div(a.L, kTransThreads);
@@ -815,7 +776,7 @@ vmscan_status run_pair(const ScanArgs& a, hipStream_t stream, int stages) {
     e = hipGetLastError();
     if (e != hipSuccess) return launch_failed(e);
     if (a.nch > 1) {
-      hipLaunchKernelGGL((chunk_state_kernel<T, MODE, ORDER>), dim3(static_cast<unsigned>(nblocks)), dim3(kThreads),
+      hipLaunchKernelGGL((chunk_state_kernel<T, MODE>), dim3(static_cast<unsigned>(nblocks)), dim3(kThreads),
                          0, stream, a);
       e = hipGetLastError();
       if (e != hipSuccess) return launch_failed(e);
@@ -823,17 +784,51 @@ vmscan_status run_pair(const ScanArgs& a, hipStream_t stream, int stages) {
   }
   if (!(stages & kStageScan)) return VMSCAN_OK;
   const size_t smem = sizeof(float) * kW * static_cast<size_t>((a.K + 1) | 1);
-  hipLaunchKernelGGL((scan_pair_kernel<T, MODE, ORDER>), dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), smem,
+  hipLaunchKernelGGL((scan_pair_kernel<T, MODE>), dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), smem,
                      stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return launch_failed(e);
   return VMSCAN_OK;
 }
 
-template <int MODE, int ORDER>
+template <int MODE>
 vmscan_status run_pair_dtype(const ScanArgs& a, vmscan_dtype dtype, hipStream_t stream, int stages = kStageAll) {
-  return dtype == VMSCAN_F32 ? run_pair<float, MODE, ORDER>(a, stream, stages)
-                             : run_pair<uint16_t, MODE, ORDER>(a, stream, stages);
+  return dtype == VMSCAN_F32 ? run_pair<float, MODE>(a, stream, stages)
+                             : run_pair<uint16_t, MODE>(a, stream, stages);
+}
+
+// SS2D workspace: the column pair's fp32 image, its transpose, the transposed x, then the B/C copy
+// and the chunk carries shared by both pairs.
+struct Ss2dLayout {
+  size_t col_img, row_img, xt, bct, agg, total;
+};
+
+Ss2dLayout ss2d_layout(int64_t batch, int64_t dim, int64_t L, int64_t K, size_t esz) {
+  Ss2dLayout w{};
+  const size_t img = round256(static_cast<size_t>(batch) * dim * L * sizeof(float));
+  w.col_img = 0;
+  w.row_img = img;
+  w.xt = 2 * img;
+  w.bct = w.xt + round256(static_cast<size_t>(batch) * dim * L * esz);
+  w.agg = w.bct + bct_bytes(batch, L);
+  w.total = w.agg + agg_bytes(batch, dim, L, K);
+  return w;
+}
+
+// Launch the batched transpose of nimg R x Cc images of element size esz.
+vmscan_status launch_transpose(const void* in, void* out, int64_t nimg, int R, int Cc, size_t esz,
+                               hipStream_t stream) {
+  const int tr = static_cast<int>(ceil_div(R, kTile)), tc = static_cast<int>(ceil_div(Cc, kTile));
+  const int64_t blocks = nimg * tr * tc;
+  if (blocks >= (int64_t{1} << 31)) return VMSCAN_ERR_SHAPE;
+  if (esz == 4)
+    hipLaunchKernelGGL(transpose_kernel<float>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                       static_cast<const float*>(in), static_cast<float*>(out), R, Cc, tr, tc);
+  else
+    hipLaunchKernelGGL(transpose_kernel<uint16_t>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(in), static_cast<uint16_t*>(out), R, Cc, tr, tc);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? VMSCAN_OK : launch_failed(e);
 }
 
 // The workspace: may be absent when nothing is needed, else at least `need` bytes; 16-byte
@@ -875,8 +870,6 @@ vmscan_status vim_args(ScanArgs& a, const void* u, const void* delta_raw, const 
   a.K = static_cast<int>(K);
   a.nch = static_cast<int>(ceil_div(seqlen, K));
   a.ngroups = static_cast<int>(groups(dim));
-  a.H = 1;
-  a.W = static_cast<int>(seqlen);
   return VMSCAN_OK;
 }
 
@@ -942,7 +935,7 @@ vmscan_status vmscan_fwd_bidir_stage(const void* u, const void* delta_raw, const
   const vmscan_status st = vim_args(a, u, delta_raw, z, A_log, A_b_log, B, C, B_b, C_b, D, D_b, delta_bias, out, batch,
                                     dim, seqlen, d_state, dtype, workspace, workspace_bytes, chunk_len);
   if (st != VMSCAN_OK) return st;
-  return run_pair_dtype<kModeVim, 0>(a, dtype, stream, stage);
+  return run_pair_dtype<kModeVim>(a, dtype, stream, stage);
 }
 
 vmscan_status vmscan_fwd_bidir(const void* u, const void* delta_raw, const void* z, const float* A_log,
@@ -962,8 +955,7 @@ size_t ss2d_cross_scan_workspace_bytes_ex(int64_t batch, int64_t dim, int64_t H,
   if (!shape_ok(batch, dim, L) || d_state != kN || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16) || chunk_len < 0)
     return 0;
   const int64_t K = plan_chunk(batch * groups(dim), L, chunk_len);
-  const size_t img = round256(static_cast<size_t>(batch) * dim * L * sizeof(float));
-  return img + bct_bytes(batch, L) + agg_bytes(batch, dim, L, K);
+  return ss2d_layout(batch, dim, L, K, dtype == VMSCAN_F32 ? 4 : 2).total;
 }
 
 size_t ss2d_cross_scan_workspace_bytes(int64_t batch, int64_t dim, int64_t H, int64_t W, int d_state,
@@ -991,10 +983,10 @@ vmscan_status ss2d_cross_scan_fwd_ex(const void* x, const void* delta_raw, const
   if (ws != VMSCAN_OK) return ws;
 
   const int64_t K = plan_chunk(batch * groups(dim), L, chunk_len);
-  const size_t img = round256(static_cast<size_t>(batch) * dim * L * sizeof(float));
+  const size_t esz = dtype == VMSCAN_F32 ? 4 : 2;
+  const Ss2dLayout lay = ss2d_layout(batch, dim, L, K, esz);
   unsigned char* wsp = static_cast<unsigned char*>(workspace);
 
-  const size_t esz = dtype == VMSCAN_F32 ? 4 : 2;
   auto off = [&](const void* p, int64_t elems) {
     return static_cast<const void*>(static_cast<const unsigned char*>(p) + elems * static_cast<int64_t>(esz));
   };
@@ -1005,33 +997,41 @@ vmscan_status ss2d_cross_scan_fwd_ex(const void* x, const void* delta_raw, const
   };
 
   ScanArgs a{};
-  a.u = x;
   a.u_bs = dim * L;
   a.z = z;
   a.out = out;
-  a.wsy = reinterpret_cast<float*>(wsp);
-  a.bct = reinterpret_cast<float*>(wsp + img);
-  a.agg = reinterpret_cast<float*>(wsp + img + bct_bytes(batch, L));
+  a.bct = reinterpret_cast<float*>(wsp + lay.bct);
+  a.agg = reinterpret_cast<float*>(wsp + lay.agg);
   a.L = L;
   a.dim = static_cast<int>(dim);
   a.batch = static_cast<int>(batch);
   a.K = static_cast<int>(K);
   a.nch = static_cast<int>(ceil_div(L, K));
   a.ngroups = static_cast<int>(groups(dim));
-  a.H = static_cast<int>(H);
-  a.W = static_cast<int>(W);
+  const int64_t nimg = batch * dim;
 
-  // Pair 1: row-major order (direction 0) and its reverse (direction 2) -> fp32 image.
-  a.d0 = dir_args(0, 0);
-  a.d1 = dir_args(2, 1);
-  vmscan_status st = run_pair_dtype<kModeFirstPair, 0>(a, dtype, stream);
+  // Column pair (direction 1 = column-major order, direction 3 = its reverse) over the transposed
+  // image x^T [W][H], whose rows are x's columns: position p = w*H + h is x^T's element p.  It
+  // writes its combined values as an fp32 image in the same column-major order.
+  vmscan_status st = launch_transpose(x, wsp + lay.xt, nimg, static_cast<int>(H), static_cast<int>(W), esz, stream);
   if (st != VMSCAN_OK) return st;
-  // Pair 2: column-major order (direction 1) and its reverse (direction 3) -> + image -> out.
-  // Its transpose and chunk-state kernels reuse the B/C and carry regions after pair 1 (same
-  // stream, so in order).
+  a.u = wsp + lay.xt;
+  a.wsy = reinterpret_cast<float*>(wsp + lay.col_img);
   a.d0 = dir_args(1, 0);
   a.d1 = dir_args(3, 1);
-  return run_pair_dtype<kModeSecondPair, 1>(a, dtype, stream);
+  st = run_pair_dtype<kModeFirstPair>(a, dtype, stream);
+  if (st != VMSCAN_OK) return st;
+  // Back to row-major pixels, then the row pair (direction 0 and its reverse, direction 2) adds
+  // that image to its own sum, applies the optional gate and stores.  Its transpose and
+  // chunk-state kernels reuse the B/C and carry regions after the column pair (same stream).
+  st = launch_transpose(wsp + lay.col_img, wsp + lay.row_img, nimg, static_cast<int>(W), static_cast<int>(H), 4,
+                        stream);
+  if (st != VMSCAN_OK) return st;
+  a.u = x;
+  a.wsy = reinterpret_cast<float*>(wsp + lay.row_img);
+  a.d0 = dir_args(0, 0);
+  a.d1 = dir_args(2, 1);
+  return run_pair_dtype<kModeSecondPair>(a, dtype, stream);
 }
 
 vmscan_status ss2d_cross_scan_fwd(const void* x, const void* delta_raw, const float* A_log, const void* B,
