@@ -402,6 +402,8 @@ __device__ __forceinline__ float single_step(const ScanArgs& a, const Lane& l, c
 
 template <typename T, int MODE, int DIR>
 __device__ __forceinline__ void chunk_state_dir(const ScanArgs& a, const Lane& l) {
+  // The last chunk in scan order carries into nothing.
+  if (DIR == 0 ? l.c == a.nch - 1 : l.c == 0) return;
   const DirArgs& da = DIR == 0 ? a.d0 : a.d1;
   float A2[kH], h[kH];
   load_a2(da, l, A2);
