@@ -145,6 +145,19 @@ __device__ __forceinline__ int logical_block(int bid, int nblocks) {
   return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
 }
 
+// The SIMD issue arbiter favours the oldest wave, so of the scan workgroups sharing a CU the first
+// would finish well before the last, which then runs alone at a fraction of the issue rate (the
+// Vim-Ti grid is a single round of three workgroups per CU).  Rotating the waves' priority every
+// window across workgroups makes them progress evenly and finish together.  `step` counts
+// windows; co-resident workgroups differ in blockIdx / 256.  (The chunk-state pass runs many
+// rounds of workgroups and is faster with the default order.)
+__device__ __forceinline__ void rotate_priority(int step) {
+  const int pr = (static_cast<int>(blockIdx.x >> 8) + step) % 3;
+  if (pr == 0) __builtin_amdgcn_s_setprio(0);
+  else if (pr == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(2);
+}
+
 struct DirArgs {
   const void* draw;    // Δ_raw; element (b, d, idx) at b*draw_bs + d*L + idx
   int64_t draw_bs;
@@ -455,40 +468,62 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(ScanArgs a) {
 // Phase 0 (steps [0, M)) stores each direction's y, including its D·u term, in the channel's LDS
 // row at the chunk positions; phase 1 (steps [M, Kc)) adds it to the other direction's stored
 // value.  Within a direction the lower-half wave writes (phase 0) or adds (phase 1) first and,
-// after a workgroup barrier, the upper-half wave adds.  Both directions run the same sequence of
-// windows and single steps, so all four waves meet the same barriers.  For an odd chunk both
+// once it has signalled that unit, the upper-half wave adds; one workgroup barrier separates the
+// phases and one precedes the epilogue.  For an odd chunk both
 // directions reach the middle token at their last phase-0 step; the backward value of that step
 // goes to the spare slot Kc.  After both phases every row holds y_f + y_b.
 
 // LDS update of one value: the lower half writes (PHASE 0) or adds (PHASE 1); then, after the
-// barrier that the caller places between them, the upper half adds.
+// lower half has signalled the unit, the upper half adds.
 template <int PHASE>
 __device__ __forceinline__ void lds_first(float* slot, float v) {
   *slot = PHASE == 1 ? *slot + v : v;
+}
+
+// Pairwise ordering of the two state halves of one direction, without a workgroup barrier: the
+// lower-half wave publishes the number of the last combine unit it has written to the LDS rows,
+// and the upper-half wave waits for it before adding.  A wave's LDS operations execute in issue
+// order, so the data writes are complete when the flag write is, and the compiler barriers keep
+// the instructions in that order.  The lower half never waits, so the wait always ends; the
+// bound only keeps a mistake from turning into a hang.
+__device__ __forceinline__ void unit_signal(int* flag, int unit) {
+  asm volatile("" ::: "memory");
+  __hip_atomic_store(flag, unit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+__device__ __forceinline__ void unit_wait(int* flag, int unit) {
+  for (int n = 0; n < (1 << 22); ++n) {
+    if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) >= unit)
+      break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");
 }
 
 template <typename T, int MODE, int DIR, int PHASE>
 __device__ __forceinline__ void run_phase(const ScanArgs& a, const Lane& l, const DirArgs& da, float bias, float Dh,
                                           int i_begin, int n_win, int i_end, int spare_step, const float (&A2)[kH],
                                           float (&h)[kH], scalar_fp bct, float (&bcA)[kBC], float (&bcB)[kBC],
-                                          float* myY) {
+                                          float* myY, int* flag, int& unit) {
   Window<T, MODE, DIR> win;
   const int full_end = i_begin + n_win * kWin;
   if (full_end > i_begin) win.load(a, l, da, i_begin);
   for (int i0 = i_begin; i0 < full_end; i0 += kWin) {
     float uu[kWin], xr[kWin], dl[kWin], du[kWin], yi[kWin], y[kWin];
+    rotate_priority(i0 / kWin);
     win.unpack(uu, xr);
     __builtin_amdgcn_sched_barrier(0);  // see chunk_state_dir
     win.load(a, l, da, i0 + kWin < full_end ? i0 + kWin : i0);
     prep_window(uu, xr, bias, Dh, dl, du, yi);
     run_steps<MODE, DIR>(l, i0, dl, du, yi, A2, h, bcA, bcB, bct, y);
     const int p0 = DIR == 0 ? i0 : l.Kc - 1 - i0;  // chunk position of step i0
+    ++unit;
     if (l.half == 0) {
 #pragma unroll
       for (int j = 0; j < kWin; ++j) lds_first<PHASE>(myY + p0 + (DIR == 0 ? j : -j), y[j]);
-    }
-    __syncthreads();
-    if (l.half == 1) {
+      unit_signal(flag, unit);
+    } else {
+      unit_wait(flag, unit);
 #pragma unroll
       for (int j = 0; j < kWin; ++j) myY[p0 + (DIR == 0 ? j : -j)] += y[j];
     }
@@ -497,9 +532,14 @@ __device__ __forceinline__ void run_phase(const ScanArgs& a, const Lane& l, cons
     float dl;
     const float v = single_step<T, MODE, DIR>(a, l, da, bias, Dh, i, A2, h, bct, bcA, &dl);
     const int pos = i == spare_step ? l.Kc : (DIR == 0 ? i : l.Kc - 1 - i);
-    if (l.half == 0) lds_first<PHASE>(myY + pos, v);
-    __syncthreads();
-    if (l.half == 1) myY[pos] += v;
+    ++unit;
+    if (l.half == 0) {
+      lds_first<PHASE>(myY + pos, v);
+      unit_signal(flag, unit);
+    } else {
+      unit_wait(flag, unit);
+      myY[pos] += v;
+    }
   }
 }
 
@@ -509,7 +549,8 @@ template <typename T, int MODE>
 __device__ __forceinline__ void epi_prefetch(const ScanArgs& a, const Lane& l, EpiZ<T>& e);
 
 template <typename T, int MODE, int DIR>
-__device__ __forceinline__ void scan_pair_dir(const ScanArgs& a, const Lane& l, float* ybuf, int ybs, EpiZ<T>& epi) {
+__device__ __forceinline__ void scan_pair_dir(const ScanArgs& a, const Lane& l, float* ybuf, int ybs, int* flag,
+                                              EpiZ<T>& epi) {
   using Dr = Dir<MODE, DIR>;
   const DirArgs& da = DIR == 0 ? a.d0 : a.d1;
   const int Kc = l.Kc;
@@ -544,10 +585,11 @@ __device__ __forceinline__ void scan_pair_dir(const ScanArgs& a, const Lane& l, 
   // middle token of an odd chunk, which is then a single step of both directions.
   const int nw0 = (odd ? M - 1 : M) / kWin;
   const int spare = (DIR == 1 && odd) ? M - 1 : -1;
-  run_phase<T, MODE, DIR, 0>(a, l, da, bias, Dh, 0, nw0, M, spare, A2, h, bct, bcA, bcB, myY);
+  int unit = 0;
+  run_phase<T, MODE, DIR, 0>(a, l, da, bias, Dh, 0, nw0, M, spare, A2, h, bct, bcA, bcB, myY, flag, unit);
   __syncthreads();
   epi_prefetch<T, MODE>(a, l, epi);
-  run_phase<T, MODE, DIR, 1>(a, l, da, bias, Dh, M, (Kc - M) / kWin, Kc, -1, A2, h, bct, bcA, bcB, myY);
+  run_phase<T, MODE, DIR, 1>(a, l, da, bias, Dh, M, (Kc - M) / kWin, Kc, -1, A2, h, bct, bcA, bcB, myY, flag, unit);
 }
 
 // Combined value of chunk position q of LDS row c (adds the spare slot at the middle token).
@@ -705,13 +747,16 @@ __device__ __forceinline__ void pair_epilogue(const ScanArgs& a, const Lane& l, 
 template <typename T, int MODE>
 __global__ __launch_bounds__(kThreads) void scan_pair_kernel(ScanArgs a) {
   extern __shared__ float ybuf[];  // [kW][ybs]: combined y of the chunk
+  __shared__ int unit_flag[2];     // per direction: last combine unit the lower half has written
   const int ybs = (a.K + 1) | 1;   // odd row stride spreads the 64 lanes over the banks
   const Lane l = lane_ctx(a);
+  if (threadIdx.x < 2) unit_flag[threadIdx.x] = 0;
+  __syncthreads();
   EpiZ<T> epi;
   if ((__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6) & 1) == 0)
-    scan_pair_dir<T, MODE, 0>(a, l, ybuf, ybs, epi);
+    scan_pair_dir<T, MODE, 0>(a, l, ybuf, ybs, &unit_flag[0], epi);
   else
-    scan_pair_dir<T, MODE, 1>(a, l, ybuf, ybs, epi);
+    scan_pair_dir<T, MODE, 1>(a, l, ybuf, ybs, &unit_flag[1], epi);
   __syncthreads();
   pair_epilogue<T, MODE>(a, l, ybuf, ybs, epi);
 }
