@@ -245,6 +245,58 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in
   }
 }
 
+// The same for 2-byte elements, moved in pairs: each lane reads two neighbouring columns of a row
+// and writes two neighbouring rows of a column as one 32-bit access.
+__global__ __launch_bounds__(256) void transpose16_kernel(const uint16_t* __restrict__ in, uint16_t* __restrict__ out,
+                                                          int R, int Cc, int tiles_r, int tiles_c) {
+  __shared__ uint16_t tile[kTile][kTile + 2];
+  const int64_t blk = blockIdx.x;
+  const int tc = static_cast<int>(blk % tiles_c);
+  const int tr = static_cast<int>((blk / tiles_c) % tiles_r);
+  const int64_t img = blk / (static_cast<int64_t>(tiles_c) * tiles_r);
+  const int64_t base = img * R * Cc;  // element offset of the image; pairs need an even total offset
+  const uint16_t* src = in + base;
+  uint16_t* dst = out + base;
+  const int r0 = tr * kTile, c0 = tc * kTile;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 pairs x 8 rows per pass
+  for (int i = ty; i < kTile; i += 8) {
+    const int r = r0 + i, c = c0 + 2 * tx;
+    if (r < R) {
+      if (c + 1 < Cc) {
+        const int64_t e = static_cast<int64_t>(r) * Cc + c;
+        if (((base + e) & 1) == 0) {
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(src + e);
+          tile[i][2 * tx] = static_cast<uint16_t>(w & 0xffffu);
+          tile[i][2 * tx + 1] = static_cast<uint16_t>(w >> 16);
+        } else {
+          tile[i][2 * tx] = src[e];
+          tile[i][2 * tx + 1] = src[e + 1];
+        }
+      } else if (c < Cc) {
+        tile[i][2 * tx] = src[static_cast<int64_t>(r) * Cc + c];
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = ty; i < kTile; i += 8) {
+    const int c = c0 + i, r = r0 + 2 * tx;
+    if (c < Cc) {
+      const int64_t e = static_cast<int64_t>(c) * R + r;
+      if (r + 1 < R) {
+        if (((base + e) & 1) == 0) {
+          *reinterpret_cast<uint32_t*>(dst + e) = static_cast<uint32_t>(tile[2 * tx][i]) |
+                                                   (static_cast<uint32_t>(tile[2 * tx + 1][i]) << 16);
+        } else {
+          dst[e] = tile[2 * tx][i];
+          dst[e + 1] = tile[2 * tx + 1][i];
+        }
+      } else if (r < R) {
+        dst[e] = tile[2 * tx][i];
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // Scan kernels.  What differs between the forward and backward waves, the Vim and SS2D pairs and
 // the two scan orders is a template parameter, so the token loop has no data-dependent branches:
@@ -872,7 +924,7 @@ vmscan_status launch_transpose(const void* in, void* out, int64_t nimg, int R, i
     hipLaunchKernelGGL(transpose_kernel<float>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
                        static_cast<const float*>(in), static_cast<float*>(out), R, Cc, tr, tc);
   else
-    hipLaunchKernelGGL(transpose_kernel<uint16_t>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+    hipLaunchKernelGGL(transpose16_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(in), static_cast<uint16_t*>(out), R, Cc, tr, tc);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? VMSCAN_OK : launch_failed(e);

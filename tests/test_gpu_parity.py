@@ -126,8 +126,9 @@ def test_config3_full_sampled():
     _report("config 3 (1248px bf16 B8 D384 L6085, batches 0,5)", O.rel_err(run_vim(p)[bsel], oracle_vim(p, batches=bsel)), 2e-2)
 
 
+# the last two span several 64 x 64 transpose tiles, with ragged and odd-sized images
 SS2D_SHAPES = [(1, 16, 1, 1), (2, 5, 1, 7), (1, 17, 7, 1), (2, 16, 3, 4), (1, 20, 7, 9), (1, 16, 16, 16), (2, 3, 5, 13),
-               (1, 16, 23, 19)]
+               (1, 16, 23, 19), (1, 4, 67, 70), (2, 3, 129, 3)]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
