@@ -59,7 +59,9 @@ constexpr int kWin = 8;                // tokens per register window
 constexpr int kBC = 2 * kH;            // floats per (position, half) in the B/C copy: 8 B, 8 C
 constexpr int kKMax = 206;             // longest LDS row: 3 workgroups of 64 x 207 floats per CU
 constexpr int kMinChunk = 32;          // shortest chunk the planner picks
-constexpr int kTargetBlocks = 768;     // planner: enough workgroups for one full round
+constexpr int kTargetBlocks = 768;     // planner: three workgroups on each of 256 CUs
+constexpr int kKSplit = 159;           // split sequences: chunks of <= 159 positions, four workgroups per CU
+constexpr int kSplitSlots = 1024;      // ... so a round is four workgroups on each of 256 CUs
 constexpr int kAggStride = kN + 1;     // per chunk: 16 end states + Σ Δ
 constexpr int kTransThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -515,6 +517,43 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(ScanArgs a) {
   else chunk_state_dir<T, MODE, 1>(a, l);
 }
 
+// Carry prefix: per (batch, channel, direction, state), walk the chunks in scan order and replace
+// each chunk's record (end state from a zero start, Σ Δ) by the state entering that chunk:
+//   h_in(first) = 0,  h_in(next) = exp(A Σ Δ) h_in + h_end,
+// exp(A Σ Δ) being the chunk's total decay.  One thread per (batch, channel, direction, state).
+__global__ __launch_bounds__(256) void carry_prefix_kernel(ScanArgs a) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t total = static_cast<int64_t>(a.batch) * a.dim * 2 * kN;
+  if (t >= total) return;
+  const int n = static_cast<int>(t % kN);
+  const int dir = static_cast<int>((t / kN) & 1);
+  const int64_t bd = t / (2 * kN);  // b * dim + d
+  const int d = static_cast<int>(bd % a.dim);
+  const DirArgs& da = dir == 0 ? a.d0 : a.d1;
+  const float A2 = -__expf(da.A_log[static_cast<int64_t>(d) * kN + n]) * kLog2e;
+  float* rec = a.agg + (bd * 2 + dir) * a.nch * kAggStride;
+  float h = 0.0f;
+  // eight chunks at a time: all their loads are in flight before the dependent updates
+  for (int k0 = 0; k0 < a.nch; k0 += 8) {
+    float hend[8], S[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int k = k0 + j < a.nch ? k0 + j : a.nch - 1;
+      const float* e = rec + (dir == 0 ? k : a.nch - 1 - k) * kAggStride;
+      hend[j] = e[n];
+      S[j] = e[kN];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int k = k0 + j;
+      if (k < a.nch) {
+        rec[(dir == 0 ? k : a.nch - 1 - k) * kAggStride + n] = h;
+        if (k + 1 < a.nch) h = __builtin_fmaf(__builtin_amdgcn_exp2f(A2 * S[j]), h, hend[j]);
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // Main pass: fused bidirectional scan of one chunk with meet-in-the-middle combination.
 // Phase 0 (steps [0, M)) stores each direction's y, including its D·u term, in the channel's LDS
@@ -616,16 +655,12 @@ __device__ __forceinline__ void scan_pair_dir(const ScanArgs& a, const Lane& l, 
   const float bias = da.bias[l.dd];
   const float Dh = l.half == 0 ? da.Dp[l.dd] : 0.0f;  // the lower half adds the D·u term
 
-  // Carry-in: fold the preceding chunks' (Σ Δ, end state) pairs in scan order.
+  // Carry-in: the state entering this chunk, which the carry-prefix kernel left in the chunk's
+  // carry record.
   if (a.nch > 1) {
-    const float* ag = a.agg + ((static_cast<int64_t>(l.b) * a.dim + l.dd) * 2 + DIR) * a.nch * kAggStride;
-    const int cnt = DIR == 0 ? l.c : a.nch - 1 - l.c;
-    for (int k = 0; k < cnt; ++k) {
-      const float* e = ag + (DIR == 0 ? k : a.nch - 1 - k) * kAggStride;
-      const float S = e[kN];
+    const float* e = a.agg + ((((static_cast<int64_t>(l.b) * a.dim + l.dd) * 2 + DIR) * a.nch) + l.c) * kAggStride;
 #pragma unroll
-      for (int n = 0; n < kH; ++n) h[n] = __builtin_fmaf(__builtin_amdgcn_exp2f(A2[n] * S), h[n], e[kH * l.half + n]);
-    }
+    for (int n = 0; n < kH; ++n) h[n] = e[kH * l.half + n];
   }
 
   const scalar_fp bct = bc_row<DIR>(a, l);
@@ -826,9 +861,13 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t plan_chunk(int64_t base, int64_t L, int64_t forced) {
   if (forced > 0) return forced < kKMax ? (forced < L ? forced : L) : (kKMax < L ? kKMax : L);
   if (L <= kKMax && (base >= kTargetBlocks / 2 || L <= kMinChunk)) return L;
-  int64_t nch = ceil_div(L, kKMax);
-  const int64_t want = ceil_div(kTargetBlocks, base);
+  // Split: chunks of at most kKSplit positions (four workgroups per CU), at least one full round of
+  // kSplitSlots workgroups, and the chunk count raised to fill the last round.
+  int64_t nch = ceil_div(L, kKSplit);
+  const int64_t want = ceil_div(kSplitSlots, base);
   if (want > nch) nch = want;
+  const int64_t fill = ceil_div(base * nch, kSplitSlots) * kSplitSlots / base;
+  if (fill > nch && ceil_div(L, fill) >= kMinChunk) nch = fill;
   int64_t K = ceil_div(L, nch);
   if (K < kMinChunk) K = kMinChunk < L ? kMinChunk : L;
   return K;
@@ -877,6 +916,10 @@ vmscan_status run_pair(const ScanArgs& a, hipStream_t stream, int stages) {
     if (a.nch > 1) {
       hipLaunchKernelGGL((chunk_state_kernel<T, MODE>), dim3(static_cast<unsigned>(nblocks)), dim3(kThreads),
                          0, stream, a);
+      e = hipGetLastError();
+      if (e != hipSuccess) return launch_failed(e);
+      const int64_t pblocks = ceil_div(static_cast<int64_t>(a.batch) * a.dim * 2 * kN, 256);
+      hipLaunchKernelGGL(carry_prefix_kernel, dim3(static_cast<unsigned>(pblocks)), dim3(256), 0, stream, a);
       e = hipGetLastError();
       if (e != hipSuccess) return launch_failed(e);
     }
