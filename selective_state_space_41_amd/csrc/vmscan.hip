@@ -60,7 +60,7 @@ constexpr int kBC = 2 * kH;            // floats per (position, half) in the B/C
 constexpr int kKMax = 206;             // longest LDS row: 3 workgroups of 64 x 207 floats per CU
 constexpr int kMinChunk = 32;          // shortest chunk the planner picks
 constexpr int kTargetBlocks = 768;     // planner: three workgroups on each of 256 CUs
-constexpr int kKSplit = 159;           // split sequences: chunks of <= 159 positions, four workgroups per CU
+constexpr int kKSplit = 158;           // split sequences: chunks of <= 158 positions (LDS rows of 159), four workgroups per CU
 constexpr int kSplitSlots = 1024;      // ... so a round is four workgroups on each of 256 CUs
 constexpr int kAggStride = kN + 1;     // per chunk: 16 end states + Σ Δ
 constexpr int kTransThreads = 256;
@@ -562,7 +562,8 @@ __global__ __launch_bounds__(256) void carry_prefix_kernel(ScanArgs a) {
 // once it has signalled that unit, the upper-half wave adds; one workgroup barrier separates the
 // phases and one precedes the epilogue.  For an odd chunk both
 // directions reach the middle token at their last phase-0 step; the backward value of that step
-// goes to the spare slot Kc.  After both phases every row holds y_f + y_b.
+// goes to the spare slot Kc, which the backward lower-half wave folds into the middle slot after
+// the phase barrier.  After both phases every row holds y_f + y_b.
 
 // LDS update of one value: the lower half writes (PHASE 0) or adds (PHASE 1); then, after the
 // lower half has signalled the unit, the upper half adds.
@@ -598,26 +599,53 @@ __device__ __forceinline__ void run_phase(const ScanArgs& a, const Lane& l, cons
                                           float* myY, int* flag, int& unit) {
   Window<T, MODE, DIR> win;
   const int full_end = i_begin + n_win * kWin;
+  constexpr int kStep = DIR == 0 ? 1 : -1;  // LDS row direction of consecutive steps
   if (full_end > i_begin) win.load(a, l, da, i_begin);
+  // Lower half: in the second phase its slots already hold the other direction's values, which
+  // are read before the window's arithmetic and added after it.  Upper half: the add of window w
+  // waits for the lower half's unit w and is done while window w + 1 is prepared, so its LDS
+  // reads overlap the Δ arithmetic instead of stalling the wave.
+  const bool lo = l.half == 0;
+  float yp[kWin];
+  int pp = -1;  // upper half: chunk position of the pending window's first step, -1 when none
   for (int i0 = i_begin; i0 < full_end; i0 += kWin) {
-    float uu[kWin], xr[kWin], dl[kWin], du[kWin], yi[kWin], y[kWin];
+    float uu[kWin], xr[kWin], dl[kWin], du[kWin], yi[kWin], y[kWin], r[kWin];
     rotate_priority(i0 / kWin);
     win.unpack(uu, xr);
     __builtin_amdgcn_sched_barrier(0);  // see chunk_state_dir
     win.load(a, l, da, i0 + kWin < full_end ? i0 + kWin : i0);
-    prep_window(uu, xr, bias, Dh, dl, du, yi);
-    run_steps<MODE, DIR>(l, i0, dl, du, yi, A2, h, bcA, bcB, bct, y);
     const int p0 = DIR == 0 ? i0 : l.Kc - 1 - i0;  // chunk position of step i0
-    ++unit;
-    if (l.half == 0) {
+    if (lo) {
+      if (PHASE == 1) {
 #pragma unroll
-      for (int j = 0; j < kWin; ++j) lds_first<PHASE>(myY + p0 + (DIR == 0 ? j : -j), y[j]);
-      unit_signal(flag, unit);
-    } else {
+        for (int j = 0; j < kWin; ++j) r[j] = myY[p0 + kStep * j];
+      }
+    } else if (pp >= 0) {
       unit_wait(flag, unit);
 #pragma unroll
-      for (int j = 0; j < kWin; ++j) myY[p0 + (DIR == 0 ? j : -j)] += y[j];
+      for (int j = 0; j < kWin; ++j) r[j] = myY[pp + kStep * j];
     }
+    prep_window(uu, xr, bias, Dh, dl, du, yi);
+    if (!lo && pp >= 0) {
+#pragma unroll
+      for (int j = 0; j < kWin; ++j) myY[pp + kStep * j] = r[j] + yp[j];
+    }
+    run_steps<MODE, DIR>(l, i0, dl, du, yi, A2, h, bcA, bcB, bct, y);
+    ++unit;
+    if (lo) {
+#pragma unroll
+      for (int j = 0; j < kWin; ++j) myY[p0 + kStep * j] = PHASE == 1 ? r[j] + y[j] : y[j];
+      unit_signal(flag, unit);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kWin; ++j) yp[j] = y[j];
+      pp = p0;
+    }
+  }
+  if (!lo && pp >= 0) {
+    unit_wait(flag, unit);
+#pragma unroll
+    for (int j = 0; j < kWin; ++j) myY[pp + kStep * j] += yp[j];
   }
   for (int i = full_end; i < i_end; ++i) {
     float dl;
@@ -675,16 +703,15 @@ __device__ __forceinline__ void scan_pair_dir(const ScanArgs& a, const Lane& l, 
   int unit = 0;
   run_phase<T, MODE, DIR, 0>(a, l, da, bias, Dh, 0, nw0, M, spare, A2, h, bct, bcA, bcB, myY, flag, unit);
   __syncthreads();
+  // Fold the backward value of an odd chunk's middle token (kept in the spare slot) into the
+  // middle slot; no wave touches either slot in the second phase.
+  if (DIR == 1 && odd && l.half == 0) myY[M - 1] += myY[Kc];
   epi_prefetch<T, MODE>(a, l, epi);
   run_phase<T, MODE, DIR, 1>(a, l, da, bias, Dh, M, (Kc - M) / kWin, Kc, -1, A2, h, bct, bcA, bcB, myY, flag, unit);
 }
 
-// Combined value of chunk position q of LDS row c (adds the spare slot at the middle token).
-__device__ __forceinline__ float row_val(const float* ybuf, int ybs, int c, int q, int Kc, int M) {
-  float v = ybuf[c * ybs + q];
-  if ((Kc & 1) && q == M - 1) v += ybuf[c * ybs + Kc];
-  return v;
-}
+// Combined value of chunk position q of LDS row c.
+__device__ __forceinline__ float row_val(const float* ybuf, int ybs, int c, int q) { return ybuf[c * ybs + q]; }
 
 template <typename T>
 __device__ __forceinline__ void store8(T* p, const float (&v)[kWin]);
@@ -727,7 +754,7 @@ __device__ __forceinline__ void epi_item(int it, int items, int ngr, int& c, int
 
 // Finish one batch of groups (first group it0, then every kThreads-th) with its gate values.
 template <typename T, int MODE>
-__device__ __forceinline__ void epi_batch(const ScanArgs& a, const float* ybuf, int ybs, int Kc, int M, int64_t base,
+__device__ __forceinline__ void epi_batch(const ScanArgs& a, const float* ybuf, int ybs, int64_t base,
                                           int items, int ngr, int it0, const Run8<T> (&zr)[kEpiBatch]) {
   const T* zb = static_cast<const T*>(a.z);
   T* ob = static_cast<T*>(a.out);
@@ -739,7 +766,7 @@ __device__ __forceinline__ void epi_batch(const ScanArgs& a, const float* ybuf, 
     const int64_t gi = base + static_cast<int64_t>(c) * a.L + q;
     float v[kWin], zz[kWin];
 #pragma unroll
-    for (int j = 0; j < kWin; ++j) v[j] = row_val(ybuf, ybs, c, q + j, Kc, M);
+    for (int j = 0; j < kWin; ++j) v[j] = row_val(ybuf, ybs, c, q + j);
     if (MODE == kModeVim) {
       zr[k].template unpack<false>(zz);
 #pragma unroll
@@ -789,7 +816,7 @@ template <typename T, int MODE>
 __device__ __forceinline__ void pair_epilogue(const ScanArgs& a, const Lane& l, const float* ybuf, int ybs,
                                               const EpiZ<T>& pre) {
   const int g_d0 = l.d - l.lane;  // first channel of the group
-  const int Kc = l.Kc, M = (Kc + 1) >> 1;
+  const int Kc = l.Kc;
   const int tid = threadIdx.x;
   const int nch_here = a.dim - g_d0 < kW ? a.dim - g_d0 : kW;
   const T* zb = static_cast<const T*>(a.z);
@@ -800,24 +827,24 @@ __device__ __forceinline__ void pair_epilogue(const ScanArgs& a, const Lane& l, 
     const int items = nch_here * ngr;
     if (tid < items) {
       if (MODE == kModeVim) {
-        epi_batch<T, MODE>(a, ybuf, ybs, Kc, M, base, items, ngr, tid, pre.zr);
+        epi_batch<T, MODE>(a, ybuf, ybs, base, items, ngr, tid, pre.zr);
       } else {
         Run8<T> zr[kEpiBatch];
         epi_load<T, MODE>(a, base, items, ngr, tid, zr);
-        epi_batch<T, MODE>(a, ybuf, ybs, Kc, M, base, items, ngr, tid, zr);
+        epi_batch<T, MODE>(a, ybuf, ybs, base, items, ngr, tid, zr);
       }
     }
     for (int it0 = tid + kThreads * kEpiBatch; it0 < items; it0 += kThreads * kEpiBatch) {
       Run8<T> zr[kEpiBatch];
       epi_load<T, MODE>(a, base, items, ngr, it0, zr);
-      epi_batch<T, MODE>(a, ybuf, ybs, Kc, M, base, items, ngr, it0, zr);
+      epi_batch<T, MODE>(a, ybuf, ybs, base, items, ngr, it0, zr);
     }
     // positions past the last full group of each row
     const int rem = Kc - ngr * kWin;
     for (int it = tid; it < nch_here * rem; it += kThreads) {
       const int c = it / rem, q = ngr * kWin + (it - (it / rem) * rem);
       const int64_t gi = base + static_cast<int64_t>(c) * a.L + q;
-      const float v = row_val(ybuf, ybs, c, q, Kc, M);
+      const float v = row_val(ybuf, ybs, c, q);
       if (MODE == kModeVim) {
         st_act(ob, gi, 0.5f * v * silu_f(ld_act(zb, gi)));
       } else if (MODE == kModeFirstPair) {

@@ -128,6 +128,12 @@ def test_workspace_queries(lib):
     assert 32 <= K <= 206
     assert lib.vmscan_fwd_bidir_workspace_bytes(I64(8), I64(384), I64(6085), 16, 1) == \
         bct_bytes(8, 6085) + agg_bytes(8, 384, 6085, K)
+    # split plans use LDS rows of at most 159 floats, so that four workgroups fit one CU's 160 KiB
+    for nb, nd, L in [(8, 384, 6085), (32, 512, 3136), (1, 384, 197), (2, 64, 1000), (4, 768, 4097), (16, 384, 207)]:
+        K = lib.vmscan_fwd_bidir_chunk_len(I64(nb), I64(nd), I64(L), 16)
+        assert 1 <= K <= min(L, 206)
+        if K < L:
+            assert K <= 158 and 4 * 64 * ((K + 1) | 1) * 4 <= 160 * 1024 - 4 * 64
     img = 32 * 512 * 3136 * 4
     assert lib.ss2d_cross_scan_workspace_bytes(I64(32), I64(512), I64(56), I64(56), 16, 1) >= img
     assert lib.ss2d_cross_scan_workspace_bytes(I64(32), I64(512), I64(0), I64(56), 16, 1) == 0
