@@ -463,12 +463,43 @@ __device__ __forceinline__ float single_step(const ScanArgs& a, const Lane& l, c
   return y;
 }
 
+// Pairwise ordering of the two state halves of one direction, without a workgroup barrier: the
+// lower-half wave publishes the number of the last combine unit it has written to the LDS rows,
+// and the upper-half wave waits for it before adding.  A wave's LDS operations execute in issue
+// order, so the data writes are complete when the flag write is, and the compiler barriers keep
+// the instructions in that order.  The lower half never waits, so the wait always ends; the
+// bound only keeps a mistake from turning into a hang.
+__device__ __forceinline__ void unit_signal(int* flag, int unit) {
+  asm volatile("" ::: "memory");
+  __hip_atomic_store(flag, unit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+__device__ __forceinline__ void unit_wait(int* flag, int unit) {
+  for (int n = 0; n < (1 << 22); ++n) {
+    if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) >= unit)
+      break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------------------------
 // Pass A: per chunk, direction and state half, the end states of the chunk scanned from a zero
 // state, and Σ Δ.
 
-template <typename T, int MODE, int DIR>
-__device__ __forceinline__ void chunk_state_dir(const ScanArgs& a, const Lane& l) {
+// Δ and Δ·u exchange between the two state halves of a direction: each wave computes them for
+// half of a window's steps and reads the other half from its partner, so softplus is evaluated
+// once per (channel, step) instead of once per wave.  Double-buffered by window parity; a wave
+// overwrites a buffer only after its partner has published the next window, which it does only
+// after reading that buffer.
+constexpr int kXHalf = kWin / 2;
+struct ChunkXchg {
+  float v[2][2][2][2][kW][kXHalf];  // [dir][window parity][half][Δ, Δ·u][lane][step]
+  int prod[2][2];                   // [dir][half]: windows published
+};
+
+template <typename T, int MODE, int DIR, int HALF>
+__device__ __forceinline__ void chunk_state_dir(const ScanArgs& a, const Lane& l, ChunkXchg& xc) {
   // The last chunk in scan order carries into nothing.
   if (DIR == 0 ? l.c == a.nch - 1 : l.c == 0) return;
   const DirArgs& da = DIR == 0 ? a.d0 : a.d1;
@@ -482,19 +513,46 @@ __device__ __forceinline__ void chunk_state_dir(const ScanArgs& a, const Lane& l
   float bcA[kBC], bcB[kBC];
   Window<T, MODE, DIR> win;
   const int full_end = (l.Kc / kWin) * kWin;
+  constexpr int me = HALF, other = 1 - HALF;
   load_bc(bct + Dir<MODE, DIR>::pos(l, 0) * kBC, bcA);
   if (full_end > 0) win.load(a, l, da, 0);
-  for (int i0 = 0; i0 < full_end; i0 += kWin) {
-    float uu[kWin], xr[kWin], dl[kWin], du[kWin], yi[kWin], y[kWin];
+  int w = 0;
+  for (int i0 = 0; i0 < full_end; i0 += kWin, ++w) {
+    float uu[kWin], xr[kWin], dl[kWin], du[kWin], y[kWin];
     win.unpack(uu, xr);
     // The prefetch must not be hoisted above the unpack: the window registers are loop-carried,
     // and a load into other registers would need a copy (and so a wait) at the loop back edge.
     // It is unconditional for the same reason (the last window reloads itself).
     __builtin_amdgcn_sched_barrier(0);
     win.load(a, l, da, i0 + kWin < full_end ? i0 + kWin : i0);
-    prep_window(uu, xr, bias, 0.0f, dl, du, yi);
+    float (&mine)[2][kW][kXHalf] = xc.v[DIR][w & 1][me];
+    const float (&theirs)[2][kW][kXHalf] = xc.v[DIR][w & 1][other];
+    float od[kXHalf], ou[kXHalf], td[kXHalf], tu[kXHalf];
+#pragma unroll
+    for (int k = 0; k < kXHalf; ++k) {
+      const int j = kXHalf * me + k;
+      od[k] = softplus_f(xr[j] + bias);
+      ou[k] = od[k] * uu[j];
+      mine[0][l.lane][k] = od[k];
+      mine[1][l.lane][k] = ou[k];
+    }
+    unit_signal(&xc.prod[DIR][me], w + 1);
+    unit_wait(&xc.prod[DIR][other], w + 1);
+#pragma unroll
+    for (int k = 0; k < kXHalf; ++k) {
+      td[k] = theirs[0][l.lane][k];
+      tu[k] = theirs[1][l.lane][k];
+    }
+#pragma unroll
+    for (int k = 0; k < kXHalf; ++k) {
+      dl[k] = me == 0 ? od[k] : td[k];
+      du[k] = me == 0 ? ou[k] : tu[k];
+      dl[kXHalf + k] = me == 0 ? td[k] : od[k];
+      du[kXHalf + k] = me == 0 ? tu[k] : ou[k];
+    }
 #pragma unroll
     for (int j = 0; j < kWin; ++j) S += dl[j];
+    const float yi[kWin] = {};
     run_steps<MODE, DIR>(l, i0, dl, du, yi, A2, h, bcA, bcB, bct, y);
   }
   for (int i = full_end; i < l.Kc; ++i) {
@@ -512,9 +570,18 @@ __device__ __forceinline__ void chunk_state_dir(const ScanArgs& a, const Lane& l
 
 template <typename T, int MODE>
 __global__ __launch_bounds__(kThreads) void chunk_state_kernel(ScanArgs a) {
+  __shared__ ChunkXchg xc;
   const Lane l = lane_ctx(a);
-  if ((__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6) & 1) == 0) chunk_state_dir<T, MODE, 0>(a, l);
-  else chunk_state_dir<T, MODE, 1>(a, l);
+  if (threadIdx.x < 4) xc.prod[threadIdx.x >> 1][threadIdx.x & 1] = 0;
+  __syncthreads();
+  const int dir = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6) & 1;
+  if (dir == 0) {
+    if (l.half == 0) chunk_state_dir<T, MODE, 0, 0>(a, l, xc);
+    else chunk_state_dir<T, MODE, 0, 1>(a, l, xc);
+  } else {
+    if (l.half == 0) chunk_state_dir<T, MODE, 1, 0>(a, l, xc);
+    else chunk_state_dir<T, MODE, 1, 1>(a, l, xc);
+  }
 }
 
 // Carry prefix: per (batch, channel, direction, state), walk the chunks in scan order and replace
@@ -570,26 +637,6 @@ __global__ __launch_bounds__(256) void carry_prefix_kernel(ScanArgs a) {
 template <int PHASE>
 __device__ __forceinline__ void lds_first(float* slot, float v) {
   *slot = PHASE == 1 ? *slot + v : v;
-}
-
-// Pairwise ordering of the two state halves of one direction, without a workgroup barrier: the
-// lower-half wave publishes the number of the last combine unit it has written to the LDS rows,
-// and the upper-half wave waits for it before adding.  A wave's LDS operations execute in issue
-// order, so the data writes are complete when the flag write is, and the compiler barriers keep
-// the instructions in that order.  The lower half never waits, so the wait always ends; the
-// bound only keeps a mistake from turning into a hang.
-__device__ __forceinline__ void unit_signal(int* flag, int unit) {
-  asm volatile("" ::: "memory");
-  __hip_atomic_store(flag, unit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-
-__device__ __forceinline__ void unit_wait(int* flag, int unit) {
-  for (int n = 0; n < (1 << 22); ++n) {
-    if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) >= unit)
-      break;
-    __builtin_amdgcn_s_sleep(1);
-  }
-  asm volatile("" ::: "memory");
 }
 
 template <typename T, int MODE, int DIR, int PHASE>
