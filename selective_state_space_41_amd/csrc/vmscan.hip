@@ -12,28 +12,31 @@
 //    over the same 64 channels (lane = channel) of one batch row: waves 0 and 2 run the forward
 //    direction, waves 1 and 3 the backward direction, and waves 0/1 keep states 0-7 of every
 //    channel, waves 2/3 states 8-15, in VGPRs.  At the Vim-Ti shape this is 3072 waves, three
-//    per SIMD.  Per state and token the VALU work is exp2(Δ·A') (A' = A·log2 e), h·a,
-//    h + (Δu)·B and y + C·h.
+//    per SIMD.  Per state and token the VALU work is exp2(Δ2·A), h·a, h + (Δ2·u)·B' and
+//    y + C·h, with Δ carried in base-2 units (Δ2 = Δ·log2 e) and B' = B·ln 2 stored in the B/C
+//    copy, so that neither factor costs an instruction in the loop.
 //  * B and C are the same for every channel of a batch row, so each wave reads its 8 B and 8 C
 //    values per token as wave-uniform scalars (one s_load_dwordx16) from an fp32
 //    [batch][direction][half][position][16] copy that a small transpose kernel writes first.
 //    No VALU instruction is spent on B/C.
 //  * u, Δ_raw (and z) are read per lane in windows of 8 consecutive tokens (16-byte loads;
 //    the hardware accepts the 2-byte-aligned rows of odd-length bf16 sequences), one window
-//    ahead of use.  Δ = softplus(Δ_raw + bias) is computed with a compensated log1p:
-//    log(1+e) = ln2·log2(s) + (e - (s - 1)), s = 1 + e.
+//    ahead of use.  Δ2 = log2(1 + 2^t), t = (Δ_raw + bias)·log2 e, is computed with a
+//    compensated log1p: log2(1 + e) = log2(s) + (e - (s - 1))·log2 e, s = 1 + e.
 //  * All four waves advance in lockstep: at step i the forward waves are at chunk position i,
 //    the backward waves at Kc-1-i.  The channel's y at a position is the sum of four partial
 //    readouts (two directions x two state halves).  They meet in one fp32 LDS row per channel in
 //    a fixed order, so the result is deterministic: per window the lower-half wave of a direction
 //    stores (first half of the steps) or adds (second half) its partial y, including the D·u
-//    term; after a workgroup barrier the upper-half wave adds its own.  A cooperative epilogue
-//    then applies the gate once, rounds once, and writes 16-byte stores.  No reversed copy of
-//    any tensor is made.
+//    term, and publishes the window in an LDS counter; the upper-half wave waits for that count
+//    and adds its own.  A workgroup barrier separates the halves of the chunk, and a cooperative
+//    epilogue then applies the gate once, rounds once, and writes 16-byte stores.  No reversed
+//    copy of any tensor is made.
 //  * Sequences longer than one LDS row are split into chunks.  A first kernel computes each
-//    chunk's end state from a zero start and its Σ Δ; the main kernel folds the preceding
-//    chunks' pairs (Σ Δ, end state) into its initial state, exp(A Σ Δ) being a chunk's total
-//    decay, so the carry crosses workgroups without re-running the recurrence.
+//    chunk's end state from a zero start and its Σ Δ2; a small prefix kernel walks the chunks in
+//    scan order and turns these into the state entering each chunk (exp2(A Σ Δ2) being a
+//    chunk's total decay); the main kernel starts each chunk from that state, so the carry
+//    crosses workgroups without re-running the recurrence.
 //  * SS2D runs as two such bidirectional pairs, both over contiguous rows: the column pair
 //    (column-major and its reverse) scans a transposed copy of x and writes an fp32 image in
 //    column-major order; that image is transposed, and the row pair (row-major and its reverse)
@@ -62,7 +65,7 @@ constexpr int kMinChunk = 32;          // shortest chunk the planner picks
 constexpr int kTargetBlocks = 768;     // planner: three workgroups on each of 256 CUs
 constexpr int kKSplit = 158;           // split sequences: chunks of <= 158 positions (LDS rows of 159), four workgroups per CU
 constexpr int kSplitSlots = 1024;      // ... so a round is four workgroups on each of 256 CUs
-constexpr int kAggStride = kN + 1;     // per chunk: 16 end states + Σ Δ
+constexpr int kAggStride = kN + 1;     // per chunk: 16 end states + Σ Δ2
 constexpr int kTransThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -122,17 +125,27 @@ struct Run8<float> {
   }
 };
 
-// softplus(x) = log(1 + e^x).  With e = e^x and s = fl(1 + e), c = e - (s - 1) is the rounding
-// error of s (exactly for e <= 1; for e > 1 it is below the result's resolution), and
-// log(1 + e) = log(s) + log(1 + c/s) ~= ln2 * log2(s) + c.  This keeps full fp32 relative
-// accuracy for the e ~ 1e-3 that the Δ bias range produces, where a plain log(1 + e) loses
-// about three digits.  Above 20 the correction to x is below fp32 resolution.
-__device__ __forceinline__ float softplus_f(float x) {
-  const float e = __builtin_amdgcn_exp2f(x * kLog2e);
+// The kernels carry Δ in base-2 units, Δ2 = Δ log2 e: then the decay is exp2(Δ2 A) with the
+// natural A = -exp(A_log), Δ u B = Δ2 u (B ln 2) with B pre-scaled in the B/C copy, and the
+// softplus argument x log2 e is one FMA of the raw input with the scaled bias.
+//
+// softplus in base-2 units: given t = x log2 e, returns log2(1 + 2^t) = softplus(x) log2 e.
+// With e = 2^t and s = fl(1 + e), c = e - (s - 1) is the rounding error of s (exactly for e <= 1;
+// for e > 1 it is below the result's resolution), and log2(1 + e) = log2(s) + log2(1 + c/s)
+// ~= log2(s) + c log2 e.  This keeps full fp32 relative accuracy for the e ~ 1e-3 that the Δ
+// bias range produces, where a plain log2(1 + e) loses about three digits.  Above x = 20 the
+// correction to x is below fp32 resolution.
+__device__ __forceinline__ float softplus2(float t) {
+  const float e = __builtin_amdgcn_exp2f(t);
   const float s = 1.0f + e;
   const float c = e - (s - 1.0f);
-  const float r = __builtin_fmaf(__builtin_amdgcn_logf(s), kLn2, c);
-  return x > 20.0f ? x : r;
+  const float r = __builtin_fmaf(c, kLog2e, __builtin_amdgcn_logf(s));
+  return t > 20.0f * kLog2e ? t : r;
+}
+
+// Base-2 softplus argument from the raw Δ input and the bias already multiplied by log2 e.
+__device__ __forceinline__ float delta2(float raw, float bias2) {
+  return softplus2(__builtin_fmaf(raw, kLog2e, bias2));
 }
 
 __device__ __forceinline__ float silu_f(float v) {
@@ -188,7 +201,7 @@ struct ScanArgs {
 enum { kModeVim = 0, kModeFirstPair = 1, kModeSecondPair = 2 };
 
 // ---------------------------------------------------------------------------------------------
-// B/C transpose: for half q, bct[b][dir][q][s][0..7] = B_dir[b][8q + 0..7, si(s)] and
+// B/C transpose: for half q, bct[b][dir][q][s][0..7] = B_dir[b][8q + 0..7, si(s)] ln 2 and
 // bct[b][dir][q][s][8..15] = C_dir[b][8q + 0..7, si(s)].
 
 template <typename T>
@@ -209,7 +222,7 @@ __global__ __launch_bounds__(kTransThreads) void bc_transpose_kernel(ScanArgs a)
     float v[kBC];
 #pragma unroll
     for (int k = 0; k < kH; ++k) {
-      v[k] = ld_act(bb, static_cast<int64_t>(kH * q + k) * a.L);
+      v[k] = ld_act(bb, static_cast<int64_t>(kH * q + k) * a.L) * kLn2;  // B ln 2: Δ2 u (B ln 2) = Δ u B
       v[kH + k] = ld_act(cb, static_cast<int64_t>(kH * q + k) * a.L);
     }
     float4* dst = reinterpret_cast<float4*>(a.bct + (((static_cast<int64_t>(b) * 2 + dir) * 2 + q) * a.L + s) * kBC);
@@ -366,11 +379,10 @@ struct Window {
   }
 };
 
-// A' = -exp(A_log) * log2 e for the wave's 8 states.
+// A = -exp(A_log) for the wave's 8 states (the decay of a step is exp2(Δ2 A)).
 __device__ __forceinline__ void load_a2(const DirArgs& da, const Lane& l, float (&A2)[kH]) {
 #pragma unroll
-  for (int k = 0; k < kH; ++k)
-    A2[k] = -__expf(da.A_log[static_cast<int64_t>(l.dd) * kN + kH * l.half + k]) * kLog2e;
+  for (int k = 0; k < kH; ++k) A2[k] = -__expf(da.A_log[static_cast<int64_t>(l.dd) * kN + kH * l.half + k]);
 }
 
 // B/C of one position for the wave's half: 8 + 8 wave-uniform floats (one s_load_dwordx16).
@@ -385,7 +397,7 @@ __device__ __forceinline__ scalar_fp bc_row(const ScanArgs& a, const Lane& l) {
   return (scalar_fp)(a.bct) + (((static_cast<int64_t>(l.b) * 2 + DIR) * 2 + l.half) * a.L) * kBC;
 }
 
-// One token for the wave's 8 states, h = exp2(Δ A') h + (Δu) B; returns yi + Σ C h.  The B/C of
+// One token for the wave's 8 states, h = exp2(Δ2 A) h + (Δ2 u)(B ln 2); returns yi + Σ C h.  The B/C of
 // the next token (nxt) is requested once this token's B values are dead (after the h updates),
 // so at most 32 SGPRs hold B/C.  Scalar loads may return out of order, so the wait for this
 // token's B/C (at its first use) covers every scalar load in flight; issuing nxt after that point
@@ -432,12 +444,13 @@ __device__ __forceinline__ void run_steps(const Lane& l, int i0, const float (&d
   }
 }
 
-// Δ and Δ·u of a window from its raw u and Δ_raw; yi = the lane's D·u share (lower half only).
-__device__ __forceinline__ void prep_window(const float (&uu)[kWin], const float (&xr)[kWin], float bias, float Dh,
+// Δ2 and Δ2·u of a window from its raw u and Δ_raw (bias2 = bias log2 e); yi = the lane's D·u
+// share (lower half only).
+__device__ __forceinline__ void prep_window(const float (&uu)[kWin], const float (&xr)[kWin], float bias2, float Dh,
                                             float (&dl)[kWin], float (&du)[kWin], float (&yi)[kWin]) {
 #pragma unroll
   for (int j = 0; j < kWin; ++j) {
-    dl[j] = softplus_f(xr[j] + bias);
+    dl[j] = delta2(xr[j], bias2);
     du[j] = dl[j] * uu[j];
     yi[j] = Dh * uu[j];
   }
@@ -445,7 +458,7 @@ __device__ __forceinline__ void prep_window(const float (&uu)[kWin], const float
 
 // One step i outside the full windows (chunk tails): raw loads, Δ, the token update and the B/C
 // prefetch of step i + 1 into bcA.  Returns the wave's partial y (with its D·u share) and sets
-// *dl_out = Δ.
+// *dl_out = Δ2.
 template <typename T, int MODE, int DIR>
 __device__ __forceinline__ float single_step(const ScanArgs& a, const Lane& l, const DirArgs& da, float bias, float Dh,
                                              int i, const float (&A2)[kH], float (&h)[kH], scalar_fp bct,
@@ -454,7 +467,7 @@ __device__ __forceinline__ float single_step(const ScanArgs& a, const Lane& l, c
   const T* ub = static_cast<const T*>(a.u) + static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(l.dd) * a.L;
   const T* db = static_cast<const T*>(da.draw) + static_cast<int64_t>(l.b) * da.draw_bs + static_cast<int64_t>(l.dd) * a.L;
   const float uu = ld_act(ub, Dr::pos(l, i));
-  const float dl = softplus_f(ld_act(db, Dr::sidx(a, l, i)) + bias);
+  const float dl = delta2(ld_act(db, Dr::sidx(a, l, i)), bias);
   float bcB[kBC];
   const float y = scan_token(dl, dl * uu, Dh * uu, A2, h, bcA, bcB, bct + Dr::pos(l, i + 1) * kBC);
 #pragma unroll
@@ -485,7 +498,7 @@ __device__ __forceinline__ void unit_wait(int* flag, int unit) {
 
 // ---------------------------------------------------------------------------------------------
 // Pass A: per chunk, direction and state half, the end states of the chunk scanned from a zero
-// state, and Σ Δ.
+// state, and Σ Δ2 (base-2 units).
 
 // Δ and Δ·u exchange between the two state halves of a direction: each wave computes them for
 // half of a window's steps and reads the other half from its partner, so softplus is evaluated
@@ -507,7 +520,7 @@ __device__ __forceinline__ void chunk_state_dir(const ScanArgs& a, const Lane& l
   load_a2(da, l, A2);
 #pragma unroll
   for (int n = 0; n < kH; ++n) h[n] = 0.0f;
-  const float bias = da.bias[l.dd];
+  const float bias = da.bias[l.dd] * kLog2e;  // base-2 units
   const scalar_fp bct = bc_row<DIR>(a, l);
   float S = 0.0f;
   float bcA[kBC], bcB[kBC];
@@ -531,7 +544,7 @@ __device__ __forceinline__ void chunk_state_dir(const ScanArgs& a, const Lane& l
 #pragma unroll
     for (int k = 0; k < kXHalf; ++k) {
       const int j = kXHalf * me + k;
-      od[k] = softplus_f(xr[j] + bias);
+      od[k] = delta2(xr[j], bias);
       ou[k] = od[k] * uu[j];
       mine[0][l.lane][k] = od[k];
       mine[1][l.lane][k] = ou[k];
@@ -585,8 +598,8 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(ScanArgs a) {
 }
 
 // Carry prefix: per (batch, channel, direction, state), walk the chunks in scan order and replace
-// each chunk's record (end state from a zero start, Σ Δ) by the state entering that chunk:
-//   h_in(first) = 0,  h_in(next) = exp(A Σ Δ) h_in + h_end,
+// each chunk's record (end state from a zero start, Σ Δ2) by the state entering that chunk:
+//   h_in(first) = 0,  h_in(next) = exp2(A Σ Δ2) h_in + h_end,
 // exp(A Σ Δ) being the chunk's total decay.  One thread per (batch, channel, direction, state).
 __global__ __launch_bounds__(256) void carry_prefix_kernel(ScanArgs a) {
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -597,7 +610,7 @@ __global__ __launch_bounds__(256) void carry_prefix_kernel(ScanArgs a) {
   const int64_t bd = t / (2 * kN);  // b * dim + d
   const int d = static_cast<int>(bd % a.dim);
   const DirArgs& da = dir == 0 ? a.d0 : a.d1;
-  const float A2 = -__expf(da.A_log[static_cast<int64_t>(d) * kN + n]) * kLog2e;
+  const float A2 = -__expf(da.A_log[static_cast<int64_t>(d) * kN + n]);  // with Σ Δ2: exp2(A Σ Δ2) = exp(A Σ Δ)
   float* rec = a.agg + (bd * 2 + dir) * a.nch * kAggStride;
   float h = 0.0f;
   // eight chunks at a time: all their loads are in flight before the dependent updates
@@ -727,7 +740,7 @@ __device__ __forceinline__ void scan_pair_dir(const ScanArgs& a, const Lane& l, 
   load_a2(da, l, A2);
 #pragma unroll
   for (int n = 0; n < kH; ++n) h[n] = 0.0f;
-  const float bias = da.bias[l.dd];
+  const float bias = da.bias[l.dd] * kLog2e;  // base-2 units
   const float Dh = l.half == 0 ? da.Dp[l.dd] : 0.0f;  // the lower half adds the D·u term
 
   // Carry-in: the state entering this chunk, which the carry-prefix kernel left in the chunk's
