@@ -12,6 +12,7 @@ from .vmscan_oracle import (  # noqa: F401
     scan_1d,
     scan_1d_semiseparable,
     vim_bidir,
+    vim_bidir_v2,
     ss2d_orders,
     ss2d_cross_scan,
     ss2d_cross_scan_pathwalk,

@@ -138,6 +138,27 @@ def vim_bidir(u, delta_raw, z, A_log, A_b_log, B, C, B_b, C_b, D, D_b, delta_bia
     return (y_f + y_b) / 2.0
 
 
+def vim_bidir_v2(u, delta_raw, delta_bias, u_b, delta_raw_b, delta_bias_b, z, A_log, A_b_log, B, C, B_b, C_b,
+                 D, D_b):
+    """Vision Mamba bidirectional scan with a fully separate backward branch (v2 parameter sets).
+
+    In v2 the backward branch has its own convolution, input projection and Δ projection
+    ([P3] §2.1: conv1d_b, x_proj_b, dt_proj_b, D_b), so besides A_b_log, B_b, C_b, D_b it has its
+    own scan input u_b, Δ_raw_b and Δ bias delta_bias_b, all given in ORIGINAL token order.  The
+    gate z is shared.
+
+        y_f = scan(u, Δ_raw; A_log, B, C, D, bias) * silu(z)
+        y_b = flip( scan(flip u_b, flip Δ_raw_b; A_b_log, flip B_b, flip C_b, D_b, bias_b) * silu(flip z) )
+        out = (y_f + y_b) / 2                                   [P3] §2.2, §4.3
+
+    ``vim_bidir`` is the case u_b = u, Δ_raw_b = Δ_raw, bias_b = bias.
+    """
+    f = lambda x: np.flip(np.asarray(x, dtype=np.float64), axis=-1)
+    y_f = scan_1d(u, delta_raw, A_log, B, C, D, delta_bias) * silu(z)
+    y_b_rev = scan_1d(f(u_b), f(delta_raw_b), A_b_log, f(B_b), f(C_b), D_b, delta_bias_b) * silu(f(z))
+    return (y_f + f(y_b_rev)) / 2.0
+
+
 def ss2d_orders(x):
     """The four cross-scan sequences of [P4] §2.2 for x[batch, dim, H, W]:
     row-major flatten, column-major flatten (transpose then flatten), and each reversed."""

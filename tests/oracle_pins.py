@@ -1,5 +1,5 @@
 """Pins for the fp64 oracle: each ``pin_*`` takes an implementation namespace (with
-``scan_1d``, ``vim_bidir``, ``ss2d_cross_scan``) and returns the list of failure messages
+``scan_1d``, ``vim_bidir``, ``vim_bidir_v2``, ``ss2d_cross_scan``) and returns the list of failure messages
 (empty = pass).  They check the oracle against facts fixed by the mathematics, not against the
 oracle itself: hand-derived closed forms, brute force on tiny inputs, linearity, the flip
 identity, limits and the SS2D reductions.  ``test_oracle_pins`` runs them on the oracle;
@@ -313,6 +313,68 @@ def pin_ss2d_transpose(impl):
     return msgs
 
 
+def rich_v2(rng, nb=2, nd=3, L=7, N=4):
+    """rich_vim plus a backward branch with its own u_b, Δ_raw_b and bias_b."""
+    p = rich_vim(rng, nb=nb, nd=nd, L=L, N=N)
+    p["u_b"] = rng.standard_normal((nb, nd, L))
+    p["delta_raw_b"] = rng.standard_normal((nb, nd, L))
+    p["delta_bias_b"] = rng.uniform(-2.5, 0.0, nd)
+    return p
+
+
+def _v2(impl, p, **over):
+    q = dict(p)
+    q.update(over)
+    return impl.vim_bidir_v2(q["u"], q["delta_raw"], q["delta_bias"], q["u_b"], q["delta_raw_b"], q["delta_bias_b"],
+                             q["z"], q["A_log"], q["A_b_log"], q["B"], q["C"], q["B_b"], q["C_b"], q["D"], q["D_b"])
+
+
+def pin_v2_single_token(impl):
+    """L = 1 with a separate backward branch: out = silu(z) (u (Δ Σ B C + D) + u_b (Δ_b Σ B_b C_b + D_b)) / 2
+    with Δ = softplus(Δ_raw + bias) and Δ_b = softplus(Δ_raw_b + bias_b)."""
+    msgs = []
+    rng = np.random.default_rng(11)
+    p = rich_v2(rng, nb=3, nd=4, L=1, N=5)
+    dl = np.logaddexp(0.0, p["delta_raw"][:, :, 0] + p["delta_bias"][None, :])
+    dlb = np.logaddexp(0.0, p["delta_raw_b"][:, :, 0] + p["delta_bias_b"][None, :])
+    bc_f = np.einsum("bn,bn->b", p["B"][:, :, 0], p["C"][:, :, 0])[:, None]
+    bc_b = np.einsum("bn,bn->b", p["B_b"][:, :, 0], p["C_b"][:, :, 0])[:, None]
+    zz = p["z"][:, :, 0]
+    g = zz / (1.0 + np.exp(-zz))
+    expect = 0.5 * (p["u"][:, :, 0] * (dl * bc_f + p["D"][None]) + p["u_b"][:, :, 0] * (dlb * bc_b + p["D_b"][None])) * g
+    _check(msgs, "v2 L=1 closed form", O.rel_err(_v2(impl, p)[:, :, 0], expect), 1e-13)
+    return msgs
+
+
+def pin_v2_semiseparable(impl):
+    """Brute force with a separate backward branch: out = silu(z) ((M_f + diag D) u + (M_b + diag D_b) u_b) / 2,
+    M_b built from Δ_b = softplus(Δ_raw_b + bias_b)."""
+    msgs = []
+    rng = np.random.default_rng(12)
+    for L in (1, 3, 8):
+        p = rich_v2(rng, nb=2, nd=2, L=L, N=3)
+        sf = O.scan_1d_semiseparable(p["u"], p["delta_raw"], p["A_log"], p["B"], p["C"], p["D"], p["delta_bias"])
+        sb = O.scan_1d_semiseparable(p["u_b"], p["delta_raw_b"], p["A_b_log"], p["B_b"], p["C_b"], p["D_b"],
+                                     p["delta_bias_b"], reverse=True)
+        expect = 0.5 * (sf + sb) * (p["z"] / (1 + np.exp(-p["z"])))
+        _check(msgs, f"v2 semiseparable L={L}", O.rel_err(_v2(impl, p), expect), 1e-12)
+    return msgs
+
+
+def pin_v2_flip_identity(impl):
+    """Exchanging the two branches (all of their inputs) and reversing every sequence reverses the output."""
+    msgs = []
+    rng = np.random.default_rng(13)
+    p = rich_v2(rng, nb=2, nd=3, L=10, N=4)
+    f = lambda a: np.flip(a, axis=-1)
+    lhs = _v2(impl, p, u=f(p["u_b"]), delta_raw=f(p["delta_raw_b"]), delta_bias=p["delta_bias_b"],
+              u_b=f(p["u"]), delta_raw_b=f(p["delta_raw"]), delta_bias_b=p["delta_bias"], z=f(p["z"]),
+              A_log=p["A_b_log"], A_b_log=p["A_log"], B=f(p["B_b"]), C=f(p["C_b"]), B_b=f(p["B"]), C_b=f(p["C"]),
+              D=p["D_b"], D_b=p["D"])
+    _check(msgs, "v2 flip identity", O.rel_err(lhs, f(_v2(impl, p))), 1e-12)
+    return msgs
+
+
 ALL_PINS = [
     pin_softplus_silu,
     pin_golden_single_token,
@@ -327,4 +389,7 @@ ALL_PINS = [
     pin_ss2d_single_pixel,
     pin_ss2d_one_row,
     pin_ss2d_transpose,
+    pin_v2_single_token,
+    pin_v2_semiseparable,
+    pin_v2_flip_identity,
 ]

@@ -81,6 +81,23 @@ def _vim(u, dr, z, Al, Abl, B, C, Bb, Cb, D, Db, bias, bug=None, scan_bug=None):
     return 0.5 * (yf + yb)
 
 
+def _v2(u, dr, bias, ub, drb, biasb, z, Al, Abl, B, C, Bb, Cb, D, Db, bug=None, scan_bug=None):
+    f = lambda a: np.flip(np.asarray(a, dtype=np.float64), axis=-1)
+    sc = lambda *a: _scan(*a, bug=scan_bug)
+    yf = sc(u, dr, Al, B, C, D, bias) * O.silu(z)
+    if bug == "v2_bwd_uses_fwd_u":
+        ub = u
+    if bug == "v2_bwd_uses_fwd_delta":
+        drb = dr
+    if bug == "v2_bwd_uses_fwd_bias":
+        biasb = bias
+    if bug == "v2_fwd_uses_bwd_bias":
+        yf = sc(u, dr, Al, B, C, D, biasb) * O.silu(z)
+    rev_u = ub if bug == "v2_ub_not_flipped" else f(ub)
+    rev = sc(rev_u, f(drb), Abl, f(Bb), f(Cb), Db, biasb)
+    return 0.5 * (yf + f(rev * O.silu(f(z))))
+
+
 def _ss2d(x, dr, Al, B, C, D, bias, z=None, bug=None, scan_bug=None):
     x = np.asarray(x, dtype=np.float64)
     nb, nd, H, W = x.shape
@@ -106,12 +123,13 @@ def _ss2d(x, dr, Al, B, C, D, bias, z=None, bug=None, scan_bug=None):
     return out
 
 
-def _impl(scan_bug=None, vim_bug=None, ss2d_bug=None):
+def _impl(scan_bug=None, vim_bug=None, ss2d_bug=None, v2_bug=None):
     return types.SimpleNamespace(
         softplus=O.softplus,
         silu=O.silu,
         scan_1d=lambda *a: _scan(*a, bug=scan_bug),
         vim_bidir=lambda *a: _vim(*a, bug=vim_bug, scan_bug=scan_bug),
+        vim_bidir_v2=lambda *a: _v2(*a, bug=v2_bug, scan_bug=scan_bug),
         ss2d_cross_scan=lambda x, dr, Al, B, C, D, bias, z=None: _ss2d(x, dr, Al, B, C, D, bias, z, bug=ss2d_bug, scan_bug=scan_bug),
     )
 
@@ -121,6 +139,7 @@ SCAN_BUGS = ["A_not_exp", "A_sign", "swap_BC", "no_softplus", "exp_not_softplus"
 VIM_BUGS = ["bwd_uses_fwd_BC", "bwd_uses_fwd_A", "bwd_BC_not_flipped", "bwd_delta_not_flipped", "bwd_D_is_fwd_D",
             "gate_not_flipped", "no_flip_back", "sum_not_avg", "gate_silu_is_sigmoid"]
 SS2D_BUGS = ["col_as_reshape", "col_not_transposed_back", "rev_not_flipped_back", "avg4"]
+V2_BUGS = ["v2_bwd_uses_fwd_u", "v2_bwd_uses_fwd_delta", "v2_bwd_uses_fwd_bias", "v2_fwd_uses_bwd_bias", "v2_ub_not_flipped"]
 
 
 def _caught(impl):
@@ -153,3 +172,8 @@ def test_vim_mutant_caught(bug):
 @pytest.mark.parametrize("bug", SS2D_BUGS)
 def test_ss2d_mutant_caught(bug):
     assert _caught(_impl(ss2d_bug=bug)), f"planted mistake {bug} passes every pin"
+
+
+@pytest.mark.parametrize("bug", V2_BUGS)
+def test_v2_mutant_caught(bug):
+    assert _caught(_impl(v2_bug=bug)), f"planted mistake {bug} passes every pin"
