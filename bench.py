@@ -1,12 +1,13 @@
 """Benchmark of the fused bidirectional selective scan (and SS2D cross-scan) on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N | --all] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N | --all] [--no-cpu] [--v2]
 
 A step is one call of the hot path over one batch of seeded synthetic input already resident in
 HBM.  The default workload is the Vim-Ti layer scan (batch 128, d_inner 384, L 197, d_state 16,
 bf16 activations, fp32 state), the configuration the metric is quoted on.  R input/output sets
 are rotated so that at least 1 GiB is touched between reuses and the 256 MB Infinity Cache cannot
-serve the inputs.  Rank 0 prints one JSON line per workload.
+serve the inputs.  Rank 0 prints one JSON line per workload.  ``--v2`` runs the Vim workloads
+through the entry point whose backward branch has its own u_b, Δ_raw_b and bias_b.
 """
 import argparse
 import hashlib
@@ -34,16 +35,16 @@ KERNEL_SRC = os.path.join(ROOT, "selective_state_space_41_amd", "csrc", "vmscan.
 METRIC = "scan tokens·channels/s (fwd, bidir) and achieved HBM GB/s vs peak, 1 GPU"
 
 
-def algorithmic_bytes(cfg):
+def algorithmic_bytes(cfg, v2=False):
     """Bytes the call must move at minimum: every input read once, the output written once."""
     c = cfg
     esz = 4 if c["dtype"] == "f32" else 2
     N = c["d_state"]
     if c["kind"] == "vim":
         nb, nd, L = c["batch"], c["dim"], c["seqlen"]
-        act = 4 * nb * nd * L * esz               # u, delta_raw, z, out
+        act = (6 if v2 else 4) * nb * nd * L * esz   # u, delta_raw, z, out (+ u_b, delta_raw_b)
         bc = 4 * nb * N * L * esz                 # B, C, B_b, C_b
-        par = 2 * nd * N * 4 + 3 * nd * 4         # A_log, A_b_log; D, D_b, bias
+        par = 2 * nd * N * 4 + (4 if v2 else 3) * nd * 4   # A_log, A_b_log; D, D_b, bias (+ bias_b)
         return act + bc + par, nb * nd * L
     nb, nd, L = c["batch"], c["dim"], c["H"] * c["W"]
     act = 2 * nb * nd * L * esz                   # x, out
@@ -193,7 +194,13 @@ def cpu_baseline(cfg_id, cfg, min_s=1.0):
                       f"slowest worker {wall:.2f} s"}
 
 
-def make_sets(cfg_id, cfg, nsets, torch):
+VIM_ACT = ("u", "delta_raw", "z", "B", "C", "B_b", "C_b")
+VIM_PAR = ("A_log", "A_b_log", "D", "D_b", "delta_bias")
+V2_ACT = ("u_b", "delta_raw_b")
+V2_PAR = ("delta_bias_b",)
+
+
+def make_sets(cfg_id, cfg, nsets, torch, v2=False):
     """Set 0 comes from the seeded generator (the parity inputs); further rotation sets are drawn on
     the device from a seeded torch generator with the same distributions."""
     import numpy as np
@@ -204,9 +211,9 @@ def make_sets(cfg_id, cfg, nsets, torch):
     g.manual_seed(41_000 + cfg_id)
     sets = []
     if cfg["kind"] == "vim":
-        p = synth.make_vim_inputs(cfg_id)
-        act_names = ("u", "delta_raw", "z", "B", "C", "B_b", "C_b")
-        par = {k: torch.from_numpy(np.ascontiguousarray(p[k])).to(dev) for k in ("A_log", "A_b_log", "D", "D_b", "delta_bias")}
+        p = synth.make_vim_v2_inputs(cfg_id) if v2 else synth.make_vim_inputs(cfg_id)
+        act_names = VIM_ACT + (V2_ACT if v2 else ())
+        par = {k: torch.from_numpy(np.ascontiguousarray(p[k])).to(dev) for k in VIM_PAR + (V2_PAR if v2 else ())}
         base = {k: torch.from_numpy(np.ascontiguousarray(p[k])).to(dev).to(dt) for k in act_names}
         for s in range(nsets):
             if s == 0:
@@ -228,10 +235,11 @@ def make_sets(cfg_id, cfg, nsets, torch):
     return sets
 
 
-def bench_config(cfg_id, steps, warmup, with_cpu, torch, V):
+def bench_config(cfg_id, steps, warmup, with_cpu, torch, V, v2=False):
     import synth
     cfg = synth.CONFIGS[cfg_id]
-    nbytes, toks = algorithmic_bytes(cfg)
+    v2 = v2 and cfg["kind"] == "vim"
+    nbytes, toks = algorithmic_bytes(cfg, v2)
     layers = cfg.get("layers", 1)
     per_set = nbytes
     nsets = max(1, math.ceil((1 << 30) / per_set)) if layers == 1 else layers
@@ -242,13 +250,13 @@ def bench_config(cfg_id, steps, warmup, with_cpu, torch, V):
         dt = torch.bfloat16
         dev = torch.device("cuda", 0)
         for layer in range(layers):
-            p = synth.make_vim_inputs(cfg_id, layer=layer)
-            act = {k: torch.from_numpy(np.ascontiguousarray(p[k])).to(dev).to(dt) for k in ("u", "delta_raw", "z", "B", "C", "B_b", "C_b")}
+            p = synth.make_vim_v2_inputs(cfg_id, layer=layer) if v2 else synth.make_vim_inputs(cfg_id, layer=layer)
+            act = {k: torch.from_numpy(np.ascontiguousarray(p[k])).to(dev).to(dt) for k in VIM_ACT + (V2_ACT if v2 else ())}
             act["out"] = torch.empty_like(act["u"])
-            par = {k: torch.from_numpy(np.ascontiguousarray(p[k])).to(dev) for k in ("A_log", "A_b_log", "D", "D_b", "delta_bias")}
+            par = {k: torch.from_numpy(np.ascontiguousarray(p[k])).to(dev) for k in VIM_PAR + (V2_PAR if v2 else ())}
             sets.append((act, par))
     else:
-        sets = make_sets(cfg_id, cfg, nsets, torch)
+        sets = make_sets(cfg_id, cfg, nsets, torch, v2)
     dev = torch.device("cuda", 0)
     ws = None
     if cfg["kind"] == "vim":
@@ -259,7 +267,11 @@ def bench_config(cfg_id, steps, warmup, with_cpu, torch, V):
 
     def call(i, stage=3):
         act, par = sets[i % len(sets)]
-        if cfg["kind"] == "vim":
+        if v2:
+            V.vmscan_fwd_bidir_v2(act["u"], act["delta_raw"], par["delta_bias"], act["u_b"], act["delta_raw_b"],
+                                  par["delta_bias_b"], act["z"], par["A_log"], par["A_b_log"], act["B"], act["C"],
+                                  act["B_b"], act["C_b"], par["D"], par["D_b"], out=act["out"], workspace=ws, stage=stage)
+        elif cfg["kind"] == "vim":
             V.vmscan_fwd_bidir(act["u"], act["delta_raw"], act["z"], par["A_log"], par["A_b_log"], act["B"], act["C"],
                                act["B_b"], act["C_b"], par["D"], par["D_b"], par["delta_bias"], out=act["out"], workspace=ws,
                                stage=stage)
@@ -302,7 +314,7 @@ def bench_config(cfg_id, steps, warmup, with_cpu, torch, V):
     is_default = cfg_id == 1
     roof = {"bound": "alu", "achieved": round(alu / 1e9, 1), "peak": round(ALU_PEAK_UPD_S / 1e9, 1), "unit": "Gupd/s",
             "frac": round(alu / ALU_PEAK_UPD_S, 4), "traffic": traffic_record(cfg["name"]),
-            "kernel": ("scan_pair_kernel<bf16, vim> (scan stage of vmscan_fwd_bidir)" if split else
+            "kernel": (("scan_pair_kernel<bf16, vim> (scan stage of vmscan_fwd_bidir" + ("_v2)" if v2 else ")")) if split else
                        "all kernels of the call (transpose, chunk states, both SS2D pairs)"),
             "kernel_avg_us": round(kern_ms * 1000, 2),
             "updates_per_launch": upd,
@@ -321,17 +333,19 @@ def bench_config(cfg_id, steps, warmup, with_cpu, torch, V):
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": cfg["name"], "batch": cfg["batch"], "dim": cfg["dim"],
+        "config": {"workload": cfg["name"] + ("_sepbwd" if v2 else ""), "batch": cfg["batch"], "dim": cfg["dim"],
                    "seqlen": cfg.get("seqlen", cfg.get("H", 0) * cfg.get("W", 0)), "d_state": cfg["d_state"],
                    "io_dtype": cfg["dtype"], "rotation_sets": len(sets),
                    "step_ms_p10_p50_p90": [step_ms[len(step_ms) // 10], step_ms[len(step_ms) // 2],
                                            step_ms[(9 * len(step_ms)) // 10]]},
         "roofline": roof,
     }
+    if v2:
+        rec["config"]["backward_branch"] = "separate u_b, delta_raw_b, delta_bias_b"
     if cfg["kind"] == "ss2d":
         rec["config"]["H"] = cfg["H"]
         rec["config"]["W"] = cfg["W"]
-    if with_cpu and is_default:
+    if with_cpu and is_default and not v2:
         rec["cpu_baseline"] = cpu_baseline(cfg_id, cfg)
     return rec
 
@@ -344,6 +358,7 @@ def main():
     ap.add_argument("--config", type=int, default=1)
     ap.add_argument("--all", action="store_true", help="one line per workload (configs 0-4)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--v2", action="store_true", help="Vim workloads with a separate backward branch (u_b, delta_raw_b, bias_b)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (counter calibration for FETCH_SIZE/WRITE_SIZE)")
     ap.add_argument("--summarize-kernels", nargs=3, metavar=("RESULT_DIR", "COMMAND", "OUT_TXT"),
@@ -389,7 +404,7 @@ def main():
     import selective_state_space_41_amd as V
     cfgs = [0, 1, 2, 3, 4] if args.all else [args.config]
     for c in cfgs:
-        rec = bench_config(c, args.steps, args.warmup, not args.no_cpu, torch, V)
+        rec = bench_config(c, args.steps, args.warmup, not args.no_cpu, torch, V, args.v2)
         print(json.dumps(rec), flush=True)
 
 

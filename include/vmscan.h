@@ -133,6 +133,41 @@ vmscan_status vmscan_fwd_bidir_stage(const void *u, const void *delta_raw, const
                                      size_t workspace_bytes, int64_t chunk_len, int stage,
                                      hipStream_t stream);
 
+/*
+ * The same bidirectional scan with a separate backward branch: in Vim's v2 parameter sets the
+ * backward branch has its own convolution, input projection and Δ projection ([P3] §2.1), so
+ * its scan input u_b, Δ input delta_raw_b and Δ bias delta_bias_b differ from the forward
+ * branch's.  With y_f the scan of (u, delta_raw, delta_bias; A_log, B, C, D) and y_b' that of
+ * the reversed (u_b, delta_raw_b; A_b_log, B_b, C_b, D_b) with delta_bias_b:
+ *   out = ( y_f + flip(y_b') ) / 2 * silu(z)                       [P3] §2.2, §4.3
+ *   u_b, delta_raw_b : [batch, dim, seqlen] activation dtype, ORIGINAL token order (the library
+ *                      walks them backwards; no flipped copy is made)
+ *   delta_bias_b     : [dim] float32
+ * Any of u_b, delta_raw_b, delta_bias_b may alias the forward branch's tensor;
+ * vmscan_fwd_bidir_stage(...) equals vmscan_fwd_bidir_v2_stage with u_b = u,
+ * delta_raw_b = delta_raw and delta_bias_b = delta_bias.  All other arguments, the workspace
+ * (same size query as vmscan_fwd_bidir_workspace_bytes[_ex]), chunk_len, stage, validation and
+ * error codes are as for vmscan_fwd_bidir_ex / vmscan_fwd_bidir_stage; out must not alias any
+ * input.
+ */
+vmscan_status vmscan_fwd_bidir_v2(const void *u, const void *delta_raw, const float *delta_bias,
+                                  const void *u_b, const void *delta_raw_b, const float *delta_bias_b,
+                                  const void *z, const float *A_log, const float *A_b_log,
+                                  const void *B, const void *C, const void *B_b, const void *C_b,
+                                  const float *D, const float *D_b, void *out,
+                                  int64_t batch, int64_t dim, int64_t seqlen, int d_state,
+                                  vmscan_dtype dtype, void *workspace, size_t workspace_bytes,
+                                  int64_t chunk_len, hipStream_t stream);
+vmscan_status vmscan_fwd_bidir_v2_stage(const void *u, const void *delta_raw, const float *delta_bias,
+                                        const void *u_b, const void *delta_raw_b,
+                                        const float *delta_bias_b, const void *z,
+                                        const float *A_log, const float *A_b_log,
+                                        const void *B, const void *C, const void *B_b, const void *C_b,
+                                        const float *D, const float *D_b, void *out,
+                                        int64_t batch, int64_t dim, int64_t seqlen, int d_state,
+                                        vmscan_dtype dtype, void *workspace, size_t workspace_bytes,
+                                        int64_t chunk_len, int stage, hipStream_t stream);
+
 /* Workspace bytes for ss2d_cross_scan_fwd / _ex (chunk_len 0 = library choice); 0 if invalid. */
 size_t ss2d_cross_scan_workspace_bytes(int64_t batch, int64_t dim, int64_t H, int64_t W, int d_state,
                                        vmscan_dtype dtype);

@@ -44,6 +44,11 @@ def _load():
     lib.vmscan_fwd_bidir_ex.argtypes = fwd_args + [_i64, _c_void_p]
     lib.vmscan_fwd_bidir_stage.restype = ctypes.c_int
     lib.vmscan_fwd_bidir_stage.argtypes = fwd_args + [_i64, ctypes.c_int, _c_void_p]
+    v2_args = [_c_void_p] * 16 + [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _c_void_p, ctypes.c_size_t, _i64]
+    lib.vmscan_fwd_bidir_v2.restype = ctypes.c_int
+    lib.vmscan_fwd_bidir_v2.argtypes = v2_args + [_c_void_p]
+    lib.vmscan_fwd_bidir_v2_stage.restype = ctypes.c_int
+    lib.vmscan_fwd_bidir_v2_stage.argtypes = v2_args + [ctypes.c_int, _c_void_p]
     lib.ss2d_cross_scan_workspace_bytes.restype = ctypes.c_size_t
     lib.ss2d_cross_scan_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int]
     lib.ss2d_cross_scan_workspace_bytes_ex.restype = ctypes.c_size_t
@@ -167,6 +172,41 @@ def vmscan_fwd_bidir(u, delta_raw, z, A_log, A_b_log, B, C, B_b, C_b, D, D_b, de
         _ptr(u), _ptr(delta_raw), _ptr(z), _ptr(A_log), _ptr(A_b_log), _ptr(B), _ptr(C), _ptr(B_b), _ptr(C_b),
         _ptr(D), _ptr(D_b), _ptr(delta_bias), _ptr(out), nb, nd, L, D_STATE, dt,
         _ptr(workspace), _nbytes(workspace), int(chunk_len), int(stage), _stream(stream, dev)))
+    return out
+
+
+def vmscan_fwd_bidir_v2(u, delta_raw, delta_bias, u_b, delta_raw_b, delta_bias_b, z, A_log, A_b_log, B, C, B_b,
+                        C_b, D, D_b, out=None, chunk_len=0, workspace=None, stream=None, stage=3):
+    """Bidirectional scan whose backward branch has its own u_b, delta_raw_b and delta_bias_b
+    (vmscan_fwd_bidir_v2_stage); the other arguments as for ``vmscan_fwd_bidir``.  u_b and
+    delta_raw_b are [batch, dim, L] in original token order, delta_bias_b is [dim] float32; any
+    of them may be the forward branch's tensor."""
+    if u.dim() != 3:
+        raise ValueError("u must be [batch, dim, L]")
+    nb, nd, L = u.shape
+    dev = u.device
+    adt = u.dtype
+    dt = _act_dtype(u)
+    for name, t in (("u", u), ("delta_raw", delta_raw), ("u_b", u_b), ("delta_raw_b", delta_raw_b), ("z", z)):
+        _need(t, name, (nb, nd, L), adt, dev)
+    for name, t in (("B", B), ("C", C), ("B_b", B_b), ("C_b", C_b)):
+        _need(t, name, (nb, D_STATE, L), adt, dev)
+    for name, t in (("A_log", A_log), ("A_b_log", A_b_log)):
+        _need(t, name, (nd, D_STATE), torch.float32, dev)
+    for name, t in (("D", D), ("D_b", D_b), ("delta_bias", delta_bias), ("delta_bias_b", delta_bias_b)):
+        _need(t, name, (nd,), torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(u)
+    else:
+        _need(out, "out", (nb, nd, L), adt, dev)
+    lib = load()
+    wsb = lib.vmscan_fwd_bidir_workspace_bytes_ex(nb, nd, L, D_STATE, dt, int(chunk_len))
+    workspace = _workspace(workspace, wsb, dev)
+    _check(lib.vmscan_fwd_bidir_v2_stage(
+        _ptr(u), _ptr(delta_raw), _ptr(delta_bias), _ptr(u_b), _ptr(delta_raw_b), _ptr(delta_bias_b), _ptr(z),
+        _ptr(A_log), _ptr(A_b_log), _ptr(B), _ptr(C), _ptr(B_b), _ptr(C_b), _ptr(D), _ptr(D_b), _ptr(out),
+        nb, nd, L, D_STATE, dt, _ptr(workspace), _nbytes(workspace), int(chunk_len), int(stage),
+        _stream(stream, dev)))
     return out
 
 

@@ -174,6 +174,7 @@ __device__ __forceinline__ void rotate_priority(int step) {
 }
 
 struct DirArgs {
+  const void* u;       // scan input, [batch][dim][L] in position order (batch stride u_bs)
   const void* draw;    // Δ_raw; element (b, d, idx) at b*draw_bs + d*L + idx
   int64_t draw_bs;
   const void* B;       // (b, n, idx) at b*bc_bs + n*L + idx
@@ -186,7 +187,6 @@ struct DirArgs {
 };
 
 struct ScanArgs {
-  const void* u;   // [batch][dim][L] (element of position s via the order map)
   int64_t u_bs;    // batch stride of u, z, out, wsy
   const void* z;   // gate, same layout as u, or null
   void* out;
@@ -366,7 +366,7 @@ struct Window {
   using Dr = Dir<MODE, DIR>;
   Run8<T> u, x;
   __device__ __forceinline__ void load(const ScanArgs& a, const Lane& l, const DirArgs& da, int i0) {
-    const T* ub = static_cast<const T*>(a.u) + static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(l.dd) * a.L;
+    const T* ub = static_cast<const T*>(da.u) + static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(l.dd) * a.L;
     const T* db = static_cast<const T*>(da.draw) + static_cast<int64_t>(l.b) * da.draw_bs + static_cast<int64_t>(l.dd) * a.L;
     const int64_t p = Dr::pos(l, i0);
     u.load(ub + (Dr::kPosSgn > 0 ? p : p - (kWin - 1)));
@@ -464,7 +464,7 @@ __device__ __forceinline__ float single_step(const ScanArgs& a, const Lane& l, c
                                              int i, const float (&A2)[kH], float (&h)[kH], scalar_fp bct,
                                              float (&bcA)[kBC], float* dl_out) {
   using Dr = Dir<MODE, DIR>;
-  const T* ub = static_cast<const T*>(a.u) + static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(l.dd) * a.L;
+  const T* ub = static_cast<const T*>(da.u) + static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(l.dd) * a.L;
   const T* db = static_cast<const T*>(da.draw) + static_cast<int64_t>(l.b) * da.draw_bs + static_cast<int64_t>(l.dd) * a.L;
   const float uu = ld_act(ub, Dr::pos(l, i));
   const float dl = delta2(ld_act(db, Dr::sidx(a, l, i)), bias);
@@ -1068,12 +1068,13 @@ vmscan_status check_workspace(const void* workspace, size_t workspace_bytes, siz
 }
 
 // Validation and kernel arguments of the bidirectional scan (shared by its entry points).
-vmscan_status vim_args(ScanArgs& a, const void* u, const void* delta_raw, const void* z, const float* A_log,
+vmscan_status vim_args(ScanArgs& a, const void* u, const void* delta_raw, const float* delta_bias, const void* u_b,
+                       const void* delta_raw_b, const float* delta_bias_b, const void* z, const float* A_log,
                        const float* A_b_log, const void* B, const void* C, const void* B_b, const void* C_b,
-                       const float* D, const float* D_b, const float* delta_bias, void* out, int64_t batch,
-                       int64_t dim, int64_t seqlen, int d_state, vmscan_dtype dtype, void* workspace,
-                       size_t workspace_bytes, int64_t chunk_len) {
-  const void* ptrs[] = {u, delta_raw, z, A_log, A_b_log, B, C, B_b, C_b, D, D_b, delta_bias, out};
+                       const float* D, const float* D_b, void* out, int64_t batch, int64_t dim, int64_t seqlen,
+                       int d_state, vmscan_dtype dtype, void* workspace, size_t workspace_bytes, int64_t chunk_len) {
+  const void* ptrs[] = {u, delta_raw, delta_bias, u_b, delta_raw_b, delta_bias_b, z, A_log, A_b_log, B, C, B_b, C_b,
+                        D, D_b, out};
   for (const void* p : ptrs)
     if (!p) return VMSCAN_ERR_NULL;
   if (!shape_ok(batch, dim, seqlen) || chunk_len < 0) return VMSCAN_ERR_SHAPE;
@@ -1084,15 +1085,14 @@ vmscan_status vim_args(ScanArgs& a, const void* u, const void* delta_raw, const 
   const vmscan_status ws =
       check_workspace(workspace, workspace_bytes, bct_bytes(batch, seqlen) + agg_bytes(batch, dim, seqlen, K));
   if (ws != VMSCAN_OK) return ws;
-  a.u = u;
   a.u_bs = dim * seqlen;
   a.z = z;
   a.out = out;
   a.wsy = nullptr;
   a.bct = static_cast<float*>(workspace);
   a.agg = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + bct_bytes(batch, seqlen));
-  a.d0 = DirArgs{delta_raw, dim * seqlen, B, C, kN * seqlen, A_log, D, delta_bias, 0};
-  a.d1 = DirArgs{delta_raw, dim * seqlen, B_b, C_b, kN * seqlen, A_b_log, D_b, delta_bias, 0};
+  a.d0 = DirArgs{u, delta_raw, dim * seqlen, B, C, kN * seqlen, A_log, D, delta_bias, 0};
+  a.d1 = DirArgs{u_b, delta_raw_b, dim * seqlen, B_b, C_b, kN * seqlen, A_b_log, D_b, delta_bias_b, 0};
   a.L = seqlen;
   a.dim = static_cast<int>(dim);
   a.batch = static_cast<int>(batch);
@@ -1153,18 +1153,42 @@ vmscan_status vmscan_fwd_bidir_ex(const void* u, const void* delta_raw, const vo
                                 seqlen, d_state, dtype, workspace, workspace_bytes, chunk_len, 3, stream);
 }
 
+vmscan_status vmscan_fwd_bidir_v2_stage(const void* u, const void* delta_raw, const float* delta_bias, const void* u_b,
+                                        const void* delta_raw_b, const float* delta_bias_b, const void* z,
+                                        const float* A_log, const float* A_b_log, const void* B, const void* C,
+                                        const void* B_b, const void* C_b, const float* D, const float* D_b, void* out,
+                                        int64_t batch, int64_t dim, int64_t seqlen, int d_state, vmscan_dtype dtype,
+                                        void* workspace, size_t workspace_bytes, int64_t chunk_len, int stage,
+                                        hipStream_t stream) {
+  if (stage < 1 || stage > 3) return VMSCAN_ERR_UNSUPPORTED;
+  ScanArgs a{};
+  const vmscan_status st =
+      vim_args(a, u, delta_raw, delta_bias, u_b, delta_raw_b, delta_bias_b, z, A_log, A_b_log, B, C, B_b, C_b, D, D_b,
+               out, batch, dim, seqlen, d_state, dtype, workspace, workspace_bytes, chunk_len);
+  if (st != VMSCAN_OK) return st;
+  return run_pair_dtype<kModeVim>(a, dtype, stream, stage);
+}
+
+vmscan_status vmscan_fwd_bidir_v2(const void* u, const void* delta_raw, const float* delta_bias, const void* u_b,
+                                  const void* delta_raw_b, const float* delta_bias_b, const void* z,
+                                  const float* A_log, const float* A_b_log, const void* B, const void* C,
+                                  const void* B_b, const void* C_b, const float* D, const float* D_b, void* out,
+                                  int64_t batch, int64_t dim, int64_t seqlen, int d_state, vmscan_dtype dtype,
+                                  void* workspace, size_t workspace_bytes, int64_t chunk_len, hipStream_t stream) {
+  return vmscan_fwd_bidir_v2_stage(u, delta_raw, delta_bias, u_b, delta_raw_b, delta_bias_b, z, A_log, A_b_log, B, C,
+                                   B_b, C_b, D, D_b, out, batch, dim, seqlen, d_state, dtype, workspace,
+                                   workspace_bytes, chunk_len, 3, stream);
+}
+
 vmscan_status vmscan_fwd_bidir_stage(const void* u, const void* delta_raw, const void* z, const float* A_log,
                                      const float* A_b_log, const void* B, const void* C, const void* B_b,
                                      const void* C_b, const float* D, const float* D_b, const float* delta_bias,
                                      void* out, int64_t batch, int64_t dim, int64_t seqlen, int d_state,
                                      vmscan_dtype dtype, void* workspace, size_t workspace_bytes, int64_t chunk_len,
                                      int stage, hipStream_t stream) {
-  if (stage < 1 || stage > 3) return VMSCAN_ERR_UNSUPPORTED;
-  ScanArgs a{};
-  const vmscan_status st = vim_args(a, u, delta_raw, z, A_log, A_b_log, B, C, B_b, C_b, D, D_b, delta_bias, out, batch,
-                                    dim, seqlen, d_state, dtype, workspace, workspace_bytes, chunk_len);
-  if (st != VMSCAN_OK) return st;
-  return run_pair_dtype<kModeVim>(a, dtype, stream, stage);
+  return vmscan_fwd_bidir_v2_stage(u, delta_raw, delta_bias, u, delta_raw, delta_bias, z, A_log, A_b_log, B, C, B_b,
+                                   C_b, D, D_b, out, batch, dim, seqlen, d_state, dtype, workspace, workspace_bytes,
+                                   chunk_len, stage, stream);
 }
 
 vmscan_status vmscan_fwd_bidir(const void* u, const void* delta_raw, const void* z, const float* A_log,
@@ -1220,8 +1244,8 @@ vmscan_status ss2d_cross_scan_fwd_ex(const void* x, const void* delta_raw, const
     return static_cast<const void*>(static_cast<const unsigned char*>(p) + elems * static_cast<int64_t>(esz));
   };
   // Direction k of delta_raw [batch, 4, dim, L] and B/C [batch, 4, 16, L]; params [4, dim(, 16)].
-  auto dir_args = [&](int k, int rev) {
-    return DirArgs{off(delta_raw, k * dim * L), 4 * dim * L, off(B, k * kN * L), off(C, k * kN * L), 4 * kN * L,
+  auto dir_args = [&](const void* u, int k, int rev) {
+    return DirArgs{u, off(delta_raw, k * dim * L), 4 * dim * L, off(B, k * kN * L), off(C, k * kN * L), 4 * kN * L,
                    A_log + k * dim * kN, D + k * dim, delta_bias + k * dim, rev};
   };
 
@@ -1244,10 +1268,9 @@ vmscan_status ss2d_cross_scan_fwd_ex(const void* x, const void* delta_raw, const
   // writes its combined values as an fp32 image in the same column-major order.
   vmscan_status st = launch_transpose(x, wsp + lay.xt, nimg, static_cast<int>(H), static_cast<int>(W), esz, stream);
   if (st != VMSCAN_OK) return st;
-  a.u = wsp + lay.xt;
   a.wsy = reinterpret_cast<float*>(wsp + lay.col_img);
-  a.d0 = dir_args(1, 0);
-  a.d1 = dir_args(3, 1);
+  a.d0 = dir_args(wsp + lay.xt, 1, 0);
+  a.d1 = dir_args(wsp + lay.xt, 3, 1);
   st = run_pair_dtype<kModeFirstPair>(a, dtype, stream);
   if (st != VMSCAN_OK) return st;
   // Back to row-major pixels, then the row pair (direction 0 and its reverse, direction 2) adds
@@ -1256,10 +1279,9 @@ vmscan_status ss2d_cross_scan_fwd_ex(const void* x, const void* delta_raw, const
   st = launch_transpose(wsp + lay.col_img, wsp + lay.row_img, nimg, static_cast<int>(W), static_cast<int>(H), 4,
                         stream);
   if (st != VMSCAN_OK) return st;
-  a.u = x;
   a.wsy = reinterpret_cast<float*>(wsp + lay.row_img);
-  a.d0 = dir_args(0, 0);
-  a.d1 = dir_args(2, 1);
+  a.d0 = dir_args(x, 0, 0);
+  a.d1 = dir_args(x, 2, 1);
   return run_pair_dtype<kModeSecondPair>(a, dtype, stream);
 }
 

@@ -7,6 +7,7 @@ from .vmscan_inputs import (  # noqa: F401
     CONFIGS,
     round_bf16,
     make_vim_inputs,
+    make_vim_v2_inputs,
     make_ss2d_inputs,
     dt_bias,
 )

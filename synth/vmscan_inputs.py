@@ -11,8 +11,9 @@ any layer can be regenerated independently.  Distributions follow the workloads:
 * Δ bias = inverse softplus of dt, dt log-uniform on [1e-3, 1e-1], computed in float64 and
   stored as float32 (the dt initialisation range stated for SS2D).
 
-Tensor ids: Vim u=0, z=1, Δ_raw=2, B=3, C=4, B_b=5, C_b=6, dt=7; SS2D x=0, z=1 and, for
-direction k, Δ_raw=10k+2, B=10k+3, C=10k+4, dt=10k+7.
+Tensor ids: Vim u=0, z=1, Δ_raw=2, B=3, C=4, B_b=5, C_b=6, dt=7 and, for a separate backward
+branch, u_b=8, Δ_raw_b=9, dt_b=17; SS2D x=0, z=1 and, for direction k, Δ_raw=10k+2, B=10k+3,
+C=10k+4, dt=10k+7.
 """
 import numpy as np
 
@@ -86,6 +87,17 @@ def make_vim_inputs(cfg, layer=0, batch=None, dim=None, seqlen=None, d_state=Non
         delta_bias=dt_bias(cfg, layer, 7, nd),
         dtype=dt,
     )
+
+
+def make_vim_v2_inputs(cfg, layer=0, batch=None, dim=None, seqlen=None, d_state=None, dtype=None):
+    """``make_vim_inputs`` plus a separate backward branch: u_b, delta_raw_b (same distributions)
+    and delta_bias_b (its own dt draw), for the bidirectional scan with v2 parameter sets."""
+    p = make_vim_inputs(cfg, layer, batch, dim, seqlen, d_state, dtype)
+    nb, nd, L = p["u"].shape
+    p["u_b"] = _normal(cfg, layer, 8, (nb, nd, L), p["dtype"])
+    p["delta_raw_b"] = _normal(cfg, layer, 9, (nb, nd, L), p["dtype"])
+    p["delta_bias_b"] = dt_bias(cfg, layer, 17, nd)
+    return p
 
 
 def make_ss2d_inputs(cfg=4, layer=0, batch=None, dim=None, H=None, W=None, d_state=None, dtype=None, with_z=False):

@@ -43,6 +43,32 @@ def oracle_vim(p, batches=None, alias_v1=False):
                        sel(p["C"]), sel(B_b), sel(C_b), p["D"], D_b, p["delta_bias"])
 
 
+def run_vim_v2(p, chunk_len=0, alias=()):
+    """vmscan_fwd_bidir_v2 on the device; names in ``alias`` (u_b, delta_raw_b, delta_bias_b) pass the
+    forward branch's tensor instead of the backward one."""
+    import selective_state_space_41_amd as V
+    dt = p["dtype"]
+    act = {k: tdev(p[k], dt) for k in ("u", "delta_raw", "u_b", "delta_raw_b", "z", "B", "C", "B_b", "C_b")}
+    par = {k: pdev(p[k]) for k in ("A_log", "A_b_log", "D", "D_b", "delta_bias", "delta_bias_b")}
+    fwd_of = {"u_b": act["u"], "delta_raw_b": act["delta_raw"], "delta_bias_b": par["delta_bias"]}
+    pick = lambda k, t: fwd_of[k] if k in alias else t
+    out = V.vmscan_fwd_bidir_v2(act["u"], act["delta_raw"], par["delta_bias"], pick("u_b", act["u_b"]),
+                                pick("delta_raw_b", act["delta_raw_b"]), pick("delta_bias_b", par["delta_bias_b"]),
+                                act["z"], par["A_log"], par["A_b_log"], act["B"], act["C"], act["B_b"], act["C_b"],
+                                par["D"], par["D_b"], chunk_len=chunk_len)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy()
+
+
+def oracle_vim_v2(p, batches=None, alias=()):
+    sel = (lambda a: a) if batches is None else (lambda a: a[batches])
+    fwd_of = {"u_b": "u", "delta_raw_b": "delta_raw", "delta_bias_b": "delta_bias"}
+    g = lambda k: p[fwd_of[k]] if k in alias else p[k]
+    return O.vim_bidir_v2(sel(p["u"]), sel(p["delta_raw"]), p["delta_bias"], sel(g("u_b")), sel(g("delta_raw_b")),
+                          g("delta_bias_b"), sel(p["z"]), p["A_log"], p["A_b_log"], sel(p["B"]), sel(p["C"]),
+                          sel(p["B_b"]), sel(p["C_b"]), p["D"], p["D_b"])
+
+
 def run_ss2d(p, chunk_len=0):
     import selective_state_space_41_amd as V
     dt = p["dtype"]

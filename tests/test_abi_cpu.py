@@ -77,6 +77,28 @@ def test_fwd_null_pointers(lib):
         assert _fwd(lib, p) == ERR_NULL, i
 
 
+def _fwd_v2(lib, ptrs, nb=2, nd=16, L=8, ds=16, dt=1, ws=None, wsb=0, chunk=0, stage=3):
+    args = [VP(p) for p in ptrs] + [I64(nb), I64(nd), I64(L), ctypes.c_int(ds), ctypes.c_int(dt),
+                                     VP(ws), ctypes.c_size_t(wsb), I64(chunk), ctypes.c_int(stage), VP(0)]
+    return lib.vmscan_fwd_bidir_v2_stage(*args)
+
+
+def test_fwd_v2_errors(lib):
+    """The separate-backward-branch entry point validates its three extra pointers like the others."""
+    for i in range(16):
+        p = _good_ptrs(16)
+        p[i] = 0
+        assert _fwd_v2(lib, p) == ERR_NULL, i
+    for i in range(16):
+        p = _good_ptrs(16)
+        p[i] += 4
+        assert _fwd_v2(lib, p) == ERR_ALIGN, i
+    assert _fwd_v2(lib, _good_ptrs(16), L=0) == ERR_SHAPE
+    assert _fwd_v2(lib, _good_ptrs(16), ds=32) == ERR_UNSUPPORTED
+    assert _fwd_v2(lib, _good_ptrs(16), stage=4) == ERR_UNSUPPORTED
+    assert _fwd_v2(lib, _good_ptrs(16), L=100, chunk=16) == ERR_WORKSPACE
+
+
 def test_fwd_bad_shapes(lib):
     for nb, nd, L in ((0, 16, 8), (2, 0, 8), (2, 16, 0), (-1, 16, 8), (1, 1, 1 << 31)):
         assert _fwd(lib, _good_ptrs(), nb=nb, nd=nd, L=L) == ERR_SHAPE

@@ -9,7 +9,7 @@ import pytest
 
 import oracle as O
 import synth
-from gpu_common import TOL, oracle_ss2d, oracle_vim, run_ss2d, run_vim
+from gpu_common import TOL, oracle_ss2d, oracle_vim, oracle_vim_v2, run_ss2d, run_vim, run_vim_v2
 
 pytestmark = pytest.mark.gpu
 
@@ -50,6 +50,32 @@ def test_vim_chunked(case, dtype):
     nb, nd, L, K = case
     p = synth.make_vim_inputs(0, layer=200 + L + K, batch=nb, dim=nd, seqlen=L, dtype=dtype)
     _report(f"vim chunked {case} {dtype}", O.rel_err(run_vim(p, chunk_len=K), oracle_vim(p)), TOL[dtype])
+
+
+V2_SHAPES = [(1, 16, 1), (2, 17, 15), (1, 40, 33), (2, 24, 197), (1, 16, 300)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", V2_SHAPES, ids=[f"b{b}d{d}l{l}" for b, d, l in V2_SHAPES])
+def test_vim_v2(shape, dtype):
+    """Separate backward branch (u_b, Δ_raw_b, bias_b), library-chosen and forced chunking."""
+    nb, nd, L = shape
+    p = synth.make_vim_v2_inputs(0, layer=300 + L, batch=nb, dim=nd, seqlen=L, dtype=dtype)
+    ref = oracle_vim_v2(p)
+    _report(f"vim v2 {shape} {dtype}", O.rel_err(run_vim_v2(p), ref), TOL[dtype])
+    if L > 20:
+        _report(f"vim v2 {shape} {dtype} K=16", O.rel_err(run_vim_v2(p, chunk_len=16), ref), TOL[dtype])
+
+
+def test_vim_v2_aliasing():
+    """Each of u_b, Δ_raw_b, bias_b may be the forward branch's tensor; with all three aliased the
+    v2 entry point gives exactly the shared-input entry point's output."""
+    p = synth.make_vim_v2_inputs(0, layer=9, batch=2, dim=48, seqlen=120, dtype="f32")
+    for alias in (("u_b",), ("delta_raw_b",), ("delta_bias_b",)):
+        _report(f"vim v2 alias {alias}", O.rel_err(run_vim_v2(p, alias=alias), oracle_vim_v2(p, alias=alias)), 1e-5)
+    all3 = ("u_b", "delta_raw_b", "delta_bias_b")
+    assert np.array_equal(run_vim_v2(p, alias=all3), run_vim(p))
+    assert np.array_equal(run_vim_v2(p, alias=all3, chunk_len=32), run_vim(p, chunk_len=32))
 
 
 def test_vim_v1_aliasing():
@@ -105,6 +131,20 @@ def test_config0_full():
 def test_config1_full():
     p = synth.make_vim_inputs(1)
     _report("config 1 (Vim-Ti bf16 B128 D384 L197)", O.rel_err(run_vim(p), oracle_vim(p)), 2e-2)
+
+
+def test_config1_v2_full_sampled():
+    """The Vim-Ti workload with a separate backward branch, in the bench's launch configuration."""
+    p = synth.make_vim_v2_inputs(1)
+    bsel = np.array([0, 63, 127])
+    _report("config 1 v2 (separate backward branch, batches 0,63,127)",
+            O.rel_err(run_vim_v2(p)[bsel], oracle_vim_v2(p, batches=bsel)), 2e-2)
+
+
+def test_config3_v2_sampled():
+    p = synth.make_vim_v2_inputs(3)
+    bsel = np.array([3])
+    _report("config 3 v2 (batch 3)", O.rel_err(run_vim_v2(p)[bsel], oracle_vim_v2(p, batches=bsel)), 2e-2)
 
 
 def test_config2_all_layers_sampled():
