@@ -13,6 +13,8 @@ from .vmscan_oracle import (  # noqa: F401
     scan_1d_semiseparable,
     vim_bidir,
     vim_bidir_v2,
+    scan_1d_bwd,
+    vim_bidir_v2_bwd,
     ss2d_orders,
     ss2d_cross_scan,
     ss2d_cross_scan_pathwalk,

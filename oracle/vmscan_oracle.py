@@ -159,6 +159,92 @@ def vim_bidir_v2(u, delta_raw, delta_bias, u_b, delta_raw_b, delta_bias_b, z, A_
     return (y_f + f(y_b_rev)) / 2.0
 
 
+def scan_1d_bwd(u, delta_raw, A_log, B, C, D, delta_bias, g):
+    """Gradients of one ungated direction (``scan_1d``) given g = dL/ds [batch, dim, L].
+
+    The pages give the forward only and ask that its gradient be checked numerically ([P5] §4
+    runs torch.autograd.gradcheck on the bidirectional scan); this is the exact derivative of
+    ``scan_1d``, by the adjoint of its recurrence.  With a_t,n = exp(Δ_t A_n) and
+    h_t = a_t h_{t-1} + Δ_t B_t u_t, the adjoint state λ_t = dL/dh_t (h_t reaches s_t directly
+    and h_{t+1} through a_{t+1}) runs backwards:
+
+        λ_t,n = g_t C_t,n + a_{t+1},n λ_{t+1},n,   λ_L = 0
+        dL/dC_t,n     = g_t h_t,n
+        dL/dB_t,n     = λ_t,n Δ_t u_t
+        dL/du_t       = g_t D + Δ_t Σ_n λ_t,n B_t,n
+        dL/dΔ_t       = Σ_n λ_t,n (A_n a_t,n h_{t-1},n + B_t,n u_t)
+        dL/dΔ_raw_t   = dL/dΔ_t sigmoid(Δ_raw_t + bias)          (softplus' = sigmoid)
+        dL/dbias      = Σ_{b,t} dL/dΔ_raw_t
+        dL/dA_n       = Σ_{b,t} λ_t,n Δ_t a_t,n h_{t-1},n,  dL/dA_log = dL/dA * A   (A = -exp(A_log))
+        dL/dD         = Σ_{b,t} g_t u_t
+
+    Returns dict(s, du, ddelta_raw, dA_log [dim, N], dB, dC [batch, N, L], dD, ddelta_bias [dim]).
+    The forward states are recomputed and kept for every t (fine at oracle sizes).
+    """
+    u = np.asarray(u, dtype=np.float64)
+    x = np.asarray(delta_raw, dtype=np.float64) + np.asarray(delta_bias, dtype=np.float64)[None, :, None]
+    A = -np.exp(np.asarray(A_log, dtype=np.float64))            # [dim, N]
+    B = np.asarray(B, dtype=np.float64)
+    C = np.asarray(C, dtype=np.float64)
+    D = np.asarray(D, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    nb, nd, L = u.shape
+    N = A.shape[1]
+    delta = softplus(x)
+    # forward, keeping h_t (index t + 1; index 0 is h_{-1} = 0) and a_t
+    hs = np.zeros((L + 1, nb, nd, N))
+    av = np.empty((L, nb, nd, N))
+    s = np.empty((nb, nd, L))
+    for t in range(L):
+        av[t] = np.exp(delta[:, :, t][:, :, None] * A[None])
+        hs[t + 1] = av[t] * hs[t] + delta[:, :, t][:, :, None] * B[:, None, :, t] * u[:, :, t][:, :, None]
+        s[:, :, t] = np.sum(hs[t + 1] * C[:, None, :, t], axis=2) + D[None, :] * u[:, :, t]
+    du = g * D[None, :, None]
+    ddelta = np.zeros((nb, nd, L))
+    dA = np.zeros((nd, N))
+    dB = np.zeros((nb, N, L))
+    dC = np.zeros((nb, N, L))
+    lam = np.zeros((nb, nd, N))
+    for t in range(L - 1, -1, -1):
+        carry = av[t + 1] * lam if t + 1 < L else 0.0
+        lam = g[:, :, t][:, :, None] * C[:, None, :, t] + carry
+        dl = delta[:, :, t][:, :, None]
+        dC[:, :, t] = np.sum(g[:, :, t][:, :, None] * hs[t + 1], axis=1)
+        dB[:, :, t] = np.sum(lam * dl * u[:, :, t][:, :, None], axis=1)
+        du[:, :, t] += delta[:, :, t] * np.sum(lam * B[:, None, :, t], axis=2)
+        decay_term = A[None] * av[t] * hs[t]
+        ddelta[:, :, t] = np.sum(lam * (decay_term + B[:, None, :, t] * u[:, :, t][:, :, None]), axis=2)
+        dA += np.sum(lam * dl * av[t] * hs[t], axis=0)
+    ddr = ddelta * expit(x)
+    return dict(s=s, du=du, ddelta_raw=ddr, ddelta_bias=ddr.sum(axis=(0, 2)), dA_log=dA * A, dB=dB, dC=dC,
+                dD=np.sum(g * u, axis=(0, 2)))
+
+
+def vim_bidir_v2_bwd(u, delta_raw, delta_bias, u_b, delta_raw_b, delta_bias_b, z, A_log, A_b_log, B, C, B_b, C_b,
+                     D, D_b, dout):
+    """Gradients of ``vim_bidir_v2`` for the upstream gradient dout = dL/dout [batch, dim, L].
+
+    out = (s_f + flip s_b') silu(z) / 2, so with σ = sigmoid(z):
+        dL/dz  = dout (s_f + s_b) / 2 * σ (1 + z (1 - σ))           (silu' = σ (1 + z (1 - σ)))
+        dL/ds  = dout silu(z) / 2 for both branches (flipped for the backward one)
+    and each branch's gradients come from ``scan_1d_bwd``; the backward branch's per-position
+    gradients are flipped back to original token order.  For shared inputs (``vim_bidir``) the
+    two branches' du, dΔ_raw and dbias add up.
+    """
+    f = lambda x: np.flip(np.asarray(x, dtype=np.float64), axis=-1)
+    z = np.asarray(z, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    gs = dout * silu(z) / 2.0
+    fw = scan_1d_bwd(u, delta_raw, A_log, B, C, D, delta_bias, gs)
+    bw = scan_1d_bwd(f(u_b), f(delta_raw_b), A_b_log, f(B_b), f(C_b), D_b, delta_bias_b, f(gs))
+    sig = expit(z)
+    dz = dout * (fw["s"] + f(bw["s"])) / 2.0 * sig * (1.0 + z * (1.0 - sig))
+    return dict(du=fw["du"], ddelta_raw=fw["ddelta_raw"], ddelta_bias=fw["ddelta_bias"],
+                du_b=f(bw["du"]), ddelta_raw_b=f(bw["ddelta_raw"]), ddelta_bias_b=bw["ddelta_bias"], dz=dz,
+                dA_log=fw["dA_log"], dA_b_log=bw["dA_log"], dB=fw["dB"], dC=fw["dC"], dB_b=f(bw["dB"]),
+                dC_b=f(bw["dC"]), dD=fw["dD"], dD_b=bw["dD"])
+
+
 def ss2d_orders(x):
     """The four cross-scan sequences of [P4] §2.2 for x[batch, dim, H, W]:
     row-major flatten, column-major flatten (transpose then flatten), and each reversed."""

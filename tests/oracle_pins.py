@@ -1,5 +1,5 @@
 """Pins for the fp64 oracle: each ``pin_*`` takes an implementation namespace (with
-``scan_1d``, ``vim_bidir``, ``vim_bidir_v2``, ``ss2d_cross_scan``) and returns the list of failure messages
+``scan_1d``, ``vim_bidir``, ``vim_bidir_v2``, ``vim_bidir_v2_bwd``, ``ss2d_cross_scan``) and returns the list of failure messages
 (empty = pass).  They check the oracle against facts fixed by the mathematics, not against the
 oracle itself: hand-derived closed forms, brute force on tiny inputs, linearity, the flip
 identity, limits and the SS2D reductions.  ``test_oracle_pins`` runs them on the oracle;
@@ -375,6 +375,77 @@ def pin_v2_flip_identity(impl):
     return msgs
 
 
+V2_NAMES = ("u", "delta_raw", "delta_bias", "u_b", "delta_raw_b", "delta_bias_b", "z", "A_log", "A_b_log", "B", "C",
+            "B_b", "C_b", "D", "D_b")
+V2_GRADS = dict(u="du", delta_raw="ddelta_raw", delta_bias="ddelta_bias", u_b="du_b", delta_raw_b="ddelta_raw_b",
+                delta_bias_b="ddelta_bias_b", z="dz", A_log="dA_log", A_b_log="dA_b_log", B="dB", C="dC", B_b="dB_b",
+                C_b="dC_b", D="dD", D_b="dD_b")
+
+
+def pin_bwd_finite_differences(impl):
+    """Every gradient of the bidirectional scan (separate backward branch) against central finite
+    differences of the forward, element by element, on a tiny input: the numerical gradient check
+    the pages run on the bidirectional scan ([P5] §4).  With step 1e-6 in fp64 the difference
+    quotient is accurate to about 1e-9 relative; a wrong index, sign, factor or a dropped term in
+    any gradient shows up at the 1e-2 level or above."""
+    msgs = []
+    rng = np.random.default_rng(14)
+    p = rich_v2(rng, nb=2, nd=2, L=5, N=3)
+    dout = rng.standard_normal(p["u"].shape)
+    loss = lambda q: float(np.sum(O.vim_bidir_v2(*[q[k] for k in V2_NAMES]) * dout))
+    grads = impl.vim_bidir_v2_bwd(*[p[k] for k in V2_NAMES], dout)
+    eps = 1e-6
+    for k in V2_NAMES:
+        x = np.asarray(p[k], dtype=np.float64)
+        fd = np.zeros_like(x)
+        for i in np.ndindex(x.shape):
+            q = dict(p)
+            xp = x.copy()
+            xp[i] += eps
+            q[k] = xp
+            lp = loss(q)
+            xm = x.copy()
+            xm[i] -= eps
+            q[k] = xm
+            fd[i] = (lp - loss(q)) / (2 * eps)
+        got = np.asarray(grads[V2_GRADS[k]], dtype=np.float64)
+        if got.shape != fd.shape:
+            msgs.append(f"d{k}: shape {got.shape} != {fd.shape}")
+            continue
+        _check(msgs, f"d{k} vs finite differences", float(np.max(np.abs(got - fd)) / max(np.max(np.abs(fd)), 1e-12)), 1e-6)
+    return msgs
+
+
+def pin_bwd_shared_inputs(impl):
+    """With the backward branch's u, Δ_raw, bias equal to the forward branch's, the gradient of the
+    shared-input scan is the sum of the two branches' gradients (finite differences of vim_bidir)."""
+    msgs = []
+    rng = np.random.default_rng(15)
+    p = rich_vim(rng, nb=1, nd=2, L=4, N=3)
+    dout = rng.standard_normal(p["u"].shape)
+    g = impl.vim_bidir_v2_bwd(p["u"], p["delta_raw"], p["delta_bias"], p["u"], p["delta_raw"], p["delta_bias"], p["z"],
+                              p["A_log"], p["A_b_log"], p["B"], p["C"], p["B_b"], p["C_b"], p["D"], p["D_b"], dout)
+    loss = lambda q: float(np.sum(O.vim_bidir(q["u"], q["delta_raw"], q["z"], q["A_log"], q["A_b_log"], q["B"], q["C"],
+                                              q["B_b"], q["C_b"], q["D"], q["D_b"], q["delta_bias"]) * dout))
+    eps = 1e-6
+    for k, gk in (("u", g["du"] + g["du_b"]), ("delta_raw", g["ddelta_raw"] + g["ddelta_raw_b"]),
+                  ("delta_bias", g["ddelta_bias"] + g["ddelta_bias_b"])):
+        x = np.asarray(p[k], dtype=np.float64)
+        fd = np.zeros_like(x)
+        for i in np.ndindex(x.shape):
+            q = dict(p)
+            xp = x.copy()
+            xp[i] += eps
+            q[k] = xp
+            lp = loss(q)
+            xm = x.copy()
+            xm[i] -= eps
+            q[k] = xm
+            fd[i] = (lp - loss(q)) / (2 * eps)
+        _check(msgs, f"shared d{k}", float(np.max(np.abs(gk - fd)) / max(np.max(np.abs(fd)), 1e-12)), 1e-6)
+    return msgs
+
+
 ALL_PINS = [
     pin_softplus_silu,
     pin_golden_single_token,
@@ -392,4 +463,6 @@ ALL_PINS = [
     pin_v2_single_token,
     pin_v2_semiseparable,
     pin_v2_flip_identity,
+    pin_bwd_finite_differences,
+    pin_bwd_shared_inputs,
 ]

@@ -98,6 +98,61 @@ def _v2(u, dr, bias, ub, drb, biasb, z, Al, Abl, B, C, Bb, Cb, D, Db, bug=None, 
     return 0.5 * (yf + f(rev * O.silu(f(z))))
 
 
+def _scan_bwd(u, dr, Al, B, C, D, bias, g, bug=None):
+    from scipy.special import expit
+    u = np.asarray(u, dtype=np.float64)
+    x = np.asarray(dr, dtype=np.float64) + np.asarray(bias, dtype=np.float64)[None, :, None]
+    A = -np.exp(np.asarray(Al, dtype=np.float64))
+    B, C, D = (np.asarray(v, dtype=np.float64) for v in (B, C, D))
+    nb, nd, L = u.shape
+    N = A.shape[1]
+    delta = np.logaddexp(0.0, x)
+    hs = np.zeros((L + 1, nb, nd, N))
+    av = np.empty((L, nb, nd, N))
+    s = np.empty((nb, nd, L))
+    for t in range(L):
+        av[t] = np.exp(delta[:, :, t][:, :, None] * A[None])
+        hs[t + 1] = av[t] * hs[t] + delta[:, :, t][:, :, None] * B[:, None, :, t] * u[:, :, t][:, :, None]
+        s[:, :, t] = np.sum(hs[t + 1] * C[:, None, :, t], axis=2) + D[None, :] * u[:, :, t]
+    du = np.zeros_like(u) if bug == "du_no_D" else g * D[None, :, None]
+    ddelta = np.zeros((nb, nd, L))
+    dA = np.zeros((nd, N))
+    dB = np.zeros((nb, N, L))
+    dC = np.zeros((nb, N, L))
+    lam = np.zeros((nb, nd, N))
+    for t in range(L - 1, -1, -1):
+        at = av[t] if bug == "lambda_same_step_decay" else (av[t + 1] if t + 1 < L else 0.0)
+        lam = g[:, :, t][:, :, None] * C[:, None, :, t] + at * lam
+        dl = delta[:, :, t][:, :, None]
+        hc = hs[t] if bug == "dC_prev_state" else hs[t + 1]
+        dC[:, :, t] = np.sum(g[:, :, t][:, :, None] * hc, axis=1)
+        dB[:, :, t] = np.sum(lam * (1.0 if bug == "dB_no_delta" else dl) * u[:, :, t][:, :, None], axis=1)
+        du[:, :, t] += delta[:, :, t] * np.sum(lam * B[:, None, :, t], axis=2)
+        hp = hs[t + 1] if bug == "ddelta_next_state" else hs[t]
+        ddelta[:, :, t] = np.sum(lam * (A[None] * av[t] * hp + B[:, None, :, t] * u[:, :, t][:, :, None]), axis=2)
+        dA += np.sum(lam * dl * av[t] * hs[t], axis=0)
+    ddr = ddelta if bug == "no_sigmoid" else ddelta * expit(x)
+    return dict(s=s, du=du, ddelta_raw=ddr, ddelta_bias=ddr.sum(axis=(0, 2)),
+                dA_log=dA if bug == "dA_log_no_chain" else dA * A, dB=dB, dC=dC, dD=np.sum(g * u, axis=(0, 2)))
+
+
+def _v2_bwd(u, dr, bias, ub, drb, biasb, z, Al, Abl, B, C, Bb, Cb, D, Db, dout, bug=None):
+    from scipy.special import expit
+    f = lambda x: np.flip(np.asarray(x, dtype=np.float64), axis=-1)
+    z = np.asarray(z, dtype=np.float64)
+    gs = dout * O.silu(z) / 2.0
+    fw = _scan_bwd(u, dr, Al, B, C, D, bias, gs, bug=bug)
+    bw = _scan_bwd(f(ub), f(drb), Abl, f(Bb), f(Cb), Db, biasb, gs if bug == "bwd_g_not_flipped" else f(gs), bug=bug)
+    sig = expit(z)
+    dsilu = O.silu(z) if bug == "dz_silu_not_derivative" else sig * (1.0 + z * (1.0 - sig))
+    dz = dout * (fw["s"] + f(bw["s"])) / 2.0 * dsilu
+    back = (lambda a: a) if bug == "bwd_grads_not_flipped" else f
+    return dict(du=fw["du"], ddelta_raw=fw["ddelta_raw"], ddelta_bias=fw["ddelta_bias"], du_b=back(bw["du"]),
+                ddelta_raw_b=back(bw["ddelta_raw"]), ddelta_bias_b=bw["ddelta_bias"], dz=dz, dA_log=fw["dA_log"],
+                dA_b_log=bw["dA_log"], dB=fw["dB"], dC=fw["dC"], dB_b=back(bw["dB"]), dC_b=back(bw["dC"]),
+                dD=fw["dD"], dD_b=bw["dD"])
+
+
 def _ss2d(x, dr, Al, B, C, D, bias, z=None, bug=None, scan_bug=None):
     x = np.asarray(x, dtype=np.float64)
     nb, nd, H, W = x.shape
@@ -123,8 +178,9 @@ def _ss2d(x, dr, Al, B, C, D, bias, z=None, bug=None, scan_bug=None):
     return out
 
 
-def _impl(scan_bug=None, vim_bug=None, ss2d_bug=None, v2_bug=None):
+def _impl(scan_bug=None, vim_bug=None, ss2d_bug=None, v2_bug=None, bwd_bug=None):
     return types.SimpleNamespace(
+        vim_bidir_v2_bwd=lambda *a: _v2_bwd(*a, bug=bwd_bug),
         softplus=O.softplus,
         silu=O.silu,
         scan_1d=lambda *a: _scan(*a, bug=scan_bug),
@@ -139,6 +195,8 @@ SCAN_BUGS = ["A_not_exp", "A_sign", "swap_BC", "no_softplus", "exp_not_softplus"
 VIM_BUGS = ["bwd_uses_fwd_BC", "bwd_uses_fwd_A", "bwd_BC_not_flipped", "bwd_delta_not_flipped", "bwd_D_is_fwd_D",
             "gate_not_flipped", "no_flip_back", "sum_not_avg", "gate_silu_is_sigmoid"]
 SS2D_BUGS = ["col_as_reshape", "col_not_transposed_back", "rev_not_flipped_back", "avg4"]
+BWD_BUGS = ["du_no_D", "lambda_same_step_decay", "dC_prev_state", "dB_no_delta", "ddelta_next_state", "no_sigmoid",
+            "dA_log_no_chain", "bwd_g_not_flipped", "dz_silu_not_derivative", "bwd_grads_not_flipped"]
 V2_BUGS = ["v2_bwd_uses_fwd_u", "v2_bwd_uses_fwd_delta", "v2_bwd_uses_fwd_bias", "v2_fwd_uses_bwd_bias", "v2_ub_not_flipped"]
 
 
@@ -177,3 +235,8 @@ def test_ss2d_mutant_caught(bug):
 @pytest.mark.parametrize("bug", V2_BUGS)
 def test_v2_mutant_caught(bug):
     assert _caught(_impl(v2_bug=bug)), f"planted mistake {bug} passes every pin"
+
+
+@pytest.mark.parametrize("bug", BWD_BUGS)
+def test_bwd_mutant_caught(bug):
+    assert _caught(_impl(bwd_bug=bug)), f"planted mistake {bug} passes every pin"
