@@ -168,6 +168,41 @@ vmscan_status vmscan_fwd_bidir_v2_stage(const void *u, const void *delta_raw, co
                                         vmscan_dtype dtype, void *workspace, size_t workspace_bytes,
                                         int64_t chunk_len, int stage, hipStream_t stream);
 
+/*
+ * Gradients of vmscan_fwd_bidir_v2 (the backward pass, for training).  The pages define the
+ * forward and check its gradient numerically ([P5] §4 gradcheck); these are its exact
+ * derivatives.  Given the forward's inputs and dout = dL/dout [batch, dim, seqlen]:
+ *   du, ddelta_raw, du_b, ddelta_raw_b, dz   : [batch, dim, seqlen]  activation dtype
+ *   dB, dC, dB_b, dC_b                       : [batch, 16, seqlen]   activation dtype
+ *   dA_log, dA_b_log                         : [dim, 16]             float32
+ *   dD, dD_b, ddelta_bias, ddelta_bias_b     : [dim]                 float32
+ * Every gradient is written (not accumulated), summed over batch where the tensor has no batch
+ * dimension, in float32 and rounded once.  du_b, ddelta_raw_b and ddelta_bias_b may each be
+ * NULL: the backward branch's gradient for that input is then ADDED to the forward branch's
+ * output (du, ddelta_raw, ddelta_bias), which is the gradient of vmscan_fwd_bidir, whose two
+ * branches share u, delta_raw and delta_bias (pass the same tensor as u_b etc. then).
+ * The library recomputes the forward: it runs the forward scan keeping the un-gated sum, then
+ * each direction forward again storing its state every 8 steps, then backwards over the
+ * sequence with the adjoint recurrence.  Workspace: vmscan_bwd_bidir_v2_workspace_bytes.
+ * Gradient outputs must not alias each other or any input.  Validation and error codes as for
+ * vmscan_fwd_bidir_v2 (all pointers but the three optional ones are required, all 16-byte
+ * aligned); launches are asynchronous on `stream`.
+ */
+size_t vmscan_bwd_bidir_v2_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen, int d_state,
+                                           vmscan_dtype dtype);
+vmscan_status vmscan_bwd_bidir_v2(const void *u, const void *delta_raw, const float *delta_bias,
+                                  const void *u_b, const void *delta_raw_b, const float *delta_bias_b,
+                                  const void *z, const float *A_log, const float *A_b_log,
+                                  const void *B, const void *C, const void *B_b, const void *C_b,
+                                  const float *D, const float *D_b, const void *dout,
+                                  void *du, void *ddelta_raw, float *ddelta_bias,
+                                  void *du_b, void *ddelta_raw_b, float *ddelta_bias_b,
+                                  void *dz, float *dA_log, float *dA_b_log,
+                                  void *dB, void *dC, void *dB_b, void *dC_b, float *dD, float *dD_b,
+                                  int64_t batch, int64_t dim, int64_t seqlen, int d_state,
+                                  vmscan_dtype dtype, void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
 /* Workspace bytes for ss2d_cross_scan_fwd / _ex (chunk_len 0 = library choice); 0 if invalid. */
 size_t ss2d_cross_scan_workspace_bytes(int64_t batch, int64_t dim, int64_t H, int64_t W, int d_state,
                                        vmscan_dtype dtype);

@@ -49,6 +49,11 @@ def _load():
     lib.vmscan_fwd_bidir_v2.argtypes = v2_args + [_c_void_p]
     lib.vmscan_fwd_bidir_v2_stage.restype = ctypes.c_int
     lib.vmscan_fwd_bidir_v2_stage.argtypes = v2_args + [ctypes.c_int, _c_void_p]
+    lib.vmscan_bwd_bidir_v2_workspace_bytes.restype = ctypes.c_size_t
+    lib.vmscan_bwd_bidir_v2_workspace_bytes.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int]
+    lib.vmscan_bwd_bidir_v2.restype = ctypes.c_int
+    lib.vmscan_bwd_bidir_v2.argtypes = ([_c_void_p] * 31 + [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _c_void_p,
+                                                           ctypes.c_size_t, _c_void_p])
     lib.ss2d_cross_scan_workspace_bytes.restype = ctypes.c_size_t
     lib.ss2d_cross_scan_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int]
     lib.ss2d_cross_scan_workspace_bytes_ex.restype = ctypes.c_size_t
@@ -208,6 +213,46 @@ def vmscan_fwd_bidir_v2(u, delta_raw, delta_bias, u_b, delta_raw_b, delta_bias_b
         nb, nd, L, D_STATE, dt, _ptr(workspace), _nbytes(workspace), int(chunk_len), int(stage),
         _stream(stream, dev)))
     return out
+
+
+def vmscan_bwd_bidir_v2(u, delta_raw, delta_bias, u_b, delta_raw_b, delta_bias_b, z, A_log, A_b_log, B, C, B_b, C_b,
+                        D, D_b, dout, shared=False, workspace=None, stream=None):
+    """Gradients of ``vmscan_fwd_bidir_v2`` for ``dout`` (vmscan_bwd_bidir_v2); returns a dict with
+    du, ddelta_raw, ddelta_bias, du_b, ddelta_raw_b, ddelta_bias_b, dz, dA_log, dA_b_log, dB, dC,
+    dB_b, dC_b, dD, dD_b.  With ``shared=True`` (u_b is u, delta_raw_b is delta_raw, delta_bias_b
+    is delta_bias, i.e. ``vmscan_fwd_bidir``) the backward branch's du, ddelta_raw and ddelta_bias
+    are added into the forward ones and the ``_b`` entries are None."""
+    if u.dim() != 3:
+        raise ValueError("u must be [batch, dim, L]")
+    nb, nd, L = u.shape
+    dev = u.device
+    adt = u.dtype
+    dt = _act_dtype(u)
+    for name, t in (("u", u), ("delta_raw", delta_raw), ("u_b", u_b), ("delta_raw_b", delta_raw_b), ("z", z),
+                    ("dout", dout)):
+        _need(t, name, (nb, nd, L), adt, dev)
+    for name, t in (("B", B), ("C", C), ("B_b", B_b), ("C_b", C_b)):
+        _need(t, name, (nb, D_STATE, L), adt, dev)
+    for name, t in (("A_log", A_log), ("A_b_log", A_b_log)):
+        _need(t, name, (nd, D_STATE), torch.float32, dev)
+    for name, t in (("D", D), ("D_b", D_b), ("delta_bias", delta_bias), ("delta_bias_b", delta_bias_b)):
+        _need(t, name, (nd,), torch.float32, dev)
+    act = lambda: torch.empty_like(u)
+    bcs = lambda: torch.empty_like(B)
+    par = lambda *s: torch.empty(*s, dtype=torch.float32, device=dev)
+    g = dict(du=act(), ddelta_raw=act(), ddelta_bias=par(nd), dz=act(), dA_log=par(nd, D_STATE),
+             dA_b_log=par(nd, D_STATE), dB=bcs(), dC=bcs(), dB_b=bcs(), dC_b=bcs(), dD=par(nd), dD_b=par(nd))
+    g["du_b"], g["ddelta_raw_b"], g["ddelta_bias_b"] = (None, None, None) if shared else (act(), act(), par(nd))
+    lib = load()
+    wsb = lib.vmscan_bwd_bidir_v2_workspace_bytes(nb, nd, L, D_STATE, dt)
+    workspace = _workspace(workspace, wsb, dev)
+    _check(lib.vmscan_bwd_bidir_v2(
+        _ptr(u), _ptr(delta_raw), _ptr(delta_bias), _ptr(u_b), _ptr(delta_raw_b), _ptr(delta_bias_b), _ptr(z),
+        _ptr(A_log), _ptr(A_b_log), _ptr(B), _ptr(C), _ptr(B_b), _ptr(C_b), _ptr(D), _ptr(D_b), _ptr(dout),
+        *[_ptr(g[k]) for k in ("du", "ddelta_raw", "ddelta_bias", "du_b", "ddelta_raw_b", "ddelta_bias_b", "dz",
+                               "dA_log", "dA_b_log", "dB", "dC", "dB_b", "dC_b", "dD", "dD_b")],
+        nb, nd, L, D_STATE, dt, _ptr(workspace), _nbytes(workspace), _stream(stream, dev)))
+    return g
 
 
 def ss2d_cross_scan_fwd(x, delta_raw, A_log, B, C, D, delta_bias, z=None, out=None, chunk_len=0,

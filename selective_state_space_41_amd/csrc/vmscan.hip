@@ -198,7 +198,9 @@ struct ScanArgs {
   int dim, batch, K, nch, ngroups;
 };
 
-enum { kModeVim = 0, kModeFirstPair = 1, kModeSecondPair = 2 };
+// kModeVimSum: Vim order, but the epilogue stores the un-gated fp32 sum y_f + y_b to wsy (the
+// backward pass needs it for dL/dz).
+enum { kModeVim = 0, kModeFirstPair = 1, kModeSecondPair = 2, kModeVimSum = 3 };
 
 // ---------------------------------------------------------------------------------------------
 // B/C transpose: for half q, bct[b][dir][q][s][0..7] = B_dir[b][8q + 0..7, si(s)] ln 2 and
@@ -316,8 +318,8 @@ __global__ __launch_bounds__(256) void transpose16_kernel(const uint16_t* __rest
 // Scan kernels.  What differs between the forward and backward waves, the Vim and SS2D pairs and
 // the two scan orders is a template parameter, so the token loop has no data-dependent branches:
 //   DIR   0: step i visits chunk position i; 1: position Kc-1-i
-//   MODE  kModeVim / kModeFirstPair / kModeSecondPair (SS2D backward tensors are stored in
-//         reversed position order; the modes differ in the epilogue)
+//   MODE  kModeVim / kModeVimSum / kModeFirstPair / kModeSecondPair (SS2D backward tensors are
+//         stored in reversed position order; the modes differ in the epilogue)
 // The state half of a wave is a wave-uniform run-time value (it only selects data).
 
 struct Lane {
@@ -347,7 +349,7 @@ __device__ __forceinline__ Lane lane_ctx(const ScanArgs& a) {
 
 template <int MODE, int DIR>
 struct Dir {
-  static constexpr bool kRev = MODE != kModeVim && DIR == 1;  // storage order reversed
+  static constexpr bool kRev = (MODE == kModeFirstPair || MODE == kModeSecondPair) && DIR == 1;  // storage reversed
   static constexpr int kPosSgn = DIR == 0 ? 1 : -1;
   static constexpr int kSidxSgn = kRev ? -kPosSgn : kPosSgn;
   // global position of step i
@@ -832,7 +834,7 @@ __device__ __forceinline__ void epi_batch(const ScanArgs& a, const float* ybuf, 
 #pragma unroll
       for (int j = 0; j < kWin; ++j) v[j] = 0.5f * v[j] * silu_f(zz[j]);  // (y_f + y_b) / 2 * silu(z)
       store8(ob + gi, v);
-    } else if (MODE == kModeFirstPair) {
+    } else if (MODE == kModeFirstPair || MODE == kModeVimSum) {
       store8(a.wsy + gi, v);
     } else {
       float w[kWin];
@@ -907,7 +909,7 @@ __device__ __forceinline__ void pair_epilogue(const ScanArgs& a, const Lane& l, 
       const float v = row_val(ybuf, ybs, c, q);
       if (MODE == kModeVim) {
         st_act(ob, gi, 0.5f * v * silu_f(ld_act(zb, gi)));
-      } else if (MODE == kModeFirstPair) {
+      } else if (MODE == kModeFirstPair || MODE == kModeVimSum) {
         a.wsy[gi] = v;
       } else {
         float w = v + a.wsy[gi];
@@ -1102,6 +1104,373 @@ vmscan_status vim_args(ScanArgs& a, const void* u, const void* delta_raw, const 
   return VMSCAN_OK;
 }
 
+// ---------------------------------------------------------------------------------------------
+// Backward pass of the bidirectional scan (gradients of vmscan_fwd_bidir_v2).
+//
+// Per direction, with g_t = dL/ds_t = dout_t silu(z_t) / 2 (the same for both directions) and
+// a_t = exp(Δ_t A), the adjoint λ_t = dL/dh_t runs against the scan order:
+//   λ_t = g_t C_t + a_{t+1} λ_{t+1},   λ after the last step = 0
+// and gives dC_t = g_t h_t, dB_t = λ_t Δ_t u_t, du_t = g_t D + Δ_t Σ λ_t B_t,
+// dΔ_t = Σ λ_t (A a_t h_{t-1} + B_t u_t), dΔ_raw_t = dΔ_t sigmoid(Δ_raw_t + bias),
+// dA = Σ λ_t Δ_t a_t h_{t-1} (dA_log = dA A), dD = Σ g_t u_t, dbias = Σ dΔ_raw_t.
+//
+// Stages (one stream): the B/C copy and chunk carries of the forward; the forward scan with the
+// un-gated sum y_f + y_b saved (kModeVimSum); gate_bwd_kernel (g and dz); bwd_scan_kernel, whose
+// four waves per workgroup (direction x state half, lane = channel) each run their direction
+// over the whole sequence twice: forward, storing the state at every 8-step window, then window
+// by window backwards, recomputing the window's states from its checkpoint and walking the
+// adjoint; and three small kernels that sum the partial results (state halves, directions when
+// the branches share inputs, channel groups, batch) and round.  In base-2 units (Δ2 = Δ log2 e,
+// B' = B ln 2 from the B/C copy): Σ λ B = log2e Σ λ B', du = Δ2 Σ λ B', dB = ln2 λ Δ2 u and
+// dA = ln2 Σ λ Δ2 a h_{t-1}; the ln 2 factors are applied when the partial sums are reduced.
+
+constexpr int kRedCols = 32;              // per lane and reduction round: 2 steps x (8 dB + 8 dC)
+constexpr int kRedStride = kRedCols + 4;  // floats per LDS row (16-byte aligned rows)
+constexpr int kParStride = 16;            // per (batch, direction, half, channel): dA[8], dD, dbias
+
+struct BwdArgs {
+  ScanArgs s;       // forward arguments: B/C copy (bct), per-direction u, Δ_raw, A_log, D, bias
+  const float* g;   // [batch][dim][L]: dout silu(z) / 2
+  float* ck;        // [batch][dir][half][nwin][dim][8]: state entering each window
+  float* gu;        // [dir][half][batch][dim][L]: the half's share of du
+  float* gx;        // [dir][half][batch][dim][L]: the half's share of dΔ_raw
+  float* dbc;       // [dir][group][batch][2][16][L]: sums over the group's channels of λ Δ2 u (dB / ln2), g h (dC)
+  float* dpar;      // [batch][dir][half][dim][kParStride]
+  int nwin;
+};
+
+// g = dout silu(z) / 2 (float32) and dz = dout (y_f + y_b) / 2 silu'(z), silu'(z) = σ (1 + z (1 - σ)).
+template <typename T>
+__global__ __launch_bounds__(256) void gate_bwd_kernel(const T* __restrict__ dout, const T* __restrict__ z,
+                                                       const float* __restrict__ ysum, float* __restrict__ g,
+                                                       T* __restrict__ dz, int64_t n) {
+  const int64_t i0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  for (int64_t i = i0; i < i0 + 4 && i < n; ++i) {
+    const float zz = ld_act(z, i), go = ld_act(dout, i);
+    const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-zz * kLog2e));
+    g[i] = 0.5f * go * zz * sg;
+    st_act(dz, i, 0.5f * go * ysum[i] * sg * (1.0f + zz * (1.0f - sg)));
+  }
+}
+
+// Column sums over the wave's 64 lanes of the 32 values each lane stored in its LDS row: lane c
+// (c < 32) returns the sum of column c; lanes 32-63 return the same sums.
+__device__ __forceinline__ float wave_column_sum(const float* rows, int lane) {
+  const int c = lane & 31, r0 = (lane >> 5) * 32;
+  float acc = 0.0f;
+#pragma unroll 8
+  for (int r = 0; r < 32; ++r) acc += rows[(r0 + r) * kRedStride + c];
+  return acc + __shfl_xor(acc, 32);
+}
+
+template <typename T, int DIR>
+__device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float* rows) {
+  const ScanArgs& a = ba.s;
+  using Dr = Dir<kModeVim, DIR>;
+  const DirArgs& da = DIR == 0 ? a.d0 : a.d1;
+  const int L = static_cast<int>(a.L);
+  const T* ub = static_cast<const T*>(da.u) + static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(l.dd) * a.L;
+  const T* xb = static_cast<const T*>(da.draw) + static_cast<int64_t>(l.b) * da.draw_bs + static_cast<int64_t>(l.dd) * a.L;
+  const float* gb = ba.g + static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(l.dd) * a.L;
+  float A[kH];
+  load_a2(da, l, A);
+  const float bias2 = da.bias[l.dd] * kLog2e;
+  const float Dh = l.half == 0 ? da.Dp[l.dd] : 0.0f;
+  const scalar_fp bct = bc_row<DIR>(a, l);
+  const float vmask = l.valid ? 1.0f : 0.0f;  // lanes past the last channel add nothing to dB/dC
+  float* ckw = ba.ck + ((static_cast<int64_t>(l.b) * 2 + DIR) * 2 + l.half) * ba.nwin * a.dim * kH;
+  auto ck_at = [&](int w) { return ckw + (static_cast<int64_t>(w) * a.dim + l.dd) * kH; };
+
+  // Forward over the sequence: the state entering each window.
+  float h[kH];
+#pragma unroll
+  for (int n = 0; n < kH; ++n) h[n] = 0.0f;
+  for (int w = 0; w < ba.nwin; ++w) {
+    if (l.valid) {
+      float* c = ck_at(w);
+#pragma unroll
+      for (int n = 0; n < kH; ++n) c[n] = h[n];
+    }
+    const int i_end = (w + 1) * kWin < L ? (w + 1) * kWin : L;
+    for (int i = w * kWin; i < i_end; ++i) {
+      const int64_t p = Dr::pos(l, i);
+      const float d2 = delta2(ld_act(xb, p), bias2);
+      const float du2 = d2 * ld_act(ub, p);
+      const scalar_fp bc = bct + p * kBC;
+#pragma unroll
+      for (int n = 0; n < kH; ++n) h[n] = __builtin_fmaf(du2, bc[n], __builtin_amdgcn_exp2f(d2 * A[n]) * h[n]);
+    }
+  }
+
+  // Backward, window by window.
+  const int64_t plane = static_cast<int64_t>(a.batch) * a.dim * a.L;
+  const int64_t row = static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(l.dd) * a.L;
+  float* guw = ba.gu + (DIR * 2 + l.half) * plane + row;
+  float* gxw = ba.gx + (DIR * 2 + l.half) * plane + row;
+  const int group = l.d / kW;
+  float* dbcw = ba.dbc + ((static_cast<int64_t>(DIR) * a.ngroups + group) * a.batch + l.b) * 2 * kN * a.L;
+  float lam[kH], anext[kH], dA[kH];
+#pragma unroll
+  for (int n = 0; n < kH; ++n) {
+    lam[n] = 0.0f;
+    anext[n] = 0.0f;
+    dA[n] = 0.0f;
+  }
+  float dD = 0.0f, dbias = 0.0f;
+  float* myrow = rows + l.lane * kRedStride;
+  for (int w = ba.nwin - 1; w >= 0; --w) {
+    const int i0 = w * kWin;
+    const int ns = L - i0 < kWin ? L - i0 : kWin;
+    float hs[kH], hh[kWin][kH], d2[kWin], du2[kWin], uu[kWin], gg[kWin], sg[kWin];
+    const float* c = ck_at(w);
+#pragma unroll
+    for (int n = 0; n < kH; ++n) hs[n] = c[n];
+#pragma unroll
+    for (int j = 0; j < kWin; ++j) {
+      if (j < ns) {
+        const int64_t p = Dr::pos(l, i0 + j);
+        const float t = __builtin_fmaf(ld_act(xb, p), kLog2e, bias2);
+        d2[j] = softplus2(t);
+        uu[j] = ld_act(ub, p);
+        du2[j] = d2[j] * uu[j];
+        gg[j] = gb[p];
+        sg[j] = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-t));  // sigmoid(Δ_raw + bias)
+        const scalar_fp bc = bct + p * kBC;
+#pragma unroll
+        for (int n = 0; n < kH; ++n) {
+          const float hp = j == 0 ? hs[n] : hh[j - 1][n];
+          hh[j][n] = __builtin_fmaf(du2[j], bc[n], __builtin_amdgcn_exp2f(d2[j] * A[n]) * hp);
+        }
+      }
+    }
+    // Reduction rounds of two steps each, from the last step of the window down (fully unrolled so
+    // that the window arrays are indexed by constants and stay in registers).
+#pragma unroll
+    for (int r = kWin / 2 - 1; r >= 0; --r) {
+      if (2 * r >= ns) continue;
+#pragma unroll
+      for (int jj = 1; jj >= 0; --jj) {
+        const int j = 2 * r + jj;
+        float vb[kH], vc[kH];
+        if (j < ns) {
+          const int64_t p = Dr::pos(l, i0 + j);
+          const scalar_fp bc = bct + p * kBC;
+          float P = 0.0f, Q = 0.0f;
+#pragma unroll
+          for (int n = 0; n < kH; ++n) {
+            const float an = __builtin_amdgcn_exp2f(d2[j] * A[n]);
+            lam[n] = __builtin_fmaf(gg[j], bc[kH + n], anext[n] * lam[n]);
+            const float hp = j == 0 ? hs[n] : hh[j - 1][n];
+            const float wv = lam[n] * an * hp;
+            Q = __builtin_fmaf(A[n], wv, Q);
+            dA[n] = __builtin_fmaf(d2[j], wv, dA[n]);
+            P = __builtin_fmaf(lam[n], bc[n], P);
+            vb[n] = vmask * lam[n] * du2[j];
+            vc[n] = vmask * gg[j] * hh[j][n];
+            anext[n] = an;
+          }
+          const float dd = __builtin_fmaf(uu[j] * kLog2e, P, Q);
+          if (l.valid) {
+            guw[p] = __builtin_fmaf(d2[j], P, Dh * gg[j]);
+            gxw[p] = sg[j] * dd;
+          }
+          dbias = __builtin_fmaf(sg[j], dd, dbias);
+          dD = __builtin_fmaf(gg[j], uu[j], dD);
+        } else {
+#pragma unroll
+          for (int n = 0; n < kH; ++n) vb[n] = vc[n] = 0.0f;
+        }
+        float4* dst = reinterpret_cast<float4*>(myrow + jj * 2 * kH);
+        dst[0] = make_float4(vb[0], vb[1], vb[2], vb[3]);
+        dst[1] = make_float4(vb[4], vb[5], vb[6], vb[7]);
+        dst[2] = make_float4(vc[0], vc[1], vc[2], vc[3]);
+        dst[3] = make_float4(vc[4], vc[5], vc[6], vc[7]);
+      }
+      // A wave's LDS accesses execute in order, so every lane's row is written before it is read
+      // and read before the next round overwrites it; the compiler barriers keep that order.
+      asm volatile("" ::: "memory");
+      const float sum = wave_column_sum(rows, l.lane);
+      asm volatile("" ::: "memory");
+      if (l.lane < kRedCols) {
+        const int jj = l.lane >> 4, ty = (l.lane >> 3) & 1, k = l.lane & 7;
+        const int j = 2 * r + jj;
+        if (j < ns) dbcw[(static_cast<int64_t>(ty) * kN + kH * l.half + k) * a.L + Dr::pos(l, i0 + j)] = sum;
+      }
+    }
+  }
+  if (l.valid) {
+    float* pp = ba.dpar + (((static_cast<int64_t>(l.b) * 2 + DIR) * 2 + l.half) * a.dim + l.d) * kParStride;
+#pragma unroll
+    for (int n = 0; n < kH; ++n) pp[n] = dA[n];
+    pp[kH] = l.half == 0 ? dD : 0.0f;
+    pp[kH + 1] = dbias;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdArgs ba) {
+  __shared__ __attribute__((aligned(16))) float rows[4][kW * kRedStride];
+  const Lane l = lane_ctx(ba.s);
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  if ((w & 1) == 0) bwd_dir<T, 0>(ba, l, rows[w]);
+  else bwd_dir<T, 1>(ba, l, rows[w]);
+}
+
+// du, dΔ_raw (and the backward branch's, or their sums when the branches share inputs):
+// elementwise over [batch][dim][L], rounded once to the activation dtype.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_combine_kernel(const float* __restrict__ gu, const float* __restrict__ gx,
+                                                          T* du, T* dx, T* du_b, T* dx_b, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n) return;
+  const float uf = gu[i] + gu[n + i], ubk = gu[2 * n + i] + gu[3 * n + i];
+  const float xf = gx[i] + gx[n + i], xbk = gx[2 * n + i] + gx[3 * n + i];
+  if (du_b) {
+    st_act(du, i, uf);
+    st_act(du_b, i, ubk);
+  } else {
+    st_act(du, i, uf + ubk);
+  }
+  if (dx_b) {
+    st_act(dx, i, xf);
+    st_act(dx_b, i, xbk);
+  } else {
+    st_act(dx, i, xf + xbk);
+  }
+}
+
+// dB, dC, dB_b, dC_b: the channel-group partial sums added up (dB scaled by ln 2), rounded once.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_bc_kernel(const float* __restrict__ dbc, T* dB, T* dC, T* dB_b, T* dC_b,
+                                                     int batch, int ngroups, int64_t L) {
+  const int64_t per = static_cast<int64_t>(batch) * 2 * kN * L;  // one (dir, group) block
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= 2 * per) return;
+  const int dir = static_cast<int>(i / per);
+  const int64_t r = i - dir * per;                    // (b, type, n, pos)
+  float s = 0.0f;
+  for (int gi = 0; gi < ngroups; ++gi) s += dbc[(static_cast<int64_t>(dir) * ngroups + gi) * per + r];
+  const int64_t bb = r / (2 * kN * L);
+  const int64_t rest = r - bb * 2 * kN * L;
+  const int ty = static_cast<int>(rest / (kN * L));
+  const int64_t o = bb * kN * L + (rest - ty * kN * L);  // (b, n, pos) in [batch][16][L]
+  T* dst = ty == 0 ? (dir == 0 ? dB : dB_b) : (dir == 0 ? dC : dC_b);
+  st_act(dst, o, ty == 0 ? s * kLn2 : s);
+}
+
+// dA_log, dD, dbias per direction: sums over batch (and state halves / directions as needed).
+__global__ __launch_bounds__(256) void bwd_param_kernel(const float* __restrict__ dpar, const float* A_log,
+                                                        const float* A_b_log, float* dA_log, float* dA_b_log,
+                                                        float* dD, float* dD_b, float* dbias, float* dbias_b,
+                                                        int batch, int dim) {
+  const int i = blockIdx.x * 256 + threadIdx.x;  // (dir, d, n)
+  if (i >= 2 * dim * kN) return;
+  const int dir = i / (dim * kN), d = (i / kN) % dim, n = i % kN;
+  const int half = n / kH;
+  auto at = [&](int b, int dr, int hf, int k) {
+    return dpar[(((static_cast<int64_t>(b) * 2 + dr) * 2 + hf) * dim + d) * kParStride + k];
+  };
+  float sa = 0.0f;
+  for (int b = 0; b < batch; ++b) sa += at(b, dir, half, n % kH);
+  const float* al = dir == 0 ? A_log : A_b_log;
+  const float An = -__expf(al[static_cast<int64_t>(d) * kN + n]);
+  (dir == 0 ? dA_log : dA_b_log)[static_cast<int64_t>(d) * kN + n] = sa * kLn2 * An;
+  if (n == 0) {
+    float sd = 0.0f, sb = 0.0f;
+    for (int b = 0; b < batch; ++b) {
+      sd += at(b, dir, 0, kH);
+      sb += at(b, dir, 0, kH + 1) + at(b, dir, 1, kH + 1);
+    }
+    (dir == 0 ? dD : dD_b)[d] = sd;
+    if (dir == 0 || dbias_b) {
+      (dir == 0 ? dbias : dbias_b)[d] = sb;
+    }
+  }
+}
+
+// Shared-input dbias: the backward branch's sum is added to the forward one (run after
+// bwd_param_kernel, which wrote the forward sum).
+__global__ __launch_bounds__(256) void bwd_bias_shared_kernel(const float* __restrict__ dpar, float* dbias, int batch,
+                                                              int dim) {
+  const int d = blockIdx.x * 256 + threadIdx.x;
+  if (d >= dim) return;
+  float sb = 0.0f;
+  for (int b = 0; b < batch; ++b)
+    for (int hf = 0; hf < 2; ++hf) sb += dpar[(((static_cast<int64_t>(b) * 2 + 1) * 2 + hf) * dim + d) * kParStride + kH + 1];
+  dbias[d] += sb;
+}
+
+struct BwdLayout {
+  size_t bct, agg, ysum, g, ck, gu, gx, dbc, dpar, total;
+};
+
+BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t L, int64_t Kf) {
+  BwdLayout w{};
+  const size_t plane = round256(static_cast<size_t>(batch) * dim * L * sizeof(float));
+  const int64_t nwin = ceil_div(L, kWin);
+  w.bct = 0;
+  w.agg = w.bct + bct_bytes(batch, L);
+  w.ysum = w.agg + agg_bytes(batch, dim, L, Kf);
+  w.g = w.ysum + plane;
+  w.ck = w.g + plane;
+  w.gu = w.ck + round256(static_cast<size_t>(batch) * 2 * 2 * nwin * dim * kH * sizeof(float));
+  w.gx = w.gu + 4 * plane;
+  w.dbc = w.gx + 4 * plane;
+  w.dpar = w.dbc + round256(static_cast<size_t>(2) * groups(dim) * batch * 2 * kN * L * sizeof(float));
+  w.total = w.dpar + round256(static_cast<size_t>(batch) * 2 * 2 * dim * kParStride * sizeof(float));
+  return w;
+}
+
+
+template <typename T>
+vmscan_status run_bwd(const ScanArgs& fwd, const BwdLayout& lay, unsigned char* wsp, const void* dout, const void* z,
+                      void* du, void* dx, float* dbias, void* du_b, void* dx_b, float* dbias_b, void* dz,
+                      const float* A_log, const float* A_b_log, float* dA_log, float* dA_b_log, void* dB, void* dC,
+                      void* dB_b, void* dC_b, float* dD, float* dD_b, hipStream_t stream) {
+  const int64_t n = static_cast<int64_t>(fwd.batch) * fwd.dim * fwd.L;
+  const int64_t nbc = static_cast<int64_t>(2) * fwd.batch * 2 * kN * fwd.L;
+  if (ceil_div(n, 256) >= (int64_t{1} << 31) || ceil_div(nbc, 256) >= (int64_t{1} << 31)) return VMSCAN_ERR_SHAPE;
+  float* ysum = reinterpret_cast<float*>(wsp + lay.ysum);
+  float* g = reinterpret_cast<float*>(wsp + lay.g);
+  // forward with the un-gated sum y_f + y_b
+  ScanArgs a = fwd;
+  a.wsy = ysum;
+  vmscan_status st = run_pair<T, kModeVimSum>(a, stream, kStageAll);
+  if (st != VMSCAN_OK) return st;
+  hipLaunchKernelGGL(gate_bwd_kernel<T>, dim3(static_cast<unsigned>(ceil_div(n, 1024))), dim3(256), 0, stream,
+                     static_cast<const T*>(dout), static_cast<const T*>(z), ysum, g, static_cast<T*>(dz), n);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return launch_failed(e);
+  BwdArgs ba{};
+  ba.s = fwd;
+  ba.s.K = static_cast<int>(fwd.L);  // one chunk: each wave walks the whole sequence
+  ba.s.nch = 1;
+  ba.g = g;
+  ba.ck = reinterpret_cast<float*>(wsp + lay.ck);
+  ba.gu = reinterpret_cast<float*>(wsp + lay.gu);
+  ba.gx = reinterpret_cast<float*>(wsp + lay.gx);
+  ba.dbc = reinterpret_cast<float*>(wsp + lay.dbc);
+  ba.dpar = reinterpret_cast<float*>(wsp + lay.dpar);
+  ba.nwin = static_cast<int>(ceil_div(fwd.L, kWin));
+  hipLaunchKernelGGL(bwd_scan_kernel<T>, dim3(static_cast<unsigned>(static_cast<int64_t>(fwd.batch) * fwd.ngroups)),
+                     dim3(kThreads), 0, stream, ba);
+  e = hipGetLastError();
+  if (e != hipSuccess) return launch_failed(e);
+  hipLaunchKernelGGL(bwd_combine_kernel<T>, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, stream,
+                     ba.gu, ba.gx, static_cast<T*>(du), static_cast<T*>(dx), static_cast<T*>(du_b),
+                     static_cast<T*>(dx_b), n);
+  hipLaunchKernelGGL(bwd_bc_kernel<T>, dim3(static_cast<unsigned>(ceil_div(nbc, 256))), dim3(256), 0, stream, ba.dbc,
+                     static_cast<T*>(dB), static_cast<T*>(dC), static_cast<T*>(dB_b), static_cast<T*>(dC_b), fwd.batch,
+                     fwd.ngroups, fwd.L);
+  hipLaunchKernelGGL(bwd_param_kernel, dim3(static_cast<unsigned>(ceil_div(2 * fwd.dim * kN, 256))), dim3(256), 0,
+                     stream, ba.dpar, A_log, A_b_log, dA_log, dA_b_log, dD, dD_b, dbias, dbias_b, fwd.batch, fwd.dim);
+  if (!dbias_b)
+    hipLaunchKernelGGL(bwd_bias_shared_kernel, dim3(static_cast<unsigned>(ceil_div(fwd.dim, 256))), dim3(256), 0,
+                       stream, ba.dpar, dbias, fwd.batch, fwd.dim);
+  e = hipGetLastError();
+  return e == hipSuccess ? VMSCAN_OK : launch_failed(e);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------------------------
@@ -1151,6 +1520,49 @@ vmscan_status vmscan_fwd_bidir_ex(const void* u, const void* delta_raw, const vo
                                   int64_t chunk_len, hipStream_t stream) {
   return vmscan_fwd_bidir_stage(u, delta_raw, z, A_log, A_b_log, B, C, B_b, C_b, D, D_b, delta_bias, out, batch, dim,
                                 seqlen, d_state, dtype, workspace, workspace_bytes, chunk_len, 3, stream);
+}
+
+size_t vmscan_bwd_bidir_v2_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen, int d_state,
+                                           vmscan_dtype dtype) {
+  if (!shape_ok(batch, dim, seqlen) || d_state != kN || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16)) return 0;
+  return bwd_layout(batch, dim, seqlen, plan_chunk(batch * groups(dim), seqlen, 0)).total;
+}
+
+vmscan_status vmscan_bwd_bidir_v2(const void* u, const void* delta_raw, const float* delta_bias, const void* u_b,
+                                  const void* delta_raw_b, const float* delta_bias_b, const void* z,
+                                  const float* A_log, const float* A_b_log, const void* B, const void* C,
+                                  const void* B_b, const void* C_b, const float* D, const float* D_b,
+                                  const void* dout, void* du, void* ddelta_raw, float* ddelta_bias, void* du_b,
+                                  void* ddelta_raw_b, float* ddelta_bias_b, void* dz, float* dA_log, float* dA_b_log,
+                                  void* dB, void* dC, void* dB_b, void* dC_b, float* dD, float* dD_b, int64_t batch,
+                                  int64_t dim, int64_t seqlen, int d_state, vmscan_dtype dtype, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  const void* need[] = {dout, du, ddelta_raw, ddelta_bias, dz, dA_log, dA_b_log, dB, dC, dB_b, dC_b, dD, dD_b};
+  for (const void* p : need)
+    if (!p) return VMSCAN_ERR_NULL;
+  if (!shape_ok(batch, dim, seqlen)) return VMSCAN_ERR_SHAPE;
+  if (d_state != kN || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16)) return VMSCAN_ERR_UNSUPPORTED;
+  const void* opt[] = {du_b, ddelta_raw_b, ddelta_bias_b};
+  for (const void* p : need)
+    if (!aligned16(p)) return VMSCAN_ERR_ALIGN;
+  for (const void* p : opt)
+    if (p && !aligned16(p)) return VMSCAN_ERR_ALIGN;
+  const int64_t Kf = plan_chunk(batch * groups(dim), seqlen, 0);
+  const BwdLayout lay = bwd_layout(batch, dim, seqlen, Kf);
+  ScanArgs a{};
+  // The forward arguments; its output pointer is unused in the sum-saving mode.
+  vmscan_status st = vim_args(a, u, delta_raw, delta_bias, u_b, delta_raw_b, delta_bias_b, z, A_log, A_b_log, B, C,
+                              B_b, C_b, D, D_b, workspace, batch, dim, seqlen, d_state, dtype, workspace,
+                              workspace_bytes, 0);
+  if (st != VMSCAN_OK) return st;
+  st = check_workspace(workspace, workspace_bytes, lay.total);
+  if (st != VMSCAN_OK) return st;
+  unsigned char* wsp = static_cast<unsigned char*>(workspace);
+  return dtype == VMSCAN_F32
+             ? run_bwd<float>(a, lay, wsp, dout, z, du, ddelta_raw, ddelta_bias, du_b, ddelta_raw_b, ddelta_bias_b, dz,
+                              A_log, A_b_log, dA_log, dA_b_log, dB, dC, dB_b, dC_b, dD, dD_b, stream)
+             : run_bwd<uint16_t>(a, lay, wsp, dout, z, du, ddelta_raw, ddelta_bias, du_b, ddelta_raw_b, ddelta_bias_b,
+                                 dz, A_log, A_b_log, dA_log, dA_b_log, dB, dC, dB_b, dC_b, dD, dD_b, stream);
 }
 
 vmscan_status vmscan_fwd_bidir_v2_stage(const void* u, const void* delta_raw, const float* delta_bias, const void* u_b,

@@ -1,0 +1,115 @@
+"""HIP backward pass (vmscan_bwd_bidir_v2) vs the fp64 oracle's gradients, tensor by tensor.
+
+Same error metric and tolerances as the forward parity tests: max_i |y_i - r_i| / max(|r_i|,
+rms(r)) <= 1e-5 for float32 activations and 2e-2 for bfloat16 activations (float32 state and
+accumulation, one rounding of each gradient)."""
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from gpu_common import TOL, pdev, tdev
+
+pytestmark = pytest.mark.gpu
+
+GRADS = ("du", "ddelta_raw", "ddelta_bias", "du_b", "ddelta_raw_b", "ddelta_bias_b", "dz", "dA_log", "dA_b_log", "dB",
+         "dC", "dB_b", "dC_b", "dD", "dD_b")
+PER_BATCH = ("du", "ddelta_raw", "du_b", "ddelta_raw_b", "dz", "dB", "dC", "dB_b", "dC_b")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import selective_state_space_41_amd  # noqa: F401
+
+
+def _report(name, err, tol):
+    print(f"[parity] {name}: err {err:.3e} (tol {tol:.0e})", flush=True)
+    assert err <= tol, f"{name}: err {err:.3e} > {tol:.0e}"
+
+
+def _dout(p, seed):
+    rng = np.random.default_rng(seed)
+    d = rng.standard_normal(p["u"].shape).astype(np.float32)
+    return synth.round_bf16(d) if p["dtype"] == "bf16" else d
+
+
+def run_bwd(p, dout, shared=False):
+    import torch
+    import selective_state_space_41_amd as V
+    dt = p["dtype"]
+    act = {k: tdev(p[k], dt) for k in ("u", "delta_raw", "u_b", "delta_raw_b", "z", "B", "C", "B_b", "C_b")}
+    par = {k: pdev(p[k]) for k in ("A_log", "A_b_log", "D", "D_b", "delta_bias", "delta_bias_b")}
+    if shared:
+        act["u_b"], act["delta_raw_b"], par["delta_bias_b"] = act["u"], act["delta_raw"], par["delta_bias"]
+    g = V.vmscan_bwd_bidir_v2(act["u"], act["delta_raw"], par["delta_bias"], act["u_b"], act["delta_raw_b"],
+                              par["delta_bias_b"], act["z"], par["A_log"], par["A_b_log"], act["B"], act["C"],
+                              act["B_b"], act["C_b"], par["D"], par["D_b"], tdev(dout, dt), shared=shared)
+    torch.cuda.synchronize()
+    return {k: (None if v is None else v.float().cpu().numpy()) for k, v in g.items()}
+
+
+def oracle_bwd(p, dout, batches=None, shared=False):
+    sel = (lambda a: a) if batches is None else (lambda a: a[batches])
+    q = dict(p)
+    if shared:
+        q["u_b"], q["delta_raw_b"], q["delta_bias_b"] = p["u"], p["delta_raw"], p["delta_bias"]
+    return O.vim_bidir_v2_bwd(sel(q["u"]), sel(q["delta_raw"]), q["delta_bias"], sel(q["u_b"]), sel(q["delta_raw_b"]),
+                              q["delta_bias_b"], sel(q["z"]), q["A_log"], q["A_b_log"], sel(q["B"]), sel(q["C"]),
+                              sel(q["B_b"]), sel(q["C_b"]), q["D"], q["D_b"], sel(dout))
+
+
+BWD_SHAPES = [(1, 16, 1), (2, 17, 9), (1, 40, 33), (2, 24, 197), (1, 16, 100), (3, 70, 64)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", BWD_SHAPES, ids=[f"b{b}d{d}l{l}" for b, d, l in BWD_SHAPES])
+def test_bwd_small(shape, dtype):
+    nb, nd, L = shape
+    p = synth.make_vim_v2_inputs(0, layer=600 + L, batch=nb, dim=nd, seqlen=L, dtype=dtype)
+    dout = _dout(p, L)
+    got, ref = run_bwd(p, dout), oracle_bwd(p, dout)
+    for k in GRADS:
+        _report(f"bwd {shape} {dtype} {k}", O.rel_err(got[k], ref[k]), TOL[dtype])
+
+
+def test_bwd_shared_inputs():
+    """NULL backward-branch gradient pointers: the two branches' du, dΔ_raw, dbias are summed."""
+    p = synth.make_vim_v2_inputs(0, layer=7, batch=2, dim=48, seqlen=77, dtype="f32")
+    dout = _dout(p, 1)
+    got, ref = run_bwd(p, dout, shared=True), oracle_bwd(p, dout, shared=True)
+    assert got["du_b"] is None and got["ddelta_raw_b"] is None and got["ddelta_bias_b"] is None
+    for k, rk in (("du", ("du", "du_b")), ("ddelta_raw", ("ddelta_raw", "ddelta_raw_b")),
+                  ("ddelta_bias", ("ddelta_bias", "ddelta_bias_b"))):
+        _report(f"bwd shared {k}", O.rel_err(got[k], ref[rk[0]] + ref[rk[1]]), 1e-5)
+    for k in ("dz", "dA_log", "dA_b_log", "dB", "dC", "dB_b", "dC_b", "dD", "dD_b"):
+        _report(f"bwd shared {k}", O.rel_err(got[k], ref[k]), 1e-5)
+
+
+def test_bwd_deterministic():
+    p = synth.make_vim_v2_inputs(0, layer=8, batch=3, dim=64, seqlen=197, dtype="bf16")
+    dout = _dout(p, 2)
+    a, b = run_bwd(p, dout), run_bwd(p, dout)
+    for k in GRADS:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_bwd_config1_full():
+    """The Vim-Ti workload (B128 D384 L197 bf16): per-batch gradients on sampled batches, the
+    batch-summed parameter gradients against the oracle over all batches (in slices)."""
+    p = synth.make_vim_v2_inputs(1)
+    dout = _dout(p, 3)
+    got = run_bwd(p, dout)
+    bsel = np.array([0, 77, 127])
+    ref = oracle_bwd(p, dout, batches=bsel)
+    for k in PER_BATCH:
+        _report(f"bwd config 1 {k} (batches 0,77,127)", O.rel_err(got[k][bsel], ref[k]), 2e-2)
+    sums = {k: 0.0 for k in ("ddelta_bias", "ddelta_bias_b", "dA_log", "dA_b_log", "dD", "dD_b")}
+    for b0 in range(0, 128, 16):
+        r = oracle_bwd(p, dout, batches=np.arange(b0, b0 + 16))
+        for k in sums:
+            sums[k] = sums[k] + r[k]
+    for k, v in sums.items():
+        _report(f"bwd config 1 {k} (all batches)", O.rel_err(got[k], v), 2e-2)
