@@ -1,13 +1,14 @@
 """Benchmark of the fused bidirectional selective scan (and SS2D cross-scan) on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N | --all] [--no-cpu] [--v2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N | --all] [--no-cpu] [--v2] [--bwd]
 
 A step is one call of the hot path over one batch of seeded synthetic input already resident in
 HBM.  The default workload is the Vim-Ti layer scan (batch 128, d_inner 384, L 197, d_state 16,
 bf16 activations, fp32 state), the configuration the metric is quoted on.  R input/output sets
 are rotated so that at least 1 GiB is touched between reuses and the 256 MB Infinity Cache cannot
 serve the inputs.  Rank 0 prints one JSON line per workload.  ``--v2`` runs the Vim workloads
-through the entry point whose backward branch has its own u_b, Δ_raw_b and bias_b.
+through the entry point whose backward branch has its own u_b, Δ_raw_b and bias_b; ``--bwd``
+times the backward pass (all gradients) of the Vim workloads instead of the forward.
 """
 import argparse
 import hashlib
@@ -29,6 +30,11 @@ HBM_PEAK_GBS = 8000.0
 # the peak is 256 * 2.4e9 * 16 = 9.83e12 updates/s.
 CUS, CLOCK_HZ = 256, 2.4e9
 ALU_PEAK_UPD_S = CUS * CLOCK_HZ / (4.0 / 128 + 1.0 / 32)
+# Backward: per state update the forward state must be rebuilt (one exp2 and three VALU ops: Δ·A',
+# h·a, h + Δu·B) and the adjoint walked (nine VALU ops with the decay reused: g·C, λ, a·h_{t-1},
+# λ·(a h_{t-1}), the dΔ and dA accumulations, Σ λ B, and the dB and dC terms), so at least
+# 12/128 + 1/32 = 1/8 CU-clock per update: 4.92e12 updates/s.
+ALU_PEAK_BWD_UPD_S = CUS * CLOCK_HZ / (12.0 / 128 + 1.0 / 32)
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SRC = os.path.join(ROOT, "selective_state_space_41_amd", "csrc", "vmscan.hip")
 
@@ -350,6 +356,63 @@ def bench_config(cfg_id, steps, warmup, with_cpu, torch, V, v2=False):
     return rec
 
 
+def bench_bwd(cfg_id, steps, warmup, torch, V, v2=False):
+    """Backward pass (vmscan_bwd_bidir_v2, every gradient) of a Vim workload; with shared inputs
+    (the forward of vmscan_fwd_bidir) unless ``v2``.  The timed region is the whole call."""
+    import numpy as np
+    import synth
+    cfg = synth.CONFIGS[cfg_id]
+    if cfg["kind"] != "vim":
+        return None
+    dev = torch.device("cuda", 0)
+    dt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
+    p = synth.make_vim_v2_inputs(cfg_id)
+    act = {k: torch.from_numpy(np.ascontiguousarray(p[k])).to(dev).to(dt) for k in VIM_ACT + V2_ACT}
+    par = {k: torch.from_numpy(np.ascontiguousarray(p[k])).to(dev) for k in VIM_PAR + V2_PAR}
+    if not v2:
+        act["u_b"], act["delta_raw_b"], par["delta_bias_b"] = act["u"], act["delta_raw"], par["delta_bias"]
+    g = torch.Generator(device=dev)
+    g.manual_seed(42_000 + cfg_id)
+    dout = torch.randn(act["u"].shape, generator=g, device=dev, dtype=torch.float32).to(dt)
+    nb, nd, L = act["u"].shape
+    wsb = V.lib.vmscan_bwd_bidir_v2_workspace_bytes(nb, nd, L, 16, 1 if cfg["dtype"] == "bf16" else 0)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+
+    def call():
+        return V.vmscan_bwd_bidir_v2(act["u"], act["delta_raw"], par["delta_bias"], act["u_b"], act["delta_raw_b"],
+                                     par["delta_bias_b"], act["z"], par["A_log"], par["A_b_log"], act["B"], act["C"],
+                                     act["B_b"], act["C_b"], par["D"], par["D_b"], dout, shared=not v2, workspace=ws)
+
+    outs = call()  # allocate the gradient tensors once; later calls write into fresh ones of the same size
+    for _ in range(warmup):
+        call()
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    upd = state_updates(cfg)
+    alu = upd / (ms * 1e-3)
+    toks = nb * nd * L
+    del outs
+    return {
+        "metric": "scan tokens·channels/s (bwd: all gradients of the bidirectional scan), 1 GPU",
+        "value": toks / (ms * 1e-3), "unit": "tokens·channels/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg["name"] + ("_sepbwd" if v2 else "") + "_backward", "batch": nb, "dim": nd,
+                   "seqlen": L, "d_state": 16, "io_dtype": cfg["dtype"], "branches": "separate" if v2 else "shared"},
+        "roofline": {"bound": "alu", "achieved": round(alu / 1e9, 1), "peak": round(ALU_PEAK_BWD_UPD_S / 1e9, 1),
+                     "unit": "Gupd/s", "frac": round(alu / ALU_PEAK_BWD_UPD_S, 4), "traffic": None,
+                     "kernel": "all kernels of vmscan_bwd_bidir_v2 (forward with saved sum, gate, adjoint scan, "
+                               "reductions)", "kernel_avg_us": round(ms * 1000, 2), "updates_per_launch": upd},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -359,6 +422,7 @@ def main():
     ap.add_argument("--all", action="store_true", help="one line per workload (configs 0-4)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--v2", action="store_true", help="Vim workloads with a separate backward branch (u_b, delta_raw_b, bias_b)")
+    ap.add_argument("--bwd", action="store_true", help="time the backward pass of the Vim workloads")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (counter calibration for FETCH_SIZE/WRITE_SIZE)")
     ap.add_argument("--summarize-kernels", nargs=3, metavar=("RESULT_DIR", "COMMAND", "OUT_TXT"),
@@ -404,7 +468,12 @@ def main():
     import selective_state_space_41_amd as V
     cfgs = [0, 1, 2, 3, 4] if args.all else [args.config]
     for c in cfgs:
-        rec = bench_config(c, args.steps, args.warmup, not args.no_cpu, torch, V, args.v2)
+        if args.bwd:
+            rec = bench_bwd(c, args.steps, args.warmup, torch, V, args.v2)
+            if rec is None:
+                continue
+        else:
+            rec = bench_config(c, args.steps, args.warmup, not args.no_cpu, torch, V, args.v2)
         print(json.dumps(rec), flush=True)
 
 

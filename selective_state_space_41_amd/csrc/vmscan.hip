@@ -143,6 +143,17 @@ __device__ __forceinline__ float softplus2(float t) {
   return t > 20.0f * kLog2e ? t : r;
 }
 
+// softplus2(t) and, from the same e = 2^t, sigmoid(x) = e / (1 + e) (the derivative of softplus).
+__device__ __forceinline__ float softplus2_sig(float t, float& sig) {
+  const float e = __builtin_amdgcn_exp2f(t);
+  const float s = 1.0f + e;
+  const float c = e - (s - 1.0f);
+  const float r = __builtin_fmaf(c, kLog2e, __builtin_amdgcn_logf(s));
+  const bool big = t > 20.0f * kLog2e;
+  sig = big ? 1.0f : e * __builtin_amdgcn_rcpf(s);
+  return big ? t : r;
+}
+
 // Base-2 softplus argument from the raw Δ input and the bias already multiplied by log2 e.
 __device__ __forceinline__ float delta2(float raw, float bias2) {
   return softplus2(__builtin_fmaf(raw, kLog2e, bias2));
@@ -1135,17 +1146,39 @@ struct BwdArgs {
   float* gu;        // [dir][half][batch][dim][L]: the half's share of du
   float* gx;        // [dir][half][batch][dim][L]: the half's share of dΔ_raw
   float* dbc;       // [dir][group][batch][2][16][L]: sums over the group's channels of λ Δ2 u (dB / ln2), g h (dC)
-  float* dpar;      // [batch][dir][half][dim][kParStride]
+  float* dpar;      // [dir][half][dim][kParStride][batch]
   int nwin;
 };
 
-// g = dout silu(z) / 2 (float32) and dz = dout (y_f + y_b) / 2 silu'(z), silu'(z) = σ (1 + z (1 - σ)).
+// g = dout silu(z) / 2 (float32) and dz = dout (y_f + y_b) / 2 silu'(z), silu'(z) = σ (1 + z (1 - σ)),
+// eight elements per thread (16-byte accesses; the flat arrays start 16-byte aligned).
 template <typename T>
 __global__ __launch_bounds__(256) void gate_bwd_kernel(const T* __restrict__ dout, const T* __restrict__ z,
                                                        const float* __restrict__ ysum, float* __restrict__ g,
                                                        T* __restrict__ dz, int64_t n) {
-  const int64_t i0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
-  for (int64_t i = i0; i < i0 + 4 && i < n; ++i) {
+  const int64_t i0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * kWin;
+  if (i0 >= n) return;
+  if (i0 + kWin <= n) {
+    Run8<T> dr, zr;
+    Run8<float> yr;
+    dr.load(dout + i0);
+    zr.load(z + i0);
+    yr.load(ysum + i0);
+    float go[kWin], zz[kWin], ys[kWin], gv[kWin], dv[kWin];
+    dr.template unpack<false>(go);
+    zr.template unpack<false>(zz);
+    yr.template unpack<false>(ys);
+#pragma unroll
+    for (int j = 0; j < kWin; ++j) {
+      const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-zz[j] * kLog2e));
+      gv[j] = 0.5f * go[j] * zz[j] * sg;
+      dv[j] = 0.5f * go[j] * ys[j] * sg * (1.0f + zz[j] * (1.0f - sg));
+    }
+    store8(g + i0, gv);
+    store8(dz + i0, dv);
+    return;
+  }
+  for (int64_t i = i0; i < n; ++i) {
     const float zz = ld_act(z, i), go = ld_act(dout, i);
     const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-zz * kLog2e));
     g[i] = 0.5f * go * zz * sg;
@@ -1157,16 +1190,36 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(const T* __restrict__ dou
 // (c < 32) returns the sum of column c; lanes 32-63 return the same sums.
 __device__ __forceinline__ float wave_column_sum(const float* rows, int lane) {
   const int c = lane & 31, r0 = (lane >> 5) * 32;
-  float acc = 0.0f;
-#pragma unroll 8
-  for (int r = 0; r < 32; ++r) acc += rows[(r0 + r) * kRedStride + c];
-  return acc + __shfl_xor(acc, 32);
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // four chains, so the adds overlap the LDS reads
+#pragma unroll
+  for (int r = 0; r < 32; ++r) acc[r & 3] += rows[(r0 + r) * kRedStride + c];
+  const float s = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  return s + __shfl_xor(s, 32);
 }
+
+// Raw inputs of one full 8-step window of the backward walk, loaded one window ahead: u and
+// Δ_raw (activation dtype), g (float32) and the checkpoint state entering the window.
+template <typename T, int DIR>
+struct RevWin {
+  using Dr = Dir<kModeVim, DIR>;
+  Run8<T> u, x;
+  Run8<float> g, ck;
+  __device__ __forceinline__ void load(const T* ub, const T* xb, const float* gb, const float* ckp, const Lane& l,
+                                       int i0) {
+    const int64_t p = Dr::pos(l, i0);
+    const int64_t lo = Dr::kPosSgn > 0 ? p : p - (kWin - 1);  // lowest position of the window
+    u.load(ub + lo);
+    x.load(xb + lo);
+    g.load(gb + lo);
+    ck.load(ckp);
+  }
+};
 
 template <typename T, int DIR>
 __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float* rows) {
   const ScanArgs& a = ba.s;
   using Dr = Dir<kModeVim, DIR>;
+  constexpr bool kRevOrder = Dr::kPosSgn < 0;  // window positions descend with the step
   const DirArgs& da = DIR == 0 ? a.d0 : a.d1;
   const int L = static_cast<int>(a.L);
   const T* ub = static_cast<const T*>(da.u) + static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(l.dd) * a.L;
@@ -1180,29 +1233,30 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
   const float vmask = l.valid ? 1.0f : 0.0f;  // lanes past the last channel add nothing to dB/dC
   float* ckw = ba.ck + ((static_cast<int64_t>(l.b) * 2 + DIR) * 2 + l.half) * ba.nwin * a.dim * kH;
   auto ck_at = [&](int w) { return ckw + (static_cast<int64_t>(w) * a.dim + l.dd) * kH; };
+  const int full_end = (L / kWin) * kWin;
 
-  // Forward over the sequence: the state entering each window.
-  float h[kH];
+  // Forward over the sequence, storing the state entering each window (the steps of the last,
+  // partial window are not needed: nothing follows them).
+  {
+    float h[kH], bcA[kBC], bcB[kBC];
 #pragma unroll
-  for (int n = 0; n < kH; ++n) h[n] = 0.0f;
-  for (int w = 0; w < ba.nwin; ++w) {
-    if (l.valid) {
-      float* c = ck_at(w);
-#pragma unroll
-      for (int n = 0; n < kH; ++n) c[n] = h[n];
+    for (int n = 0; n < kH; ++n) h[n] = 0.0f;
+    Window<T, kModeVim, DIR> win;
+    load_bc(bct + Dr::pos(l, 0) * kBC, bcA);
+    if (full_end > 0) win.load(a, l, da, 0);
+    for (int i0 = 0; i0 < full_end; i0 += kWin) {
+      if (l.valid) store8(ck_at(i0 / kWin), h);
+      float uu[kWin], xr[kWin], dl[kWin], du[kWin], yi[kWin], y[kWin];
+      win.unpack(uu, xr);
+      __builtin_amdgcn_sched_barrier(0);  // see chunk_state_dir
+      win.load(a, l, da, i0 + kWin < full_end ? i0 + kWin : i0);
+      prep_window(uu, xr, bias2, 0.0f, dl, du, yi);
+      run_steps<kModeVim, DIR>(l, i0, dl, du, yi, A, h, bcA, bcB, bct, y);
     }
-    const int i_end = (w + 1) * kWin < L ? (w + 1) * kWin : L;
-    for (int i = w * kWin; i < i_end; ++i) {
-      const int64_t p = Dr::pos(l, i);
-      const float d2 = delta2(ld_act(xb, p), bias2);
-      const float du2 = d2 * ld_act(ub, p);
-      const scalar_fp bc = bct + p * kBC;
-#pragma unroll
-      for (int n = 0; n < kH; ++n) h[n] = __builtin_fmaf(du2, bc[n], __builtin_amdgcn_exp2f(d2 * A[n]) * h[n]);
-    }
+    if (full_end < L && l.valid) store8(ck_at(full_end / kWin), h);
   }
 
-  // Backward, window by window.
+  // Backward, window by window from the last.
   const int64_t plane = static_cast<int64_t>(a.batch) * a.dim * a.L;
   const int64_t row = static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(l.dd) * a.L;
   float* guw = ba.gu + (DIR * 2 + l.half) * plane + row;
@@ -1218,92 +1272,140 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
   }
   float dD = 0.0f, dbias = 0.0f;
   float* myrow = rows + l.lane * kRedStride;
-  for (int w = ba.nwin - 1; w >= 0; --w) {
+  RevWin<T, DIR> rw;
+  const int nwin = ba.nwin;
+  if (full_end > 0) rw.load(ub, xb, gb, ck_at(full_end / kWin - 1), l, full_end - kWin);
+  for (int w = nwin - 1; w >= 0; --w) {
     const int i0 = w * kWin;
+    // Steps j >= ns (only in a last, partial window) are padding: Δ = 0 and g = 0 make them leave
+    // the state and the adjoint unchanged and contribute nothing; their loads use step ns - 1.
     const int ns = L - i0 < kWin ? L - i0 : kWin;
-    float hs[kH], hh[kWin][kH], d2[kWin], du2[kWin], uu[kWin], gg[kWin], sg[kWin];
-    const float* c = ck_at(w);
+    float hs[kH], d2[kWin], uu[kWin], gg[kWin], xr[kWin], sg[kWin];
+    if (ns == kWin) {
+      rw.u.template unpack<kRevOrder>(uu);
+      rw.x.template unpack<kRevOrder>(xr);
+      rw.g.template unpack<kRevOrder>(gg);
+      rw.ck.template unpack<false>(hs);
+      __builtin_amdgcn_sched_barrier(0);
+      if (w > 0) rw.load(ub, xb, gb, ck_at(w - 1), l, i0 - kWin);  // the next window down
+    } else {
+      const float* c = ck_at(w);
 #pragma unroll
-    for (int n = 0; n < kH; ++n) hs[n] = c[n];
+      for (int n = 0; n < kH; ++n) hs[n] = c[n];
 #pragma unroll
-    for (int j = 0; j < kWin; ++j) {
-      if (j < ns) {
-        const int64_t p = Dr::pos(l, i0 + j);
-        const float t = __builtin_fmaf(ld_act(xb, p), kLog2e, bias2);
-        d2[j] = softplus2(t);
+      for (int j = 0; j < kWin; ++j) {
+        const int64_t p = Dr::pos(l, i0 + (j < ns ? j : ns - 1));
+        xr[j] = ld_act(xb, p);
         uu[j] = ld_act(ub, p);
-        du2[j] = d2[j] * uu[j];
-        gg[j] = gb[p];
-        sg[j] = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-t));  // sigmoid(Δ_raw + bias)
-        const scalar_fp bc = bct + p * kBC;
-#pragma unroll
-        for (int n = 0; n < kH; ++n) {
-          const float hp = j == 0 ? hs[n] : hh[j - 1][n];
-          hh[j][n] = __builtin_fmaf(du2[j], bc[n], __builtin_amdgcn_exp2f(d2[j] * A[n]) * hp);
-        }
+        gg[j] = j < ns ? gb[p] : 0.0f;
       }
     }
-    // Reduction rounds of two steps each, from the last step of the window down (fully unrolled so
-    // that the window arrays are indexed by constants and stay in registers).
 #pragma unroll
-    for (int r = kWin / 2 - 1; r >= 0; --r) {
-      if (2 * r >= ns) continue;
+    for (int j = 0; j < kWin; ++j) {
+      const float dv = softplus2_sig(__builtin_fmaf(xr[j], kLog2e, bias2), sg[j]);
+      d2[j] = j < ns ? dv : 0.0f;
+    }
+    auto bc_at = [&](int j) { return bct + Dr::pos(l, i0 + (j < ns ? j : ns - 1)) * kBC; };
+    // The window is walked in two halves (steps 7..4, then 3..0).  Each half first rebuilds its
+    // four states from the checkpoint (the upper half runs through steps 0..3 without keeping
+    // them), so only five states per lane are held at a time.
 #pragma unroll
-      for (int jj = 1; jj >= 0; --jj) {
-        const int j = 2 * r + jj;
-        float vb[kH], vc[kH];
-        if (j < ns) {
-          const int64_t p = Dr::pos(l, i0 + j);
-          const scalar_fp bc = bct + p * kBC;
-          float P = 0.0f, Q = 0.0f;
+    for (int hf = 1; hf >= 0; --hf) {
+      const int j0 = 4 * hf;
+      float hq[5][kH];  // hq[0] = state before step j0, hq[1 + k] = state after step j0 + k
+      {
+        float hcur[kH], bc0[kBC], bc1[kBC];
+#pragma unroll
+        for (int n = 0; n < kH; ++n) hcur[n] = hs[n];
+        load_bc(bc_at(0), bc0);
+#pragma unroll
+        for (int j = 0; j < j0 + 4; ++j) {
+          float (&cur)[kBC] = (j & 1) ? bc1 : bc0;
+          float (&nxt)[kBC] = (j & 1) ? bc0 : bc1;
+          __builtin_amdgcn_sched_barrier(0);
+          if (j + 1 < j0 + 4) load_bc(bc_at(j + 1), nxt);
+          __builtin_amdgcn_sched_barrier(0);
+          if (j == j0) {
+#pragma unroll
+            for (int n = 0; n < kH; ++n) hq[0][n] = hcur[n];
+          }
+          const float du2 = d2[j] * uu[j];
+#pragma unroll
+          for (int n = 0; n < kH; ++n) hcur[n] = __builtin_fmaf(du2, cur[n], __builtin_amdgcn_exp2f(d2[j] * A[n]) * hcur[n]);
+          if (j >= j0) {
+#pragma unroll
+            for (int n = 0; n < kH; ++n) hq[1 + j - j0][n] = hcur[n];
+          }
+        }
+      }
+      // The decays are recomputed in the walk rather than kept from the rebuild (more registers);
+      // hiding Δ2 from the compiler stops it from reusing the earlier values.
+#pragma unroll
+      for (int j = j0; j < j0 + 4; ++j) asm volatile("" : "+v"(d2[j]));
+      float bc0[kBC], bc1[kBC];
+      load_bc(bc_at(j0 + 3), bc1);
+#pragma unroll
+      for (int r = 1; r >= 0; --r) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int jj = 1; jj >= 0; --jj) {
+          const int k = 2 * r + jj, j = j0 + k;
+          float (&cur)[kBC] = (j & 1) ? bc1 : bc0;
+          float (&nxt)[kBC] = (j & 1) ? bc0 : bc1;
+          float vb[kH], vc[kH];
+          float P[2] = {0.0f, 0.0f}, Q[2] = {0.0f, 0.0f};  // two chains each
+          const float mdu = vmask * d2[j] * uu[j], mg = vmask * gg[j];
 #pragma unroll
           for (int n = 0; n < kH; ++n) {
             const float an = __builtin_amdgcn_exp2f(d2[j] * A[n]);
-            lam[n] = __builtin_fmaf(gg[j], bc[kH + n], anext[n] * lam[n]);
-            const float hp = j == 0 ? hs[n] : hh[j - 1][n];
-            const float wv = lam[n] * an * hp;
-            Q = __builtin_fmaf(A[n], wv, Q);
+            lam[n] = __builtin_fmaf(gg[j], cur[kH + n], anext[n] * lam[n]);
+            const float wv = lam[n] * (an * hq[k][n]);
+            Q[n & 1] = __builtin_fmaf(A[n], wv, Q[n & 1]);
             dA[n] = __builtin_fmaf(d2[j], wv, dA[n]);
-            P = __builtin_fmaf(lam[n], bc[n], P);
-            vb[n] = vmask * lam[n] * du2[j];
-            vc[n] = vmask * gg[j] * hh[j][n];
+            P[n & 1] = __builtin_fmaf(lam[n], cur[n], P[n & 1]);
+            vb[n] = lam[n] * mdu;
+            vc[n] = mg * hq[k + 1][n];
             anext[n] = an;
           }
-          const float dd = __builtin_fmaf(uu[j] * kLog2e, P, Q);
-          if (l.valid) {
-            guw[p] = __builtin_fmaf(d2[j], P, Dh * gg[j]);
-            gxw[p] = sg[j] * dd;
-          }
-          dbias = __builtin_fmaf(sg[j], dd, dbias);
+          __builtin_amdgcn_sched_barrier(0);
+          if (j > j0) load_bc(bc_at(j - 1), nxt);
+          __builtin_amdgcn_sched_barrier(0);
+          const float Ps = P[0] + P[1];
+          const float dd = __builtin_fmaf(uu[j] * kLog2e, Ps, Q[0] + Q[1]);
+          const float gx = sg[j] * dd;
+          dbias += j < ns ? gx : 0.0f;
           dD = __builtin_fmaf(gg[j], uu[j], dD);
-        } else {
-#pragma unroll
-          for (int n = 0; n < kH; ++n) vb[n] = vc[n] = 0.0f;
+          if (l.valid && j < ns) {
+            const int64_t p = Dr::pos(l, i0 + j);
+            guw[p] = __builtin_fmaf(d2[j], Ps, Dh * gg[j]);
+            gxw[p] = gx;
+          }
+          float4* dst = reinterpret_cast<float4*>(myrow + jj * 2 * kH);
+          dst[0] = make_float4(vb[0], vb[1], vb[2], vb[3]);
+          dst[1] = make_float4(vb[4], vb[5], vb[6], vb[7]);
+          dst[2] = make_float4(vc[0], vc[1], vc[2], vc[3]);
+          dst[3] = make_float4(vc[4], vc[5], vc[6], vc[7]);
         }
-        float4* dst = reinterpret_cast<float4*>(myrow + jj * 2 * kH);
-        dst[0] = make_float4(vb[0], vb[1], vb[2], vb[3]);
-        dst[1] = make_float4(vb[4], vb[5], vb[6], vb[7]);
-        dst[2] = make_float4(vc[0], vc[1], vc[2], vc[3]);
-        dst[3] = make_float4(vc[4], vc[5], vc[6], vc[7]);
-      }
-      // A wave's LDS accesses execute in order, so every lane's row is written before it is read
-      // and read before the next round overwrites it; the compiler barriers keep that order.
-      asm volatile("" ::: "memory");
-      const float sum = wave_column_sum(rows, l.lane);
-      asm volatile("" ::: "memory");
-      if (l.lane < kRedCols) {
-        const int jj = l.lane >> 4, ty = (l.lane >> 3) & 1, k = l.lane & 7;
-        const int j = 2 * r + jj;
-        if (j < ns) dbcw[(static_cast<int64_t>(ty) * kN + kH * l.half + k) * a.L + Dr::pos(l, i0 + j)] = sum;
+        // A wave's LDS accesses execute in order, so every lane's row is written before it is
+        // read and read before the next round overwrites it; the compiler barriers keep that order.
+        asm volatile("" ::: "memory");
+        const float sum = wave_column_sum(rows, l.lane);
+        asm volatile("" ::: "memory");
+        if (l.lane < kRedCols) {
+          const int jj = l.lane >> 4, ty = (l.lane >> 3) & 1, kk = l.lane & 7;
+          const int j = j0 + 2 * r + jj;
+          if (j < ns) dbcw[(static_cast<int64_t>(ty) * kN + kH * l.half + kk) * a.L + Dr::pos(l, i0 + j)] = sum;
+        }
       }
     }
   }
   if (l.valid) {
-    float* pp = ba.dpar + (((static_cast<int64_t>(l.b) * 2 + DIR) * 2 + l.half) * a.dim + l.d) * kParStride;
+    // [dir][half][dim][kParStride][batch]: the batch sums read contiguous runs
+    float* pp = ba.dpar + ((static_cast<int64_t>(DIR) * 2 + l.half) * a.dim + l.d) * kParStride * a.batch + l.b;
 #pragma unroll
-    for (int n = 0; n < kH; ++n) pp[n] = dA[n];
-    pp[kH] = l.half == 0 ? dD : 0.0f;
-    pp[kH + 1] = dbias;
+    for (int n = 0; n < kH; ++n) pp[n * a.batch] = dA[n];
+    pp[kH * a.batch] = l.half == 0 ? dD : 0.0f;
+    pp[(kH + 1) * a.batch] = dbias;
   }
 }
 
@@ -1358,46 +1460,51 @@ __global__ __launch_bounds__(256) void bwd_bc_kernel(const float* __restrict__ d
   st_act(dst, o, ty == 0 ? s * kLn2 : s);
 }
 
-// dA_log, dD, dbias per direction: sums over batch (and state halves / directions as needed).
+// dA_log, dD, dbias per direction: sums over batch (and state halves); for shared inputs
+// (dbias_b NULL) the backward branch's dbias is added to the forward one.  One wave per output
+// value: the lanes take batch entries (contiguous in the partial-sum layout) and a butterfly
+// adds them up.
+__device__ __forceinline__ float wave_batch_sum(const float* p, int batch, int lane) {
+  float s = 0.0f;
+  for (int b = lane; b < batch; b += kW) s += p[b];
+#pragma unroll
+  for (int m = kW / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+  return s;
+}
+
 __global__ __launch_bounds__(256) void bwd_param_kernel(const float* __restrict__ dpar, const float* A_log,
                                                         const float* A_b_log, float* dA_log, float* dA_b_log,
                                                         float* dD, float* dD_b, float* dbias, float* dbias_b,
                                                         int batch, int dim) {
-  const int i = blockIdx.x * 256 + threadIdx.x;  // (dir, d, n)
-  if (i >= 2 * dim * kN) return;
-  const int dir = i / (dim * kN), d = (i / kN) % dim, n = i % kN;
-  const int half = n / kH;
-  auto at = [&](int b, int dr, int hf, int k) {
-    return dpar[(((static_cast<int64_t>(b) * 2 + dr) * 2 + hf) * dim + d) * kParStride + k];
+  // items: (dir, d, n) for dA_log, then (dir, d, {dD, dbias})
+  const int item = blockIdx.x * 4 + static_cast<int>(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int nA = 2 * dim * kN;
+  if (item >= nA + 4 * dim) return;
+  auto at = [&](int dr, int hf, int k) {
+    return dpar + ((static_cast<int64_t>(dr) * 2 + hf) * dim) * kParStride * batch + static_cast<int64_t>(k) * batch;
   };
-  float sa = 0.0f;
-  for (int b = 0; b < batch; ++b) sa += at(b, dir, half, n % kH);
-  const float* al = dir == 0 ? A_log : A_b_log;
-  const float An = -__expf(al[static_cast<int64_t>(d) * kN + n]);
-  (dir == 0 ? dA_log : dA_b_log)[static_cast<int64_t>(d) * kN + n] = sa * kLn2 * An;
-  if (n == 0) {
-    float sd = 0.0f, sb = 0.0f;
-    for (int b = 0; b < batch; ++b) {
-      sd += at(b, dir, 0, kH);
-      sb += at(b, dir, 0, kH + 1) + at(b, dir, 1, kH + 1);
+  if (item < nA) {
+    const int dir = item / (dim * kN), d = (item / kN) % dim, n = item % kN;
+    const float s = wave_batch_sum(at(dir, n / kH, n % kH) + static_cast<int64_t>(d) * kParStride * batch, batch, lane);
+    if (lane == 0) {
+      const float An = -__expf((dir == 0 ? A_log : A_b_log)[static_cast<int64_t>(d) * kN + n]);
+      (dir == 0 ? dA_log : dA_b_log)[static_cast<int64_t>(d) * kN + n] = s * kLn2 * An;
     }
-    (dir == 0 ? dD : dD_b)[d] = sd;
-    if (dir == 0 || dbias_b) {
-      (dir == 0 ? dbias : dbias_b)[d] = sb;
-    }
+    return;
   }
-}
-
-// Shared-input dbias: the backward branch's sum is added to the forward one (run after
-// bwd_param_kernel, which wrote the forward sum).
-__global__ __launch_bounds__(256) void bwd_bias_shared_kernel(const float* __restrict__ dpar, float* dbias, int batch,
-                                                              int dim) {
-  const int d = blockIdx.x * 256 + threadIdx.x;
-  if (d >= dim) return;
-  float sb = 0.0f;
-  for (int b = 0; b < batch; ++b)
-    for (int hf = 0; hf < 2; ++hf) sb += dpar[(((static_cast<int64_t>(b) * 2 + 1) * 2 + hf) * dim + d) * kParStride + kH + 1];
-  dbias[d] += sb;
+  const int r = item - nA, dir = r / (2 * dim), d = (r / 2) % dim, which = r & 1;
+  const int64_t off = static_cast<int64_t>(d) * kParStride * batch;
+  if (which == 0) {
+    const float s = wave_batch_sum(at(dir, 0, kH) + off, batch, lane);
+    if (lane == 0) (dir == 0 ? dD : dD_b)[d] = s;
+    return;
+  }
+  if (dir == 1 && !dbias_b) return;  // added into dbias by the forward item
+  float s = wave_batch_sum(at(dir, 0, kH + 1) + off, batch, lane) + wave_batch_sum(at(dir, 1, kH + 1) + off, batch, lane);
+  if (dir == 0 && !dbias_b)
+    s += wave_batch_sum(at(1, 0, kH + 1) + off, batch, lane) + wave_batch_sum(at(1, 1, kH + 1) + off, batch, lane);
+  if (lane == 0) (dir == 0 ? dbias : dbias_b)[d] = s;
 }
 
 struct BwdLayout {
@@ -1437,7 +1544,7 @@ vmscan_status run_bwd(const ScanArgs& fwd, const BwdLayout& lay, unsigned char* 
   a.wsy = ysum;
   vmscan_status st = run_pair<T, kModeVimSum>(a, stream, kStageAll);
   if (st != VMSCAN_OK) return st;
-  hipLaunchKernelGGL(gate_bwd_kernel<T>, dim3(static_cast<unsigned>(ceil_div(n, 1024))), dim3(256), 0, stream,
+  hipLaunchKernelGGL(gate_bwd_kernel<T>, dim3(static_cast<unsigned>(ceil_div(n, 256 * kWin))), dim3(256), 0, stream,
                      static_cast<const T*>(dout), static_cast<const T*>(z), ysum, g, static_cast<T*>(dz), n);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return launch_failed(e);
@@ -1462,11 +1569,8 @@ vmscan_status run_bwd(const ScanArgs& fwd, const BwdLayout& lay, unsigned char* 
   hipLaunchKernelGGL(bwd_bc_kernel<T>, dim3(static_cast<unsigned>(ceil_div(nbc, 256))), dim3(256), 0, stream, ba.dbc,
                      static_cast<T*>(dB), static_cast<T*>(dC), static_cast<T*>(dB_b), static_cast<T*>(dC_b), fwd.batch,
                      fwd.ngroups, fwd.L);
-  hipLaunchKernelGGL(bwd_param_kernel, dim3(static_cast<unsigned>(ceil_div(2 * fwd.dim * kN, 256))), dim3(256), 0,
+  hipLaunchKernelGGL(bwd_param_kernel, dim3(static_cast<unsigned>(ceil_div(2 * fwd.dim * kN + 4 * fwd.dim, 4))), dim3(256), 0,
                      stream, ba.dpar, A_log, A_b_log, dA_log, dA_b_log, dD, dD_b, dbias, dbias_b, fwd.batch, fwd.dim);
-  if (!dbias_b)
-    hipLaunchKernelGGL(bwd_bias_shared_kernel, dim3(static_cast<unsigned>(ceil_div(fwd.dim, 256))), dim3(256), 0,
-                       stream, ba.dpar, dbias, fwd.batch, fwd.dim);
   e = hipGetLastError();
   return e == hipSuccess ? VMSCAN_OK : launch_failed(e);
 }
