@@ -1199,26 +1199,69 @@ __device__ __forceinline__ float wave_column_sum(const float* rows, int lane) {
 
 // Raw inputs of one full 8-step window of the backward walk, loaded one window ahead: u and
 // Δ_raw (activation dtype), g (float32) and the checkpoint state entering the window.
-template <typename T, int DIR>
+template <typename T, int MODE, int DIR>
 struct RevWin {
-  using Dr = Dir<kModeVim, DIR>;
+  using Dr = Dir<MODE, DIR>;
   Run8<T> u, x;
   Run8<float> g, ck;
-  __device__ __forceinline__ void load(const T* ub, const T* xb, const float* gb, const float* ckp, const Lane& l,
-                                       int i0) {
+  __device__ __forceinline__ void load(const ScanArgs& a, const T* ub, const T* xb, const float* gb, const float* ckp,
+                                       const Lane& l, int i0) {
     const int64_t p = Dr::pos(l, i0);
     const int64_t lo = Dr::kPosSgn > 0 ? p : p - (kWin - 1);  // lowest position of the window
+    const int64_t si = Dr::sidx(a, l, i0);
     u.load(ub + lo);
-    x.load(xb + lo);
+    x.load(xb + (Dr::kSidxSgn > 0 ? si : si - (kWin - 1)));
     g.load(gb + lo);
     ck.load(ckp);
   }
 };
 
-template <typename T, int DIR>
+// Forward over the sequence, storing the state entering each 8-step window (the steps of a last,
+// partial window are not needed: nothing follows them).  Its own kernel: it needs few registers
+// and so runs at full occupancy.
+template <typename T, int MODE, int DIR>
+__device__ __forceinline__ void bwd_ckpt_dir(const BwdArgs& ba, const Lane& l) {
+  const ScanArgs& a = ba.s;
+  using Dr = Dir<MODE, DIR>;
+  const DirArgs& da = DIR == 0 ? a.d0 : a.d1;
+  const int L = static_cast<int>(a.L);
+  float A[kH];
+  load_a2(da, l, A);
+  const float bias2 = da.bias[l.dd] * kLog2e;
+  const scalar_fp bct = bc_row<DIR>(a, l);
+  float* ckw = ba.ck + ((static_cast<int64_t>(l.b) * 2 + DIR) * 2 + l.half) * ba.nwin * a.dim * kH;
+  auto ck_at = [&](int w) { return ckw + (static_cast<int64_t>(w) * a.dim + l.dd) * kH; };
+  const int full_end = (L / kWin) * kWin;
+  float h[kH], bcA[kBC], bcB[kBC];
+#pragma unroll
+  for (int n = 0; n < kH; ++n) h[n] = 0.0f;
+  Window<T, MODE, DIR> win;
+  load_bc(bct + Dr::pos(l, 0) * kBC, bcA);
+  if (full_end > 0) win.load(a, l, da, 0);
+  for (int i0 = 0; i0 < full_end; i0 += kWin) {
+    if (l.valid) store8(ck_at(i0 / kWin), h);
+    float uu[kWin], xr[kWin], dl[kWin], du[kWin], yi[kWin], y[kWin];
+    win.unpack(uu, xr);
+    __builtin_amdgcn_sched_barrier(0);  // see chunk_state_dir
+    win.load(a, l, da, i0 + kWin < full_end ? i0 + kWin : i0);
+    prep_window(uu, xr, bias2, 0.0f, dl, du, yi);
+    run_steps<MODE, DIR>(l, i0, dl, du, yi, A, h, bcA, bcB, bct, y);
+  }
+  if (full_end < L && l.valid) store8(ck_at(full_end / kWin), h);
+}
+
+template <typename T, int MODE>
+__global__ __launch_bounds__(kThreads) void bwd_ckpt_kernel(BwdArgs ba) {
+  const Lane l = lane_ctx(ba.s);
+  if ((__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6) & 1) == 0) bwd_ckpt_dir<T, MODE, 0>(ba, l);
+  else bwd_ckpt_dir<T, MODE, 1>(ba, l);
+}
+
+// The adjoint walk of one direction and state half, window by window from the last.
+template <typename T, int MODE, int DIR>
 __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float* rows) {
   const ScanArgs& a = ba.s;
-  using Dr = Dir<kModeVim, DIR>;
+  using Dr = Dir<MODE, DIR>;
   constexpr bool kRevOrder = Dr::kPosSgn < 0;  // window positions descend with the step
   const DirArgs& da = DIR == 0 ? a.d0 : a.d1;
   const int L = static_cast<int>(a.L);
@@ -1234,27 +1277,6 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
   float* ckw = ba.ck + ((static_cast<int64_t>(l.b) * 2 + DIR) * 2 + l.half) * ba.nwin * a.dim * kH;
   auto ck_at = [&](int w) { return ckw + (static_cast<int64_t>(w) * a.dim + l.dd) * kH; };
   const int full_end = (L / kWin) * kWin;
-
-  // Forward over the sequence, storing the state entering each window (the steps of the last,
-  // partial window are not needed: nothing follows them).
-  {
-    float h[kH], bcA[kBC], bcB[kBC];
-#pragma unroll
-    for (int n = 0; n < kH; ++n) h[n] = 0.0f;
-    Window<T, kModeVim, DIR> win;
-    load_bc(bct + Dr::pos(l, 0) * kBC, bcA);
-    if (full_end > 0) win.load(a, l, da, 0);
-    for (int i0 = 0; i0 < full_end; i0 += kWin) {
-      if (l.valid) store8(ck_at(i0 / kWin), h);
-      float uu[kWin], xr[kWin], dl[kWin], du[kWin], yi[kWin], y[kWin];
-      win.unpack(uu, xr);
-      __builtin_amdgcn_sched_barrier(0);  // see chunk_state_dir
-      win.load(a, l, da, i0 + kWin < full_end ? i0 + kWin : i0);
-      prep_window(uu, xr, bias2, 0.0f, dl, du, yi);
-      run_steps<kModeVim, DIR>(l, i0, dl, du, yi, A, h, bcA, bcB, bct, y);
-    }
-    if (full_end < L && l.valid) store8(ck_at(full_end / kWin), h);
-  }
 
   // Backward, window by window from the last.
   const int64_t plane = static_cast<int64_t>(a.batch) * a.dim * a.L;
@@ -1272,9 +1294,9 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
   }
   float dD = 0.0f, dbias = 0.0f;
   float* myrow = rows + l.lane * kRedStride;
-  RevWin<T, DIR> rw;
+  RevWin<T, MODE, DIR> rw;
   const int nwin = ba.nwin;
-  if (full_end > 0) rw.load(ub, xb, gb, ck_at(full_end / kWin - 1), l, full_end - kWin);
+  if (full_end > 0) rw.load(a, ub, xb, gb, ck_at(full_end / kWin - 1), l, full_end - kWin);
   for (int w = nwin - 1; w >= 0; --w) {
     const int i0 = w * kWin;
     // Steps j >= ns (only in a last, partial window) are padding: Δ = 0 and g = 0 make them leave
@@ -1283,19 +1305,20 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
     float hs[kH], d2[kWin], uu[kWin], gg[kWin], xr[kWin], sg[kWin];
     if (ns == kWin) {
       rw.u.template unpack<kRevOrder>(uu);
-      rw.x.template unpack<kRevOrder>(xr);
+      rw.x.template unpack<(Dr::kSidxSgn < 0)>(xr);
       rw.g.template unpack<kRevOrder>(gg);
       rw.ck.template unpack<false>(hs);
       __builtin_amdgcn_sched_barrier(0);
-      if (w > 0) rw.load(ub, xb, gb, ck_at(w - 1), l, i0 - kWin);  // the next window down
+      if (w > 0) rw.load(a, ub, xb, gb, ck_at(w - 1), l, i0 - kWin);  // the next window down
     } else {
       const float* c = ck_at(w);
 #pragma unroll
       for (int n = 0; n < kH; ++n) hs[n] = c[n];
 #pragma unroll
       for (int j = 0; j < kWin; ++j) {
-        const int64_t p = Dr::pos(l, i0 + (j < ns ? j : ns - 1));
-        xr[j] = ld_act(xb, p);
+        const int ij = i0 + (j < ns ? j : ns - 1);
+        const int64_t p = Dr::pos(l, ij);
+        xr[j] = ld_act(xb, Dr::sidx(a, l, ij));
         uu[j] = ld_act(ub, p);
         gg[j] = j < ns ? gb[p] : 0.0f;
       }
@@ -1376,9 +1399,8 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
           dbias += j < ns ? gx : 0.0f;
           dD = __builtin_fmaf(gg[j], uu[j], dD);
           if (l.valid && j < ns) {
-            const int64_t p = Dr::pos(l, i0 + j);
-            guw[p] = __builtin_fmaf(d2[j], Ps, Dh * gg[j]);
-            gxw[p] = gx;
+            guw[Dr::pos(l, i0 + j)] = __builtin_fmaf(d2[j], Ps, Dh * gg[j]);
+            gxw[Dr::sidx(a, l, i0 + j)] = gx;  // Δ_raw's own storage order
           }
           float4* dst = reinterpret_cast<float4*>(myrow + jj * 2 * kH);
           dst[0] = make_float4(vb[0], vb[1], vb[2], vb[3]);
@@ -1394,7 +1416,7 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
         if (l.lane < kRedCols) {
           const int jj = l.lane >> 4, ty = (l.lane >> 3) & 1, kk = l.lane & 7;
           const int j = j0 + 2 * r + jj;
-          if (j < ns) dbcw[(static_cast<int64_t>(ty) * kN + kH * l.half + kk) * a.L + Dr::pos(l, i0 + j)] = sum;
+          if (j < ns) dbcw[(static_cast<int64_t>(ty) * kN + kH * l.half + kk) * a.L + Dr::sidx(a, l, i0 + j)] = sum;
         }
       }
     }
@@ -1409,13 +1431,13 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
   }
 }
 
-template <typename T>
+template <typename T, int MODE>
 __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdArgs ba) {
   __shared__ __attribute__((aligned(16))) float rows[4][kW * kRedStride];
   const Lane l = lane_ctx(ba.s);
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-  if ((w & 1) == 0) bwd_dir<T, 0>(ba, l, rows[w]);
-  else bwd_dir<T, 1>(ba, l, rows[w]);
+  if ((w & 1) == 0) bwd_dir<T, MODE, 0>(ba, l, rows[w]);
+  else bwd_dir<T, MODE, 1>(ba, l, rows[w]);
 }
 
 // du, dΔ_raw (and the backward branch's, or their sums when the branches share inputs):
@@ -1559,8 +1581,11 @@ vmscan_status run_bwd(const ScanArgs& fwd, const BwdLayout& lay, unsigned char* 
   ba.dbc = reinterpret_cast<float*>(wsp + lay.dbc);
   ba.dpar = reinterpret_cast<float*>(wsp + lay.dpar);
   ba.nwin = static_cast<int>(ceil_div(fwd.L, kWin));
-  hipLaunchKernelGGL(bwd_scan_kernel<T>, dim3(static_cast<unsigned>(static_cast<int64_t>(fwd.batch) * fwd.ngroups)),
-                     dim3(kThreads), 0, stream, ba);
+  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(fwd.batch) * fwd.ngroups));
+  hipLaunchKernelGGL((bwd_ckpt_kernel<T, kModeVim>), grid, dim3(kThreads), 0, stream, ba);
+  e = hipGetLastError();
+  if (e != hipSuccess) return launch_failed(e);
+  hipLaunchKernelGGL((bwd_scan_kernel<T, kModeVim>), grid, dim3(kThreads), 0, stream, ba);
   e = hipGetLastError();
   if (e != hipSuccess) return launch_failed(e);
   hipLaunchKernelGGL(bwd_combine_kernel<T>, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, stream,
