@@ -17,6 +17,7 @@ from .vmscan_oracle import (  # noqa: F401
     vim_bidir_v2_bwd,
     ss2d_orders,
     ss2d_cross_scan,
+    ss2d_cross_scan_bwd,
     ss2d_cross_scan_pathwalk,
     rel_err,
 )

@@ -279,6 +279,55 @@ def ss2d_cross_scan(x, delta_raw, A_log, B, C, D, delta_bias, z=None):
     return out
 
 
+def ss2d_cross_scan_bwd(x, delta_raw, A_log, B, C, D, delta_bias, z, dout):
+    """Gradients of ``ss2d_cross_scan`` for dout = dL/dout [batch, dim, H, W] (z may be None).
+
+    out = silu(z) Σ_k back_k(y_k) with y_k the scan of the k-th ordering of x, so the gradient
+    reaching direction k's outputs is the same ordering applied to dL/d(Σ) = dout silu(z) (or
+    dout without a gate); ``scan_1d_bwd`` gives that direction's gradients, and its du, in
+    direction k's scan order, is mapped back to pixels and summed into dx.  Per-direction
+    tensors (Δ_raw, B, C) keep their scan order.  dz = dout Σ_k back_k(y_k) silu'(z).
+    Returns dict(dx, ddelta_raw [batch,4,dim,L], dA_log [4,dim,N], dB, dC [batch,4,N,L],
+    dD, ddelta_bias [4,dim], dz (None without z)).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    nb, nd, H, W = x.shape
+    L = H * W
+    seqs = ss2d_orders(x)
+    col_back = lambda y: np.swapaxes(y.reshape(nb, nd, W, H), 2, 3).reshape(nb, nd, L)
+    backs = [lambda y: y, col_back, lambda y: np.flip(y, axis=-1), lambda y: col_back(np.flip(y, axis=-1))]
+    if z is not None:
+        z = np.asarray(z, dtype=np.float64)
+        gsum = dout * silu(z)
+    else:
+        gsum = dout
+    gorders = ss2d_orders(gsum)       # dL/dy_k: the k-th ordering of the merged gradient
+    dx = np.zeros((nb, nd, L))
+    ysum = np.zeros((nb, nd, L))
+    res = dict(ddelta_raw=np.zeros((nb, 4, nd, L)), dA_log=np.zeros(np.asarray(A_log).shape),
+               dB=np.zeros((nb, 4) + np.asarray(B).shape[2:]), dC=np.zeros((nb, 4) + np.asarray(C).shape[2:]),
+               dD=np.zeros(np.asarray(D).shape), ddelta_bias=np.zeros(np.asarray(delta_bias).shape))
+    for k in range(4):
+        r = scan_1d_bwd(seqs[k], np.asarray(delta_raw)[:, k], np.asarray(A_log)[k], np.asarray(B)[:, k],
+                        np.asarray(C)[:, k], np.asarray(D)[k], np.asarray(delta_bias)[k], gorders[k])
+        dx += backs[k](r["du"])
+        ysum += backs[k](r["s"])
+        res["ddelta_raw"][:, k] = r["ddelta_raw"]
+        res["dA_log"][k] = r["dA_log"]
+        res["dB"][:, k] = r["dB"]
+        res["dC"][:, k] = r["dC"]
+        res["dD"][k] = r["dD"]
+        res["ddelta_bias"][k] = r["ddelta_bias"]
+    res["dx"] = dx.reshape(nb, nd, H, W)
+    if z is not None:
+        sig = expit(z)
+        res["dz"] = dout * ysum.reshape(nb, nd, H, W) * sig * (1.0 + z * (1.0 - sig))
+    else:
+        res["dz"] = None
+    return res
+
+
 def ss2d_cross_scan_pathwalk(x, delta_raw, A_log, B, C, D, delta_bias, z=None):
     """SS2D by walking each direction's path pixel by pixel with explicit (h, w) coordinates
     (pure Python loops; tiny inputs only).  Independent of the reshape/transpose/flip code in

@@ -1,5 +1,6 @@
 """Pins for the fp64 oracle: each ``pin_*`` takes an implementation namespace (with
-``scan_1d``, ``vim_bidir``, ``vim_bidir_v2``, ``vim_bidir_v2_bwd``, ``ss2d_cross_scan``) and returns the list of failure messages
+``scan_1d``, ``vim_bidir``, ``vim_bidir_v2``, ``vim_bidir_v2_bwd``, ``ss2d_cross_scan``,
+``ss2d_cross_scan_bwd``) and returns the list of failure messages
 (empty = pass).  They check the oracle against facts fixed by the mathematics, not against the
 oracle itself: hand-derived closed forms, brute force on tiny inputs, linearity, the flip
 identity, limits and the SS2D reductions.  ``test_oracle_pins`` runs them on the oracle;
@@ -446,6 +447,48 @@ def pin_bwd_shared_inputs(impl):
     return msgs
 
 
+SS2D_NAMES = ("x", "delta_raw", "A_log", "B", "C", "D", "delta_bias")
+SS2D_GRADS = dict(x="dx", delta_raw="ddelta_raw", A_log="dA_log", B="dB", C="dC", D="dD", delta_bias="ddelta_bias",
+                  z="dz")
+
+
+def pin_ss2d_bwd_finite_differences(impl):
+    """Every SS2D gradient, with and without the gate, against central finite differences of the
+    forward on a tiny non-square image (so the row and column orders differ)."""
+    msgs = []
+    rng = np.random.default_rng(16)
+    for gated in (False, True):
+        p = rich_ss2d(rng, nb=1, nd=2, H=2, W=3, N=2)
+        p["z"] = rng.standard_normal(p["x"].shape) if gated else None
+        dout = rng.standard_normal(p["x"].shape)
+        names = SS2D_NAMES + (("z",) if gated else ())
+        loss = lambda q: float(np.sum(O.ss2d_cross_scan(*[q[k] for k in SS2D_NAMES], q["z"]) * dout))
+        grads = impl.ss2d_cross_scan_bwd(*[p[k] for k in SS2D_NAMES], p["z"], dout)
+        if not gated and grads["dz"] is not None:
+            msgs.append("ungated dz is not None")
+        eps = 1e-6
+        for k in names:
+            x = np.asarray(p[k], dtype=np.float64)
+            fd = np.zeros_like(x)
+            for i in np.ndindex(x.shape):
+                q = dict(p)
+                xp = x.copy()
+                xp[i] += eps
+                q[k] = xp
+                lp = loss(q)
+                xm = x.copy()
+                xm[i] -= eps
+                q[k] = xm
+                fd[i] = (lp - loss(q)) / (2 * eps)
+            got = np.asarray(grads[SS2D_GRADS[k]], dtype=np.float64)
+            if got.shape != fd.shape:
+                msgs.append(f"ss2d d{k}: shape {got.shape} != {fd.shape}")
+                continue
+            err = float(np.max(np.abs(got - fd)) / max(np.max(np.abs(fd)), 1e-12))
+            _check(msgs, f"ss2d d{k} vs finite differences (gated={gated})", err, 1e-6)
+    return msgs
+
+
 ALL_PINS = [
     pin_softplus_silu,
     pin_golden_single_token,
@@ -465,4 +508,5 @@ ALL_PINS = [
     pin_v2_flip_identity,
     pin_bwd_finite_differences,
     pin_bwd_shared_inputs,
+    pin_ss2d_bwd_finite_differences,
 ]

@@ -153,6 +153,35 @@ def _v2_bwd(u, dr, bias, ub, drb, biasb, z, Al, Abl, B, C, Bb, Cb, D, Db, dout, 
                 dD=fw["dD"], dD_b=bw["dD"])
 
 
+def _ss2d_bwd(x, dr, Al, B, C, D, bias, z, dout, bug=None):
+    """A copy of the oracle's SS2D gradient with an optional planted mistake."""
+    r = O.ss2d_cross_scan_bwd(x, dr, Al, B, C, D, bias, z, dout)
+    if bug is None:
+        return r
+    x = np.asarray(x, dtype=np.float64)
+    nb, nd, H, W = x.shape
+    L = H * W
+    seqs = O.ss2d_orders(x)
+    gsum = np.asarray(dout, dtype=np.float64) * (O.silu(z) if z is not None else 1.0)
+    gord = O.ss2d_orders(gsum)
+    if bug == "g_not_reordered":
+        gord = [gsum.reshape(nb, nd, L)] * 4
+    col_back = lambda y: np.swapaxes(y.reshape(nb, nd, W, H), 2, 3).reshape(nb, nd, L)
+    backs = [lambda y: y, col_back, lambda y: np.flip(y, axis=-1), lambda y: col_back(np.flip(y, axis=-1))]
+    if bug == "du_not_mapped_back":
+        backs = [lambda y: y] * 4
+    dx = np.zeros((nb, nd, L))
+    out = dict(r)
+    for k in range(4):
+        rk = O.scan_1d_bwd(seqs[k], np.asarray(dr)[:, k], np.asarray(Al)[k], np.asarray(B)[:, k], np.asarray(C)[:, k],
+                           np.asarray(D)[k], np.asarray(bias)[k], gord[k])
+        dx += backs[k](rk["du"])
+    out["dx"] = dx.reshape(nb, nd, H, W)
+    if bug == "dz_missing_silu_derivative" and z is not None:
+        out["dz"] = np.asarray(dout) * O.ss2d_cross_scan(x, dr, Al, B, C, D, bias)  # silu'(z) factor dropped
+    return out
+
+
 def _ss2d(x, dr, Al, B, C, D, bias, z=None, bug=None, scan_bug=None):
     x = np.asarray(x, dtype=np.float64)
     nb, nd, H, W = x.shape
@@ -178,8 +207,9 @@ def _ss2d(x, dr, Al, B, C, D, bias, z=None, bug=None, scan_bug=None):
     return out
 
 
-def _impl(scan_bug=None, vim_bug=None, ss2d_bug=None, v2_bug=None, bwd_bug=None):
+def _impl(scan_bug=None, vim_bug=None, ss2d_bug=None, v2_bug=None, bwd_bug=None, ss2d_bwd_bug=None):
     return types.SimpleNamespace(
+        ss2d_cross_scan_bwd=lambda *a: _ss2d_bwd(*a, bug=ss2d_bwd_bug),
         vim_bidir_v2_bwd=lambda *a: _v2_bwd(*a, bug=bwd_bug),
         softplus=O.softplus,
         silu=O.silu,
@@ -195,6 +225,7 @@ SCAN_BUGS = ["A_not_exp", "A_sign", "swap_BC", "no_softplus", "exp_not_softplus"
 VIM_BUGS = ["bwd_uses_fwd_BC", "bwd_uses_fwd_A", "bwd_BC_not_flipped", "bwd_delta_not_flipped", "bwd_D_is_fwd_D",
             "gate_not_flipped", "no_flip_back", "sum_not_avg", "gate_silu_is_sigmoid"]
 SS2D_BUGS = ["col_as_reshape", "col_not_transposed_back", "rev_not_flipped_back", "avg4"]
+SS2D_BWD_BUGS = ["g_not_reordered", "du_not_mapped_back", "dz_missing_silu_derivative"]
 BWD_BUGS = ["du_no_D", "lambda_same_step_decay", "dC_prev_state", "dB_no_delta", "ddelta_next_state", "no_sigmoid",
             "dA_log_no_chain", "bwd_g_not_flipped", "dz_silu_not_derivative", "bwd_grads_not_flipped"]
 V2_BUGS = ["v2_bwd_uses_fwd_u", "v2_bwd_uses_fwd_delta", "v2_bwd_uses_fwd_bias", "v2_fwd_uses_bwd_bias", "v2_ub_not_flipped"]
@@ -240,3 +271,8 @@ def test_v2_mutant_caught(bug):
 @pytest.mark.parametrize("bug", BWD_BUGS)
 def test_bwd_mutant_caught(bug):
     assert _caught(_impl(bwd_bug=bug)), f"planted mistake {bug} passes every pin"
+
+
+@pytest.mark.parametrize("bug", SS2D_BWD_BUGS)
+def test_ss2d_bwd_mutant_caught(bug):
+    assert _caught(_impl(ss2d_bwd_bug=bug)), f"planted mistake {bug} passes every pin"
