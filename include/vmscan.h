@@ -203,6 +203,34 @@ vmscan_status vmscan_bwd_bidir_v2(const void *u, const void *delta_raw, const fl
                                   vmscan_dtype dtype, void *workspace, size_t workspace_bytes,
                                   hipStream_t stream);
 
+/*
+ * Gradients of ss2d_cross_scan_fwd (the SS2D backward pass).  Given the forward's inputs and
+ * dout = dL/dout [batch, dim, H, W]:
+ *   dx                 : [batch, dim, H, W]          activation dtype
+ *   ddelta_raw         : [batch, 4, dim, H*W]        activation dtype, each direction's scan order
+ *   dB, dC             : [batch, 4, 16, H*W]         activation dtype, each direction's scan order
+ *   dA_log             : [4, dim, 16]                float32
+ *   dD, ddelta_bias    : [4, dim]                    float32
+ *   dz                 : [batch, dim, H, W]          activation dtype; NULL exactly when z is NULL
+ * Every gradient is written (not accumulated), batch-summed where the tensor has no batch
+ * dimension, in float32 and rounded once.  The gradient reaching direction k is dout silu(z)
+ * (or dout) in that direction's scan order; each direction's adjoint is walked as in
+ * vmscan_bwd_bidir_v2 and its du is mapped back to pixels and summed into dx.  With a gate the
+ * library first recomputes the un-gated forward sum for dz.  Workspace:
+ * ss2d_cross_scan_bwd_workspace_bytes.  Outputs must not alias each other or any input.
+ * Validation and error codes as for ss2d_cross_scan_fwd (z and dz must both be given or both be
+ * NULL, else VMSCAN_ERR_NULL); launches are asynchronous on `stream`.
+ */
+size_t ss2d_cross_scan_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t H, int64_t W, int d_state,
+                                           vmscan_dtype dtype);
+vmscan_status ss2d_cross_scan_bwd(const void *x, const void *delta_raw, const float *A_log,
+                                  const void *B, const void *C, const float *D, const float *delta_bias,
+                                  const void *z, const void *dout, void *dx, void *ddelta_raw,
+                                  float *dA_log, void *dB, void *dC, float *dD, float *ddelta_bias,
+                                  void *dz, int64_t batch, int64_t dim, int64_t H, int64_t W,
+                                  int d_state, vmscan_dtype dtype, void *workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
 /* Workspace bytes for ss2d_cross_scan_fwd / _ex (chunk_len 0 = library choice); 0 if invalid. */
 size_t ss2d_cross_scan_workspace_bytes(int64_t batch, int64_t dim, int64_t H, int64_t W, int d_state,
                                        vmscan_dtype dtype);

@@ -54,6 +54,11 @@ def _load():
     lib.vmscan_bwd_bidir_v2.restype = ctypes.c_int
     lib.vmscan_bwd_bidir_v2.argtypes = ([_c_void_p] * 31 + [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _c_void_p,
                                                            ctypes.c_size_t, _c_void_p])
+    lib.ss2d_cross_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.ss2d_cross_scan_bwd_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int]
+    lib.ss2d_cross_scan_bwd.restype = ctypes.c_int
+    lib.ss2d_cross_scan_bwd.argtypes = ([_c_void_p] * 17 + [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int,
+                                                           _c_void_p, ctypes.c_size_t, _c_void_p])
     lib.ss2d_cross_scan_workspace_bytes.restype = ctypes.c_size_t
     lib.ss2d_cross_scan_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int]
     lib.ss2d_cross_scan_workspace_bytes_ex.restype = ctypes.c_size_t
@@ -289,6 +294,39 @@ def ss2d_cross_scan_fwd(x, delta_raw, A_log, B, C, D, delta_bias, z=None, out=No
         _ptr(x), _ptr(delta_raw), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(delta_bias), _ptr(z), _ptr(out),
         nb, nd, H, W, D_STATE, dt, _ptr(workspace), _nbytes(workspace), int(chunk_len), _stream(stream, dev)))
     return out
+
+
+def ss2d_cross_scan_bwd(x, delta_raw, A_log, B, C, D, delta_bias, z, dout, workspace=None, stream=None):
+    """Gradients of ``ss2d_cross_scan_fwd`` for ``dout`` (ss2d_cross_scan_bwd); returns a dict with
+    dx, ddelta_raw, dA_log, dB, dC, dD, ddelta_bias and dz (None when z is None)."""
+    if x.dim() != 4:
+        raise ValueError("x must be [batch, dim, H, W]")
+    nb, nd, H, W = x.shape
+    L = H * W
+    dev = x.device
+    adt = x.dtype
+    dt = _act_dtype(x)
+    _need(x, "x", (nb, nd, H, W), adt, dev)
+    _need(dout, "dout", (nb, nd, H, W), adt, dev)
+    _need(delta_raw, "delta_raw", (nb, 4, nd, L), adt, dev)
+    _need(B, "B", (nb, 4, D_STATE, L), adt, dev)
+    _need(C, "C", (nb, 4, D_STATE, L), adt, dev)
+    _need(A_log, "A_log", (4, nd, D_STATE), torch.float32, dev)
+    _need(D, "D", (4, nd), torch.float32, dev)
+    _need(delta_bias, "delta_bias", (4, nd), torch.float32, dev)
+    if z is not None:
+        _need(z, "z", (nb, nd, H, W), adt, dev)
+    g = dict(dx=torch.empty_like(x), ddelta_raw=torch.empty_like(delta_raw), dA_log=torch.empty_like(A_log),
+             dB=torch.empty_like(B), dC=torch.empty_like(C), dD=torch.empty_like(D),
+             ddelta_bias=torch.empty_like(delta_bias), dz=torch.empty_like(x) if z is not None else None)
+    lib = load()
+    wsb = lib.ss2d_cross_scan_bwd_workspace_bytes(nb, nd, H, W, D_STATE, dt)
+    workspace = _workspace(workspace, wsb, dev)
+    _check(lib.ss2d_cross_scan_bwd(
+        _ptr(x), _ptr(delta_raw), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(delta_bias), _ptr(z), _ptr(dout),
+        *[_ptr(g[k]) for k in ("dx", "ddelta_raw", "dA_log", "dB", "dC", "dD", "ddelta_bias", "dz")],
+        nb, nd, H, W, D_STATE, dt, _ptr(workspace), _nbytes(workspace), _stream(stream, dev)))
+    return g
 
 
 def fwd_bidir_chunk_len(batch, dim, seqlen):

@@ -209,9 +209,10 @@ struct ScanArgs {
   int dim, batch, K, nch, ngroups;
 };
 
-// kModeVimSum: Vim order, but the epilogue stores the un-gated fp32 sum y_f + y_b to wsy (the
-// backward pass needs it for dL/dz).
-enum { kModeVim = 0, kModeFirstPair = 1, kModeSecondPair = 2, kModeVimSum = 3 };
+// kModeVimSum: Vim order, but the epilogue stores the un-gated fp32 sum y_f + y_b to wsy;
+// kModeSecondPairSum: the SS2D row pair, storing the un-gated fp32 sum of all four directions to
+// out (as float).  The backward passes need these sums for dL/dz.
+enum { kModeVim = 0, kModeFirstPair = 1, kModeSecondPair = 2, kModeVimSum = 3, kModeSecondPairSum = 4 };
 
 // ---------------------------------------------------------------------------------------------
 // B/C transpose: for half q, bct[b][dir][q][s][0..7] = B_dir[b][8q + 0..7, si(s)] ln 2 and
@@ -360,7 +361,8 @@ __device__ __forceinline__ Lane lane_ctx(const ScanArgs& a) {
 
 template <int MODE, int DIR>
 struct Dir {
-  static constexpr bool kRev = (MODE == kModeFirstPair || MODE == kModeSecondPair) && DIR == 1;  // storage reversed
+  static constexpr bool kRev =
+      (MODE == kModeFirstPair || MODE == kModeSecondPair || MODE == kModeSecondPairSum) && DIR == 1;  // stored reversed
   static constexpr int kPosSgn = DIR == 0 ? 1 : -1;
   static constexpr int kSidxSgn = kRev ? -kPosSgn : kPosSgn;
   // global position of step i
@@ -847,6 +849,14 @@ __device__ __forceinline__ void epi_batch(const ScanArgs& a, const float* ybuf, 
       store8(ob + gi, v);
     } else if (MODE == kModeFirstPair || MODE == kModeVimSum) {
       store8(a.wsy + gi, v);
+    } else if (MODE == kModeSecondPairSum) {
+      float w[kWin];
+      Run8<float> wr;
+      wr.load(a.wsy + gi);
+      wr.template unpack<false>(w);
+#pragma unroll
+      for (int j = 0; j < kWin; ++j) v[j] += w[j];
+      store8(static_cast<float*>(a.out) + gi, v);
     } else {
       float w[kWin];
       Run8<float> wr;
@@ -922,6 +932,8 @@ __device__ __forceinline__ void pair_epilogue(const ScanArgs& a, const Lane& l, 
         st_act(ob, gi, 0.5f * v * silu_f(ld_act(zb, gi)));
       } else if (MODE == kModeFirstPair || MODE == kModeVimSum) {
         a.wsy[gi] = v;
+      } else if (MODE == kModeSecondPairSum) {
+        static_cast<float*>(a.out)[gi] = v + a.wsy[gi];
       } else {
         float w = v + a.wsy[gi];
         if (zb) w *= silu_f(ld_act(zb, gi));
@@ -1150,39 +1162,52 @@ struct BwdArgs {
   int nwin;
 };
 
-// g = dout silu(z) / 2 (float32) and dz = dout (y_f + y_b) / 2 silu'(z), silu'(z) = σ (1 + z (1 - σ)),
-// eight elements per thread (16-byte accesses; the flat arrays start 16-byte aligned).
+// g = scale dout silu(z) (float32) and dz = scale dout ysum silu'(z), silu'(z) = σ (1 + z (1 - σ)),
+// with scale 1/2 for the averaged Vim directions and 1 for SS2D; without a gate (z NULL, SS2D)
+// g = dout and there is no dz.  Eight elements per thread (16-byte accesses; the flat arrays start
+// 16-byte aligned).
 template <typename T>
 __global__ __launch_bounds__(256) void gate_bwd_kernel(const T* __restrict__ dout, const T* __restrict__ z,
                                                        const float* __restrict__ ysum, float* __restrict__ g,
-                                                       T* __restrict__ dz, int64_t n) {
+                                                       T* __restrict__ dz, int64_t n, float scale) {
   const int64_t i0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * kWin;
   if (i0 >= n) return;
   if (i0 + kWin <= n) {
     Run8<T> dr, zr;
     Run8<float> yr;
+    float go[kWin], zz[kWin], ys[kWin], gv[kWin], dv[kWin];
     dr.load(dout + i0);
+    dr.template unpack<false>(go);
+    if (!z) {
+#pragma unroll
+      for (int j = 0; j < kWin; ++j) gv[j] = scale * go[j];
+      store8(g + i0, gv);
+      return;
+    }
     zr.load(z + i0);
     yr.load(ysum + i0);
-    float go[kWin], zz[kWin], ys[kWin], gv[kWin], dv[kWin];
-    dr.template unpack<false>(go);
     zr.template unpack<false>(zz);
     yr.template unpack<false>(ys);
 #pragma unroll
     for (int j = 0; j < kWin; ++j) {
       const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-zz[j] * kLog2e));
-      gv[j] = 0.5f * go[j] * zz[j] * sg;
-      dv[j] = 0.5f * go[j] * ys[j] * sg * (1.0f + zz[j] * (1.0f - sg));
+      gv[j] = scale * go[j] * zz[j] * sg;
+      dv[j] = scale * go[j] * ys[j] * sg * (1.0f + zz[j] * (1.0f - sg));
     }
     store8(g + i0, gv);
     store8(dz + i0, dv);
     return;
   }
   for (int64_t i = i0; i < n; ++i) {
-    const float zz = ld_act(z, i), go = ld_act(dout, i);
+    const float go = ld_act(dout, i);
+    if (!z) {
+      g[i] = scale * go;
+      continue;
+    }
+    const float zz = ld_act(z, i);
     const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-zz * kLog2e));
-    g[i] = 0.5f * go * zz * sg;
-    st_act(dz, i, 0.5f * go * ysum[i] * sg * (1.0f + zz * (1.0f - sg)));
+    g[i] = scale * go * zz * sg;
+    st_act(dz, i, scale * go * ysum[i] * sg * (1.0f + zz * (1.0f - sg)));
   }
 }
 
@@ -1466,7 +1491,7 @@ __global__ __launch_bounds__(256) void bwd_combine_kernel(const float* __restric
 // dB, dC, dB_b, dC_b: the channel-group partial sums added up (dB scaled by ln 2), rounded once.
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_bc_kernel(const float* __restrict__ dbc, T* dB, T* dC, T* dB_b, T* dC_b,
-                                                     int batch, int ngroups, int64_t L) {
+                                                     int batch, int ngroups, int64_t L, int64_t out_bstride) {
   const int64_t per = static_cast<int64_t>(batch) * 2 * kN * L;  // one (dir, group) block
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= 2 * per) return;
@@ -1477,7 +1502,7 @@ __global__ __launch_bounds__(256) void bwd_bc_kernel(const float* __restrict__ d
   const int64_t bb = r / (2 * kN * L);
   const int64_t rest = r - bb * 2 * kN * L;
   const int ty = static_cast<int>(rest / (kN * L));
-  const int64_t o = bb * kN * L + (rest - ty * kN * L);  // (b, n, pos) in [batch][16][L]
+  const int64_t o = bb * out_bstride + (rest - ty * kN * L);  // (b, n, index); [16][L] per batch
   T* dst = ty == 0 ? (dir == 0 ? dB : dB_b) : (dir == 0 ? dC : dC_b);
   st_act(dst, o, ty == 0 ? s * kLn2 : s);
 }
@@ -1529,6 +1554,23 @@ __global__ __launch_bounds__(256) void bwd_param_kernel(const float* __restrict_
   if (lane == 0) (dir == 0 ? dbias : dbias_b)[d] = s;
 }
 
+// out[b][r] (batch stride out_bstride) = the sum of up to five float32 planes [batch][n_b] at
+// (b, r), in float32, rounded once to O.  Used for the SS2D gradients: dx from the row pair's
+// four partial planes plus the transposed column-pair plane, dΔ_raw per direction from its two
+// state halves.
+template <typename O>
+__global__ __launch_bounds__(256) void sum_planes_kernel(const float* p0, const float* p1, const float* p2,
+                                                         const float* p3, const float* p4, O* out, int64_t n_b,
+                                                         int batch, int64_t out_bstride) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n_b * batch) return;
+  float s = p0[i] + p1[i];
+  if (p2) s += p2[i] + p3[i];
+  if (p4) s += p4[i];
+  const int64_t b = i / n_b;
+  st_act(out, b * out_bstride + (i - b * n_b), s);
+}
+
 struct BwdLayout {
   size_t bct, agg, ysum, g, ck, gu, gx, dbc, dpar, total;
 };
@@ -1567,7 +1609,7 @@ vmscan_status run_bwd(const ScanArgs& fwd, const BwdLayout& lay, unsigned char* 
   vmscan_status st = run_pair<T, kModeVimSum>(a, stream, kStageAll);
   if (st != VMSCAN_OK) return st;
   hipLaunchKernelGGL(gate_bwd_kernel<T>, dim3(static_cast<unsigned>(ceil_div(n, 256 * kWin))), dim3(256), 0, stream,
-                     static_cast<const T*>(dout), static_cast<const T*>(z), ysum, g, static_cast<T*>(dz), n);
+                     static_cast<const T*>(dout), static_cast<const T*>(z), ysum, g, static_cast<T*>(dz), n, 0.5f);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return launch_failed(e);
   BwdArgs ba{};
@@ -1593,9 +1635,162 @@ vmscan_status run_bwd(const ScanArgs& fwd, const BwdLayout& lay, unsigned char* 
                      static_cast<T*>(dx_b), n);
   hipLaunchKernelGGL(bwd_bc_kernel<T>, dim3(static_cast<unsigned>(ceil_div(nbc, 256))), dim3(256), 0, stream, ba.dbc,
                      static_cast<T*>(dB), static_cast<T*>(dC), static_cast<T*>(dB_b), static_cast<T*>(dC_b), fwd.batch,
-                     fwd.ngroups, fwd.L);
+                     fwd.ngroups, fwd.L, kN * fwd.L);
   hipLaunchKernelGGL(bwd_param_kernel, dim3(static_cast<unsigned>(ceil_div(2 * fwd.dim * kN + 4 * fwd.dim, 4))), dim3(256), 0,
                      stream, ba.dpar, A_log, A_b_log, dA_log, dA_b_log, dD, dD_b, dbias, dbias_b, fwd.batch, fwd.dim);
+  e = hipGetLastError();
+  return e == hipSuccess ? VMSCAN_OK : launch_failed(e);
+}
+
+
+// SS2D backward workspace: the forward's (images, transposed x, B/C copy, carries), then the
+// un-gated sum, the row- and column-order g, the checkpoints and the partial gradients.
+struct Ss2dBwdLayout {
+  Ss2dLayout f;
+  size_t ysum, g, gcol, ck, gu, gx, dbc, dpar, total;
+};
+
+Ss2dBwdLayout ss2d_bwd_layout(int64_t batch, int64_t dim, int64_t L, int64_t Kf, size_t esz) {
+  Ss2dBwdLayout w{};
+  w.f = ss2d_layout(batch, dim, L, Kf, esz);
+  const size_t plane = round256(static_cast<size_t>(batch) * dim * L * sizeof(float));
+  const int64_t nwin = ceil_div(L, kWin);
+  w.ysum = round256(w.f.total);
+  w.g = w.ysum + plane;
+  w.gcol = w.g + plane;
+  w.ck = w.gcol + plane;
+  w.gu = w.ck + round256(static_cast<size_t>(batch) * 2 * 2 * nwin * dim * kH * sizeof(float));
+  w.gx = w.gu + 4 * plane;
+  w.dbc = w.gx + 4 * plane;
+  w.dpar = w.dbc + round256(static_cast<size_t>(2) * groups(dim) * batch * 2 * kN * L * sizeof(float));
+  w.total = w.dpar + round256(static_cast<size_t>(batch) * 2 * 2 * dim * kParStride * sizeof(float));
+  return w;
+}
+
+// The gradients of one SS2D pair (directions k0 and k1 = its reverse) from g in the pair's
+// position order: checkpoints, adjoint walk, then dΔ_raw, dB, dC and the parameter sums written
+// for both directions.  The pair's du (four float32 planes in position order) stays in ba.gu.
+template <typename T>
+vmscan_status ss2d_pair_bwd(BwdArgs& ba, int k0, int k1, void* ddelta_raw, void* dB, void* dC, float* dA_log,
+                            const float* A_log, float* dD, float* ddelta_bias, hipStream_t stream) {
+  const ScanArgs& a = ba.s;
+  const int64_t DL = static_cast<int64_t>(a.dim) * a.L;
+  vmscan_status st = run_pair<T, kModeSecondPair>(a, stream, kStagePrepare);  // B/C copy (one chunk)
+  if (st != VMSCAN_OK) return st;
+  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.batch) * a.ngroups));
+  hipLaunchKernelGGL((bwd_ckpt_kernel<T, kModeSecondPair>), grid, dim3(kThreads), 0, stream, ba);
+  hipLaunchKernelGGL((bwd_scan_kernel<T, kModeSecondPair>), grid, dim3(kThreads), 0, stream, ba);
+  const int64_t n = static_cast<int64_t>(a.batch) * DL;
+  const int64_t plane = n;
+  T* ddr = static_cast<T*>(ddelta_raw);
+  const dim3 pg(static_cast<unsigned>(ceil_div(n, 256)));
+  hipLaunchKernelGGL(sum_planes_kernel<T>, pg, dim3(256), 0, stream, ba.gx, ba.gx + plane, nullptr, nullptr, nullptr,
+                     ddr + k0 * DL, DL, a.batch, 4 * DL);
+  hipLaunchKernelGGL(sum_planes_kernel<T>, pg, dim3(256), 0, stream, ba.gx + 2 * plane, ba.gx + 3 * plane, nullptr,
+                     nullptr, nullptr, ddr + k1 * DL, DL, a.batch, 4 * DL);
+  const int64_t NL = static_cast<int64_t>(kN) * a.L;
+  const int64_t nbc = static_cast<int64_t>(2) * a.batch * 2 * NL;
+  hipLaunchKernelGGL(bwd_bc_kernel<T>, dim3(static_cast<unsigned>(ceil_div(nbc, 256))), dim3(256), 0, stream, ba.dbc,
+                     static_cast<T*>(dB) + k0 * NL, static_cast<T*>(dC) + k0 * NL, static_cast<T*>(dB) + k1 * NL,
+                     static_cast<T*>(dC) + k1 * NL, a.batch, a.ngroups, a.L, 4 * NL);
+  const int64_t dN = static_cast<int64_t>(a.dim) * kN;
+  hipLaunchKernelGGL(bwd_param_kernel, dim3(static_cast<unsigned>(ceil_div(2 * a.dim * kN + 4 * a.dim, 4))), dim3(256),
+                     0, stream, ba.dpar, A_log + k0 * dN, A_log + k1 * dN, dA_log + k0 * dN, dA_log + k1 * dN,
+                     dD + k0 * a.dim, dD + k1 * a.dim, ddelta_bias + k0 * a.dim, ddelta_bias + k1 * a.dim, a.batch,
+                     a.dim);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? VMSCAN_OK : launch_failed(e);
+}
+
+template <typename T>
+vmscan_status run_ss2d_bwd(const void* x, const void* delta_raw, const float* A_log, const void* B, const void* C,
+                           const float* D, const float* delta_bias, const void* z, const void* dout, void* dx,
+                           void* ddelta_raw, float* dA_log, void* dB, void* dC, float* dD, float* ddelta_bias,
+                           void* dz, int64_t batch, int64_t dim, int64_t H, int64_t W, unsigned char* wsp,
+                           const Ss2dBwdLayout& lay, int64_t Kf, hipStream_t stream) {
+  const int64_t L = H * W;
+  const size_t esz = sizeof(T);
+  const int64_t nimg = batch * dim, n = nimg * L;
+  if (ceil_div(n, 256) >= (int64_t{1} << 31)) return VMSCAN_ERR_SHAPE;
+  auto off = [&](const void* p, int64_t elems) {
+    return static_cast<const void*>(static_cast<const unsigned char*>(p) + elems * static_cast<int64_t>(esz));
+  };
+  auto dir_args = [&](const void* u, int k, int rev) {
+    return DirArgs{u, off(delta_raw, k * dim * L), 4 * dim * L, off(B, k * kN * L), off(C, k * kN * L), 4 * kN * L,
+                   A_log + k * dim * kN, D + k * dim, delta_bias + k * dim, rev};
+  };
+  float* ysum = reinterpret_cast<float*>(wsp + lay.ysum);
+  float* g = reinterpret_cast<float*>(wsp + lay.g);
+  float* gcol = reinterpret_cast<float*>(wsp + lay.gcol);
+  ScanArgs a{};
+  a.u_bs = dim * L;
+  a.z = nullptr;
+  a.bct = reinterpret_cast<float*>(wsp + lay.f.bct);
+  a.agg = reinterpret_cast<float*>(wsp + lay.f.agg);
+  a.L = L;
+  a.dim = static_cast<int>(dim);
+  a.batch = static_cast<int>(batch);
+  a.K = static_cast<int>(Kf);
+  a.nch = static_cast<int>(ceil_div(L, Kf));
+  a.ngroups = static_cast<int>(groups(dim));
+  const void* xt = wsp + lay.f.xt;
+  vmscan_status st = launch_transpose(x, wsp + lay.f.xt, nimg, static_cast<int>(H), static_cast<int>(W), esz, stream);
+  if (st != VMSCAN_OK) return st;
+  if (z) {
+    // the forward's un-gated four-direction sum, as float32 (same pairs as ss2d_cross_scan_fwd)
+    a.wsy = reinterpret_cast<float*>(wsp + lay.f.col_img);
+    a.d0 = dir_args(xt, 1, 0);
+    a.d1 = dir_args(xt, 3, 1);
+    st = run_pair<T, kModeFirstPair>(a, stream, kStageAll);
+    if (st != VMSCAN_OK) return st;
+    st = launch_transpose(wsp + lay.f.col_img, wsp + lay.f.row_img, nimg, static_cast<int>(W), static_cast<int>(H), 4,
+                          stream);
+    if (st != VMSCAN_OK) return st;
+    a.wsy = reinterpret_cast<float*>(wsp + lay.f.row_img);
+    a.out = ysum;
+    a.d0 = dir_args(x, 0, 0);
+    a.d1 = dir_args(x, 2, 1);
+    st = run_pair<T, kModeSecondPairSum>(a, stream, kStageAll);
+    if (st != VMSCAN_OK) return st;
+  }
+  hipLaunchKernelGGL(gate_bwd_kernel<T>, dim3(static_cast<unsigned>(ceil_div(n, 256 * kWin))), dim3(256), 0, stream,
+                     static_cast<const T*>(dout), static_cast<const T*>(z), ysum, g, static_cast<T*>(dz), n, 1.0f);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return launch_failed(e);
+  // g in column-major order for the column pair
+  st = launch_transpose(g, gcol, nimg, static_cast<int>(H), static_cast<int>(W), 4, stream);
+  if (st != VMSCAN_OK) return st;
+  BwdArgs ba{};
+  ba.s = a;
+  ba.s.K = static_cast<int>(L);  // one chunk: each wave walks the whole sequence
+  ba.s.nch = 1;
+  ba.ck = reinterpret_cast<float*>(wsp + lay.ck);
+  ba.gu = reinterpret_cast<float*>(wsp + lay.gu);
+  ba.gx = reinterpret_cast<float*>(wsp + lay.gx);
+  ba.dbc = reinterpret_cast<float*>(wsp + lay.dbc);
+  ba.dpar = reinterpret_cast<float*>(wsp + lay.dpar);
+  ba.nwin = static_cast<int>(ceil_div(L, kWin));
+  // column pair: directions 1 and 3 over x^T with g in column order
+  ba.g = gcol;
+  ba.s.d0 = dir_args(xt, 1, 0);
+  ba.s.d1 = dir_args(xt, 3, 1);
+  st = ss2d_pair_bwd<T>(ba, 1, 3, ddelta_raw, dB, dC, dA_log, A_log, dD, ddelta_bias, stream);
+  if (st != VMSCAN_OK) return st;
+  // its du back to row-major pixels: sum the four partial planes (column order), transpose
+  float* col = reinterpret_cast<float*>(wsp + lay.f.col_img);
+  float* rowp = reinterpret_cast<float*>(wsp + lay.f.row_img);
+  hipLaunchKernelGGL(sum_planes_kernel<float>, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, stream,
+                     ba.gu, ba.gu + n, ba.gu + 2 * n, ba.gu + 3 * n, nullptr, col, n, 1, n);
+  st = launch_transpose(col, rowp, nimg, static_cast<int>(W), static_cast<int>(H), 4, stream);
+  if (st != VMSCAN_OK) return st;
+  // row pair: directions 0 and 2 over x with g in row order
+  ba.g = g;
+  ba.s.d0 = dir_args(x, 0, 0);
+  ba.s.d1 = dir_args(x, 2, 1);
+  st = ss2d_pair_bwd<T>(ba, 0, 2, ddelta_raw, dB, dC, dA_log, A_log, dD, ddelta_bias, stream);
+  if (st != VMSCAN_OK) return st;
+  hipLaunchKernelGGL(sum_planes_kernel<T>, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, stream, ba.gu,
+                     ba.gu + n, ba.gu + 2 * n, ba.gu + 3 * n, rowp, static_cast<T*>(dx), n, 1, n);
   e = hipGetLastError();
   return e == hipSuccess ? VMSCAN_OK : launch_failed(e);
 }
@@ -1824,6 +2019,45 @@ vmscan_status ss2d_cross_scan_fwd_ex(const void* x, const void* delta_raw, const
   a.d0 = dir_args(x, 0, 0);
   a.d1 = dir_args(x, 2, 1);
   return run_pair_dtype<kModeSecondPair>(a, dtype, stream);
+}
+
+size_t ss2d_cross_scan_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t H, int64_t W, int d_state,
+                                           vmscan_dtype dtype) {
+  if (H < 1 || W < 1 || H >= (int64_t{1} << 31) || W >= (int64_t{1} << 31)) return 0;
+  const int64_t L = H * W;
+  if (!shape_ok(batch, dim, L) || d_state != kN || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16)) return 0;
+  return ss2d_bwd_layout(batch, dim, L, plan_chunk(batch * groups(dim), L, 0), dtype == VMSCAN_F32 ? 4 : 2).total;
+}
+
+vmscan_status ss2d_cross_scan_bwd(const void* x, const void* delta_raw, const float* A_log, const void* B,
+                                  const void* C, const float* D, const float* delta_bias, const void* z,
+                                  const void* dout, void* dx, void* ddelta_raw, float* dA_log, void* dB, void* dC,
+                                  float* dD, float* ddelta_bias, void* dz, int64_t batch, int64_t dim, int64_t H,
+                                  int64_t W, int d_state, vmscan_dtype dtype, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  const void* ptrs[] = {x, delta_raw, A_log, B, C, D, delta_bias, dout, dx, ddelta_raw, dA_log, dB, dC, dD,
+                        ddelta_bias};
+  for (const void* p : ptrs)
+    if (!p) return VMSCAN_ERR_NULL;
+  if ((z == nullptr) != (dz == nullptr)) return VMSCAN_ERR_NULL;  // the gate and its gradient come together
+  if (H < 1 || W < 1 || H >= (int64_t{1} << 31) || W >= (int64_t{1} << 31)) return VMSCAN_ERR_SHAPE;
+  const int64_t L = H * W;
+  if (!shape_ok(batch, dim, L)) return VMSCAN_ERR_SHAPE;
+  if (d_state != kN || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16)) return VMSCAN_ERR_UNSUPPORTED;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return VMSCAN_ERR_ALIGN;
+  if (z && (!aligned16(z) || !aligned16(dz))) return VMSCAN_ERR_ALIGN;
+  const int64_t Kf = plan_chunk(batch * groups(dim), L, 0);
+  const size_t esz = dtype == VMSCAN_F32 ? 4 : 2;
+  const Ss2dBwdLayout lay = ss2d_bwd_layout(batch, dim, L, Kf, esz);
+  const vmscan_status ws = check_workspace(workspace, workspace_bytes, lay.total);
+  if (ws != VMSCAN_OK) return ws;
+  unsigned char* wsp = static_cast<unsigned char*>(workspace);
+  return dtype == VMSCAN_F32
+             ? run_ss2d_bwd<float>(x, delta_raw, A_log, B, C, D, delta_bias, z, dout, dx, ddelta_raw, dA_log, dB, dC,
+                                   dD, ddelta_bias, dz, batch, dim, H, W, wsp, lay, Kf, stream)
+             : run_ss2d_bwd<uint16_t>(x, delta_raw, A_log, B, C, D, delta_bias, z, dout, dx, ddelta_raw, dA_log, dB,
+                                      dC, dD, ddelta_bias, dz, batch, dim, H, W, wsp, lay, Kf, stream);
 }
 
 vmscan_status ss2d_cross_scan_fwd(const void* x, const void* delta_raw, const float* A_log, const void* B,
