@@ -363,7 +363,7 @@ def bench_bwd(cfg_id, steps, warmup, torch, V, v2=False):
     import synth
     cfg = synth.CONFIGS[cfg_id]
     if cfg["kind"] != "vim":
-        return None
+        return bench_ss2d_bwd(cfg_id, steps, warmup, torch, V)
     dev = torch.device("cuda", 0)
     dt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
     p = synth.make_vim_v2_inputs(cfg_id)
@@ -410,6 +410,56 @@ def bench_bwd(cfg_id, steps, warmup, torch, V, v2=False):
                      "unit": "Gupd/s", "frac": round(alu / ALU_PEAK_BWD_UPD_S, 4), "traffic": None,
                      "kernel": "all kernels of vmscan_bwd_bidir_v2 (forward with saved sum, gate, adjoint scan, "
                                "reductions)", "kernel_avg_us": round(ms * 1000, 2), "updates_per_launch": upd},
+    }
+
+
+def bench_ss2d_bwd(cfg_id, steps, warmup, torch, V):
+    """Backward pass of the SS2D cross-scan (ss2d_cross_scan_bwd, every gradient, no gate as in
+    the 56x56 workload); the timed region is the whole call."""
+    import numpy as np
+    import synth
+    cfg = synth.CONFIGS[cfg_id]
+    dev = torch.device("cuda", 0)
+    dt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
+    p = synth.make_ss2d_inputs(cfg_id)
+    act = {k: torch.from_numpy(np.ascontiguousarray(p[k])).to(dev).to(dt) for k in ("x", "delta_raw", "B", "C")}
+    par = {k: torch.from_numpy(np.ascontiguousarray(p[k])).to(dev) for k in ("A_log", "D", "delta_bias")}
+    g = torch.Generator(device=dev)
+    g.manual_seed(43_000 + cfg_id)
+    dout = torch.randn(act["x"].shape, generator=g, device=dev, dtype=torch.float32).to(dt)
+    nb, nd, H, W = act["x"].shape
+    wsb = V.lib.ss2d_cross_scan_bwd_workspace_bytes(nb, nd, H, W, 16, 1 if cfg["dtype"] == "bf16" else 0)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+
+    def call():
+        return V.ss2d_cross_scan_bwd(act["x"], act["delta_raw"], par["A_log"], act["B"], act["C"], par["D"],
+                                     par["delta_bias"], None, dout, workspace=ws)
+
+    for _ in range(max(1, warmup)):
+        call()
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    upd = state_updates(cfg)
+    alu = upd / (ms * 1e-3)
+    toks = nb * nd * H * W
+    return {
+        "metric": "scan tokens·channels/s (bwd: all gradients of the SS2D cross-scan), 1 GPU",
+        "value": toks / (ms * 1e-3), "unit": "tokens·channels/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg["name"] + "_backward", "batch": nb, "dim": nd, "H": H, "W": W, "d_state": 16,
+                   "io_dtype": cfg["dtype"]},
+        "roofline": {"bound": "alu", "achieved": round(alu / 1e9, 1), "peak": round(ALU_PEAK_BWD_UPD_S / 1e9, 1),
+                     "unit": "Gupd/s", "frac": round(alu / ALU_PEAK_BWD_UPD_S, 4), "traffic": None,
+                     "kernel": "all kernels of ss2d_cross_scan_bwd (transposes, two pairs of adjoint scans, reductions)",
+                     "kernel_avg_us": round(ms * 1000, 2), "updates_per_launch": upd},
     }
 
 
