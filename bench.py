@@ -1,6 +1,7 @@
 """Benchmark of the fused bidirectional selective scan (and SS2D cross-scan) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N | --all] [--no-cpu] [--v2] [--bwd]
+                    [--d-state 32]
 
 A step is one call of the hot path over one batch of seeded synthetic input already resident in
 HBM.  The default workload is the Vim-Ti layer scan (batch 128, d_inner 384, L 197, d_state 16,
@@ -8,7 +9,8 @@ bf16 activations, fp32 state), the configuration the metric is quoted on.  R inp
 are rotated so that at least 1 GiB is touched between reuses and the 256 MB Infinity Cache cannot
 serve the inputs.  Rank 0 prints one JSON line per workload.  ``--v2`` runs the Vim workloads
 through the entry point whose backward branch has its own u_b, Δ_raw_b and bias_b; ``--bwd``
-times the backward pass (all gradients) of the Vim workloads instead of the forward.
+times the backward pass (all gradients) of the Vim workloads instead of the forward; ``--d-state
+32`` runs the forward workloads with 32 states instead of 16.
 """
 import argparse
 import hashlib
@@ -217,7 +219,8 @@ def make_sets(cfg_id, cfg, nsets, torch, v2=False):
     g.manual_seed(41_000 + cfg_id)
     sets = []
     if cfg["kind"] == "vim":
-        p = synth.make_vim_v2_inputs(cfg_id) if v2 else synth.make_vim_inputs(cfg_id)
+        mk = synth.make_vim_v2_inputs if v2 else synth.make_vim_inputs
+        p = mk(cfg_id, d_state=cfg["d_state"])
         act_names = VIM_ACT + (V2_ACT if v2 else ())
         par = {k: torch.from_numpy(np.ascontiguousarray(p[k])).to(dev) for k in VIM_PAR + (V2_PAR if v2 else ())}
         base = {k: torch.from_numpy(np.ascontiguousarray(p[k])).to(dev).to(dt) for k in act_names}
@@ -229,7 +232,7 @@ def make_sets(cfg_id, cfg, nsets, torch, v2=False):
             act["out"] = torch.empty_like(act["u"])
             sets.append((act, par))
     else:
-        p = synth.make_ss2d_inputs(cfg_id)
+        p = synth.make_ss2d_inputs(cfg_id, d_state=cfg["d_state"])
         act_names = ("x", "delta_raw", "B", "C")
         par = {k: torch.from_numpy(np.ascontiguousarray(p[k])).to(dev) for k in ("A_log", "D", "delta_bias")}
         base = {k: torch.from_numpy(np.ascontiguousarray(p[k])).to(dev).to(dt) for k in act_names}
@@ -241,9 +244,12 @@ def make_sets(cfg_id, cfg, nsets, torch, v2=False):
     return sets
 
 
-def bench_config(cfg_id, steps, warmup, with_cpu, torch, V, v2=False):
+def bench_config(cfg_id, steps, warmup, with_cpu, torch, V, v2=False, d_state=None):
     import synth
-    cfg = synth.CONFIGS[cfg_id]
+    cfg = dict(synth.CONFIGS[cfg_id])
+    if d_state and d_state != cfg["d_state"]:
+        cfg["d_state"] = d_state
+        cfg["name"] = cfg["name"] + f"_n{d_state}"
     v2 = v2 and cfg["kind"] == "vim"
     nbytes, toks = algorithmic_bytes(cfg, v2)
     layers = cfg.get("layers", 1)
@@ -256,7 +262,8 @@ def bench_config(cfg_id, steps, warmup, with_cpu, torch, V, v2=False):
         dt = torch.bfloat16
         dev = torch.device("cuda", 0)
         for layer in range(layers):
-            p = synth.make_vim_v2_inputs(cfg_id, layer=layer) if v2 else synth.make_vim_inputs(cfg_id, layer=layer)
+            mk = synth.make_vim_v2_inputs if v2 else synth.make_vim_inputs
+            p = mk(cfg_id, layer=layer, d_state=cfg["d_state"])
             act = {k: torch.from_numpy(np.ascontiguousarray(p[k])).to(dev).to(dt) for k in VIM_ACT + (V2_ACT if v2 else ())}
             act["out"] = torch.empty_like(act["u"])
             par = {k: torch.from_numpy(np.ascontiguousarray(p[k])).to(dev) for k in VIM_PAR + (V2_PAR if v2 else ())}
@@ -266,9 +273,11 @@ def bench_config(cfg_id, steps, warmup, with_cpu, torch, V, v2=False):
     dev = torch.device("cuda", 0)
     ws = None
     if cfg["kind"] == "vim":
-        wsb = V.lib.vmscan_fwd_bidir_workspace_bytes(cfg["batch"], cfg["dim"], cfg["seqlen"], 16, 1 if cfg["dtype"] == "bf16" else 0)
+        wsb = V.lib.vmscan_fwd_bidir_workspace_bytes(cfg["batch"], cfg["dim"], cfg["seqlen"], cfg["d_state"],
+                                                     1 if cfg["dtype"] == "bf16" else 0)
     else:
-        wsb = V.lib.ss2d_cross_scan_workspace_bytes(cfg["batch"], cfg["dim"], cfg["H"], cfg["W"], 16, 1 if cfg["dtype"] == "bf16" else 0)
+        wsb = V.lib.ss2d_cross_scan_workspace_bytes(cfg["batch"], cfg["dim"], cfg["H"], cfg["W"], cfg["d_state"],
+                                                    1 if cfg["dtype"] == "bf16" else 0)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
 
     def call(i, stage=3):
@@ -317,7 +326,7 @@ def bench_config(cfg_id, steps, warmup, with_cpu, torch, V, v2=False):
     upd = state_updates(cfg)
     alu = upd / (kern_ms * 1e-3)
     dtype = "f32"  # arithmetic and state are fp32; activations are stored as cfg["dtype"]
-    is_default = cfg_id == 1
+    is_default = cfg_id == 1 and cfg["d_state"] == synth.CONFIGS[cfg_id]["d_state"]
     roof = {"bound": "alu", "achieved": round(alu / 1e9, 1), "peak": round(ALU_PEAK_UPD_S / 1e9, 1), "unit": "Gupd/s",
             "frac": round(alu / ALU_PEAK_UPD_S, 4), "traffic": traffic_record(cfg["name"]),
             "kernel": (("scan_pair_kernel<bf16, vim> (scan stage of vmscan_fwd_bidir" + ("_v2)" if v2 else ")")) if split else
@@ -473,6 +482,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--v2", action="store_true", help="Vim workloads with a separate backward branch (u_b, delta_raw_b, bias_b)")
     ap.add_argument("--bwd", action="store_true", help="time the backward pass of the Vim workloads")
+    ap.add_argument("--d-state", type=int, default=None, choices=(16, 32),
+                    help="state size of the forward workloads (default: the workload's own, 16)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (counter calibration for FETCH_SIZE/WRITE_SIZE)")
     ap.add_argument("--summarize-kernels", nargs=3, metavar=("RESULT_DIR", "COMMAND", "OUT_TXT"),
@@ -515,6 +526,9 @@ def main():
         print(json.dumps({"calibration": "copy", "bytes_read_per_dispatch": n * 4, "bytes_written_per_dispatch": n * 4,
                           "dispatches": max(1, args.steps)}), flush=True)
         return
+    if args.bwd and args.d_state not in (None, 16):
+        print("bench.py: the backward pass takes d_state 16 only", file=sys.stderr)
+        sys.exit(2)
     import selective_state_space_41_amd as V
     cfgs = [0, 1, 2, 3, 4] if args.all else [args.config]
     for c in cfgs:
@@ -523,7 +537,7 @@ def main():
             if rec is None:
                 continue
         else:
-            rec = bench_config(c, args.steps, args.warmup, not args.no_cpu, torch, V, args.v2)
+            rec = bench_config(c, args.steps, args.warmup, not args.no_cpu, torch, V, args.v2, args.d_state)
         print(json.dumps(rec), flush=True)
 
 

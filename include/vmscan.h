@@ -30,7 +30,10 @@
  *   - Activation dtype: VMSCAN_F32 (float) or VMSCAN_BF16 (bfloat16 bit patterns, 2 bytes) for
  *     u/x, delta_raw, z, B, C and out.  A_log, D and delta_bias are always float32.  The state
  *     and all arithmetic are float32; bf16 outputs are rounded to nearest even once, at the store.
- *   - d_state must be 16 (else VMSCAN_ERR_UNSUPPORTED).
+ *   - d_state: the forward entry points take 16 or 32, the backward entry points 16 only (else
+ *     VMSCAN_ERR_UNSUPPORTED; the workspace and chunk-length queries return 0).  The pages use
+ *     16 and suggest a larger state for high-resolution inputs ([P3] §4.1; [P4] §4.2 gives the
+ *     16-32 range).  The workspace size depends on d_state.
  *   - Errors: arguments are validated synchronously and a status is returned before anything is
  *     enqueued; on success the kernels are enqueued on `stream` (NULL = the default stream) and the
  *     call returns without waiting.  A failed launch returns VMSCAN_ERR_HIP and the hipError_t
@@ -186,7 +189,7 @@ vmscan_status vmscan_fwd_bidir_v2_stage(const void *u, const void *delta_raw, co
  * sequence with the adjoint recurrence.  Workspace: vmscan_bwd_bidir_v2_workspace_bytes.
  * Gradient outputs must not alias each other or any input.  Validation and error codes as for
  * vmscan_fwd_bidir_v2 (all pointers but the three optional ones are required, all 16-byte
- * aligned); launches are asynchronous on `stream`.
+ * aligned); launches are asynchronous on `stream`.  d_state must be 16.
  */
 size_t vmscan_bwd_bidir_v2_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen, int d_state,
                                            vmscan_dtype dtype);

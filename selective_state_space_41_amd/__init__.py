@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(_PKG, "libvmscan.so")
 
 VMSCAN_F32 = 0
 VMSCAN_BF16 = 1
-D_STATE = 16
+D_STATE = 16          # the usual state size; the forward entry points also take 32
+D_STATES_FWD = (16, 32)
 
 _c_void_p = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -148,27 +149,36 @@ def _nbytes(t):
     return t.numel() if t is not None else 0
 
 
+def _d_state(A_log):
+    """d_state from the last dimension of A_log (the library rejects sizes it does not take)."""
+    if A_log.dim() < 1:
+        raise ValueError("A_log must have a state dimension")
+    return int(A_log.shape[-1])
+
+
 def vmscan_fwd_bidir(u, delta_raw, z, A_log, A_b_log, B, C, B_b, C_b, D, D_b, delta_bias,
                      out=None, chunk_len=0, workspace=None, stream=None, stage=3):
     """Bidirectional selective scan with the silu(z) gate; returns ``out`` [batch, dim, L].
 
-    u, delta_raw, z: [batch, dim, L]; A_log, A_b_log: [dim, 16] float32; B, C, B_b, C_b:
-    [batch, 16, L] (original token order); D, D_b, delta_bias: [dim] float32.  Activations are
+    u, delta_raw, z: [batch, dim, L]; A_log, A_b_log: [dim, N] float32 (d_state N = 16 or 32,
+    taken from A_log); B, C, B_b, C_b: [batch, N, L] (original token order); D, D_b, delta_bias:
+    [dim] float32.  Activations are
     float32 or bfloat16 (all the same).  ``chunk_len`` 0 lets the library choose.  ``stage``
     1 / 2 runs only the preparation (B/C copy, chunk carries) / the fused scan
     (vmscan_fwd_bidir_stage); 3 runs both."""
     if u.dim() != 3:
         raise ValueError("u must be [batch, dim, L]")
     nb, nd, L = u.shape
+    ns = _d_state(A_log)
     dev = u.device
     adt = u.dtype
     dt = _act_dtype(u)
     for name, t in (("u", u), ("delta_raw", delta_raw), ("z", z)):
         _need(t, name, (nb, nd, L), adt, dev)
     for name, t in (("B", B), ("C", C), ("B_b", B_b), ("C_b", C_b)):
-        _need(t, name, (nb, D_STATE, L), adt, dev)
+        _need(t, name, (nb, ns, L), adt, dev)
     for name, t in (("A_log", A_log), ("A_b_log", A_b_log)):
-        _need(t, name, (nd, D_STATE), torch.float32, dev)
+        _need(t, name, (nd, ns), torch.float32, dev)
     for name, t in (("D", D), ("D_b", D_b), ("delta_bias", delta_bias)):
         _need(t, name, (nd,), torch.float32, dev)
     if out is None:
@@ -176,11 +186,11 @@ def vmscan_fwd_bidir(u, delta_raw, z, A_log, A_b_log, B, C, B_b, C_b, D, D_b, de
     else:
         _need(out, "out", (nb, nd, L), adt, dev)
     lib = load()
-    wsb = lib.vmscan_fwd_bidir_workspace_bytes_ex(nb, nd, L, D_STATE, dt, int(chunk_len))
+    wsb = lib.vmscan_fwd_bidir_workspace_bytes_ex(nb, nd, L, ns, dt, int(chunk_len))
     workspace = _workspace(workspace, wsb, dev)
     _check(lib.vmscan_fwd_bidir_stage(
         _ptr(u), _ptr(delta_raw), _ptr(z), _ptr(A_log), _ptr(A_b_log), _ptr(B), _ptr(C), _ptr(B_b), _ptr(C_b),
-        _ptr(D), _ptr(D_b), _ptr(delta_bias), _ptr(out), nb, nd, L, D_STATE, dt,
+        _ptr(D), _ptr(D_b), _ptr(delta_bias), _ptr(out), nb, nd, L, ns, dt,
         _ptr(workspace), _nbytes(workspace), int(chunk_len), int(stage), _stream(stream, dev)))
     return out
 
@@ -194,15 +204,16 @@ def vmscan_fwd_bidir_v2(u, delta_raw, delta_bias, u_b, delta_raw_b, delta_bias_b
     if u.dim() != 3:
         raise ValueError("u must be [batch, dim, L]")
     nb, nd, L = u.shape
+    ns = _d_state(A_log)
     dev = u.device
     adt = u.dtype
     dt = _act_dtype(u)
     for name, t in (("u", u), ("delta_raw", delta_raw), ("u_b", u_b), ("delta_raw_b", delta_raw_b), ("z", z)):
         _need(t, name, (nb, nd, L), adt, dev)
     for name, t in (("B", B), ("C", C), ("B_b", B_b), ("C_b", C_b)):
-        _need(t, name, (nb, D_STATE, L), adt, dev)
+        _need(t, name, (nb, ns, L), adt, dev)
     for name, t in (("A_log", A_log), ("A_b_log", A_b_log)):
-        _need(t, name, (nd, D_STATE), torch.float32, dev)
+        _need(t, name, (nd, ns), torch.float32, dev)
     for name, t in (("D", D), ("D_b", D_b), ("delta_bias", delta_bias), ("delta_bias_b", delta_bias_b)):
         _need(t, name, (nd,), torch.float32, dev)
     if out is None:
@@ -210,12 +221,12 @@ def vmscan_fwd_bidir_v2(u, delta_raw, delta_bias, u_b, delta_raw_b, delta_bias_b
     else:
         _need(out, "out", (nb, nd, L), adt, dev)
     lib = load()
-    wsb = lib.vmscan_fwd_bidir_workspace_bytes_ex(nb, nd, L, D_STATE, dt, int(chunk_len))
+    wsb = lib.vmscan_fwd_bidir_workspace_bytes_ex(nb, nd, L, ns, dt, int(chunk_len))
     workspace = _workspace(workspace, wsb, dev)
     _check(lib.vmscan_fwd_bidir_v2_stage(
         _ptr(u), _ptr(delta_raw), _ptr(delta_bias), _ptr(u_b), _ptr(delta_raw_b), _ptr(delta_bias_b), _ptr(z),
         _ptr(A_log), _ptr(A_b_log), _ptr(B), _ptr(C), _ptr(B_b), _ptr(C_b), _ptr(D), _ptr(D_b), _ptr(out),
-        nb, nd, L, D_STATE, dt, _ptr(workspace), _nbytes(workspace), int(chunk_len), int(stage),
+        nb, nd, L, ns, dt, _ptr(workspace), _nbytes(workspace), int(chunk_len), int(stage),
         _stream(stream, dev)))
     return out
 
@@ -226,10 +237,11 @@ def vmscan_bwd_bidir_v2(u, delta_raw, delta_bias, u_b, delta_raw_b, delta_bias_b
     du, ddelta_raw, ddelta_bias, du_b, ddelta_raw_b, ddelta_bias_b, dz, dA_log, dA_b_log, dB, dC,
     dB_b, dC_b, dD, dD_b.  With ``shared=True`` (u_b is u, delta_raw_b is delta_raw, delta_bias_b
     is delta_bias, i.e. ``vmscan_fwd_bidir``) the backward branch's du, ddelta_raw and ddelta_bias
-    are added into the forward ones and the ``_b`` entries are None."""
+    are added into the forward ones and the ``_b`` entries are None.  d_state 16 only."""
     if u.dim() != 3:
         raise ValueError("u must be [batch, dim, L]")
     nb, nd, L = u.shape
+    ns = _d_state(A_log)
     dev = u.device
     adt = u.dtype
     dt = _act_dtype(u)
@@ -237,26 +249,26 @@ def vmscan_bwd_bidir_v2(u, delta_raw, delta_bias, u_b, delta_raw_b, delta_bias_b
                     ("dout", dout)):
         _need(t, name, (nb, nd, L), adt, dev)
     for name, t in (("B", B), ("C", C), ("B_b", B_b), ("C_b", C_b)):
-        _need(t, name, (nb, D_STATE, L), adt, dev)
+        _need(t, name, (nb, ns, L), adt, dev)
     for name, t in (("A_log", A_log), ("A_b_log", A_b_log)):
-        _need(t, name, (nd, D_STATE), torch.float32, dev)
+        _need(t, name, (nd, ns), torch.float32, dev)
     for name, t in (("D", D), ("D_b", D_b), ("delta_bias", delta_bias), ("delta_bias_b", delta_bias_b)):
         _need(t, name, (nd,), torch.float32, dev)
     act = lambda: torch.empty_like(u)
     bcs = lambda: torch.empty_like(B)
     par = lambda *s: torch.empty(*s, dtype=torch.float32, device=dev)
-    g = dict(du=act(), ddelta_raw=act(), ddelta_bias=par(nd), dz=act(), dA_log=par(nd, D_STATE),
-             dA_b_log=par(nd, D_STATE), dB=bcs(), dC=bcs(), dB_b=bcs(), dC_b=bcs(), dD=par(nd), dD_b=par(nd))
+    g = dict(du=act(), ddelta_raw=act(), ddelta_bias=par(nd), dz=act(), dA_log=par(nd, ns),
+             dA_b_log=par(nd, ns), dB=bcs(), dC=bcs(), dB_b=bcs(), dC_b=bcs(), dD=par(nd), dD_b=par(nd))
     g["du_b"], g["ddelta_raw_b"], g["ddelta_bias_b"] = (None, None, None) if shared else (act(), act(), par(nd))
     lib = load()
-    wsb = lib.vmscan_bwd_bidir_v2_workspace_bytes(nb, nd, L, D_STATE, dt)
+    wsb = lib.vmscan_bwd_bidir_v2_workspace_bytes(nb, nd, L, ns, dt)
     workspace = _workspace(workspace, wsb, dev)
     _check(lib.vmscan_bwd_bidir_v2(
         _ptr(u), _ptr(delta_raw), _ptr(delta_bias), _ptr(u_b), _ptr(delta_raw_b), _ptr(delta_bias_b), _ptr(z),
         _ptr(A_log), _ptr(A_b_log), _ptr(B), _ptr(C), _ptr(B_b), _ptr(C_b), _ptr(D), _ptr(D_b), _ptr(dout),
         *[_ptr(g[k]) for k in ("du", "ddelta_raw", "ddelta_bias", "du_b", "ddelta_raw_b", "ddelta_bias_b", "dz",
                                "dA_log", "dA_b_log", "dB", "dC", "dB_b", "dC_b", "dD", "dD_b")],
-        nb, nd, L, D_STATE, dt, _ptr(workspace), _nbytes(workspace), _stream(stream, dev)))
+        nb, nd, L, ns, dt, _ptr(workspace), _nbytes(workspace), _stream(stream, dev)))
     return g
 
 
@@ -264,21 +276,22 @@ def ss2d_cross_scan_fwd(x, delta_raw, A_log, B, C, D, delta_bias, z=None, out=No
                         workspace=None, stream=None):
     """SS2D four-direction cross-scan with cross-merge; returns ``out`` [batch, dim, H, W].
 
-    x: [batch, dim, H, W]; delta_raw: [batch, 4, dim, H*W]; A_log: [4, dim, 16] float32;
-    B, C: [batch, 4, 16, H*W] (each direction's scan order); D, delta_bias: [4, dim] float32;
-    z: optional [batch, dim, H, W] gate."""
+    x: [batch, dim, H, W]; delta_raw: [batch, 4, dim, H*W]; A_log: [4, dim, N] float32 (d_state
+    N = 16 or 32); B, C: [batch, 4, N, H*W] (each direction's scan order); D, delta_bias: [4, dim]
+    float32; z: optional [batch, dim, H, W] gate."""
     if x.dim() != 4:
         raise ValueError("x must be [batch, dim, H, W]")
     nb, nd, H, W = x.shape
     L = H * W
+    ns = _d_state(A_log)
     dev = x.device
     adt = x.dtype
     dt = _act_dtype(x)
     _need(x, "x", (nb, nd, H, W), adt, dev)
     _need(delta_raw, "delta_raw", (nb, 4, nd, L), adt, dev)
-    _need(B, "B", (nb, 4, D_STATE, L), adt, dev)
-    _need(C, "C", (nb, 4, D_STATE, L), adt, dev)
-    _need(A_log, "A_log", (4, nd, D_STATE), torch.float32, dev)
+    _need(B, "B", (nb, 4, ns, L), adt, dev)
+    _need(C, "C", (nb, 4, ns, L), adt, dev)
+    _need(A_log, "A_log", (4, nd, ns), torch.float32, dev)
     _need(D, "D", (4, nd), torch.float32, dev)
     _need(delta_bias, "delta_bias", (4, nd), torch.float32, dev)
     if z is not None:
@@ -288,30 +301,31 @@ def ss2d_cross_scan_fwd(x, delta_raw, A_log, B, C, D, delta_bias, z=None, out=No
     else:
         _need(out, "out", (nb, nd, H, W), adt, dev)
     lib = load()
-    wsb = lib.ss2d_cross_scan_workspace_bytes_ex(nb, nd, H, W, D_STATE, dt, int(chunk_len))
+    wsb = lib.ss2d_cross_scan_workspace_bytes_ex(nb, nd, H, W, ns, dt, int(chunk_len))
     workspace = _workspace(workspace, wsb, dev)
     _check(lib.ss2d_cross_scan_fwd_ex(
         _ptr(x), _ptr(delta_raw), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(delta_bias), _ptr(z), _ptr(out),
-        nb, nd, H, W, D_STATE, dt, _ptr(workspace), _nbytes(workspace), int(chunk_len), _stream(stream, dev)))
+        nb, nd, H, W, ns, dt, _ptr(workspace), _nbytes(workspace), int(chunk_len), _stream(stream, dev)))
     return out
 
 
 def ss2d_cross_scan_bwd(x, delta_raw, A_log, B, C, D, delta_bias, z, dout, workspace=None, stream=None):
     """Gradients of ``ss2d_cross_scan_fwd`` for ``dout`` (ss2d_cross_scan_bwd); returns a dict with
-    dx, ddelta_raw, dA_log, dB, dC, dD, ddelta_bias and dz (None when z is None)."""
+    dx, ddelta_raw, dA_log, dB, dC, dD, ddelta_bias and dz (None when z is None).  d_state 16 only."""
     if x.dim() != 4:
         raise ValueError("x must be [batch, dim, H, W]")
     nb, nd, H, W = x.shape
     L = H * W
+    ns = _d_state(A_log)
     dev = x.device
     adt = x.dtype
     dt = _act_dtype(x)
     _need(x, "x", (nb, nd, H, W), adt, dev)
     _need(dout, "dout", (nb, nd, H, W), adt, dev)
     _need(delta_raw, "delta_raw", (nb, 4, nd, L), adt, dev)
-    _need(B, "B", (nb, 4, D_STATE, L), adt, dev)
-    _need(C, "C", (nb, 4, D_STATE, L), adt, dev)
-    _need(A_log, "A_log", (4, nd, D_STATE), torch.float32, dev)
+    _need(B, "B", (nb, 4, ns, L), adt, dev)
+    _need(C, "C", (nb, 4, ns, L), adt, dev)
+    _need(A_log, "A_log", (4, nd, ns), torch.float32, dev)
     _need(D, "D", (4, nd), torch.float32, dev)
     _need(delta_bias, "delta_bias", (4, nd), torch.float32, dev)
     if z is not None:
@@ -320,14 +334,14 @@ def ss2d_cross_scan_bwd(x, delta_raw, A_log, B, C, D, delta_bias, z, dout, works
              dB=torch.empty_like(B), dC=torch.empty_like(C), dD=torch.empty_like(D),
              ddelta_bias=torch.empty_like(delta_bias), dz=torch.empty_like(x) if z is not None else None)
     lib = load()
-    wsb = lib.ss2d_cross_scan_bwd_workspace_bytes(nb, nd, H, W, D_STATE, dt)
+    wsb = lib.ss2d_cross_scan_bwd_workspace_bytes(nb, nd, H, W, ns, dt)
     workspace = _workspace(workspace, wsb, dev)
     _check(lib.ss2d_cross_scan_bwd(
         _ptr(x), _ptr(delta_raw), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(delta_bias), _ptr(z), _ptr(dout),
         *[_ptr(g[k]) for k in ("dx", "ddelta_raw", "dA_log", "dB", "dC", "dD", "ddelta_bias", "dz")],
-        nb, nd, H, W, D_STATE, dt, _ptr(workspace), _nbytes(workspace), _stream(stream, dev)))
+        nb, nd, H, W, ns, dt, _ptr(workspace), _nbytes(workspace), _stream(stream, dev)))
     return g
 
 
-def fwd_bidir_chunk_len(batch, dim, seqlen):
-    return int(load().vmscan_fwd_bidir_chunk_len(batch, dim, seqlen, D_STATE))
+def fwd_bidir_chunk_len(batch, dim, seqlen, d_state=D_STATE):
+    return int(load().vmscan_fwd_bidir_chunk_len(batch, dim, seqlen, d_state))

@@ -54,10 +54,10 @@
 
 namespace {
 
-constexpr int kN = 16;                 // d_state
-constexpr int kH = 8;                  // states per wave: two waves per (channel, direction)
+constexpr int kN = 16;                 // d_state of the backward pass; the forward takes 16 or 32
+constexpr int kH = 8;                  // states per wave: d_state / 8 waves (parts) per (channel, direction)
 constexpr int kW = 64;                 // channels per workgroup = lanes per wave
-constexpr int kThreads = 4 * kW;       // waves: (fwd, lo) (bwd, lo) (fwd, hi) (bwd, hi)
+constexpr int kThreads = 4 * kW;       // d_state 16 workgroup: (fwd, lo) (bwd, lo) (fwd, hi) (bwd, hi)
 constexpr int kWin = 8;                // tokens per register window
 constexpr int kBC = 2 * kH;            // floats per (position, half) in the B/C copy: 8 B, 8 C
 constexpr int kKMax = 206;             // longest LDS row: 3 workgroups of 64 x 207 floats per CU
@@ -65,7 +65,6 @@ constexpr int kMinChunk = 32;          // shortest chunk the planner picks
 constexpr int kTargetBlocks = 768;     // planner: three workgroups on each of 256 CUs
 constexpr int kKSplit = 158;           // split sequences: chunks of <= 158 positions (LDS rows of 159), four workgroups per CU
 constexpr int kSplitSlots = 1024;      // ... so a round is four workgroups on each of 256 CUs
-constexpr int kAggStride = kN + 1;     // per chunk: 16 end states + Σ Δ2
 constexpr int kTransThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -202,11 +201,12 @@ struct ScanArgs {
   const void* z;   // gate, same layout as u, or null
   void* out;
   float* wsy;      // fp32 image of the first SS2D pair
-  float* bct;      // [batch][2][2][L][kBC] fp32 B/C copy in position order
-  float* agg;      // [batch][dim][2][nch][kAggStride]
+  float* bct;      // [batch][2][parts][L][kBC] fp32 B/C copy in position order
+  float* agg;      // [batch][dim][2][nch][ns + 1]
   DirArgs d0, d1;  // forward and backward direction of the pair
   int64_t L;
   int dim, batch, K, nch, ngroups;
+  int ns, parts;   // d_state and its parts of 8 states (one wave per direction and part)
 };
 
 // kModeVimSum: Vim order, but the epilogue stores the un-gated fp32 sum y_f + y_b to wsy;
@@ -215,7 +215,7 @@ struct ScanArgs {
 enum { kModeVim = 0, kModeFirstPair = 1, kModeSecondPair = 2, kModeVimSum = 3, kModeSecondPairSum = 4 };
 
 // ---------------------------------------------------------------------------------------------
-// B/C transpose: for half q, bct[b][dir][q][s][0..7] = B_dir[b][8q + 0..7, si(s)] ln 2 and
+// B/C transpose: for state part q, bct[b][dir][q][s][0..7] = B_dir[b][8q + 0..7, si(s)] ln 2 and
 // bct[b][dir][q][s][8..15] = C_dir[b][8q + 0..7, si(s)].
 
 template <typename T>
@@ -232,14 +232,14 @@ __global__ __launch_bounds__(kTransThreads) void bc_transpose_kernel(ScanArgs a)
   const T* bb = static_cast<const T*>(da.B) + static_cast<int64_t>(b) * da.bc_bs + si;
   const T* cb = static_cast<const T*>(da.C) + static_cast<int64_t>(b) * da.bc_bs + si;
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
+  for (int q = 0; q < a.parts; ++q) {
     float v[kBC];
 #pragma unroll
     for (int k = 0; k < kH; ++k) {
       v[k] = ld_act(bb, static_cast<int64_t>(kH * q + k) * a.L) * kLn2;  // B ln 2: Δ2 u (B ln 2) = Δ u B
       v[kH + k] = ld_act(cb, static_cast<int64_t>(kH * q + k) * a.L);
     }
-    float4* dst = reinterpret_cast<float4*>(a.bct + (((static_cast<int64_t>(b) * 2 + dir) * 2 + q) * a.L + s) * kBC);
+    float4* dst = reinterpret_cast<float4*>(a.bct + (((static_cast<int64_t>(b) * 2 + dir) * a.parts + q) * a.L + s) * kBC);
 #pragma unroll
     for (int k = 0; k < kBC / 4; ++k) dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
   }
@@ -335,7 +335,7 @@ __global__ __launch_bounds__(256) void transpose16_kernel(const uint16_t* __rest
 // The state half of a wave is a wave-uniform run-time value (it only selects data).
 
 struct Lane {
-  int b, c, lane, d, dd, half;  // dd: channel clamped into range for the loads of inactive lanes
+  int b, c, lane, d, dd, part;  // dd: channel clamped into range for the loads of inactive lanes
   bool valid;
   int64_t s_lo;
   int Kc;
@@ -350,7 +350,7 @@ __device__ __forceinline__ Lane lane_ctx(const ScanArgs& a) {
   l.c = rest % a.nch;
   l.b = rest / a.nch;
   l.lane = threadIdx.x & (kW - 1);
-  l.half = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 7);
+  l.part = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 7);  // state part: wave / 2
   l.d = g * kW + l.lane;
   l.valid = l.d < a.dim;
   l.dd = l.valid ? l.d : a.dim - 1;
@@ -394,10 +394,10 @@ struct Window {
   }
 };
 
-// A = -exp(A_log) for the wave's 8 states (the decay of a step is exp2(Δ2 A)).
-__device__ __forceinline__ void load_a2(const DirArgs& da, const Lane& l, float (&A2)[kH]) {
+// A = -exp(A_log) for the wave's 8 states (the decay of a step is exp2(Δ2 A)); ns = d_state.
+__device__ __forceinline__ void load_a2(const DirArgs& da, const Lane& l, int ns, float (&A2)[kH]) {
 #pragma unroll
-  for (int k = 0; k < kH; ++k) A2[k] = -__expf(da.A_log[static_cast<int64_t>(l.dd) * kN + kH * l.half + k]);
+  for (int k = 0; k < kH; ++k) A2[k] = -__expf(da.A_log[static_cast<int64_t>(l.dd) * ns + kH * l.part + k]);
 }
 
 // B/C of one position for the wave's half: 8 + 8 wave-uniform floats (one s_load_dwordx16).
@@ -409,7 +409,7 @@ __device__ __forceinline__ void load_bc(scalar_fp p, float (&bc)[kBC]) {
 // The wave's row of the B/C copy.
 template <int DIR>
 __device__ __forceinline__ scalar_fp bc_row(const ScanArgs& a, const Lane& l) {
-  return (scalar_fp)(a.bct) + (((static_cast<int64_t>(l.b) * 2 + DIR) * 2 + l.half) * a.L) * kBC;
+  return (scalar_fp)(a.bct) + (((static_cast<int64_t>(l.b) * 2 + DIR) * a.parts + l.part) * a.L) * kBC;
 }
 
 // One token for the wave's 8 states, h = exp2(Δ2 A) h + (Δ2 u)(B ln 2); returns yi + Σ C h.  The B/C of
@@ -491,12 +491,13 @@ __device__ __forceinline__ float single_step(const ScanArgs& a, const Lane& l, c
   return y;
 }
 
-// Pairwise ordering of the two state halves of one direction, without a workgroup barrier: the
-// lower-half wave publishes the number of the last combine unit it has written to the LDS rows,
-// and the upper-half wave waits for it before adding.  A wave's LDS operations execute in issue
-// order, so the data writes are complete when the flag write is, and the compiler barriers keep
-// the instructions in that order.  The lower half never waits, so the wait always ends; the
-// bound only keeps a mistake from turning into a hang.
+// Ordering of the state parts of one direction, without a workgroup barrier: part 0 publishes the
+// number of the last combine unit it has written to the LDS rows, and part p > 0 waits for part
+// p - 1's number before adding (and, unless it is the last part, publishes its own).  A wave's
+// LDS operations execute in issue order, so the data writes are complete when the flag write is,
+// and the compiler barriers keep the instructions in that order.  Part 0 never waits and each
+// wait is on a lower part, so every wait ends; the bound only keeps a mistake from turning into
+// a hang.
 __device__ __forceinline__ void unit_signal(int* flag, int unit) {
   asm volatile("" ::: "memory");
   __hip_atomic_store(flag, unit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -515,24 +516,25 @@ __device__ __forceinline__ void unit_wait(int* flag, int unit) {
 // Pass A: per chunk, direction and state half, the end states of the chunk scanned from a zero
 // state, and Σ Δ2 (base-2 units).
 
-// Δ and Δ·u exchange between the two state halves of a direction: each wave computes them for
-// half of a window's steps and reads the other half from its partner, so softplus is evaluated
-// once per (channel, step) instead of once per wave.  Double-buffered by window parity; a wave
-// overwrites a buffer only after its partner has published the next window, which it does only
-// after reading that buffer.
-constexpr int kXHalf = kWin / 2;
+// Δ and Δ·u exchange between the NP state parts of a direction: each wave computes them for 8/NP
+// of a window's steps and reads the rest from the other parts, so softplus is evaluated once per
+// (channel, step) instead of once per wave.  Double-buffered by window parity; a wave overwrites
+// a buffer only after every other part has published the next window, which each does only after
+// reading that buffer.
+template <int NP>
 struct ChunkXchg {
-  float v[2][2][2][2][kW][kXHalf];  // [dir][window parity][half][Δ, Δ·u][lane][step]
-  int prod[2][2];                   // [dir][half]: windows published
+  static constexpr int kX = kWin / NP;  // steps per part and window
+  float v[2][2][NP][2][kW][kX];         // [dir][window parity][part][Δ, Δ·u][lane][step]
+  int prod[2][NP];                      // [dir][part]: windows published
 };
 
-template <typename T, int MODE, int DIR, int HALF>
-__device__ __forceinline__ void chunk_state_dir(const ScanArgs& a, const Lane& l, ChunkXchg& xc) {
+template <typename T, int MODE, int DIR, int PART, int NP>
+__device__ __forceinline__ void chunk_state_dir(const ScanArgs& a, const Lane& l, ChunkXchg<NP>& xc) {
   // The last chunk in scan order carries into nothing.
   if (DIR == 0 ? l.c == a.nch - 1 : l.c == 0) return;
   const DirArgs& da = DIR == 0 ? a.d0 : a.d1;
   float A2[kH], h[kH];
-  load_a2(da, l, A2);
+  load_a2(da, l, a.ns, A2);
 #pragma unroll
   for (int n = 0; n < kH; ++n) h[n] = 0.0f;
   const float bias = da.bias[l.dd] * kLog2e;  // base-2 units
@@ -541,7 +543,7 @@ __device__ __forceinline__ void chunk_state_dir(const ScanArgs& a, const Lane& l
   float bcA[kBC], bcB[kBC];
   Window<T, MODE, DIR> win;
   const int full_end = (l.Kc / kWin) * kWin;
-  constexpr int me = HALF, other = 1 - HALF;
+  constexpr int me = PART, kX = ChunkXchg<NP>::kX;
   load_bc(bct + Dir<MODE, DIR>::pos(l, 0) * kBC, bcA);
   if (full_end > 0) win.load(a, l, da, 0);
   int w = 0;
@@ -553,30 +555,27 @@ __device__ __forceinline__ void chunk_state_dir(const ScanArgs& a, const Lane& l
     // It is unconditional for the same reason (the last window reloads itself).
     __builtin_amdgcn_sched_barrier(0);
     win.load(a, l, da, i0 + kWin < full_end ? i0 + kWin : i0);
-    float (&mine)[2][kW][kXHalf] = xc.v[DIR][w & 1][me];
-    const float (&theirs)[2][kW][kXHalf] = xc.v[DIR][w & 1][other];
-    float od[kXHalf], ou[kXHalf], td[kXHalf], tu[kXHalf];
+    float (&mine)[2][kW][kX] = xc.v[DIR][w & 1][me];
 #pragma unroll
-    for (int k = 0; k < kXHalf; ++k) {
-      const int j = kXHalf * me + k;
-      od[k] = delta2(xr[j], bias);
-      ou[k] = od[k] * uu[j];
-      mine[0][l.lane][k] = od[k];
-      mine[1][l.lane][k] = ou[k];
+    for (int k = 0; k < kX; ++k) {
+      const int j = kX * me + k;
+      dl[j] = delta2(xr[j], bias);
+      du[j] = dl[j] * uu[j];
+      mine[0][l.lane][k] = dl[j];
+      mine[1][l.lane][k] = du[j];
     }
     unit_signal(&xc.prod[DIR][me], w + 1);
-    unit_wait(&xc.prod[DIR][other], w + 1);
 #pragma unroll
-    for (int k = 0; k < kXHalf; ++k) {
-      td[k] = theirs[0][l.lane][k];
-      tu[k] = theirs[1][l.lane][k];
-    }
+    for (int q = 0; q < NP; ++q)
+      if (q != me) unit_wait(&xc.prod[DIR][q], w + 1);
 #pragma unroll
-    for (int k = 0; k < kXHalf; ++k) {
-      dl[k] = me == 0 ? od[k] : td[k];
-      du[k] = me == 0 ? ou[k] : tu[k];
-      dl[kXHalf + k] = me == 0 ? td[k] : od[k];
-      du[kXHalf + k] = me == 0 ? tu[k] : ou[k];
+    for (int q = 0; q < NP; ++q) {
+      if (q == me) continue;
+#pragma unroll
+      for (int k = 0; k < kX; ++k) {
+        dl[kX * q + k] = xc.v[DIR][w & 1][q][0][l.lane][k];
+        du[kX * q + k] = xc.v[DIR][w & 1][q][1][l.lane][k];
+      }
     }
 #pragma unroll
     for (int j = 0; j < kWin; ++j) S += dl[j];
@@ -589,27 +588,33 @@ __device__ __forceinline__ void chunk_state_dir(const ScanArgs& a, const Lane& l
     S += dl;
   }
   if (l.valid) {
-    float* ag = a.agg + ((((static_cast<int64_t>(l.b) * a.dim + l.d) * 2 + DIR) * a.nch) + l.c) * kAggStride;
+    constexpr int kStride = kH * NP + 1;
+    float* ag = a.agg + ((((static_cast<int64_t>(l.b) * a.dim + l.d) * 2 + DIR) * a.nch) + l.c) * kStride;
 #pragma unroll
-    for (int n = 0; n < kH; ++n) ag[kH * l.half + n] = h[n];
-    if (l.half == 0) ag[kN] = S;
+    for (int n = 0; n < kH; ++n) ag[kH * l.part + n] = h[n];
+    if (l.part == 0) ag[kH * NP] = S;
   }
 }
 
-template <typename T, int MODE>
-__global__ __launch_bounds__(kThreads) void chunk_state_kernel(ScanArgs a) {
-  __shared__ ChunkXchg xc;
+template <typename T, int MODE, int DIR, int NP>
+__device__ __forceinline__ void chunk_state_part(const ScanArgs& a, const Lane& l, ChunkXchg<NP>& xc) {
+  switch (l.part) {
+    case 0: chunk_state_dir<T, MODE, DIR, 0, NP>(a, l, xc); break;
+    case 1: chunk_state_dir<T, MODE, DIR, 1, NP>(a, l, xc); break;
+    case 2: if constexpr (NP > 2) chunk_state_dir<T, MODE, DIR, 2, NP>(a, l, xc); break;
+    default: if constexpr (NP > 3) chunk_state_dir<T, MODE, DIR, 3, NP>(a, l, xc); break;
+  }
+}
+
+template <typename T, int MODE, int NP>
+__global__ __launch_bounds__(2 * kW * NP) void chunk_state_kernel(ScanArgs a) {
+  __shared__ ChunkXchg<NP> xc;
   const Lane l = lane_ctx(a);
-  if (threadIdx.x < 4) xc.prod[threadIdx.x >> 1][threadIdx.x & 1] = 0;
+  if (threadIdx.x < 2 * NP) xc.prod[threadIdx.x / NP][threadIdx.x % NP] = 0;
   __syncthreads();
   const int dir = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6) & 1;
-  if (dir == 0) {
-    if (l.half == 0) chunk_state_dir<T, MODE, 0, 0>(a, l, xc);
-    else chunk_state_dir<T, MODE, 0, 1>(a, l, xc);
-  } else {
-    if (l.half == 0) chunk_state_dir<T, MODE, 1, 0>(a, l, xc);
-    else chunk_state_dir<T, MODE, 1, 1>(a, l, xc);
-  }
+  if (dir == 0) chunk_state_part<T, MODE, 0, NP>(a, l, xc);
+  else chunk_state_part<T, MODE, 1, NP>(a, l, xc);
 }
 
 // Carry prefix: per (batch, channel, direction, state), walk the chunks in scan order and replace
@@ -618,15 +623,16 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(ScanArgs a) {
 // exp(A Σ Δ) being the chunk's total decay.  One thread per (batch, channel, direction, state).
 __global__ __launch_bounds__(256) void carry_prefix_kernel(ScanArgs a) {
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t total = static_cast<int64_t>(a.batch) * a.dim * 2 * kN;
+  const int ns = a.ns, stride = ns + 1;
+  const int64_t total = static_cast<int64_t>(a.batch) * a.dim * 2 * ns;
   if (t >= total) return;
-  const int n = static_cast<int>(t % kN);
-  const int dir = static_cast<int>((t / kN) & 1);
-  const int64_t bd = t / (2 * kN);  // b * dim + d
+  const int n = static_cast<int>(t % ns);
+  const int dir = static_cast<int>((t / ns) & 1);
+  const int64_t bd = t / (2 * ns);  // b * dim + d
   const int d = static_cast<int>(bd % a.dim);
   const DirArgs& da = dir == 0 ? a.d0 : a.d1;
-  const float A2 = -__expf(da.A_log[static_cast<int64_t>(d) * kN + n]);  // with Σ Δ2: exp2(A Σ Δ2) = exp(A Σ Δ)
-  float* rec = a.agg + (bd * 2 + dir) * a.nch * kAggStride;
+  const float A2 = -__expf(da.A_log[static_cast<int64_t>(d) * ns + n]);  // with Σ Δ2: exp2(A Σ Δ2) = exp(A Σ Δ)
+  float* rec = a.agg + (bd * 2 + dir) * a.nch * stride;
   float h = 0.0f;
   // eight chunks at a time: all their loads are in flight before the dependent updates
   for (int k0 = 0; k0 < a.nch; k0 += 8) {
@@ -634,15 +640,15 @@ __global__ __launch_bounds__(256) void carry_prefix_kernel(ScanArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int k = k0 + j < a.nch ? k0 + j : a.nch - 1;
-      const float* e = rec + (dir == 0 ? k : a.nch - 1 - k) * kAggStride;
+      const float* e = rec + (dir == 0 ? k : a.nch - 1 - k) * stride;
       hend[j] = e[n];
-      S[j] = e[kN];
+      S[j] = e[ns];
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int k = k0 + j;
       if (k < a.nch) {
-        rec[(dir == 0 ? k : a.nch - 1 - k) * kAggStride + n] = h;
+        rec[(dir == 0 ? k : a.nch - 1 - k) * stride + n] = h;
         if (k + 1 < a.nch) h = __builtin_fmaf(__builtin_amdgcn_exp2f(A2 * S[j]), h, hend[j]);
       }
     }
@@ -653,34 +659,36 @@ __global__ __launch_bounds__(256) void carry_prefix_kernel(ScanArgs a) {
 // Main pass: fused bidirectional scan of one chunk with meet-in-the-middle combination.
 // Phase 0 (steps [0, M)) stores each direction's y, including its D·u term, in the channel's LDS
 // row at the chunk positions; phase 1 (steps [M, Kc)) adds it to the other direction's stored
-// value.  Within a direction the lower-half wave writes (phase 0) or adds (phase 1) first and,
-// once it has signalled that unit, the upper-half wave adds; one workgroup barrier separates the
-// phases and one precedes the epilogue.  For an odd chunk both
+// value.  Within a direction the part-0 wave writes (phase 0) or adds (phase 1) first and, in
+// part order, each other part adds once the part below has signalled that unit; one workgroup
+// barrier separates the phases and one precedes the epilogue.  For an odd chunk both
 // directions reach the middle token at their last phase-0 step; the backward value of that step
-// goes to the spare slot Kc, which the backward lower-half wave folds into the middle slot after
+// goes to the spare slot Kc, which the backward part-0 wave folds into the middle slot after
 // the phase barrier.  After both phases every row holds y_f + y_b.
 
-// LDS update of one value: the lower half writes (PHASE 0) or adds (PHASE 1); then, after the
-// lower half has signalled the unit, the upper half adds.
+// LDS update of one value by part 0: a write (PHASE 0) or an add (PHASE 1).
 template <int PHASE>
 __device__ __forceinline__ void lds_first(float* slot, float v) {
   *slot = PHASE == 1 ? *slot + v : v;
 }
 
-template <typename T, int MODE, int DIR, int PHASE>
+template <typename T, int MODE, int DIR, int PHASE, int NP>
 __device__ __forceinline__ void run_phase(const ScanArgs& a, const Lane& l, const DirArgs& da, float bias, float Dh,
                                           int i_begin, int n_win, int i_end, int spare_step, const float (&A2)[kH],
                                           float (&h)[kH], scalar_fp bct, float (&bcA)[kBC], float (&bcB)[kBC],
-                                          float* myY, int* flag, int& unit) {
+                                          float* myY, int* flags, int& unit) {
   Window<T, MODE, DIR> win;
   const int full_end = i_begin + n_win * kWin;
   constexpr int kStep = DIR == 0 ? 1 : -1;  // LDS row direction of consecutive steps
   if (full_end > i_begin) win.load(a, l, da, i_begin);
-  // Lower half: in the second phase its slots already hold the other direction's values, which
-  // are read before the window's arithmetic and added after it.  Upper half: the add of window w
-  // waits for the lower half's unit w and is done while window w + 1 is prepared, so its LDS
+  // Part 0: in the second phase its slots already hold the other direction's values, which are
+  // read before the window's arithmetic and added after it.  Other parts: the add of window w
+  // waits for the lower part's unit w and is done while window w + 1 is prepared, so its LDS
   // reads overlap the Δ arithmetic instead of stalling the wave.
-  const bool lo = l.half == 0;
+  const bool lo = l.part == 0;
+  int* const wait_flag = flags + (lo ? 0 : l.part - 1);
+  int* const own_flag = flags + l.part;
+  const bool relay = NP > 2 && !lo && l.part < NP - 1;  // a middle part publishes its own adds
   float yp[kWin];
   int pp = -1;  // upper half: chunk position of the pending window's first step, -1 when none
   for (int i0 = i_begin; i0 < full_end; i0 += kWin) {
@@ -696,7 +704,7 @@ __device__ __forceinline__ void run_phase(const ScanArgs& a, const Lane& l, cons
         for (int j = 0; j < kWin; ++j) r[j] = myY[p0 + kStep * j];
       }
     } else if (pp >= 0) {
-      unit_wait(flag, unit);
+      unit_wait(wait_flag, unit);
 #pragma unroll
       for (int j = 0; j < kWin; ++j) r[j] = myY[pp + kStep * j];
     }
@@ -704,13 +712,14 @@ __device__ __forceinline__ void run_phase(const ScanArgs& a, const Lane& l, cons
     if (!lo && pp >= 0) {
 #pragma unroll
       for (int j = 0; j < kWin; ++j) myY[pp + kStep * j] = r[j] + yp[j];
+      if (relay) unit_signal(own_flag, unit);
     }
     run_steps<MODE, DIR>(l, i0, dl, du, yi, A2, h, bcA, bcB, bct, y);
     ++unit;
     if (lo) {
 #pragma unroll
       for (int j = 0; j < kWin; ++j) myY[p0 + kStep * j] = PHASE == 1 ? r[j] + y[j] : y[j];
-      unit_signal(flag, unit);
+      unit_signal(own_flag, unit);
     } else {
 #pragma unroll
       for (int j = 0; j < kWin; ++j) yp[j] = y[j];
@@ -718,32 +727,34 @@ __device__ __forceinline__ void run_phase(const ScanArgs& a, const Lane& l, cons
     }
   }
   if (!lo && pp >= 0) {
-    unit_wait(flag, unit);
+    unit_wait(wait_flag, unit);
 #pragma unroll
     for (int j = 0; j < kWin; ++j) myY[pp + kStep * j] += yp[j];
+    if (relay) unit_signal(own_flag, unit);
   }
   for (int i = full_end; i < i_end; ++i) {
     float dl;
     const float v = single_step<T, MODE, DIR>(a, l, da, bias, Dh, i, A2, h, bct, bcA, &dl);
     const int pos = i == spare_step ? l.Kc : (DIR == 0 ? i : l.Kc - 1 - i);
     ++unit;
-    if (l.half == 0) {
+    if (lo) {
       lds_first<PHASE>(myY + pos, v);
-      unit_signal(flag, unit);
+      unit_signal(own_flag, unit);
     } else {
-      unit_wait(flag, unit);
+      unit_wait(wait_flag, unit);
       myY[pos] += v;
+      if (relay) unit_signal(own_flag, unit);
     }
   }
 }
 
 template <typename T>
 struct EpiZ;
-template <typename T, int MODE>
+template <typename T, int MODE, int NP>
 __device__ __forceinline__ void epi_prefetch(const ScanArgs& a, const Lane& l, EpiZ<T>& e);
 
-template <typename T, int MODE, int DIR>
-__device__ __forceinline__ void scan_pair_dir(const ScanArgs& a, const Lane& l, float* ybuf, int ybs, int* flag,
+template <typename T, int MODE, int DIR, int NP>
+__device__ __forceinline__ void scan_pair_dir(const ScanArgs& a, const Lane& l, float* ybuf, int ybs, int* flags,
                                               EpiZ<T>& epi) {
   using Dr = Dir<MODE, DIR>;
   const DirArgs& da = DIR == 0 ? a.d0 : a.d1;
@@ -752,18 +763,18 @@ __device__ __forceinline__ void scan_pair_dir(const ScanArgs& a, const Lane& l, 
   const bool odd = (Kc & 1) != 0;
 
   float A2[kH], h[kH];
-  load_a2(da, l, A2);
+  load_a2(da, l, a.ns, A2);
 #pragma unroll
   for (int n = 0; n < kH; ++n) h[n] = 0.0f;
   const float bias = da.bias[l.dd] * kLog2e;  // base-2 units
-  const float Dh = l.half == 0 ? da.Dp[l.dd] : 0.0f;  // the lower half adds the D·u term
+  const float Dh = l.part == 0 ? da.Dp[l.dd] : 0.0f;  // part 0 adds the D·u term
 
   // Carry-in: the state entering this chunk, which the carry-prefix kernel left in the chunk's
   // carry record.
   if (a.nch > 1) {
-    const float* e = a.agg + ((((static_cast<int64_t>(l.b) * a.dim + l.dd) * 2 + DIR) * a.nch) + l.c) * kAggStride;
+    const float* e = a.agg + ((((static_cast<int64_t>(l.b) * a.dim + l.dd) * 2 + DIR) * a.nch) + l.c) * (kH * NP + 1);
 #pragma unroll
-    for (int n = 0; n < kH; ++n) h[n] = e[kH * l.half + n];
+    for (int n = 0; n < kH; ++n) h[n] = e[kH * l.part + n];
   }
 
   const scalar_fp bct = bc_row<DIR>(a, l);
@@ -776,13 +787,14 @@ __device__ __forceinline__ void scan_pair_dir(const ScanArgs& a, const Lane& l, 
   const int nw0 = (odd ? M - 1 : M) / kWin;
   const int spare = (DIR == 1 && odd) ? M - 1 : -1;
   int unit = 0;
-  run_phase<T, MODE, DIR, 0>(a, l, da, bias, Dh, 0, nw0, M, spare, A2, h, bct, bcA, bcB, myY, flag, unit);
+  run_phase<T, MODE, DIR, 0, NP>(a, l, da, bias, Dh, 0, nw0, M, spare, A2, h, bct, bcA, bcB, myY, flags, unit);
   __syncthreads();
   // Fold the backward value of an odd chunk's middle token (kept in the spare slot) into the
   // middle slot; no wave touches either slot in the second phase.
-  if (DIR == 1 && odd && l.half == 0) myY[M - 1] += myY[Kc];
-  epi_prefetch<T, MODE>(a, l, epi);
-  run_phase<T, MODE, DIR, 1>(a, l, da, bias, Dh, M, (Kc - M) / kWin, Kc, -1, A2, h, bct, bcA, bcB, myY, flag, unit);
+  if (DIR == 1 && odd && l.part == 0) myY[M - 1] += myY[Kc];
+  epi_prefetch<T, MODE, NP>(a, l, epi);
+  run_phase<T, MODE, DIR, 1, NP>(a, l, da, bias, Dh, M, (Kc - M) / kWin, Kc, -1, A2, h, bct, bcA, bcB, myY, flags,
+                                 unit);
 }
 
 // Combined value of chunk position q of LDS row c.
@@ -811,7 +823,7 @@ __device__ __forceinline__ void store8(float* p, const float (&v)[kWin]) {
 // threads on consecutive groups of a row, so the 16-byte loads and stores are contiguous), and
 // each thread issues the gate loads of kEpiBatch groups before using any of them.  Column order
 // (second SS2D pair): position by position, pixel index advanced incrementally.
-constexpr int kEpiBatch = 8;  // kThreads * kEpiBatch >= 64 * (kKMax / 8): one batch per chunk
+constexpr int kEpiBatch = 8;  // threads * kEpiBatch >= 64 * (kKMax / 8): one batch per chunk
 
 // Gate values of the first epilogue batch, requested before the second phase so that they have
 // arrived when the epilogue starts.
@@ -827,17 +839,17 @@ __device__ __forceinline__ void epi_item(int it, int items, int ngr, int& c, int
   q = (itc - c * ngr) * kWin;
 }
 
-// Finish one batch of groups (first group it0, then every kThreads-th) with its gate values.
-template <typename T, int MODE>
+// Finish one batch of groups (first group it0, then every NTH-th) with its gate values.
+template <typename T, int MODE, int NTH>
 __device__ __forceinline__ void epi_batch(const ScanArgs& a, const float* ybuf, int ybs, int64_t base,
                                           int items, int ngr, int it0, const Run8<T> (&zr)[kEpiBatch]) {
   const T* zb = static_cast<const T*>(a.z);
   T* ob = static_cast<T*>(a.out);
 #pragma unroll
   for (int k = 0; k < kEpiBatch; ++k) {
-    if (it0 + k * kThreads >= items) break;
+    if (it0 + k * NTH >= items) break;
     int c, q;
-    epi_item(it0 + k * kThreads, items, ngr, c, q);
+    epi_item(it0 + k * NTH, items, ngr, c, q);
     const int64_t gi = base + static_cast<int64_t>(c) * a.L + q;
     float v[kWin], zz[kWin];
 #pragma unroll
@@ -870,7 +882,7 @@ __device__ __forceinline__ void epi_batch(const ScanArgs& a, const float* ybuf, 
   }
 }
 
-template <typename T, int MODE>
+template <typename T, int MODE, int NTH>
 __device__ __forceinline__ void epi_load(const ScanArgs& a, int64_t base, int items, int ngr, int it0,
                                          Run8<T> (&zr)[kEpiBatch]) {
   const T* zb = static_cast<const T*>(a.z);
@@ -878,12 +890,12 @@ __device__ __forceinline__ void epi_load(const ScanArgs& a, int64_t base, int it
 #pragma unroll
   for (int k = 0; k < kEpiBatch; ++k) {
     int c, q;
-    epi_item(it0 + k * kThreads, items, ngr, c, q);
+    epi_item(it0 + k * NTH, items, ngr, c, q);
     zr[k].load(zb + base + static_cast<int64_t>(c) * a.L + q);
   }
 }
 
-template <typename T, int MODE>
+template <typename T, int MODE, int NP>
 __device__ __forceinline__ void epi_prefetch(const ScanArgs& a, const Lane& l, EpiZ<T>& e) {
   if (MODE != kModeVim) return;
   const int g_d0 = l.d - l.lane;
@@ -892,12 +904,13 @@ __device__ __forceinline__ void epi_prefetch(const ScanArgs& a, const Lane& l, E
   const int items = nch_here * ngr;
   if (static_cast<int>(threadIdx.x) >= items) return;
   const int64_t base = static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(g_d0) * a.L + l.s_lo;
-  epi_load<T, MODE>(a, base, items, ngr, static_cast<int>(threadIdx.x), e.zr);
+  epi_load<T, MODE, 2 * kW * NP>(a, base, items, ngr, static_cast<int>(threadIdx.x), e.zr);
 }
 
-template <typename T, int MODE>
+template <typename T, int MODE, int NP>
 __device__ __forceinline__ void pair_epilogue(const ScanArgs& a, const Lane& l, const float* ybuf, int ybs,
                                               const EpiZ<T>& pre) {
+  constexpr int NTH = 2 * kW * NP;  // threads of the workgroup
   const int g_d0 = l.d - l.lane;  // first channel of the group
   const int Kc = l.Kc;
   const int tid = threadIdx.x;
@@ -910,21 +923,21 @@ __device__ __forceinline__ void pair_epilogue(const ScanArgs& a, const Lane& l, 
     const int items = nch_here * ngr;
     if (tid < items) {
       if (MODE == kModeVim) {
-        epi_batch<T, MODE>(a, ybuf, ybs, base, items, ngr, tid, pre.zr);
+        epi_batch<T, MODE, NTH>(a, ybuf, ybs, base, items, ngr, tid, pre.zr);
       } else {
         Run8<T> zr[kEpiBatch];
-        epi_load<T, MODE>(a, base, items, ngr, tid, zr);
-        epi_batch<T, MODE>(a, ybuf, ybs, base, items, ngr, tid, zr);
+        epi_load<T, MODE, NTH>(a, base, items, ngr, tid, zr);
+        epi_batch<T, MODE, NTH>(a, ybuf, ybs, base, items, ngr, tid, zr);
       }
     }
-    for (int it0 = tid + kThreads * kEpiBatch; it0 < items; it0 += kThreads * kEpiBatch) {
+    for (int it0 = tid + NTH * kEpiBatch; it0 < items; it0 += NTH * kEpiBatch) {
       Run8<T> zr[kEpiBatch];
-      epi_load<T, MODE>(a, base, items, ngr, it0, zr);
-      epi_batch<T, MODE>(a, ybuf, ybs, base, items, ngr, it0, zr);
+      epi_load<T, MODE, NTH>(a, base, items, ngr, it0, zr);
+      epi_batch<T, MODE, NTH>(a, ybuf, ybs, base, items, ngr, it0, zr);
     }
     // positions past the last full group of each row
     const int rem = Kc - ngr * kWin;
-    for (int it = tid; it < nch_here * rem; it += kThreads) {
+    for (int it = tid; it < nch_here * rem; it += NTH) {
       const int c = it / rem, q = ngr * kWin + (it - (it / rem) * rem);
       const int64_t gi = base + static_cast<int64_t>(c) * a.L + q;
       const float v = row_val(ybuf, ybs, c, q);
@@ -943,21 +956,22 @@ __device__ __forceinline__ void pair_epilogue(const ScanArgs& a, const Lane& l, 
   }
 }
 
-template <typename T, int MODE>
-__global__ __launch_bounds__(kThreads) void scan_pair_kernel(ScanArgs a) {
-  extern __shared__ float ybuf[];  // [kW][ybs]: combined y of the chunk
-  __shared__ int unit_flag[2];     // per direction: last combine unit the lower half has written
-  const int ybs = (a.K + 1) | 1;   // odd row stride spreads the 64 lanes over the banks
+// Workgroup: 2 NP waves, wave w on direction w & 1 and state part w >> 1 (states 8p .. 8p + 7).
+template <typename T, int MODE, int NP>
+__global__ __launch_bounds__(2 * kW * NP) void scan_pair_kernel(ScanArgs a) {
+  extern __shared__ float ybuf[];    // [kW][ybs]: combined y of the chunk
+  __shared__ int unit_flag[2][NP];   // per direction and part: last combine unit the part has written
+  const int ybs = (a.K + 1) | 1;     // odd row stride spreads the 64 lanes over the banks
   const Lane l = lane_ctx(a);
-  if (threadIdx.x < 2) unit_flag[threadIdx.x] = 0;
+  if (threadIdx.x < 2 * NP) unit_flag[threadIdx.x / NP][threadIdx.x % NP] = 0;
   __syncthreads();
   EpiZ<T> epi;
   if ((__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6) & 1) == 0)
-    scan_pair_dir<T, MODE, 0>(a, l, ybuf, ybs, &unit_flag[0], epi);
+    scan_pair_dir<T, MODE, 0, NP>(a, l, ybuf, ybs, unit_flag[0], epi);
   else
-    scan_pair_dir<T, MODE, 1>(a, l, ybuf, ybs, &unit_flag[1], epi);
+    scan_pair_dir<T, MODE, 1, NP>(a, l, ybuf, ybs, unit_flag[1], epi);
   __syncthreads();
-  pair_epilogue<T, MODE>(a, l, ybuf, ybs, epi);
+  pair_epilogue<T, MODE, NP>(a, l, ybuf, ybs, epi);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -989,14 +1003,21 @@ int64_t groups(int64_t dim) { return ceil_div(dim, kW); }
 
 size_t round256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-size_t bct_bytes(int64_t batch, int64_t L) {
-  return round256(static_cast<size_t>(batch) * 2 * 2 * L * kBC * sizeof(float));
+// d_state values the forward kernels take: whole parts of 8 states, one wave per direction and part.
+bool d_state_ok(int d_state) { return d_state == 16 || d_state == 32; }
+
+// Channel groups weighted by the waves of one workgroup (2 per part), in units of the 4-wave
+// workgroup of d_state 16: what the chunk planner counts.
+int64_t plan_base(int64_t batch, int64_t dim, int ns) { return batch * groups(dim) * (ns / kN); }
+
+size_t bct_bytes(int64_t batch, int64_t L, int ns = kN) {
+  return round256(static_cast<size_t>(batch) * 2 * (ns / kH) * L * kBC * sizeof(float));
 }
 
-size_t agg_bytes(int64_t batch, int64_t dim, int64_t L, int64_t K) {
+size_t agg_bytes(int64_t batch, int64_t dim, int64_t L, int64_t K, int ns = kN) {
   const int64_t nch = ceil_div(L, K);
   if (nch <= 1) return 0;
-  return round256(static_cast<size_t>(batch) * dim * 2 * nch * kAggStride * sizeof(float));
+  return round256(static_cast<size_t>(batch) * dim * 2 * nch * (ns + 1) * sizeof(float));
 }
 
 bool shape_ok(int64_t batch, int64_t dim, int64_t L) {
@@ -1015,8 +1036,8 @@ enum { kStagePrepare = 1, kStageScan = 2, kStageAll = 3 };
 
 // Stage kStagePrepare writes the fp32 B/C copy and, for a split sequence, runs the chunk-state
 // kernel; stage kStageScan runs the main kernel.
-template <typename T, int MODE>
-vmscan_status run_pair(const ScanArgs& a, hipStream_t stream, int stages) {
+template <typename T, int MODE, int NP>
+vmscan_status run_pair_np(const ScanArgs& a, hipStream_t stream, int stages) {
   const int64_t nblocks = static_cast<int64_t>(a.batch) * a.nch * a.ngroups;
   const int64_t tblocks = static_cast<int64_t>(a.batch) * 2 * ceil_div(a.L, kTransThreads);
   if (nblocks >= (int64_t{1} << 31) || tblocks >= (int64_t{1} << 31)) return VMSCAN_ERR_SHAPE;
@@ -1026,11 +1047,11 @@ vmscan_status run_pair(const ScanArgs& a, hipStream_t stream, int stages) {
     e = hipGetLastError();
     if (e != hipSuccess) return launch_failed(e);
     if (a.nch > 1) {
-      hipLaunchKernelGGL((chunk_state_kernel<T, MODE>), dim3(static_cast<unsigned>(nblocks)), dim3(kThreads),
+      hipLaunchKernelGGL((chunk_state_kernel<T, MODE, NP>), dim3(static_cast<unsigned>(nblocks)), dim3(2 * kW * NP),
                          0, stream, a);
       e = hipGetLastError();
       if (e != hipSuccess) return launch_failed(e);
-      const int64_t pblocks = ceil_div(static_cast<int64_t>(a.batch) * a.dim * 2 * kN, 256);
+      const int64_t pblocks = ceil_div(static_cast<int64_t>(a.batch) * a.dim * 2 * a.ns, 256);
       hipLaunchKernelGGL(carry_prefix_kernel, dim3(static_cast<unsigned>(pblocks)), dim3(256), 0, stream, a);
       e = hipGetLastError();
       if (e != hipSuccess) return launch_failed(e);
@@ -1038,11 +1059,21 @@ vmscan_status run_pair(const ScanArgs& a, hipStream_t stream, int stages) {
   }
   if (!(stages & kStageScan)) return VMSCAN_OK;
   const size_t smem = sizeof(float) * kW * static_cast<size_t>((a.K + 1) | 1);
-  hipLaunchKernelGGL((scan_pair_kernel<T, MODE>), dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), smem,
+  hipLaunchKernelGGL((scan_pair_kernel<T, MODE, NP>), dim3(static_cast<unsigned>(nblocks)), dim3(2 * kW * NP), smem,
                      stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return launch_failed(e);
   return VMSCAN_OK;
+}
+
+// The modes that save float32 sums for the backward pass run with d_state 16 only.
+template <typename T, int MODE>
+vmscan_status run_pair(const ScanArgs& a, hipStream_t stream, int stages) {
+  if (a.parts == 2) return run_pair_np<T, MODE, 2>(a, stream, stages);
+  if constexpr (MODE == kModeVim || MODE == kModeFirstPair || MODE == kModeSecondPair) {
+    if (a.parts == 4) return run_pair_np<T, MODE, 4>(a, stream, stages);
+  }
+  return VMSCAN_ERR_UNSUPPORTED;
 }
 
 template <int MODE>
@@ -1057,15 +1088,15 @@ struct Ss2dLayout {
   size_t col_img, row_img, xt, bct, agg, total;
 };
 
-Ss2dLayout ss2d_layout(int64_t batch, int64_t dim, int64_t L, int64_t K, size_t esz) {
+Ss2dLayout ss2d_layout(int64_t batch, int64_t dim, int64_t L, int64_t K, size_t esz, int ns = kN) {
   Ss2dLayout w{};
   const size_t img = round256(static_cast<size_t>(batch) * dim * L * sizeof(float));
   w.col_img = 0;
   w.row_img = img;
   w.xt = 2 * img;
   w.bct = w.xt + round256(static_cast<size_t>(batch) * dim * L * esz);
-  w.agg = w.bct + bct_bytes(batch, L);
-  w.total = w.agg + agg_bytes(batch, dim, L, K);
+  w.agg = w.bct + bct_bytes(batch, L, ns);
+  w.total = w.agg + agg_bytes(batch, dim, L, K, ns);
   return w;
 }
 
@@ -1103,21 +1134,24 @@ vmscan_status vim_args(ScanArgs& a, const void* u, const void* delta_raw, const 
   for (const void* p : ptrs)
     if (!p) return VMSCAN_ERR_NULL;
   if (!shape_ok(batch, dim, seqlen) || chunk_len < 0) return VMSCAN_ERR_SHAPE;
-  if (d_state != kN || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16)) return VMSCAN_ERR_UNSUPPORTED;
+  if (!d_state_ok(d_state) || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16)) return VMSCAN_ERR_UNSUPPORTED;
   for (const void* p : ptrs)
     if (!aligned16(p)) return VMSCAN_ERR_ALIGN;
-  const int64_t K = plan_chunk(batch * groups(dim), seqlen, chunk_len);
-  const vmscan_status ws =
-      check_workspace(workspace, workspace_bytes, bct_bytes(batch, seqlen) + agg_bytes(batch, dim, seqlen, K));
+  const int ns = d_state;
+  const int64_t K = plan_chunk(plan_base(batch, dim, ns), seqlen, chunk_len);
+  const vmscan_status ws = check_workspace(workspace, workspace_bytes,
+                                           bct_bytes(batch, seqlen, ns) + agg_bytes(batch, dim, seqlen, K, ns));
   if (ws != VMSCAN_OK) return ws;
   a.u_bs = dim * seqlen;
   a.z = z;
   a.out = out;
   a.wsy = nullptr;
   a.bct = static_cast<float*>(workspace);
-  a.agg = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + bct_bytes(batch, seqlen));
-  a.d0 = DirArgs{u, delta_raw, dim * seqlen, B, C, kN * seqlen, A_log, D, delta_bias, 0};
-  a.d1 = DirArgs{u_b, delta_raw_b, dim * seqlen, B_b, C_b, kN * seqlen, A_b_log, D_b, delta_bias_b, 0};
+  a.agg = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + bct_bytes(batch, seqlen, ns));
+  a.d0 = DirArgs{u, delta_raw, dim * seqlen, B, C, ns * seqlen, A_log, D, delta_bias, 0};
+  a.d1 = DirArgs{u_b, delta_raw_b, dim * seqlen, B_b, C_b, ns * seqlen, A_b_log, D_b, delta_bias_b, 0};
+  a.ns = ns;
+  a.parts = ns / kH;
   a.L = seqlen;
   a.dim = static_cast<int>(dim);
   a.batch = static_cast<int>(batch);
@@ -1251,10 +1285,10 @@ __device__ __forceinline__ void bwd_ckpt_dir(const BwdArgs& ba, const Lane& l) {
   const DirArgs& da = DIR == 0 ? a.d0 : a.d1;
   const int L = static_cast<int>(a.L);
   float A[kH];
-  load_a2(da, l, A);
+  load_a2(da, l, a.ns, A);
   const float bias2 = da.bias[l.dd] * kLog2e;
   const scalar_fp bct = bc_row<DIR>(a, l);
-  float* ckw = ba.ck + ((static_cast<int64_t>(l.b) * 2 + DIR) * 2 + l.half) * ba.nwin * a.dim * kH;
+  float* ckw = ba.ck + ((static_cast<int64_t>(l.b) * 2 + DIR) * 2 + l.part) * ba.nwin * a.dim * kH;
   auto ck_at = [&](int w) { return ckw + (static_cast<int64_t>(w) * a.dim + l.dd) * kH; };
   const int full_end = (L / kWin) * kWin;
   float h[kH], bcA[kBC], bcB[kBC];
@@ -1294,20 +1328,20 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
   const T* xb = static_cast<const T*>(da.draw) + static_cast<int64_t>(l.b) * da.draw_bs + static_cast<int64_t>(l.dd) * a.L;
   const float* gb = ba.g + static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(l.dd) * a.L;
   float A[kH];
-  load_a2(da, l, A);
+  load_a2(da, l, a.ns, A);
   const float bias2 = da.bias[l.dd] * kLog2e;
-  const float Dh = l.half == 0 ? da.Dp[l.dd] : 0.0f;
+  const float Dh = l.part == 0 ? da.Dp[l.dd] : 0.0f;
   const scalar_fp bct = bc_row<DIR>(a, l);
   const float vmask = l.valid ? 1.0f : 0.0f;  // lanes past the last channel add nothing to dB/dC
-  float* ckw = ba.ck + ((static_cast<int64_t>(l.b) * 2 + DIR) * 2 + l.half) * ba.nwin * a.dim * kH;
+  float* ckw = ba.ck + ((static_cast<int64_t>(l.b) * 2 + DIR) * 2 + l.part) * ba.nwin * a.dim * kH;
   auto ck_at = [&](int w) { return ckw + (static_cast<int64_t>(w) * a.dim + l.dd) * kH; };
   const int full_end = (L / kWin) * kWin;
 
   // Backward, window by window from the last.
   const int64_t plane = static_cast<int64_t>(a.batch) * a.dim * a.L;
   const int64_t row = static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(l.dd) * a.L;
-  float* guw = ba.gu + (DIR * 2 + l.half) * plane + row;
-  float* gxw = ba.gx + (DIR * 2 + l.half) * plane + row;
+  float* guw = ba.gu + (DIR * 2 + l.part) * plane + row;
+  float* gxw = ba.gx + (DIR * 2 + l.part) * plane + row;
   const int group = l.d / kW;
   float* dbcw = ba.dbc + ((static_cast<int64_t>(DIR) * a.ngroups + group) * a.batch + l.b) * 2 * kN * a.L;
   float lam[kH], anext[kH], dA[kH];
@@ -1441,17 +1475,17 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
         if (l.lane < kRedCols) {
           const int jj = l.lane >> 4, ty = (l.lane >> 3) & 1, kk = l.lane & 7;
           const int j = j0 + 2 * r + jj;
-          if (j < ns) dbcw[(static_cast<int64_t>(ty) * kN + kH * l.half + kk) * a.L + Dr::sidx(a, l, i0 + j)] = sum;
+          if (j < ns) dbcw[(static_cast<int64_t>(ty) * kN + kH * l.part + kk) * a.L + Dr::sidx(a, l, i0 + j)] = sum;
         }
       }
     }
   }
   if (l.valid) {
     // [dir][half][dim][kParStride][batch]: the batch sums read contiguous runs
-    float* pp = ba.dpar + ((static_cast<int64_t>(DIR) * 2 + l.half) * a.dim + l.d) * kParStride * a.batch + l.b;
+    float* pp = ba.dpar + ((static_cast<int64_t>(DIR) * 2 + l.part) * a.dim + l.d) * kParStride * a.batch + l.b;
 #pragma unroll
     for (int n = 0; n < kH; ++n) pp[n * a.batch] = dA[n];
-    pp[kH * a.batch] = l.half == 0 ? dD : 0.0f;
+    pp[kH * a.batch] = l.part == 0 ? dD : 0.0f;
     pp[(kH + 1) * a.batch] = dbias;
   }
 }
@@ -1723,6 +1757,8 @@ vmscan_status run_ss2d_bwd(const void* x, const void* delta_raw, const float* A_
   float* g = reinterpret_cast<float*>(wsp + lay.g);
   float* gcol = reinterpret_cast<float*>(wsp + lay.gcol);
   ScanArgs a{};
+  a.ns = kN;
+  a.parts = kN / kH;
   a.u_bs = dim * L;
   a.z = nullptr;
   a.bct = reinterpret_cast<float*>(wsp + lay.f.bct);
@@ -1807,7 +1843,8 @@ const char* vmscan_status_string(vmscan_status s) {
     case VMSCAN_OK: return "VMSCAN_OK";
     case VMSCAN_ERR_NULL: return "VMSCAN_ERR_NULL: a required pointer is NULL";
     case VMSCAN_ERR_SHAPE: return "VMSCAN_ERR_SHAPE: a size is < 1 or too large";
-    case VMSCAN_ERR_UNSUPPORTED: return "VMSCAN_ERR_UNSUPPORTED: d_state must be 16 and dtype F32 or BF16";
+    case VMSCAN_ERR_UNSUPPORTED:
+      return "VMSCAN_ERR_UNSUPPORTED: d_state must be 16 or 32 (16 for the backward passes) and dtype F32 or BF16";
     case VMSCAN_ERR_ALIGN: return "VMSCAN_ERR_ALIGN: a pointer is not 16-byte aligned";
     case VMSCAN_ERR_WORKSPACE: return "VMSCAN_ERR_WORKSPACE: workspace missing or too small";
     case VMSCAN_ERR_HIP: return "VMSCAN_ERR_HIP: a HIP call failed (see vmscan_last_hip_error)";
@@ -1818,17 +1855,17 @@ const char* vmscan_status_string(vmscan_status s) {
 int vmscan_last_hip_error(void) { return g_last_hip_error; }
 
 int64_t vmscan_fwd_bidir_chunk_len(int64_t batch, int64_t dim, int64_t seqlen, int d_state) {
-  if (!shape_ok(batch, dim, seqlen) || d_state != kN) return 0;
-  return plan_chunk(batch * groups(dim), seqlen, 0);
+  if (!shape_ok(batch, dim, seqlen) || !d_state_ok(d_state)) return 0;
+  return plan_chunk(plan_base(batch, dim, d_state), seqlen, 0);
 }
 
 size_t vmscan_fwd_bidir_workspace_bytes_ex(int64_t batch, int64_t dim, int64_t seqlen, int d_state,
                                            vmscan_dtype dtype, int64_t chunk_len) {
-  if (!shape_ok(batch, dim, seqlen) || d_state != kN || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16) ||
+  if (!shape_ok(batch, dim, seqlen) || !d_state_ok(d_state) || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16) ||
       chunk_len < 0)
     return 0;
-  const int64_t K = plan_chunk(batch * groups(dim), seqlen, chunk_len);
-  return bct_bytes(batch, seqlen) + agg_bytes(batch, dim, seqlen, K);
+  const int64_t K = plan_chunk(plan_base(batch, dim, d_state), seqlen, chunk_len);
+  return bct_bytes(batch, seqlen, d_state) + agg_bytes(batch, dim, seqlen, K, d_state);
 }
 
 size_t vmscan_fwd_bidir_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen, int d_state,
@@ -1941,10 +1978,11 @@ size_t ss2d_cross_scan_workspace_bytes_ex(int64_t batch, int64_t dim, int64_t H,
                                           vmscan_dtype dtype, int64_t chunk_len) {
   if (H < 1 || W < 1 || H >= (int64_t{1} << 31) || W >= (int64_t{1} << 31)) return 0;
   const int64_t L = H * W;
-  if (!shape_ok(batch, dim, L) || d_state != kN || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16) || chunk_len < 0)
+  if (!shape_ok(batch, dim, L) || !d_state_ok(d_state) || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16) ||
+      chunk_len < 0)
     return 0;
-  const int64_t K = plan_chunk(batch * groups(dim), L, chunk_len);
-  return ss2d_layout(batch, dim, L, K, dtype == VMSCAN_F32 ? 4 : 2).total;
+  const int64_t K = plan_chunk(plan_base(batch, dim, d_state), L, chunk_len);
+  return ss2d_layout(batch, dim, L, K, dtype == VMSCAN_F32 ? 4 : 2, d_state).total;
 }
 
 size_t ss2d_cross_scan_workspace_bytes(int64_t batch, int64_t dim, int64_t H, int64_t W, int d_state,
@@ -1963,7 +2001,7 @@ vmscan_status ss2d_cross_scan_fwd_ex(const void* x, const void* delta_raw, const
   if (H < 1 || W < 1 || H >= (int64_t{1} << 31) || W >= (int64_t{1} << 31) || chunk_len < 0) return VMSCAN_ERR_SHAPE;
   const int64_t L = H * W;
   if (!shape_ok(batch, dim, L)) return VMSCAN_ERR_SHAPE;
-  if (d_state != kN || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16)) return VMSCAN_ERR_UNSUPPORTED;
+  if (!d_state_ok(d_state) || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16)) return VMSCAN_ERR_UNSUPPORTED;
   for (const void* p : ptrs)
     if (!aligned16(p)) return VMSCAN_ERR_ALIGN;
   if (z && !aligned16(z)) return VMSCAN_ERR_ALIGN;
@@ -1971,21 +2009,24 @@ vmscan_status ss2d_cross_scan_fwd_ex(const void* x, const void* delta_raw, const
   const vmscan_status ws = check_workspace(workspace, workspace_bytes, need);
   if (ws != VMSCAN_OK) return ws;
 
-  const int64_t K = plan_chunk(batch * groups(dim), L, chunk_len);
+  const int ns = d_state;
+  const int64_t K = plan_chunk(plan_base(batch, dim, ns), L, chunk_len);
   const size_t esz = dtype == VMSCAN_F32 ? 4 : 2;
-  const Ss2dLayout lay = ss2d_layout(batch, dim, L, K, esz);
+  const Ss2dLayout lay = ss2d_layout(batch, dim, L, K, esz, ns);
   unsigned char* wsp = static_cast<unsigned char*>(workspace);
 
   auto off = [&](const void* p, int64_t elems) {
     return static_cast<const void*>(static_cast<const unsigned char*>(p) + elems * static_cast<int64_t>(esz));
   };
-  // Direction k of delta_raw [batch, 4, dim, L] and B/C [batch, 4, 16, L]; params [4, dim(, 16)].
+  // Direction k of delta_raw [batch, 4, dim, L] and B/C [batch, 4, ns, L]; params [4, dim(, ns)].
   auto dir_args = [&](const void* u, int k, int rev) {
-    return DirArgs{u, off(delta_raw, k * dim * L), 4 * dim * L, off(B, k * kN * L), off(C, k * kN * L), 4 * kN * L,
-                   A_log + k * dim * kN, D + k * dim, delta_bias + k * dim, rev};
+    return DirArgs{u, off(delta_raw, k * dim * L), 4 * dim * L, off(B, k * ns * L), off(C, k * ns * L), 4 * ns * L,
+                   A_log + k * dim * ns, D + k * dim, delta_bias + k * dim, rev};
   };
 
   ScanArgs a{};
+  a.ns = ns;
+  a.parts = ns / kH;
   a.u_bs = dim * L;
   a.z = z;
   a.out = out;

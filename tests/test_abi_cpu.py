@@ -94,7 +94,8 @@ def test_fwd_v2_errors(lib):
         p[i] += 4
         assert _fwd_v2(lib, p) == ERR_ALIGN, i
     assert _fwd_v2(lib, _good_ptrs(16), L=0) == ERR_SHAPE
-    assert _fwd_v2(lib, _good_ptrs(16), ds=32) == ERR_UNSUPPORTED
+    assert _fwd_v2(lib, _good_ptrs(16), ds=24) == ERR_UNSUPPORTED
+    assert _fwd_v2(lib, _good_ptrs(16), ds=32) == ERR_WORKSPACE  # d_state 32 passes to the workspace check
     assert _fwd_v2(lib, _good_ptrs(16), stage=4) == ERR_UNSUPPORTED
     assert _fwd_v2(lib, _good_ptrs(16), L=100, chunk=16) == ERR_WORKSPACE
 
@@ -106,9 +107,13 @@ def test_fwd_bad_shapes(lib):
 
 
 def test_fwd_unsupported(lib):
-    assert _fwd(lib, _good_ptrs(), ds=8) == ERR_UNSUPPORTED
-    assert _fwd(lib, _good_ptrs(), ds=32) == ERR_UNSUPPORTED
+    for ds in (0, 8, 24, 48, 64, -16):
+        assert _fwd(lib, _good_ptrs(), ds=ds) == ERR_UNSUPPORTED, ds
     assert _fwd(lib, _good_ptrs(), dt=2) == ERR_UNSUPPORTED
+    assert _fwd(lib, _good_ptrs(), ds=32, dt=2) == ERR_UNSUPPORTED
+    # d_state 16 and 32 are taken: validation goes on to the workspace
+    for ds in (16, 32):
+        assert _fwd(lib, _good_ptrs(), ds=ds) == ERR_WORKSPACE, ds
 
 
 def test_fwd_misaligned(lib):
@@ -122,13 +127,14 @@ def r256(x):
     return (x + 255) // 256 * 256
 
 
-def bct_bytes(nb, L):
-    return r256(nb * 2 * L * 32 * 4)
+def bct_bytes(nb, L, ns=16):
+    # per batch and direction, ns / 8 parts of L positions x (8 B + 8 C) float32
+    return r256(nb * 2 * (ns // 8) * L * 16 * 4)
 
 
-def agg_bytes(nb, nd, L, K):
+def agg_bytes(nb, nd, L, K, ns=16):
     nch = -(-L // K)
-    return 0 if nch <= 1 else r256(nb * nd * 2 * nch * 17 * 4)
+    return 0 if nch <= 1 else r256(nb * nd * 2 * nch * (ns + 1) * 4)
 
 
 def test_fwd_workspace(lib):
@@ -136,6 +142,11 @@ def test_fwd_workspace(lib):
     need = lib.vmscan_fwd_bidir_workspace_bytes_ex(I64(2), I64(16), I64(100), 16, 1, I64(16))
     assert need == bct_bytes(2, 100) + agg_bytes(2, 16, 100, 16)
     assert lib.vmscan_fwd_bidir_workspace_bytes_ex(I64(2), I64(16), I64(100), 16, 1, I64(100)) == bct_bytes(2, 100)
+    need32 = lib.vmscan_fwd_bidir_workspace_bytes_ex(I64(2), I64(16), I64(100), 32, 1, I64(16))
+    assert need32 == bct_bytes(2, 100, 32) + agg_bytes(2, 16, 100, 16, 32)
+    assert _fwd(lib, _good_ptrs(), L=100, chunk=16, ds=32, ws=0x80000, wsb=need32 - 1) == ERR_WORKSPACE
+    assert _fwd(lib, _good_ptrs(), L=100, chunk=16, ds=32, ws=0x80008, wsb=need32) == ERR_ALIGN
+    assert lib.vmscan_fwd_bidir_workspace_bytes_ex(I64(2), I64(16), I64(100), 24, 1, I64(16)) == 0
     assert _fwd(lib, _good_ptrs(), L=100, chunk=16) == ERR_WORKSPACE
     assert _fwd(lib, _good_ptrs(), L=100, chunk=16) == ERR_WORKSPACE
     assert _fwd(lib, _good_ptrs(), L=100, chunk=16, ws=0x80000, wsb=need - 1) == ERR_WORKSPACE
@@ -156,8 +167,17 @@ def test_workspace_queries(lib):
         assert 1 <= K <= min(L, 206)
         if K < L:
             assert K <= 158 and 4 * 64 * ((K + 1) | 1) * 4 <= 160 * 1024 - 4 * 64
+    # d_state 32: the planner counts its 8-wave workgroups double
+    for nb, nd, L in [(8, 384, 6085), (1, 384, 197), (128, 384, 197), (2, 64, 1000)]:
+        K32 = lib.vmscan_fwd_bidir_chunk_len(I64(nb), I64(nd), I64(L), 32)
+        assert 1 <= K32 <= min(L, 206)
+        assert K32 >= lib.vmscan_fwd_bidir_chunk_len(I64(nb), I64(nd), I64(L), 16)
+    assert lib.vmscan_fwd_bidir_chunk_len(I64(8), I64(384), I64(6085), 24) == 0
     img = 32 * 512 * 3136 * 4
     assert lib.ss2d_cross_scan_workspace_bytes(I64(32), I64(512), I64(56), I64(56), 16, 1) >= img
+    assert lib.ss2d_cross_scan_workspace_bytes(I64(32), I64(512), I64(56), I64(56), 32, 1) > \
+        lib.ss2d_cross_scan_workspace_bytes(I64(32), I64(512), I64(56), I64(56), 16, 1)
+    assert lib.ss2d_cross_scan_workspace_bytes(I64(32), I64(512), I64(56), I64(56), 24, 1) == 0
     assert lib.ss2d_cross_scan_workspace_bytes(I64(32), I64(512), I64(0), I64(56), 16, 1) == 0
 
 
@@ -202,6 +222,28 @@ def test_stage_errors(lib):
         p[4] = 0
         assert _stage(lib, p, st) == ERR_NULL
         assert _stage(lib, _good_ptrs(), st, L=0) == ERR_SHAPE
-        assert _stage(lib, _good_ptrs(), st, ds=32) == ERR_UNSUPPORTED
+        assert _stage(lib, _good_ptrs(), st, ds=48) == ERR_UNSUPPORTED
         assert _stage(lib, _good_ptrs(), st, ws=0) == ERR_WORKSPACE
         assert _stage(lib, _good_ptrs(), st, ws=0x80008) == ERR_ALIGN
+
+
+def test_ss2d_d_state(lib):
+    assert _ss(lib, _good_ptrs(8), ds=32, ws=0) == ERR_WORKSPACE  # 32 is taken
+    for ds in (8, 24, 64):
+        assert _ss(lib, _good_ptrs(8), ds=ds) == ERR_UNSUPPORTED, ds
+
+
+def test_bwd_d_state_16_only(lib):
+    """The backward entry points take d_state 16 only: 32 is rejected before anything runs."""
+    lib.vmscan_bwd_bidir_v2_workspace_bytes.restype = ctypes.c_size_t
+    lib.ss2d_cross_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
+    assert lib.vmscan_bwd_bidir_v2_workspace_bytes(I64(2), I64(16), I64(8), 16, 1) > 0
+    assert lib.vmscan_bwd_bidir_v2_workspace_bytes(I64(2), I64(16), I64(8), 32, 1) == 0
+    assert lib.ss2d_cross_scan_bwd_workspace_bytes(I64(2), I64(16), I64(4), I64(5), 16, 1) > 0
+    assert lib.ss2d_cross_scan_bwd_workspace_bytes(I64(2), I64(16), I64(4), I64(5), 32, 1) == 0
+    vim = [VP(p) for p in _good_ptrs(31)] + [I64(2), I64(16), I64(8), ctypes.c_int(32), ctypes.c_int(1),
+                                             VP(0x100000), ctypes.c_size_t(1 << 30), VP(0)]
+    assert lib.vmscan_bwd_bidir_v2(*vim) == ERR_UNSUPPORTED
+    ss = [VP(p) for p in _good_ptrs(17)] + [I64(2), I64(16), I64(4), I64(5), ctypes.c_int(32), ctypes.c_int(1),
+                                            VP(0x100000), ctypes.c_size_t(1 << 30), VP(0)]
+    assert lib.ss2d_cross_scan_bwd(*ss) == ERR_UNSUPPORTED

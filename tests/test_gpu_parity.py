@@ -195,3 +195,81 @@ def test_config4_full_sampled():
     p = synth.make_ss2d_inputs(4)
     bsel = np.array([0, 31])
     _report("config 4 (SS2D bf16 B32 D512 56x56, batches 0,31)", O.rel_err(run_ss2d(p)[bsel], oracle_ss2d(p, batches=bsel)), 2e-2)
+
+
+# d_state 32: four state parts of 8 per direction (eight waves per workgroup)
+DS32_SHAPES = [(1, 16, 1), (2, 17, 15), (1, 40, 33), (2, 24, 197), (1, 70, 130)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", DS32_SHAPES, ids=[f"b{b}d{d}l{l}" for b, d, l in DS32_SHAPES])
+def test_vim_d_state32(shape, dtype):
+    nb, nd, L = shape
+    p = synth.make_vim_inputs(0, layer=600 + L, batch=nb, dim=nd, seqlen=L, d_state=32, dtype=dtype)
+    ref = oracle_vim(p)
+    _report(f"vim N=32 {shape} {dtype}", O.rel_err(run_vim(p), ref), TOL[dtype])
+    if L > 20:
+        for K in (16, 33):
+            _report(f"vim N=32 {shape} {dtype} K={K}", O.rel_err(run_vim(p, chunk_len=K), ref), TOL[dtype])
+
+
+def test_vim_v2_d_state32():
+    p = synth.make_vim_v2_inputs(0, layer=650, batch=2, dim=40, seqlen=150, d_state=32, dtype="f32")
+    ref = oracle_vim_v2(p)
+    _report("vim v2 N=32", O.rel_err(run_vim_v2(p), ref), 1e-5)
+    _report("vim v2 N=32 K=40", O.rel_err(run_vim_v2(p, chunk_len=40), ref), 1e-5)
+
+
+def test_vim_d_state32_deterministic():
+    p = synth.make_vim_inputs(1, layer=4, batch=3, dim=96, seqlen=197, d_state=32)
+    assert np.array_equal(run_vim(p), run_vim(p))
+    assert np.array_equal(run_vim(p, chunk_len=48), run_vim(p, chunk_len=48))
+
+
+def test_config1_d_state32_sampled():
+    """The Vim-Ti workload (bf16, batch 128, 384 channels, 197 tokens) with d_state 32, in the
+    library-chosen launch configuration."""
+    p = synth.make_vim_inputs(1, d_state=32)
+    bsel = np.array([0, 77, 127])
+    _report("config 1 N=32 (batches 0,77,127)", O.rel_err(run_vim(p)[bsel], oracle_vim(p, batches=bsel)), 2e-2)
+
+
+def test_config3_d_state32_sampled():
+    """1248-pixel Vim-Ti (6085 tokens, split into chunks) with d_state 32."""
+    p = synth.make_vim_inputs(3, d_state=32)
+    bsel = np.array([6])
+    _report("config 3 N=32 (batch 6)", O.rel_err(run_vim(p)[bsel], oracle_vim(p, batches=bsel)), 2e-2)
+
+
+SS2D32_SHAPES = [(1, 16, 1, 1), (2, 5, 3, 7), (1, 20, 7, 9), (1, 16, 23, 19), (2, 3, 67, 5)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", SS2D32_SHAPES, ids=[f"b{b}d{d}h{h}w{w}" for b, d, h, w in SS2D32_SHAPES])
+def test_ss2d_d_state32(shape, dtype):
+    nb, nd, H, W = shape
+    p = synth.make_ss2d_inputs(4, layer=700 + H * 31 + W, batch=nb, dim=nd, H=H, W=W, d_state=32, dtype=dtype,
+                               with_z=(H * W) % 2 == 1)
+    ref = oracle_ss2d(p)
+    _report(f"ss2d N=32 {shape} {dtype}", O.rel_err(run_ss2d(p), ref), TOL[dtype])
+    if H * W > 40:
+        _report(f"ss2d N=32 {shape} {dtype} K=24", O.rel_err(run_ss2d(p, chunk_len=24), ref), TOL[dtype])
+
+
+# SS2D with the gate at the inner widths of d_model 256 with ssm_ratio 1.5 / 2.0 / 2.5
+GATED_RATIOS = [(384, 16), (512, 16), (640, 16), (384, 32), (640, 32)]
+
+
+@pytest.mark.parametrize("case", GATED_RATIOS, ids=[f"d{d}n{n}" for d, n in GATED_RATIOS])
+def test_ss2d_gated_ssm_ratio(case):
+    nd, N = case
+    p = synth.make_ss2d_inputs(4, layer=800 + nd + N, batch=2, dim=nd, H=14, W=14, d_state=N, dtype="bf16",
+                               with_z=True)
+    _report(f"ss2d gated dim {nd} N={N}", O.rel_err(run_ss2d(p), oracle_ss2d(p)), 2e-2)
+
+
+def test_config4_d_state32_sampled():
+    """The VMamba SS2D workload (bf16, batch 32, 512 channels, 56 x 56) with d_state 32."""
+    p = synth.make_ss2d_inputs(4, d_state=32)
+    bsel = np.array([17])
+    _report("config 4 N=32 (batch 17)", O.rel_err(run_ss2d(p)[bsel], oracle_ss2d(p, batches=bsel)), 2e-2)
