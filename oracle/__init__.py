@@ -19,5 +19,7 @@ from .vmscan_oracle import (  # noqa: F401
     ss2d_cross_scan,
     ss2d_cross_scan_bwd,
     ss2d_cross_scan_pathwalk,
+    conv1d_silu,
+    conv2d_silu,
     rel_err,
 )

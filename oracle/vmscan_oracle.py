@@ -364,6 +364,55 @@ def ss2d_cross_scan_pathwalk(x, delta_raw, A_log, B, C, D, delta_bias, z=None):
     return out
 
 
+def conv1d_silu(x, w, b, reverse=False):
+    """The local mixing in front of the Vim scan: u = silu(conv1d(x) + b), depthwise over channels.
+
+    x: [batch, dim, L]; w: [dim, K] (K = d_conv); b: [dim].  [P3] §2.1 gives each branch a
+    Conv1d of kernel size d_conv over d_inner channels (v2 has its own conv1d_b) and §2.2 runs
+    the backward branch on the flipped sequence.  Readings: one filter per channel (depthwise);
+    causal, i.e. K - 1 zeros in front and the first L outputs kept, so
+        pre[t] = b + sum_k w[k] x[t - (K - 1) + k];
+    SiLU after the convolution.  ``reverse`` is the backward branch expressed in original token
+    order: the same convolution applied to the flipped sequence, flipped back (anti-causal)."""
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    if reverse:
+        return np.flip(conv1d_silu(np.flip(x, axis=-1), w, b), axis=-1)
+    K = w.shape[1]
+    L = x.shape[-1]
+    padded = np.concatenate([np.zeros(x.shape[:-1] + (K - 1,)), x], axis=-1)
+    pre = np.broadcast_to(b[None, :, None], x.shape).copy()
+    for k in range(K):
+        pre += w[None, :, k, None] * padded[..., k:k + L]
+    return silu(pre)
+
+
+def conv2d_silu(x, w, b, act=True):
+    """The local mixing in front of SS2D: x' = silu(conv2d(x) + b), depthwise, K x K.
+
+    x: [batch, dim, H, W]; w: [dim, K, K] (K = d_conv, odd); b: [dim].  [P4] §2.1 applies a
+    depthwise conv2d when d_conv > 1 (3 in its table) before the core.  Readings: zero padding
+    (K - 1) / 2 on every side so the image keeps its size, cross-correlation as in the usual
+    conv layer,
+        pre[i, j] = b + sum_{a, c} w[a, c] x[i - (K - 1) / 2 + a, j - (K - 1) / 2 + c];
+    SiLU after it when ``act`` (the snippet on the page shows the convolution only; the module's
+    activation is SiLU)."""
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    K = w.shape[1]
+    assert K % 2 == 1 and w.shape[2] == K
+    p = (K - 1) // 2
+    H, W = x.shape[-2:]
+    padded = np.pad(x, ((0, 0), (0, 0), (p, p), (p, p)))
+    pre = np.broadcast_to(b[None, :, None, None], x.shape).copy()
+    for a in range(K):
+        for c in range(K):
+            pre += w[None, :, a, c, None, None] * padded[..., a:a + H, c:c + W]
+    return silu(pre) if act else pre
+
+
 def rel_err(y, r):
     """Parity error: max_i |y_i - r_i| / max(|r_i|, rms(r)).
 

@@ -1,6 +1,6 @@
 """Pins for the fp64 oracle: each ``pin_*`` takes an implementation namespace (with
 ``scan_1d``, ``vim_bidir``, ``vim_bidir_v2``, ``vim_bidir_v2_bwd``, ``ss2d_cross_scan``,
-``ss2d_cross_scan_bwd``) and returns the list of failure messages
+``ss2d_cross_scan_bwd``, ``conv1d_silu``, ``conv2d_silu``) and returns the list of failure messages
 (empty = pass).  They check the oracle against facts fixed by the mathematics, not against the
 oracle itself: hand-derived closed forms, brute force on tiny inputs, linearity, the flip
 identity, limits and the SS2D reductions.  ``test_oracle_pins`` runs them on the oracle;
@@ -489,6 +489,103 @@ def pin_ss2d_bwd_finite_differences(impl):
     return msgs
 
 
+def _conv1d_impulse_pre(K, w, b, L, j, reverse):
+    """Pre-activation of the depthwise conv1d for a unit impulse at position j, written from the
+    tap arithmetic: causally the impulse reaches t = j .. j + K - 1 with weight w[K - 1 - (t - j)];
+    the reversed branch mirrors that to t = j - K + 1 .. j with weight w[K - 1 - (j - t)]."""
+    pre = np.full(L, b)
+    for t in range(L):
+        lag = (j - t) if reverse else (t - j)
+        if 0 <= lag <= K - 1:
+            pre[t] += w[K - 1 - lag]
+    return pre
+
+
+def pin_conv1d_impulse(impl):
+    """Unit impulses through the front convolution, both branches, every width 1-4, and a
+    random input as the superposition of its impulses (the pre-activation is affine)."""
+    msgs = []
+    rng = np.random.default_rng(11)
+    L = 9
+    for K in (1, 2, 3, 4):
+        nd = 3
+        w = rng.standard_normal((nd, K))
+        b = rng.standard_normal(nd)
+        for reverse in (False, True):
+            for j in (0, 4, L - 1):
+                x = np.zeros((1, nd, L))
+                x[0, :, j] = 1.0
+                got = np.asarray(impl.conv1d_silu(x, w, b, reverse), dtype=np.float64)
+                exp = np.stack([O.silu(_conv1d_impulse_pre(K, w[d], b[d], L, j, reverse)) for d in range(nd)])
+                _check(msgs, f"conv1d impulse K={K} rev={reverse} j={j}", O.rel_err(got[0], exp), 1e-14)
+            x = rng.standard_normal((2, nd, L))
+            pre = np.zeros((2, nd, L))
+            for bb in range(2):
+                for d in range(nd):
+                    pre[bb, d] = b[d] + sum(x[bb, d, j] * (_conv1d_impulse_pre(K, w[d], b[d], L, j, reverse) - b[d])
+                                            for j in range(L))
+            got = np.asarray(impl.conv1d_silu(x, w, b, reverse), dtype=np.float64)
+            _check(msgs, f"conv1d superposition K={K} rev={reverse}", O.rel_err(got, O.silu(pre)), 1e-13)
+    return msgs
+
+
+def pin_conv1d_numpy(impl):
+    """The causal branch against numpy's full convolution with the kernel reversed (numpy
+    convolves; the layer correlates), truncated to the first L outputs."""
+    msgs = []
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((2, 3, 13))
+    w = rng.standard_normal((3, 4))
+    b = rng.standard_normal(3)
+    exp = np.empty_like(x)
+    for bb in range(2):
+        for d in range(3):
+            exp[bb, d] = O.silu(b[d] + np.convolve(x[bb, d], w[d][::-1])[:13])
+    _check(msgs, "conv1d vs np.convolve", O.rel_err(impl.conv1d_silu(x, w, b, False), exp), 1e-13)
+    return msgs
+
+
+def pin_conv2d_scipy(impl):
+    """The SS2D front against scipy's 2-D correlation with zero fill and 'same' output size,
+    with and without the activation."""
+    from scipy.signal import correlate2d
+    msgs = []
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal((2, 3, 5, 7))
+    w = rng.standard_normal((3, 3, 3))
+    b = rng.standard_normal(3)
+    pre = np.empty_like(x)
+    for bb in range(2):
+        for d in range(3):
+            pre[bb, d] = b[d] + correlate2d(x[bb, d], w[d], mode="same", boundary="fill")
+    _check(msgs, "conv2d vs correlate2d", O.rel_err(impl.conv2d_silu(x, w, b, True), O.silu(pre)), 1e-13)
+    _check(msgs, "conv2d no act vs correlate2d", O.rel_err(impl.conv2d_silu(x, w, b, False), pre), 1e-13)
+    return msgs
+
+
+def pin_conv2d_impulse(impl):
+    """A unit impulse at (i0, j0) reaches (i, j) with weight w[i0 - i + 1, j0 - j + 1] (3 x 3
+    correlation, one pixel of zero padding), including at the image corners."""
+    msgs = []
+    rng = np.random.default_rng(14)
+    H, W = 4, 5
+    w = rng.standard_normal((2, 3, 3))
+    b = rng.standard_normal(2)
+    for i0, j0 in ((0, 0), (2, 3), (H - 1, W - 1), (0, W - 1)):
+        x = np.zeros((1, 2, H, W))
+        x[0, :, i0, j0] = 1.0
+        exp = np.empty((2, H, W))
+        for d in range(2):
+            for i in range(H):
+                for j in range(W):
+                    a, c = i0 - i + 1, j0 - j + 1
+                    exp[d, i, j] = b[d] + (w[d, a, c] if 0 <= a < 3 and 0 <= c < 3 else 0.0)
+        _check(msgs, f"conv2d impulse ({i0},{j0})", O.rel_err(impl.conv2d_silu(x, w, b, False)[0], exp), 1e-14)
+        _check(msgs, f"conv2d impulse act ({i0},{j0})", O.rel_err(impl.conv2d_silu(x, w, b, True)[0], O.silu(exp)),
+               1e-14)
+    return msgs
+
+
 ALL_PINS = [
     pin_softplus_silu,
     pin_golden_single_token,
@@ -509,4 +606,8 @@ ALL_PINS = [
     pin_bwd_finite_differences,
     pin_bwd_shared_inputs,
     pin_ss2d_bwd_finite_differences,
+    pin_conv1d_impulse,
+    pin_conv1d_numpy,
+    pin_conv2d_scipy,
+    pin_conv2d_impulse,
 ]

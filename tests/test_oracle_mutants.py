@@ -207,8 +207,60 @@ def _ss2d(x, dr, Al, B, C, D, bias, z=None, bug=None, scan_bug=None):
     return out
 
 
-def _impl(scan_bug=None, vim_bug=None, ss2d_bug=None, v2_bug=None, bwd_bug=None, ss2d_bwd_bug=None):
+def _conv1d(x, w, b, reverse=False, bug=None):
+    """Front conv1d + SiLU written per output element, with a planted mistake."""
+    x = np.asarray(x, dtype=np.float64)
+    nb, nd, L = x.shape
+    K = w.shape[1]
+    out = np.empty_like(x)
+    for bb in range(nb):
+        for d in range(nd):
+            for t in range(L):
+                acc = 0.0 if bug == "conv1d_no_bias" else b[d]
+                for k in range(K):
+                    if bug == "conv1d_drop_tap" and k == 0 and K > 1:
+                        continue
+                    wk = w[d, K - 1 - k] if bug == "conv1d_convolution" else w[d, k]
+                    if reverse and bug != "conv1d_rev_causal":
+                        src = t + (K - 1) - k
+                    elif bug == "conv1d_anticausal":
+                        src = t + k
+                    else:
+                        src = t - (K - 1) + k
+                    if 0 <= src < L:
+                        acc += wk * x[bb, d, src]
+                out[bb, d, t] = acc if bug == "conv1d_no_silu" else acc / (1.0 + np.exp(-acc))
+    return out
+
+
+def _conv2d(x, w, b, act=True, bug=None):
+    """Front conv2d (+ SiLU) written per output pixel, with a planted mistake."""
+    x = np.asarray(x, dtype=np.float64)
+    nb, nd, H, W = x.shape
+    K = w.shape[1]
+    p = (K - 1) // 2
+    out = np.empty_like(x)
+    for bb in range(nb):
+        for d in range(nd):
+            for i in range(H):
+                for j in range(W):
+                    acc = 0.0 if bug == "conv2d_no_bias" else b[d]
+                    for a in range(K):
+                        for c in range(K):
+                            wac = {"conv2d_w_transposed": w[d, c, a],
+                                   "conv2d_convolution": w[d, K - 1 - a, K - 1 - c]}.get(bug, w[d, a, c])
+                            off = 0 if bug == "conv2d_pad_offset" else p
+                            si, sj = i - off + a, j - off + c
+                            if 0 <= si < H and 0 <= sj < W:
+                                acc += wac * x[bb, d, si, sj]
+                    out[bb, d, i, j] = acc / (1.0 + np.exp(-acc)) if act else acc
+    return out
+
+
+def _impl(scan_bug=None, vim_bug=None, ss2d_bug=None, v2_bug=None, bwd_bug=None, ss2d_bwd_bug=None, conv_bug=None):
     return types.SimpleNamespace(
+        conv1d_silu=lambda x, w, b, reverse=False: _conv1d(x, w, b, reverse, bug=conv_bug),
+        conv2d_silu=lambda x, w, b, act=True: _conv2d(x, w, b, act, bug=conv_bug),
         ss2d_cross_scan_bwd=lambda *a: _ss2d_bwd(*a, bug=ss2d_bwd_bug),
         vim_bidir_v2_bwd=lambda *a: _v2_bwd(*a, bug=bwd_bug),
         softplus=O.softplus,
@@ -228,6 +280,8 @@ SS2D_BUGS = ["col_as_reshape", "col_not_transposed_back", "rev_not_flipped_back"
 SS2D_BWD_BUGS = ["g_not_reordered", "du_not_mapped_back", "dz_missing_silu_derivative"]
 BWD_BUGS = ["du_no_D", "lambda_same_step_decay", "dC_prev_state", "dB_no_delta", "ddelta_next_state", "no_sigmoid",
             "dA_log_no_chain", "bwd_g_not_flipped", "dz_silu_not_derivative", "bwd_grads_not_flipped"]
+CONV_BUGS = ["conv1d_no_bias", "conv1d_drop_tap", "conv1d_convolution", "conv1d_rev_causal", "conv1d_anticausal",
+             "conv1d_no_silu", "conv2d_no_bias", "conv2d_w_transposed", "conv2d_convolution", "conv2d_pad_offset"]
 V2_BUGS = ["v2_bwd_uses_fwd_u", "v2_bwd_uses_fwd_delta", "v2_bwd_uses_fwd_bias", "v2_fwd_uses_bwd_bias", "v2_ub_not_flipped"]
 
 
@@ -276,3 +330,9 @@ def test_bwd_mutant_caught(bug):
 @pytest.mark.parametrize("bug", SS2D_BWD_BUGS)
 def test_ss2d_bwd_mutant_caught(bug):
     assert _caught(_impl(ss2d_bwd_bug=bug)), f"planted mistake {bug} passes every pin"
+
+
+@pytest.mark.parametrize("bug", CONV_BUGS)
+def test_conv_mutant_caught(bug):
+    assert _caught(_impl(conv_bug=bug)), f"planted mistake {bug} passes every pin"
+
