@@ -1,7 +1,7 @@
 """Benchmark of the fused bidirectional selective scan (and SS2D cross-scan) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N | --all] [--no-cpu] [--v2] [--bwd]
-                    [--d-state 32]
+                    [--d-state 32] [--front]
 
 A step is one call of the hot path over one batch of seeded synthetic input already resident in
 HBM.  The default workload is the Vim-Ti layer scan (batch 128, d_inner 384, L 197, d_state 16,
@@ -10,7 +10,8 @@ are rotated so that at least 1 GiB is touched between reuses and the 256 MB Infi
 serve the inputs.  Rank 0 prints one JSON line per workload.  ``--v2`` runs the Vim workloads
 through the entry point whose backward branch has its own u_b, Δ_raw_b and bias_b; ``--bwd``
 times the backward pass (all gradients) of the Vim workloads instead of the forward; ``--d-state
-32`` runs the forward workloads with 32 states instead of 16.
+32`` runs the forward workloads with 32 states instead of 16; ``--front`` times the front
+convolution that produces the scan input followed by the scan.
 """
 import argparse
 import hashlib
@@ -422,6 +423,117 @@ def bench_bwd(cfg_id, steps, warmup, torch, V, v2=False):
     }
 
 
+def front_bytes(cfg):
+    """Algorithmic bytes of the front convolution: x read once, its outputs written once (u and
+    u_b for Vim; the row-major and transposed copies for SS2D); weights are negligible."""
+    esz = 4 if cfg["dtype"] == "f32" else 2
+    n = cfg["batch"] * cfg["dim"] * (cfg["seqlen"] if cfg["kind"] == "vim" else cfg["H"] * cfg["W"])
+    return 3 * n * esz
+
+
+def bench_front(cfg_id, steps, warmup, torch, V):
+    """Front convolution + scan as one step: Vim: conv1d + SiLU for both branches
+    (vmscan_conv1d_silu_fwd) then the scan with a separate backward branch; SS2D: the 3 x 3
+    conv2d + SiLU writing both layouts (ss2d_conv2d_silu_fwd) then the cross-scan reading the
+    transposed copy (ss2d_cross_scan_fwd_xt).  Input sets are drawn on the device and rotated
+    so that at least 1 GiB is touched between reuses."""
+    import numpy as np
+    import synth
+    cfg = synth.CONFIGS[cfg_id]
+    dev = torch.device("cuda", 0)
+    dt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
+    g = torch.Generator(device=dev)
+    g.manual_seed(44_000 + cfg_id)
+    rnd = lambda shape: torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(dt)
+    vim = cfg["kind"] == "vim"
+    if vim:
+        c = synth.make_conv1d_inputs(cfg_id)
+        p = synth.make_vim_v2_inputs(cfg_id, batch=1)  # parameters only
+        nb, nd, L = cfg["batch"], cfg["dim"], cfg["seqlen"]
+        N = cfg["d_state"]
+        act_shapes = {k: (nb, nd, L) for k in ("x", "delta_raw", "delta_raw_b", "z")}
+        act_shapes.update({k: (nb, N, L) for k in ("B", "C", "B_b", "C_b")})
+        par = {k: torch.from_numpy(np.ascontiguousarray(p[k])).to(dev) for k in VIM_PAR + V2_PAR}
+        wsb = V.lib.vmscan_fwd_bidir_workspace_bytes(nb, nd, L, N, 1 if dt == torch.bfloat16 else 0)
+        toks = nb * nd * L
+    else:
+        c = synth.make_conv2d_inputs(cfg_id)
+        p = synth.make_ss2d_inputs(cfg_id, batch=1)
+        nb, nd, H, W = cfg["batch"], cfg["dim"], cfg["H"], cfg["W"]
+        L, N = H * W, cfg["d_state"]
+        act_shapes = {"x": (nb, nd, H, W), "delta_raw": (nb, 4, nd, L), "B": (nb, 4, N, L), "C": (nb, 4, N, L)}
+        par = {k: torch.from_numpy(np.ascontiguousarray(p[k])).to(dev) for k in ("A_log", "D", "delta_bias")}
+        wsb = V.lib.ss2d_cross_scan_workspace_bytes(nb, nd, H, W, N, 1 if dt == torch.bfloat16 else 0)
+        toks = nb * nd * L
+    wts = {k: torch.from_numpy(np.ascontiguousarray(v)).to(dev) for k, v in c.items() if k.startswith("conv_")}
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    esz = 2 if dt == torch.bfloat16 else 4
+    per_set = sum(int(np.prod(s)) for s in act_shapes.values()) * esz + 3 * toks * esz
+    nsets = max(1, math.ceil((1 << 30) / per_set))
+    sets = []
+    for _ in range(nsets):
+        a = {k: rnd(s) for k, s in act_shapes.items()}
+        a["u"], a["u_b"] = torch.empty_like(a["x"]), torch.empty_like(a["x"])
+        if not vim:
+            a["xT"] = torch.empty((nb, nd, W, H), dtype=dt, device=dev)
+        a["out"] = torch.empty_like(a["x"])
+        sets.append(a)
+
+    def front(a):
+        if vim:
+            V.conv1d_silu_fwd(a["x"], wts["conv_w"], wts["conv_b"], wts["conv_w_b"], wts["conv_b_b"], u=a["u"],
+                              u_b=a["u_b"])
+        else:
+            V.ss2d_conv2d_silu_fwd(a["x"], wts["conv_w"], wts["conv_b"], x_out=a["u"], xT_out=a["xT"])
+
+    def scan(a):
+        if vim:
+            V.vmscan_fwd_bidir_v2(a["u"], a["delta_raw"], par["delta_bias"], a["u_b"], a["delta_raw_b"],
+                                  par["delta_bias_b"], a["z"], par["A_log"], par["A_b_log"], a["B"], a["C"], a["B_b"],
+                                  a["C_b"], par["D"], par["D_b"], out=a["out"], workspace=ws)
+        else:
+            V.ss2d_cross_scan_fwd(a["u"], a["delta_raw"], par["A_log"], a["B"], a["C"], par["D"], par["delta_bias"],
+                                  out=a["out"], workspace=ws, xT=a["xT"])
+
+    for i in range(warmup):
+        front(sets[i % nsets])
+        scan(sets[i % nsets])
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        a = sets[(warmup + i) % nsets]
+        ev[i][0].record(stream)
+        front(a)
+        ev[i][1].record(stream)
+        scan(a)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0][0].elapsed_time(ev[-1][2]) / steps
+    front_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    scan_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    fb = front_bytes(cfg)
+    gbs = fb / (front_ms * 1e-3) / 1e9
+    upd = state_updates(cfg)
+    alu = upd / (scan_ms * 1e-3)
+    return {
+        "metric": METRIC + " (front convolution + scan)",
+        "value": toks / (ms * 1e-3), "unit": "tokens·channels/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg["name"] + "_front", "batch": nb, "dim": nd, "seqlen": L, "d_state": N,
+                   "io_dtype": cfg["dtype"], "rotation_sets": nsets,
+                   "front": "conv1d d_conv 4 + SiLU, both branches" if vim else "conv2d 3x3 + SiLU, row-major and transposed"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "conv1d_front_kernel" if vim else "conv2d_front_kernel",
+                     "kernel_avg_us": round(front_ms * 1000, 2), "algorithmic_bytes_per_launch": fb,
+                     "scan": {"bound": "alu", "achieved": round(alu / 1e9, 1), "peak": round(ALU_PEAK_UPD_S / 1e9, 1),
+                              "unit": "Gupd/s", "frac": round(alu / ALU_PEAK_UPD_S, 4),
+                              "avg_us": round(scan_ms * 1000, 2)}},
+    }
+
+
 def bench_ss2d_bwd(cfg_id, steps, warmup, torch, V):
     """Backward pass of the SS2D cross-scan (ss2d_cross_scan_bwd, every gradient, no gate as in
     the 56x56 workload); the timed region is the whole call."""
@@ -482,6 +594,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--v2", action="store_true", help="Vim workloads with a separate backward branch (u_b, delta_raw_b, bias_b)")
     ap.add_argument("--bwd", action="store_true", help="time the backward pass of the Vim workloads")
+    ap.add_argument("--front", action="store_true",
+                    help="time the front convolution (conv1d / conv2d + SiLU) followed by the scan")
     ap.add_argument("--d-state", type=int, default=None, choices=(16, 32),
                     help="state size of the forward workloads (default: the workload's own, 16)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -532,7 +646,9 @@ def main():
     import selective_state_space_41_amd as V
     cfgs = [0, 1, 2, 3, 4] if args.all else [args.config]
     for c in cfgs:
-        if args.bwd:
+        if args.front:
+            rec = bench_front(c, args.steps, args.warmup, torch, V)
+        elif args.bwd:
             rec = bench_bwd(c, args.steps, args.warmup, torch, V, args.v2)
             if rec is None:
                 continue

@@ -270,6 +270,57 @@ vmscan_status ss2d_cross_scan_fwd_ex(const void *x, const void *delta_raw, const
                                      vmscan_dtype dtype, void *workspace, size_t workspace_bytes,
                                      int64_t chunk_len, hipStream_t stream);
 
+/*
+ * ss2d_cross_scan_fwd_ex with x's transposed copy supplied by the caller (for instance the xT_out
+ * of ss2d_conv2d_silu_fwd): xT [batch, dim, W, H], activation dtype, must equal x transposed in
+ * its last two dimensions; the column-major scans read it instead of a copy made here.  xT NULL
+ * gives VMSCAN_ERR_NULL; the rest (arguments, workspace query, errors) as ss2d_cross_scan_fwd_ex.
+ */
+vmscan_status ss2d_cross_scan_fwd_xt(const void *x, const void *xT, const void *delta_raw,
+                                     const float *A_log, const void *B, const void *C, const float *D,
+                                     const float *delta_bias, const void *z, void *out,
+                                     int64_t batch, int64_t dim, int64_t H, int64_t W, int d_state,
+                                     vmscan_dtype dtype, void *workspace, size_t workspace_bytes,
+                                     int64_t chunk_len, hipStream_t stream);
+
+/*
+ * Front of the Vim scan: the depthwise convolution + SiLU that produces the scan input u
+ * ([P3] §2.1: each branch's Conv1d of width d_conv over the d_inner channels, v2's conv1d_b for
+ * the backward branch; §2.2: the backward branch works on the flipped sequence).  Per
+ * (batch b, channel d, position t), with K = d_conv:
+ *   u[b,d,t]   = silu(conv_b[d]   + Σ_k conv_w[d,k]   x[b,d,t-(K-1)+k])      (causal)
+ *   u_b[b,d,t] = silu(conv_b_b[d] + Σ_k conv_w_b[d,k] x[b,d,t+(K-1)-k])      (the flipped branch's
+ *                causal convolution, stored in original token order as vmscan_fwd_bidir_v2's u_b)
+ * with x = 0 outside [0, seqlen).  v1 (shared convolution): pass conv_w and conv_b again as
+ * conv_w_b and conv_b_b.
+ *   x, u, u_b            : [batch, dim, seqlen]   activation dtype
+ *   conv_w, conv_w_b     : [dim, d_conv]          float32, d_conv in 1..4
+ *   conv_b, conv_b_b     : [dim]                  float32
+ * conv_w_b, conv_b_b and u_b are all NULL (forward branch only) or all set (else
+ * VMSCAN_ERR_NULL).  x is read once; u and u_b are written once, rounded once.  Outputs must not
+ * alias x.  No workspace.  Errors as for the other entry points.
+ */
+vmscan_status vmscan_conv1d_silu_fwd(const void *x, const float *conv_w, const float *conv_b,
+                                     const float *conv_w_b, const float *conv_b_b, void *u, void *u_b,
+                                     int64_t batch, int64_t dim, int64_t seqlen, int d_conv,
+                                     vmscan_dtype dtype, hipStream_t stream);
+
+/*
+ * Front of SS2D: the depthwise 3 x 3 convolution ([P4] §2.1, d_conv = 3 in its table), optionally
+ * followed by SiLU, written in the two layouts the cross-scan reads:
+ *   pre[b,d,i,j] = conv_b[d] + Σ_{a,c} conv_w[d,a,c] x[b,d,i-1+a,j-1+c]   (zero padding)
+ *   x_out[b,d,i,j] = xT_out[b,d,j,i] = act ? silu(pre) : pre
+ *   x, x_out             : [batch, dim, H, W]     activation dtype
+ *   xT_out               : [batch, dim, W, H]     activation dtype, or NULL (row-major only)
+ *   conv_w               : [dim, 3, 3]            float32
+ *   conv_b               : [dim]                  float32
+ * d_conv must be 3 and act 0 or 1 (else VMSCAN_ERR_UNSUPPORTED).  x is read once, each output
+ * written once; both hold the same rounded values.  Outputs must not alias x.  No workspace.
+ */
+vmscan_status ss2d_conv2d_silu_fwd(const void *x, const float *conv_w, const float *conv_b, int act,
+                                   void *x_out, void *xT_out, int64_t batch, int64_t dim, int64_t H,
+                                   int64_t W, int d_conv, vmscan_dtype dtype, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -69,6 +69,13 @@ def _load():
     lib.ss2d_cross_scan_fwd.argtypes = ss_args + [_c_void_p]
     lib.ss2d_cross_scan_fwd_ex.restype = ctypes.c_int
     lib.ss2d_cross_scan_fwd_ex.argtypes = ss_args + [_i64, _c_void_p]
+    lib.ss2d_cross_scan_fwd_xt.restype = ctypes.c_int
+    lib.ss2d_cross_scan_fwd_xt.argtypes = [_c_void_p] + ss_args + [_i64, _c_void_p]
+    lib.vmscan_conv1d_silu_fwd.restype = ctypes.c_int
+    lib.vmscan_conv1d_silu_fwd.argtypes = [_c_void_p] * 7 + [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _c_void_p]
+    lib.ss2d_conv2d_silu_fwd.restype = ctypes.c_int
+    lib.ss2d_conv2d_silu_fwd.argtypes = ([_c_void_p] * 3 + [ctypes.c_int] + [_c_void_p] * 2 +
+                                         [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _c_void_p])
     return lib
 
 
@@ -273,12 +280,14 @@ def vmscan_bwd_bidir_v2(u, delta_raw, delta_bias, u_b, delta_raw_b, delta_bias_b
 
 
 def ss2d_cross_scan_fwd(x, delta_raw, A_log, B, C, D, delta_bias, z=None, out=None, chunk_len=0,
-                        workspace=None, stream=None):
+                        workspace=None, stream=None, xT=None):
     """SS2D four-direction cross-scan with cross-merge; returns ``out`` [batch, dim, H, W].
 
     x: [batch, dim, H, W]; delta_raw: [batch, 4, dim, H*W]; A_log: [4, dim, N] float32 (d_state
     N = 16 or 32); B, C: [batch, 4, N, H*W] (each direction's scan order); D, delta_bias: [4, dim]
-    float32; z: optional [batch, dim, H, W] gate."""
+    float32; z: optional [batch, dim, H, W] gate; xT: optional [batch, dim, W, H], x transposed
+    (as written by ``ss2d_conv2d_silu_fwd``), read instead of a copy made by the call
+    (ss2d_cross_scan_fwd_xt)."""
     if x.dim() != 4:
         raise ValueError("x must be [batch, dim, H, W]")
     nb, nd, H, W = x.shape
@@ -303,9 +312,13 @@ def ss2d_cross_scan_fwd(x, delta_raw, A_log, B, C, D, delta_bias, z=None, out=No
     lib = load()
     wsb = lib.ss2d_cross_scan_workspace_bytes_ex(nb, nd, H, W, ns, dt, int(chunk_len))
     workspace = _workspace(workspace, wsb, dev)
-    _check(lib.ss2d_cross_scan_fwd_ex(
-        _ptr(x), _ptr(delta_raw), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(delta_bias), _ptr(z), _ptr(out),
-        nb, nd, H, W, ns, dt, _ptr(workspace), _nbytes(workspace), int(chunk_len), _stream(stream, dev)))
+    args = (_ptr(delta_raw), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(delta_bias), _ptr(z), _ptr(out),
+            nb, nd, H, W, ns, dt, _ptr(workspace), _nbytes(workspace), int(chunk_len), _stream(stream, dev))
+    if xT is None:
+        _check(lib.ss2d_cross_scan_fwd_ex(_ptr(x), *args))
+    else:
+        _need(xT, "xT", (nb, nd, W, H), adt, dev)
+        _check(lib.ss2d_cross_scan_fwd_xt(_ptr(x), _ptr(xT), *args))
     return out
 
 
@@ -341,6 +354,65 @@ def ss2d_cross_scan_bwd(x, delta_raw, A_log, B, C, D, delta_bias, z, dout, works
         *[_ptr(g[k]) for k in ("dx", "ddelta_raw", "dA_log", "dB", "dC", "dD", "ddelta_bias", "dz")],
         nb, nd, H, W, ns, dt, _ptr(workspace), _nbytes(workspace), _stream(stream, dev)))
     return g
+
+
+def conv1d_silu_fwd(x, conv_w, conv_b, conv_w_b=None, conv_b_b=None, u=None, u_b=None, stream=None):
+    """Front of the Vim scan (vmscan_conv1d_silu_fwd): u = silu(causal depthwise conv1d(x) + conv_b)
+    and, when conv_w_b / conv_b_b are given, u_b = the flipped branch's convolution in original
+    token order.  x: [batch, dim, L] float32 or bfloat16; conv_w(_b): [dim, d_conv] float32
+    (d_conv 1..4); conv_b(_b): [dim] float32.  Returns (u, u_b), u_b None for one branch."""
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, dim, L]")
+    nb, nd, L = x.shape
+    dev, adt, dt = x.device, x.dtype, _act_dtype(x)
+    if conv_w.dim() != 2:
+        raise ValueError("conv_w must be [dim, d_conv]")
+    K = int(conv_w.shape[1])
+    _need(conv_w, "conv_w", (nd, K), torch.float32, dev)
+    _need(conv_b, "conv_b", (nd,), torch.float32, dev)
+    two = conv_w_b is not None or conv_b_b is not None
+    if two:
+        _need(conv_w_b, "conv_w_b", (nd, K), torch.float32, dev)
+        _need(conv_b_b, "conv_b_b", (nd,), torch.float32, dev)
+    if u is None:
+        u = torch.empty_like(x)
+    _need(u, "u", (nb, nd, L), adt, dev)
+    if two:
+        if u_b is None:
+            u_b = torch.empty_like(x)
+        _need(u_b, "u_b", (nb, nd, L), adt, dev)
+    else:
+        u_b = None
+    _check(load().vmscan_conv1d_silu_fwd(_ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(conv_w_b), _ptr(conv_b_b),
+                                         _ptr(u), _ptr(u_b), nb, nd, L, K, dt, _stream(stream, dev)))
+    return u, u_b
+
+
+def ss2d_conv2d_silu_fwd(x, conv_w, conv_b, act=True, transposed=True, x_out=None, xT_out=None, stream=None):
+    """Front of SS2D (ss2d_conv2d_silu_fwd): depthwise 3 x 3 convolution (+ SiLU when ``act``) of
+    x [batch, dim, H, W]; conv_w [dim, 3, 3], conv_b [dim] float32.  Returns (x_out, xT_out):
+    the result row-major and, when ``transposed``, also as [batch, dim, W, H]."""
+    if x.dim() != 4:
+        raise ValueError("x must be [batch, dim, H, W]")
+    nb, nd, H, W = x.shape
+    dev, adt, dt = x.device, x.dtype, _act_dtype(x)
+    if conv_w.dim() != 3:
+        raise ValueError("conv_w must be [dim, K, K]")
+    K = int(conv_w.shape[1])
+    _need(conv_w, "conv_w", (nd, K, K), torch.float32, dev)
+    _need(conv_b, "conv_b", (nd,), torch.float32, dev)
+    if x_out is None:
+        x_out = torch.empty_like(x)
+    _need(x_out, "x_out", (nb, nd, H, W), adt, dev)
+    if transposed:
+        if xT_out is None:
+            xT_out = torch.empty((nb, nd, W, H), dtype=adt, device=dev)
+        _need(xT_out, "xT_out", (nb, nd, W, H), adt, dev)
+    else:
+        xT_out = None
+    _check(load().ss2d_conv2d_silu_fwd(_ptr(x), _ptr(conv_w), _ptr(conv_b), int(bool(act)), _ptr(x_out),
+                                       _ptr(xT_out), nb, nd, H, W, K, dt, _stream(stream, dev)))
+    return x_out, xT_out
 
 
 def fwd_bidir_chunk_len(batch, dim, seqlen, d_state=D_STATE):

@@ -231,7 +231,6 @@ __global__ __launch_bounds__(kTransThreads) void bc_transpose_kernel(ScanArgs a)
   const int64_t si = da.rev ? a.L - 1 - s : s;
   const T* bb = static_cast<const T*>(da.B) + static_cast<int64_t>(b) * da.bc_bs + si;
   const T* cb = static_cast<const T*>(da.C) + static_cast<int64_t>(b) * da.bc_bs + si;
-#pragma unroll
   for (int q = 0; q < a.parts; ++q) {
     float v[kBC];
 #pragma unroll
@@ -972,6 +971,312 @@ __global__ __launch_bounds__(2 * kW * NP) void scan_pair_kernel(ScanArgs a) {
     scan_pair_dir<T, MODE, 1, NP>(a, l, ybuf, ybs, unit_flag[1], epi);
   __syncthreads();
   pair_epilogue<T, MODE, NP>(a, l, ybuf, ybs, epi);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Front convolutions: the local mixing that produces the scan input.  Both are streaming kernels
+// bound by HBM: the scans are bound by the vector ALU, so recomputing the convolution and SiLU
+// in every wave of a scan would cost more issue slots than one pass over the activations, and the
+// projections that make Δ, B and C need the convolved activations anyway.
+
+constexpr int kConvMax = 4;  // widest conv1d
+
+// Taps of one channel's width-K filter placed in a width-4 window: causal, tap k multiplies
+// x[t - 3 + k] (the filter sits at the right end); reversed, tap i multiplies x[t + i]
+// (w[K - 1 - i]).  Width 4 is one 16-byte load (the weights start 16-byte aligned).
+__device__ __forceinline__ void conv_taps(const float* w, int64_t d, int K, bool rev, float (&t)[kConvMax]) {
+  if (K == kConvMax) {
+    const float4 q = *reinterpret_cast<const float4*>(w + d * kConvMax);
+    const float v[kConvMax] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int k = 0; k < kConvMax; ++k) t[k] = v[rev ? kConvMax - 1 - k : k];
+    return;
+  }
+#pragma unroll
+  for (int k = 0; k < kConvMax; ++k) {
+    if (rev) t[k] = k < K ? w[d * K + K - 1 - k] : 0.0f;
+    else t[k] = k >= kConvMax - K ? w[d * K + k - (kConvMax - K)] : 0.0f;
+  }
+}
+
+// Vim: u = silu(b + Σ_k w[k] x[t - (K-1) + k]) (causal, the forward branch) and
+// u_b = silu(b_b + Σ_k w_b[k] x[t + (K-1) - k]) (the flipped branch's causal convolution, in
+// original token order), depthwise, from one read of x.
+//
+// A workgroup owns a contiguous span of the flat [rows][L] tensor: whole rows when a row has at
+// most 256 runs of 8 positions (kRowsPerBlock rows), else 256 runs of one row.  The span and
+// 3 positions on each side are staged in LDS with aligned 16-byte loads; each thread then
+// computes one run of 8 positions of one row from LDS (positions outside its row read as zero, so
+// the taps need no masks and a run has one channel), writes its results back to LDS, and the
+// span is stored with aligned 16-byte stores (element stores only in the span's first and last
+// 8-element blocks).  Every global access of a wave is thus full-width and aligned; the run
+// arithmetic is 4 FMAs and a SiLU per output.
+constexpr int kFrontRuns = 256;                      // runs per workgroup
+constexpr int kFrontSpan = kFrontRuns * kWin;        // positions per workgroup, at most
+constexpr int kFrontIn = kFrontSpan + 2 * kWin + 8;  // staged input, aligned start, both halos
+
+template <typename T>
+__global__ __launch_bounds__(kFrontRuns) void conv1d_front_kernel(
+    const T* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
+    const float* __restrict__ w_b, const float* __restrict__ bias_b, T* __restrict__ u, T* __restrict__ u_b, int rows,
+    int dim, int L, int K, int rpr, int rows_per_block, int blocks_per_row, float inv_rpr) {
+  constexpr int kHalo = kConvMax - 1;
+  __shared__ __attribute__((aligned(16))) float xin[kFrontIn];
+  __shared__ __attribute__((aligned(16))) T yout[2][kFrontSpan + 2 * kWin];
+  const int tid = threadIdx.x;
+  const int64_t total = static_cast<int64_t>(rows) * L;
+  // this workgroup's rows / runs and this thread's run
+  int row, t0;
+  int64_t S, E;  // flat span [S, E)
+  bool active;
+  if (rows_per_block > 0) {
+    const int r0 = static_cast<int>(blockIdx.x) * rows_per_block;
+    const int nr = rows - r0 < rows_per_block ? rows - r0 : rows_per_block;
+    // tid / rpr for tid < 256: the float quotient is within 1e-5 of (tid + 0.5) / rpr, at least
+    // 0.5 / rpr from an integer
+    const int lr = static_cast<int>((static_cast<float>(tid) + 0.5f) * inv_rpr);
+    row = r0 + lr;
+    t0 = (tid - lr * rpr) * kWin;
+    active = lr < nr;
+    S = static_cast<int64_t>(r0) * L;
+    E = static_cast<int64_t>(r0 + nr) * L;
+  } else {
+    row = static_cast<int>(blockIdx.x) / blocks_per_row;
+    const int seg = static_cast<int>(blockIdx.x) - row * blocks_per_row;
+    t0 = (seg * kFrontRuns + tid) * kWin;
+    active = t0 < L;
+    S = static_cast<int64_t>(row) * L + static_cast<int64_t>(seg) * kFrontSpan;
+    const int64_t seg_end = static_cast<int64_t>(seg + 1) * kFrontSpan;
+    E = static_cast<int64_t>(row) * L + (seg_end < L ? seg_end : L);
+  }
+  // the run's filter taps and biases, requested together with the staged input
+  const int d = (active ? row : 0) % dim;
+  float tap[2][kConvMax], b0[2];
+  conv_taps(w, d, K, false, tap[0]);
+  b0[0] = bias[d];
+  if (u_b) {
+    conv_taps(w_b, d, K, true, tap[1]);
+    b0[1] = bias_b[d];
+  }
+  // stage x[A, A + 8 nchunk) with A = S - 3 rounded down to a multiple of 8
+  const int64_t A = (S - kHalo) & ~static_cast<int64_t>(kWin - 1);
+  const int nchunk = static_cast<int>((E + kHalo - A + kWin - 1) / kWin);
+  for (int c = tid; c < nchunk; c += kFrontRuns) {
+    const int64_t f = A + static_cast<int64_t>(c) * kWin;
+    float v[kWin];
+    if (f >= 0 && f + kWin <= total) {
+      Run8<T> r;
+      r.load(x + f);
+      r.template unpack<false>(v);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kWin; ++j) v[j] = f + j >= 0 && f + j < total ? ld_act(x, f + j) : 0.0f;
+    }
+    float4* dst = reinterpret_cast<float4*>(xin + c * kWin);
+    dst[0] = make_float4(v[0], v[1], v[2], v[3]);
+    dst[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+  __syncthreads();
+  const int64_t B = S & ~static_cast<int64_t>(kWin - 1);  // aligned start of the output blocks
+  if (active) {
+    const int n = L - t0 < kWin ? L - t0 : kWin;
+    const int64_t f = static_cast<int64_t>(row) * L + t0;
+    const int o = static_cast<int>(f - kHalo - A);
+    // xs[i] = x at row position t0 - 3 + i, zero outside the row
+    float xs[kWin + 2 * kHalo];
+#pragma unroll
+    for (int i = 0; i < kWin + 2 * kHalo; ++i) {
+      const int t = t0 - kHalo + i;
+      xs[i] = t >= 0 && t < L ? xin[o + i] : 0.0f;
+    }
+    const int oy = static_cast<int>(f - B);
+#pragma unroll
+    for (int br = 0; br < 2; ++br) {
+      if (br == 1 && !u_b) break;
+#pragma unroll
+      for (int j = 0; j < kWin; ++j) {
+        float acc = b0[br];
+#pragma unroll
+        for (int k = 0; k < kConvMax; ++k) acc = __builtin_fmaf(tap[br][k], xs[br == 0 ? j + k : kHalo + j + k], acc);
+        if (j < n) {
+          const float y = silu_f(acc);
+          if constexpr (sizeof(T) == 2) yout[br][oy + j] = f32_to_bf16_rne(y);
+          else yout[br][oy + j] = y;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // store [S, E) in aligned blocks of 8; the first and last block may be partly outside
+  const int nout = static_cast<int>((E - B + kWin - 1) / kWin);
+  for (int br = 0; br < 2; ++br) {
+    if (br == 1 && !u_b) break;
+    T* out = br == 0 ? u : u_b;
+    for (int c = tid; c < nout; c += kFrontRuns) {
+      const int64_t f = B + static_cast<int64_t>(c) * kWin;
+      const T* src = &yout[br][c * kWin];
+      if (f >= S && f + kWin <= E) {
+        if constexpr (sizeof(T) == 2) {
+          uint4 r;
+          __builtin_memcpy(&r, src, sizeof(r));
+          __builtin_memcpy(out + f, &r, sizeof(r));
+        } else {
+          float4 r0, r1;
+          __builtin_memcpy(&r0, src, sizeof(r0));
+          __builtin_memcpy(&r1, src + 4, sizeof(r1));
+          __builtin_memcpy(out + f, &r0, sizeof(r0));
+          __builtin_memcpy(out + f + 4, &r1, sizeof(r1));
+        }
+      } else {
+        for (int j = 0; j < kWin; ++j)
+          if (f + j >= S && f + j < E) out[f + j] = src[j];
+      }
+    }
+  }
+}
+
+// SS2D: x' = act(b + Σ_{a,c} w[a][c] x[i - 1 + a][j - 1 + c]) (3 x 3, depthwise, zero padding),
+// written both row-major (the row scans) and transposed (the column scans), from one read of x.
+// One workgroup per 64 x 64 tile of one image.  The tile and its one-pixel border are staged in
+// LDS as float (all of a thread's loads issued before any is used; an image that is a single
+// aligned tile, like 56 x 56, is read as one flat run of 16-byte blocks); each thread computes a strip
+// of 16 rows of one column, sliding the 3 x 3 window down in registers (3 LDS reads per pixel);
+// the results then replace the input tile in LDS, and both copies are stored from there in pairs
+// of neighbouring elements (one 4-byte store per pair when aligned), rows of the tile for the
+// row-major copy and columns for the transposed one.  One LDS tile per workgroup keeps eight
+// workgroups resident per CU.
+template <typename T>
+__device__ __forceinline__ void store_pair(T* p, int64_t e, float v0, float v1, bool two) {
+  if (!two) {
+    st_act(p, e, v0);
+    return;
+  }
+  if constexpr (sizeof(T) == 2) {
+    if ((e & 1) == 0) {
+      *reinterpret_cast<uint32_t*>(p + e) =
+          static_cast<uint32_t>(f32_to_bf16_rne(v0)) | (static_cast<uint32_t>(f32_to_bf16_rne(v1)) << 16);
+      return;
+    }
+  } else {
+    if ((e & 1) == 0) {
+      *reinterpret_cast<float2*>(p + e) = make_float2(v0, v1);
+      return;
+    }
+  }
+  st_act(p, e, v0);
+  st_act(p, e + 1, v1);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void conv2d_front_kernel(const T* __restrict__ x, const float* __restrict__ w,
+                                                           const float* __restrict__ bias, int act,
+                                                           T* __restrict__ xo, T* __restrict__ xto, int dim, int H,
+                                                           int W, int tiles_r, int tiles_c) {
+  constexpr int kIn = kTile + 2;
+  constexpr int kInS = kIn + 1;        // input tile row stride
+  constexpr int kOutS = kTile + 1;     // output tile row stride (same storage)
+  constexpr int kLoads = (kIn * kIn + 255) / 256;
+  constexpr int kStrip = kTile / 4;    // rows per thread
+  __shared__ float tile[kIn * kInS];
+  const int64_t blk = blockIdx.x;
+  const int tc = static_cast<int>(blk % tiles_c);
+  const int tr = static_cast<int>((blk / tiles_c) % tiles_r);
+  const int64_t img = blk / (static_cast<int64_t>(tiles_c) * tiles_r);
+  const int d = static_cast<int>(img % dim);
+  const int64_t base = img * H * W;
+  const int r0 = tr * kTile, c0 = tc * kTile;
+  float wk[9];
+#pragma unroll
+  for (int k = 0; k < 9; ++k) wk[k] = w[static_cast<int64_t>(d) * 9 + k];
+  const float b = bias[d];
+  if (tiles_r == 1 && tiles_c == 1 && (base & (kWin - 1)) == 0) {
+    // The image is one tile and starts 8-element aligned: read it as one flat run of aligned
+    // 8-element blocks (its tail element by element) and zero the tile cells outside it.
+    const int hw = H * W, nblk = hw / kWin;
+    for (int c = threadIdx.x; c < nblk; c += 256) {
+      Run8<T> r;
+      r.load(x + base + c * kWin);
+      float v[kWin];
+      r.template unpack<false>(v);
+#pragma unroll
+      for (int j = 0; j < kWin; ++j) {
+        const int e = c * kWin + j, rr = e / W;
+        tile[(rr + 1) * kInS + e - rr * W + 1] = v[j];
+      }
+    }
+    for (int e = nblk * kWin + threadIdx.x; e < hw; e += 256) {
+      const int rr = e / W;
+      tile[(rr + 1) * kInS + e - rr * W + 1] = ld_act(x, base + e);
+    }
+    for (int idx = threadIdx.x; idx < kIn * kIn; idx += 256) {
+      const int r = idx / kIn, c = idx - (idx / kIn) * kIn;
+      if (r == 0 || c == 0 || r > H || c > W) tile[r * kInS + c] = 0.0f;
+    }
+  } else {
+    float ld[kLoads];
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) {
+      const int idx = static_cast<int>(threadIdx.x) + 256 * k;
+      const int r = idx / kIn, c = idx - (idx / kIn) * kIn;
+      const int gr = r0 - 1 + r, gc = c0 - 1 + c;
+      const bool in = idx < kIn * kIn && gr >= 0 && gr < H && gc >= 0 && gc < W;
+      ld[k] = in ? ld_act(x, base + static_cast<int64_t>(gr) * W + gc) : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) {
+      const int idx = static_cast<int>(threadIdx.x) + 256 * k;
+      if (idx < kIn * kIn) tile[(idx / kIn) * kInS + idx - (idx / kIn) * kIn] = ld[k];
+    }
+  }
+  __syncthreads();
+  const int tx = threadIdx.x & (kTile - 1), ty = threadIdx.x >> 6;
+  const int i0 = ty * kStrip;
+  float a0[3], a1[3], a2[3], v[kStrip];
+#pragma unroll
+  for (int c = 0; c < 3; ++c) {
+    a0[c] = tile[i0 * kInS + tx + c];
+    a1[c] = tile[(i0 + 1) * kInS + tx + c];
+  }
+#pragma unroll
+  for (int k = 0; k < kStrip; ++k) {
+#pragma unroll
+    for (int c = 0; c < 3; ++c) a2[c] = tile[(i0 + k + 2) * kInS + tx + c];
+    float acc = b;
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+      acc = __builtin_fmaf(wk[c], a0[c], acc);
+      acc = __builtin_fmaf(wk[3 + c], a1[c], acc);
+      acc = __builtin_fmaf(wk[6 + c], a2[c], acc);
+    }
+    v[k] = act ? silu_f(acc) : acc;
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+      a0[c] = a1[c];
+      a1[c] = a2[c];
+    }
+  }
+  __syncthreads();  // every read of the input tile is done
+#pragma unroll
+  for (int k = 0; k < kStrip; ++k) tile[(i0 + k) * kOutS + tx] = v[k];
+  __syncthreads();
+  // row-major copy: pair p = (row i, columns 2q, 2q + 1); 64 x 32 pairs, 8 per thread
+  const int q = threadIdx.x & 31, i1 = threadIdx.x >> 5;
+#pragma unroll
+  for (int k = 0; k < kTile / 8; ++k) {
+    const int i = i1 + 8 * k, gr = r0 + i, gc = c0 + 2 * q;
+    if (gr < H && gc < W)
+      store_pair(xo, base + static_cast<int64_t>(gr) * W + gc, tile[i * kOutS + 2 * q], tile[i * kOutS + 2 * q + 1],
+                 gc + 1 < W);
+  }
+  if (!xto) return;
+  // transposed copy [W][H]: pair = (column c, rows 2q, 2q + 1)
+#pragma unroll
+  for (int k = 0; k < kTile / 8; ++k) {
+    const int c = i1 + 8 * k, gc = c0 + c, gr = r0 + 2 * q;
+    if (gc < W && gr < H)
+      store_pair(xto, base + static_cast<int64_t>(gc) * H + gr, tile[2 * q * kOutS + c], tile[(2 * q + 1) * kOutS + c],
+                 gr + 1 < H);
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1990,11 +2295,13 @@ size_t ss2d_cross_scan_workspace_bytes(int64_t batch, int64_t dim, int64_t H, in
   return ss2d_cross_scan_workspace_bytes_ex(batch, dim, H, W, d_state, dtype, 0);
 }
 
-vmscan_status ss2d_cross_scan_fwd_ex(const void* x, const void* delta_raw, const float* A_log, const void* B,
-                                     const void* C, const float* D, const float* delta_bias, const void* z,
-                                     void* out, int64_t batch, int64_t dim, int64_t H, int64_t W, int d_state,
-                                     vmscan_dtype dtype, void* workspace, size_t workspace_bytes,
-                                     int64_t chunk_len, hipStream_t stream) {
+namespace {
+
+// The SS2D forward with x's transposed copy either made here (xT NULL) or given by the caller.
+vmscan_status ss2d_fwd_impl(const void* x, const void* xT, const void* delta_raw, const float* A_log, const void* B,
+                            const void* C, const float* D, const float* delta_bias, const void* z, void* out,
+                            int64_t batch, int64_t dim, int64_t H, int64_t W, int d_state, vmscan_dtype dtype,
+                            void* workspace, size_t workspace_bytes, int64_t chunk_len, hipStream_t stream) {
   const void* ptrs[] = {x, delta_raw, A_log, B, C, D, delta_bias, out};
   for (const void* p : ptrs)
     if (!p) return VMSCAN_ERR_NULL;
@@ -2004,7 +2311,7 @@ vmscan_status ss2d_cross_scan_fwd_ex(const void* x, const void* delta_raw, const
   if (!d_state_ok(d_state) || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16)) return VMSCAN_ERR_UNSUPPORTED;
   for (const void* p : ptrs)
     if (!aligned16(p)) return VMSCAN_ERR_ALIGN;
-  if (z && !aligned16(z)) return VMSCAN_ERR_ALIGN;
+  if ((z && !aligned16(z)) || (xT && !aligned16(xT))) return VMSCAN_ERR_ALIGN;
   const size_t need = ss2d_cross_scan_workspace_bytes_ex(batch, dim, H, W, d_state, dtype, chunk_len);
   const vmscan_status ws = check_workspace(workspace, workspace_bytes, need);
   if (ws != VMSCAN_OK) return ws;
@@ -2043,11 +2350,15 @@ vmscan_status ss2d_cross_scan_fwd_ex(const void* x, const void* delta_raw, const
   // Column pair (direction 1 = column-major order, direction 3 = its reverse) over the transposed
   // image x^T [W][H], whose rows are x's columns: position p = w*H + h is x^T's element p.  It
   // writes its combined values as an fp32 image in the same column-major order.
-  vmscan_status st = launch_transpose(x, wsp + lay.xt, nimg, static_cast<int>(H), static_cast<int>(W), esz, stream);
-  if (st != VMSCAN_OK) return st;
+  vmscan_status st = VMSCAN_OK;
+  if (!xT) {
+    st = launch_transpose(x, wsp + lay.xt, nimg, static_cast<int>(H), static_cast<int>(W), esz, stream);
+    if (st != VMSCAN_OK) return st;
+    xT = wsp + lay.xt;
+  }
   a.wsy = reinterpret_cast<float*>(wsp + lay.col_img);
-  a.d0 = dir_args(wsp + lay.xt, 1, 0);
-  a.d1 = dir_args(wsp + lay.xt, 3, 1);
+  a.d0 = dir_args(xT, 1, 0);
+  a.d1 = dir_args(xT, 3, 1);
   st = run_pair_dtype<kModeFirstPair>(a, dtype, stream);
   if (st != VMSCAN_OK) return st;
   // Back to row-major pixels, then the row pair (direction 0 and its reverse, direction 2) adds
@@ -2060,6 +2371,95 @@ vmscan_status ss2d_cross_scan_fwd_ex(const void* x, const void* delta_raw, const
   a.d0 = dir_args(x, 0, 0);
   a.d1 = dir_args(x, 2, 1);
   return run_pair_dtype<kModeSecondPair>(a, dtype, stream);
+}
+
+}  // namespace
+
+vmscan_status ss2d_cross_scan_fwd_ex(const void* x, const void* delta_raw, const float* A_log, const void* B,
+                                     const void* C, const float* D, const float* delta_bias, const void* z,
+                                     void* out, int64_t batch, int64_t dim, int64_t H, int64_t W, int d_state,
+                                     vmscan_dtype dtype, void* workspace, size_t workspace_bytes,
+                                     int64_t chunk_len, hipStream_t stream) {
+  return ss2d_fwd_impl(x, nullptr, delta_raw, A_log, B, C, D, delta_bias, z, out, batch, dim, H, W, d_state, dtype,
+                       workspace, workspace_bytes, chunk_len, stream);
+}
+
+vmscan_status ss2d_cross_scan_fwd_xt(const void* x, const void* xT, const void* delta_raw, const float* A_log,
+                                     const void* B, const void* C, const float* D, const float* delta_bias,
+                                     const void* z, void* out, int64_t batch, int64_t dim, int64_t H, int64_t W,
+                                     int d_state, vmscan_dtype dtype, void* workspace, size_t workspace_bytes,
+                                     int64_t chunk_len, hipStream_t stream) {
+  if (!xT) return VMSCAN_ERR_NULL;
+  return ss2d_fwd_impl(x, xT, delta_raw, A_log, B, C, D, delta_bias, z, out, batch, dim, H, W, d_state, dtype,
+                       workspace, workspace_bytes, chunk_len, stream);
+}
+
+vmscan_status vmscan_conv1d_silu_fwd(const void* x, const float* conv_w, const float* conv_b, const float* conv_w_b,
+                                     const float* conv_b_b, void* u, void* u_b, int64_t batch, int64_t dim,
+                                     int64_t seqlen, int d_conv, vmscan_dtype dtype, hipStream_t stream) {
+  if (!x || !conv_w || !conv_b || !u) return VMSCAN_ERR_NULL;
+  // the backward branch's weights, bias and output come together
+  const int nb_set = (conv_w_b != nullptr) + (conv_b_b != nullptr) + (u_b != nullptr);
+  if (nb_set != 0 && nb_set != 3) return VMSCAN_ERR_NULL;
+  if (!shape_ok(batch, dim, seqlen)) return VMSCAN_ERR_SHAPE;
+  if (d_conv < 1 || d_conv > kConvMax || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16)) return VMSCAN_ERR_UNSUPPORTED;
+  const void* ptrs[] = {x, conv_w, conv_b, conv_w_b, conv_b_b, u, u_b};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return VMSCAN_ERR_ALIGN;
+  // a workgroup per kFrontRuns runs: whole rows when a row has at most kFrontRuns runs
+  if (batch * dim >= (int64_t{1} << 31) || seqlen >= (int64_t{1} << 30)) return VMSCAN_ERR_SHAPE;
+  const int rows = static_cast<int>(batch * dim), Li = static_cast<int>(seqlen), di = static_cast<int>(dim);
+  const int rpr = static_cast<int>(ceil_div(seqlen, kWin));
+  int rows_per_block = 0, blocks_per_row = 0;
+  int64_t blocks;
+  if (rpr <= kFrontRuns) {
+    rows_per_block = kFrontRuns / rpr;
+    blocks = ceil_div(rows, rows_per_block);
+  } else {
+    blocks_per_row = static_cast<int>(ceil_div(rpr, kFrontRuns));
+    blocks = static_cast<int64_t>(rows) * blocks_per_row;
+  }
+  if (blocks >= (int64_t{1} << 31)) return VMSCAN_ERR_SHAPE;
+  const dim3 grid(static_cast<unsigned>(blocks));
+  const float inv = 1.0f / static_cast<float>(rpr);
+  if (dtype == VMSCAN_F32)
+    hipLaunchKernelGGL(conv1d_front_kernel<float>, grid, dim3(kFrontRuns), 0, stream, static_cast<const float*>(x),
+                       conv_w, conv_b, conv_w_b, conv_b_b, static_cast<float*>(u), static_cast<float*>(u_b), rows, di,
+                       Li, d_conv, rpr, rows_per_block, blocks_per_row, inv);
+  else
+    hipLaunchKernelGGL(conv1d_front_kernel<uint16_t>, grid, dim3(kFrontRuns), 0, stream,
+                       static_cast<const uint16_t*>(x), conv_w, conv_b, conv_w_b, conv_b_b, static_cast<uint16_t*>(u),
+                       static_cast<uint16_t*>(u_b), rows, di, Li, d_conv, rpr, rows_per_block, blocks_per_row, inv);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? VMSCAN_OK : launch_failed(e);
+}
+
+vmscan_status ss2d_conv2d_silu_fwd(const void* x, const float* conv_w, const float* conv_b, int act, void* x_out,
+                                   void* xT_out, int64_t batch, int64_t dim, int64_t H, int64_t W, int d_conv,
+                                   vmscan_dtype dtype, hipStream_t stream) {
+  if (!x || !conv_w || !conv_b || !x_out) return VMSCAN_ERR_NULL;
+  if (H < 1 || W < 1 || H >= (int64_t{1} << 31) || W >= (int64_t{1} << 31)) return VMSCAN_ERR_SHAPE;
+  if (!shape_ok(batch, dim, H * W)) return VMSCAN_ERR_SHAPE;
+  if (d_conv != 3 || (act != 0 && act != 1) || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16))
+    return VMSCAN_ERR_UNSUPPORTED;
+  const void* ptrs[] = {x, conv_w, conv_b, x_out, xT_out};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return VMSCAN_ERR_ALIGN;
+  const int tr = static_cast<int>(ceil_div(H, kTile)), tc = static_cast<int>(ceil_div(W, kTile));
+  const int64_t blocks = batch * dim * tr * tc;
+  if (blocks >= (int64_t{1} << 31)) return VMSCAN_ERR_SHAPE;
+  if (dtype == VMSCAN_F32)
+    hipLaunchKernelGGL(conv2d_front_kernel<float>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                       static_cast<const float*>(x), conv_w, conv_b, act, static_cast<float*>(x_out),
+                       static_cast<float*>(xT_out), static_cast<int>(dim), static_cast<int>(H), static_cast<int>(W),
+                       tr, tc);
+  else
+    hipLaunchKernelGGL(conv2d_front_kernel<uint16_t>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(x), conv_w, conv_b, act, static_cast<uint16_t*>(x_out),
+                       static_cast<uint16_t*>(xT_out), static_cast<int>(dim), static_cast<int>(H),
+                       static_cast<int>(W), tr, tc);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? VMSCAN_OK : launch_failed(e);
 }
 
 size_t ss2d_cross_scan_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t H, int64_t W, int d_state,

@@ -9,5 +9,7 @@ from .vmscan_inputs import (  # noqa: F401
     make_vim_inputs,
     make_vim_v2_inputs,
     make_ss2d_inputs,
+    make_conv1d_inputs,
+    make_conv2d_inputs,
     dt_bias,
 )

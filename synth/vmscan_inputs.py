@@ -11,9 +11,13 @@ any layer can be regenerated independently.  Distributions follow the workloads:
 * Δ bias = inverse softplus of dt, dt log-uniform on [1e-3, 1e-1], computed in float64 and
   stored as float32 (the dt initialisation range stated for SS2D).
 
+* Front convolutions: the pre-convolution activation x ~ N(0, 1) like the others; weights and
+  bias uniform on [-1/sqrt(fan_in), 1/sqrt(fan_in)] with fan_in = d_conv (conv1d) or d_conv^2
+  (depthwise conv2d), the default initialisation of a convolution layer.
+
 Tensor ids: Vim u=0, z=1, Δ_raw=2, B=3, C=4, B_b=5, C_b=6, dt=7 and, for a separate backward
 branch, u_b=8, Δ_raw_b=9, dt_b=17; SS2D x=0, z=1 and, for direction k, Δ_raw=10k+2, B=10k+3,
-C=10k+4, dt=10k+7.
+C=10k+4, dt=10k+7.  Front convolutions: x=50, conv_w=51, conv_b=52, conv_w_b=53, conv_b_b=54.
 """
 import numpy as np
 
@@ -124,3 +128,45 @@ def make_ss2d_inputs(cfg=4, layer=0, batch=None, dim=None, H=None, W=None, d_sta
         dtype=dt,
     )
     return out
+
+
+def _uniform(cfg, layer, tid, shape, bound):
+    return _rng(cfg, layer, tid).uniform(-bound, bound, size=shape).astype(np.float32)
+
+
+def make_conv1d_inputs(cfg=1, layer=0, batch=None, dim=None, seqlen=None, d_conv=4, dtype=None):
+    """Inputs of the Vim front convolution: x [batch, dim, L] (pre-convolution activation) and
+    both branches' depthwise weights [dim, d_conv] and biases [dim]."""
+    c = CONFIGS[cfg]
+    nb = c["batch"] if batch is None else batch
+    nd = c["dim"] if dim is None else dim
+    L = c["seqlen"] if seqlen is None else seqlen
+    dt = c["dtype"] if dtype is None else dtype
+    bound = 1.0 / np.sqrt(d_conv)
+    return dict(
+        x=_normal(cfg, layer, 50, (nb, nd, L), dt),
+        conv_w=_uniform(cfg, layer, 51, (nd, d_conv), bound),
+        conv_b=_uniform(cfg, layer, 52, (nd,), bound),
+        conv_w_b=_uniform(cfg, layer, 53, (nd, d_conv), bound),
+        conv_b_b=_uniform(cfg, layer, 54, (nd,), bound),
+        dtype=dt,
+    )
+
+
+def make_conv2d_inputs(cfg=4, layer=0, batch=None, dim=None, H=None, W=None, d_conv=3, dtype=None):
+    """Inputs of the SS2D front convolution: x [batch, dim, H, W] (pre-convolution activation),
+    depthwise weights [dim, d_conv, d_conv] and bias [dim]."""
+    c = CONFIGS[cfg]
+    nb = c["batch"] if batch is None else batch
+    nd = c["dim"] if dim is None else dim
+    h = c["H"] if H is None else H
+    w = c["W"] if W is None else W
+    dt = c["dtype"] if dtype is None else dtype
+    bound = 1.0 / d_conv
+    return dict(
+        x=_normal(cfg, layer, 50, (nb, nd, h, w), dt),
+        conv_w=_uniform(cfg, layer, 51, (nd, d_conv, d_conv), bound),
+        conv_b=_uniform(cfg, layer, 52, (nd,), bound),
+        dtype=dt,
+    )
+

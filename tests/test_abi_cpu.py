@@ -247,3 +247,67 @@ def test_bwd_d_state_16_only(lib):
     ss = [VP(p) for p in _good_ptrs(17)] + [I64(2), I64(16), I64(4), I64(5), ctypes.c_int(32), ctypes.c_int(1),
                                             VP(0x100000), ctypes.c_size_t(1 << 30), VP(0)]
     assert lib.ss2d_cross_scan_bwd(*ss) == ERR_UNSUPPORTED
+
+
+def _c1(lib, ptrs, nb=2, nd=16, L=8, K=4, dt=1):
+    args = [VP(p) for p in ptrs] + [I64(nb), I64(nd), I64(L), ctypes.c_int(K), ctypes.c_int(dt), VP(0)]
+    return lib.vmscan_conv1d_silu_fwd(*args)
+
+
+def test_conv1d_front_errors(lib):
+    for i in (0, 1, 2, 5):
+        p = _good_ptrs(7)
+        p[i] = 0
+        assert _c1(lib, p) == ERR_NULL, i
+    for i in (3, 4, 6):  # one of the backward branch's three pointers missing
+        p = _good_ptrs(7)
+        p[i] = 0
+        assert _c1(lib, p) == ERR_NULL, i
+    assert _c1(lib, _good_ptrs(7), L=0) == ERR_SHAPE
+    assert _c1(lib, _good_ptrs(7), nb=-1) == ERR_SHAPE
+    for K in (0, 5, -1):
+        assert _c1(lib, _good_ptrs(7), K=K) == ERR_UNSUPPORTED, K
+    assert _c1(lib, _good_ptrs(7), dt=3) == ERR_UNSUPPORTED
+    for i in range(7):
+        p = _good_ptrs(7)
+        p[i] += 8
+        assert _c1(lib, p) == ERR_ALIGN, i
+
+
+def _c2(lib, ptrs, act=1, nb=2, nd=16, H=4, W=5, K=3, dt=1):
+    args = [VP(p) for p in ptrs[:3]] + [ctypes.c_int(act)] + [VP(p) for p in ptrs[3:]] + \
+        [I64(nb), I64(nd), I64(H), I64(W), ctypes.c_int(K), ctypes.c_int(dt), VP(0)]
+    return lib.ss2d_conv2d_silu_fwd(*args)
+
+
+def test_conv2d_front_errors(lib):
+    for i in range(4):
+        p = _good_ptrs(5)
+        p[i] = 0
+        assert _c2(lib, p) == ERR_NULL, i
+    assert _c2(lib, _good_ptrs(5), H=0) == ERR_SHAPE
+    assert _c2(lib, _good_ptrs(5), W=-2) == ERR_SHAPE
+    for K in (1, 2, 5):
+        assert _c2(lib, _good_ptrs(5), K=K) == ERR_UNSUPPORTED, K
+    assert _c2(lib, _good_ptrs(5), act=2) == ERR_UNSUPPORTED
+    assert _c2(lib, _good_ptrs(5), dt=2) == ERR_UNSUPPORTED
+    for i in range(5):
+        p = _good_ptrs(5)
+        p[i] += 4
+        assert _c2(lib, p) == ERR_ALIGN, i
+
+
+def test_ss2d_xt_errors(lib):
+    """The cross-scan taking x's transposed copy: NULL copy, misaligned copy, and otherwise the
+    same validation as ss2d_cross_scan_fwd_ex."""
+    def call(xt, **kw):
+        ptrs = _good_ptrs(8)
+        args = [VP(ptrs[0]), VP(xt)] + [VP(p) for p in ptrs[1:7]] + [VP(0), VP(ptrs[7])] + \
+            [I64(kw.get("nb", 2)), I64(16), I64(4), I64(5), ctypes.c_int(kw.get("ds", 16)), ctypes.c_int(1),
+             VP(0x100000), ctypes.c_size_t(1 << 30), I64(0), VP(0)]
+        return lib.ss2d_cross_scan_fwd_xt(*args)
+    assert call(0) == ERR_NULL
+    assert call(0x90004) == ERR_ALIGN
+    assert call(0x90000, nb=0) == ERR_SHAPE
+    assert call(0x90000, ds=8) == ERR_UNSUPPORTED
+
