@@ -619,8 +619,10 @@ __global__ __launch_bounds__(2 * kW * NP) void chunk_state_kernel(ScanArgs a) {
 // Carry prefix: per (batch, channel, direction, state), walk the chunks in scan order and replace
 // each chunk's record (end state from a zero start, Σ Δ2) by the state entering that chunk:
 //   h_in(first) = 0,  h_in(next) = exp2(A Σ Δ2) h_in + h_end,
-// exp(A Σ Δ) being the chunk's total decay.  One thread per (batch, channel, direction, state).
-__global__ __launch_bounds__(256) void carry_prefix_kernel(ScanArgs a) {
+// exp(A Σ Δ) being the chunk's total decay.  With `reverse` the walk runs against the scan order
+// (the adjoint records of the backward pass, whose carries flow from later chunks to earlier
+// ones).  One thread per (batch, channel, direction, state).
+__global__ __launch_bounds__(256) void carry_prefix_kernel(ScanArgs a, float* recs, int reverse) {
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int ns = a.ns, stride = ns + 1;
   const int64_t total = static_cast<int64_t>(a.batch) * a.dim * 2 * ns;
@@ -631,7 +633,8 @@ __global__ __launch_bounds__(256) void carry_prefix_kernel(ScanArgs a) {
   const int d = static_cast<int>(bd % a.dim);
   const DirArgs& da = dir == 0 ? a.d0 : a.d1;
   const float A2 = -__expf(da.A_log[static_cast<int64_t>(d) * ns + n]);  // with Σ Δ2: exp2(A Σ Δ2) = exp(A Σ Δ)
-  float* rec = a.agg + (bd * 2 + dir) * a.nch * stride;
+  float* rec = recs + (bd * 2 + dir) * a.nch * stride;
+  const bool up = (dir == 0) != (reverse != 0);  // the walk visits chunks in increasing order
   float h = 0.0f;
   // eight chunks at a time: all their loads are in flight before the dependent updates
   for (int k0 = 0; k0 < a.nch; k0 += 8) {
@@ -639,7 +642,7 @@ __global__ __launch_bounds__(256) void carry_prefix_kernel(ScanArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int k = k0 + j < a.nch ? k0 + j : a.nch - 1;
-      const float* e = rec + (dir == 0 ? k : a.nch - 1 - k) * stride;
+      const float* e = rec + (up ? k : a.nch - 1 - k) * stride;
       hend[j] = e[n];
       S[j] = e[ns];
     }
@@ -647,7 +650,7 @@ __global__ __launch_bounds__(256) void carry_prefix_kernel(ScanArgs a) {
     for (int j = 0; j < 8; ++j) {
       const int k = k0 + j;
       if (k < a.nch) {
-        rec[(dir == 0 ? k : a.nch - 1 - k) * stride + n] = h;
+        rec[(up ? k : a.nch - 1 - k) * stride + n] = h;
         if (k + 1 < a.nch) h = __builtin_fmaf(__builtin_amdgcn_exp2f(A2 * S[j]), h, hend[j]);
       }
     }
@@ -1300,8 +1303,27 @@ int64_t plan_chunk(int64_t base, int64_t L, int64_t forced) {
   const int64_t fill = ceil_div(base * nch, kSplitSlots) * kSplitSlots / base;
   if (fill > nch && ceil_div(L, fill) >= kMinChunk) nch = fill;
   int64_t K = ceil_div(L, nch);
-  if (K < kMinChunk) K = kMinChunk < L ? kMinChunk : L;
-  return K;
+  if (K < kMinChunk) K = kMinChunk;
+  // whole windows of 8 steps: no chunk but the last has a ragged window
+  K = ceil_div(K, kWin) * kWin;
+  if (K > kKSplit) K = (kKSplit / kWin) * kWin;
+  return K < L ? K : L;
+}
+
+// Backward chunks.  A split adds two passes over the sequence (the forward carries and the adjoint
+// records), which only pays when the unsplit walk would leave CUs idle: with at least one
+// workgroup per CU (kBwdSplitBelow) the sequence stays whole.  Otherwise the chunks are whole
+// multiples m of the forward's chunks Kf, so that the forward carries give the state entering
+// each, and as few as still give kBwdTargetBlocks workgroups (measured best on the 1248-pixel
+// Vim and 56 x 56 SS2D workloads among 512, 1024, 2048 and the forward's own chunks).
+constexpr int64_t kBwdSplitBelow = 256;
+constexpr int64_t kBwdTargetBlocks = 1024;
+int64_t bwd_chunk(int64_t base, int64_t L, int64_t Kf) {
+  const int64_t nch_f = ceil_div(L, Kf);
+  if (nch_f <= 1 || base >= kBwdSplitBelow) return L;
+  int64_t m = nch_f / ceil_div(kBwdTargetBlocks, base);
+  if (m < 1) m = 1;
+  return m * Kf;
 }
 
 int64_t groups(int64_t dim) { return ceil_div(dim, kW); }
@@ -1357,7 +1379,7 @@ vmscan_status run_pair_np(const ScanArgs& a, hipStream_t stream, int stages) {
       e = hipGetLastError();
       if (e != hipSuccess) return launch_failed(e);
       const int64_t pblocks = ceil_div(static_cast<int64_t>(a.batch) * a.dim * 2 * a.ns, 256);
-      hipLaunchKernelGGL(carry_prefix_kernel, dim3(static_cast<unsigned>(pblocks)), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL(carry_prefix_kernel, dim3(static_cast<unsigned>(pblocks)), dim3(256), 0, stream, a, a.agg, 0);
       e = hipGetLastError();
       if (e != hipSuccess) return launch_failed(e);
     }
@@ -1491,14 +1513,18 @@ constexpr int kRedStride = kRedCols + 4;  // floats per LDS row (16-byte aligned
 constexpr int kParStride = 16;            // per (batch, direction, half, channel): dA[8], dD, dbias
 
 struct BwdArgs {
-  ScanArgs s;       // forward arguments: B/C copy (bct), per-direction u, Δ_raw, A_log, D, bias
+  ScanArgs s;       // forward arguments: B/C copy (bct), per-direction u, Δ_raw, A_log, D, bias; the
+                    // chunking (K, nch) and, for split sequences, the forward carries (agg: the state
+                    // entering each chunk)
   const float* g;   // [batch][dim][L]: dout silu(z) / 2
-  float* ck;        // [batch][dir][half][nwin][dim][8]: state entering each window
+  float* ck;        // [batch][dir][half][nch * wpc][dim][8]: state entering each window of each chunk
+  float* adj;       // split sequences: [batch][dim][dir][nch][kN + 1] adjoint records, then carries
   float* gu;        // [dir][half][batch][dim][L]: the half's share of du
   float* gx;        // [dir][half][batch][dim][L]: the half's share of dΔ_raw
   float* dbc;       // [dir][group][batch][2][16][L]: sums over the group's channels of λ Δ2 u (dB / ln2), g h (dC)
-  float* dpar;      // [dir][half][dim][kParStride][batch]
-  int nwin;
+  float* dpar;      // [dir][half][dim][kParStride][batch * nch]
+  int wpc;          // windows per chunk, ceil(K / 8)
+  int fnch, fm;     // the forward's chunk count, and forward chunks per backward chunk
 };
 
 // g = scale dout silu(z) (float32) and dz = scale dout ysum silu'(z), silu'(z) = σ (1 + z (1 - σ)),
@@ -1588,17 +1614,29 @@ __device__ __forceinline__ void bwd_ckpt_dir(const BwdArgs& ba, const Lane& l) {
   const ScanArgs& a = ba.s;
   using Dr = Dir<MODE, DIR>;
   const DirArgs& da = DIR == 0 ? a.d0 : a.d1;
-  const int L = static_cast<int>(a.L);
+  const int L = l.Kc;  // steps of this chunk
   float A[kH];
   load_a2(da, l, a.ns, A);
   const float bias2 = da.bias[l.dd] * kLog2e;
   const scalar_fp bct = bc_row<DIR>(a, l);
-  float* ckw = ba.ck + ((static_cast<int64_t>(l.b) * 2 + DIR) * 2 + l.part) * ba.nwin * a.dim * kH;
-  auto ck_at = [&](int w) { return ckw + (static_cast<int64_t>(w) * a.dim + l.dd) * kH; };
+  float* ckw = ba.ck + ((static_cast<int64_t>(l.b) * 2 + DIR) * 2 + l.part) * a.nch * ba.wpc * a.dim * kH;
+  auto ck_at = [&](int w) {
+    return ckw + ((static_cast<int64_t>(l.c) * ba.wpc + w) * a.dim + l.dd) * kH;
+  };
   const int full_end = (L / kWin) * kWin;
   float h[kH], bcA[kBC], bcB[kBC];
+  if (ba.fnch > 1) {
+    // the state entering the chunk, left by the forward's carry prefix for its forward chunk
+    // where this direction enters: the first, or (backward direction) the last of the chunk's
+    const int last = (l.c + 1) * ba.fm < ba.fnch ? (l.c + 1) * ba.fm - 1 : ba.fnch - 1;
+    const int cf = DIR == 0 ? l.c * ba.fm : last;
+    const float* e = a.agg + ((((static_cast<int64_t>(l.b) * a.dim + l.dd) * 2 + DIR) * ba.fnch) + cf) * (kN + 1);
 #pragma unroll
-  for (int n = 0; n < kH; ++n) h[n] = 0.0f;
+    for (int n = 0; n < kH; ++n) h[n] = e[kH * l.part + n];
+  } else {
+#pragma unroll
+    for (int n = 0; n < kH; ++n) h[n] = 0.0f;
+  }
   Window<T, MODE, DIR> win;
   load_bc(bct + Dr::pos(l, 0) * kBC, bcA);
   if (full_end > 0) win.load(a, l, da, 0);
@@ -1621,14 +1659,87 @@ __global__ __launch_bounds__(kThreads) void bwd_ckpt_kernel(BwdArgs ba) {
   else bwd_ckpt_dir<T, MODE, 1>(ba, l);
 }
 
-// The adjoint walk of one direction and state half, window by window from the last.
+// Adjoint chunk records (split sequences).  Within a chunk the adjoint obeys
+//   λ_i = g_i C_i + a_{i+1} λ_{i+1}
+// and, written from its last step's successor, λ_i = λ_i^0 + (a_{i+1} ... a_{Kc-1}) μ, where λ^0 is
+// the walk started from zero and μ = a λ is what the next chunk in scan order passes back.  So each
+// chunk passes X = a_0 λ_0^0 + (a_0 ... a_{Kc-1}) μ to the previous one: a reverse carry prefix over
+// the records (X, Σ Δ2) gives every chunk its μ.  This pass computes the records: per direction and
+// state half, the walk from zero over the chunk's steps, last first (windows of 8 with the previous
+// window's loads in flight).  It needs no forward state.
+template <typename T, int MODE, int DIR>
+__device__ __forceinline__ void adj_state_dir(const BwdArgs& ba, const Lane& l) {
+  const ScanArgs& a = ba.s;
+  // The first chunk in scan order passes nothing back.
+  if (DIR == 0 ? l.c == 0 : l.c == a.nch - 1) return;
+  using Dr = Dir<MODE, DIR>;
+  constexpr bool kRevOrder = Dr::kPosSgn < 0;
+  const DirArgs& da = DIR == 0 ? a.d0 : a.d1;
+  const T* xb = static_cast<const T*>(da.draw) + static_cast<int64_t>(l.b) * da.draw_bs + static_cast<int64_t>(l.dd) * a.L;
+  const float* gb = ba.g + static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(l.dd) * a.L;
+  float A[kH];
+  load_a2(da, l, a.ns, A);
+  const float bias2 = da.bias[l.dd] * kLog2e;
+  const scalar_fp bct = bc_row<DIR>(a, l);
+  float lam[kH], anext[kH];
+#pragma unroll
+  for (int n = 0; n < kH; ++n) {
+    lam[n] = 0.0f;
+    anext[n] = 0.0f;
+  }
+  float S = 0.0f;
+  auto step = [&](float d2, float gv, scalar_fp c) {
+#pragma unroll
+    for (int n = 0; n < kH; ++n) {
+      lam[n] = __builtin_fmaf(gv, c[kH + n], anext[n] * lam[n]);
+      anext[n] = __builtin_amdgcn_exp2f(d2 * A[n]);
+    }
+    S += d2;
+  };
+  const int Kc = l.Kc, full_end = (Kc / kWin) * kWin;
+  for (int i = Kc - 1; i >= full_end; --i)
+    step(delta2(ld_act(xb, Dr::sidx(a, l, i)), bias2), gb[Dr::pos(l, i)], bct + Dr::pos(l, i) * kBC);
+  Run8<T> xw;
+  Run8<float> gw;
+  auto wload = [&](int i0) {
+    const int64_t p = Dr::pos(l, i0);
+    const int64_t si = Dr::sidx(a, l, i0);
+    xw.load(xb + (Dr::kSidxSgn > 0 ? si : si - (kWin - 1)));
+    gw.load(gb + (Dr::kPosSgn > 0 ? p : p - (kWin - 1)));
+  };
+  if (full_end > 0) wload(full_end - kWin);
+  for (int i0 = full_end - kWin; i0 >= 0; i0 -= kWin) {
+    float xr[kWin], gg[kWin];
+    xw.template unpack<(Dr::kSidxSgn < 0)>(xr);
+    gw.template unpack<kRevOrder>(gg);
+    __builtin_amdgcn_sched_barrier(0);
+    wload(i0 > 0 ? i0 - kWin : i0);
+#pragma unroll
+    for (int j = kWin - 1; j >= 0; --j) step(delta2(xr[j], bias2), gg[j], bct + Dr::pos(l, i0 + j) * kBC);
+  }
+  if (l.valid) {
+    float* rec = ba.adj + ((((static_cast<int64_t>(l.b) * a.dim + l.d) * 2 + DIR) * a.nch) + l.c) * (kN + 1);
+#pragma unroll
+    for (int n = 0; n < kH; ++n) rec[kH * l.part + n] = anext[n] * lam[n];  // X = a_0 λ_0
+    if (l.part == 0) rec[kN] = S;
+  }
+}
+
+template <typename T, int MODE>
+__global__ __launch_bounds__(kThreads) void adj_state_kernel(BwdArgs ba) {
+  const Lane l = lane_ctx(ba.s);
+  if ((__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6) & 1) == 0) adj_state_dir<T, MODE, 0>(ba, l);
+  else adj_state_dir<T, MODE, 1>(ba, l);
+}
+
+// The adjoint walk of one direction and state half over one chunk, window by window from the last.
 template <typename T, int MODE, int DIR>
 __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float* rows) {
   const ScanArgs& a = ba.s;
   using Dr = Dir<MODE, DIR>;
   constexpr bool kRevOrder = Dr::kPosSgn < 0;  // window positions descend with the step
   const DirArgs& da = DIR == 0 ? a.d0 : a.d1;
-  const int L = static_cast<int>(a.L);
+  const int L = l.Kc;  // steps of this chunk
   const T* ub = static_cast<const T*>(da.u) + static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(l.dd) * a.L;
   const T* xb = static_cast<const T*>(da.draw) + static_cast<int64_t>(l.b) * da.draw_bs + static_cast<int64_t>(l.dd) * a.L;
   const float* gb = ba.g + static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(l.dd) * a.L;
@@ -1638,8 +1749,10 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
   const float Dh = l.part == 0 ? da.Dp[l.dd] : 0.0f;
   const scalar_fp bct = bc_row<DIR>(a, l);
   const float vmask = l.valid ? 1.0f : 0.0f;  // lanes past the last channel add nothing to dB/dC
-  float* ckw = ba.ck + ((static_cast<int64_t>(l.b) * 2 + DIR) * 2 + l.part) * ba.nwin * a.dim * kH;
-  auto ck_at = [&](int w) { return ckw + (static_cast<int64_t>(w) * a.dim + l.dd) * kH; };
+  float* ckw = ba.ck + ((static_cast<int64_t>(l.b) * 2 + DIR) * 2 + l.part) * a.nch * ba.wpc * a.dim * kH;
+  auto ck_at = [&](int w) {
+    return ckw + ((static_cast<int64_t>(l.c) * ba.wpc + w) * a.dim + l.dd) * kH;
+  };
   const int full_end = (L / kWin) * kWin;
 
   // Backward, window by window from the last.
@@ -1649,17 +1762,22 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
   float* gxw = ba.gx + (DIR * 2 + l.part) * plane + row;
   const int group = l.d / kW;
   float* dbcw = ba.dbc + ((static_cast<int64_t>(DIR) * a.ngroups + group) * a.batch + l.b) * 2 * kN * a.L;
+  // The walk starts after the chunk's last step with a λ = μ, passed back by the chunks after it
+  // (zero for the last chunk in scan order and for an unsplit sequence).
   float lam[kH], anext[kH], dA[kH];
+  const float* mu = ba.adj ? ba.adj + ((((static_cast<int64_t>(l.b) * a.dim + l.dd) * 2 + DIR) * a.nch) + l.c) * (kN + 1) +
+                                 kH * l.part
+                           : nullptr;
 #pragma unroll
   for (int n = 0; n < kH; ++n) {
-    lam[n] = 0.0f;
-    anext[n] = 0.0f;
+    lam[n] = mu ? mu[n] : 0.0f;
+    anext[n] = 1.0f;
     dA[n] = 0.0f;
   }
   float dD = 0.0f, dbias = 0.0f;
   float* myrow = rows + l.lane * kRedStride;
   RevWin<T, MODE, DIR> rw;
-  const int nwin = ba.nwin;
+  const int nwin = (L + kWin - 1) / kWin;
   if (full_end > 0) rw.load(a, ub, xb, gb, ck_at(full_end / kWin - 1), l, full_end - kWin);
   for (int w = nwin - 1; w >= 0; --w) {
     const int i0 = w * kWin;
@@ -1786,12 +1904,14 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
     }
   }
   if (l.valid) {
-    // [dir][half][dim][kParStride][batch]: the batch sums read contiguous runs
-    float* pp = ba.dpar + ((static_cast<int64_t>(DIR) * 2 + l.part) * a.dim + l.d) * kParStride * a.batch + l.b;
+    // [dir][half][dim][kParStride][batch * nch]: the sums over batch and chunks read contiguous runs
+    const int64_t nbc = static_cast<int64_t>(a.batch) * a.nch;
+    float* pp = ba.dpar + ((static_cast<int64_t>(DIR) * 2 + l.part) * a.dim + l.d) * kParStride * nbc +
+                static_cast<int64_t>(l.b) * a.nch + l.c;
 #pragma unroll
-    for (int n = 0; n < kH; ++n) pp[n * a.batch] = dA[n];
-    pp[kH * a.batch] = l.part == 0 ? dD : 0.0f;
-    pp[(kH + 1) * a.batch] = dbias;
+    for (int n = 0; n < kH; ++n) pp[n * nbc] = dA[n];
+    pp[kH * nbc] = l.part == 0 ? dD : 0.0f;
+    pp[(kH + 1) * nbc] = dbias;
   }
 }
 
@@ -1910,25 +2030,60 @@ __global__ __launch_bounds__(256) void sum_planes_kernel(const float* p0, const 
   st_act(out, b * out_bstride + (i - b * n_b), s);
 }
 
+// Backward buffers that depend on the chunking (the forward's: chunks of Kf): checkpoints of every
+// window of every chunk, the adjoint records (split sequences only) and the per-chunk parameter sums.
+size_t ck_bytes(int64_t batch, int64_t dim, int64_t L, int64_t Kf) {
+  return round256(static_cast<size_t>(batch) * 2 * 2 * ceil_div(L, Kf) * ceil_div(Kf, kWin) * dim * kH * sizeof(float));
+}
+size_t dpar_bytes(int64_t batch, int64_t dim, int64_t L, int64_t Kf) {
+  return round256(static_cast<size_t>(batch) * ceil_div(L, Kf) * 2 * 2 * dim * kParStride * sizeof(float));
+}
+
 struct BwdLayout {
-  size_t bct, agg, ysum, g, ck, gu, gx, dbc, dpar, total;
+  size_t bct, agg, ysum, g, ck, adj, gu, gx, dbc, dpar, total;
 };
 
 BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t L, int64_t Kf) {
   BwdLayout w{};
   const size_t plane = round256(static_cast<size_t>(batch) * dim * L * sizeof(float));
-  const int64_t nwin = ceil_div(L, kWin);
+  const int64_t Kb = bwd_chunk(batch * groups(dim), L, Kf);
   w.bct = 0;
   w.agg = w.bct + bct_bytes(batch, L);
   w.ysum = w.agg + agg_bytes(batch, dim, L, Kf);
   w.g = w.ysum + plane;
   w.ck = w.g + plane;
-  w.gu = w.ck + round256(static_cast<size_t>(batch) * 2 * 2 * nwin * dim * kH * sizeof(float));
+  w.adj = w.ck + ck_bytes(batch, dim, L, Kb);
+  w.gu = w.adj + agg_bytes(batch, dim, L, Kb);
   w.gx = w.gu + 4 * plane;
   w.dbc = w.gx + 4 * plane;
   w.dpar = w.dbc + round256(static_cast<size_t>(2) * groups(dim) * batch * 2 * kN * L * sizeof(float));
-  w.total = w.dpar + round256(static_cast<size_t>(batch) * 2 * 2 * dim * kParStride * sizeof(float));
+  w.total = w.dpar + dpar_bytes(batch, dim, L, Kb);
   return w;
+}
+
+// Checkpoints, then (split sequences) the adjoint records and their reverse carry prefix, then the
+// adjoint walk; every kernel runs one workgroup per (batch, chunk, channel group).
+template <typename T, int MODE>
+vmscan_status launch_bwd_scans(const BwdArgs& ba, hipStream_t stream) {
+  const ScanArgs& a = ba.s;
+  const int64_t nblocks = static_cast<int64_t>(a.batch) * a.nch * a.ngroups;
+  if (nblocks >= (int64_t{1} << 31)) return VMSCAN_ERR_SHAPE;
+  const dim3 grid(static_cast<unsigned>(nblocks));
+  hipLaunchKernelGGL((bwd_ckpt_kernel<T, MODE>), grid, dim3(kThreads), 0, stream, ba);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return launch_failed(e);
+  if (a.nch > 1) {
+    hipLaunchKernelGGL((adj_state_kernel<T, MODE>), grid, dim3(kThreads), 0, stream, ba);
+    e = hipGetLastError();
+    if (e != hipSuccess) return launch_failed(e);
+    const int64_t pblocks = ceil_div(static_cast<int64_t>(a.batch) * a.dim * 2 * kN, 256);
+    hipLaunchKernelGGL(carry_prefix_kernel, dim3(static_cast<unsigned>(pblocks)), dim3(256), 0, stream, a, ba.adj, 1);
+    e = hipGetLastError();
+    if (e != hipSuccess) return launch_failed(e);
+  }
+  hipLaunchKernelGGL((bwd_scan_kernel<T, MODE>), grid, dim3(kThreads), 0, stream, ba);
+  e = hipGetLastError();
+  return e == hipSuccess ? VMSCAN_OK : launch_failed(e);
 }
 
 
@@ -1952,23 +2107,22 @@ vmscan_status run_bwd(const ScanArgs& fwd, const BwdLayout& lay, unsigned char* 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return launch_failed(e);
   BwdArgs ba{};
-  ba.s = fwd;
-  ba.s.K = static_cast<int>(fwd.L);  // one chunk: each wave walks the whole sequence
-  ba.s.nch = 1;
+  ba.s = fwd;  // the forward's carries (the state entering each forward chunk) are in agg
+  const int64_t Kb = bwd_chunk(static_cast<int64_t>(fwd.batch) * fwd.ngroups, fwd.L, fwd.K);
+  ba.s.K = static_cast<int>(Kb);
+  ba.s.nch = static_cast<int>(ceil_div(fwd.L, Kb));
+  ba.fnch = ba.s.nch > 1 ? fwd.nch : 1;  // an unsplit walk starts from zero and reads no carries
+  ba.fm = ba.s.nch > 1 ? static_cast<int>(Kb / fwd.K) : 1;
   ba.g = g;
   ba.ck = reinterpret_cast<float*>(wsp + lay.ck);
+  ba.adj = ba.s.nch > 1 ? reinterpret_cast<float*>(wsp + lay.adj) : nullptr;
   ba.gu = reinterpret_cast<float*>(wsp + lay.gu);
   ba.gx = reinterpret_cast<float*>(wsp + lay.gx);
   ba.dbc = reinterpret_cast<float*>(wsp + lay.dbc);
   ba.dpar = reinterpret_cast<float*>(wsp + lay.dpar);
-  ba.nwin = static_cast<int>(ceil_div(fwd.L, kWin));
-  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(fwd.batch) * fwd.ngroups));
-  hipLaunchKernelGGL((bwd_ckpt_kernel<T, kModeVim>), grid, dim3(kThreads), 0, stream, ba);
-  e = hipGetLastError();
-  if (e != hipSuccess) return launch_failed(e);
-  hipLaunchKernelGGL((bwd_scan_kernel<T, kModeVim>), grid, dim3(kThreads), 0, stream, ba);
-  e = hipGetLastError();
-  if (e != hipSuccess) return launch_failed(e);
+  ba.wpc = static_cast<int>(ceil_div(Kb, kWin));
+  st = launch_bwd_scans<T, kModeVim>(ba, stream);
+  if (st != VMSCAN_OK) return st;
   hipLaunchKernelGGL(bwd_combine_kernel<T>, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, stream,
                      ba.gu, ba.gx, static_cast<T*>(du), static_cast<T*>(dx), static_cast<T*>(du_b),
                      static_cast<T*>(dx_b), n);
@@ -1976,7 +2130,8 @@ vmscan_status run_bwd(const ScanArgs& fwd, const BwdLayout& lay, unsigned char* 
                      static_cast<T*>(dB), static_cast<T*>(dC), static_cast<T*>(dB_b), static_cast<T*>(dC_b), fwd.batch,
                      fwd.ngroups, fwd.L, kN * fwd.L);
   hipLaunchKernelGGL(bwd_param_kernel, dim3(static_cast<unsigned>(ceil_div(2 * fwd.dim * kN + 4 * fwd.dim, 4))), dim3(256), 0,
-                     stream, ba.dpar, A_log, A_b_log, dA_log, dA_b_log, dD, dD_b, dbias, dbias_b, fwd.batch, fwd.dim);
+                     stream, ba.dpar, A_log, A_b_log, dA_log, dA_b_log, dD, dD_b, dbias, dbias_b,
+                     fwd.batch * ba.s.nch, fwd.dim);
   e = hipGetLastError();
   return e == hipSuccess ? VMSCAN_OK : launch_failed(e);
 }
@@ -1986,23 +2141,24 @@ vmscan_status run_bwd(const ScanArgs& fwd, const BwdLayout& lay, unsigned char* 
 // un-gated sum, the row- and column-order g, the checkpoints and the partial gradients.
 struct Ss2dBwdLayout {
   Ss2dLayout f;
-  size_t ysum, g, gcol, ck, gu, gx, dbc, dpar, total;
+  size_t ysum, g, gcol, ck, adj, gu, gx, dbc, dpar, total;
 };
 
 Ss2dBwdLayout ss2d_bwd_layout(int64_t batch, int64_t dim, int64_t L, int64_t Kf, size_t esz) {
   Ss2dBwdLayout w{};
   w.f = ss2d_layout(batch, dim, L, Kf, esz);
   const size_t plane = round256(static_cast<size_t>(batch) * dim * L * sizeof(float));
-  const int64_t nwin = ceil_div(L, kWin);
+  const int64_t Kb = bwd_chunk(batch * groups(dim), L, Kf);
   w.ysum = round256(w.f.total);
   w.g = w.ysum + plane;
   w.gcol = w.g + plane;
   w.ck = w.gcol + plane;
-  w.gu = w.ck + round256(static_cast<size_t>(batch) * 2 * 2 * nwin * dim * kH * sizeof(float));
+  w.adj = w.ck + ck_bytes(batch, dim, L, Kb);
+  w.gu = w.adj + agg_bytes(batch, dim, L, Kb);
   w.gx = w.gu + 4 * plane;
   w.dbc = w.gx + 4 * plane;
   w.dpar = w.dbc + round256(static_cast<size_t>(2) * groups(dim) * batch * 2 * kN * L * sizeof(float));
-  w.total = w.dpar + round256(static_cast<size_t>(batch) * 2 * 2 * dim * kParStride * sizeof(float));
+  w.total = w.dpar + dpar_bytes(batch, dim, L, Kb);
   return w;
 }
 
@@ -2014,11 +2170,14 @@ vmscan_status ss2d_pair_bwd(BwdArgs& ba, int k0, int k1, void* ddelta_raw, void*
                             const float* A_log, float* dD, float* ddelta_bias, hipStream_t stream) {
   const ScanArgs& a = ba.s;
   const int64_t DL = static_cast<int64_t>(a.dim) * a.L;
-  vmscan_status st = run_pair<T, kModeSecondPair>(a, stream, kStagePrepare);  // B/C copy (one chunk)
+  // the pair's B/C copy and, for a split sequence, its forward carries (in the forward's chunks)
+  ScanArgs af = a;
+  af.K = ba.fnch > 1 ? static_cast<int>(a.K / ba.fm) : static_cast<int>(a.L);
+  af.nch = ba.fnch;
+  vmscan_status st = run_pair<T, kModeSecondPair>(af, stream, kStagePrepare);
   if (st != VMSCAN_OK) return st;
-  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.batch) * a.ngroups));
-  hipLaunchKernelGGL((bwd_ckpt_kernel<T, kModeSecondPair>), grid, dim3(kThreads), 0, stream, ba);
-  hipLaunchKernelGGL((bwd_scan_kernel<T, kModeSecondPair>), grid, dim3(kThreads), 0, stream, ba);
+  st = launch_bwd_scans<T, kModeSecondPair>(ba, stream);
+  if (st != VMSCAN_OK) return st;
   const int64_t n = static_cast<int64_t>(a.batch) * DL;
   const int64_t plane = n;
   T* ddr = static_cast<T*>(ddelta_raw);
@@ -2035,8 +2194,8 @@ vmscan_status ss2d_pair_bwd(BwdArgs& ba, int k0, int k1, void* ddelta_raw, void*
   const int64_t dN = static_cast<int64_t>(a.dim) * kN;
   hipLaunchKernelGGL(bwd_param_kernel, dim3(static_cast<unsigned>(ceil_div(2 * a.dim * kN + 4 * a.dim, 4))), dim3(256),
                      0, stream, ba.dpar, A_log + k0 * dN, A_log + k1 * dN, dA_log + k0 * dN, dA_log + k1 * dN,
-                     dD + k0 * a.dim, dD + k1 * a.dim, ddelta_bias + k0 * a.dim, ddelta_bias + k1 * a.dim, a.batch,
-                     a.dim);
+                     dD + k0 * a.dim, dD + k1 * a.dim, ddelta_bias + k0 * a.dim, ddelta_bias + k1 * a.dim,
+                     a.batch * a.nch, a.dim);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? VMSCAN_OK : launch_failed(e);
 }
@@ -2102,15 +2261,19 @@ vmscan_status run_ss2d_bwd(const void* x, const void* delta_raw, const float* A_
   st = launch_transpose(g, gcol, nimg, static_cast<int>(H), static_cast<int>(W), 4, stream);
   if (st != VMSCAN_OK) return st;
   BwdArgs ba{};
-  ba.s = a;
-  ba.s.K = static_cast<int>(L);  // one chunk: each wave walks the whole sequence
-  ba.s.nch = 1;
+  ba.s = a;  // each pair's forward carries (chunks of Kf) are made by its prepare stage
+  const int64_t Kb = bwd_chunk(batch * a.ngroups, L, Kf);
+  ba.s.K = static_cast<int>(Kb);
+  ba.s.nch = static_cast<int>(ceil_div(L, Kb));
+  ba.fnch = ba.s.nch > 1 ? a.nch : 1;  // an unsplit walk needs no forward carries
+  ba.fm = ba.s.nch > 1 ? static_cast<int>(Kb / Kf) : 1;
   ba.ck = reinterpret_cast<float*>(wsp + lay.ck);
+  ba.adj = ba.s.nch > 1 ? reinterpret_cast<float*>(wsp + lay.adj) : nullptr;
   ba.gu = reinterpret_cast<float*>(wsp + lay.gu);
   ba.gx = reinterpret_cast<float*>(wsp + lay.gx);
   ba.dbc = reinterpret_cast<float*>(wsp + lay.dbc);
   ba.dpar = reinterpret_cast<float*>(wsp + lay.dpar);
-  ba.nwin = static_cast<int>(ceil_div(L, kWin));
+  ba.wpc = static_cast<int>(ceil_div(Kb, kWin));
   // column pair: directions 1 and 3 over x^T with g in column order
   ba.g = gcol;
   ba.s.d0 = dir_args(xt, 1, 0);

@@ -115,6 +115,38 @@ def test_bwd_config1_full():
         _report(f"bwd config 1 {k} (all batches)", O.rel_err(got[k], v), 2e-2)
 
 
+def test_bwd_config3_chunked():
+    """The 1248-pixel Vim-Ti workload (B8 D384 L6085 bf16), whose sequence the backward pass splits
+    into the forward's chunks (checkpoints from the forward carries, adjoint carries passed back):
+    every gradient against the oracle over all eight batches."""
+    p = synth.make_vim_v2_inputs(3)
+    dout = _dout(p, 5)
+    got = run_bwd(p, dout)
+    ref = oracle_bwd(p, dout)
+    for k in GRADS:
+        _report(f"bwd config 3 {k}", O.rel_err(got[k], ref[k]), 2e-2)
+
+
+@pytest.mark.parametrize("L", [40, 64, 65, 300, 1001])
+def test_bwd_chunk_boundaries(L):
+    """Sequences split into 2 to 32 chunks, whole and ragged, with float32 inputs (tight tolerance)."""
+    p = synth.make_vim_v2_inputs(0, layer=900 + L, batch=1, dim=24, seqlen=L, dtype="f32")
+    dout = _dout(p, L)
+    got, ref = run_bwd(p, dout), oracle_bwd(p, dout)
+    for k in GRADS:
+        _report(f"bwd L={L} {k}", O.rel_err(got[k], ref[k]), 1e-5)
+
+
+def test_bwd_whole_walk_split_forward():
+    """At least one workgroup per CU (43 batches x 6 channel groups): the forward splits the
+    230-token sequence into chunks, the backward walks it whole."""
+    p = synth.make_vim_v2_inputs(0, layer=950, batch=43, dim=384, seqlen=230, dtype="f32")
+    dout = _dout(p, 9)
+    got, ref = run_bwd(p, dout), oracle_bwd(p, dout)
+    for k in GRADS:
+        _report(f"bwd whole walk {k}", O.rel_err(got[k], ref[k]), 1e-5)
+
+
 SS2D_GRADS = ("dx", "ddelta_raw", "dA_log", "dB", "dC", "dD", "ddelta_bias", "dz")
 
 
