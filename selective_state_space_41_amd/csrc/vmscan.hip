@@ -1732,9 +1732,29 @@ __global__ __launch_bounds__(kThreads) void adj_state_kernel(BwdArgs ba) {
   else adj_state_dir<T, MODE, 1>(ba, l);
 }
 
+// Per-wave LDS staging of one window's outputs, so that each is stored as runs of 8 positions
+// (32 bytes per lane) rather than one scattered 4-byte store per step: du and dΔ_raw shares
+// [2][step][lane] (conflict-free: lanes on consecutive words) and the dB/dC column sums
+// [16 (B/C, state)][step].
+constexpr int kStageFloats = 2 * kWin * kW + 2 * kH * kWin;
+
+// Store a window's 8 values v[j] (step j) at the 8 consecutive indices lo..lo+7 that the steps
+// occupy in ascending (ASC) or descending order; only the first ns steps when ns < 8.
+template <bool ASC>
+__device__ __forceinline__ void store_window(float* base, int64_t lo, const float (&v)[kWin], int ns) {
+  if (ns == kWin) {
+    float o[kWin];
+#pragma unroll
+    for (int j = 0; j < kWin; ++j) o[j] = v[ASC ? j : kWin - 1 - j];
+    store8(base + lo, o);
+    return;
+  }
+  for (int j = 0; j < ns; ++j) base[ASC ? lo + j : lo + kWin - 1 - j] = v[j];
+}
+
 // The adjoint walk of one direction and state half over one chunk, window by window from the last.
 template <typename T, int MODE, int DIR>
-__device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float* rows) {
+__device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float* rows, float* stage) {
   const ScanArgs& a = ba.s;
   using Dr = Dir<MODE, DIR>;
   constexpr bool kRevOrder = Dr::kPosSgn < 0;  // window positions descend with the step
@@ -1880,10 +1900,8 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
           const float gx = sg[j] * dd;
           dbias += j < ns ? gx : 0.0f;
           dD = __builtin_fmaf(gg[j], uu[j], dD);
-          if (l.valid && j < ns) {
-            guw[Dr::pos(l, i0 + j)] = __builtin_fmaf(d2[j], Ps, Dh * gg[j]);
-            gxw[Dr::sidx(a, l, i0 + j)] = gx;  // Δ_raw's own storage order
-          }
+          stage[j * kW + l.lane] = __builtin_fmaf(d2[j], Ps, Dh * gg[j]);  // du share
+          stage[(kWin + j) * kW + l.lane] = gx;                           // dΔ_raw share
           float4* dst = reinterpret_cast<float4*>(myrow + jj * 2 * kH);
           dst[0] = make_float4(vb[0], vb[1], vb[2], vb[3]);
           dst[1] = make_float4(vb[4], vb[5], vb[6], vb[7]);
@@ -1896,12 +1914,35 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
         const float sum = wave_column_sum(rows, l.lane);
         asm volatile("" ::: "memory");
         if (l.lane < kRedCols) {
-          const int jj = l.lane >> 4, ty = (l.lane >> 3) & 1, kk = l.lane & 7;
-          const int j = j0 + 2 * r + jj;
-          if (j < ns) dbcw[(static_cast<int64_t>(ty) * kN + kH * l.part + kk) * a.L + Dr::sidx(a, l, i0 + j)] = sum;
+          const int jj = l.lane >> 4, tk = l.lane & 15;  // tk = (B or C) * 8 + state
+          stage[2 * kWin * kW + tk * kWin + j0 + 2 * r + jj] = sum;
         }
       }
     }
+    // The window's outputs, from the staging area: a wave's LDS accesses execute in order, so every
+    // value is written before it is read here (and read before the next window overwrites it).
+    asm volatile("" ::: "memory");
+    if (l.valid) {
+      float v[kWin];
+#pragma unroll
+      for (int j = 0; j < kWin; ++j) v[j] = stage[j * kW + l.lane];
+      const int64_t plo = Dr::kPosSgn > 0 ? Dr::pos(l, i0) : Dr::pos(l, i0) - (kWin - 1);
+      store_window<(Dr::kPosSgn > 0)>(guw, plo, v, ns);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < kWin; ++j) v[j] = stage[(kWin + j) * kW + l.lane];
+      const int64_t slo = Dr::kSidxSgn > 0 ? Dr::sidx(a, l, i0) : Dr::sidx(a, l, i0) - (kWin - 1);
+      store_window<(Dr::kSidxSgn > 0)>(gxw, slo, v, ns);  // Δ_raw's own storage order
+    }
+    if (l.lane < 2 * kH) {
+      const int ty = l.lane >> 3, kk = l.lane & 7;
+      float v[kWin];
+#pragma unroll
+      for (int j = 0; j < kWin; ++j) v[j] = stage[2 * kWin * kW + l.lane * kWin + j];
+      const int64_t slo = Dr::kSidxSgn > 0 ? Dr::sidx(a, l, i0) : Dr::sidx(a, l, i0) - (kWin - 1);
+      store_window<(Dr::kSidxSgn > 0)>(dbcw + (static_cast<int64_t>(ty) * kN + kH * l.part + kk) * a.L, slo, v, ns);
+    }
+    asm volatile("" ::: "memory");
   }
   if (l.valid) {
     // [dir][half][dim][kParStride][batch * nch]: the sums over batch and chunks read contiguous runs
@@ -1918,10 +1959,11 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
 template <typename T, int MODE>
 __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdArgs ba) {
   __shared__ __attribute__((aligned(16))) float rows[4][kW * kRedStride];
+  __shared__ __attribute__((aligned(16))) float stage[4][kStageFloats];
   const Lane l = lane_ctx(ba.s);
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-  if ((w & 1) == 0) bwd_dir<T, MODE, 0>(ba, l, rows[w]);
-  else bwd_dir<T, MODE, 1>(ba, l, rows[w]);
+  if ((w & 1) == 0) bwd_dir<T, MODE, 0>(ba, l, rows[w], stage[w]);
+  else bwd_dir<T, MODE, 1>(ba, l, rows[w], stage[w]);
 }
 
 // du, dΔ_raw (and the backward branch's, or their sums when the branches share inputs):
