@@ -203,6 +203,66 @@ def cpu_baseline(cfg_id, cfg, min_s=1.0):
                       f"slowest worker {wall:.2f} s"}
 
 
+def cpu_sample(kind, cfg_id, cfg, min_s=3.0):
+    """The fp64 oracle of one bench leg on a bounded sample of its workload: one batch, in this
+    process (one core; the oracle is plain elementwise numpy), repeated for at least ``min_s``
+    seconds.  ``kind``: "v2", "n32", "bwd", "front"."""
+    import numpy as np
+    import oracle as O
+    import synth
+    N = cfg["d_state"]
+    if cfg["kind"] == "vim":
+        p = synth.make_vim_v2_inputs(cfg_id, batch=1, d_state=N)
+        toks = cfg["dim"] * cfg["seqlen"]
+        v2args = lambda q: (q["u"], q["delta_raw"], q["delta_bias"], q["u_b"], q["delta_raw_b"], q["delta_bias_b"],
+                            q["z"], q["A_log"], q["A_b_log"], q["B"], q["C"], q["B_b"], q["C_b"], q["D"], q["D_b"])
+        if kind == "bwd":
+            dout = np.random.default_rng(1).standard_normal(p["u"].shape)
+            fn = lambda: O.vim_bidir_v2_bwd(*v2args(p), dout)
+            what = "vim_bidir_v2_bwd (all 15 gradients)"
+        elif kind == "front":
+            c = synth.make_conv1d_inputs(cfg_id, batch=1)
+
+            def fn():
+                q = dict(p)
+                q["u"] = O.conv1d_silu(c["x"], c["conv_w"], c["conv_b"])
+                q["u_b"] = O.conv1d_silu(c["x"], c["conv_w_b"], c["conv_b_b"], reverse=True)
+                return O.vim_bidir_v2(*v2args(q))
+            what = "conv1d_silu (both branches) + vim_bidir_v2"
+        elif kind == "v2":
+            fn = lambda: O.vim_bidir_v2(*v2args(p))
+            what = "vim_bidir_v2"
+        else:
+            fn = lambda: O.vim_bidir(p["u"], p["delta_raw"], p["z"], p["A_log"], p["A_b_log"], p["B"], p["C"],
+                                     p["B_b"], p["C_b"], p["D"], p["D_b"], p["delta_bias"])
+            what = f"vim_bidir (d_state {N})"
+    else:
+        p = synth.make_ss2d_inputs(cfg_id, batch=1, d_state=N)
+        toks = cfg["dim"] * cfg["H"] * cfg["W"]
+        args = (p["delta_raw"], p["A_log"], p["B"], p["C"], p["D"], p["delta_bias"])
+        if kind == "bwd":
+            dout = np.random.default_rng(1).standard_normal(p["x"].shape)
+            fn = lambda: O.ss2d_cross_scan_bwd(p["x"], *args, None, dout)
+            what = "ss2d_cross_scan_bwd (all gradients)"
+        elif kind == "front":
+            c = synth.make_conv2d_inputs(cfg_id, batch=1)
+            fn = lambda: O.ss2d_cross_scan(O.conv2d_silu(c["x"], c["conv_w"], c["conv_b"]), *args)
+            what = "conv2d_silu + ss2d_cross_scan"
+        else:
+            fn = lambda: O.ss2d_cross_scan(p["x"], *args)
+            what = f"ss2d_cross_scan (d_state {N})"
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_s:
+            break
+    return {"value": reps * toks / dt, "unit": "tokens·channels/s", "cores": 1, "kind": "oracle",
+            "sample": f"{cfg['name']}: batch 1 of {cfg['batch']}, {what}, repeated {reps}x in {dt:.1f} s on one "
+                      f"core (fp64 numpy oracle)"}
+
+
 VIM_ACT = ("u", "delta_raw", "z", "B", "C", "B_b", "C_b")
 VIM_PAR = ("A_log", "A_b_log", "D", "D_b", "delta_bias")
 V2_ACT = ("u_b", "delta_raw_b")
@@ -363,17 +423,19 @@ def bench_config(cfg_id, steps, warmup, with_cpu, torch, V, v2=False, d_state=No
         rec["config"]["W"] = cfg["W"]
     if with_cpu and is_default and not v2:
         rec["cpu_baseline"] = cpu_baseline(cfg_id, cfg)
+    elif with_cpu and (v2 or cfg["d_state"] != synth.CONFIGS[cfg_id]["d_state"]):
+        rec["cpu_baseline"] = cpu_sample("v2" if v2 else "n32", cfg_id, cfg)
     return rec
 
 
-def bench_bwd(cfg_id, steps, warmup, torch, V, v2=False):
+def bench_bwd(cfg_id, steps, warmup, torch, V, v2=False, with_cpu=False):
     """Backward pass (vmscan_bwd_bidir_v2, every gradient) of a Vim workload; with shared inputs
     (the forward of vmscan_fwd_bidir) unless ``v2``.  The timed region is the whole call."""
     import numpy as np
     import synth
     cfg = synth.CONFIGS[cfg_id]
     if cfg["kind"] != "vim":
-        return bench_ss2d_bwd(cfg_id, steps, warmup, torch, V)
+        return bench_ss2d_bwd(cfg_id, steps, warmup, torch, V, with_cpu)
     dev = torch.device("cuda", 0)
     dt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
     p = synth.make_vim_v2_inputs(cfg_id)
@@ -409,7 +471,7 @@ def bench_bwd(cfg_id, steps, warmup, torch, V, v2=False):
     alu = upd / (ms * 1e-3)
     toks = nb * nd * L
     del outs
-    return {
+    rec = {
         "metric": "scan tokens·channels/s (bwd: all gradients of the bidirectional scan), 1 GPU",
         "value": toks / (ms * 1e-3), "unit": "tokens·channels/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
@@ -421,6 +483,9 @@ def bench_bwd(cfg_id, steps, warmup, torch, V, v2=False):
                      "kernel": "all kernels of vmscan_bwd_bidir_v2 (forward with saved sum, gate, adjoint scan, "
                                "reductions)", "kernel_avg_us": round(ms * 1000, 2), "updates_per_launch": upd},
     }
+    if with_cpu:
+        rec["cpu_baseline"] = cpu_sample("bwd", cfg_id, cfg)
+    return rec
 
 
 def front_bytes(cfg):
@@ -431,7 +496,7 @@ def front_bytes(cfg):
     return 3 * n * esz
 
 
-def bench_front(cfg_id, steps, warmup, torch, V):
+def bench_front(cfg_id, steps, warmup, torch, V, with_cpu=False):
     """Front convolution + scan as one step: Vim: conv1d + SiLU for both branches
     (vmscan_conv1d_silu_fwd) then the scan with a separate backward branch; SS2D: the 3 x 3
     conv2d + SiLU writing both layouts (ss2d_conv2d_silu_fwd) then the cross-scan reading the
@@ -516,7 +581,7 @@ def bench_front(cfg_id, steps, warmup, torch, V):
     gbs = fb / (front_ms * 1e-3) / 1e9
     upd = state_updates(cfg)
     alu = upd / (scan_ms * 1e-3)
-    return {
+    rec = {
         "metric": METRIC + " (front convolution + scan)",
         "value": toks / (ms * 1e-3), "unit": "tokens·channels/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
@@ -532,9 +597,12 @@ def bench_front(cfg_id, steps, warmup, torch, V):
                               "unit": "Gupd/s", "frac": round(alu / ALU_PEAK_UPD_S, 4),
                               "avg_us": round(scan_ms * 1000, 2)}},
     }
+    if with_cpu:
+        rec["cpu_baseline"] = cpu_sample("front", cfg_id, cfg)
+    return rec
 
 
-def bench_ss2d_bwd(cfg_id, steps, warmup, torch, V):
+def bench_ss2d_bwd(cfg_id, steps, warmup, torch, V, with_cpu=False):
     """Backward pass of the SS2D cross-scan (ss2d_cross_scan_bwd, every gradient, no gate as in
     the 56x56 workload); the timed region is the whole call."""
     import numpy as np
@@ -570,7 +638,7 @@ def bench_ss2d_bwd(cfg_id, steps, warmup, torch, V):
     upd = state_updates(cfg)
     alu = upd / (ms * 1e-3)
     toks = nb * nd * H * W
-    return {
+    rec = {
         "metric": "scan tokens·channels/s (bwd: all gradients of the SS2D cross-scan), 1 GPU",
         "value": toks / (ms * 1e-3), "unit": "tokens·channels/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
@@ -582,6 +650,9 @@ def bench_ss2d_bwd(cfg_id, steps, warmup, torch, V):
                      "kernel": "all kernels of ss2d_cross_scan_bwd (transposes, two pairs of adjoint scans, reductions)",
                      "kernel_avg_us": round(ms * 1000, 2), "updates_per_launch": upd},
     }
+    if with_cpu:
+        rec["cpu_baseline"] = cpu_sample("bwd", cfg_id, cfg)
+    return rec
 
 
 def main():
@@ -647,9 +718,9 @@ def main():
     cfgs = [0, 1, 2, 3, 4] if args.all else [args.config]
     for c in cfgs:
         if args.front:
-            rec = bench_front(c, args.steps, args.warmup, torch, V)
+            rec = bench_front(c, args.steps, args.warmup, torch, V, not args.no_cpu)
         elif args.bwd:
-            rec = bench_bwd(c, args.steps, args.warmup, torch, V, args.v2)
+            rec = bench_bwd(c, args.steps, args.warmup, torch, V, args.v2, not args.no_cpu)
             if rec is None:
                 continue
         else:
