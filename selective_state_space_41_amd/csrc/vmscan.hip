@@ -340,10 +340,10 @@ struct Lane {
   int Kc;
 };
 
-__device__ __forceinline__ Lane lane_ctx(const ScanArgs& a) {
+__device__ __forceinline__ Lane lane_ctx(const ScanArgs& a, int bid) {
   Lane l;
   const int nblocks = a.batch * a.nch * a.ngroups;
-  const int tile = logical_block(static_cast<int>(blockIdx.x), nblocks);
+  const int tile = logical_block(bid, nblocks);
   const int g = tile % a.ngroups;
   const int rest = tile / a.ngroups;
   l.c = rest % a.nch;
@@ -357,6 +357,8 @@ __device__ __forceinline__ Lane lane_ctx(const ScanArgs& a) {
   l.Kc = static_cast<int>(a.L - l.s_lo < a.K ? a.L - l.s_lo : a.K);
   return l;
 }
+
+__device__ __forceinline__ Lane lane_ctx(const ScanArgs& a) { return lane_ctx(a, static_cast<int>(blockIdx.x)); }
 
 template <int MODE, int DIR>
 struct Dir {
@@ -1652,11 +1654,20 @@ __device__ __forceinline__ void bwd_ckpt_dir(const BwdArgs& ba, const Lane& l) {
   if (full_end < L && l.valid) store8(ck_at(full_end / kWin), h);
 }
 
+// The backward kernels run one argument set, or two (SETS = 2: the two SS2D pairs in one launch,
+// the first set's workgroups first); both sets have the same workgroup count.
 template <typename T, int MODE>
-__global__ __launch_bounds__(kThreads) void bwd_ckpt_kernel(BwdArgs ba) {
-  const Lane l = lane_ctx(ba.s);
+__device__ __forceinline__ void bwd_ckpt_block(const BwdArgs& ba, int bid) {
+  const Lane l = lane_ctx(ba.s, bid);
   if ((__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6) & 1) == 0) bwd_ckpt_dir<T, MODE, 0>(ba, l);
   else bwd_ckpt_dir<T, MODE, 1>(ba, l);
+}
+
+template <typename T, int MODE, int SETS>
+__global__ __launch_bounds__(kThreads) void bwd_ckpt_kernel(BwdArgs b0, BwdArgs b1) {
+  const int nb = b0.s.batch * b0.s.nch * b0.s.ngroups, bid = static_cast<int>(blockIdx.x);
+  if (SETS == 1 || bid < nb) bwd_ckpt_block<T, MODE>(b0, bid);
+  else bwd_ckpt_block<T, MODE>(b1, bid - nb);
 }
 
 // Adjoint chunk records (split sequences).  Within a chunk the adjoint obeys
@@ -1726,10 +1737,17 @@ __device__ __forceinline__ void adj_state_dir(const BwdArgs& ba, const Lane& l) 
 }
 
 template <typename T, int MODE>
-__global__ __launch_bounds__(kThreads) void adj_state_kernel(BwdArgs ba) {
-  const Lane l = lane_ctx(ba.s);
+__device__ __forceinline__ void adj_state_block(const BwdArgs& ba, int bid) {
+  const Lane l = lane_ctx(ba.s, bid);
   if ((__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6) & 1) == 0) adj_state_dir<T, MODE, 0>(ba, l);
   else adj_state_dir<T, MODE, 1>(ba, l);
+}
+
+template <typename T, int MODE, int SETS>
+__global__ __launch_bounds__(kThreads) void adj_state_kernel(BwdArgs b0, BwdArgs b1) {
+  const int nb = b0.s.batch * b0.s.nch * b0.s.ngroups, bid = static_cast<int>(blockIdx.x);
+  if (SETS == 1 || bid < nb) adj_state_block<T, MODE>(b0, bid);
+  else adj_state_block<T, MODE>(b1, bid - nb);
 }
 
 // Per-wave LDS staging of one window's outputs, so that each is stored as runs of 8 positions
@@ -1957,13 +1975,21 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
 }
 
 template <typename T, int MODE>
-__global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdArgs ba) {
+__device__ __forceinline__ void bwd_scan_block(const BwdArgs& ba, int bid, float* rows, float* stage) {
+  const Lane l = lane_ctx(ba.s, bid);
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  if ((w & 1) == 0) bwd_dir<T, MODE, 0>(ba, l, rows, stage);
+  else bwd_dir<T, MODE, 1>(ba, l, rows, stage);
+}
+
+template <typename T, int MODE, int SETS>
+__global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdArgs b0, BwdArgs b1) {
   __shared__ __attribute__((aligned(16))) float rows[4][kW * kRedStride];
   __shared__ __attribute__((aligned(16))) float stage[4][kStageFloats];
-  const Lane l = lane_ctx(ba.s);
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-  if ((w & 1) == 0) bwd_dir<T, MODE, 0>(ba, l, rows[w], stage[w]);
-  else bwd_dir<T, MODE, 1>(ba, l, rows[w], stage[w]);
+  const int nb = b0.s.batch * b0.s.nch * b0.s.ngroups, bid = static_cast<int>(blockIdx.x);
+  if (SETS == 1 || bid < nb) bwd_scan_block<T, MODE>(b0, bid, rows[w], stage[w]);
+  else bwd_scan_block<T, MODE>(b1, bid - nb, rows[w], stage[w]);
 }
 
 // du, dΔ_raw (and the backward branch's, or their sums when the branches share inputs):
@@ -2105,25 +2131,30 @@ BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t L, int64_t Kf) {
 
 // Checkpoints, then (split sequences) the adjoint records and their reverse carry prefix, then the
 // adjoint walk; every kernel runs one workgroup per (batch, chunk, channel group).
-template <typename T, int MODE>
-vmscan_status launch_bwd_scans(const BwdArgs& ba, hipStream_t stream) {
-  const ScanArgs& a = ba.s;
-  const int64_t nblocks = static_cast<int64_t>(a.batch) * a.nch * a.ngroups;
+// every kernel runs one workgroup per (set, batch, chunk, channel group).  SETS = 2 runs b0 and b1
+// (same shapes and chunking) in the same launches.
+template <typename T, int MODE, int SETS>
+vmscan_status launch_bwd_scans(const BwdArgs& b0, const BwdArgs& b1, hipStream_t stream) {
+  const ScanArgs& a = b0.s;
+  const int64_t nblocks = static_cast<int64_t>(a.batch) * a.nch * a.ngroups * SETS;
   if (nblocks >= (int64_t{1} << 31)) return VMSCAN_ERR_SHAPE;
   const dim3 grid(static_cast<unsigned>(nblocks));
-  hipLaunchKernelGGL((bwd_ckpt_kernel<T, MODE>), grid, dim3(kThreads), 0, stream, ba);
+  hipLaunchKernelGGL((bwd_ckpt_kernel<T, MODE, SETS>), grid, dim3(kThreads), 0, stream, b0, b1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return launch_failed(e);
   if (a.nch > 1) {
-    hipLaunchKernelGGL((adj_state_kernel<T, MODE>), grid, dim3(kThreads), 0, stream, ba);
+    hipLaunchKernelGGL((adj_state_kernel<T, MODE, SETS>), grid, dim3(kThreads), 0, stream, b0, b1);
     e = hipGetLastError();
     if (e != hipSuccess) return launch_failed(e);
     const int64_t pblocks = ceil_div(static_cast<int64_t>(a.batch) * a.dim * 2 * kN, 256);
-    hipLaunchKernelGGL(carry_prefix_kernel, dim3(static_cast<unsigned>(pblocks)), dim3(256), 0, stream, a, ba.adj, 1);
-    e = hipGetLastError();
-    if (e != hipSuccess) return launch_failed(e);
+    for (int k = 0; k < SETS; ++k) {
+      const BwdArgs& b = k == 0 ? b0 : b1;
+      hipLaunchKernelGGL(carry_prefix_kernel, dim3(static_cast<unsigned>(pblocks)), dim3(256), 0, stream, b.s, b.adj, 1);
+      e = hipGetLastError();
+      if (e != hipSuccess) return launch_failed(e);
+    }
   }
-  hipLaunchKernelGGL((bwd_scan_kernel<T, MODE>), grid, dim3(kThreads), 0, stream, ba);
+  hipLaunchKernelGGL((bwd_scan_kernel<T, MODE, SETS>), grid, dim3(kThreads), 0, stream, b0, b1);
   e = hipGetLastError();
   return e == hipSuccess ? VMSCAN_OK : launch_failed(e);
 }
@@ -2163,7 +2194,7 @@ vmscan_status run_bwd(const ScanArgs& fwd, const BwdLayout& lay, unsigned char* 
   ba.dbc = reinterpret_cast<float*>(wsp + lay.dbc);
   ba.dpar = reinterpret_cast<float*>(wsp + lay.dpar);
   ba.wpc = static_cast<int>(ceil_div(Kb, kWin));
-  st = launch_bwd_scans<T, kModeVim>(ba, stream);
+  st = launch_bwd_scans<T, kModeVim, 1>(ba, ba, stream);
   if (st != VMSCAN_OK) return st;
   hipLaunchKernelGGL(bwd_combine_kernel<T>, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, stream,
                      ba.gu, ba.gx, static_cast<T*>(du), static_cast<T*>(dx), static_cast<T*>(du_b),
@@ -2181,9 +2212,18 @@ vmscan_status run_bwd(const ScanArgs& fwd, const BwdLayout& lay, unsigned char* 
 
 // SS2D backward workspace: the forward's (images, transposed x, B/C copy, carries), then the
 // un-gated sum, the row- and column-order g, the checkpoints and the partial gradients.
+// Per-pair backward buffers (the two pairs share launches): the B/C copy and forward carries, the
+// checkpoints and adjoint records, the du and dΔ_raw shares, the dB/dC and parameter partials.
+// Pair 0 uses the forward layout's B/C copy and carries.
+struct PairBufs {
+  size_t bct, agg, ck, adj, gu, gx, dbc, dpar;
+};
+
 struct Ss2dBwdLayout {
   Ss2dLayout f;
-  size_t ysum, g, gcol, ck, adj, gu, gx, dbc, dpar, total;
+  size_t ysum, g, gcol;
+  PairBufs p[2];
+  size_t total;
 };
 
 Ss2dBwdLayout ss2d_bwd_layout(int64_t batch, int64_t dim, int64_t L, int64_t Kf, size_t esz) {
@@ -2194,32 +2234,52 @@ Ss2dBwdLayout ss2d_bwd_layout(int64_t batch, int64_t dim, int64_t L, int64_t Kf,
   w.ysum = round256(w.f.total);
   w.g = w.ysum + plane;
   w.gcol = w.g + plane;
-  w.ck = w.gcol + plane;
-  w.adj = w.ck + ck_bytes(batch, dim, L, Kb);
-  w.gu = w.adj + agg_bytes(batch, dim, L, Kb);
-  w.gx = w.gu + 4 * plane;
-  w.dbc = w.gx + 4 * plane;
-  w.dpar = w.dbc + round256(static_cast<size_t>(2) * groups(dim) * batch * 2 * kN * L * sizeof(float));
-  w.total = w.dpar + dpar_bytes(batch, dim, L, Kb);
+  size_t o = w.gcol + plane;
+  for (int k = 0; k < 2; ++k) {
+    PairBufs& q = w.p[k];
+    if (k == 0) {
+      q.bct = w.f.bct;
+      q.agg = w.f.agg;
+    } else {
+      q.bct = o;
+      o += bct_bytes(batch, L);
+      q.agg = o;
+      o += agg_bytes(batch, dim, L, Kf);
+    }
+    q.ck = o;
+    o += ck_bytes(batch, dim, L, Kb);
+    q.adj = o;
+    o += agg_bytes(batch, dim, L, Kb);
+    q.gu = o;
+    o += 4 * plane;
+    q.gx = o;
+    o += 4 * plane;
+    q.dbc = o;
+    o += round256(static_cast<size_t>(2) * groups(dim) * batch * 2 * kN * L * sizeof(float));
+    q.dpar = o;
+    o += dpar_bytes(batch, dim, L, Kb);
+  }
+  w.total = o;
   return w;
 }
 
-// The gradients of one SS2D pair (directions k0 and k1 = its reverse) from g in the pair's
-// position order: checkpoints, adjoint walk, then dΔ_raw, dB, dC and the parameter sums written
-// for both directions.  The pair's du (four float32 planes in position order) stays in ba.gu.
+// One SS2D pair (directions k0 and k1 = its reverse) before its adjoint walk: its B/C copy and,
+// for a split sequence, its forward carries (in the forward's chunks).
 template <typename T>
-vmscan_status ss2d_pair_bwd(BwdArgs& ba, int k0, int k1, void* ddelta_raw, void* dB, void* dC, float* dA_log,
-                            const float* A_log, float* dD, float* ddelta_bias, hipStream_t stream) {
+vmscan_status ss2d_pair_prepare(const BwdArgs& ba, hipStream_t stream) {
+  ScanArgs af = ba.s;
+  af.K = ba.fnch > 1 ? static_cast<int>(ba.s.K / ba.fm) : static_cast<int>(ba.s.L);
+  af.nch = ba.fnch;
+  return run_pair<T, kModeSecondPair>(af, stream, kStagePrepare);
+}
+
+// ... and after it: dΔ_raw, dB, dC and the parameter sums written for both directions.  The pair's
+// du (four float32 planes in position order) stays in ba.gu.
+template <typename T>
+vmscan_status ss2d_pair_post(const BwdArgs& ba, int k0, int k1, void* ddelta_raw, void* dB, void* dC, float* dA_log,
+                             const float* A_log, float* dD, float* ddelta_bias, hipStream_t stream) {
   const ScanArgs& a = ba.s;
   const int64_t DL = static_cast<int64_t>(a.dim) * a.L;
-  // the pair's B/C copy and, for a split sequence, its forward carries (in the forward's chunks)
-  ScanArgs af = a;
-  af.K = ba.fnch > 1 ? static_cast<int>(a.K / ba.fm) : static_cast<int>(a.L);
-  af.nch = ba.fnch;
-  vmscan_status st = run_pair<T, kModeSecondPair>(af, stream, kStagePrepare);
-  if (st != VMSCAN_OK) return st;
-  st = launch_bwd_scans<T, kModeSecondPair>(ba, stream);
-  if (st != VMSCAN_OK) return st;
   const int64_t n = static_cast<int64_t>(a.batch) * DL;
   const int64_t plane = n;
   T* ddr = static_cast<T*>(ddelta_raw);
@@ -2302,25 +2362,39 @@ vmscan_status run_ss2d_bwd(const void* x, const void* delta_raw, const float* A_
   // g in column-major order for the column pair
   st = launch_transpose(g, gcol, nimg, static_cast<int>(H), static_cast<int>(W), 4, stream);
   if (st != VMSCAN_OK) return st;
-  BwdArgs ba{};
-  ba.s = a;  // each pair's forward carries (chunks of Kf) are made by its prepare stage
+  // Both pairs' adjoint walks in the same launches (twice the workgroups of one pair), each with its
+  // own buffers: the column pair (directions 1 and 3 over x^T, g in column order) and the row
+  // pair (directions 0 and 2 over x, g in row order).
+  BwdArgs bp[2];
   const int64_t Kb = bwd_chunk(batch * a.ngroups, L, Kf);
-  ba.s.K = static_cast<int>(Kb);
-  ba.s.nch = static_cast<int>(ceil_div(L, Kb));
-  ba.fnch = ba.s.nch > 1 ? a.nch : 1;  // an unsplit walk needs no forward carries
-  ba.fm = ba.s.nch > 1 ? static_cast<int>(Kb / Kf) : 1;
-  ba.ck = reinterpret_cast<float*>(wsp + lay.ck);
-  ba.adj = ba.s.nch > 1 ? reinterpret_cast<float*>(wsp + lay.adj) : nullptr;
-  ba.gu = reinterpret_cast<float*>(wsp + lay.gu);
-  ba.gx = reinterpret_cast<float*>(wsp + lay.gx);
-  ba.dbc = reinterpret_cast<float*>(wsp + lay.dbc);
-  ba.dpar = reinterpret_cast<float*>(wsp + lay.dpar);
-  ba.wpc = static_cast<int>(ceil_div(Kb, kWin));
-  // column pair: directions 1 and 3 over x^T with g in column order
-  ba.g = gcol;
-  ba.s.d0 = dir_args(xt, 1, 0);
-  ba.s.d1 = dir_args(xt, 3, 1);
-  st = ss2d_pair_bwd<T>(ba, 1, 3, ddelta_raw, dB, dC, dA_log, A_log, dD, ddelta_bias, stream);
+  for (int k = 0; k < 2; ++k) {
+    BwdArgs& ba = bp[k];
+    const PairBufs& q = lay.p[k];
+    ba = BwdArgs{};
+    ba.s = a;
+    ba.s.bct = reinterpret_cast<float*>(wsp + q.bct);
+    ba.s.agg = reinterpret_cast<float*>(wsp + q.agg);
+    ba.s.K = static_cast<int>(Kb);
+    ba.s.nch = static_cast<int>(ceil_div(L, Kb));
+    ba.fnch = ba.s.nch > 1 ? a.nch : 1;  // an unsplit walk needs no forward carries
+    ba.fm = ba.s.nch > 1 ? static_cast<int>(Kb / Kf) : 1;
+    ba.ck = reinterpret_cast<float*>(wsp + q.ck);
+    ba.adj = ba.s.nch > 1 ? reinterpret_cast<float*>(wsp + q.adj) : nullptr;
+    ba.gu = reinterpret_cast<float*>(wsp + q.gu);
+    ba.gx = reinterpret_cast<float*>(wsp + q.gx);
+    ba.dbc = reinterpret_cast<float*>(wsp + q.dbc);
+    ba.dpar = reinterpret_cast<float*>(wsp + q.dpar);
+    ba.wpc = static_cast<int>(ceil_div(Kb, kWin));
+    ba.g = k == 0 ? gcol : g;
+    ba.s.d0 = k == 0 ? dir_args(xt, 1, 0) : dir_args(x, 0, 0);
+    ba.s.d1 = k == 0 ? dir_args(xt, 3, 1) : dir_args(x, 2, 1);
+    st = ss2d_pair_prepare<T>(ba, stream);
+    if (st != VMSCAN_OK) return st;
+  }
+  st = launch_bwd_scans<T, kModeSecondPair, 2>(bp[0], bp[1], stream);
+  if (st != VMSCAN_OK) return st;
+  const BwdArgs& ba = bp[0];
+  st = ss2d_pair_post<T>(bp[0], 1, 3, ddelta_raw, dB, dC, dA_log, A_log, dD, ddelta_bias, stream);
   if (st != VMSCAN_OK) return st;
   // its du back to row-major pixels: sum the four partial planes (column order), transpose
   float* col = reinterpret_cast<float*>(wsp + lay.f.col_img);
@@ -2329,14 +2403,12 @@ vmscan_status run_ss2d_bwd(const void* x, const void* delta_raw, const float* A_
                      ba.gu, ba.gu + n, ba.gu + 2 * n, ba.gu + 3 * n, nullptr, col, n, 1, n);
   st = launch_transpose(col, rowp, nimg, static_cast<int>(W), static_cast<int>(H), 4, stream);
   if (st != VMSCAN_OK) return st;
-  // row pair: directions 0 and 2 over x with g in row order
-  ba.g = g;
-  ba.s.d0 = dir_args(x, 0, 0);
-  ba.s.d1 = dir_args(x, 2, 1);
-  st = ss2d_pair_bwd<T>(ba, 0, 2, ddelta_raw, dB, dC, dA_log, A_log, dD, ddelta_bias, stream);
+  // the row pair's gradients, and dx = its du plus the column pair's, transposed
+  const BwdArgs& br = bp[1];
+  st = ss2d_pair_post<T>(br, 0, 2, ddelta_raw, dB, dC, dA_log, A_log, dD, ddelta_bias, stream);
   if (st != VMSCAN_OK) return st;
-  hipLaunchKernelGGL(sum_planes_kernel<T>, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, stream, ba.gu,
-                     ba.gu + n, ba.gu + 2 * n, ba.gu + 3 * n, rowp, static_cast<T*>(dx), n, 1, n);
+  hipLaunchKernelGGL(sum_planes_kernel<T>, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, stream, br.gu,
+                     br.gu + n, br.gu + 2 * n, br.gu + 3 * n, rowp, static_cast<T*>(dx), n, 1, n);
   e = hipGetLastError();
   return e == hipSuccess ? VMSCAN_OK : launch_failed(e);
 }
