@@ -186,7 +186,10 @@ vmscan_status vmscan_fwd_bidir_v2_stage(const void *u, const void *delta_raw, co
  * branches share u, delta_raw and delta_bias (pass the same tensor as u_b etc. then).
  * The library recomputes the forward: it runs the forward scan keeping the un-gated sum, then
  * each direction forward again storing its state every 8 steps, then backwards over the
- * sequence with the adjoint recurrence.  Workspace: vmscan_bwd_bidir_v2_workspace_bytes.
+ * sequence with the adjoint recurrence.  A long sequence with few (batch, channel-group) tiles
+ * is split into chunks, the adjoint carry between them coming from a reverse carry pass; the
+ * result does not depend on the split beyond float32 rounding order.  Workspace:
+ * vmscan_bwd_bidir_v2_workspace_bytes.
  * Gradient outputs must not alias each other or any input.  Validation and error codes as for
  * vmscan_fwd_bidir_v2 (all pointers but the three optional ones are required, all 16-byte
  * aligned); launches are asynchronous on `stream`.  d_state must be 16.
@@ -222,7 +225,7 @@ vmscan_status vmscan_bwd_bidir_v2(const void *u, const void *delta_raw, const fl
  * library first recomputes the un-gated forward sum for dz.  Workspace:
  * ss2d_cross_scan_bwd_workspace_bytes.  Outputs must not alias each other or any input.
  * Validation and error codes as for ss2d_cross_scan_fwd (z and dz must both be given or both be
- * NULL, else VMSCAN_ERR_NULL); launches are asynchronous on `stream`.
+ * NULL, else VMSCAN_ERR_NULL); launches are asynchronous on `stream`.  d_state must be 16.
  */
 size_t ss2d_cross_scan_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t H, int64_t W, int d_state,
                                            vmscan_dtype dtype);

@@ -17,7 +17,7 @@
 //    copy, so that neither factor costs an instruction in the loop.
 //  * B and C are the same for every channel of a batch row, so each wave reads its 8 B and 8 C
 //    values per token as wave-uniform scalars (one s_load_dwordx16) from an fp32
-//    [batch][direction][half][position][16] copy that a small transpose kernel writes first.
+//    [batch][direction][part][position][16] copy that a small transpose kernel writes first.
 //    No VALU instruction is spent on B/C.
 //  * u, Δ_raw (and z) are read per lane in windows of 8 consecutive tokens (16-byte loads;
 //    the hardware accepts the 2-byte-aligned rows of odd-length bf16 sequences), one window
@@ -44,6 +44,16 @@
 //  * Workgroup ids are remapped so that the workgroups one XCD receives (the hardware deals
 //    them round-robin over 8 XCDs) are consecutive tiles of the same batch row, which then
 //    share their B/C reads in that XCD's L2.
+//  * d_state 32 keeps 8 states per wave: four state parts per direction, eight waves per
+//    workgroup, whose partial readouts meet in the LDS row in part order (each part waits for the
+//    one below it).
+//  * The backward pass (gradients of every input) recomputes the forward: a checkpoint pass
+//    stores each direction's state every 8 steps, then the adjoint walk goes back window by
+//    window, rebuilding a window's states from its checkpoint.  Long sequences with few
+//    workgroups are split into chunks; the adjoint carry between chunks comes from per-chunk
+//    records and the same carry prefix run against the scan order.
+//  * The front convolutions that produce the scan input (Vim: causal conv1d + SiLU for both
+//    branches; SS2D: 3 x 3 conv2d + SiLU written row-major and transposed) are streaming kernels.
 
 #include <hip/hip_runtime.h>
 
@@ -59,7 +69,7 @@ constexpr int kH = 8;                  // states per wave: d_state / 8 waves (pa
 constexpr int kW = 64;                 // channels per workgroup = lanes per wave
 constexpr int kThreads = 4 * kW;       // d_state 16 workgroup: (fwd, lo) (bwd, lo) (fwd, hi) (bwd, hi)
 constexpr int kWin = 8;                // tokens per register window
-constexpr int kBC = 2 * kH;            // floats per (position, half) in the B/C copy: 8 B, 8 C
+constexpr int kBC = 2 * kH;            // floats per (position, state part) in the B/C copy: 8 B, 8 C
 constexpr int kKMax = 206;             // longest LDS row: 3 workgroups of 64 x 207 floats per CU
 constexpr int kMinChunk = 32;          // shortest chunk the planner picks
 constexpr int kTargetBlocks = 768;     // planner: three workgroups on each of 256 CUs
@@ -331,7 +341,7 @@ __global__ __launch_bounds__(256) void transpose16_kernel(const uint16_t* __rest
 //   DIR   0: step i visits chunk position i; 1: position Kc-1-i
 //   MODE  kModeVim / kModeVimSum / kModeFirstPair / kModeSecondPair (SS2D backward tensors are
 //         stored in reversed position order; the modes differ in the epilogue)
-// The state half of a wave is a wave-uniform run-time value (it only selects data).
+// The state part of a wave is a wave-uniform run-time value (it only selects data).
 
 struct Lane {
   int b, c, lane, d, dd, part;  // dd: channel clamped into range for the loads of inactive lanes
@@ -401,7 +411,7 @@ __device__ __forceinline__ void load_a2(const DirArgs& da, const Lane& l, int ns
   for (int k = 0; k < kH; ++k) A2[k] = -__expf(da.A_log[static_cast<int64_t>(l.dd) * ns + kH * l.part + k]);
 }
 
-// B/C of one position for the wave's half: 8 + 8 wave-uniform floats (one s_load_dwordx16).
+// B/C of one position for the wave's state part: 8 + 8 wave-uniform floats (one s_load_dwordx16).
 __device__ __forceinline__ void load_bc(scalar_fp p, float (&bc)[kBC]) {
 #pragma unroll
   for (int q = 0; q < kBC; ++q) bc[q] = p[q];
@@ -461,7 +471,7 @@ __device__ __forceinline__ void run_steps(const Lane& l, int i0, const float (&d
 }
 
 // Δ2 and Δ2·u of a window from its raw u and Δ_raw (bias2 = bias log2 e); yi = the lane's D·u
-// share (lower half only).
+// share (state part 0 only).
 __device__ __forceinline__ void prep_window(const float (&uu)[kWin], const float (&xr)[kWin], float bias2, float Dh,
                                             float (&dl)[kWin], float (&du)[kWin], float (&yi)[kWin]) {
 #pragma unroll
@@ -514,7 +524,7 @@ __device__ __forceinline__ void unit_wait(int* flag, int unit) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Pass A: per chunk, direction and state half, the end states of the chunk scanned from a zero
+// Pass A: per chunk, direction and state part, the end states of the chunk scanned from a zero
 // state, and Σ Δ2 (base-2 units).
 
 // Δ and Δ·u exchange between the NP state parts of a direction: each wave computes them for 8/NP
@@ -694,7 +704,7 @@ __device__ __forceinline__ void run_phase(const ScanArgs& a, const Lane& l, cons
   int* const own_flag = flags + l.part;
   const bool relay = NP > 2 && !lo && l.part < NP - 1;  // a middle part publishes its own adds
   float yp[kWin];
-  int pp = -1;  // upper half: chunk position of the pending window's first step, -1 when none
+  int pp = -1;  // parts above 0: chunk position of the pending window's first step, -1 when none
   for (int i0 = i_begin; i0 < full_end; i0 += kWin) {
     float uu[kWin], xr[kWin], dl[kWin], du[kWin], yi[kWin], y[kWin], r[kWin];
     rotate_priority(i0 / kWin);
