@@ -10,7 +10,7 @@ are rotated so that at least 1 GiB is touched between reuses and the 256 MB Infi
 serve the inputs.  Rank 0 prints one JSON line per workload.  ``--v2`` runs the Vim workloads
 through the entry point whose backward branch has its own u_b, Δ_raw_b and bias_b; ``--bwd``
 times the backward pass (all gradients) of the Vim workloads instead of the forward; ``--d-state
-32`` runs the forward workloads with 32 states instead of 16; ``--front`` times the front
+32`` runs the workloads (forward or backward) with 32 states instead of 16; ``--front`` times the front
 convolution that produces the scan input followed by the scan.
 """
 import argparse
@@ -307,10 +307,7 @@ def make_sets(cfg_id, cfg, nsets, torch, v2=False):
 
 def bench_config(cfg_id, steps, warmup, with_cpu, torch, V, v2=False, d_state=None):
     import synth
-    cfg = dict(synth.CONFIGS[cfg_id])
-    if d_state and d_state != cfg["d_state"]:
-        cfg["d_state"] = d_state
-        cfg["name"] = cfg["name"] + f"_n{d_state}"
+    cfg = with_d_state(cfg_id, d_state)
     v2 = v2 and cfg["kind"] == "vim"
     nbytes, toks = algorithmic_bytes(cfg, v2)
     layers = cfg.get("layers", 1)
@@ -428,17 +425,28 @@ def bench_config(cfg_id, steps, warmup, with_cpu, torch, V, v2=False, d_state=No
     return rec
 
 
-def bench_bwd(cfg_id, steps, warmup, torch, V, v2=False, with_cpu=False):
+def with_d_state(cfg_id, d_state):
+    """The workload's configuration, at another state size if ``d_state`` differs from its own."""
+    import synth
+    cfg = dict(synth.CONFIGS[cfg_id])
+    if d_state and d_state != cfg["d_state"]:
+        cfg["d_state"] = d_state
+        cfg["name"] = cfg["name"] + f"_n{d_state}"
+    return cfg
+
+
+def bench_bwd(cfg_id, steps, warmup, torch, V, v2=False, with_cpu=False, d_state=None):
     """Backward pass (vmscan_bwd_bidir_v2, every gradient) of a Vim workload; with shared inputs
     (the forward of vmscan_fwd_bidir) unless ``v2``.  The timed region is the whole call."""
     import numpy as np
     import synth
-    cfg = synth.CONFIGS[cfg_id]
+    cfg = with_d_state(cfg_id, d_state)
     if cfg["kind"] != "vim":
-        return bench_ss2d_bwd(cfg_id, steps, warmup, torch, V, with_cpu)
+        return bench_ss2d_bwd(cfg_id, steps, warmup, torch, V, with_cpu, d_state)
     dev = torch.device("cuda", 0)
     dt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
-    p = synth.make_vim_v2_inputs(cfg_id)
+    N = cfg["d_state"]
+    p = synth.make_vim_v2_inputs(cfg_id, d_state=N)
     act = {k: torch.from_numpy(np.ascontiguousarray(p[k])).to(dev).to(dt) for k in VIM_ACT + V2_ACT}
     par = {k: torch.from_numpy(np.ascontiguousarray(p[k])).to(dev) for k in VIM_PAR + V2_PAR}
     if not v2:
@@ -447,7 +455,7 @@ def bench_bwd(cfg_id, steps, warmup, torch, V, v2=False, with_cpu=False):
     g.manual_seed(42_000 + cfg_id)
     dout = torch.randn(act["u"].shape, generator=g, device=dev, dtype=torch.float32).to(dt)
     nb, nd, L = act["u"].shape
-    wsb = V.lib.vmscan_bwd_bidir_v2_workspace_bytes(nb, nd, L, 16, 1 if cfg["dtype"] == "bf16" else 0)
+    wsb = V.lib.vmscan_bwd_bidir_v2_workspace_bytes(nb, nd, L, N, 1 if cfg["dtype"] == "bf16" else 0)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
 
     def call():
@@ -477,7 +485,7 @@ def bench_bwd(cfg_id, steps, warmup, torch, V, v2=False, with_cpu=False):
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": cfg["name"] + ("_sepbwd" if v2 else "") + "_backward", "batch": nb, "dim": nd,
-                   "seqlen": L, "d_state": 16, "io_dtype": cfg["dtype"], "branches": "separate" if v2 else "shared"},
+                   "seqlen": L, "d_state": N, "io_dtype": cfg["dtype"], "branches": "separate" if v2 else "shared"},
         "roofline": {"bound": "alu", "achieved": round(alu / 1e9, 1), "peak": round(ALU_PEAK_BWD_UPD_S / 1e9, 1),
                      "unit": "Gupd/s", "frac": round(alu / ALU_PEAK_BWD_UPD_S, 4), "traffic": None,
                      "kernel": "all kernels of vmscan_bwd_bidir_v2 (forward with saved sum, gate, adjoint scan, "
@@ -602,22 +610,23 @@ def bench_front(cfg_id, steps, warmup, torch, V, with_cpu=False):
     return rec
 
 
-def bench_ss2d_bwd(cfg_id, steps, warmup, torch, V, with_cpu=False):
+def bench_ss2d_bwd(cfg_id, steps, warmup, torch, V, with_cpu=False, d_state=None):
     """Backward pass of the SS2D cross-scan (ss2d_cross_scan_bwd, every gradient, no gate as in
     the 56x56 workload); the timed region is the whole call."""
     import numpy as np
     import synth
-    cfg = synth.CONFIGS[cfg_id]
+    cfg = with_d_state(cfg_id, d_state)
     dev = torch.device("cuda", 0)
     dt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
-    p = synth.make_ss2d_inputs(cfg_id)
+    N = cfg["d_state"]
+    p = synth.make_ss2d_inputs(cfg_id, d_state=N)
     act = {k: torch.from_numpy(np.ascontiguousarray(p[k])).to(dev).to(dt) for k in ("x", "delta_raw", "B", "C")}
     par = {k: torch.from_numpy(np.ascontiguousarray(p[k])).to(dev) for k in ("A_log", "D", "delta_bias")}
     g = torch.Generator(device=dev)
     g.manual_seed(43_000 + cfg_id)
     dout = torch.randn(act["x"].shape, generator=g, device=dev, dtype=torch.float32).to(dt)
     nb, nd, H, W = act["x"].shape
-    wsb = V.lib.ss2d_cross_scan_bwd_workspace_bytes(nb, nd, H, W, 16, 1 if cfg["dtype"] == "bf16" else 0)
+    wsb = V.lib.ss2d_cross_scan_bwd_workspace_bytes(nb, nd, H, W, N, 1 if cfg["dtype"] == "bf16" else 0)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
 
     def call():
@@ -643,7 +652,7 @@ def bench_ss2d_bwd(cfg_id, steps, warmup, torch, V, with_cpu=False):
         "value": toks / (ms * 1e-3), "unit": "tokens·channels/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": cfg["name"] + "_backward", "batch": nb, "dim": nd, "H": H, "W": W, "d_state": 16,
+        "config": {"workload": cfg["name"] + "_backward", "batch": nb, "dim": nd, "H": H, "W": W, "d_state": N,
                    "io_dtype": cfg["dtype"]},
         "roofline": {"bound": "alu", "achieved": round(alu / 1e9, 1), "peak": round(ALU_PEAK_BWD_UPD_S / 1e9, 1),
                      "unit": "Gupd/s", "frac": round(alu / ALU_PEAK_BWD_UPD_S, 4), "traffic": None,
@@ -668,7 +677,7 @@ def main():
     ap.add_argument("--front", action="store_true",
                     help="time the front convolution (conv1d / conv2d + SiLU) followed by the scan")
     ap.add_argument("--d-state", type=int, default=None, choices=(16, 32),
-                    help="state size of the forward workloads (default: the workload's own, 16)")
+                    help="state size of the workloads, forward or backward (default: the workload's own, 16)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (counter calibration for FETCH_SIZE/WRITE_SIZE)")
     ap.add_argument("--summarize-kernels", nargs=3, metavar=("RESULT_DIR", "COMMAND", "OUT_TXT"),
@@ -711,16 +720,13 @@ def main():
         print(json.dumps({"calibration": "copy", "bytes_read_per_dispatch": n * 4, "bytes_written_per_dispatch": n * 4,
                           "dispatches": max(1, args.steps)}), flush=True)
         return
-    if args.bwd and args.d_state not in (None, 16):
-        print("bench.py: the backward pass takes d_state 16 only", file=sys.stderr)
-        sys.exit(2)
     import selective_state_space_41_amd as V
     cfgs = [0, 1, 2, 3, 4] if args.all else [args.config]
     for c in cfgs:
         if args.front:
             rec = bench_front(c, args.steps, args.warmup, torch, V, not args.no_cpu)
         elif args.bwd:
-            rec = bench_bwd(c, args.steps, args.warmup, torch, V, args.v2, not args.no_cpu)
+            rec = bench_bwd(c, args.steps, args.warmup, torch, V, args.v2, not args.no_cpu, args.d_state)
             if rec is None:
                 continue
         else:

@@ -30,7 +30,7 @@
  *   - Activation dtype: VMSCAN_F32 (float) or VMSCAN_BF16 (bfloat16 bit patterns, 2 bytes) for
  *     u/x, delta_raw, z, B, C and out.  A_log, D and delta_bias are always float32.  The state
  *     and all arithmetic are float32; bf16 outputs are rounded to nearest even once, at the store.
- *   - d_state: the forward entry points take 16 or 32, the backward entry points 16 only (else
+ *   - d_state: every scan entry point, forward and backward, takes 16 or 32 (else
  *     VMSCAN_ERR_UNSUPPORTED; the workspace and chunk-length queries return 0).  The pages use
  *     16 and suggest a larger state for high-resolution inputs ([P3] §4.1; [P4] §4.2 gives the
  *     16-32 range).  The workspace size depends on d_state.
@@ -192,7 +192,8 @@ vmscan_status vmscan_fwd_bidir_v2_stage(const void *u, const void *delta_raw, co
  * vmscan_bwd_bidir_v2_workspace_bytes.
  * Gradient outputs must not alias each other or any input.  Validation and error codes as for
  * vmscan_fwd_bidir_v2 (all pointers but the three optional ones are required, all 16-byte
- * aligned); launches are asynchronous on `stream`.  d_state must be 16.
+ * aligned); launches are asynchronous on `stream`.  d_state 16 or 32 (B, C, dB, dC are then
+ * [batch, d_state, seqlen]; A_log, dA_log [dim, d_state]).
  */
 size_t vmscan_bwd_bidir_v2_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen, int d_state,
                                            vmscan_dtype dtype);
@@ -214,8 +215,8 @@ vmscan_status vmscan_bwd_bidir_v2(const void *u, const void *delta_raw, const fl
  * dout = dL/dout [batch, dim, H, W]:
  *   dx                 : [batch, dim, H, W]          activation dtype
  *   ddelta_raw         : [batch, 4, dim, H*W]        activation dtype, each direction's scan order
- *   dB, dC             : [batch, 4, 16, H*W]         activation dtype, each direction's scan order
- *   dA_log             : [4, dim, 16]                float32
+ *   dB, dC             : [batch, 4, N, H*W]          activation dtype, each direction's scan order
+ *   dA_log             : [4, dim, N]                 float32  (N = d_state, 16 or 32)
  *   dD, ddelta_bias    : [4, dim]                    float32
  *   dz                 : [batch, dim, H, W]          activation dtype; NULL exactly when z is NULL
  * Every gradient is written (not accumulated), batch-summed where the tensor has no batch
@@ -225,7 +226,7 @@ vmscan_status vmscan_bwd_bidir_v2(const void *u, const void *delta_raw, const fl
  * library first recomputes the un-gated forward sum for dz.  Workspace:
  * ss2d_cross_scan_bwd_workspace_bytes.  Outputs must not alias each other or any input.
  * Validation and error codes as for ss2d_cross_scan_fwd (z and dz must both be given or both be
- * NULL, else VMSCAN_ERR_NULL); launches are asynchronous on `stream`.  d_state must be 16.
+ * NULL, else VMSCAN_ERR_NULL); launches are asynchronous on `stream`.  d_state 16 or 32.
  */
 size_t ss2d_cross_scan_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t H, int64_t W, int d_state,
                                            vmscan_dtype dtype);

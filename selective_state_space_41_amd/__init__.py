@@ -244,7 +244,7 @@ def vmscan_bwd_bidir_v2(u, delta_raw, delta_bias, u_b, delta_raw_b, delta_bias_b
     du, ddelta_raw, ddelta_bias, du_b, ddelta_raw_b, ddelta_bias_b, dz, dA_log, dA_b_log, dB, dC,
     dB_b, dC_b, dD, dD_b.  With ``shared=True`` (u_b is u, delta_raw_b is delta_raw, delta_bias_b
     is delta_bias, i.e. ``vmscan_fwd_bidir``) the backward branch's du, ddelta_raw and ddelta_bias
-    are added into the forward ones and the ``_b`` entries are None.  d_state 16 only."""
+    are added into the forward ones and the ``_b`` entries are None.  d_state 16 or 32."""
     if u.dim() != 3:
         raise ValueError("u must be [batch, dim, L]")
     nb, nd, L = u.shape
@@ -324,7 +324,7 @@ def ss2d_cross_scan_fwd(x, delta_raw, A_log, B, C, D, delta_bias, z=None, out=No
 
 def ss2d_cross_scan_bwd(x, delta_raw, A_log, B, C, D, delta_bias, z, dout, workspace=None, stream=None):
     """Gradients of ``ss2d_cross_scan_fwd`` for ``dout`` (ss2d_cross_scan_bwd); returns a dict with
-    dx, ddelta_raw, dA_log, dB, dC, dD, ddelta_bias and dz (None when z is None).  d_state 16 only."""
+    dx, ddelta_raw, dA_log, dB, dC, dD, ddelta_bias and dz (None when z is None).  d_state 16 or 32."""
     if x.dim() != 4:
         raise ValueError("x must be [batch, dim, H, W]")
     nb, nd, H, W = x.shape

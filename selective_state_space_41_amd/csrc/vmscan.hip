@@ -51,7 +51,8 @@
 //    stores each direction's state every 8 steps, then the adjoint walk goes back window by
 //    window, rebuilding a window's states from its checkpoint.  Long sequences with few
 //    workgroups are split into chunks; the adjoint carry between chunks comes from per-chunk
-//    records and the same carry prefix run against the scan order.
+//    records and the same carry prefix run against the scan order.  Its state parts are
+//    independent, so its workgroups stay at four waves; d_state 32 runs two per tile.
 //  * The front convolutions that produce the scan input (Vim: causal conv1d + SiLU for both
 //    branches; SS2D: 3 x 3 conv2d + SiLU written row-major and transposed) are streaming kernels.
 
@@ -64,7 +65,7 @@
 
 namespace {
 
-constexpr int kN = 16;                 // d_state of the backward pass; the forward takes 16 or 32
+constexpr int kN = 16;                 // the smaller d_state (four-wave forward workgroup); 32 also taken
 constexpr int kH = 8;                  // states per wave: d_state / 8 waves (parts) per (channel, direction)
 constexpr int kW = 64;                 // channels per workgroup = lanes per wave
 constexpr int kThreads = 4 * kW;       // d_state 16 workgroup: (fwd, lo) (bwd, lo) (fwd, hi) (bwd, hi)
@@ -350,10 +351,8 @@ struct Lane {
   int Kc;
 };
 
-__device__ __forceinline__ Lane lane_ctx(const ScanArgs& a, int bid) {
+__device__ __forceinline__ Lane lane_at(const ScanArgs& a, int tile) {
   Lane l;
-  const int nblocks = a.batch * a.nch * a.ngroups;
-  const int tile = logical_block(bid, nblocks);
   const int g = tile % a.ngroups;
   const int rest = tile / a.ngroups;
   l.c = rest % a.nch;
@@ -366,6 +365,10 @@ __device__ __forceinline__ Lane lane_ctx(const ScanArgs& a, int bid) {
   l.s_lo = static_cast<int64_t>(l.c) * a.K;
   l.Kc = static_cast<int>(a.L - l.s_lo < a.K ? a.L - l.s_lo : a.K);
   return l;
+}
+
+__device__ __forceinline__ Lane lane_ctx(const ScanArgs& a, int bid) {
+  return lane_at(a, logical_block(bid, a.batch * a.nch * a.ngroups));
 }
 
 __device__ __forceinline__ Lane lane_ctx(const ScanArgs& a) { return lane_ctx(a, static_cast<int>(blockIdx.x)); }
@@ -1405,13 +1408,10 @@ vmscan_status run_pair_np(const ScanArgs& a, hipStream_t stream, int stages) {
   return VMSCAN_OK;
 }
 
-// The modes that save float32 sums for the backward pass run with d_state 16 only.
 template <typename T, int MODE>
 vmscan_status run_pair(const ScanArgs& a, hipStream_t stream, int stages) {
   if (a.parts == 2) return run_pair_np<T, MODE, 2>(a, stream, stages);
-  if constexpr (MODE == kModeVim || MODE == kModeFirstPair || MODE == kModeSecondPair) {
-    if (a.parts == 4) return run_pair_np<T, MODE, 4>(a, stream, stages);
-  }
+  if (a.parts == 4) return run_pair_np<T, MODE, 4>(a, stream, stages);
   return VMSCAN_ERR_UNSUPPORTED;
 }
 
@@ -1511,30 +1511,31 @@ vmscan_status vim_args(ScanArgs& a, const void* u, const void* delta_raw, const 
 // dA = Σ λ_t Δ_t a_t h_{t-1} (dA_log = dA A), dD = Σ g_t u_t, dbias = Σ dΔ_raw_t.
 //
 // Stages (one stream): the B/C copy and chunk carries of the forward; the forward scan with the
-// un-gated sum y_f + y_b saved (kModeVimSum); gate_bwd_kernel (g and dz); bwd_scan_kernel, whose
-// four waves per workgroup (direction x state half, lane = channel) each run their direction
-// over the whole sequence twice: forward, storing the state at every 8-step window, then window
-// by window backwards, recomputing the window's states from its checkpoint and walking the
-// adjoint; and three small kernels that sum the partial results (state halves, directions when
+// un-gated sum y_f + y_b saved (kModeVimSum); gate_bwd_kernel (g and dz); the backward kernels,
+// whose four waves per workgroup (direction x state part of 8, lane = channel; d_state 32: two
+// workgroups per tile) each run their direction over the chunk twice: forward, storing the state
+// at every 8-step window (bwd_ckpt_kernel), then window by window backwards, recomputing the
+// window's states from its checkpoint and walking the adjoint (bwd_scan_kernel); and three small
+// kernels that sum the partial results (state parts, directions when
 // the branches share inputs, channel groups, batch) and round.  In base-2 units (Δ2 = Δ log2 e,
 // B' = B ln 2 from the B/C copy): Σ λ B = log2e Σ λ B', du = Δ2 Σ λ B', dB = ln2 λ Δ2 u and
 // dA = ln2 Σ λ Δ2 a h_{t-1}; the ln 2 factors are applied when the partial sums are reduced.
 
 constexpr int kRedCols = 32;              // per lane and reduction round: 2 steps x (8 dB + 8 dC)
 constexpr int kRedStride = kRedCols + 4;  // floats per LDS row (16-byte aligned rows)
-constexpr int kParStride = 16;            // per (batch, direction, half, channel): dA[8], dD, dbias
+constexpr int kParStride = 16;            // per (batch, direction, part, channel): dA[8], dD, dbias
 
 struct BwdArgs {
   ScanArgs s;       // forward arguments: B/C copy (bct), per-direction u, Δ_raw, A_log, D, bias; the
                     // chunking (K, nch) and, for split sequences, the forward carries (agg: the state
                     // entering each chunk)
   const float* g;   // [batch][dim][L]: dout silu(z) / 2
-  float* ck;        // [batch][dir][half][nch * wpc][dim][8]: state entering each window of each chunk
-  float* adj;       // split sequences: [batch][dim][dir][nch][kN + 1] adjoint records, then carries
-  float* gu;        // [dir][half][batch][dim][L]: the half's share of du
-  float* gx;        // [dir][half][batch][dim][L]: the half's share of dΔ_raw
-  float* dbc;       // [dir][group][batch][2][16][L]: sums over the group's channels of λ Δ2 u (dB / ln2), g h (dC)
-  float* dpar;      // [dir][half][dim][kParStride][batch * nch]
+  float* ck;        // [batch][dir][part][nch * wpc][dim][8]: state entering each window of each chunk
+  float* adj;       // split sequences: [batch][dim][dir][nch][ns + 1] adjoint records, then carries
+  float* gu;        // [dir][part][batch][dim][L]: the part's share of du
+  float* gx;        // [dir][part][batch][dim][L]: the part's share of dΔ_raw
+  float* dbc;       // [dir][group][batch][2][ns][L]: sums over the group's channels of λ Δ2 u (dB / ln2), g h (dC)
+  float* dpar;      // [dir][part][dim][kParStride][batch * nch]
   int wpc;          // windows per chunk, ceil(K / 8)
   int fnch, fm;     // the forward's chunk count, and forward chunks per backward chunk
 };
@@ -1631,7 +1632,7 @@ __device__ __forceinline__ void bwd_ckpt_dir(const BwdArgs& ba, const Lane& l) {
   load_a2(da, l, a.ns, A);
   const float bias2 = da.bias[l.dd] * kLog2e;
   const scalar_fp bct = bc_row<DIR>(a, l);
-  float* ckw = ba.ck + ((static_cast<int64_t>(l.b) * 2 + DIR) * 2 + l.part) * a.nch * ba.wpc * a.dim * kH;
+  float* ckw = ba.ck + ((static_cast<int64_t>(l.b) * 2 + DIR) * a.parts + l.part) * a.nch * ba.wpc * a.dim * kH;
   auto ck_at = [&](int w) {
     return ckw + ((static_cast<int64_t>(l.c) * ba.wpc + w) * a.dim + l.dd) * kH;
   };
@@ -1642,7 +1643,7 @@ __device__ __forceinline__ void bwd_ckpt_dir(const BwdArgs& ba, const Lane& l) {
     // where this direction enters: the first, or (backward direction) the last of the chunk's
     const int last = (l.c + 1) * ba.fm < ba.fnch ? (l.c + 1) * ba.fm - 1 : ba.fnch - 1;
     const int cf = DIR == 0 ? l.c * ba.fm : last;
-    const float* e = a.agg + ((((static_cast<int64_t>(l.b) * a.dim + l.dd) * 2 + DIR) * ba.fnch) + cf) * (kN + 1);
+    const float* e = a.agg + ((((static_cast<int64_t>(l.b) * a.dim + l.dd) * 2 + DIR) * ba.fnch) + cf) * (a.ns + 1);
 #pragma unroll
     for (int n = 0; n < kH; ++n) h[n] = e[kH * l.part + n];
   } else {
@@ -1665,17 +1666,30 @@ __device__ __forceinline__ void bwd_ckpt_dir(const BwdArgs& ba, const Lane& l) {
 }
 
 // The backward kernels run one argument set, or two (SETS = 2: the two SS2D pairs in one launch,
-// the first set's workgroups first); both sets have the same workgroup count.
+// the first set's workgroups first); both sets have the same workgroup count and d_state.
+// The backward walks of different state parts are independent, so its workgroups always hold four
+// waves (two directions x two parts): d_state 32 runs two workgroups per (batch, chunk, channel
+// group), adjacent in the XCD-local order (they read the same inputs), the second on parts 2, 3.
+__device__ __forceinline__ int bwd_blocks(const ScanArgs& a) { return a.batch * a.nch * a.ngroups * (a.parts >> 1); }
+
+__device__ __forceinline__ Lane bwd_lane(const ScanArgs& a, int bid) {
+  const int pq = a.parts >> 1;
+  const int t = logical_block(bid, bwd_blocks(a));
+  Lane l = lane_at(a, t / pq);
+  l.part += 2 * (t % pq);
+  return l;
+}
+
 template <typename T, int MODE>
 __device__ __forceinline__ void bwd_ckpt_block(const BwdArgs& ba, int bid) {
-  const Lane l = lane_ctx(ba.s, bid);
+  const Lane l = bwd_lane(ba.s, bid);
   if ((__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6) & 1) == 0) bwd_ckpt_dir<T, MODE, 0>(ba, l);
   else bwd_ckpt_dir<T, MODE, 1>(ba, l);
 }
 
 template <typename T, int MODE, int SETS>
 __global__ __launch_bounds__(kThreads) void bwd_ckpt_kernel(BwdArgs b0, BwdArgs b1) {
-  const int nb = b0.s.batch * b0.s.nch * b0.s.ngroups, bid = static_cast<int>(blockIdx.x);
+  const int nb = bwd_blocks(b0.s), bid = static_cast<int>(blockIdx.x);
   if (SETS == 1 || bid < nb) bwd_ckpt_block<T, MODE>(b0, bid);
   else bwd_ckpt_block<T, MODE>(b1, bid - nb);
 }
@@ -1686,7 +1700,7 @@ __global__ __launch_bounds__(kThreads) void bwd_ckpt_kernel(BwdArgs b0, BwdArgs 
 // the walk started from zero and μ = a λ is what the next chunk in scan order passes back.  So each
 // chunk passes X = a_0 λ_0^0 + (a_0 ... a_{Kc-1}) μ to the previous one: a reverse carry prefix over
 // the records (X, Σ Δ2) gives every chunk its μ.  This pass computes the records: per direction and
-// state half, the walk from zero over the chunk's steps, last first (windows of 8 with the previous
+// state part, the walk from zero over the chunk's steps, last first (windows of 8 with the previous
 // window's loads in flight).  It needs no forward state.
 template <typename T, int MODE, int DIR>
 __device__ __forceinline__ void adj_state_dir(const BwdArgs& ba, const Lane& l) {
@@ -1739,23 +1753,23 @@ __device__ __forceinline__ void adj_state_dir(const BwdArgs& ba, const Lane& l) 
     for (int j = kWin - 1; j >= 0; --j) step(delta2(xr[j], bias2), gg[j], bct + Dr::pos(l, i0 + j) * kBC);
   }
   if (l.valid) {
-    float* rec = ba.adj + ((((static_cast<int64_t>(l.b) * a.dim + l.d) * 2 + DIR) * a.nch) + l.c) * (kN + 1);
+    float* rec = ba.adj + ((((static_cast<int64_t>(l.b) * a.dim + l.d) * 2 + DIR) * a.nch) + l.c) * (a.ns + 1);
 #pragma unroll
     for (int n = 0; n < kH; ++n) rec[kH * l.part + n] = anext[n] * lam[n];  // X = a_0 λ_0
-    if (l.part == 0) rec[kN] = S;
+    if (l.part == 0) rec[a.ns] = S;
   }
 }
 
 template <typename T, int MODE>
 __device__ __forceinline__ void adj_state_block(const BwdArgs& ba, int bid) {
-  const Lane l = lane_ctx(ba.s, bid);
+  const Lane l = bwd_lane(ba.s, bid);
   if ((__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6) & 1) == 0) adj_state_dir<T, MODE, 0>(ba, l);
   else adj_state_dir<T, MODE, 1>(ba, l);
 }
 
 template <typename T, int MODE, int SETS>
 __global__ __launch_bounds__(kThreads) void adj_state_kernel(BwdArgs b0, BwdArgs b1) {
-  const int nb = b0.s.batch * b0.s.nch * b0.s.ngroups, bid = static_cast<int>(blockIdx.x);
+  const int nb = bwd_blocks(b0.s), bid = static_cast<int>(blockIdx.x);
   if (SETS == 1 || bid < nb) adj_state_block<T, MODE>(b0, bid);
   else adj_state_block<T, MODE>(b1, bid - nb);
 }
@@ -1780,7 +1794,7 @@ __device__ __forceinline__ void store_window(float* base, int64_t lo, const floa
   for (int j = 0; j < ns; ++j) base[ASC ? lo + j : lo + kWin - 1 - j] = v[j];
 }
 
-// The adjoint walk of one direction and state half over one chunk, window by window from the last.
+// The adjoint walk of one direction and state part over one chunk, window by window from the last.
 template <typename T, int MODE, int DIR>
 __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float* rows, float* stage) {
   const ScanArgs& a = ba.s;
@@ -1797,7 +1811,7 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
   const float Dh = l.part == 0 ? da.Dp[l.dd] : 0.0f;
   const scalar_fp bct = bc_row<DIR>(a, l);
   const float vmask = l.valid ? 1.0f : 0.0f;  // lanes past the last channel add nothing to dB/dC
-  float* ckw = ba.ck + ((static_cast<int64_t>(l.b) * 2 + DIR) * 2 + l.part) * a.nch * ba.wpc * a.dim * kH;
+  float* ckw = ba.ck + ((static_cast<int64_t>(l.b) * 2 + DIR) * a.parts + l.part) * a.nch * ba.wpc * a.dim * kH;
   auto ck_at = [&](int w) {
     return ckw + ((static_cast<int64_t>(l.c) * ba.wpc + w) * a.dim + l.dd) * kH;
   };
@@ -1806,14 +1820,14 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
   // Backward, window by window from the last.
   const int64_t plane = static_cast<int64_t>(a.batch) * a.dim * a.L;
   const int64_t row = static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(l.dd) * a.L;
-  float* guw = ba.gu + (DIR * 2 + l.part) * plane + row;
-  float* gxw = ba.gx + (DIR * 2 + l.part) * plane + row;
+  float* guw = ba.gu + (DIR * a.parts + l.part) * plane + row;
+  float* gxw = ba.gx + (DIR * a.parts + l.part) * plane + row;
   const int group = l.d / kW;
-  float* dbcw = ba.dbc + ((static_cast<int64_t>(DIR) * a.ngroups + group) * a.batch + l.b) * 2 * kN * a.L;
+  float* dbcw = ba.dbc + ((static_cast<int64_t>(DIR) * a.ngroups + group) * a.batch + l.b) * 2 * a.ns * a.L;
   // The walk starts after the chunk's last step with a λ = μ, passed back by the chunks after it
   // (zero for the last chunk in scan order and for an unsplit sequence).
   float lam[kH], anext[kH], dA[kH];
-  const float* mu = ba.adj ? ba.adj + ((((static_cast<int64_t>(l.b) * a.dim + l.dd) * 2 + DIR) * a.nch) + l.c) * (kN + 1) +
+  const float* mu = ba.adj ? ba.adj + ((((static_cast<int64_t>(l.b) * a.dim + l.dd) * 2 + DIR) * a.nch) + l.c) * (a.ns + 1) +
                                  kH * l.part
                            : nullptr;
 #pragma unroll
@@ -1968,14 +1982,14 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
 #pragma unroll
       for (int j = 0; j < kWin; ++j) v[j] = stage[2 * kWin * kW + l.lane * kWin + j];
       const int64_t slo = Dr::kSidxSgn > 0 ? Dr::sidx(a, l, i0) : Dr::sidx(a, l, i0) - (kWin - 1);
-      store_window<(Dr::kSidxSgn > 0)>(dbcw + (static_cast<int64_t>(ty) * kN + kH * l.part + kk) * a.L, slo, v, ns);
+      store_window<(Dr::kSidxSgn > 0)>(dbcw + (static_cast<int64_t>(ty) * a.ns + kH * l.part + kk) * a.L, slo, v, ns);
     }
     asm volatile("" ::: "memory");
   }
   if (l.valid) {
     // [dir][half][dim][kParStride][batch * nch]: the sums over batch and chunks read contiguous runs
     const int64_t nbc = static_cast<int64_t>(a.batch) * a.nch;
-    float* pp = ba.dpar + ((static_cast<int64_t>(DIR) * 2 + l.part) * a.dim + l.d) * kParStride * nbc +
+    float* pp = ba.dpar + ((static_cast<int64_t>(DIR) * a.parts + l.part) * a.dim + l.d) * kParStride * nbc +
                 static_cast<int64_t>(l.b) * a.nch + l.c;
 #pragma unroll
     for (int n = 0; n < kH; ++n) pp[n * nbc] = dA[n];
@@ -1986,7 +2000,7 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
 
 template <typename T, int MODE>
 __device__ __forceinline__ void bwd_scan_block(const BwdArgs& ba, int bid, float* rows, float* stage) {
-  const Lane l = lane_ctx(ba.s, bid);
+  const Lane l = bwd_lane(ba.s, bid);
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   if ((w & 1) == 0) bwd_dir<T, MODE, 0>(ba, l, rows, stage);
   else bwd_dir<T, MODE, 1>(ba, l, rows, stage);
@@ -1997,20 +2011,26 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdArgs b0, BwdArgs 
   __shared__ __attribute__((aligned(16))) float rows[4][kW * kRedStride];
   __shared__ __attribute__((aligned(16))) float stage[4][kStageFloats];
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-  const int nb = b0.s.batch * b0.s.nch * b0.s.ngroups, bid = static_cast<int>(blockIdx.x);
+  const int nb = bwd_blocks(b0.s), bid = static_cast<int>(blockIdx.x);
   if (SETS == 1 || bid < nb) bwd_scan_block<T, MODE>(b0, bid, rows[w], stage[w]);
   else bwd_scan_block<T, MODE>(b1, bid - nb, rows[w], stage[w]);
 }
 
 // du, dΔ_raw (and the backward branch's, or their sums when the branches share inputs):
-// elementwise over [batch][dim][L], rounded once to the activation dtype.
+// elementwise over [batch][dim][L], the state parts' shares added in float32 and rounded once to
+// the activation dtype.
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_combine_kernel(const float* __restrict__ gu, const float* __restrict__ gx,
-                                                          T* du, T* dx, T* du_b, T* dx_b, int64_t n) {
+                                                          T* du, T* dx, T* du_b, T* dx_b, int64_t n, int parts) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= n) return;
-  const float uf = gu[i] + gu[n + i], ubk = gu[2 * n + i] + gu[3 * n + i];
-  const float xf = gx[i] + gx[n + i], xbk = gx[2 * n + i] + gx[3 * n + i];
+  float uf = 0.0f, ubk = 0.0f, xf = 0.0f, xbk = 0.0f;
+  for (int k = 0; k < parts; ++k) {
+    uf += gu[k * n + i];
+    ubk += gu[(parts + k) * n + i];
+    xf += gx[k * n + i];
+    xbk += gx[(parts + k) * n + i];
+  }
   if (du_b) {
     st_act(du, i, uf);
     st_act(du_b, i, ubk);
@@ -2028,23 +2048,23 @@ __global__ __launch_bounds__(256) void bwd_combine_kernel(const float* __restric
 // dB, dC, dB_b, dC_b: the channel-group partial sums added up (dB scaled by ln 2), rounded once.
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_bc_kernel(const float* __restrict__ dbc, T* dB, T* dC, T* dB_b, T* dC_b,
-                                                     int batch, int ngroups, int64_t L, int64_t out_bstride) {
-  const int64_t per = static_cast<int64_t>(batch) * 2 * kN * L;  // one (dir, group) block
+                                                     int batch, int ngroups, int64_t L, int64_t out_bstride, int ns) {
+  const int64_t per = static_cast<int64_t>(batch) * 2 * ns * L;  // one (dir, group) block
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= 2 * per) return;
   const int dir = static_cast<int>(i / per);
   const int64_t r = i - dir * per;                    // (b, type, n, pos)
   float s = 0.0f;
   for (int gi = 0; gi < ngroups; ++gi) s += dbc[(static_cast<int64_t>(dir) * ngroups + gi) * per + r];
-  const int64_t bb = r / (2 * kN * L);
-  const int64_t rest = r - bb * 2 * kN * L;
-  const int ty = static_cast<int>(rest / (kN * L));
-  const int64_t o = bb * out_bstride + (rest - ty * kN * L);  // (b, n, index); [16][L] per batch
+  const int64_t bb = r / (2 * ns * L);
+  const int64_t rest = r - bb * 2 * ns * L;
+  const int ty = static_cast<int>(rest / (ns * L));
+  const int64_t o = bb * out_bstride + (rest - ty * ns * L);  // (b, n, index); [ns][L] per batch
   T* dst = ty == 0 ? (dir == 0 ? dB : dB_b) : (dir == 0 ? dC : dC_b);
   st_act(dst, o, ty == 0 ? s * kLn2 : s);
 }
 
-// dA_log, dD, dbias per direction: sums over batch (and state halves); for shared inputs
+// dA_log, dD, dbias per direction: sums over batch (and state parts); for shared inputs
 // (dbias_b NULL) the backward branch's dbias is added to the forward one.  One wave per output
 // value: the lanes take batch entries (contiguous in the partial-sum layout) and a butterfly
 // adds them up.
@@ -2059,21 +2079,21 @@ __device__ __forceinline__ float wave_batch_sum(const float* p, int batch, int l
 __global__ __launch_bounds__(256) void bwd_param_kernel(const float* __restrict__ dpar, const float* A_log,
                                                         const float* A_b_log, float* dA_log, float* dA_b_log,
                                                         float* dD, float* dD_b, float* dbias, float* dbias_b,
-                                                        int batch, int dim) {
+                                                        int batch, int dim, int ns) {
   // items: (dir, d, n) for dA_log, then (dir, d, {dD, dbias})
   const int item = blockIdx.x * 4 + static_cast<int>(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int nA = 2 * dim * kN;
+  const int nA = 2 * dim * ns, parts = ns / kH;
   if (item >= nA + 4 * dim) return;
-  auto at = [&](int dr, int hf, int k) {
-    return dpar + ((static_cast<int64_t>(dr) * 2 + hf) * dim) * kParStride * batch + static_cast<int64_t>(k) * batch;
+  auto at = [&](int dr, int pt, int k) {
+    return dpar + ((static_cast<int64_t>(dr) * parts + pt) * dim) * kParStride * batch + static_cast<int64_t>(k) * batch;
   };
   if (item < nA) {
-    const int dir = item / (dim * kN), d = (item / kN) % dim, n = item % kN;
+    const int dir = item / (dim * ns), d = (item / ns) % dim, n = item % ns;
     const float s = wave_batch_sum(at(dir, n / kH, n % kH) + static_cast<int64_t>(d) * kParStride * batch, batch, lane);
     if (lane == 0) {
-      const float An = -__expf((dir == 0 ? A_log : A_b_log)[static_cast<int64_t>(d) * kN + n]);
-      (dir == 0 ? dA_log : dA_b_log)[static_cast<int64_t>(d) * kN + n] = s * kLn2 * An;
+      const float An = -__expf((dir == 0 ? A_log : A_b_log)[static_cast<int64_t>(d) * ns + n]);
+      (dir == 0 ? dA_log : dA_b_log)[static_cast<int64_t>(d) * ns + n] = s * kLn2 * An;
     }
     return;
   }
@@ -2085,68 +2105,76 @@ __global__ __launch_bounds__(256) void bwd_param_kernel(const float* __restrict_
     return;
   }
   if (dir == 1 && !dbias_b) return;  // added into dbias by the forward item
-  float s = wave_batch_sum(at(dir, 0, kH + 1) + off, batch, lane) + wave_batch_sum(at(dir, 1, kH + 1) + off, batch, lane);
+  float s = 0.0f;
+  for (int pt = 0; pt < parts; ++pt) s += wave_batch_sum(at(dir, pt, kH + 1) + off, batch, lane);
   if (dir == 0 && !dbias_b)
-    s += wave_batch_sum(at(1, 0, kH + 1) + off, batch, lane) + wave_batch_sum(at(1, 1, kH + 1) + off, batch, lane);
+    for (int pt = 0; pt < parts; ++pt) s += wave_batch_sum(at(1, pt, kH + 1) + off, batch, lane);
   if (lane == 0) (dir == 0 ? dbias : dbias_b)[d] = s;
 }
 
-// out[b][r] (batch stride out_bstride) = the sum of up to five float32 planes [batch][n_b] at
-// (b, r), in float32, rounded once to O.  Used for the SS2D gradients: dx from the row pair's
-// four partial planes plus the transposed column-pair plane, dΔ_raw per direction from its two
-// state halves.
+// out[b][r] (batch stride out_bstride) = the sum of np float32 planes [batch][n_b] (plane k at
+// base + k * pstride) and, if given, one more plane `extra`, at (b, r), in float32, rounded once
+// to O.  Used for the SS2D gradients: dx from the row pair's partial planes (two directions x the
+// state parts) plus the transposed column-pair plane, dΔ_raw per direction from its state parts.
 template <typename O>
-__global__ __launch_bounds__(256) void sum_planes_kernel(const float* p0, const float* p1, const float* p2,
-                                                         const float* p3, const float* p4, O* out, int64_t n_b,
-                                                         int batch, int64_t out_bstride) {
+__global__ __launch_bounds__(256) void sum_planes_kernel(const float* base, int np, int64_t pstride,
+                                                         const float* extra, O* out, int64_t n_b, int batch,
+                                                         int64_t out_bstride) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= n_b * batch) return;
-  float s = p0[i] + p1[i];
-  if (p2) s += p2[i] + p3[i];
-  if (p4) s += p4[i];
+  float s = 0.0f;
+  for (int k = 0; k < np; ++k) s += base[k * pstride + i];
+  if (extra) s += extra[i];
   const int64_t b = i / n_b;
   st_act(out, b * out_bstride + (i - b * n_b), s);
 }
 
 // Backward buffers that depend on the chunking (the forward's: chunks of Kf): checkpoints of every
 // window of every chunk, the adjoint records (split sequences only) and the per-chunk parameter sums.
-size_t ck_bytes(int64_t batch, int64_t dim, int64_t L, int64_t Kf) {
-  return round256(static_cast<size_t>(batch) * 2 * 2 * ceil_div(L, Kf) * ceil_div(Kf, kWin) * dim * kH * sizeof(float));
+size_t ck_bytes(int64_t batch, int64_t dim, int64_t L, int64_t Kf, int ns) {
+  return round256(static_cast<size_t>(batch) * 2 * (ns / kH) * ceil_div(L, Kf) * ceil_div(Kf, kWin) * dim * kH *
+                  sizeof(float));
 }
-size_t dpar_bytes(int64_t batch, int64_t dim, int64_t L, int64_t Kf) {
-  return round256(static_cast<size_t>(batch) * ceil_div(L, Kf) * 2 * 2 * dim * kParStride * sizeof(float));
+size_t dpar_bytes(int64_t batch, int64_t dim, int64_t L, int64_t Kf, int ns) {
+  return round256(static_cast<size_t>(batch) * ceil_div(L, Kf) * 2 * (ns / kH) * dim * kParStride * sizeof(float));
+}
+// the dB / dC partial sums: [dir][group][batch][2][ns][L]
+size_t dbc_bytes(int64_t batch, int64_t dim, int64_t L, int ns) {
+  return round256(static_cast<size_t>(2) * groups(dim) * batch * 2 * ns * L * sizeof(float));
 }
 
 struct BwdLayout {
   size_t bct, agg, ysum, g, ck, adj, gu, gx, dbc, dpar, total;
 };
 
-BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t L, int64_t Kf) {
+// The planes of du / dΔ_raw shares are [dir][part][batch][dim][L], each plane rounded up to 256 bytes
+// only as a whole block: the kernels index plane k at k * batch * dim * L elements.
+BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t L, int64_t Kf, int ns) {
   BwdLayout w{};
+  const size_t planes = round256(static_cast<size_t>(2) * (ns / kH) * batch * dim * L * sizeof(float));
   const size_t plane = round256(static_cast<size_t>(batch) * dim * L * sizeof(float));
-  const int64_t Kb = bwd_chunk(batch * groups(dim), L, Kf);
+  const int64_t Kb = bwd_chunk(plan_base(batch, dim, ns), L, Kf);
   w.bct = 0;
-  w.agg = w.bct + bct_bytes(batch, L);
-  w.ysum = w.agg + agg_bytes(batch, dim, L, Kf);
+  w.agg = w.bct + bct_bytes(batch, L, ns);
+  w.ysum = w.agg + agg_bytes(batch, dim, L, Kf, ns);
   w.g = w.ysum + plane;
   w.ck = w.g + plane;
-  w.adj = w.ck + ck_bytes(batch, dim, L, Kb);
-  w.gu = w.adj + agg_bytes(batch, dim, L, Kb);
-  w.gx = w.gu + 4 * plane;
-  w.dbc = w.gx + 4 * plane;
-  w.dpar = w.dbc + round256(static_cast<size_t>(2) * groups(dim) * batch * 2 * kN * L * sizeof(float));
-  w.total = w.dpar + dpar_bytes(batch, dim, L, Kb);
+  w.adj = w.ck + ck_bytes(batch, dim, L, Kb, ns);
+  w.gu = w.adj + agg_bytes(batch, dim, L, Kb, ns);
+  w.gx = w.gu + planes;
+  w.dbc = w.gx + planes;
+  w.dpar = w.dbc + dbc_bytes(batch, dim, L, ns);
+  w.total = w.dpar + dpar_bytes(batch, dim, L, Kb, ns);
   return w;
 }
 
 // Checkpoints, then (split sequences) the adjoint records and their reverse carry prefix, then the
-// adjoint walk; every kernel runs one workgroup per (batch, chunk, channel group).
-// every kernel runs one workgroup per (set, batch, chunk, channel group).  SETS = 2 runs b0 and b1
-// (same shapes and chunking) in the same launches.
+// adjoint walk; every kernel runs one workgroup per (set, batch, chunk, channel group, pair of
+// state parts).  SETS = 2 runs b0 and b1 (same shapes, d_state and chunking) in the same launches.
 template <typename T, int MODE, int SETS>
 vmscan_status launch_bwd_scans(const BwdArgs& b0, const BwdArgs& b1, hipStream_t stream) {
   const ScanArgs& a = b0.s;
-  const int64_t nblocks = static_cast<int64_t>(a.batch) * a.nch * a.ngroups * SETS;
+  const int64_t nblocks = static_cast<int64_t>(a.batch) * a.nch * a.ngroups * (a.parts / 2) * SETS;
   if (nblocks >= (int64_t{1} << 31)) return VMSCAN_ERR_SHAPE;
   const dim3 grid(static_cast<unsigned>(nblocks));
   hipLaunchKernelGGL((bwd_ckpt_kernel<T, MODE, SETS>), grid, dim3(kThreads), 0, stream, b0, b1);
@@ -2156,7 +2184,7 @@ vmscan_status launch_bwd_scans(const BwdArgs& b0, const BwdArgs& b1, hipStream_t
     hipLaunchKernelGGL((adj_state_kernel<T, MODE, SETS>), grid, dim3(kThreads), 0, stream, b0, b1);
     e = hipGetLastError();
     if (e != hipSuccess) return launch_failed(e);
-    const int64_t pblocks = ceil_div(static_cast<int64_t>(a.batch) * a.dim * 2 * kN, 256);
+    const int64_t pblocks = ceil_div(static_cast<int64_t>(a.batch) * a.dim * 2 * a.ns, 256);
     for (int k = 0; k < SETS; ++k) {
       const BwdArgs& b = k == 0 ? b0 : b1;
       hipLaunchKernelGGL(carry_prefix_kernel, dim3(static_cast<unsigned>(pblocks)), dim3(256), 0, stream, b.s, b.adj, 1);
@@ -2175,8 +2203,9 @@ vmscan_status run_bwd(const ScanArgs& fwd, const BwdLayout& lay, unsigned char* 
                       void* du, void* dx, float* dbias, void* du_b, void* dx_b, float* dbias_b, void* dz,
                       const float* A_log, const float* A_b_log, float* dA_log, float* dA_b_log, void* dB, void* dC,
                       void* dB_b, void* dC_b, float* dD, float* dD_b, hipStream_t stream) {
+  const int ns = fwd.ns;
   const int64_t n = static_cast<int64_t>(fwd.batch) * fwd.dim * fwd.L;
-  const int64_t nbc = static_cast<int64_t>(2) * fwd.batch * 2 * kN * fwd.L;
+  const int64_t nbc = static_cast<int64_t>(2) * fwd.batch * 2 * ns * fwd.L;
   if (ceil_div(n, 256) >= (int64_t{1} << 31) || ceil_div(nbc, 256) >= (int64_t{1} << 31)) return VMSCAN_ERR_SHAPE;
   float* ysum = reinterpret_cast<float*>(wsp + lay.ysum);
   float* g = reinterpret_cast<float*>(wsp + lay.g);
@@ -2191,7 +2220,7 @@ vmscan_status run_bwd(const ScanArgs& fwd, const BwdLayout& lay, unsigned char* 
   if (e != hipSuccess) return launch_failed(e);
   BwdArgs ba{};
   ba.s = fwd;  // the forward's carries (the state entering each forward chunk) are in agg
-  const int64_t Kb = bwd_chunk(static_cast<int64_t>(fwd.batch) * fwd.ngroups, fwd.L, fwd.K);
+  const int64_t Kb = bwd_chunk(plan_base(fwd.batch, fwd.dim, ns), fwd.L, fwd.K);
   ba.s.K = static_cast<int>(Kb);
   ba.s.nch = static_cast<int>(ceil_div(fwd.L, Kb));
   ba.fnch = ba.s.nch > 1 ? fwd.nch : 1;  // an unsplit walk starts from zero and reads no carries
@@ -2208,13 +2237,13 @@ vmscan_status run_bwd(const ScanArgs& fwd, const BwdLayout& lay, unsigned char* 
   if (st != VMSCAN_OK) return st;
   hipLaunchKernelGGL(bwd_combine_kernel<T>, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, stream,
                      ba.gu, ba.gx, static_cast<T*>(du), static_cast<T*>(dx), static_cast<T*>(du_b),
-                     static_cast<T*>(dx_b), n);
+                     static_cast<T*>(dx_b), n, fwd.parts);
   hipLaunchKernelGGL(bwd_bc_kernel<T>, dim3(static_cast<unsigned>(ceil_div(nbc, 256))), dim3(256), 0, stream, ba.dbc,
                      static_cast<T*>(dB), static_cast<T*>(dC), static_cast<T*>(dB_b), static_cast<T*>(dC_b), fwd.batch,
-                     fwd.ngroups, fwd.L, kN * fwd.L);
-  hipLaunchKernelGGL(bwd_param_kernel, dim3(static_cast<unsigned>(ceil_div(2 * fwd.dim * kN + 4 * fwd.dim, 4))), dim3(256), 0,
-                     stream, ba.dpar, A_log, A_b_log, dA_log, dA_b_log, dD, dD_b, dbias, dbias_b,
-                     fwd.batch * ba.s.nch, fwd.dim);
+                     fwd.ngroups, fwd.L, static_cast<int64_t>(ns) * fwd.L, ns);
+  hipLaunchKernelGGL(bwd_param_kernel, dim3(static_cast<unsigned>(ceil_div(2 * fwd.dim * ns + 4 * fwd.dim, 4))),
+                     dim3(256), 0, stream, ba.dpar, A_log, A_b_log, dA_log, dA_b_log, dD, dD_b, dbias, dbias_b,
+                     fwd.batch * ba.s.nch, fwd.dim, ns);
   e = hipGetLastError();
   return e == hipSuccess ? VMSCAN_OK : launch_failed(e);
 }
@@ -2236,11 +2265,12 @@ struct Ss2dBwdLayout {
   size_t total;
 };
 
-Ss2dBwdLayout ss2d_bwd_layout(int64_t batch, int64_t dim, int64_t L, int64_t Kf, size_t esz) {
+Ss2dBwdLayout ss2d_bwd_layout(int64_t batch, int64_t dim, int64_t L, int64_t Kf, size_t esz, int ns) {
   Ss2dBwdLayout w{};
-  w.f = ss2d_layout(batch, dim, L, Kf, esz);
+  w.f = ss2d_layout(batch, dim, L, Kf, esz, ns);
   const size_t plane = round256(static_cast<size_t>(batch) * dim * L * sizeof(float));
-  const int64_t Kb = bwd_chunk(batch * groups(dim), L, Kf);
+  const size_t planes = round256(static_cast<size_t>(2) * (ns / kH) * batch * dim * L * sizeof(float));
+  const int64_t Kb = bwd_chunk(plan_base(batch, dim, ns), L, Kf);
   w.ysum = round256(w.f.total);
   w.g = w.ysum + plane;
   w.gcol = w.g + plane;
@@ -2252,22 +2282,22 @@ Ss2dBwdLayout ss2d_bwd_layout(int64_t batch, int64_t dim, int64_t L, int64_t Kf,
       q.agg = w.f.agg;
     } else {
       q.bct = o;
-      o += bct_bytes(batch, L);
+      o += bct_bytes(batch, L, ns);
       q.agg = o;
-      o += agg_bytes(batch, dim, L, Kf);
+      o += agg_bytes(batch, dim, L, Kf, ns);
     }
     q.ck = o;
-    o += ck_bytes(batch, dim, L, Kb);
+    o += ck_bytes(batch, dim, L, Kb, ns);
     q.adj = o;
-    o += agg_bytes(batch, dim, L, Kb);
+    o += agg_bytes(batch, dim, L, Kb, ns);
     q.gu = o;
-    o += 4 * plane;
+    o += planes;
     q.gx = o;
-    o += 4 * plane;
+    o += planes;
     q.dbc = o;
-    o += round256(static_cast<size_t>(2) * groups(dim) * batch * 2 * kN * L * sizeof(float));
+    o += dbc_bytes(batch, dim, L, ns);
     q.dpar = o;
-    o += dpar_bytes(batch, dim, L, Kb);
+    o += dpar_bytes(batch, dim, L, Kb, ns);
   }
   w.total = o;
   return w;
@@ -2284,7 +2314,7 @@ vmscan_status ss2d_pair_prepare(const BwdArgs& ba, hipStream_t stream) {
 }
 
 // ... and after it: dΔ_raw, dB, dC and the parameter sums written for both directions.  The pair's
-// du (four float32 planes in position order) stays in ba.gu.
+// du (2 x parts float32 planes in position order) stays in ba.gu.
 template <typename T>
 vmscan_status ss2d_pair_post(const BwdArgs& ba, int k0, int k1, void* ddelta_raw, void* dB, void* dC, float* dA_log,
                              const float* A_log, float* dD, float* ddelta_bias, hipStream_t stream) {
@@ -2294,20 +2324,21 @@ vmscan_status ss2d_pair_post(const BwdArgs& ba, int k0, int k1, void* ddelta_raw
   const int64_t plane = n;
   T* ddr = static_cast<T*>(ddelta_raw);
   const dim3 pg(static_cast<unsigned>(ceil_div(n, 256)));
-  hipLaunchKernelGGL(sum_planes_kernel<T>, pg, dim3(256), 0, stream, ba.gx, ba.gx + plane, nullptr, nullptr, nullptr,
-                     ddr + k0 * DL, DL, a.batch, 4 * DL);
-  hipLaunchKernelGGL(sum_planes_kernel<T>, pg, dim3(256), 0, stream, ba.gx + 2 * plane, ba.gx + 3 * plane, nullptr,
-                     nullptr, nullptr, ddr + k1 * DL, DL, a.batch, 4 * DL);
-  const int64_t NL = static_cast<int64_t>(kN) * a.L;
+  hipLaunchKernelGGL(sum_planes_kernel<T>, pg, dim3(256), 0, stream, ba.gx, a.parts, plane, nullptr, ddr + k0 * DL, DL,
+                     a.batch, 4 * DL);
+  hipLaunchKernelGGL(sum_planes_kernel<T>, pg, dim3(256), 0, stream, ba.gx + a.parts * plane, a.parts, plane, nullptr,
+                     ddr + k1 * DL, DL, a.batch, 4 * DL);
+  const int ns = a.ns;
+  const int64_t NL = static_cast<int64_t>(ns) * a.L;
   const int64_t nbc = static_cast<int64_t>(2) * a.batch * 2 * NL;
   hipLaunchKernelGGL(bwd_bc_kernel<T>, dim3(static_cast<unsigned>(ceil_div(nbc, 256))), dim3(256), 0, stream, ba.dbc,
                      static_cast<T*>(dB) + k0 * NL, static_cast<T*>(dC) + k0 * NL, static_cast<T*>(dB) + k1 * NL,
-                     static_cast<T*>(dC) + k1 * NL, a.batch, a.ngroups, a.L, 4 * NL);
-  const int64_t dN = static_cast<int64_t>(a.dim) * kN;
-  hipLaunchKernelGGL(bwd_param_kernel, dim3(static_cast<unsigned>(ceil_div(2 * a.dim * kN + 4 * a.dim, 4))), dim3(256),
+                     static_cast<T*>(dC) + k1 * NL, a.batch, a.ngroups, a.L, 4 * NL, ns);
+  const int64_t dN = static_cast<int64_t>(a.dim) * ns;
+  hipLaunchKernelGGL(bwd_param_kernel, dim3(static_cast<unsigned>(ceil_div(2 * a.dim * ns + 4 * a.dim, 4))), dim3(256),
                      0, stream, ba.dpar, A_log + k0 * dN, A_log + k1 * dN, dA_log + k0 * dN, dA_log + k1 * dN,
                      dD + k0 * a.dim, dD + k1 * a.dim, ddelta_bias + k0 * a.dim, ddelta_bias + k1 * a.dim,
-                     a.batch * a.nch, a.dim);
+                     a.batch * a.nch, a.dim, ns);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? VMSCAN_OK : launch_failed(e);
 }
@@ -2316,7 +2347,7 @@ template <typename T>
 vmscan_status run_ss2d_bwd(const void* x, const void* delta_raw, const float* A_log, const void* B, const void* C,
                            const float* D, const float* delta_bias, const void* z, const void* dout, void* dx,
                            void* ddelta_raw, float* dA_log, void* dB, void* dC, float* dD, float* ddelta_bias,
-                           void* dz, int64_t batch, int64_t dim, int64_t H, int64_t W, unsigned char* wsp,
+                           void* dz, int64_t batch, int64_t dim, int64_t H, int64_t W, int ns, unsigned char* wsp,
                            const Ss2dBwdLayout& lay, int64_t Kf, hipStream_t stream) {
   const int64_t L = H * W;
   const size_t esz = sizeof(T);
@@ -2326,15 +2357,15 @@ vmscan_status run_ss2d_bwd(const void* x, const void* delta_raw, const float* A_
     return static_cast<const void*>(static_cast<const unsigned char*>(p) + elems * static_cast<int64_t>(esz));
   };
   auto dir_args = [&](const void* u, int k, int rev) {
-    return DirArgs{u, off(delta_raw, k * dim * L), 4 * dim * L, off(B, k * kN * L), off(C, k * kN * L), 4 * kN * L,
-                   A_log + k * dim * kN, D + k * dim, delta_bias + k * dim, rev};
+    return DirArgs{u, off(delta_raw, k * dim * L), 4 * dim * L, off(B, k * ns * L), off(C, k * ns * L), 4 * ns * L,
+                   A_log + k * dim * ns, D + k * dim, delta_bias + k * dim, rev};
   };
   float* ysum = reinterpret_cast<float*>(wsp + lay.ysum);
   float* g = reinterpret_cast<float*>(wsp + lay.g);
   float* gcol = reinterpret_cast<float*>(wsp + lay.gcol);
   ScanArgs a{};
-  a.ns = kN;
-  a.parts = kN / kH;
+  a.ns = ns;
+  a.parts = ns / kH;
   a.u_bs = dim * L;
   a.z = nullptr;
   a.bct = reinterpret_cast<float*>(wsp + lay.f.bct);
@@ -2376,7 +2407,7 @@ vmscan_status run_ss2d_bwd(const void* x, const void* delta_raw, const float* A_
   // own buffers: the column pair (directions 1 and 3 over x^T, g in column order) and the row
   // pair (directions 0 and 2 over x, g in row order).
   BwdArgs bp[2];
-  const int64_t Kb = bwd_chunk(batch * a.ngroups, L, Kf);
+  const int64_t Kb = bwd_chunk(plan_base(batch, dim, ns), L, Kf);
   for (int k = 0; k < 2; ++k) {
     BwdArgs& ba = bp[k];
     const PairBufs& q = lay.p[k];
@@ -2406,11 +2437,11 @@ vmscan_status run_ss2d_bwd(const void* x, const void* delta_raw, const float* A_
   const BwdArgs& ba = bp[0];
   st = ss2d_pair_post<T>(bp[0], 1, 3, ddelta_raw, dB, dC, dA_log, A_log, dD, ddelta_bias, stream);
   if (st != VMSCAN_OK) return st;
-  // its du back to row-major pixels: sum the four partial planes (column order), transpose
+  // its du back to row-major pixels: sum the partial planes (column order), transpose
   float* col = reinterpret_cast<float*>(wsp + lay.f.col_img);
   float* rowp = reinterpret_cast<float*>(wsp + lay.f.row_img);
   hipLaunchKernelGGL(sum_planes_kernel<float>, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, stream,
-                     ba.gu, ba.gu + n, ba.gu + 2 * n, ba.gu + 3 * n, nullptr, col, n, 1, n);
+                     ba.gu, 2 * a.parts, n, nullptr, col, n, 1, n);
   st = launch_transpose(col, rowp, nimg, static_cast<int>(W), static_cast<int>(H), 4, stream);
   if (st != VMSCAN_OK) return st;
   // the row pair's gradients, and dx = its du plus the column pair's, transposed
@@ -2418,7 +2449,7 @@ vmscan_status run_ss2d_bwd(const void* x, const void* delta_raw, const float* A_
   st = ss2d_pair_post<T>(br, 0, 2, ddelta_raw, dB, dC, dA_log, A_log, dD, ddelta_bias, stream);
   if (st != VMSCAN_OK) return st;
   hipLaunchKernelGGL(sum_planes_kernel<T>, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, stream, br.gu,
-                     br.gu + n, br.gu + 2 * n, br.gu + 3 * n, rowp, static_cast<T*>(dx), n, 1, n);
+                     2 * a.parts, n, rowp, static_cast<T*>(dx), n, 1, n);
   e = hipGetLastError();
   return e == hipSuccess ? VMSCAN_OK : launch_failed(e);
 }
@@ -2436,7 +2467,7 @@ const char* vmscan_status_string(vmscan_status s) {
     case VMSCAN_ERR_NULL: return "VMSCAN_ERR_NULL: a required pointer is NULL";
     case VMSCAN_ERR_SHAPE: return "VMSCAN_ERR_SHAPE: a size is < 1 or too large";
     case VMSCAN_ERR_UNSUPPORTED:
-      return "VMSCAN_ERR_UNSUPPORTED: d_state must be 16 or 32 (16 for the backward passes) and dtype F32 or BF16";
+      return "VMSCAN_ERR_UNSUPPORTED: d_state must be 16 or 32 and dtype F32 or BF16";
     case VMSCAN_ERR_ALIGN: return "VMSCAN_ERR_ALIGN: a pointer is not 16-byte aligned";
     case VMSCAN_ERR_WORKSPACE: return "VMSCAN_ERR_WORKSPACE: workspace missing or too small";
     case VMSCAN_ERR_HIP: return "VMSCAN_ERR_HIP: a HIP call failed (see vmscan_last_hip_error)";
@@ -2477,8 +2508,8 @@ vmscan_status vmscan_fwd_bidir_ex(const void* u, const void* delta_raw, const vo
 
 size_t vmscan_bwd_bidir_v2_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen, int d_state,
                                            vmscan_dtype dtype) {
-  if (!shape_ok(batch, dim, seqlen) || d_state != kN || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16)) return 0;
-  return bwd_layout(batch, dim, seqlen, plan_chunk(batch * groups(dim), seqlen, 0)).total;
+  if (!shape_ok(batch, dim, seqlen) || !d_state_ok(d_state) || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16)) return 0;
+  return bwd_layout(batch, dim, seqlen, plan_chunk(plan_base(batch, dim, d_state), seqlen, 0), d_state).total;
 }
 
 vmscan_status vmscan_bwd_bidir_v2(const void* u, const void* delta_raw, const float* delta_bias, const void* u_b,
@@ -2494,14 +2525,14 @@ vmscan_status vmscan_bwd_bidir_v2(const void* u, const void* delta_raw, const fl
   for (const void* p : need)
     if (!p) return VMSCAN_ERR_NULL;
   if (!shape_ok(batch, dim, seqlen)) return VMSCAN_ERR_SHAPE;
-  if (d_state != kN || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16)) return VMSCAN_ERR_UNSUPPORTED;
+  if (!d_state_ok(d_state) || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16)) return VMSCAN_ERR_UNSUPPORTED;
   const void* opt[] = {du_b, ddelta_raw_b, ddelta_bias_b};
   for (const void* p : need)
     if (!aligned16(p)) return VMSCAN_ERR_ALIGN;
   for (const void* p : opt)
     if (p && !aligned16(p)) return VMSCAN_ERR_ALIGN;
-  const int64_t Kf = plan_chunk(batch * groups(dim), seqlen, 0);
-  const BwdLayout lay = bwd_layout(batch, dim, seqlen, Kf);
+  const int64_t Kf = plan_chunk(plan_base(batch, dim, d_state), seqlen, 0);
+  const BwdLayout lay = bwd_layout(batch, dim, seqlen, Kf, d_state);
   ScanArgs a{};
   // The forward arguments; its output pointer is unused in the sum-saving mode.
   vmscan_status st = vim_args(a, u, delta_raw, delta_bias, u_b, delta_raw_b, delta_bias_b, z, A_log, A_b_log, B, C,
@@ -2753,8 +2784,10 @@ size_t ss2d_cross_scan_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t H
                                            vmscan_dtype dtype) {
   if (H < 1 || W < 1 || H >= (int64_t{1} << 31) || W >= (int64_t{1} << 31)) return 0;
   const int64_t L = H * W;
-  if (!shape_ok(batch, dim, L) || d_state != kN || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16)) return 0;
-  return ss2d_bwd_layout(batch, dim, L, plan_chunk(batch * groups(dim), L, 0), dtype == VMSCAN_F32 ? 4 : 2).total;
+  if (!shape_ok(batch, dim, L) || !d_state_ok(d_state) || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16)) return 0;
+  return ss2d_bwd_layout(batch, dim, L, plan_chunk(plan_base(batch, dim, d_state), L, 0), dtype == VMSCAN_F32 ? 4 : 2,
+                         d_state)
+      .total;
 }
 
 vmscan_status ss2d_cross_scan_bwd(const void* x, const void* delta_raw, const float* A_log, const void* B,
@@ -2771,21 +2804,21 @@ vmscan_status ss2d_cross_scan_bwd(const void* x, const void* delta_raw, const fl
   if (H < 1 || W < 1 || H >= (int64_t{1} << 31) || W >= (int64_t{1} << 31)) return VMSCAN_ERR_SHAPE;
   const int64_t L = H * W;
   if (!shape_ok(batch, dim, L)) return VMSCAN_ERR_SHAPE;
-  if (d_state != kN || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16)) return VMSCAN_ERR_UNSUPPORTED;
+  if (!d_state_ok(d_state) || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16)) return VMSCAN_ERR_UNSUPPORTED;
   for (const void* p : ptrs)
     if (!aligned16(p)) return VMSCAN_ERR_ALIGN;
   if (z && (!aligned16(z) || !aligned16(dz))) return VMSCAN_ERR_ALIGN;
-  const int64_t Kf = plan_chunk(batch * groups(dim), L, 0);
+  const int64_t Kf = plan_chunk(plan_base(batch, dim, d_state), L, 0);
   const size_t esz = dtype == VMSCAN_F32 ? 4 : 2;
-  const Ss2dBwdLayout lay = ss2d_bwd_layout(batch, dim, L, Kf, esz);
+  const Ss2dBwdLayout lay = ss2d_bwd_layout(batch, dim, L, Kf, esz, d_state);
   const vmscan_status ws = check_workspace(workspace, workspace_bytes, lay.total);
   if (ws != VMSCAN_OK) return ws;
   unsigned char* wsp = static_cast<unsigned char*>(workspace);
   return dtype == VMSCAN_F32
              ? run_ss2d_bwd<float>(x, delta_raw, A_log, B, C, D, delta_bias, z, dout, dx, ddelta_raw, dA_log, dB, dC,
-                                   dD, ddelta_bias, dz, batch, dim, H, W, wsp, lay, Kf, stream)
+                                   dD, ddelta_bias, dz, batch, dim, H, W, d_state, wsp, lay, Kf, stream)
              : run_ss2d_bwd<uint16_t>(x, delta_raw, A_log, B, C, D, delta_bias, z, dout, dx, ddelta_raw, dA_log, dB,
-                                      dC, dD, ddelta_bias, dz, batch, dim, H, W, wsp, lay, Kf, stream);
+                                      dC, dD, ddelta_bias, dz, batch, dim, H, W, d_state, wsp, lay, Kf, stream);
 }
 
 vmscan_status ss2d_cross_scan_fwd(const void* x, const void* delta_raw, const float* A_log, const void* B,

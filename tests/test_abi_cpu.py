@@ -233,20 +233,25 @@ def test_ss2d_d_state(lib):
         assert _ss(lib, _good_ptrs(8), ds=ds) == ERR_UNSUPPORTED, ds
 
 
-def test_bwd_d_state_16_only(lib):
-    """The backward entry points take d_state 16 only: 32 is rejected before anything runs."""
+def test_bwd_d_state(lib):
+    """The backward entry points take d_state 16 or 32 (parts of 8 states); any other size is
+    rejected before anything runs, and d_state 32 needs more workspace than 16."""
     lib.vmscan_bwd_bidir_v2_workspace_bytes.restype = ctypes.c_size_t
     lib.ss2d_cross_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
-    assert lib.vmscan_bwd_bidir_v2_workspace_bytes(I64(2), I64(16), I64(8), 16, 1) > 0
-    assert lib.vmscan_bwd_bidir_v2_workspace_bytes(I64(2), I64(16), I64(8), 32, 1) == 0
-    assert lib.ss2d_cross_scan_bwd_workspace_bytes(I64(2), I64(16), I64(4), I64(5), 16, 1) > 0
-    assert lib.ss2d_cross_scan_bwd_workspace_bytes(I64(2), I64(16), I64(4), I64(5), 32, 1) == 0
-    vim = [VP(p) for p in _good_ptrs(31)] + [I64(2), I64(16), I64(8), ctypes.c_int(32), ctypes.c_int(1),
-                                             VP(0x100000), ctypes.c_size_t(1 << 30), VP(0)]
-    assert lib.vmscan_bwd_bidir_v2(*vim) == ERR_UNSUPPORTED
-    ss = [VP(p) for p in _good_ptrs(17)] + [I64(2), I64(16), I64(4), I64(5), ctypes.c_int(32), ctypes.c_int(1),
-                                            VP(0x100000), ctypes.c_size_t(1 << 30), VP(0)]
-    assert lib.ss2d_cross_scan_bwd(*ss) == ERR_UNSUPPORTED
+    v16 = lib.vmscan_bwd_bidir_v2_workspace_bytes(I64(2), I64(16), I64(8), 16, 1)
+    v32 = lib.vmscan_bwd_bidir_v2_workspace_bytes(I64(2), I64(16), I64(8), 32, 1)
+    s16 = lib.ss2d_cross_scan_bwd_workspace_bytes(I64(2), I64(16), I64(4), I64(5), 16, 1)
+    s32 = lib.ss2d_cross_scan_bwd_workspace_bytes(I64(2), I64(16), I64(4), I64(5), 32, 1)
+    assert 0 < v16 < v32 and 0 < s16 < s32
+    for bad in (0, 8, 24, 64):
+        assert lib.vmscan_bwd_bidir_v2_workspace_bytes(I64(2), I64(16), I64(8), bad, 1) == 0, bad
+        assert lib.ss2d_cross_scan_bwd_workspace_bytes(I64(2), I64(16), I64(4), I64(5), bad, 1) == 0, bad
+        vim = [VP(p) for p in _good_ptrs(31)] + [I64(2), I64(16), I64(8), ctypes.c_int(bad), ctypes.c_int(1),
+                                                 VP(0x100000), ctypes.c_size_t(1 << 30), VP(0)]
+        assert lib.vmscan_bwd_bidir_v2(*vim) == ERR_UNSUPPORTED, bad
+        ss = [VP(p) for p in _good_ptrs(17)] + [I64(2), I64(16), I64(4), I64(5), ctypes.c_int(bad),
+                                                ctypes.c_int(1), VP(0x100000), ctypes.c_size_t(1 << 30), VP(0)]
+        assert lib.ss2d_cross_scan_bwd(*ss) == ERR_UNSUPPORTED, bad
 
 
 def _c1(lib, ptrs, nb=2, nd=16, L=8, K=4, dt=1):

@@ -203,3 +203,84 @@ def test_ss2d_bwd_config4_sampled():
     gsub = run_ss2d_bwd(sub, np.ascontiguousarray(dout[bsel]))
     for k in ("dA_log", "dD", "ddelta_bias"):
         _report(f"ss2d bwd config 4 shape, batches 0,31 as a batch: {k}", O.rel_err(gsub[k], ref[k]), 2e-2)
+
+
+def test_bwd_very_long_sequence():
+    """The backward pass over 30001 tokens of one batch row (hundreds of chunks in the forward,
+    tens in the backward), float32."""
+    p = synth.make_vim_v2_inputs(0, layer=991, batch=1, dim=64, seqlen=30001, dtype="f32")
+    dout = _dout(p, 11)
+    got, ref = run_bwd(p, dout), oracle_bwd(p, dout)
+    for k in GRADS:
+        _report(f"bwd L=30001 {k}", O.rel_err(got[k], ref[k]), 1e-5)
+
+
+BWD32_SHAPES = [(1, 16, 1), (2, 17, 9), (1, 40, 33), (2, 24, 197), (3, 70, 64)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", BWD32_SHAPES, ids=[f"b{b}d{d}l{l}" for b, d, l in BWD32_SHAPES])
+def test_bwd_d_state32_small(shape, dtype):
+    """d_state 32: two workgroups per channel group, each on two of the four 8-state parts."""
+    nb, nd, L = shape
+    p = synth.make_vim_v2_inputs(0, layer=1600 + L, batch=nb, dim=nd, seqlen=L, d_state=32, dtype=dtype)
+    dout = _dout(p, L + 1)
+    got, ref = run_bwd(p, dout), oracle_bwd(p, dout)
+    for k in GRADS:
+        _report(f"bwd n32 {shape} {dtype} {k}", O.rel_err(got[k], ref[k]), TOL[dtype])
+
+
+@pytest.mark.parametrize("L", [65, 1001])
+def test_bwd_d_state32_chunk_boundaries(L):
+    """d_state 32 over sequences the backward splits (carries of 32 states and ΣΔ per chunk)."""
+    p = synth.make_vim_v2_inputs(0, layer=1900 + L, batch=1, dim=24, seqlen=L, d_state=32, dtype="f32")
+    dout = _dout(p, L + 2)
+    got, ref = run_bwd(p, dout), oracle_bwd(p, dout)
+    for k in GRADS:
+        _report(f"bwd n32 L={L} {k}", O.rel_err(got[k], ref[k]), 1e-5)
+
+
+def test_bwd_d_state32_shared_inputs():
+    p = synth.make_vim_v2_inputs(0, layer=17, batch=2, dim=48, seqlen=77, d_state=32, dtype="f32")
+    dout = _dout(p, 4)
+    got, ref = run_bwd(p, dout, shared=True), oracle_bwd(p, dout, shared=True)
+    for k, rk in (("du", ("du", "du_b")), ("ddelta_raw", ("ddelta_raw", "ddelta_raw_b")),
+                  ("ddelta_bias", ("ddelta_bias", "ddelta_bias_b"))):
+        _report(f"bwd n32 shared {k}", O.rel_err(got[k], ref[rk[0]] + ref[rk[1]]), 1e-5)
+
+
+def test_bwd_d_state32_config1_sampled():
+    """The Vim-Ti shape (B128 D384 L197 bf16) at d_state 32, as the bench's d_state-32 backward
+    leg runs it: per-batch gradients on sampled batches; the batch-summed parameter gradients on
+    those batches run as a batch of their own."""
+    p = synth.make_vim_v2_inputs(1, d_state=32)
+    dout = _dout(p, 6)
+    got = run_bwd(p, dout)
+    bsel = np.array([0, 64, 127])
+    ref = oracle_bwd(p, dout, batches=bsel)
+    for k in PER_BATCH:
+        _report(f"bwd n32 config 1 {k} (batches 0,64,127)", O.rel_err(got[k][bsel], ref[k]), 2e-2)
+    per = ("u", "delta_raw", "u_b", "delta_raw_b", "z", "B", "C", "B_b", "C_b")
+    sub = {k: (v[bsel] if k in per else v) for k, v in p.items()}
+    gsub = run_bwd(sub, np.ascontiguousarray(dout[bsel]))
+    for k in ("ddelta_bias", "ddelta_bias_b", "dA_log", "dA_b_log", "dD", "dD_b"):
+        _report(f"bwd n32 config 1 shape, batches 0,64,127 as a batch: {k}", O.rel_err(gsub[k], ref[k]), 2e-2)
+
+
+SS2D32_SHAPES = [(1, 16, 1, 1), (2, 5, 3, 4), (1, 17, 7, 9), (1, 4, 67, 70)]
+
+
+@pytest.mark.parametrize("gated", [False, True])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", SS2D32_SHAPES, ids=[f"b{b}d{d}h{h}w{w}" for b, d, h, w in SS2D32_SHAPES])
+def test_ss2d_bwd_d_state32(shape, dtype, gated):
+    nb, nd, H, W = shape
+    p = synth.make_ss2d_inputs(4, layer=1700 + H * 31 + W, batch=nb, dim=nd, H=H, W=W, d_state=32, dtype=dtype,
+                               with_z=gated)
+    dout = _dout(dict(u=p["x"], dtype=dtype), H * W + 3)
+    got, ref = run_ss2d_bwd(p, dout), oracle_ss2d_bwd(p, dout)
+    for k in SS2D_GRADS:
+        if ref[k] is None:
+            assert got[k] is None
+            continue
+        _report(f"ss2d bwd n32 {shape} {dtype} gated={gated} {k}", O.rel_err(got[k], ref[k]), TOL[dtype])

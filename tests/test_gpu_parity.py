@@ -273,3 +273,10 @@ def test_config4_d_state32_sampled():
     p = synth.make_ss2d_inputs(4, d_state=32)
     bsel = np.array([17])
     _report("config 4 N=32 (batch 17)", O.rel_err(run_ss2d(p)[bsel], oracle_ss2d(p, batches=bsel)), 2e-2)
+
+
+def test_vim_very_long_sequence():
+    """70001 tokens for one batch row of 64 channels: hundreds of chunks, so the carry prefix walks
+    a long chain (float32, tight tolerance)."""
+    p = synth.make_vim_inputs(0, layer=990, batch=1, dim=64, seqlen=70001, dtype="f32")
+    _report("vim L=70001", O.rel_err(run_vim(p), oracle_vim(p)), 1e-5)
