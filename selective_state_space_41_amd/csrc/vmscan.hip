@@ -1532,8 +1532,8 @@ struct BwdArgs {
   const float* g;   // [batch][dim][L]: dout silu(z) / 2
   float* ck;        // [batch][dir][part][nch * wpc][dim][8]: state entering each window of each chunk
   float* adj;       // split sequences: [batch][dim][dir][nch][ns + 1] adjoint records, then carries
-  float* gu;        // [dir][part][batch][dim][L]: the part's share of du
-  float* gx;        // [dir][part][batch][dim][L]: the part's share of dΔ_raw
+  float* gu;        // [dir][part / 2][batch][dim][L]: the share of du of a pair of state parts
+  float* gx;        // [dir][part / 2][batch][dim][L]: the share of dΔ_raw of a pair of state parts
   float* dbc;       // [dir][group][batch][2][ns][L]: sums over the group's channels of λ Δ2 u (dB / ln2), g h (dC)
   float* dpar;      // [dir][part][dim][kParStride][batch * nch]
   int wpc;          // windows per chunk, ceil(K / 8)
@@ -1796,7 +1796,7 @@ __device__ __forceinline__ void store_window(float* base, int64_t lo, const floa
 
 // The adjoint walk of one direction and state part over one chunk, window by window from the last.
 template <typename T, int MODE, int DIR>
-__device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float* rows, float* stage) {
+__device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float* rows, float* stage, int* pf) {
   const ScanArgs& a = ba.s;
   using Dr = Dir<MODE, DIR>;
   constexpr bool kRevOrder = Dr::kPosSgn < 0;  // window positions descend with the step
@@ -1820,8 +1820,9 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
   // Backward, window by window from the last.
   const int64_t plane = static_cast<int64_t>(a.batch) * a.dim * a.L;
   const int64_t row = static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(l.dd) * a.L;
-  float* guw = ba.gu + (DIR * a.parts + l.part) * plane + row;
-  float* gxw = ba.gx + (DIR * a.parts + l.part) * plane + row;
+  // one plane per direction and pair of parts: [dir][part / 2][batch][dim][L]
+  float* guw = ba.gu + (DIR * (a.parts / 2) + l.part / 2) * plane + row;
+  float* gxw = ba.gx + (DIR * (a.parts / 2) + l.part / 2) * plane + row;
   const int group = l.d / kW;
   float* dbcw = ba.dbc + ((static_cast<int64_t>(DIR) * a.ngroups + group) * a.batch + l.b) * 2 * a.ns * a.L;
   // The walk starts after the chunk's last step with a λ = μ, passed back by the chunks after it
@@ -1837,6 +1838,7 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
     dA[n] = 0.0f;
   }
   float dD = 0.0f, dbias = 0.0f;
+  int nstaged = 0;  // windows staged so far
   float* myrow = rows + l.lane * kRedStride;
   RevWin<T, MODE, DIR> rw;
   const int nwin = (L + kWin - 1) / kWin;
@@ -1909,6 +1911,8 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
       // hiding Δ2 from the compiler stops it from reusing the earlier values.
 #pragma unroll
       for (int j = j0; j < j0 + 4; ++j) asm volatile("" : "+v"(d2[j]));
+      // the upper part's staging area is free once the lower part has read the previous window
+      if (hf == 1 && (l.part & 1)) unit_wait(&pf[1], nstaged);
       float bc0[kBC], bc1[kBC];
       load_bc(bc_at(j0 + 3), bc1);
 #pragma unroll
@@ -1961,18 +1965,25 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
         }
       }
     }
-    // The window's outputs, from the staging area: a wave's LDS accesses execute in order, so every
-    // value is written before it is read here (and read before the next window overwrites it).
-    asm volatile("" ::: "memory");
-    if (l.valid) {
+    // The window's outputs, from the staging areas.  The workgroup's two waves of this direction
+    // (parts p and p + 1: waves w and w + 2) walk the same steps: the upper part publishes its du
+    // and dΔ_raw shares (pf[0] = windows staged), the lower part adds them to its own, stores the
+    // sums and releases the upper part's staging area (pf[1] = windows consumed).  A wave's LDS
+    // accesses execute in order, so data written before a flag is seen by whoever sees the flag,
+    // and its own dB/dC sums are written before it reads them.
+    ++nstaged;
+    if (l.part & 1) unit_signal(&pf[0], nstaged);
+    else unit_wait(&pf[0], nstaged);
+    if ((l.part & 1) == 0 && l.valid) {
+      const float* up = stage + 2 * kStageFloats;  // wave w + 2
       float v[kWin];
 #pragma unroll
-      for (int j = 0; j < kWin; ++j) v[j] = stage[j * kW + l.lane];
+      for (int j = 0; j < kWin; ++j) v[j] = stage[j * kW + l.lane] + up[j * kW + l.lane];
       const int64_t plo = Dr::kPosSgn > 0 ? Dr::pos(l, i0) : Dr::pos(l, i0) - (kWin - 1);
       store_window<(Dr::kPosSgn > 0)>(guw, plo, v, ns);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < kWin; ++j) v[j] = stage[(kWin + j) * kW + l.lane];
+      for (int j = 0; j < kWin; ++j) v[j] = stage[(kWin + j) * kW + l.lane] + up[(kWin + j) * kW + l.lane];
       const int64_t slo = Dr::kSidxSgn > 0 ? Dr::sidx(a, l, i0) : Dr::sidx(a, l, i0) - (kWin - 1);
       store_window<(Dr::kSidxSgn > 0)>(gxw, slo, v, ns);  // Δ_raw's own storage order
     }
@@ -1984,6 +1995,7 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
       const int64_t slo = Dr::kSidxSgn > 0 ? Dr::sidx(a, l, i0) : Dr::sidx(a, l, i0) - (kWin - 1);
       store_window<(Dr::kSidxSgn > 0)>(dbcw + (static_cast<int64_t>(ty) * a.ns + kH * l.part + kk) * a.L, slo, v, ns);
     }
+    if ((l.part & 1) == 0) unit_signal(&pf[1], nstaged);
     asm volatile("" ::: "memory");
   }
   if (l.valid) {
@@ -1999,37 +2011,43 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
 }
 
 template <typename T, int MODE>
-__device__ __forceinline__ void bwd_scan_block(const BwdArgs& ba, int bid, float* rows, float* stage) {
+__device__ __forceinline__ void bwd_scan_block(const BwdArgs& ba, int bid, float* rows, float* stage, int (*pflag)[2]) {
   const Lane l = bwd_lane(ba.s, bid);
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-  if ((w & 1) == 0) bwd_dir<T, MODE, 0>(ba, l, rows, stage);
-  else bwd_dir<T, MODE, 1>(ba, l, rows, stage);
+  if ((w & 1) == 0) bwd_dir<T, MODE, 0>(ba, l, rows, stage, pflag[0]);
+  else bwd_dir<T, MODE, 1>(ba, l, rows, stage, pflag[1]);
 }
 
 template <typename T, int MODE, int SETS>
 __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdArgs b0, BwdArgs b1) {
   __shared__ __attribute__((aligned(16))) float rows[4][kW * kRedStride];
   __shared__ __attribute__((aligned(16))) float stage[4][kStageFloats];
+  __shared__ int pflag[2][2];  // per direction: windows staged by the upper part, consumed by the lower
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  if (threadIdx.x < 4) pflag[threadIdx.x >> 1][threadIdx.x & 1] = 0;
+  __syncthreads();
   const int nb = bwd_blocks(b0.s), bid = static_cast<int>(blockIdx.x);
-  if (SETS == 1 || bid < nb) bwd_scan_block<T, MODE>(b0, bid, rows[w], stage[w]);
-  else bwd_scan_block<T, MODE>(b1, bid - nb, rows[w], stage[w]);
+  // one copy of the body: the argument set is picked by address (both live in the kernel
+  // argument segment)
+  const bool first = SETS == 1 || bid < nb;
+  const BwdArgs* ba = first ? &b0 : &b1;
+  bwd_scan_block<T, MODE>(*ba, first ? bid : bid - nb, rows[w], stage[w], pflag);
 }
 
 // du, dΔ_raw (and the backward branch's, or their sums when the branches share inputs):
-// elementwise over [batch][dim][L], the state parts' shares added in float32 and rounded once to
-// the activation dtype.
+// elementwise over [batch][dim][L], the np shares per direction (one per pair of state parts)
+// added in float32 and rounded once to the activation dtype.
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_combine_kernel(const float* __restrict__ gu, const float* __restrict__ gx,
-                                                          T* du, T* dx, T* du_b, T* dx_b, int64_t n, int parts) {
+                                                          T* du, T* dx, T* du_b, T* dx_b, int64_t n, int np) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= n) return;
   float uf = 0.0f, ubk = 0.0f, xf = 0.0f, xbk = 0.0f;
-  for (int k = 0; k < parts; ++k) {
+  for (int k = 0; k < np; ++k) {
     uf += gu[k * n + i];
-    ubk += gu[(parts + k) * n + i];
+    ubk += gu[(np + k) * n + i];
     xf += gx[k * n + i];
-    xbk += gx[(parts + k) * n + i];
+    xbk += gx[(np + k) * n + i];
   }
   if (du_b) {
     st_act(du, i, uf);
@@ -2114,8 +2132,9 @@ __global__ __launch_bounds__(256) void bwd_param_kernel(const float* __restrict_
 
 // out[b][r] (batch stride out_bstride) = the sum of np float32 planes [batch][n_b] (plane k at
 // base + k * pstride) and, if given, one more plane `extra`, at (b, r), in float32, rounded once
-// to O.  Used for the SS2D gradients: dx from the row pair's partial planes (two directions x the
-// state parts) plus the transposed column-pair plane, dΔ_raw per direction from its state parts.
+// to O.  Used for the SS2D gradients: dx from the row pair's partial planes (two directions x
+// pairs of state parts) plus the transposed column-pair plane, dΔ_raw per direction from its
+// planes.
 template <typename O>
 __global__ __launch_bounds__(256) void sum_planes_kernel(const float* base, int np, int64_t pstride,
                                                          const float* extra, O* out, int64_t n_b, int batch,
@@ -2147,11 +2166,11 @@ struct BwdLayout {
   size_t bct, agg, ysum, g, ck, adj, gu, gx, dbc, dpar, total;
 };
 
-// The planes of du / dΔ_raw shares are [dir][part][batch][dim][L], each plane rounded up to 256 bytes
-// only as a whole block: the kernels index plane k at k * batch * dim * L elements.
+// The planes of du / dΔ_raw shares are [dir][part / 2][batch][dim][L], rounded up to 256 bytes only
+// as a whole block: the kernels index plane k at k * batch * dim * L elements.
 BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t L, int64_t Kf, int ns) {
   BwdLayout w{};
-  const size_t planes = round256(static_cast<size_t>(2) * (ns / kH) * batch * dim * L * sizeof(float));
+  const size_t planes = round256(static_cast<size_t>(2) * (ns / kH / 2) * batch * dim * L * sizeof(float));
   const size_t plane = round256(static_cast<size_t>(batch) * dim * L * sizeof(float));
   const int64_t Kb = bwd_chunk(plan_base(batch, dim, ns), L, Kf);
   w.bct = 0;
@@ -2237,7 +2256,7 @@ vmscan_status run_bwd(const ScanArgs& fwd, const BwdLayout& lay, unsigned char* 
   if (st != VMSCAN_OK) return st;
   hipLaunchKernelGGL(bwd_combine_kernel<T>, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, stream,
                      ba.gu, ba.gx, static_cast<T*>(du), static_cast<T*>(dx), static_cast<T*>(du_b),
-                     static_cast<T*>(dx_b), n, fwd.parts);
+                     static_cast<T*>(dx_b), n, fwd.parts / 2);
   hipLaunchKernelGGL(bwd_bc_kernel<T>, dim3(static_cast<unsigned>(ceil_div(nbc, 256))), dim3(256), 0, stream, ba.dbc,
                      static_cast<T*>(dB), static_cast<T*>(dC), static_cast<T*>(dB_b), static_cast<T*>(dC_b), fwd.batch,
                      fwd.ngroups, fwd.L, static_cast<int64_t>(ns) * fwd.L, ns);
@@ -2269,7 +2288,7 @@ Ss2dBwdLayout ss2d_bwd_layout(int64_t batch, int64_t dim, int64_t L, int64_t Kf,
   Ss2dBwdLayout w{};
   w.f = ss2d_layout(batch, dim, L, Kf, esz, ns);
   const size_t plane = round256(static_cast<size_t>(batch) * dim * L * sizeof(float));
-  const size_t planes = round256(static_cast<size_t>(2) * (ns / kH) * batch * dim * L * sizeof(float));
+  const size_t planes = round256(static_cast<size_t>(2) * (ns / kH / 2) * batch * dim * L * sizeof(float));
   const int64_t Kb = bwd_chunk(plan_base(batch, dim, ns), L, Kf);
   w.ysum = round256(w.f.total);
   w.g = w.ysum + plane;
@@ -2314,7 +2333,7 @@ vmscan_status ss2d_pair_prepare(const BwdArgs& ba, hipStream_t stream) {
 }
 
 // ... and after it: dΔ_raw, dB, dC and the parameter sums written for both directions.  The pair's
-// du (2 x parts float32 planes in position order) stays in ba.gu.
+// du (parts float32 planes in position order: two directions x parts / 2) stays in ba.gu.
 template <typename T>
 vmscan_status ss2d_pair_post(const BwdArgs& ba, int k0, int k1, void* ddelta_raw, void* dB, void* dC, float* dA_log,
                              const float* A_log, float* dD, float* ddelta_bias, hipStream_t stream) {
@@ -2324,9 +2343,10 @@ vmscan_status ss2d_pair_post(const BwdArgs& ba, int k0, int k1, void* ddelta_raw
   const int64_t plane = n;
   T* ddr = static_cast<T*>(ddelta_raw);
   const dim3 pg(static_cast<unsigned>(ceil_div(n, 256)));
-  hipLaunchKernelGGL(sum_planes_kernel<T>, pg, dim3(256), 0, stream, ba.gx, a.parts, plane, nullptr, ddr + k0 * DL, DL,
+  const int np = a.parts / 2;  // planes per direction
+  hipLaunchKernelGGL(sum_planes_kernel<T>, pg, dim3(256), 0, stream, ba.gx, np, plane, nullptr, ddr + k0 * DL, DL,
                      a.batch, 4 * DL);
-  hipLaunchKernelGGL(sum_planes_kernel<T>, pg, dim3(256), 0, stream, ba.gx + a.parts * plane, a.parts, plane, nullptr,
+  hipLaunchKernelGGL(sum_planes_kernel<T>, pg, dim3(256), 0, stream, ba.gx + np * plane, np, plane, nullptr,
                      ddr + k1 * DL, DL, a.batch, 4 * DL);
   const int ns = a.ns;
   const int64_t NL = static_cast<int64_t>(ns) * a.L;
@@ -2441,7 +2461,7 @@ vmscan_status run_ss2d_bwd(const void* x, const void* delta_raw, const float* A_
   float* col = reinterpret_cast<float*>(wsp + lay.f.col_img);
   float* rowp = reinterpret_cast<float*>(wsp + lay.f.row_img);
   hipLaunchKernelGGL(sum_planes_kernel<float>, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, stream,
-                     ba.gu, 2 * a.parts, n, nullptr, col, n, 1, n);
+                     ba.gu, a.parts, n, nullptr, col, n, 1, n);
   st = launch_transpose(col, rowp, nimg, static_cast<int>(W), static_cast<int>(H), 4, stream);
   if (st != VMSCAN_OK) return st;
   // the row pair's gradients, and dx = its du plus the column pair's, transposed
@@ -2449,7 +2469,7 @@ vmscan_status run_ss2d_bwd(const void* x, const void* delta_raw, const float* A_
   st = ss2d_pair_post<T>(br, 0, 2, ddelta_raw, dB, dC, dA_log, A_log, dD, ddelta_bias, stream);
   if (st != VMSCAN_OK) return st;
   hipLaunchKernelGGL(sum_planes_kernel<T>, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, stream, br.gu,
-                     2 * a.parts, n, rowp, static_cast<T*>(dx), n, 1, n);
+                     a.parts, n, rowp, static_cast<T*>(dx), n, 1, n);
   e = hipGetLastError();
   return e == hipSuccess ? VMSCAN_OK : launch_failed(e);
 }
