@@ -218,6 +218,8 @@ struct ScanArgs {
   int64_t L;
   int dim, batch, K, nch, ngroups;
   int ns, parts;   // d_state and its parts of 8 states (one wave per direction and part)
+  float* ck;       // kModeVimSum of an unsplit sequence, or null: the state entering each window of
+  int ck_wpc;      // the two-phase walk, [batch][dir][part][ck_wpc][dim][8] (the backward checkpoints)
 };
 
 // kModeVimSum: Vim order, but the epilogue stores the un-gated fp32 sum y_f + y_b to wsy;
@@ -681,7 +683,9 @@ __global__ __launch_bounds__(256) void carry_prefix_kernel(ScanArgs a, float* re
 // barrier separates the phases and one precedes the epilogue.  For an odd chunk both
 // directions reach the middle token at their last phase-0 step; the backward value of that step
 // goes to the spare slot Kc, which the backward part-0 wave folds into the middle slot after
-// the phase barrier.  After both phases every row holds y_f + y_b.
+// the phase barrier.  After both phases every row holds y_f + y_b.  In kModeVimSum with a
+// checkpoint buffer the walk also stores the state entering each of its windows and single-step
+// runs, which the backward walk then visits in the same two-phase schedule.
 
 // LDS update of one value by part 0: a write (PHASE 0) or an add (PHASE 1).
 template <int PHASE>
@@ -689,13 +693,41 @@ __device__ __forceinline__ void lds_first(float* slot, float v) {
   *slot = PHASE == 1 ? *slot + v : v;
 }
 
+// Eight consecutive values of one lane, stored as one 16-byte (bf16) or two 16-byte (fp32) writes.
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const float (&v)[kWin]);
+template <>
+__device__ __forceinline__ void store8(uint16_t* p, const float (&v)[kWin]) {
+  uint32_t w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    w[k] = static_cast<uint32_t>(f32_to_bf16_rne(v[2 * k])) | (static_cast<uint32_t>(f32_to_bf16_rne(v[2 * k + 1])) << 16);
+  const uint4 r = make_uint4(w[0], w[1], w[2], w[3]);
+  __builtin_memcpy(p, &r, sizeof(r));
+}
+template <>
+__device__ __forceinline__ void store8(float* p, const float (&v)[kWin]) {
+  const float4 r0 = make_float4(v[0], v[1], v[2], v[3]), r1 = make_float4(v[4], v[5], v[6], v[7]);
+  __builtin_memcpy(p, &r0, sizeof(r0));
+  __builtin_memcpy(p + 4, &r1, sizeof(r1));
+}
+
 template <typename T, int MODE, int DIR, int PHASE, int NP>
 __device__ __forceinline__ void run_phase(const ScanArgs& a, const Lane& l, const DirArgs& da, float bias, float Dh,
                                           int i_begin, int n_win, int i_end, int spare_step, const float (&A2)[kH],
                                           float (&h)[kH], scalar_fp bct, float (&bcA)[kBC], float (&bcB)[kBC],
-                                          float* myY, int* flags, int& unit) {
+                                          float* myY, int* flags, int& unit, int slot0) {
   Window<T, MODE, DIR> win;
   const int full_end = i_begin + n_win * kWin;
+  // kModeVimSum with a checkpoint buffer: the state entering each window and the single steps
+  // (slots slot0, slot0 + 1, ...), for the backward walk.
+  float* ckp = nullptr;
+  if constexpr (MODE == kModeVimSum) {
+    if (a.ck)
+      ckp = a.ck + ((static_cast<int64_t>(l.b) * 2 + DIR) * a.parts + l.part) * a.ck_wpc * a.dim * kH +
+            (static_cast<int64_t>(slot0) * a.dim + l.dd) * kH;
+  }
+  const int64_t ck_slot = static_cast<int64_t>(a.dim) * kH;  // floats per slot
   constexpr int kStep = DIR == 0 ? 1 : -1;  // LDS row direction of consecutive steps
   if (full_end > i_begin) win.load(a, l, da, i_begin);
   // Part 0: in the second phase its slots already hold the other direction's values, which are
@@ -731,6 +763,9 @@ __device__ __forceinline__ void run_phase(const ScanArgs& a, const Lane& l, cons
       for (int j = 0; j < kWin; ++j) myY[pp + kStep * j] = r[j] + yp[j];
       if (relay) unit_signal(own_flag, unit);
     }
+    if constexpr (MODE == kModeVimSum) {
+      if (ckp && l.valid) store8(ckp + ((i0 - i_begin) / kWin) * ck_slot, h);
+    }
     run_steps<MODE, DIR>(l, i0, dl, du, yi, A2, h, bcA, bcB, bct, y);
     ++unit;
     if (lo) {
@@ -748,6 +783,9 @@ __device__ __forceinline__ void run_phase(const ScanArgs& a, const Lane& l, cons
 #pragma unroll
     for (int j = 0; j < kWin; ++j) myY[pp + kStep * j] += yp[j];
     if (relay) unit_signal(own_flag, unit);
+  }
+  if constexpr (MODE == kModeVimSum) {
+    if (ckp && l.valid && full_end < i_end) store8(ckp + n_win * ck_slot, h);
   }
   for (int i = full_end; i < i_end; ++i) {
     float dl;
@@ -804,36 +842,18 @@ __device__ __forceinline__ void scan_pair_dir(const ScanArgs& a, const Lane& l, 
   const int nw0 = (odd ? M - 1 : M) / kWin;
   const int spare = (DIR == 1 && odd) ? M - 1 : -1;
   int unit = 0;
-  run_phase<T, MODE, DIR, 0, NP>(a, l, da, bias, Dh, 0, nw0, M, spare, A2, h, bct, bcA, bcB, myY, flags, unit);
+  run_phase<T, MODE, DIR, 0, NP>(a, l, da, bias, Dh, 0, nw0, M, spare, A2, h, bct, bcA, bcB, myY, flags, unit, 0);
   __syncthreads();
   // Fold the backward value of an odd chunk's middle token (kept in the spare slot) into the
   // middle slot; no wave touches either slot in the second phase.
   if (DIR == 1 && odd && l.part == 0) myY[M - 1] += myY[Kc];
   epi_prefetch<T, MODE, NP>(a, l, epi);
   run_phase<T, MODE, DIR, 1, NP>(a, l, da, bias, Dh, M, (Kc - M) / kWin, Kc, -1, A2, h, bct, bcA, bcB, myY, flags,
-                                 unit);
+                                 unit, nw0 + (nw0 * kWin < M ? 1 : 0));
 }
 
 // Combined value of chunk position q of LDS row c.
 __device__ __forceinline__ float row_val(const float* ybuf, int ybs, int c, int q) { return ybuf[c * ybs + q]; }
-
-template <typename T>
-__device__ __forceinline__ void store8(T* p, const float (&v)[kWin]);
-template <>
-__device__ __forceinline__ void store8(uint16_t* p, const float (&v)[kWin]) {
-  uint32_t w[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k)
-    w[k] = static_cast<uint32_t>(f32_to_bf16_rne(v[2 * k])) | (static_cast<uint32_t>(f32_to_bf16_rne(v[2 * k + 1])) << 16);
-  const uint4 r = make_uint4(w[0], w[1], w[2], w[3]);
-  __builtin_memcpy(p, &r, sizeof(r));
-}
-template <>
-__device__ __forceinline__ void store8(float* p, const float (&v)[kWin]) {
-  const float4 r0 = make_float4(v[0], v[1], v[2], v[3]), r1 = make_float4(v[4], v[5], v[6], v[7]);
-  __builtin_memcpy(p, &r0, sizeof(r0));
-  __builtin_memcpy(p + 4, &r1, sizeof(r1));
-}
 
 // Outputs of one chunk from the combined LDS rows.  Row-major order: the chunk's part of each
 // channel row is cut into groups of 8 positions; the threads take groups in turn (consecutive
@@ -1536,7 +1556,8 @@ struct BwdArgs {
   float* gx;        // [dir][part / 2][batch][dim][L]: the share of dΔ_raw of a pair of state parts
   float* dbc;       // [dir][group][batch][2][ns][L]: sums over the group's channels of λ Δ2 u (dB / ln2), g h (dC)
   float* dpar;      // [dir][part][dim][kParStride][batch * nch]
-  int wpc;          // windows per chunk, ceil(K / 8)
+  int wpc;          // checkpoint slots per chunk (at least the windows of the schedule)
+  int msched;       // 1: windows of the forward's two-phase walk, whose checkpoints it stored
   int fnch, fm;     // the forward's chunk count, and forward chunks per backward chunk
 };
 
@@ -1794,6 +1815,44 @@ __device__ __forceinline__ void store_window(float* base, int64_t lo, const floa
   for (int j = 0; j < ns; ++j) base[ASC ? lo + j : lo + kWin - 1 - j] = v[j];
 }
 
+// Windows of a chunk of Kc steps in the walk's step order: uniform windows of kWin steps from step 0
+// (the last one ragged), or, for checkpoints left by the forward scan, its two-phase schedule:
+// whole windows up to the middle step M = ceil(Kc / 2) (stopping before the middle token of an
+// odd chunk), the steps left before M, whole windows from M, and the steps left at the end.
+struct WinSched {
+  int Kc, M, nw0, s1, n;
+  bool two;
+};
+
+__device__ __forceinline__ WinSched win_sched(int msched, int Kc) {
+  WinSched w{};
+  w.Kc = Kc;
+  w.two = msched != 0;
+  if (!w.two) {
+    w.n = (Kc + kWin - 1) / kWin;
+    return w;
+  }
+  w.M = (Kc + 1) >> 1;
+  w.nw0 = ((Kc & 1) ? w.M - 1 : w.M) / kWin;
+  w.s1 = w.nw0 + (w.nw0 * kWin < w.M ? 1 : 0);
+  w.n = w.s1 + (Kc - w.M + kWin - 1) / kWin;
+  return w;
+}
+
+// First step i0 and length of window s.
+__device__ __forceinline__ void win_at(const WinSched& w, int s, int& i0, int& len) {
+  if (!w.two || s < w.nw0) {
+    i0 = s * kWin;
+  } else if (s < w.s1) {
+    i0 = w.nw0 * kWin;
+    len = w.M - i0;
+    return;
+  } else {
+    i0 = w.M + (s - w.s1) * kWin;
+  }
+  len = w.Kc - i0 < kWin ? w.Kc - i0 : kWin;
+}
+
 // The adjoint walk of one direction and state part over one chunk, window by window from the last.
 template <typename T, int MODE, int DIR>
 __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float* rows, float* stage, int* pf) {
@@ -1815,7 +1874,6 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
   auto ck_at = [&](int w) {
     return ckw + ((static_cast<int64_t>(l.c) * ba.wpc + w) * a.dim + l.dd) * kH;
   };
-  const int full_end = (L / kWin) * kWin;
 
   // Backward, window by window from the last.
   const int64_t plane = static_cast<int64_t>(a.batch) * a.dim * a.L;
@@ -1841,13 +1899,20 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
   int nstaged = 0;  // windows staged so far
   float* myrow = rows + l.lane * kRedStride;
   RevWin<T, MODE, DIR> rw;
-  const int nwin = (L + kWin - 1) / kWin;
-  if (full_end > 0) rw.load(a, ub, xb, gb, ck_at(full_end / kWin - 1), l, full_end - kWin);
+  const WinSched sched = win_sched(ba.msched, L);
+  const int nwin = sched.n;
+  {
+    int i0l, nl;
+    win_at(sched, nwin - 1, i0l, nl);
+    if (nl == kWin) rw.load(a, ub, xb, gb, ck_at(nwin - 1), l, i0l);
+  }
   for (int w = nwin - 1; w >= 0; --w) {
-    const int i0 = w * kWin;
-    // Steps j >= ns (only in a last, partial window) are padding: Δ = 0 and g = 0 make them leave
-    // the state and the adjoint unchanged and contribute nothing; their loads use step ns - 1.
-    const int ns = L - i0 < kWin ? L - i0 : kWin;
+    // Steps j >= ns (only in a partial window) are padding: Δ = 0 and g = 0 make them leave the
+    // state and the adjoint unchanged and contribute nothing; their loads use step ns - 1.  A
+    // whole window's raw inputs were loaded during the previous window (rw).
+    int i0, ns, i0n = 0, nsn = 0;
+    win_at(sched, w, i0, ns);
+    if (w > 0) win_at(sched, w - 1, i0n, nsn);
     float hs[kH], d2[kWin], uu[kWin], gg[kWin], xr[kWin], sg[kWin];
     if (ns == kWin) {
       rw.u.template unpack<kRevOrder>(uu);
@@ -1855,7 +1920,7 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
       rw.g.template unpack<kRevOrder>(gg);
       rw.ck.template unpack<false>(hs);
       __builtin_amdgcn_sched_barrier(0);
-      if (w > 0) rw.load(a, ub, xb, gb, ck_at(w - 1), l, i0 - kWin);  // the next window down
+      if (nsn == kWin) rw.load(a, ub, xb, gb, ck_at(w - 1), l, i0n);  // the next window down
     } else {
       const float* c = ck_at(w);
 #pragma unroll
@@ -1868,6 +1933,7 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
         uu[j] = ld_act(ub, p);
         gg[j] = j < ns ? gb[p] : 0.0f;
       }
+      if (nsn == kWin) rw.load(a, ub, xb, gb, ck_at(w - 1), l, i0n);
     }
 #pragma unroll
     for (int j = 0; j < kWin; ++j) {
@@ -2150,8 +2216,10 @@ __global__ __launch_bounds__(256) void sum_planes_kernel(const float* base, int 
 
 // Backward buffers that depend on the chunking (the forward's: chunks of Kf): checkpoints of every
 // window of every chunk, the adjoint records (split sequences only) and the per-chunk parameter sums.
+// Checkpoint slots per chunk: its windows, one more for the forward's two-phase schedule.
+int64_t ck_slots(int64_t K) { return ceil_div(K, kWin) + 1; }
 size_t ck_bytes(int64_t batch, int64_t dim, int64_t L, int64_t Kf, int ns) {
-  return round256(static_cast<size_t>(batch) * 2 * (ns / kH) * ceil_div(L, Kf) * ceil_div(Kf, kWin) * dim * kH *
+  return round256(static_cast<size_t>(batch) * 2 * (ns / kH) * ceil_div(L, Kf) * ck_slots(Kf) * dim * kH *
                   sizeof(float));
 }
 size_t dpar_bytes(int64_t batch, int64_t dim, int64_t L, int64_t Kf, int ns) {
@@ -2196,9 +2264,12 @@ vmscan_status launch_bwd_scans(const BwdArgs& b0, const BwdArgs& b1, hipStream_t
   const int64_t nblocks = static_cast<int64_t>(a.batch) * a.nch * a.ngroups * (a.parts / 2) * SETS;
   if (nblocks >= (int64_t{1} << 31)) return VMSCAN_ERR_SHAPE;
   const dim3 grid(static_cast<unsigned>(nblocks));
-  hipLaunchKernelGGL((bwd_ckpt_kernel<T, MODE, SETS>), grid, dim3(kThreads), 0, stream, b0, b1);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return launch_failed(e);
+  hipError_t e;
+  if (!b0.msched) {  // else the forward scan stored the checkpoints
+    hipLaunchKernelGGL((bwd_ckpt_kernel<T, MODE, SETS>), grid, dim3(kThreads), 0, stream, b0, b1);
+    e = hipGetLastError();
+    if (e != hipSuccess) return launch_failed(e);
+  }
   if (a.nch > 1) {
     hipLaunchKernelGGL((adj_state_kernel<T, MODE, SETS>), grid, dim3(kThreads), 0, stream, b0, b1);
     e = hipGetLastError();
@@ -2228,15 +2299,6 @@ vmscan_status run_bwd(const ScanArgs& fwd, const BwdLayout& lay, unsigned char* 
   if (ceil_div(n, 256) >= (int64_t{1} << 31) || ceil_div(nbc, 256) >= (int64_t{1} << 31)) return VMSCAN_ERR_SHAPE;
   float* ysum = reinterpret_cast<float*>(wsp + lay.ysum);
   float* g = reinterpret_cast<float*>(wsp + lay.g);
-  // forward with the un-gated sum y_f + y_b
-  ScanArgs a = fwd;
-  a.wsy = ysum;
-  vmscan_status st = run_pair<T, kModeVimSum>(a, stream, kStageAll);
-  if (st != VMSCAN_OK) return st;
-  hipLaunchKernelGGL(gate_bwd_kernel<T>, dim3(static_cast<unsigned>(ceil_div(n, 256 * kWin))), dim3(256), 0, stream,
-                     static_cast<const T*>(dout), static_cast<const T*>(z), ysum, g, static_cast<T*>(dz), n, 0.5f);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return launch_failed(e);
   BwdArgs ba{};
   ba.s = fwd;  // the forward's carries (the state entering each forward chunk) are in agg
   const int64_t Kb = bwd_chunk(plan_base(fwd.batch, fwd.dim, ns), fwd.L, fwd.K);
@@ -2251,7 +2313,24 @@ vmscan_status run_bwd(const ScanArgs& fwd, const BwdLayout& lay, unsigned char* 
   ba.gx = reinterpret_cast<float*>(wsp + lay.gx);
   ba.dbc = reinterpret_cast<float*>(wsp + lay.dbc);
   ba.dpar = reinterpret_cast<float*>(wsp + lay.dpar);
-  ba.wpc = static_cast<int>(ceil_div(Kb, kWin));
+  ba.wpc = static_cast<int>(ck_slots(Kb));
+  // When neither pass splits the sequence, the forward scan below stores the checkpoints itself
+  // (the state entering each window of its two-phase walk) and the adjoint walk follows that
+  // schedule; otherwise the checkpoint kernel walks each backward chunk again.
+  ba.msched = fwd.nch == 1 && ba.s.nch == 1 ? 1 : 0;
+  // forward with the un-gated sum y_f + y_b
+  ScanArgs a = fwd;
+  a.wsy = ysum;
+  if (ba.msched) {
+    a.ck = ba.ck;
+    a.ck_wpc = ba.wpc;
+  }
+  vmscan_status st = run_pair<T, kModeVimSum>(a, stream, kStageAll);
+  if (st != VMSCAN_OK) return st;
+  hipLaunchKernelGGL(gate_bwd_kernel<T>, dim3(static_cast<unsigned>(ceil_div(n, 256 * kWin))), dim3(256), 0, stream,
+                     static_cast<const T*>(dout), static_cast<const T*>(z), ysum, g, static_cast<T*>(dz), n, 0.5f);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return launch_failed(e);
   st = launch_bwd_scans<T, kModeVim, 1>(ba, ba, stream);
   if (st != VMSCAN_OK) return st;
   hipLaunchKernelGGL(bwd_combine_kernel<T>, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, stream,
@@ -2445,7 +2524,7 @@ vmscan_status run_ss2d_bwd(const void* x, const void* delta_raw, const float* A_
     ba.gx = reinterpret_cast<float*>(wsp + q.gx);
     ba.dbc = reinterpret_cast<float*>(wsp + q.dbc);
     ba.dpar = reinterpret_cast<float*>(wsp + q.dpar);
-    ba.wpc = static_cast<int>(ceil_div(Kb, kWin));
+    ba.wpc = static_cast<int>(ck_slots(Kb));
     ba.g = k == 0 ? gcol : g;
     ba.s.d0 = k == 0 ? dir_args(xt, 1, 0) : dir_args(x, 0, 0);
     ba.s.d1 = k == 0 ? dir_args(xt, 3, 1) : dir_args(x, 2, 1);

@@ -137,6 +137,21 @@ def test_bwd_chunk_boundaries(L):
         _report(f"bwd L={L} {k}", O.rel_err(got[k], ref[k]), 1e-5)
 
 
+SCHED_L = [2, 7, 8, 15, 16, 17, 23, 24, 31, 32, 33, 47, 48, 49, 127]
+
+
+@pytest.mark.parametrize("L", SCHED_L)
+def test_bwd_window_schedule(L):
+    """Unsplit sequences, whose checkpoints the forward scan stores at the windows of its two-phase
+    walk (whole windows up to the middle step, the steps left before it, whole windows after it,
+    the steps left at the end): lengths around multiples of 8 and 16, odd and even, float32."""
+    p = synth.make_vim_v2_inputs(0, layer=1300 + L, batch=2, dim=20, seqlen=L, dtype="f32")
+    dout = _dout(p, L + 7)
+    got, ref = run_bwd(p, dout), oracle_bwd(p, dout)
+    for k in GRADS:
+        _report(f"bwd schedule L={L} {k}", O.rel_err(got[k], ref[k]), 1e-5)
+
+
 def test_bwd_whole_walk_split_forward():
     """At least one workgroup per CU (43 batches x 6 channel groups): the forward splits the
     230-token sequence into chunks, the backward walks it whole."""
