@@ -2130,22 +2130,43 @@ __global__ __launch_bounds__(256) void bwd_combine_kernel(const float* __restric
 }
 
 // dB, dC, dB_b, dC_b: the channel-group partial sums added up (dB scaled by ln 2), rounded once.
+// A thread takes 8 consecutive (state, index) elements of one (batch, direction, B or C) row
+// (grid: x over the ns * L elements, a multiple of 16; y over batch x 4), as whole 32-byte loads
+// and 16/32-byte stores.
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_bc_kernel(const float* __restrict__ dbc, T* dB, T* dC, T* dB_b, T* dC_b,
                                                      int batch, int ngroups, int64_t L, int64_t out_bstride, int ns) {
-  const int64_t per = static_cast<int64_t>(batch) * 2 * ns * L;  // one (dir, group) block
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= 2 * per) return;
-  const int dir = static_cast<int>(i / per);
-  const int64_t r = i - dir * per;                    // (b, type, n, pos)
-  float s = 0.0f;
-  for (int gi = 0; gi < ngroups; ++gi) s += dbc[(static_cast<int64_t>(dir) * ngroups + gi) * per + r];
-  const int64_t bb = r / (2 * ns * L);
-  const int64_t rest = r - bb * 2 * ns * L;
-  const int ty = static_cast<int>(rest / (ns * L));
-  const int64_t o = bb * out_bstride + (rest - ty * ns * L);  // (b, n, index); [ns][L] per batch
-  T* dst = ty == 0 ? (dir == 0 ? dB : dB_b) : (dir == 0 ? dC : dC_b);
-  st_act(dst, o, ty == 0 ? s * kLn2 : s);
+  const int64_t NL = static_cast<int64_t>(ns) * L;
+  const int64_t q0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * kWin;
+  if (q0 >= NL) return;
+  for (int y = static_cast<int>(blockIdx.y); y < 4 * batch; y += static_cast<int>(gridDim.y)) {
+    const int b = y >> 2, dir = (y >> 1) & 1, ty = y & 1;
+    float s[kWin] = {};
+    for (int gi = 0; gi < ngroups; ++gi) {
+      float v[kWin];
+      Run8<float> r;
+      r.load(dbc + (((static_cast<int64_t>(dir) * ngroups + gi) * batch + b) * 2 + ty) * NL + q0);
+      r.template unpack<false>(v);
+#pragma unroll
+      for (int j = 0; j < kWin; ++j) s[j] += v[j];
+    }
+    if (ty == 0) {
+#pragma unroll
+      for (int j = 0; j < kWin; ++j) s[j] *= kLn2;
+    }
+    T* dst = ty == 0 ? (dir == 0 ? dB : dB_b) : (dir == 0 ? dC : dC_b);
+    store8(dst + static_cast<int64_t>(b) * out_bstride + q0, s);
+  }
+}
+
+template <typename T>
+void launch_bwd_bc(const float* dbc, T* dB, T* dC, T* dB_b, T* dC_b, int batch, int ngroups, int64_t L,
+                   int64_t out_bstride, int ns, hipStream_t stream) {
+  const int64_t NL = static_cast<int64_t>(ns) * L;
+  const dim3 grid(static_cast<unsigned>(ceil_div(NL, 256 * kWin)),
+                  static_cast<unsigned>(4 * static_cast<int64_t>(batch) < 65535 ? 4 * batch : 65535));
+  hipLaunchKernelGGL(bwd_bc_kernel<T>, grid, dim3(256), 0, stream, dbc, dB, dC, dB_b, dC_b, batch, ngroups, L,
+                     out_bstride, ns);
 }
 
 // dA_log, dD, dbias per direction: sums over batch (and state parts); for shared inputs
@@ -2200,18 +2221,53 @@ __global__ __launch_bounds__(256) void bwd_param_kernel(const float* __restrict_
 // base + k * pstride) and, if given, one more plane `extra`, at (b, r), in float32, rounded once
 // to O.  Used for the SS2D gradients: dx from the row pair's partial planes (two directions x
 // pairs of state parts) plus the transposed column-pair plane, dΔ_raw per direction from its
-// planes.
+// planes.  A thread takes 8 consecutive elements of one batch entry (grid: x over n_b, y over the
+// batch); when n_b is a multiple of 8 they move as whole 32-byte loads and 16/32-byte stores.
 template <typename O>
 __global__ __launch_bounds__(256) void sum_planes_kernel(const float* base, int np, int64_t pstride,
                                                          const float* extra, O* out, int64_t n_b, int batch,
                                                          int64_t out_bstride) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= n_b * batch) return;
-  float s = 0.0f;
-  for (int k = 0; k < np; ++k) s += base[k * pstride + i];
-  if (extra) s += extra[i];
-  const int64_t b = i / n_b;
-  st_act(out, b * out_bstride + (i - b * n_b), s);
+  const int64_t r0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * kWin;
+  if (r0 >= n_b) return;
+  for (int b = static_cast<int>(blockIdx.y); b < batch; b += static_cast<int>(gridDim.y)) {
+    const int64_t i0 = static_cast<int64_t>(b) * n_b + r0;
+    O* o = out + static_cast<int64_t>(b) * out_bstride + r0;
+    if (n_b % kWin == 0) {
+      float s[kWin] = {};
+      for (int k = 0; k < np; ++k) {
+        float v[kWin];
+        Run8<float> r;
+        r.load(base + k * pstride + i0);
+        r.template unpack<false>(v);
+#pragma unroll
+        for (int j = 0; j < kWin; ++j) s[j] += v[j];
+      }
+      if (extra) {
+        float v[kWin];
+        Run8<float> r;
+        r.load(extra + i0);
+        r.template unpack<false>(v);
+#pragma unroll
+        for (int j = 0; j < kWin; ++j) s[j] += v[j];
+      }
+      store8(o, s);
+    } else {
+      for (int j = 0; j < kWin && r0 + j < n_b; ++j) {
+        float s = 0.0f;
+        for (int k = 0; k < np; ++k) s += base[k * pstride + i0 + j];
+        if (extra) s += extra[i0 + j];
+        st_act(o, j, s);
+      }
+    }
+  }
+}
+
+template <typename O>
+void launch_sum_planes(const float* base, int np, int64_t pstride, const float* extra, O* out, int64_t n_b, int batch,
+                       int64_t out_bstride, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(ceil_div(n_b, 256 * kWin)), static_cast<unsigned>(batch < 65535 ? batch : 65535));
+  hipLaunchKernelGGL(sum_planes_kernel<O>, grid, dim3(256), 0, stream, base, np, pstride, extra, out, n_b, batch,
+                     out_bstride);
 }
 
 // Backward buffers that depend on the chunking (the forward's: chunks of Kf): checkpoints of every
@@ -2336,9 +2392,8 @@ vmscan_status run_bwd(const ScanArgs& fwd, const BwdLayout& lay, unsigned char* 
   hipLaunchKernelGGL(bwd_combine_kernel<T>, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, stream,
                      ba.gu, ba.gx, static_cast<T*>(du), static_cast<T*>(dx), static_cast<T*>(du_b),
                      static_cast<T*>(dx_b), n, fwd.parts / 2);
-  hipLaunchKernelGGL(bwd_bc_kernel<T>, dim3(static_cast<unsigned>(ceil_div(nbc, 256))), dim3(256), 0, stream, ba.dbc,
-                     static_cast<T*>(dB), static_cast<T*>(dC), static_cast<T*>(dB_b), static_cast<T*>(dC_b), fwd.batch,
-                     fwd.ngroups, fwd.L, static_cast<int64_t>(ns) * fwd.L, ns);
+  launch_bwd_bc<T>(ba.dbc, static_cast<T*>(dB), static_cast<T*>(dC), static_cast<T*>(dB_b), static_cast<T*>(dC_b),
+                   fwd.batch, fwd.ngroups, fwd.L, static_cast<int64_t>(ns) * fwd.L, ns, stream);
   hipLaunchKernelGGL(bwd_param_kernel, dim3(static_cast<unsigned>(ceil_div(2 * fwd.dim * ns + 4 * fwd.dim, 4))),
                      dim3(256), 0, stream, ba.dpar, A_log, A_b_log, dA_log, dA_b_log, dD, dD_b, dbias, dbias_b,
                      fwd.batch * ba.s.nch, fwd.dim, ns);
@@ -2421,18 +2476,13 @@ vmscan_status ss2d_pair_post(const BwdArgs& ba, int k0, int k1, void* ddelta_raw
   const int64_t n = static_cast<int64_t>(a.batch) * DL;
   const int64_t plane = n;
   T* ddr = static_cast<T*>(ddelta_raw);
-  const dim3 pg(static_cast<unsigned>(ceil_div(n, 256)));
   const int np = a.parts / 2;  // planes per direction
-  hipLaunchKernelGGL(sum_planes_kernel<T>, pg, dim3(256), 0, stream, ba.gx, np, plane, nullptr, ddr + k0 * DL, DL,
-                     a.batch, 4 * DL);
-  hipLaunchKernelGGL(sum_planes_kernel<T>, pg, dim3(256), 0, stream, ba.gx + np * plane, np, plane, nullptr,
-                     ddr + k1 * DL, DL, a.batch, 4 * DL);
+  launch_sum_planes<T>(ba.gx, np, plane, nullptr, ddr + k0 * DL, DL, a.batch, 4 * DL, stream);
+  launch_sum_planes<T>(ba.gx + np * plane, np, plane, nullptr, ddr + k1 * DL, DL, a.batch, 4 * DL, stream);
   const int ns = a.ns;
   const int64_t NL = static_cast<int64_t>(ns) * a.L;
-  const int64_t nbc = static_cast<int64_t>(2) * a.batch * 2 * NL;
-  hipLaunchKernelGGL(bwd_bc_kernel<T>, dim3(static_cast<unsigned>(ceil_div(nbc, 256))), dim3(256), 0, stream, ba.dbc,
-                     static_cast<T*>(dB) + k0 * NL, static_cast<T*>(dC) + k0 * NL, static_cast<T*>(dB) + k1 * NL,
-                     static_cast<T*>(dC) + k1 * NL, a.batch, a.ngroups, a.L, 4 * NL, ns);
+  launch_bwd_bc<T>(ba.dbc, static_cast<T*>(dB) + k0 * NL, static_cast<T*>(dC) + k0 * NL, static_cast<T*>(dB) + k1 * NL,
+                   static_cast<T*>(dC) + k1 * NL, a.batch, a.ngroups, a.L, 4 * NL, ns, stream);
   const int64_t dN = static_cast<int64_t>(a.dim) * ns;
   hipLaunchKernelGGL(bwd_param_kernel, dim3(static_cast<unsigned>(ceil_div(2 * a.dim * ns + 4 * a.dim, 4))), dim3(256),
                      0, stream, ba.dpar, A_log + k0 * dN, A_log + k1 * dN, dA_log + k0 * dN, dA_log + k1 * dN,
@@ -2539,16 +2589,14 @@ vmscan_status run_ss2d_bwd(const void* x, const void* delta_raw, const float* A_
   // its du back to row-major pixels: sum the partial planes (column order), transpose
   float* col = reinterpret_cast<float*>(wsp + lay.f.col_img);
   float* rowp = reinterpret_cast<float*>(wsp + lay.f.row_img);
-  hipLaunchKernelGGL(sum_planes_kernel<float>, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, stream,
-                     ba.gu, a.parts, n, nullptr, col, n, 1, n);
+  launch_sum_planes<float>(ba.gu, a.parts, n, nullptr, col, n, 1, n, stream);
   st = launch_transpose(col, rowp, nimg, static_cast<int>(W), static_cast<int>(H), 4, stream);
   if (st != VMSCAN_OK) return st;
   // the row pair's gradients, and dx = its du plus the column pair's, transposed
   const BwdArgs& br = bp[1];
   st = ss2d_pair_post<T>(br, 0, 2, ddelta_raw, dB, dC, dA_log, A_log, dD, ddelta_bias, stream);
   if (st != VMSCAN_OK) return st;
-  hipLaunchKernelGGL(sum_planes_kernel<T>, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, stream, br.gu,
-                     a.parts, n, rowp, static_cast<T*>(dx), n, 1, n);
+  launch_sum_planes<T>(br.gu, a.parts, n, rowp, static_cast<T*>(dx), n, 1, n, stream);
   e = hipGetLastError();
   return e == hipSuccess ? VMSCAN_OK : launch_failed(e);
 }
