@@ -2065,7 +2065,7 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
     asm volatile("" ::: "memory");
   }
   if (l.valid) {
-    // [dir][half][dim][kParStride][batch * nch]: the sums over batch and chunks read contiguous runs
+    // [dir][part][dim][kParStride][batch * nch]: the sums over batch and chunks read contiguous runs
     const int64_t nbc = static_cast<int64_t>(a.batch) * a.nch;
     float* pp = ba.dpar + ((static_cast<int64_t>(DIR) * a.parts + l.part) * a.dim + l.d) * kParStride * nbc +
                 static_cast<int64_t>(l.b) * a.nch + l.c;
