@@ -178,7 +178,11 @@ def scan_1d_bwd(u, delta_raw, A_log, B, C, D, delta_bias, g):
         dL/dA_n       = Σ_{b,t} λ_t,n Δ_t a_t,n h_{t-1},n,  dL/dA_log = dL/dA * A   (A = -exp(A_log))
         dL/dD         = Σ_{b,t} g_t u_t
 
-    Returns dict(s, du, ddelta_raw, dA_log [dim, N], dB, dC [batch, N, L], dD, ddelta_bias [dim]).
+    Returns dict(s, du, ddelta_raw, dA_log [dim, N], dB, dC [batch, N, L], dD, ddelta_bias [dim]),
+    and du_abs, ddelta_raw_abs: the same sums with every term replaced by its absolute value
+    (|g D| + Δ Σ_n |λ B|, and sigmoid · Σ_n |λ| (|A a h| + |B u|)).  They are not gradients but the
+    scale of the rounding error of a finite-precision evaluation of those sums (which can cancel
+    heavily), used by the tests' error bound.
     The forward states are recomputed and kept for every t (fine at oracle sizes).
     """
     u = np.asarray(u, dtype=np.float64)
@@ -200,7 +204,9 @@ def scan_1d_bwd(u, delta_raw, A_log, B, C, D, delta_bias, g):
         hs[t + 1] = av[t] * hs[t] + delta[:, :, t][:, :, None] * B[:, None, :, t] * u[:, :, t][:, :, None]
         s[:, :, t] = np.sum(hs[t + 1] * C[:, None, :, t], axis=2) + D[None, :] * u[:, :, t]
     du = g * D[None, :, None]
+    du_abs = np.abs(du)
     ddelta = np.zeros((nb, nd, L))
+    ddelta_abs = np.zeros((nb, nd, L))
     dA = np.zeros((nd, N))
     dB = np.zeros((nb, N, L))
     dC = np.zeros((nb, N, L))
@@ -212,12 +218,15 @@ def scan_1d_bwd(u, delta_raw, A_log, B, C, D, delta_bias, g):
         dC[:, :, t] = np.sum(g[:, :, t][:, :, None] * hs[t + 1], axis=1)
         dB[:, :, t] = np.sum(lam * dl * u[:, :, t][:, :, None], axis=1)
         du[:, :, t] += delta[:, :, t] * np.sum(lam * B[:, None, :, t], axis=2)
+        du_abs[:, :, t] += delta[:, :, t] * np.sum(np.abs(lam * B[:, None, :, t]), axis=2)
         decay_term = A[None] * av[t] * hs[t]
-        ddelta[:, :, t] = np.sum(lam * (decay_term + B[:, None, :, t] * u[:, :, t][:, :, None]), axis=2)
+        input_term = B[:, None, :, t] * u[:, :, t][:, :, None]
+        ddelta[:, :, t] = np.sum(lam * (decay_term + input_term), axis=2)
+        ddelta_abs[:, :, t] = np.sum(np.abs(lam) * (np.abs(decay_term) + np.abs(input_term)), axis=2)
         dA += np.sum(lam * dl * av[t] * hs[t], axis=0)
     ddr = ddelta * expit(x)
     return dict(s=s, du=du, ddelta_raw=ddr, ddelta_bias=ddr.sum(axis=(0, 2)), dA_log=dA * A, dB=dB, dC=dC,
-                dD=np.sum(g * u, axis=(0, 2)))
+                dD=np.sum(g * u, axis=(0, 2)), du_abs=du_abs, ddelta_raw_abs=ddelta_abs * expit(x))
 
 
 def vim_bidir_v2_bwd(u, delta_raw, delta_bias, u_b, delta_raw_b, delta_bias_b, z, A_log, A_b_log, B, C, B_b, C_b,
@@ -242,7 +251,9 @@ def vim_bidir_v2_bwd(u, delta_raw, delta_bias, u_b, delta_raw_b, delta_bias_b, z
     return dict(du=fw["du"], ddelta_raw=fw["ddelta_raw"], ddelta_bias=fw["ddelta_bias"],
                 du_b=f(bw["du"]), ddelta_raw_b=f(bw["ddelta_raw"]), ddelta_bias_b=bw["ddelta_bias"], dz=dz,
                 dA_log=fw["dA_log"], dA_b_log=bw["dA_log"], dB=fw["dB"], dC=fw["dC"], dB_b=f(bw["dB"]),
-                dC_b=f(bw["dC"]), dD=fw["dD"], dD_b=bw["dD"])
+                dC_b=f(bw["dC"]), dD=fw["dD"], dD_b=bw["dD"],
+                du_abs=fw["du_abs"], ddelta_raw_abs=fw["ddelta_raw_abs"], du_b_abs=f(bw["du_abs"]),
+                ddelta_raw_b_abs=f(bw["ddelta_raw_abs"]))
 
 
 def ss2d_orders(x):
@@ -288,7 +299,8 @@ def ss2d_cross_scan_bwd(x, delta_raw, A_log, B, C, D, delta_bias, z, dout):
     direction k's scan order, is mapped back to pixels and summed into dx.  Per-direction
     tensors (Δ_raw, B, C) keep their scan order.  dz = dout Σ_k back_k(y_k) silu'(z).
     Returns dict(dx, ddelta_raw [batch,4,dim,L], dA_log [4,dim,N], dB, dC [batch,4,N,L],
-    dD, ddelta_bias [4,dim], dz (None without z)).
+    dD, ddelta_bias [4,dim], dz (None without z)), and dx_abs, ddelta_raw_abs (the absolute-value
+    sums of ``scan_1d_bwd``, mapped and added the same way).
     """
     x = np.asarray(x, dtype=np.float64)
     dout = np.asarray(dout, dtype=np.float64)
@@ -304,22 +316,27 @@ def ss2d_cross_scan_bwd(x, delta_raw, A_log, B, C, D, delta_bias, z, dout):
         gsum = dout
     gorders = ss2d_orders(gsum)       # dL/dy_k: the k-th ordering of the merged gradient
     dx = np.zeros((nb, nd, L))
+    dx_abs = np.zeros((nb, nd, L))
     ysum = np.zeros((nb, nd, L))
     res = dict(ddelta_raw=np.zeros((nb, 4, nd, L)), dA_log=np.zeros(np.asarray(A_log).shape),
                dB=np.zeros((nb, 4) + np.asarray(B).shape[2:]), dC=np.zeros((nb, 4) + np.asarray(C).shape[2:]),
-               dD=np.zeros(np.asarray(D).shape), ddelta_bias=np.zeros(np.asarray(delta_bias).shape))
+               dD=np.zeros(np.asarray(D).shape), ddelta_bias=np.zeros(np.asarray(delta_bias).shape),
+               ddelta_raw_abs=np.zeros((nb, 4, nd, L)))
     for k in range(4):
         r = scan_1d_bwd(seqs[k], np.asarray(delta_raw)[:, k], np.asarray(A_log)[k], np.asarray(B)[:, k],
                         np.asarray(C)[:, k], np.asarray(D)[k], np.asarray(delta_bias)[k], gorders[k])
         dx += backs[k](r["du"])
+        dx_abs += backs[k](r["du_abs"])
         ysum += backs[k](r["s"])
         res["ddelta_raw"][:, k] = r["ddelta_raw"]
+        res["ddelta_raw_abs"][:, k] = r["ddelta_raw_abs"]
         res["dA_log"][k] = r["dA_log"]
         res["dB"][:, k] = r["dB"]
         res["dC"][:, k] = r["dC"]
         res["dD"][k] = r["dD"]
         res["ddelta_bias"][k] = r["ddelta_bias"]
     res["dx"] = dx.reshape(nb, nd, H, W)
+    res["dx_abs"] = dx_abs.reshape(nb, nd, H, W)
     if z is not None:
         sig = expit(z)
         res["dz"] = dout * ysum.reshape(nb, nd, H, W) * sig * (1.0 + z * (1.0 - sig))

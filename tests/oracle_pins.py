@@ -586,6 +586,43 @@ def pin_conv2d_impulse(impl):
     return msgs
 
 
+def pin_bwd_abs_sums(impl):
+    """The absolute-value sums that scale the parity bound of du, dΔ_raw and dx: each bounds its
+    gradient (triangle inequality), and with a single term (one state, D = 0; for dΔ_raw also
+    u = 0, which removes the input term) it equals the gradient's magnitude.  These sums are a
+    diagnostic of the oracle; a copy that does not produce them (the planted-mistake copies of
+    the gradients) is not checked here."""
+    msgs = []
+    rng = np.random.default_rng(15)
+    p = rich_v2(rng, nb=2, nd=3, L=6, N=4)
+    dout = rng.standard_normal(p["u"].shape)
+    gr = impl.vim_bidir_v2_bwd(*[p[k] for k in V2_NAMES], dout)
+    if "du_abs" not in gr:
+        return msgs
+    for k in ("du", "ddelta_raw", "du_b", "ddelta_raw_b"):
+        over = float(np.max(np.abs(gr[k]) - gr[k + "_abs"]))
+        _check(msgs, f"|{k}| <= {k}_abs", max(over, 0.0), 1e-12)
+        _check(msgs, f"{k}_abs not a plain copy of |{k}|", 1.0 if np.allclose(np.abs(gr[k]), gr[k + "_abs"]) else 0.0, 0.0)
+    q = rich_v2(rng, nb=2, nd=3, L=6, N=1)
+    q["D"] = np.zeros_like(q["D"])
+    q["D_b"] = np.zeros_like(q["D_b"])
+    g1 = impl.vim_bidir_v2_bwd(*[q[k] for k in V2_NAMES], dout)
+    for k in ("du", "du_b"):
+        _check(msgs, f"single-term {k}_abs = |{k}|", float(np.max(np.abs(np.abs(g1[k]) - g1[k + "_abs"]))), 1e-12)
+    q["u"] = np.zeros_like(q["u"])
+    g0 = impl.vim_bidir_v2_bwd(*[q[k] for k in V2_NAMES], dout)
+    _check(msgs, "single-term ddelta_raw_abs = |ddelta_raw|",
+           float(np.max(np.abs(np.abs(g0["ddelta_raw"]) - g0["ddelta_raw_abs"]))), 1e-12)
+    s2 = rich_ss2d(rng, nb=1, nd=2, H=3, W=4, N=3)
+    d2 = rng.standard_normal(s2["x"].shape)
+    gs = impl.ss2d_cross_scan_bwd(s2["x"], s2["delta_raw"], s2["A_log"], s2["B"], s2["C"], s2["D"],
+                                  s2["delta_bias"], None, d2)
+    for k in ("dx", "ddelta_raw"):
+        over = float(np.max(np.abs(gs[k]) - gs[k + "_abs"]))
+        _check(msgs, f"ss2d |{k}| <= {k}_abs", max(over, 0.0), 1e-12)
+    return msgs
+
+
 ALL_PINS = [
     pin_softplus_silu,
     pin_golden_single_token,
@@ -606,6 +643,7 @@ ALL_PINS = [
     pin_bwd_finite_differences,
     pin_bwd_shared_inputs,
     pin_ss2d_bwd_finite_differences,
+    pin_bwd_abs_sums,
     pin_conv1d_impulse,
     pin_conv1d_numpy,
     pin_conv2d_scipy,
