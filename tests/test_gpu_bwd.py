@@ -182,6 +182,19 @@ def test_bwd_window_schedule(L):
         _report(f"bwd schedule L={L} {k}", grad_err(got[k], ref, k, 1e-5), 1e-5)
 
 
+@pytest.mark.parametrize("L", [100, 197])
+def test_bwd_window_schedule_long(L):
+    """The same two-phase schedule on longer unsplit sequences (384 single-group tiles keep the
+    forward whole), float32: a middle run left before the middle step and a ragged end."""
+    import selective_state_space_41_amd as V
+    assert V.fwd_bidir_chunk_len(384, 64, L) == L
+    p = synth.make_vim_v2_inputs(0, layer=1400 + L, batch=384, dim=64, seqlen=L, dtype="f32")
+    dout = _dout(p, L + 11)
+    got, ref = run_bwd(p, dout), oracle_bwd(p, dout)
+    for k in GRADS:
+        _report(f"bwd schedule L={L} (384 tiles) {k}", grad_err(got[k], ref, k, 1e-5), 1e-5)
+
+
 def test_bwd_whole_walk_split_forward():
     """At least one workgroup per CU (43 batches x 6 channel groups): the forward splits the
     230-token sequence into chunks, the backward walks it whole."""
