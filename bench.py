@@ -701,8 +701,8 @@ def main():
         summarize_traffic(w, like, {"fetch": fd, "write": wd, "copy_fetch": cfd, "copy_write": cwd}, json.loads(cmds))
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the path shards over "
-              "batch/channels with no communication, see the design notes.", file=sys.stderr)
+        print(f"bench.py: runs on one GPU only (got --gpus {args.gpus}); multi-GPU sharding over batch and "
+              "channels is not implemented.", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
