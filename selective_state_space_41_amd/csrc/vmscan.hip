@@ -220,9 +220,15 @@ struct ScanArgs {
   int ns, parts;   // d_state and its parts of 8 states (one wave per direction and part)
   float* ck;       // kModeVimSum of an unsplit sequence, or null: the state entering each window of
   int ck_wpc;      // the two-phase walk, [batch][dir][part][ck_wpc][dim][8] (the backward checkpoints)
+  // kModeVimSum: the gate's backward in the epilogue, from the un-gated sum y_f + y_b and
+  // dout (same layout as u): gout = dout silu(z) / 2 (float32), dzout = dout (y_f + y_b) silu'(z) / 2.
+  const void* dout;
+  float* gout;
+  void* dzout;
 };
 
-// kModeVimSum: Vim order, but the epilogue stores the un-gated fp32 sum y_f + y_b to wsy;
+// kModeVimSum: Vim order, but the epilogue turns the un-gated sum y_f + y_b into the gate's
+// backward (g and dz, see ScanArgs::dout);
 // kModeSecondPairSum: the SS2D row pair, storing the un-gated fp32 sum of all four directions to
 // out (as float).  The backward passes need these sums for dL/dz.
 enum { kModeVim = 0, kModeFirstPair = 1, kModeSecondPair = 2, kModeVimSum = 3, kModeSecondPairSum = 4 };
@@ -896,7 +902,21 @@ __device__ __forceinline__ void epi_batch(const ScanArgs& a, const float* ybuf, 
 #pragma unroll
       for (int j = 0; j < kWin; ++j) v[j] = 0.5f * v[j] * silu_f(zz[j]);  // (y_f + y_b) / 2 * silu(z)
       store8(ob + gi, v);
-    } else if (MODE == kModeFirstPair || MODE == kModeVimSum) {
+    } else if (MODE == kModeVimSum) {
+      float go[kWin], gv[kWin], dv[kWin];
+      Run8<T> dr;
+      dr.load(static_cast<const T*>(a.dout) + gi);
+      zr[k].template unpack<false>(zz);
+      dr.template unpack<false>(go);
+#pragma unroll
+      for (int j = 0; j < kWin; ++j) {
+        const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-zz[j] * kLog2e));
+        gv[j] = 0.5f * go[j] * zz[j] * sg;
+        dv[j] = 0.5f * go[j] * v[j] * sg * (1.0f + zz[j] * (1.0f - sg));
+      }
+      store8(a.gout + gi, gv);
+      store8(static_cast<T*>(a.dzout) + gi, dv);
+    } else if (MODE == kModeFirstPair) {
       store8(a.wsy + gi, v);
     } else if (MODE == kModeSecondPairSum) {
       float w[kWin];
@@ -923,7 +943,7 @@ template <typename T, int MODE, int NTH>
 __device__ __forceinline__ void epi_load(const ScanArgs& a, int64_t base, int items, int ngr, int it0,
                                          Run8<T> (&zr)[kEpiBatch]) {
   const T* zb = static_cast<const T*>(a.z);
-  if (!(MODE == kModeVim || (MODE == kModeSecondPair && zb))) return;
+  if (!(MODE == kModeVim || MODE == kModeVimSum || (MODE == kModeSecondPair && zb))) return;
 #pragma unroll
   for (int k = 0; k < kEpiBatch; ++k) {
     int c, q;
@@ -980,7 +1000,12 @@ __device__ __forceinline__ void pair_epilogue(const ScanArgs& a, const Lane& l, 
       const float v = row_val(ybuf, ybs, c, q);
       if (MODE == kModeVim) {
         st_act(ob, gi, 0.5f * v * silu_f(ld_act(zb, gi)));
-      } else if (MODE == kModeFirstPair || MODE == kModeVimSum) {
+      } else if (MODE == kModeVimSum) {
+        const float zz = ld_act(zb, gi), go = ld_act(static_cast<const T*>(a.dout), gi);
+        const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-zz * kLog2e));
+        a.gout[gi] = 0.5f * go * zz * sg;
+        st_act(static_cast<T*>(a.dzout), gi, 0.5f * go * v * sg * (1.0f + zz * (1.0f - sg)));
+      } else if (MODE == kModeFirstPair) {
         a.wsy[gi] = v;
       } else if (MODE == kModeSecondPairSum) {
         static_cast<float*>(a.out)[gi] = v + a.wsy[gi];
@@ -2287,7 +2312,7 @@ size_t dbc_bytes(int64_t batch, int64_t dim, int64_t L, int ns) {
 }
 
 struct BwdLayout {
-  size_t bct, agg, ysum, g, ck, adj, gu, gx, dbc, dpar, total;
+  size_t bct, agg, g, ck, adj, gu, gx, dbc, dpar, total;
 };
 
 // The planes of du / dΔ_raw shares are [dir][part / 2][batch][dim][L], rounded up to 256 bytes only
@@ -2299,8 +2324,7 @@ BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t L, int64_t Kf, int ns) 
   const int64_t Kb = bwd_chunk(plan_base(batch, dim, ns), L, Kf);
   w.bct = 0;
   w.agg = w.bct + bct_bytes(batch, L, ns);
-  w.ysum = w.agg + agg_bytes(batch, dim, L, Kf, ns);
-  w.g = w.ysum + plane;
+  w.g = w.agg + agg_bytes(batch, dim, L, Kf, ns);
   w.ck = w.g + plane;
   w.adj = w.ck + ck_bytes(batch, dim, L, Kb, ns);
   w.gu = w.adj + agg_bytes(batch, dim, L, Kb, ns);
@@ -2353,7 +2377,6 @@ vmscan_status run_bwd(const ScanArgs& fwd, const BwdLayout& lay, unsigned char* 
   const int64_t n = static_cast<int64_t>(fwd.batch) * fwd.dim * fwd.L;
   const int64_t nbc = static_cast<int64_t>(2) * fwd.batch * 2 * ns * fwd.L;
   if (ceil_div(n, 256) >= (int64_t{1} << 31) || ceil_div(nbc, 256) >= (int64_t{1} << 31)) return VMSCAN_ERR_SHAPE;
-  float* ysum = reinterpret_cast<float*>(wsp + lay.ysum);
   float* g = reinterpret_cast<float*>(wsp + lay.g);
   BwdArgs ba{};
   ba.s = fwd;  // the forward's carries (the state entering each forward chunk) are in agg
@@ -2376,17 +2399,17 @@ vmscan_status run_bwd(const ScanArgs& fwd, const BwdLayout& lay, unsigned char* 
   ba.msched = fwd.nch == 1 && ba.s.nch == 1 ? 1 : 0;
   // forward with the un-gated sum y_f + y_b
   ScanArgs a = fwd;
-  a.wsy = ysum;
+  a.wsy = nullptr;
+  a.dout = dout;  // the epilogue computes g and dz (the gate's backward)
+  a.gout = g;
+  a.dzout = dz;
   if (ba.msched) {
     a.ck = ba.ck;
     a.ck_wpc = ba.wpc;
   }
   vmscan_status st = run_pair<T, kModeVimSum>(a, stream, kStageAll);
   if (st != VMSCAN_OK) return st;
-  hipLaunchKernelGGL(gate_bwd_kernel<T>, dim3(static_cast<unsigned>(ceil_div(n, 256 * kWin))), dim3(256), 0, stream,
-                     static_cast<const T*>(dout), static_cast<const T*>(z), ysum, g, static_cast<T*>(dz), n, 0.5f);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return launch_failed(e);
+  hipError_t e;
   st = launch_bwd_scans<T, kModeVim, 1>(ba, ba, stream);
   if (st != VMSCAN_OK) return st;
   hipLaunchKernelGGL(bwd_combine_kernel<T>, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, stream,
