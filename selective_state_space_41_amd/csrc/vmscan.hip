@@ -280,6 +280,31 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in
   const T* src = in + img * R * Cc;
   T* dst = out + img * R * Cc;
   const int r0 = tr * kTile, c0 = tc * kTile;
+  if (sizeof(T) == 4 && (R & 3) == 0 && (Cc & 3) == 0) {
+    // 4-byte elements, both sides multiples of 4: runs of 4 along each side's contiguous
+    // dimension as single 16-byte accesses (the images start 16-byte aligned)
+    const int tq = threadIdx.x & 15, tw = threadIdx.x >> 4;  // run of 4, row (column) of the pass
+    for (int i = tw; i < kTile; i += 16) {
+      const int r = r0 + i, c = c0 + 4 * tq;
+      if (r < R && c < Cc) {
+        T v[4];
+        __builtin_memcpy(v, src + static_cast<int64_t>(r) * Cc + c, sizeof(v));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) tile[i][4 * tq + k] = v[k];
+      }
+    }
+    __syncthreads();
+    for (int i = tw; i < kTile; i += 16) {
+      const int c = c0 + i, r = r0 + 4 * tq;
+      if (c < Cc && r < R) {
+        T v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = tile[4 * tq + k][i];
+        __builtin_memcpy(dst + static_cast<int64_t>(c) * R + r, v, sizeof(v));
+      }
+    }
+    return;
+  }
   const int tx = threadIdx.x & (kTile - 1), ty = threadIdx.x >> 6;
   for (int i = ty; i < kTile; i += 4) {
     const int r = r0 + i, c = c0 + tx;
