@@ -330,6 +330,31 @@ __global__ __launch_bounds__(256) void transpose16_kernel(const uint16_t* __rest
   const uint16_t* src = in + base;
   uint16_t* dst = out + base;
   const int r0 = tr * kTile, c0 = tc * kTile;
+  if ((R & 7) == 0 && (Cc & 7) == 0) {
+    // both sides multiples of 8: runs of 8 elements as single 16-byte accesses (the images start
+    // 16-byte aligned)
+    const int tq = threadIdx.x & 7, tw = threadIdx.x >> 3;  // run of 8, row (column) of the pass
+    for (int i = tw; i < kTile; i += 32) {
+      const int r = r0 + i, c = c0 + 8 * tq;
+      if (r < R && c < Cc) {
+        uint16_t v[8];
+        __builtin_memcpy(v, src + static_cast<int64_t>(r) * Cc + c, sizeof(v));
+#pragma unroll
+        for (int k = 0; k < 8; ++k) tile[i][8 * tq + k] = v[k];
+      }
+    }
+    __syncthreads();
+    for (int i = tw; i < kTile; i += 32) {
+      const int c = c0 + i, r = r0 + 8 * tq;
+      if (c < Cc && r < R) {
+        uint16_t v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = tile[8 * tq + k][i];
+        __builtin_memcpy(dst + static_cast<int64_t>(c) * R + r, v, sizeof(v));
+      }
+    }
+    return;
+  }
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 pairs x 8 rows per pass
   for (int i = ty; i < kTile; i += 8) {
     const int r = r0 + i, c = c0 + 2 * tx;
