@@ -184,9 +184,10 @@ vmscan_status vmscan_fwd_bidir_v2_stage(const void *u, const void *delta_raw, co
  * NULL: the backward branch's gradient for that input is then ADDED to the forward branch's
  * output (du, ddelta_raw, ddelta_bias), which is the gradient of vmscan_fwd_bidir, whose two
  * branches share u, delta_raw and delta_bias (pass the same tensor as u_b etc. then).
- * The library recomputes the forward: it runs the forward scan keeping the un-gated sum and
- * stores the state at window boundaries (in that scan when the sequence is not split, else in a
- * second forward pass per direction), then walks backwards over the sequence with the adjoint
+ * The library recomputes the forward: it runs the forward scan, which turns the un-gated sum into
+ * dz and the scan's output gradient at once (the sum itself is not stored), and it stores the
+ * state at window boundaries (in that scan when the sequence is not split, else in a second
+ * forward pass per direction), then walks backwards over the sequence with the adjoint
  * recurrence, window by window from those states.  A long sequence with few (batch, channel-group) tiles
  * is split into chunks, the adjoint carry between them coming from a reverse carry pass; the
  * result does not depend on the split beyond float32 rounding order.  Workspace:
