@@ -1636,8 +1636,8 @@ struct BwdArgs {
   int fnch, fm;     // the forward's chunk count, and forward chunks per backward chunk
 };
 
-// g = scale dout silu(z) (float32) and dz = scale dout ysum silu'(z), silu'(z) = σ (1 + z (1 - σ)),
-// with scale 1/2 for the averaged Vim directions and 1 for SS2D; without a gate (z NULL, SS2D)
+// SS2D gate backward: g = scale dout silu(z) (float32) and dz = scale dout ysum silu'(z), with
+// silu'(z) = σ (1 + z (1 - σ)) and scale 1 for the summed directions; without a gate (z NULL)
 // g = dout and there is no dz.  Eight elements per thread (16-byte accesses; the flat arrays start
 // 16-byte aligned).
 template <typename T>
