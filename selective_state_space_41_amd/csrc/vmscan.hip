@@ -21,8 +21,9 @@
 //    No VALU instruction is spent on B/C.
 //  * u, Δ_raw (and z) are read per lane in windows of 8 consecutive tokens (16-byte loads;
 //    the hardware accepts the 2-byte-aligned rows of odd-length bf16 sequences), one window
-//    ahead of use.  Δ2 = log2(1 + 2^t), t = (Δ_raw + bias)·log2 e, is computed with a
-//    compensated log1p: log2(1 + e) = log2(s) + (e - (s - 1))·log2 e, s = 1 + e.
+//    ahead of use.  Δ2 = log2(1 + 2^t), t = (Δ_raw + bias)·log2 e, is computed as
+//    max(t, 0) + log2(1 + e), e = 2^-|t|, with a compensated log1p: log2(1 + e) = log2(s) +
+//    (e - (s - 1))·log2 e, s = 1 + e.
 //  * All four waves advance in lockstep: at step i the forward waves are at chunk position i,
 //    the backward waves at Kc-1-i.  The channel's y at a position is the sum of four partial
 //    readouts (two directions x two state halves).  They meet in one fp32 LDS row per channel in
@@ -139,29 +140,30 @@ struct Run8<float> {
 // natural A = -exp(A_log), Δ u B = Δ2 u (B ln 2) with B pre-scaled in the B/C copy, and the
 // softplus argument x log2 e is one FMA of the raw input with the scaled bias.
 //
-// softplus in base-2 units: given t = x log2 e, returns log2(1 + 2^t) = softplus(x) log2 e.
-// With e = 2^t and s = fl(1 + e), c = e - (s - 1) is the rounding error of s (exactly for e <= 1;
-// for e > 1 it is below the result's resolution), and log2(1 + e) = log2(s) + log2(1 + c/s)
-// ~= log2(s) + c log2 e.  This keeps full fp32 relative accuracy for the e ~ 1e-3 that the Δ
-// bias range produces, where a plain log2(1 + e) loses about three digits.  Above x = 20 the
-// correction to x is below fp32 resolution.
+// softplus in base-2 units: given t = x log2 e, returns log2(1 + 2^t) = softplus(x) log2 e,
+// evaluated as max(t, 0) + log2(1 + e) with e = 2^-|t| <= 1.  With s = fl(1 + e) in [1, 2],
+// c = e - (s - 1) is exactly the rounding error of s, and log2(1 + e) = log2(s) + log2(1 + c/s)
+// ~= log2(s) + c log2 e, off by at most |c| (1 - 1/s) log2 e < 2^-24: full fp32 relative
+// accuracy both for the e ~ 1e-3 that the Δ bias range produces (where a plain log2(1 + e) loses
+// about three digits) and for every large t, with no threshold branch.  (Applying the
+// correction to 1 + 2^t itself would be wrong for t > 24: there c is the rounding error of a
+// number above 2^24, up to 1, not a small fraction of s.)
 __device__ __forceinline__ float softplus2(float t) {
-  const float e = __builtin_amdgcn_exp2f(t);
+  const float e = __builtin_amdgcn_exp2f(-__builtin_fabsf(t));
   const float s = 1.0f + e;
   const float c = e - (s - 1.0f);
-  const float r = __builtin_fmaf(c, kLog2e, __builtin_amdgcn_logf(s));
-  return t > 20.0f * kLog2e ? t : r;
+  return __builtin_fmaxf(t, 0.0f) + __builtin_fmaf(c, kLog2e, __builtin_amdgcn_logf(s));
 }
 
-// softplus2(t) and, from the same e = 2^t, sigmoid(x) = e / (1 + e) (the derivative of softplus).
+// softplus2(t) and, from the same e = 2^-|t|, sigmoid(x) (the derivative of softplus):
+// 1 / (1 + e) for x >= 0, e / (1 + e) for x < 0.
 __device__ __forceinline__ float softplus2_sig(float t, float& sig) {
-  const float e = __builtin_amdgcn_exp2f(t);
+  const float e = __builtin_amdgcn_exp2f(-__builtin_fabsf(t));
   const float s = 1.0f + e;
   const float c = e - (s - 1.0f);
-  const float r = __builtin_fmaf(c, kLog2e, __builtin_amdgcn_logf(s));
-  const bool big = t > 20.0f * kLog2e;
-  sig = big ? 1.0f : e * __builtin_amdgcn_rcpf(s);
-  return big ? t : r;
+  const float q = __builtin_amdgcn_rcpf(s);
+  sig = t >= 0.0f ? q : e * q;
+  return __builtin_fmaxf(t, 0.0f) + __builtin_fmaf(c, kLog2e, __builtin_amdgcn_logf(s));
 }
 
 // Base-2 softplus argument from the raw Δ input and the bias already multiplied by log2 e.
@@ -469,7 +471,7 @@ struct Window {
 // A = -exp(A_log) for the wave's 8 states (the decay of a step is exp2(Δ2 A)); ns = d_state.
 __device__ __forceinline__ void load_a2(const DirArgs& da, const Lane& l, int ns, float (&A2)[kH]) {
 #pragma unroll
-  for (int k = 0; k < kH; ++k) A2[k] = -__expf(da.A_log[static_cast<int64_t>(l.dd) * ns + kH * l.part + k]);
+  for (int k = 0; k < kH; ++k) A2[k] = -expf(da.A_log[static_cast<int64_t>(l.dd) * ns + kH * l.part + k]);
 }
 
 // B/C of one position for the wave's state part: 8 + 8 wave-uniform floats (one s_load_dwordx16).
@@ -705,7 +707,7 @@ __global__ __launch_bounds__(256) void carry_prefix_kernel(ScanArgs a, float* re
   const int64_t bd = t / (2 * ns);  // b * dim + d
   const int d = static_cast<int>(bd % a.dim);
   const DirArgs& da = dir == 0 ? a.d0 : a.d1;
-  const float A2 = -__expf(da.A_log[static_cast<int64_t>(d) * ns + n]);  // with Σ Δ2: exp2(A Σ Δ2) = exp(A Σ Δ)
+  const float A2 = -expf(da.A_log[static_cast<int64_t>(d) * ns + n]);  // with Σ Δ2: exp2(A Σ Δ2) = exp(A Σ Δ)
   float* rec = recs + (bd * 2 + dir) * a.nch * stride;
   const bool up = (dir == 0) != (reverse != 0);  // the walk visits chunks in increasing order
   float h = 0.0f;
@@ -2272,7 +2274,7 @@ __global__ __launch_bounds__(256) void bwd_param_kernel(const float* __restrict_
     const int dir = item / (dim * ns), d = (item / ns) % dim, n = item % ns;
     const float s = wave_batch_sum(at(dir, n / kH, n % kH) + static_cast<int64_t>(d) * kParStride * batch, batch, lane);
     if (lane == 0) {
-      const float An = -__expf((dir == 0 ? A_log : A_b_log)[static_cast<int64_t>(d) * ns + n]);
+      const float An = -expf((dir == 0 ? A_log : A_b_log)[static_cast<int64_t>(d) * ns + n]);
       (dir == 0 ? dA_log : dA_b_log)[static_cast<int64_t>(d) * ns + n] = s * kLn2 * An;
     }
     return;
