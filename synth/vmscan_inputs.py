@@ -18,6 +18,13 @@ any layer can be regenerated independently.  Distributions follow the workloads:
 Tensor ids: Vim u=0, z=1, Δ_raw=2, B=3, C=4, B_b=5, C_b=6, dt=7 and, for a separate backward
 branch, u_b=8, Δ_raw_b=9, dt_b=17; SS2D x=0, z=1 and, for direction k, Δ_raw=10k+2, B=10k+3,
 C=10k+4, dt=10k+7.  Front convolutions: x=50, conv_w=51, conv_b=52, conv_w_b=53, conv_b_b=54.
+
+Independent parameters (``params="indep"``): the parity tests also draw the parameters the
+pages initialise to shared constants, so that every per-channel, per-direction and per-branch
+parameter differs from every other (v2 gives the backward branch its own parameter set; SS2D
+gives each direction its own projections).  A_log = log(1..N) + U[-0.5, 0.5] per (channel,
+state), D ~ U[-1.5, 1.5] per channel, each tensor from its own stream: Vim A_log=20, A_b_log=21,
+D=22, D_b=23; SS2D direction k A_log=10k+5, D=10k+6 (its Δ bias already has its own draw).
 """
 import numpy as np
 
@@ -63,19 +70,39 @@ def a_log_init(dim, d_state):
     return np.tile(np.log(np.arange(1, d_state + 1, dtype=np.float64)), (dim, 1)).astype(np.float32)
 
 
-def make_vim_inputs(cfg, layer=0, batch=None, dim=None, seqlen=None, d_state=None, dtype=None):
+def a_log_indep(cfg, layer, tid, dim, d_state):
+    """A_log = log(1..d_state) + U[-0.5, 0.5], drawn per (channel, state) (float32)."""
+    jitter = _rng(cfg, layer, tid).uniform(-0.5, 0.5, size=(dim, d_state))
+    return (np.log(np.arange(1, d_state + 1, dtype=np.float64))[None, :] + jitter).astype(np.float32)
+
+
+def d_indep(cfg, layer, tid, dim):
+    """D ~ U[-1.5, 1.5] per channel (float32)."""
+    return _rng(cfg, layer, tid).uniform(-1.5, 1.5, size=dim).astype(np.float32)
+
+
+def make_vim_inputs(cfg, layer=0, batch=None, dim=None, seqlen=None, d_state=None, dtype=None, params="init"):
     """Inputs of one bidirectional Vim scan call as a dict of float32 numpy arrays.
 
     Defaults come from ``CONFIGS[cfg]``; the overrides give smaller or ragged shapes with the
     same distributions (used by the parity tests).  Values of bf16 workloads are already
-    rounded to bf16."""
+    rounded to bf16.  ``params="indep"`` draws A_log, A_b_log, D and D_b independently (see the
+    module docstring) instead of the shared initial values."""
     c = CONFIGS.get(cfg, CONFIGS[0])
     nb = c["batch"] if batch is None else batch
     nd = c["dim"] if dim is None else dim
     L = c["seqlen"] if seqlen is None else seqlen
     N = c["d_state"] if d_state is None else d_state
     dt = c["dtype"] if dtype is None else dtype
-    al = a_log_init(nd, N)
+    if params not in ("init", "indep"):
+        raise ValueError(f"params must be 'init' or 'indep', not {params!r}")
+    if params == "indep":
+        al, alb = a_log_indep(cfg, layer, 20, nd, N), a_log_indep(cfg, layer, 21, nd, N)
+        dd, ddb = d_indep(cfg, layer, 22, nd), d_indep(cfg, layer, 23, nd)
+    else:
+        al = a_log_init(nd, N)
+        alb = al.copy()
+        dd, ddb = np.ones(nd, dtype=np.float32), np.ones(nd, dtype=np.float32)
     return dict(
         u=_normal(cfg, layer, 0, (nb, nd, L), dt),
         z=_normal(cfg, layer, 1, (nb, nd, L), dt),
@@ -85,18 +112,18 @@ def make_vim_inputs(cfg, layer=0, batch=None, dim=None, seqlen=None, d_state=Non
         B_b=_normal(cfg, layer, 5, (nb, N, L), dt),
         C_b=_normal(cfg, layer, 6, (nb, N, L), dt),
         A_log=al,
-        A_b_log=al.copy(),
-        D=np.ones(nd, dtype=np.float32),
-        D_b=np.ones(nd, dtype=np.float32),
+        A_b_log=alb,
+        D=dd,
+        D_b=ddb,
         delta_bias=dt_bias(cfg, layer, 7, nd),
         dtype=dt,
     )
 
 
-def make_vim_v2_inputs(cfg, layer=0, batch=None, dim=None, seqlen=None, d_state=None, dtype=None):
+def make_vim_v2_inputs(cfg, layer=0, batch=None, dim=None, seqlen=None, d_state=None, dtype=None, params="init"):
     """``make_vim_inputs`` plus a separate backward branch: u_b, delta_raw_b (same distributions)
     and delta_bias_b (its own dt draw), for the bidirectional scan with v2 parameter sets."""
-    p = make_vim_inputs(cfg, layer, batch, dim, seqlen, d_state, dtype)
+    p = make_vim_inputs(cfg, layer, batch, dim, seqlen, d_state, dtype, params)
     nb, nd, L = p["u"].shape
     p["u_b"] = _normal(cfg, layer, 8, (nb, nd, L), p["dtype"])
     p["delta_raw_b"] = _normal(cfg, layer, 9, (nb, nd, L), p["dtype"])
@@ -104,10 +131,12 @@ def make_vim_v2_inputs(cfg, layer=0, batch=None, dim=None, seqlen=None, d_state=
     return p
 
 
-def make_ss2d_inputs(cfg=4, layer=0, batch=None, dim=None, H=None, W=None, d_state=None, dtype=None, with_z=False):
+def make_ss2d_inputs(cfg=4, layer=0, batch=None, dim=None, H=None, W=None, d_state=None, dtype=None, with_z=False,
+                     params="init"):
     """Inputs of one SS2D cross-scan call: x [batch, dim, H, W]; delta_raw [batch, 4, dim, H*W];
     B, C [batch, 4, N, H*W] (scan order of each direction); A_log [4, dim, N]; D, delta_bias
-    [4, dim]; z [batch, dim, H, W] only when ``with_z``."""
+    [4, dim]; z [batch, dim, H, W] only when ``with_z``.  ``params="indep"`` draws every
+    direction's A_log and D independently (see the module docstring)."""
     c = CONFIGS.get(cfg, CONFIGS[4])
     nb = c["batch"] if batch is None else batch
     nd = c["dim"] if dim is None else dim
@@ -116,13 +145,21 @@ def make_ss2d_inputs(cfg=4, layer=0, batch=None, dim=None, H=None, W=None, d_sta
     N = c["d_state"] if d_state is None else d_state
     dt = c["dtype"] if dtype is None else dtype
     L = h * w
+    if params not in ("init", "indep"):
+        raise ValueError(f"params must be 'init' or 'indep', not {params!r}")
+    if params == "indep":
+        al = np.stack([a_log_indep(cfg, layer, 10 * k + 5, nd, N) for k in range(4)], axis=0)
+        dd = np.stack([d_indep(cfg, layer, 10 * k + 6, nd) for k in range(4)], axis=0)
+    else:
+        al = np.stack([a_log_init(nd, N) for _ in range(4)], axis=0)
+        dd = np.ones((4, nd), dtype=np.float32)
     out = dict(
         x=_normal(cfg, layer, 0, (nb, nd, h, w), dt),
         delta_raw=np.stack([_normal(cfg, layer, 10 * k + 2, (nb, nd, L), dt) for k in range(4)], axis=1),
         B=np.stack([_normal(cfg, layer, 10 * k + 3, (nb, N, L), dt) for k in range(4)], axis=1),
         C=np.stack([_normal(cfg, layer, 10 * k + 4, (nb, N, L), dt) for k in range(4)], axis=1),
-        A_log=np.stack([a_log_init(nd, N) for _ in range(4)], axis=0),
-        D=np.ones((4, nd), dtype=np.float32),
+        A_log=al,
+        D=dd,
         delta_bias=np.stack([dt_bias(cfg, layer, 10 * k + 7, nd) for k in range(4)], axis=0),
         z=_normal(cfg, layer, 1, (nb, nd, h, w), dt) if with_z else None,
         dtype=dt,
