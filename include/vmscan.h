@@ -24,7 +24,8 @@
  *
  * Conventions shared by every entry point:
  *   - Ownership: every pointer is caller-owned DEVICE memory (except `stream`).  The library never
- *     allocates or frees memory and keeps no state other than a thread-local last HIP error.
+ *     allocates or frees memory.  Its only state is a thread-local last HIP error and, for
+ *     vmscan_fwd_bidir_noalloc, the address of its fixed device scratch buffer on each device.
  *   - Layout: all tensors are dense, row-major, with the shapes stated per argument.  Every
  *     pointer must be 16-byte aligned (else VMSCAN_ERR_ALIGN).  `out` must not alias an input.
  *   - Activation dtype: VMSCAN_F32 (float) or VMSCAN_BF16 (bfloat16 bit patterns, 2 bytes) for
@@ -60,7 +61,8 @@ typedef enum {
   VMSCAN_ERR_UNSUPPORTED = 3, /* d_state or dtype not supported                                */
   VMSCAN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                              */
   VMSCAN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the queried size               */
-  VMSCAN_ERR_HIP = 6          /* a HIP call failed; see vmscan_last_hip_error()                */
+  VMSCAN_ERR_HIP = 6,         /* a HIP call failed; see vmscan_last_hip_error()                */
+  VMSCAN_ERR_SCRATCH = 7      /* the call needs more than VMSCAN_SCRATCH_BYTES (no-alloc entry) */
 } vmscan_status;
 
 typedef enum { VMSCAN_F32 = 0, VMSCAN_BF16 = 1 } vmscan_dtype;
@@ -116,6 +118,31 @@ vmscan_status vmscan_fwd_bidir_ex(const void *u, const void *delta_raw, const vo
                                   void *out, int64_t batch, int64_t dim, int64_t seqlen, int d_state,
                                   vmscan_dtype dtype, void *workspace, size_t workspace_bytes,
                                   int64_t chunk_len, hipStream_t stream);
+
+/*
+ * vmscan_fwd_bidir for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same computation, kernels and
+ * results as vmscan_fwd_bidir (bit for bit), with the workspace taken from a fixed scratch
+ * buffer of VMSCAN_SCRATCH_BYTES that the library holds in device memory (a file-scope device
+ * array, one per GPU, loaded with the library's code object and kept until the process ends)
+ * instead of a caller's workspace.  The caller still passes every input and the output, with
+ * the layouts, validation and error codes of vmscan_fwd_bidir.  The call allocates nothing
+ * (no hipMalloc/hipFree or allocating library routine); on its first call on a device it looks
+ * up that device's copy of the buffer (hipGetSymbolAddress, with that device current).
+ * A shape whose workspace (vmscan_fwd_bidir_workspace_bytes) exceeds VMSCAN_SCRATCH_BYTES
+ * returns VMSCAN_ERR_SCRATCH before anything is enqueued; the other entry points take such shapes.
+ * Every call on one GPU uses that GPU's one buffer: calls that overlap on one GPU (on different
+ * streams or from different threads) race and give unspecified results; calls ordered on one
+ * stream are safe.  The buffer keeps the last call's contents; the forward scan needs none of
+ * them cleared.
+ */
+#define VMSCAN_SCRATCH_BYTES ((size_t)64 << 20)
+vmscan_status vmscan_fwd_bidir_noalloc(const void *u, const void *delta_raw, const void *z,
+                                       const float *A_log, const float *A_b_log,
+                                       const void *B, const void *C, const void *B_b, const void *C_b,
+                                       const float *D, const float *D_b, const float *delta_bias,
+                                       void *out, int64_t batch, int64_t dim, int64_t seqlen,
+                                       int d_state, vmscan_dtype dtype, hipStream_t stream);
 
 /*
  * The two stages of vmscan_fwd_bidir_ex, for callers that time or overlap them separately:

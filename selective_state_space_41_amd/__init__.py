@@ -45,6 +45,9 @@ def _load():
     lib.vmscan_fwd_bidir_ex.argtypes = fwd_args + [_i64, _c_void_p]
     lib.vmscan_fwd_bidir_stage.restype = ctypes.c_int
     lib.vmscan_fwd_bidir_stage.argtypes = fwd_args + [_i64, ctypes.c_int, _c_void_p]
+    lib.vmscan_fwd_bidir_noalloc.restype = ctypes.c_int
+    lib.vmscan_fwd_bidir_noalloc.argtypes = [_c_void_p] * 13 + [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int,
+                                                                 _c_void_p]
     v2_args = [_c_void_p] * 16 + [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _c_void_p, ctypes.c_size_t, _i64]
     lib.vmscan_fwd_bidir_v2.restype = ctypes.c_int
     lib.vmscan_fwd_bidir_v2.argtypes = v2_args + [_c_void_p]
@@ -199,6 +202,36 @@ def vmscan_fwd_bidir(u, delta_raw, z, A_log, A_b_log, B, C, B_b, C_b, D, D_b, de
         _ptr(u), _ptr(delta_raw), _ptr(z), _ptr(A_log), _ptr(A_b_log), _ptr(B), _ptr(C), _ptr(B_b), _ptr(C_b),
         _ptr(D), _ptr(D_b), _ptr(delta_bias), _ptr(out), nb, nd, L, ns, dt,
         _ptr(workspace), _nbytes(workspace), int(chunk_len), int(stage), _stream(stream, dev)))
+    return out
+
+
+SCRATCH_BYTES = 64 << 20  # VMSCAN_SCRATCH_BYTES: the no-allocation entry point's fixed scratch
+
+
+def vmscan_fwd_bidir_noalloc(u, delta_raw, z, A_log, A_b_log, B, C, B_b, C_b, D, D_b, delta_bias, out,
+                             stream=None):
+    """vmscan_fwd_bidir without any device allocation: the library's fixed per-GPU scratch buffer
+    stands in for the workspace, and the caller passes ``out``.  Same arguments and result as
+    ``vmscan_fwd_bidir`` (bit for bit); raises for shapes whose workspace would exceed
+    ``SCRATCH_BYTES``.  Calls that overlap on one GPU share that buffer and race."""
+    if u.dim() != 3:
+        raise ValueError("u must be [batch, dim, L]")
+    nb, nd, L = u.shape
+    ns = _d_state(A_log)
+    dev = u.device
+    adt = u.dtype
+    dt = _act_dtype(u)
+    for name, t in (("u", u), ("delta_raw", delta_raw), ("z", z), ("out", out)):
+        _need(t, name, (nb, nd, L), adt, dev)
+    for name, t in (("B", B), ("C", C), ("B_b", B_b), ("C_b", C_b)):
+        _need(t, name, (nb, ns, L), adt, dev)
+    for name, t in (("A_log", A_log), ("A_b_log", A_b_log)):
+        _need(t, name, (nd, ns), torch.float32, dev)
+    for name, t in (("D", D), ("D_b", D_b), ("delta_bias", delta_bias)):
+        _need(t, name, (nd,), torch.float32, dev)
+    _check(load().vmscan_fwd_bidir_noalloc(
+        _ptr(u), _ptr(delta_raw), _ptr(z), _ptr(A_log), _ptr(A_b_log), _ptr(B), _ptr(C), _ptr(B_b), _ptr(C_b),
+        _ptr(D), _ptr(D_b), _ptr(delta_bias), _ptr(out), nb, nd, L, ns, dt, _stream(stream, dev)))
     return out
 
 

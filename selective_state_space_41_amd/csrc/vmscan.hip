@@ -61,6 +61,7 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <mutex>
 
 #include "vmscan.h"
 
@@ -2676,6 +2677,39 @@ vmscan_status run_ss2d_bwd(const void* x, const void* delta_raw, const float* A_
   return e == hipSuccess ? VMSCAN_OK : launch_failed(e);
 }
 
+// Fixed scratch for vmscan_fwd_bidir_noalloc: device memory the code object brings with it, so
+// that entry point never allocates.  Each GPU the library is loaded on holds its own copy until
+// the process ends.  In host code `scratch` names a host-side stand-in, not device memory: the
+// device address of each GPU's copy comes from hipGetSymbolAddress (scratch_ptr) and only that
+// address is ever passed to a kernel.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[VMSCAN_SCRATCH_BYTES];
+
+namespace {
+
+// The current device's copy of `scratch`, looked up once per device (with that device current).
+vmscan_status scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return launch_failed(e);
+  if (dev < 0 || dev >= kMaxDevices) return VMSCAN_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return launch_failed(e);
+    if (!p) return launch_failed(hipErrorInvalidSymbol);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return VMSCAN_OK;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------------------------
@@ -2693,6 +2727,8 @@ const char* vmscan_status_string(vmscan_status s) {
     case VMSCAN_ERR_ALIGN: return "VMSCAN_ERR_ALIGN: a pointer is not 16-byte aligned";
     case VMSCAN_ERR_WORKSPACE: return "VMSCAN_ERR_WORKSPACE: workspace missing or too small";
     case VMSCAN_ERR_HIP: return "VMSCAN_ERR_HIP: a HIP call failed (see vmscan_last_hip_error)";
+    case VMSCAN_ERR_SCRATCH:
+      return "VMSCAN_ERR_SCRATCH: the call needs more workspace than the fixed scratch buffer (VMSCAN_SCRATCH_BYTES)";
   }
   return "VMSCAN_ERR_UNKNOWN";
 }
@@ -2817,6 +2853,28 @@ vmscan_status vmscan_fwd_bidir(const void* u, const void* delta_raw, const void*
                                hipStream_t stream) {
   return vmscan_fwd_bidir_ex(u, delta_raw, z, A_log, A_b_log, B, C, B_b, C_b, D, D_b, delta_bias, out, batch, dim,
                              seqlen, d_state, dtype, workspace, workspace_bytes, 0, stream);
+}
+
+vmscan_status vmscan_fwd_bidir_noalloc(const void* u, const void* delta_raw, const void* z, const float* A_log,
+                                       const float* A_b_log, const void* B, const void* C, const void* B_b,
+                                       const void* C_b, const float* D, const float* D_b, const float* delta_bias,
+                                       void* out, int64_t batch, int64_t dim, int64_t seqlen, int d_state,
+                                       vmscan_dtype dtype, hipStream_t stream) {
+  // Validate every argument first (a stand-in workspace that passes the workspace checks), so
+  // that bad arguments are reported as by vmscan_fwd_bidir, before any HIP call.
+  ScanArgs a{};
+  vmscan_status st = vim_args(a, u, delta_raw, delta_bias, u, delta_raw, delta_bias, z, A_log, A_b_log, B, C, B_b,
+                              C_b, D, D_b, out, batch, dim, seqlen, d_state, dtype,
+                              reinterpret_cast<void*>(static_cast<uintptr_t>(256)), SIZE_MAX, 0);
+  if (st != VMSCAN_OK) return st;
+  if (vmscan_fwd_bidir_workspace_bytes(batch, dim, seqlen, d_state, dtype) > VMSCAN_SCRATCH_BYTES)
+    return VMSCAN_ERR_SCRATCH;
+  void* ws = nullptr;
+  st = scratch_ptr(&ws);
+  if (st != VMSCAN_OK) return st;
+  return vmscan_fwd_bidir_v2_stage(u, delta_raw, delta_bias, u, delta_raw, delta_bias, z, A_log, A_b_log, B, C, B_b,
+                                   C_b, D, D_b, out, batch, dim, seqlen, d_state, dtype, ws, VMSCAN_SCRATCH_BYTES, 0,
+                                   kStageAll, stream);
 }
 
 size_t ss2d_cross_scan_workspace_bytes_ex(int64_t batch, int64_t dim, int64_t H, int64_t W, int d_state,
