@@ -183,11 +183,13 @@ def _cpu_worker(args):
 
 def cpu_baseline(cfg_id, cfg, min_s=1.0):
     """The fp64 oracle on the same workload: the batches of the Vim-Ti scan are split into
-    slices over a process pool (one process per host core, at most 16) and each process repeats
+    slices over a process pool (one process per host core, at most 16: the host share of a
+    one-GPU machine, whatever os.cpu_count() reports; both counts are recorded) and each process repeats
     its slice for at least ``min_s`` seconds.  Throughput = tokens·channels computed / slowest
     worker's compute time (input generation excluded)."""
     import multiprocessing as mp
-    workers = max(1, min(16, os.cpu_count() or 1))
+    host = os.cpu_count() or 1
+    workers = max(1, min(16, host))  # a one-GPU box's share of the host is 16 cores
     nb = cfg["batch"]
     per = math.ceil(nb / workers)
     slices = [(cfg_id, (i, min(nb, i + per)), min_s) for i in range(0, nb, per)]
@@ -197,7 +199,8 @@ def cpu_baseline(cfg_id, cfg, min_s=1.0):
     tpb = cfg["dim"] * cfg["seqlen"]
     work = sum(r * (b[1][1] - b[1][0]) * tpb for (r, _), b in zip(res, slices))
     wall = max(t for _, t in res)
-    return {"value": work / wall, "unit": "tokens·channels/s", "cores": len(slices), "kind": "oracle",
+    return {"value": work / wall, "unit": "tokens·channels/s", "cores": len(slices), "host_cores": host,
+            "kind": "oracle",
             "sample": f"{cfg['name']}: batch slices of {per} (all {nb} batches), each repeated for >= {min_s:.0f} s "
                       f"in its own process (fp64 numpy oracle); {sum(t for _, t in res):.1f} CPU-s in total, "
                       f"slowest worker {wall:.2f} s"}
@@ -338,46 +341,55 @@ def bench_config(cfg_id, steps, warmup, with_cpu, torch, V, v2=False, d_state=No
                                                     1 if cfg["dtype"] == "bf16" else 0)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
 
-    def call(i, stage=3):
-        act, par = sets[i % len(sets)]
+    def prepare(i, stage=3):
+        """The call on rotation set i, validated and marshalled once (the timed loops then make only
+        the C calls)."""
+        act, par = sets[i]
         if v2:
-            V.vmscan_fwd_bidir_v2(act["u"], act["delta_raw"], par["delta_bias"], act["u_b"], act["delta_raw_b"],
-                                  par["delta_bias_b"], act["z"], par["A_log"], par["A_b_log"], act["B"], act["C"],
-                                  act["B_b"], act["C_b"], par["D"], par["D_b"], out=act["out"], workspace=ws, stage=stage)
-        elif cfg["kind"] == "vim":
-            V.vmscan_fwd_bidir(act["u"], act["delta_raw"], act["z"], par["A_log"], par["A_b_log"], act["B"], act["C"],
-                               act["B_b"], act["C_b"], par["D"], par["D_b"], par["delta_bias"], out=act["out"], workspace=ws,
-                               stage=stage)
-        else:
-            V.ss2d_cross_scan_fwd(act["x"], act["delta_raw"], par["A_log"], act["B"], act["C"], par["D"],
-                                  par["delta_bias"], out=act["out"], workspace=ws)
+            return V.vmscan_fwd_bidir_v2(act["u"], act["delta_raw"], par["delta_bias"], act["u_b"], act["delta_raw_b"],
+                                         par["delta_bias_b"], act["z"], par["A_log"], par["A_b_log"], act["B"],
+                                         act["C"], act["B_b"], act["C_b"], par["D"], par["D_b"], out=act["out"],
+                                         workspace=ws, stage=stage, prepare=True)
+        if cfg["kind"] == "vim":
+            return V.vmscan_fwd_bidir(act["u"], act["delta_raw"], act["z"], par["A_log"], par["A_b_log"], act["B"],
+                                      act["C"], act["B_b"], act["C_b"], par["D"], par["D_b"], par["delta_bias"],
+                                      out=act["out"], workspace=ws, stage=stage, prepare=True)
+        return V.ss2d_cross_scan_fwd(act["x"], act["delta_raw"], par["A_log"], act["B"], act["C"], par["D"],
+                                     par["delta_bias"], out=act["out"], workspace=ws, prepare=True)
 
+    full = [prepare(i) for i in range(len(sets))]
     for i in range(warmup):
-        call(i)
+        full[i % len(sets)]()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)   # the binding launches on this stream
-    split = cfg["kind"] == "vim"              # Vim: time the scan stage (dominant kernel) on its own
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    e_end = torch.cuda.Event(enable_timing=True)
+    # The step: one whole call (all kernels of the path), back to back.
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     for i in range(steps):
-        ev[i][0].record(stream)
-        if split:
-            call(warmup + i, stage=1)
-            ev[i][1].record(stream)
-            call(warmup + i, stage=2)
-        else:
-            call(warmup + i)
-            ev[i][1].record(stream)
-    e_end.record(stream)
+        ev[i].record(stream)
+        full[(warmup + i) % len(sets)]()
+    ev[steps].record(stream)
     torch.cuda.synchronize()
-    total_ms = ev[0][0].elapsed_time(e_end)
-    step_ms = sorted(ev[i][0].elapsed_time(ev[i + 1][0] if i + 1 < steps else e_end) for i in range(steps))
+    total_ms = ev[0].elapsed_time(ev[steps])
+    step_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    # The dominant kernel on its own (Vim: the scan stage, timed between events after its
+    # preparation stage); SS2D: the whole call.
+    split = cfg["kind"] == "vim"
     if split:
-        scan_ms = [ev[i][1].elapsed_time(ev[i + 1][0] if i + 1 < steps else e_end) for i in range(steps)]
+        prep = [prepare(i, stage=1) for i in range(len(sets))]
+        scan = [prepare(i, stage=2) for i in range(len(sets))]
+        ek = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            j = (warmup + i) % len(sets)
+            prep[j]()
+            ek[i][0].record(stream)
+            scan[j]()
+            ek[i][1].record(stream)
+        torch.cuda.synchronize()
+        kern_ms = sum(a.elapsed_time(b) for a, b in ek) / steps
     else:
-        scan_ms = [ev[i][0].elapsed_time(ev[i + 1][0] if i + 1 < steps else e_end) for i in range(steps)]
-    kern_ms = sum(scan_ms) / steps
+        kern_ms = total_ms / steps
     ms = total_ms / steps
     value = toks / (ms * 1e-3)
     gbs = nbytes / (ms * 1e-3) / 1e9
@@ -391,6 +403,7 @@ def bench_config(cfg_id, steps, warmup, with_cpu, torch, V, v2=False, d_state=No
                        "all kernels of the call (transpose, chunk states, both SS2D pairs)"),
             "kernel_avg_us": round(kern_ms * 1000, 2),
             "updates_per_launch": upd,
+            "call_frac": round(upd / (ms * 1e-3) / ALU_PEAK_UPD_S, 4),
             "hbm": {"achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                     "algorithmic_bytes_per_step": nbytes}}
     rec = {
@@ -458,12 +471,11 @@ def bench_bwd(cfg_id, steps, warmup, torch, V, v2=False, with_cpu=False, d_state
     wsb = V.lib.vmscan_bwd_bidir_v2_workspace_bytes(nb, nd, L, N, 1 if cfg["dtype"] == "bf16" else 0)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
 
-    def call():
-        return V.vmscan_bwd_bidir_v2(act["u"], act["delta_raw"], par["delta_bias"], act["u_b"], act["delta_raw_b"],
-                                     par["delta_bias_b"], act["z"], par["A_log"], par["A_b_log"], act["B"], act["C"],
-                                     act["B_b"], act["C_b"], par["D"], par["D_b"], dout, shared=not v2, workspace=ws)
-
-    outs = call()  # allocate the gradient tensors once; later calls write into fresh ones of the same size
+    # validated once; each call rewrites the same gradient tensors
+    call, outs = V.vmscan_bwd_bidir_v2(act["u"], act["delta_raw"], par["delta_bias"], act["u_b"], act["delta_raw_b"],
+                                       par["delta_bias_b"], act["z"], par["A_log"], par["A_b_log"], act["B"], act["C"],
+                                       act["B_b"], act["C_b"], par["D"], par["D_b"], dout, shared=not v2, workspace=ws,
+                                       prepare=True)
     for _ in range(warmup):
         call()
     stream = torch.cuda.current_stream(dev)
@@ -559,27 +571,30 @@ def bench_front(cfg_id, steps, warmup, torch, V, with_cpu=False):
         else:
             V.ss2d_conv2d_silu_fwd(a["x"], wts["conv_w"], wts["conv_b"], x_out=a["u"], xT_out=a["xT"])
 
-    def scan(a):
+    scans = []
+    for a in sets:
         if vim:
-            V.vmscan_fwd_bidir_v2(a["u"], a["delta_raw"], par["delta_bias"], a["u_b"], a["delta_raw_b"],
-                                  par["delta_bias_b"], a["z"], par["A_log"], par["A_b_log"], a["B"], a["C"], a["B_b"],
-                                  a["C_b"], par["D"], par["D_b"], out=a["out"], workspace=ws)
+            scans.append(V.vmscan_fwd_bidir_v2(a["u"], a["delta_raw"], par["delta_bias"], a["u_b"], a["delta_raw_b"],
+                                               par["delta_bias_b"], a["z"], par["A_log"], par["A_b_log"], a["B"],
+                                               a["C"], a["B_b"], a["C_b"], par["D"], par["D_b"], out=a["out"],
+                                               workspace=ws, prepare=True))
         else:
-            V.ss2d_cross_scan_fwd(a["u"], a["delta_raw"], par["A_log"], a["B"], a["C"], par["D"], par["delta_bias"],
-                                  out=a["out"], workspace=ws, xT=a["xT"])
+            scans.append(V.ss2d_cross_scan_fwd(a["u"], a["delta_raw"], par["A_log"], a["B"], a["C"], par["D"],
+                                               par["delta_bias"], out=a["out"], workspace=ws, xT=a["xT"],
+                                               prepare=True))
 
     for i in range(warmup):
         front(sets[i % nsets])
-        scan(sets[i % nsets])
+        scans[i % nsets]()
     stream = torch.cuda.current_stream(dev)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
     for i in range(steps):
-        a = sets[(warmup + i) % nsets]
+        k = (warmup + i) % nsets
         ev[i][0].record(stream)
-        front(a)
+        front(sets[k])
         ev[i][1].record(stream)
-        scan(a)
+        scans[k]()
         ev[i][2].record(stream)
     torch.cuda.synchronize()
     ms = ev[0][0].elapsed_time(ev[-1][2]) / steps
@@ -629,10 +644,8 @@ def bench_ss2d_bwd(cfg_id, steps, warmup, torch, V, with_cpu=False, d_state=None
     wsb = V.lib.ss2d_cross_scan_bwd_workspace_bytes(nb, nd, H, W, N, 1 if cfg["dtype"] == "bf16" else 0)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
 
-    def call():
-        return V.ss2d_cross_scan_bwd(act["x"], act["delta_raw"], par["A_log"], act["B"], act["C"], par["D"],
-                                     par["delta_bias"], None, dout, workspace=ws)
-
+    call, outs = V.ss2d_cross_scan_bwd(act["x"], act["delta_raw"], par["A_log"], act["B"], act["C"], par["D"],
+                                       par["delta_bias"], None, dout, workspace=ws, prepare=True)
     for _ in range(max(1, warmup)):
         call()
     stream = torch.cuda.current_stream(dev)

@@ -111,6 +111,18 @@ def _check(code):
         raise RuntimeError(msg)
 
 
+def _call(fn, args, prepare, keep):
+    """Make the C call now, or with ``prepare`` return a callable that makes it again with the same
+    validated and marshalled arguments (no per-call checks: for timing and serving loops that
+    repeat one call on the same tensors, which ``keep`` holds alive)."""
+    if prepare:
+        def run(_keep=keep):
+            _check(fn(*args))
+        return run
+    _check(fn(*args))
+    return None
+
+
 def _act_dtype(t):
     if t.dtype == torch.float32:
         return VMSCAN_F32
@@ -167,7 +179,7 @@ def _d_state(A_log):
 
 
 def vmscan_fwd_bidir(u, delta_raw, z, A_log, A_b_log, B, C, B_b, C_b, D, D_b, delta_bias,
-                     out=None, chunk_len=0, workspace=None, stream=None, stage=3):
+                     out=None, chunk_len=0, workspace=None, stream=None, stage=3, prepare=False):
     """Bidirectional selective scan with the silu(z) gate; returns ``out`` [batch, dim, L].
 
     u, delta_raw, z: [batch, dim, L]; A_log, A_b_log: [dim, N] float32 (d_state N = 16 or 32,
@@ -175,7 +187,8 @@ def vmscan_fwd_bidir(u, delta_raw, z, A_log, A_b_log, B, C, B_b, C_b, D, D_b, de
     [dim] float32.  Activations are
     float32 or bfloat16 (all the same).  ``chunk_len`` 0 lets the library choose.  ``stage``
     1 / 2 runs only the preparation (B/C copy, chunk carries) / the fused scan
-    (vmscan_fwd_bidir_stage); 3 runs both."""
+    (vmscan_fwd_bidir_stage); 3 runs both.  ``prepare=True`` validates once and returns a callable
+    that repeats the call on the same tensors and stream."""
     if u.dim() != 3:
         raise ValueError("u must be [batch, dim, L]")
     nb, nd, L = u.shape
@@ -198,11 +211,12 @@ def vmscan_fwd_bidir(u, delta_raw, z, A_log, A_b_log, B, C, B_b, C_b, D, D_b, de
     lib = load()
     wsb = lib.vmscan_fwd_bidir_workspace_bytes_ex(nb, nd, L, ns, dt, int(chunk_len))
     workspace = _workspace(workspace, wsb, dev)
-    _check(lib.vmscan_fwd_bidir_stage(
-        _ptr(u), _ptr(delta_raw), _ptr(z), _ptr(A_log), _ptr(A_b_log), _ptr(B), _ptr(C), _ptr(B_b), _ptr(C_b),
-        _ptr(D), _ptr(D_b), _ptr(delta_bias), _ptr(out), nb, nd, L, ns, dt,
-        _ptr(workspace), _nbytes(workspace), int(chunk_len), int(stage), _stream(stream, dev)))
-    return out
+    args = (_ptr(u), _ptr(delta_raw), _ptr(z), _ptr(A_log), _ptr(A_b_log), _ptr(B), _ptr(C), _ptr(B_b), _ptr(C_b),
+            _ptr(D), _ptr(D_b), _ptr(delta_bias), _ptr(out), nb, nd, L, ns, dt,
+            _ptr(workspace), _nbytes(workspace), int(chunk_len), int(stage), _stream(stream, dev))
+    run = _call(lib.vmscan_fwd_bidir_stage, args, prepare, (u, delta_raw, z, A_log, A_b_log, B, C, B_b, C_b, D, D_b,
+                                                            delta_bias, out, workspace))
+    return run if prepare else out
 
 
 SCRATCH_BYTES = 64 << 20  # VMSCAN_SCRATCH_BYTES: the no-allocation entry point's fixed scratch
@@ -236,11 +250,11 @@ def vmscan_fwd_bidir_noalloc(u, delta_raw, z, A_log, A_b_log, B, C, B_b, C_b, D,
 
 
 def vmscan_fwd_bidir_v2(u, delta_raw, delta_bias, u_b, delta_raw_b, delta_bias_b, z, A_log, A_b_log, B, C, B_b,
-                        C_b, D, D_b, out=None, chunk_len=0, workspace=None, stream=None, stage=3):
+                        C_b, D, D_b, out=None, chunk_len=0, workspace=None, stream=None, stage=3, prepare=False):
     """Bidirectional scan whose backward branch has its own u_b, delta_raw_b and delta_bias_b
     (vmscan_fwd_bidir_v2_stage); the other arguments as for ``vmscan_fwd_bidir``.  u_b and
     delta_raw_b are [batch, dim, L] in original token order, delta_bias_b is [dim] float32; any
-    of them may be the forward branch's tensor."""
+    of them may be the forward branch's tensor.  ``prepare`` as for ``vmscan_fwd_bidir``."""
     if u.dim() != 3:
         raise ValueError("u must be [batch, dim, L]")
     nb, nd, L = u.shape
@@ -263,21 +277,24 @@ def vmscan_fwd_bidir_v2(u, delta_raw, delta_bias, u_b, delta_raw_b, delta_bias_b
     lib = load()
     wsb = lib.vmscan_fwd_bidir_workspace_bytes_ex(nb, nd, L, ns, dt, int(chunk_len))
     workspace = _workspace(workspace, wsb, dev)
-    _check(lib.vmscan_fwd_bidir_v2_stage(
-        _ptr(u), _ptr(delta_raw), _ptr(delta_bias), _ptr(u_b), _ptr(delta_raw_b), _ptr(delta_bias_b), _ptr(z),
-        _ptr(A_log), _ptr(A_b_log), _ptr(B), _ptr(C), _ptr(B_b), _ptr(C_b), _ptr(D), _ptr(D_b), _ptr(out),
-        nb, nd, L, ns, dt, _ptr(workspace), _nbytes(workspace), int(chunk_len), int(stage),
-        _stream(stream, dev)))
-    return out
+    args = (_ptr(u), _ptr(delta_raw), _ptr(delta_bias), _ptr(u_b), _ptr(delta_raw_b), _ptr(delta_bias_b), _ptr(z),
+            _ptr(A_log), _ptr(A_b_log), _ptr(B), _ptr(C), _ptr(B_b), _ptr(C_b), _ptr(D), _ptr(D_b), _ptr(out),
+            nb, nd, L, ns, dt, _ptr(workspace), _nbytes(workspace), int(chunk_len), int(stage),
+            _stream(stream, dev))
+    run = _call(lib.vmscan_fwd_bidir_v2_stage, args, prepare, (u, delta_raw, delta_bias, u_b, delta_raw_b,
+                                                               delta_bias_b, z, A_log, A_b_log, B, C, B_b, C_b, D,
+                                                               D_b, out, workspace))
+    return run if prepare else out
 
 
 def vmscan_bwd_bidir_v2(u, delta_raw, delta_bias, u_b, delta_raw_b, delta_bias_b, z, A_log, A_b_log, B, C, B_b, C_b,
-                        D, D_b, dout, shared=False, workspace=None, stream=None):
+                        D, D_b, dout, shared=False, workspace=None, stream=None, prepare=False):
     """Gradients of ``vmscan_fwd_bidir_v2`` for ``dout`` (vmscan_bwd_bidir_v2); returns a dict with
     du, ddelta_raw, ddelta_bias, du_b, ddelta_raw_b, ddelta_bias_b, dz, dA_log, dA_b_log, dB, dC,
     dB_b, dC_b, dD, dD_b.  With ``shared=True`` (u_b is u, delta_raw_b is delta_raw, delta_bias_b
     is delta_bias, i.e. ``vmscan_fwd_bidir``) the backward branch's du, ddelta_raw and ddelta_bias
-    are added into the forward ones and the ``_b`` entries are None.  d_state 16 or 32."""
+    are added into the forward ones and the ``_b`` entries are None.  d_state 16 or 32.  With
+    ``prepare`` it returns (callable, gradient dict): each call rewrites the same gradient tensors."""
     if u.dim() != 3:
         raise ValueError("u must be [batch, dim, L]")
     nb, nd, L = u.shape
@@ -303,24 +320,25 @@ def vmscan_bwd_bidir_v2(u, delta_raw, delta_bias, u_b, delta_raw_b, delta_bias_b
     lib = load()
     wsb = lib.vmscan_bwd_bidir_v2_workspace_bytes(nb, nd, L, ns, dt)
     workspace = _workspace(workspace, wsb, dev)
-    _check(lib.vmscan_bwd_bidir_v2(
-        _ptr(u), _ptr(delta_raw), _ptr(delta_bias), _ptr(u_b), _ptr(delta_raw_b), _ptr(delta_bias_b), _ptr(z),
-        _ptr(A_log), _ptr(A_b_log), _ptr(B), _ptr(C), _ptr(B_b), _ptr(C_b), _ptr(D), _ptr(D_b), _ptr(dout),
-        *[_ptr(g[k]) for k in ("du", "ddelta_raw", "ddelta_bias", "du_b", "ddelta_raw_b", "ddelta_bias_b", "dz",
-                               "dA_log", "dA_b_log", "dB", "dC", "dB_b", "dC_b", "dD", "dD_b")],
-        nb, nd, L, ns, dt, _ptr(workspace), _nbytes(workspace), _stream(stream, dev)))
-    return g
+    args = (_ptr(u), _ptr(delta_raw), _ptr(delta_bias), _ptr(u_b), _ptr(delta_raw_b), _ptr(delta_bias_b), _ptr(z),
+            _ptr(A_log), _ptr(A_b_log), _ptr(B), _ptr(C), _ptr(B_b), _ptr(C_b), _ptr(D), _ptr(D_b), _ptr(dout),
+            *[_ptr(g[k]) for k in ("du", "ddelta_raw", "ddelta_bias", "du_b", "ddelta_raw_b", "ddelta_bias_b", "dz",
+                                   "dA_log", "dA_b_log", "dB", "dC", "dB_b", "dC_b", "dD", "dD_b")],
+            nb, nd, L, ns, dt, _ptr(workspace), _nbytes(workspace), _stream(stream, dev))
+    run = _call(lib.vmscan_bwd_bidir_v2, args, prepare, (u, delta_raw, delta_bias, u_b, delta_raw_b, delta_bias_b, z,
+                                                         A_log, A_b_log, B, C, B_b, C_b, D, D_b, dout, g, workspace))
+    return (run, g) if prepare else g
 
 
 def ss2d_cross_scan_fwd(x, delta_raw, A_log, B, C, D, delta_bias, z=None, out=None, chunk_len=0,
-                        workspace=None, stream=None, xT=None):
+                        workspace=None, stream=None, xT=None, prepare=False):
     """SS2D four-direction cross-scan with cross-merge; returns ``out`` [batch, dim, H, W].
 
     x: [batch, dim, H, W]; delta_raw: [batch, 4, dim, H*W]; A_log: [4, dim, N] float32 (d_state
     N = 16 or 32); B, C: [batch, 4, N, H*W] (each direction's scan order); D, delta_bias: [4, dim]
     float32; z: optional [batch, dim, H, W] gate; xT: optional [batch, dim, W, H], x transposed
     (as written by ``ss2d_conv2d_silu_fwd``), read instead of a copy made by the call
-    (ss2d_cross_scan_fwd_xt)."""
+    (ss2d_cross_scan_fwd_xt).  ``prepare`` as for ``vmscan_fwd_bidir``."""
     if x.dim() != 4:
         raise ValueError("x must be [batch, dim, H, W]")
     nb, nd, H, W = x.shape
@@ -347,17 +365,20 @@ def ss2d_cross_scan_fwd(x, delta_raw, A_log, B, C, D, delta_bias, z=None, out=No
     workspace = _workspace(workspace, wsb, dev)
     args = (_ptr(delta_raw), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(delta_bias), _ptr(z), _ptr(out),
             nb, nd, H, W, ns, dt, _ptr(workspace), _nbytes(workspace), int(chunk_len), _stream(stream, dev))
+    keep = (x, xT, delta_raw, A_log, B, C, D, delta_bias, z, out, workspace)
     if xT is None:
-        _check(lib.ss2d_cross_scan_fwd_ex(_ptr(x), *args))
+        run = _call(lib.ss2d_cross_scan_fwd_ex, (_ptr(x),) + args, prepare, keep)
     else:
         _need(xT, "xT", (nb, nd, W, H), adt, dev)
-        _check(lib.ss2d_cross_scan_fwd_xt(_ptr(x), _ptr(xT), *args))
-    return out
+        run = _call(lib.ss2d_cross_scan_fwd_xt, (_ptr(x), _ptr(xT)) + args, prepare, keep)
+    return run if prepare else out
 
 
-def ss2d_cross_scan_bwd(x, delta_raw, A_log, B, C, D, delta_bias, z, dout, workspace=None, stream=None):
+def ss2d_cross_scan_bwd(x, delta_raw, A_log, B, C, D, delta_bias, z, dout, workspace=None, stream=None,
+                        prepare=False):
     """Gradients of ``ss2d_cross_scan_fwd`` for ``dout`` (ss2d_cross_scan_bwd); returns a dict with
-    dx, ddelta_raw, dA_log, dB, dC, dD, ddelta_bias and dz (None when z is None).  d_state 16 or 32."""
+    dx, ddelta_raw, dA_log, dB, dC, dD, ddelta_bias and dz (None when z is None).  d_state 16 or 32.
+    ``prepare`` as for ``vmscan_bwd_bidir_v2``."""
     if x.dim() != 4:
         raise ValueError("x must be [batch, dim, H, W]")
     nb, nd, H, W = x.shape
@@ -382,11 +403,12 @@ def ss2d_cross_scan_bwd(x, delta_raw, A_log, B, C, D, delta_bias, z, dout, works
     lib = load()
     wsb = lib.ss2d_cross_scan_bwd_workspace_bytes(nb, nd, H, W, ns, dt)
     workspace = _workspace(workspace, wsb, dev)
-    _check(lib.ss2d_cross_scan_bwd(
-        _ptr(x), _ptr(delta_raw), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(delta_bias), _ptr(z), _ptr(dout),
-        *[_ptr(g[k]) for k in ("dx", "ddelta_raw", "dA_log", "dB", "dC", "dD", "ddelta_bias", "dz")],
-        nb, nd, H, W, ns, dt, _ptr(workspace), _nbytes(workspace), _stream(stream, dev)))
-    return g
+    args = (_ptr(x), _ptr(delta_raw), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(delta_bias), _ptr(z), _ptr(dout),
+            *[_ptr(g[k]) for k in ("dx", "ddelta_raw", "dA_log", "dB", "dC", "dD", "ddelta_bias", "dz")],
+            nb, nd, H, W, ns, dt, _ptr(workspace), _nbytes(workspace), _stream(stream, dev))
+    run = _call(lib.ss2d_cross_scan_bwd, args, prepare, (x, delta_raw, A_log, B, C, D, delta_bias, z, dout, g,
+                                                         workspace))
+    return (run, g) if prepare else g
 
 
 def conv1d_silu_fwd(x, conv_w, conv_b, conv_w_b=None, conv_b_b=None, u=None, u_b=None, stream=None):

@@ -2,6 +2,8 @@
 
 ``python -m selective_state_space_41_amd.build`` (or ``build()``) runs hipcc on
 ``csrc/vmscan.hip`` and writes ``libvmscan.so`` next to this file; it always recompiles.
+``python -m selective_state_space_41_amd.build --probe`` builds only the issue-rate
+microbenchmark (``csrc/probe.hip`` -> ``vmscan_probe``), which is not part of the library.
 """
 import os
 import shutil
@@ -35,20 +37,26 @@ def _run(cmd):
 
 
 def build(verbose=False):
-    """Compile libvmscan.so and the throughput probe executable."""
+    """Compile libvmscan.so."""
     hipcc = _hipcc()
     tmp = LIB + ".tmp"
     out = _run([hipcc, *HIP_FLAGS, "-shared", "-I", os.path.join(ROOT, "include"),
                 "-o", tmp, os.path.join(PKG, "csrc", "vmscan.hip")])
     os.replace(tmp, LIB)
-    probe_src = os.path.join(PKG, "csrc", "probe.hip")
-    if os.path.exists(probe_src):
-        out += _run([hipcc, *HIP_FLAGS, "-o", PROBE + ".tmp", probe_src])
-        os.replace(PROBE + ".tmp", PROBE)
     if verbose and out.strip():
         print(out)
     return LIB
 
 
+def build_probe(verbose=False):
+    """Compile the issue-rate microbenchmark executable (measures the gfx950 VALU, exp2 and
+    scan-token rates the kernel design relies on)."""
+    out = _run([_hipcc(), *HIP_FLAGS, "-o", PROBE + ".tmp", os.path.join(PKG, "csrc", "probe.hip")])
+    os.replace(PROBE + ".tmp", PROBE)
+    if verbose and out.strip():
+        print(out)
+    return PROBE
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build_probe(verbose="-v" in sys.argv) if "--probe" in sys.argv else build(verbose="-v" in sys.argv))
