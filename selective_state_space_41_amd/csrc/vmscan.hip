@@ -487,13 +487,16 @@ __device__ __forceinline__ scalar_fp bc_row(const ScanArgs& a, const Lane& l) {
   return (scalar_fp)(a.bct) + (((static_cast<int64_t>(l.b) * 2 + DIR) * a.parts + l.part) * a.L) * kBC;
 }
 
-// One token for the wave's 8 states, h = exp2(Δ2 A) h + (Δ2 u)(B ln 2); returns yi + Σ C h.  The B/C of
-// the next token (nxt) is requested once this token's B values are dead (after the h updates),
-// so at most 32 SGPRs hold B/C.  Scalar loads may return out of order, so the wait for this
-// token's B/C (at its first use) covers every scalar load in flight; issuing nxt after that point
-// leaves it the readout plus the next token's decays to arrive.
+// One token for the wave's 8 states, h = exp2(Δ2 A) h + (Δ2 u)(B ln 2); returns yi + Σ C h.  Scalar
+// loads may return out of order, so any wait for one covers every scalar load in flight: the token
+// first waits for its own B/C (requested a token ago), then requests the next token's (nxt), which
+// so has this whole token's work to arrive before the next token waits for it.  32 SGPRs hold B/C.
 __device__ __forceinline__ float scan_token(float dl, float du, float yi, const float (&A2)[kH], float (&h)[kH],
                                            const float (&cur)[kBC], float (&nxt)[kBC], scalar_fp nxt_p) {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited for
+  __builtin_amdgcn_sched_barrier(0);
+  load_bc(nxt_p, nxt);
+  __builtin_amdgcn_sched_barrier(0);
   float an[kH];
 #pragma unroll
   for (int n = 0; n < kH; ++n) an[n] = __builtin_amdgcn_exp2f(dl * A2[n]);
@@ -502,9 +505,6 @@ __device__ __forceinline__ float scan_token(float dl, float du, float yi, const 
     h[n] = h[n] * an[n];
     h[n] = __builtin_fmaf(du, cur[n], h[n]);
   }
-  __builtin_amdgcn_sched_barrier(0);
-  load_bc(nxt_p, nxt);
-  __builtin_amdgcn_sched_barrier(0);
   float y0 = yi, y1 = 0.0f;
 #pragma unroll
   for (int n = 0; n < kH; n += 2) {
@@ -1090,6 +1090,220 @@ __global__ __launch_bounds__(2 * kW * NP) void scan_pair_kernel(ScanArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// Whole-sequence walk of one bidirectional pair (SS2D sequences too long for an LDS row).
+//
+// A sequence longer than an LDS row would otherwise be cut into chunks, and every chunk but the
+// last needs its end state from a second pass over it (the chunk pass), about 0.8 of a scan's
+// work.  When the (batch, channel-group) tiles alone fill the GPU, each pair instead walks its
+// sequence whole: the same meet-in-the-middle schedule as scan_pair_kernel, but the channel's y
+// row lives in global memory, position-major ([position][64 lanes] per tile), so every store of
+// one step is one 256-byte line whatever the order of the positions.  Within a direction the
+// state parts add their partial readouts in part order through a small LDS ring of windows (the
+// last part adds its own and does the global store or, in the second half, the read-add of the
+// other direction's value); the first part reuses a ring slot only after the last part has
+// consumed it.  The fp32 sums of both directions are what the merge kernel then reads.
+
+constexpr int kRing = 2;  // windows in flight between the first and the last state part
+
+template <int NP>
+struct WalkShared {
+  float ring[2][kRing][kWin][kW];  // [dir][slot][step][lane]: partial y of a window, parts so far
+  int prod[2][NP];                 // [dir][part]: units the part has added to its ring slot
+  int cons[2];                     // [dir]: units the last part has consumed
+};
+
+// One window (len steps at positions p0 + kStep j) of partial readouts y: combined over the state
+// parts in part order through the ring; the last part then stores the direction's value (PHASE
+// 0) or adds it to the other direction's value r (PHASE 1) in the global row G.  keep >= 0: the
+// step at that index is the odd sequence's middle token in the backward direction, whose value
+// is returned in *vkeep instead of being stored (it is added after the phase barrier).
+template <int DIR, int PHASE, int NP, int LEN>
+__device__ __forceinline__ void walk_combine(WalkShared<NP>& sh, const Lane& l, int unit, const float (&y)[LEN],
+                                             const float (&r)[LEN], float* G, int64_t p0, int kStep, int keep,
+                                             float* vkeep) {
+  float* slot = &sh.ring[DIR][unit % kRing][0][0];
+  if (l.part == 0) {
+    unit_wait(&sh.cons[DIR], unit - kRing + 1);  // the last part is done with this slot's previous use
+#pragma unroll
+    for (int j = 0; j < LEN; ++j) slot[j * kW + l.lane] = y[j];
+    unit_signal(&sh.prod[DIR][0], unit + 1);
+    return;
+  }
+  unit_wait(&sh.prod[DIR][l.part - 1], unit + 1);
+  float v[LEN];
+#pragma unroll
+  for (int j = 0; j < LEN; ++j) v[j] = slot[j * kW + l.lane] + y[j];
+  if (l.part < NP - 1) {
+#pragma unroll
+    for (int j = 0; j < LEN; ++j) slot[j * kW + l.lane] = v[j];
+    unit_signal(&sh.prod[DIR][l.part], unit + 1);
+    return;
+  }
+  asm volatile("" ::: "memory");  // the slot is read before it is released
+  unit_signal(&sh.cons[DIR], unit + 1);
+#pragma unroll
+  for (int j = 0; j < LEN; ++j) {
+    float* g = G + (p0 + kStep * j) * kW + l.lane;
+    if (PHASE == 1) *g = r[j] + v[j];
+    else if (j == keep) *vkeep = v[j];
+    else *g = v[j];
+  }
+}
+
+template <typename T, int DIR, int PHASE, int NP>
+__device__ __forceinline__ void walk_phase(const ScanArgs& a, const Lane& l, const DirArgs& da, float bias, float Dh,
+                                           int i_begin, int n_win, int i_end, int keep_step, const float (&A2)[kH],
+                                           float (&h)[kH], scalar_fp bct, float (&bcA)[kBC], float (&bcB)[kBC],
+                                           float* G, WalkShared<NP>& sh, int& unit, float* vkeep) {
+  constexpr int MODE = kModeFirstPair;  // pair semantics: the backward direction's inputs are stored reversed
+  Window<T, MODE, DIR> win;
+  const int full_end = i_begin + n_win * kWin;
+  constexpr int kStep = DIR == 0 ? 1 : -1;
+  const bool last = l.part == NP - 1;
+  if (full_end > i_begin) win.load(a, l, da, i_begin);
+  for (int i0 = i_begin; i0 < full_end; i0 += kWin) {
+    float uu[kWin], xr[kWin], dl[kWin], du[kWin], yi[kWin], y[kWin], r[kWin];
+    rotate_priority(i0 / kWin);
+    win.unpack(uu, xr);
+    __builtin_amdgcn_sched_barrier(0);  // see chunk_state_dir
+    win.load(a, l, da, i0 + kWin < full_end ? i0 + kWin : i0);
+    const int64_t p0 = DIR == 0 ? i0 : l.Kc - 1 - i0;
+    if (PHASE == 1 && last) {
+      // the other direction's values, requested a window's work before they are added
+#pragma unroll
+      for (int j = 0; j < kWin; ++j) r[j] = G[(p0 + kStep * j) * kW + l.lane];
+    }
+    prep_window(uu, xr, bias, Dh, dl, du, yi);
+    run_steps<MODE, DIR>(l, i0, dl, du, yi, A2, h, bcA, bcB, bct, y);
+    walk_combine<DIR, PHASE, NP, kWin>(sh, l, unit, y, r, G, p0, kStep, -1, vkeep);
+    ++unit;
+  }
+  for (int i = full_end; i < i_end; ++i) {
+    float dl, y[1], r[1];
+    const int64_t pos = DIR == 0 ? i : l.Kc - 1 - i;
+    if (PHASE == 1 && last) r[0] = G[pos * kW + l.lane];
+    y[0] = single_step<T, MODE, DIR>(a, l, da, bias, Dh, i, A2, h, bct, bcA, &dl);
+    walk_combine<DIR, PHASE, NP, 1>(sh, l, unit, y, r, G, pos, kStep, i == keep_step ? 0 : -1, vkeep);
+    ++unit;
+  }
+}
+
+template <typename T, int DIR, int NP>
+__device__ __forceinline__ void walk_dir(const ScanArgs& a, const Lane& l, WalkShared<NP>& sh) {
+  using Dr = Dir<kModeFirstPair, DIR>;
+  const DirArgs& da = DIR == 0 ? a.d0 : a.d1;
+  const int L = l.Kc;
+  const int M = (L + 1) >> 1;  // steps of the first half
+  const bool odd = (L & 1) != 0;
+  float A2[kH], h[kH];
+  load_a2(da, l, a.ns, A2);
+#pragma unroll
+  for (int n = 0; n < kH; ++n) h[n] = 0.0f;
+  const float bias = da.bias[l.dd] * kLog2e;
+  const float Dh = l.part == 0 ? da.Dp[l.dd] : 0.0f;
+  const scalar_fp bct = bc_row<DIR>(a, l);
+  float* G = a.wsy + ((static_cast<int64_t>(l.b) * a.ngroups + l.d / kW) * a.L) * kW;
+  float bcA[kBC], bcB[kBC];
+  load_bc(bct + Dr::pos(l, 0) * kBC, bcA);
+  const int nw0 = (odd ? M - 1 : M) / kWin;
+  // In an odd sequence both directions reach the middle token at step M - 1: the forward one
+  // stores it, the backward one adds its value after the phase barrier.
+  const int keep = (DIR == 1 && odd) ? M - 1 : -1;
+  float vmid = 0.0f;
+  int unit = 0;
+  walk_phase<T, DIR, 0, NP>(a, l, da, bias, Dh, 0, nw0, M, keep, A2, h, bct, bcA, bcB, G, sh, unit, &vmid);
+  __syncthreads();  // first halves of both directions stored (global memory, workgroup scope)
+  if (keep >= 0 && l.part == NP - 1) G[static_cast<int64_t>(M - 1) * kW + l.lane] += vmid;
+  walk_phase<T, DIR, 1, NP>(a, l, da, bias, Dh, M, (L - M) / kWin, L, -1, A2, h, bct, bcA, bcB, G, sh, unit, &vmid);
+}
+
+// Workgroup: 2 NP waves on one (batch, channel group) tile of one pair, wave w on direction w & 1
+// and state part w >> 1.  Two pairs (argument sets) per launch, the first set's tiles first.
+template <typename T, int NP>
+__global__ __launch_bounds__(2 * kW * NP) void walk_pair_kernel(ScanArgs a0, ScanArgs a1) {
+  __shared__ WalkShared<NP> sh;
+  const int nb = a0.batch * a0.ngroups, bid = static_cast<int>(blockIdx.x);
+  const bool first = bid < nb;
+  const ScanArgs* ap = first ? &a0 : &a1;
+  const ScanArgs& a = *ap;
+  const Lane l = lane_at(a, logical_block(first ? bid : bid - nb, nb));
+  if (threadIdx.x < 2 * NP) sh.prod[threadIdx.x / NP][threadIdx.x % NP] = 0;
+  if (threadIdx.x < 2) sh.cons[threadIdx.x] = 0;
+  __syncthreads();
+  if ((__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6) & 1) == 0) walk_dir<T, 0, NP>(a, l, sh);
+  else walk_dir<T, 1, NP>(a, l, sh);
+}
+
+// Cross-merge of the two pairs' sums: out[b][d][h][w] = (R[h W + w] + C[w H + h]) (times
+// silu(z)), with R (row pair, row-major positions) and C (column pair, column-major positions)
+// the walk's [batch][group][position][64] float32 rows.  A workgroup takes 64 pixels of one
+// (batch, channel group): it reads the 64 x 64 sums pixel by pixel (256-byte lines), turns them
+// channel-major through LDS and stores each channel's 64 pixels contiguously.
+template <typename T>
+__global__ __launch_bounds__(256) void walk_merge_kernel(const float* __restrict__ R, const float* __restrict__ Cs,
+                                                         const T* __restrict__ z, T* __restrict__ out, int dim, int H,
+                                                         int W, int ngroups) {
+  __shared__ float tile[64][kW + 1];
+  const int L = H * W;
+  const int nblk = (L + 63) / 64;
+  const int64_t blk = blockIdx.x;
+  const int pb = static_cast<int>(blk % nblk);
+  const int64_t bg = blk / nblk;  // b * ngroups + g
+  const int g = static_cast<int>(bg % ngroups);
+  const int64_t b = bg / ngroups;
+  const int p0 = pb * 64;
+  const float* Rt = R + bg * L * kW;
+  const float* Ct = Cs + bg * L * kW;
+  {
+    const int k = threadIdx.x >> 2, cq = (threadIdx.x & 3) * 16;  // pixel, 16 channels
+    const int p = p0 + k;
+    if (p < L) {
+      const int hh = p / W, ww = p - hh * W;
+      const float4* rr = reinterpret_cast<const float4*>(Rt + static_cast<int64_t>(p) * kW + cq);
+      const float4* cc = reinterpret_cast<const float4*>(Ct + (static_cast<int64_t>(ww) * H + hh) * kW + cq);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 a = rr[q], c = cc[q];
+        tile[k][cq + 4 * q] = a.x + c.x;
+        tile[k][cq + 4 * q + 1] = a.y + c.y;
+        tile[k][cq + 4 * q + 2] = a.z + c.z;
+        tile[k][cq + 4 * q + 3] = a.w + c.w;
+      }
+    }
+  }
+  __syncthreads();
+  const int c = threadIdx.x >> 3, k0 = (threadIdx.x & 7) * kWin;  // channel (pass 1: 0-31), 8 pixels
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int cc = c + 32 * pass;
+    const int d = g * kW + cc;
+    if (d >= dim) break;
+    const int64_t e0 = (b * dim + d) * L + p0 + k0;  // first element of the run
+    float v[kWin];
+#pragma unroll
+    for (int j = 0; j < kWin; ++j) v[j] = tile[k0 + j][cc];
+    if (p0 + k0 + kWin <= L && (e0 & 7) == 0) {
+      // a whole run of 8 starting at a multiple of 8 elements: 16-byte (bf16) / 32-byte accesses
+      if (z) {
+        Run8<T> zr;
+        float zz[kWin];
+        zr.load(z + e0);
+        zr.template unpack<false>(zz);
+#pragma unroll
+        for (int j = 0; j < kWin; ++j) v[j] *= silu_f(zz[j]);
+      }
+      store8(out + e0, v);
+    } else {
+      for (int j = 0; j < kWin && p0 + k0 + j < L; ++j) {
+        float w = v[j];
+        if (z) w *= silu_f(ld_act(z, e0 + j));
+        st_act(out, e0 + j, w);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // Front convolutions: the local mixing that produces the scan input.  Both are streaming kernels
 // bound by HBM: the scans are bound by the vector ALU, so recomputing the convolution and SiLU
 // in every wave of a scan would cost more issue slots than one pass over the activations, and the
@@ -1534,6 +1748,33 @@ Ss2dLayout ss2d_layout(int64_t batch, int64_t dim, int64_t L, int64_t K, size_t 
   w.bct = w.xt + round256(static_cast<size_t>(batch) * dim * L * esz);
   w.agg = w.bct + bct_bytes(batch, L, ns);
   w.total = w.agg + agg_bytes(batch, dim, L, K, ns);
+  return w;
+}
+
+// SS2D whole-sequence walk (walk_pair_kernel): chosen for sequences longer than an LDS row when
+// the (batch, channel-group) tiles of both pairs give at least two waves per SIMD
+// (kWalkTiles four-wave units), or forced by a chunk length of at least the sequence.
+constexpr int64_t kWalkTiles = 256;
+bool ss2d_walk(int64_t batch, int64_t dim, int64_t L, int ns, int64_t chunk_len) {
+  if (chunk_len > 0) return chunk_len >= L;
+  return L > kKMax && batch * groups(dim) * (ns / kN) >= kWalkTiles;
+}
+
+// Walk workspace: the two pairs' float32 rows [batch][group][L][64], the transposed x, and each
+// pair's B/C copy.
+struct Ss2dWalkLayout {
+  size_t rows_r, rows_c, xt, bct_r, bct_c, total;
+};
+
+Ss2dWalkLayout ss2d_walk_layout(int64_t batch, int64_t dim, int64_t L, size_t esz, int ns) {
+  Ss2dWalkLayout w{};
+  const size_t rows = round256(static_cast<size_t>(batch) * groups(dim) * kW * L * sizeof(float));
+  w.rows_r = 0;
+  w.rows_c = rows;
+  w.xt = 2 * rows;
+  w.bct_r = w.xt + round256(static_cast<size_t>(batch) * dim * L * esz);
+  w.bct_c = w.bct_r + bct_bytes(batch, L, ns);
+  w.total = w.bct_c + bct_bytes(batch, L, ns);
   return w;
 }
 
@@ -2884,6 +3125,8 @@ size_t ss2d_cross_scan_workspace_bytes_ex(int64_t batch, int64_t dim, int64_t H,
   if (!shape_ok(batch, dim, L) || !d_state_ok(d_state) || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16) ||
       chunk_len < 0)
     return 0;
+  if (ss2d_walk(batch, dim, L, d_state, chunk_len))
+    return ss2d_walk_layout(batch, dim, L, dtype == VMSCAN_F32 ? 4 : 2, d_state).total;
   const int64_t K = plan_chunk(plan_base(batch, dim, d_state), L, chunk_len);
   return ss2d_layout(batch, dim, L, K, dtype == VMSCAN_F32 ? 4 : 2, d_state).total;
 }
@@ -2894,6 +3137,78 @@ size_t ss2d_cross_scan_workspace_bytes(int64_t batch, int64_t dim, int64_t H, in
 }
 
 namespace {
+
+// The SS2D forward as two whole-sequence pair walks (column pair over x^T, row pair over x) in one
+// launch, then the cross-merge; arguments already validated.
+vmscan_status ss2d_walk_fwd(const void* x, const void* xT, const void* delta_raw, const float* A_log, const void* B,
+                            const void* C, const float* D, const float* delta_bias, const void* z, void* out,
+                            int64_t batch, int64_t dim, int64_t H, int64_t W, int ns, vmscan_dtype dtype,
+                            void* workspace, hipStream_t stream) {
+  const int64_t L = H * W;
+  const size_t esz = dtype == VMSCAN_F32 ? 4 : 2;
+  const Ss2dWalkLayout lay = ss2d_walk_layout(batch, dim, L, esz, ns);
+  unsigned char* wsp = static_cast<unsigned char*>(workspace);
+  const int64_t ngr = groups(dim);
+  const int64_t nb = batch * ngr;
+  const int64_t tblocks = batch * 2 * ceil_div(L, kTransThreads);
+  const int64_t mblocks = nb * ceil_div(L, 64);
+  if (2 * nb >= (int64_t{1} << 31) || tblocks >= (int64_t{1} << 31) || mblocks >= (int64_t{1} << 31))
+    return VMSCAN_ERR_SHAPE;
+  vmscan_status st = VMSCAN_OK;
+  if (!xT) {
+    st = launch_transpose(x, wsp + lay.xt, batch * dim, static_cast<int>(H), static_cast<int>(W), esz, stream);
+    if (st != VMSCAN_OK) return st;
+    xT = wsp + lay.xt;
+  }
+  auto off = [&](const void* p, int64_t elems) {
+    return static_cast<const void*>(static_cast<const unsigned char*>(p) + elems * static_cast<int64_t>(esz));
+  };
+  auto dir_args = [&](const void* u, int k, int rev) {
+    return DirArgs{u, off(delta_raw, k * dim * L), 4 * dim * L, off(B, k * ns * L), off(C, k * ns * L), 4 * ns * L,
+                   A_log + k * dim * ns, D + k * dim, delta_bias + k * dim, rev};
+  };
+  ScanArgs a[2] = {};
+  for (int k = 0; k < 2; ++k) {  // 0: column pair (directions 1, 3) over x^T; 1: row pair (0, 2) over x
+    ScanArgs& s = a[k];
+    s.ns = ns;
+    s.parts = ns / kH;
+    s.u_bs = dim * L;
+    s.L = L;
+    s.dim = static_cast<int>(dim);
+    s.batch = static_cast<int>(batch);
+    s.K = static_cast<int>(L);
+    s.nch = 1;
+    s.ngroups = static_cast<int>(ngr);
+    s.wsy = reinterpret_cast<float*>(wsp + (k == 0 ? lay.rows_c : lay.rows_r));
+    s.bct = reinterpret_cast<float*>(wsp + (k == 0 ? lay.bct_c : lay.bct_r));
+    s.d0 = k == 0 ? dir_args(xT, 1, 0) : dir_args(x, 0, 0);
+    s.d1 = k == 0 ? dir_args(xT, 3, 1) : dir_args(x, 2, 1);
+    if (dtype == VMSCAN_F32)
+      hipLaunchKernelGGL(bc_transpose_kernel<float>, dim3(static_cast<unsigned>(tblocks)), dim3(kTransThreads), 0,
+                         stream, s);
+    else
+      hipLaunchKernelGGL(bc_transpose_kernel<uint16_t>, dim3(static_cast<unsigned>(tblocks)), dim3(kTransThreads), 0,
+                         stream, s);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return launch_failed(e);
+  }
+  const dim3 grid(static_cast<unsigned>(2 * nb));
+  if (dtype == VMSCAN_F32) {
+    if (ns == 16) hipLaunchKernelGGL((walk_pair_kernel<float, 2>), grid, dim3(2 * kW * 2), 0, stream, a[0], a[1]);
+    else hipLaunchKernelGGL((walk_pair_kernel<float, 4>), grid, dim3(2 * kW * 4), 0, stream, a[0], a[1]);
+    hipLaunchKernelGGL(walk_merge_kernel<float>, dim3(static_cast<unsigned>(mblocks)), dim3(256), 0, stream,
+                       a[1].wsy, a[0].wsy, static_cast<const float*>(z), static_cast<float*>(out),
+                       static_cast<int>(dim), static_cast<int>(H), static_cast<int>(W), static_cast<int>(ngr));
+  } else {
+    if (ns == 16) hipLaunchKernelGGL((walk_pair_kernel<uint16_t, 2>), grid, dim3(2 * kW * 2), 0, stream, a[0], a[1]);
+    else hipLaunchKernelGGL((walk_pair_kernel<uint16_t, 4>), grid, dim3(2 * kW * 4), 0, stream, a[0], a[1]);
+    hipLaunchKernelGGL(walk_merge_kernel<uint16_t>, dim3(static_cast<unsigned>(mblocks)), dim3(256), 0, stream,
+                       a[1].wsy, a[0].wsy, static_cast<const uint16_t*>(z), static_cast<uint16_t*>(out),
+                       static_cast<int>(dim), static_cast<int>(H), static_cast<int>(W), static_cast<int>(ngr));
+  }
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? VMSCAN_OK : launch_failed(e);
+}
 
 // The SS2D forward with x's transposed copy either made here (xT NULL) or given by the caller.
 vmscan_status ss2d_fwd_impl(const void* x, const void* xT, const void* delta_raw, const float* A_log, const void* B,
@@ -2915,8 +3230,11 @@ vmscan_status ss2d_fwd_impl(const void* x, const void* xT, const void* delta_raw
   if (ws != VMSCAN_OK) return ws;
 
   const int ns = d_state;
-  const int64_t K = plan_chunk(plan_base(batch, dim, ns), L, chunk_len);
   const size_t esz = dtype == VMSCAN_F32 ? 4 : 2;
+  if (ss2d_walk(batch, dim, L, ns, chunk_len))
+    return ss2d_walk_fwd(x, xT, delta_raw, A_log, B, C, D, delta_bias, z, out, batch, dim, H, W, ns, dtype, workspace,
+                         stream);
+  const int64_t K = plan_chunk(plan_base(batch, dim, ns), L, chunk_len);
   const Ss2dLayout lay = ss2d_layout(batch, dim, L, K, esz, ns);
   unsigned char* wsp = static_cast<unsigned char*>(workspace);
 

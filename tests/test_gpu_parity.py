@@ -280,3 +280,44 @@ def test_vim_very_long_sequence():
     a long chain (float32, tight tolerance)."""
     p = synth.make_vim_inputs(0, layer=990, batch=1, dim=64, seqlen=70001, dtype="f32")
     _report("vim L=70001", O.rel_err(run_vim(p), oracle_vim(p)), 1e-5)
+
+
+# The SS2D forward walking each sequence whole (the library's choice for long sequences with many
+# (batch, channel-group) tiles, forced here by a chunk length of H*W): pair rows in float32
+# workspace rows, parts combined through an LDS ring, odd middle token, the cross-merge kernel.
+WALK_SHAPES = [(1, 16, 1, 1), (2, 5, 1, 7), (1, 17, 7, 1), (2, 16, 3, 4), (1, 20, 7, 9), (1, 70, 16, 16),
+               (2, 3, 23, 19), (1, 4, 67, 70)]
+
+
+@pytest.mark.parametrize("gated", [False, True])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", WALK_SHAPES, ids=[f"b{b}d{d}h{h}w{w}" for b, d, h, w in WALK_SHAPES])
+def test_ss2d_walk(shape, dtype, gated):
+    nb, nd, H, W = shape
+    p = synth.make_ss2d_inputs(4, layer=3300 + H * 31 + W, batch=nb, dim=nd, H=H, W=W, dtype=dtype, with_z=gated,
+                               params="indep")
+    _report(f"ss2d walk {shape} {dtype} gated={gated}", O.rel_err(run_ss2d(p, chunk_len=H * W), oracle_ss2d(p)),
+            TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(1, 16, 1, 1), (2, 5, 3, 7), (1, 70, 9, 11)], ids=str)
+def test_ss2d_walk_d_state32(shape, dtype):
+    nb, nd, H, W = shape
+    p = synth.make_ss2d_inputs(4, layer=3400 + H * 31 + W, batch=nb, dim=nd, H=H, W=W, d_state=32, dtype=dtype,
+                               with_z=True, params="indep")
+    _report(f"ss2d walk N=32 {shape} {dtype}", O.rel_err(run_ss2d(p, chunk_len=H * W), oracle_ss2d(p)), TOL[dtype])
+
+
+def test_ss2d_walk_deterministic():
+    """Bit-identical results run to run (the part and direction sums are added in a fixed order)."""
+    p = synth.make_ss2d_inputs(4, layer=3500, batch=2, dim=70, H=13, W=17, dtype="bf16", with_z=True)
+    assert np.array_equal(run_ss2d(p, chunk_len=13 * 17), run_ss2d(p, chunk_len=13 * 17))
+
+
+def test_ss2d_walk_is_default_for_config4():
+    import selective_state_space_41_amd as V
+    lib = V.load()
+    walk = lib.ss2d_cross_scan_workspace_bytes_ex(32, 512, 56, 56, 16, 1, 56 * 56)
+    assert lib.ss2d_cross_scan_workspace_bytes(32, 512, 56, 56, 16, 1) == walk
+    assert lib.ss2d_cross_scan_workspace_bytes_ex(32, 512, 56, 56, 16, 1, 150) != walk
