@@ -42,6 +42,13 @@
  *   - Workspace: caller-provided device scratch of at least the queried size.  When the query
  *     returns 0 none is needed and `workspace` may be NULL (if given, it must still be 16-byte
  *     aligned).  Its contents on entry are ignored.
+ *   - Wait status: the waves that hold different state parts of one direction wait for each other
+ *     through LDS counters.  Every such wait ends by construction; it is also bounded, and a wait
+ *     that runs out of its bound stores 1 into the first int32 of the workspace (the call's status
+ *     word, which the call's first kernel sets to 0).  So after the call's kernels have finished,
+ *     that word reads 0 unless the results are unspecified.  A library built with
+ *     -DVMSCAN_CHECK_WAITS checks the word itself: each scan entry point then waits for its kernels
+ *     and returns VMSCAN_ERR_WAIT if it is set.  (A stage-2-only call leaves the word of its stage 1.)
  */
 #ifndef VMSCAN_H
 #define VMSCAN_H
@@ -62,7 +69,8 @@ typedef enum {
   VMSCAN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                              */
   VMSCAN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the queried size               */
   VMSCAN_ERR_HIP = 6,         /* a HIP call failed; see vmscan_last_hip_error()                */
-  VMSCAN_ERR_SCRATCH = 7      /* the call needs more than VMSCAN_SCRATCH_BYTES (no-alloc entry) */
+  VMSCAN_ERR_SCRATCH = 7,     /* the call needs more than VMSCAN_SCRATCH_BYTES (no-alloc entry) */
+  VMSCAN_ERR_WAIT = 8         /* a bounded wait gave up (builds with VMSCAN_CHECK_WAITS only)   */
 } vmscan_status;
 
 typedef enum { VMSCAN_F32 = 0, VMSCAN_BF16 = 1 } vmscan_dtype;

@@ -228,6 +228,10 @@ struct ScanArgs {
   const void* dout;
   float* gout;
   void* dzout;
+  // The call's wait status word (the first word of the workspace): set to 1 by a wave whose bounded
+  // wait for another state part gave up; cleared by the call's first B/C copy (werr_clear).
+  int* werr;
+  int werr_clear;
 };
 
 // kModeVimSum: Vim order, but the epilogue turns the un-gated sum y_f + y_b into the gate's
@@ -248,6 +252,7 @@ __global__ __launch_bounds__(kTransThreads) void bc_transpose_kernel(ScanArgs a)
   const int dir = static_cast<int>((blk / ntile) & 1);
   const int b = static_cast<int>(blk / (2 * ntile));
   const int64_t s = tile * kTransThreads + threadIdx.x;
+  if (a.werr_clear && blk == 0 && threadIdx.x == 0) *a.werr = 0;  // the call's first kernel with the word
   if (s >= a.L) return;
   const DirArgs& da = dir == 0 ? a.d0 : a.d1;
   const int64_t si = da.rev ? a.L - 1 - s : s;
@@ -572,18 +577,23 @@ __device__ __forceinline__ float single_step(const ScanArgs& a, const Lane& l, c
 // LDS operations execute in issue order, so the data writes are complete when the flag write is,
 // and the compiler barriers keep the instructions in that order.  Part 0 never waits and each
 // wait is on a lower part, so every wait ends; the bound only keeps a mistake from turning into
-// a hang.
+// a hang, and a wait that gives up sets the call's status word (a vector store) so that the
+// mistake is reported instead of returning silently wrong results.
 __device__ __forceinline__ void unit_signal(int* flag, int unit) {
   asm volatile("" ::: "memory");
   __hip_atomic_store(flag, unit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-__device__ __forceinline__ void unit_wait(int* flag, int unit) {
+__device__ __forceinline__ void unit_wait(int* flag, int unit, int* werr) {
   for (int n = 0; n < (1 << 22); ++n) {
-    if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) >= unit)
-      break;
+    if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) >= unit) {
+      asm volatile("" ::: "memory");
+      return;
+    }
     __builtin_amdgcn_s_sleep(1);
   }
+  // The wait gave up: the results of this call are unspecified.  Say so in the status word.
+  if (werr) *werr = 1;
   asm volatile("" ::: "memory");
 }
 
@@ -642,7 +652,7 @@ __device__ __forceinline__ void chunk_state_dir(const ScanArgs& a, const Lane& l
     unit_signal(&xc.prod[DIR][me], w + 1);
 #pragma unroll
     for (int q = 0; q < NP; ++q)
-      if (q != me) unit_wait(&xc.prod[DIR][q], w + 1);
+      if (q != me) unit_wait(&xc.prod[DIR][q], w + 1, a.werr);
 #pragma unroll
     for (int q = 0; q < NP; ++q) {
       if (q == me) continue;
@@ -812,7 +822,7 @@ __device__ __forceinline__ void run_phase(const ScanArgs& a, const Lane& l, cons
         for (int j = 0; j < kWin; ++j) r[j] = myY[p0 + kStep * j];
       }
     } else if (pp >= 0) {
-      unit_wait(wait_flag, unit);
+      unit_wait(wait_flag, unit, a.werr);
 #pragma unroll
       for (int j = 0; j < kWin; ++j) r[j] = myY[pp + kStep * j];
     }
@@ -838,7 +848,7 @@ __device__ __forceinline__ void run_phase(const ScanArgs& a, const Lane& l, cons
     }
   }
   if (!lo && pp >= 0) {
-    unit_wait(wait_flag, unit);
+    unit_wait(wait_flag, unit, a.werr);
 #pragma unroll
     for (int j = 0; j < kWin; ++j) myY[pp + kStep * j] += yp[j];
     if (relay) unit_signal(own_flag, unit);
@@ -855,7 +865,7 @@ __device__ __forceinline__ void run_phase(const ScanArgs& a, const Lane& l, cons
       lds_first<PHASE>(myY + pos, v);
       unit_signal(own_flag, unit);
     } else {
-      unit_wait(wait_flag, unit);
+      unit_wait(wait_flag, unit, a.werr);
       myY[pos] += v;
       if (relay) unit_signal(own_flag, unit);
     }
@@ -1120,16 +1130,16 @@ struct WalkShared {
 template <int DIR, int PHASE, int NP, int LEN>
 __device__ __forceinline__ void walk_combine(WalkShared<NP>& sh, const Lane& l, int unit, const float (&y)[LEN],
                                              const float (&r)[LEN], float* G, int64_t p0, int kStep, int keep,
-                                             float* vkeep) {
+                                             float* vkeep, int* werr) {
   float* slot = &sh.ring[DIR][unit % kRing][0][0];
   if (l.part == 0) {
-    unit_wait(&sh.cons[DIR], unit - kRing + 1);  // the last part is done with this slot's previous use
+    unit_wait(&sh.cons[DIR], unit - kRing + 1, werr);  // the last part is done with this slot's previous use
 #pragma unroll
     for (int j = 0; j < LEN; ++j) slot[j * kW + l.lane] = y[j];
     unit_signal(&sh.prod[DIR][0], unit + 1);
     return;
   }
-  unit_wait(&sh.prod[DIR][l.part - 1], unit + 1);
+  unit_wait(&sh.prod[DIR][l.part - 1], unit + 1, werr);
   float v[LEN];
 #pragma unroll
   for (int j = 0; j < LEN; ++j) v[j] = slot[j * kW + l.lane] + y[j];
@@ -1175,7 +1185,7 @@ __device__ __forceinline__ void walk_phase(const ScanArgs& a, const Lane& l, con
     }
     prep_window(uu, xr, bias, Dh, dl, du, yi);
     run_steps<MODE, DIR>(l, i0, dl, du, yi, A2, h, bcA, bcB, bct, y);
-    walk_combine<DIR, PHASE, NP, kWin>(sh, l, unit, y, r, G, p0, kStep, -1, vkeep);
+    walk_combine<DIR, PHASE, NP, kWin>(sh, l, unit, y, r, G, p0, kStep, -1, vkeep, a.werr);
     ++unit;
   }
   for (int i = full_end; i < i_end; ++i) {
@@ -1183,7 +1193,7 @@ __device__ __forceinline__ void walk_phase(const ScanArgs& a, const Lane& l, con
     const int64_t pos = DIR == 0 ? i : l.Kc - 1 - i;
     if (PHASE == 1 && last) r[0] = G[pos * kW + l.lane];
     y[0] = single_step<T, MODE, DIR>(a, l, da, bias, Dh, i, A2, h, bct, bcA, &dl);
-    walk_combine<DIR, PHASE, NP, 1>(sh, l, unit, y, r, G, pos, kStep, i == keep_step ? 0 : -1, vkeep);
+    walk_combine<DIR, PHASE, NP, 1>(sh, l, unit, y, r, G, pos, kStep, i == keep_step ? 0 : -1, vkeep, a.werr);
     ++unit;
   }
 }
@@ -1657,6 +1667,10 @@ int64_t groups(int64_t dim) { return ceil_div(dim, kW); }
 
 size_t round256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// Every workspace starts with the call's wait status word (int32, 0 = every wait ended), padded
+// to 256 bytes; the scratch regions follow.
+constexpr size_t kStatusBytes = 256;
+
 // d_state values the forward kernels take: whole parts of 8 states, one wave per direction and part.
 bool d_state_ok(int d_state) { return d_state == 16 || d_state == 32; }
 
@@ -1684,6 +1698,25 @@ bool shape_ok(int64_t batch, int64_t dim, int64_t L) {
 vmscan_status launch_failed(hipError_t e) {
   g_last_hip_error = static_cast<int>(e);
   return VMSCAN_ERR_HIP;
+}
+
+// The end of an entry point.  In a build with VMSCAN_CHECK_WAITS the call waits for its kernels and
+// reads the workspace's status word, so that a wait between state parts that gave up is reported
+// as VMSCAN_ERR_WAIT; otherwise the word is left for the caller to read.
+vmscan_status finish_call(vmscan_status st, const void* workspace, hipStream_t stream) {
+#ifdef VMSCAN_CHECK_WAITS
+  if (st != VMSCAN_OK || !workspace) return st;
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return launch_failed(e);
+  int word = 0;
+  e = hipMemcpy(&word, workspace, sizeof(word), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return launch_failed(e);
+  return word ? VMSCAN_ERR_WAIT : VMSCAN_OK;
+#else
+  (void)workspace;
+  (void)stream;
+  return st;
+#endif
 }
 
 enum { kStagePrepare = 1, kStageScan = 2, kStageAll = 3 };
@@ -1742,9 +1775,9 @@ struct Ss2dLayout {
 Ss2dLayout ss2d_layout(int64_t batch, int64_t dim, int64_t L, int64_t K, size_t esz, int ns = kN) {
   Ss2dLayout w{};
   const size_t img = round256(static_cast<size_t>(batch) * dim * L * sizeof(float));
-  w.col_img = 0;
-  w.row_img = img;
-  w.xt = 2 * img;
+  w.col_img = kStatusBytes;
+  w.row_img = w.col_img + img;
+  w.xt = w.row_img + img;
   w.bct = w.xt + round256(static_cast<size_t>(batch) * dim * L * esz);
   w.agg = w.bct + bct_bytes(batch, L, ns);
   w.total = w.agg + agg_bytes(batch, dim, L, K, ns);
@@ -1769,9 +1802,9 @@ struct Ss2dWalkLayout {
 Ss2dWalkLayout ss2d_walk_layout(int64_t batch, int64_t dim, int64_t L, size_t esz, int ns) {
   Ss2dWalkLayout w{};
   const size_t rows = round256(static_cast<size_t>(batch) * groups(dim) * kW * L * sizeof(float));
-  w.rows_r = 0;
-  w.rows_c = rows;
-  w.xt = 2 * rows;
+  w.rows_r = kStatusBytes;
+  w.rows_c = w.rows_r + rows;
+  w.xt = w.rows_c + rows;
   w.bct_r = w.xt + round256(static_cast<size_t>(batch) * dim * L * esz);
   w.bct_c = w.bct_r + bct_bytes(batch, L, ns);
   w.total = w.bct_c + bct_bytes(batch, L, ns);
@@ -1818,14 +1851,16 @@ vmscan_status vim_args(ScanArgs& a, const void* u, const void* delta_raw, const 
   const int ns = d_state;
   const int64_t K = plan_chunk(plan_base(batch, dim, ns), seqlen, chunk_len);
   const vmscan_status ws = check_workspace(workspace, workspace_bytes,
-                                           bct_bytes(batch, seqlen, ns) + agg_bytes(batch, dim, seqlen, K, ns));
+                                           kStatusBytes + bct_bytes(batch, seqlen, ns) + agg_bytes(batch, dim, seqlen, K, ns));
   if (ws != VMSCAN_OK) return ws;
   a.u_bs = dim * seqlen;
   a.z = z;
   a.out = out;
   a.wsy = nullptr;
-  a.bct = static_cast<float*>(workspace);
-  a.agg = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + bct_bytes(batch, seqlen, ns));
+  a.werr = static_cast<int*>(workspace);
+  a.werr_clear = 1;
+  a.bct = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + kStatusBytes);
+  a.agg = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + kStatusBytes + bct_bytes(batch, seqlen, ns));
   a.d0 = DirArgs{u, delta_raw, dim * seqlen, B, C, ns * seqlen, A_log, D, delta_bias, 0};
   a.d1 = DirArgs{u_b, delta_raw_b, dim * seqlen, B_b, C_b, ns * seqlen, A_b_log, D_b, delta_bias_b, 0};
   a.ns = ns;
@@ -2297,7 +2332,7 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
 #pragma unroll
       for (int j = j0; j < j0 + 4; ++j) asm volatile("" : "+v"(d2[j]));
       // the upper part's staging area is free once the lower part has read the previous window
-      if (hf == 1 && (l.part & 1)) unit_wait(&pf[1], nstaged);
+      if (hf == 1 && (l.part & 1)) unit_wait(&pf[1], nstaged, a.werr);
       float bc0[kBC], bc1[kBC];
       load_bc(bc_at(j0 + 3), bc1);
 #pragma unroll
@@ -2358,7 +2393,7 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
     // and its own dB/dC sums are written before it reads them.
     ++nstaged;
     if (l.part & 1) unit_signal(&pf[0], nstaged);
-    else unit_wait(&pf[0], nstaged);
+    else unit_wait(&pf[0], nstaged, a.werr);
     if ((l.part & 1) == 0 && l.valid) {
       const float* up = stage + 2 * kStageFloats;  // wave w + 2
       float v[kWin];
@@ -2616,7 +2651,7 @@ BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t L, int64_t Kf, int ns) 
   const size_t planes = round256(static_cast<size_t>(2) * (ns / kH / 2) * batch * dim * L * sizeof(float));
   const size_t plane = round256(static_cast<size_t>(batch) * dim * L * sizeof(float));
   const int64_t Kb = bwd_chunk(plan_base(batch, dim, ns), L, Kf);
-  w.bct = 0;
+  w.bct = kStatusBytes;  // after the status word, as in the forward's workspace
   w.agg = w.bct + bct_bytes(batch, L, ns);
   w.g = w.agg + agg_bytes(batch, dim, L, Kf, ns);
   w.ck = w.g + plane;
@@ -2703,6 +2738,7 @@ vmscan_status run_bwd(const ScanArgs& fwd, const BwdLayout& lay, unsigned char* 
   }
   vmscan_status st = run_pair<T, kModeVimSum>(a, stream, kStageAll);
   if (st != VMSCAN_OK) return st;
+  ba.s.werr_clear = 0;
   hipError_t e;
   st = launch_bwd_scans<T, kModeVim, 1>(ba, ba, stream);
   if (st != VMSCAN_OK) return st;
@@ -2834,6 +2870,8 @@ vmscan_status run_ss2d_bwd(const void* x, const void* delta_raw, const float* A_
   a.parts = ns / kH;
   a.u_bs = dim * L;
   a.z = nullptr;
+  a.werr = reinterpret_cast<int*>(wsp);
+  a.werr_clear = 1;  // the first B/C copy of the call clears the status word
   a.bct = reinterpret_cast<float*>(wsp + lay.f.bct);
   a.agg = reinterpret_cast<float*>(wsp + lay.f.agg);
   a.L = L;
@@ -2852,6 +2890,7 @@ vmscan_status run_ss2d_bwd(const void* x, const void* delta_raw, const float* A_
     a.d1 = dir_args(xt, 3, 1);
     st = run_pair<T, kModeFirstPair>(a, stream, kStageAll);
     if (st != VMSCAN_OK) return st;
+    a.werr_clear = 0;
     st = launch_transpose(wsp + lay.f.col_img, wsp + lay.f.row_img, nimg, static_cast<int>(W), static_cast<int>(H), 4,
                           stream);
     if (st != VMSCAN_OK) return st;
@@ -2897,6 +2936,7 @@ vmscan_status run_ss2d_bwd(const void* x, const void* delta_raw, const float* A_
     ba.s.d1 = k == 0 ? dir_args(xt, 3, 1) : dir_args(x, 2, 1);
     st = ss2d_pair_prepare<T>(ba, stream);
     if (st != VMSCAN_OK) return st;
+    a.werr_clear = 0;
   }
   st = launch_bwd_scans<T, kModeSecondPair, 2>(bp[0], bp[1], stream);
   if (st != VMSCAN_OK) return st;
@@ -2970,6 +3010,8 @@ const char* vmscan_status_string(vmscan_status s) {
     case VMSCAN_ERR_HIP: return "VMSCAN_ERR_HIP: a HIP call failed (see vmscan_last_hip_error)";
     case VMSCAN_ERR_SCRATCH:
       return "VMSCAN_ERR_SCRATCH: the call needs more workspace than the fixed scratch buffer (VMSCAN_SCRATCH_BYTES)";
+    case VMSCAN_ERR_WAIT:
+      return "VMSCAN_ERR_WAIT: a wait between the waves of a workgroup gave up; the results are unspecified";
   }
   return "VMSCAN_ERR_UNKNOWN";
 }
@@ -2987,7 +3029,7 @@ size_t vmscan_fwd_bidir_workspace_bytes_ex(int64_t batch, int64_t dim, int64_t s
       chunk_len < 0)
     return 0;
   const int64_t K = plan_chunk(plan_base(batch, dim, d_state), seqlen, chunk_len);
-  return bct_bytes(batch, seqlen, d_state) + agg_bytes(batch, dim, seqlen, K, d_state);
+  return kStatusBytes + bct_bytes(batch, seqlen, d_state) + agg_bytes(batch, dim, seqlen, K, d_state);
 }
 
 size_t vmscan_fwd_bidir_workspace_bytes(int64_t batch, int64_t dim, int64_t seqlen, int d_state,
@@ -3041,11 +3083,12 @@ vmscan_status vmscan_bwd_bidir_v2(const void* u, const void* delta_raw, const fl
   st = check_workspace(workspace, workspace_bytes, lay.total);
   if (st != VMSCAN_OK) return st;
   unsigned char* wsp = static_cast<unsigned char*>(workspace);
-  return dtype == VMSCAN_F32
-             ? run_bwd<float>(a, lay, wsp, dout, z, du, ddelta_raw, ddelta_bias, du_b, ddelta_raw_b, ddelta_bias_b, dz,
-                              A_log, A_b_log, dA_log, dA_b_log, dB, dC, dB_b, dC_b, dD, dD_b, stream)
-             : run_bwd<uint16_t>(a, lay, wsp, dout, z, du, ddelta_raw, ddelta_bias, du_b, ddelta_raw_b, ddelta_bias_b,
-                                 dz, A_log, A_b_log, dA_log, dA_b_log, dB, dC, dB_b, dC_b, dD, dD_b, stream);
+  st = dtype == VMSCAN_F32
+           ? run_bwd<float>(a, lay, wsp, dout, z, du, ddelta_raw, ddelta_bias, du_b, ddelta_raw_b, ddelta_bias_b, dz,
+                            A_log, A_b_log, dA_log, dA_b_log, dB, dC, dB_b, dC_b, dD, dD_b, stream)
+           : run_bwd<uint16_t>(a, lay, wsp, dout, z, du, ddelta_raw, ddelta_bias, du_b, ddelta_raw_b, ddelta_bias_b,
+                               dz, A_log, A_b_log, dA_log, dA_b_log, dB, dC, dB_b, dC_b, dD, dD_b, stream);
+  return finish_call(st, workspace, stream);
 }
 
 vmscan_status vmscan_fwd_bidir_v2_stage(const void* u, const void* delta_raw, const float* delta_bias, const void* u_b,
@@ -3061,7 +3104,7 @@ vmscan_status vmscan_fwd_bidir_v2_stage(const void* u, const void* delta_raw, co
       vim_args(a, u, delta_raw, delta_bias, u_b, delta_raw_b, delta_bias_b, z, A_log, A_b_log, B, C, B_b, C_b, D, D_b,
                out, batch, dim, seqlen, d_state, dtype, workspace, workspace_bytes, chunk_len);
   if (st != VMSCAN_OK) return st;
-  return run_pair_dtype<kModeVim>(a, dtype, stream, stage);
+  return finish_call(run_pair_dtype<kModeVim>(a, dtype, stream, stage), workspace, stream);
 }
 
 vmscan_status vmscan_fwd_bidir_v2(const void* u, const void* delta_raw, const float* delta_bias, const void* u_b,
@@ -3180,6 +3223,8 @@ vmscan_status ss2d_walk_fwd(const void* x, const void* xT, const void* delta_raw
     s.nch = 1;
     s.ngroups = static_cast<int>(ngr);
     s.wsy = reinterpret_cast<float*>(wsp + (k == 0 ? lay.rows_c : lay.rows_r));
+    s.werr = reinterpret_cast<int*>(wsp);
+    s.werr_clear = k == 0 ? 1 : 0;
     s.bct = reinterpret_cast<float*>(wsp + (k == 0 ? lay.bct_c : lay.bct_r));
     s.d0 = k == 0 ? dir_args(xT, 1, 0) : dir_args(x, 0, 0);
     s.d1 = k == 0 ? dir_args(xT, 3, 1) : dir_args(x, 2, 1);
@@ -3253,6 +3298,8 @@ vmscan_status ss2d_fwd_impl(const void* x, const void* xT, const void* delta_raw
   a.u_bs = dim * L;
   a.z = z;
   a.out = out;
+  a.werr = reinterpret_cast<int*>(wsp);
+  a.werr_clear = 1;  // the column pair's B/C copy runs first
   a.bct = reinterpret_cast<float*>(wsp + lay.bct);
   a.agg = reinterpret_cast<float*>(wsp + lay.agg);
   a.L = L;
@@ -3286,6 +3333,7 @@ vmscan_status ss2d_fwd_impl(const void* x, const void* xT, const void* delta_raw
   a.wsy = reinterpret_cast<float*>(wsp + lay.row_img);
   a.d0 = dir_args(x, 0, 0);
   a.d1 = dir_args(x, 2, 1);
+  a.werr_clear = 0;
   return run_pair_dtype<kModeSecondPair>(a, dtype, stream);
 }
 
@@ -3296,8 +3344,9 @@ vmscan_status ss2d_cross_scan_fwd_ex(const void* x, const void* delta_raw, const
                                      void* out, int64_t batch, int64_t dim, int64_t H, int64_t W, int d_state,
                                      vmscan_dtype dtype, void* workspace, size_t workspace_bytes,
                                      int64_t chunk_len, hipStream_t stream) {
-  return ss2d_fwd_impl(x, nullptr, delta_raw, A_log, B, C, D, delta_bias, z, out, batch, dim, H, W, d_state, dtype,
-                       workspace, workspace_bytes, chunk_len, stream);
+  return finish_call(ss2d_fwd_impl(x, nullptr, delta_raw, A_log, B, C, D, delta_bias, z, out, batch, dim, H, W,
+                                   d_state, dtype, workspace, workspace_bytes, chunk_len, stream),
+                     workspace, stream);
 }
 
 vmscan_status ss2d_cross_scan_fwd_xt(const void* x, const void* xT, const void* delta_raw, const float* A_log,
@@ -3306,8 +3355,9 @@ vmscan_status ss2d_cross_scan_fwd_xt(const void* x, const void* xT, const void* 
                                      int d_state, vmscan_dtype dtype, void* workspace, size_t workspace_bytes,
                                      int64_t chunk_len, hipStream_t stream) {
   if (!xT) return VMSCAN_ERR_NULL;
-  return ss2d_fwd_impl(x, xT, delta_raw, A_log, B, C, D, delta_bias, z, out, batch, dim, H, W, d_state, dtype,
-                       workspace, workspace_bytes, chunk_len, stream);
+  return finish_call(ss2d_fwd_impl(x, xT, delta_raw, A_log, B, C, D, delta_bias, z, out, batch, dim, H, W, d_state,
+                                   dtype, workspace, workspace_bytes, chunk_len, stream),
+                     workspace, stream);
 }
 
 vmscan_status vmscan_conv1d_silu_fwd(const void* x, const float* conv_w, const float* conv_b, const float* conv_w_b,
@@ -3412,11 +3462,13 @@ vmscan_status ss2d_cross_scan_bwd(const void* x, const void* delta_raw, const fl
   const vmscan_status ws = check_workspace(workspace, workspace_bytes, lay.total);
   if (ws != VMSCAN_OK) return ws;
   unsigned char* wsp = static_cast<unsigned char*>(workspace);
-  return dtype == VMSCAN_F32
-             ? run_ss2d_bwd<float>(x, delta_raw, A_log, B, C, D, delta_bias, z, dout, dx, ddelta_raw, dA_log, dB, dC,
-                                   dD, ddelta_bias, dz, batch, dim, H, W, d_state, wsp, lay, Kf, stream)
-             : run_ss2d_bwd<uint16_t>(x, delta_raw, A_log, B, C, D, delta_bias, z, dout, dx, ddelta_raw, dA_log, dB,
-                                      dC, dD, ddelta_bias, dz, batch, dim, H, W, d_state, wsp, lay, Kf, stream);
+  const vmscan_status st =
+      dtype == VMSCAN_F32
+          ? run_ss2d_bwd<float>(x, delta_raw, A_log, B, C, D, delta_bias, z, dout, dx, ddelta_raw, dA_log, dB, dC, dD,
+                                ddelta_bias, dz, batch, dim, H, W, d_state, wsp, lay, Kf, stream)
+          : run_ss2d_bwd<uint16_t>(x, delta_raw, A_log, B, C, D, delta_bias, z, dout, dx, ddelta_raw, dA_log, dB, dC,
+                                   dD, ddelta_bias, dz, batch, dim, H, W, d_state, wsp, lay, Kf, stream);
+  return finish_call(st, workspace, stream);
 }
 
 vmscan_status ss2d_cross_scan_fwd(const void* x, const void* delta_raw, const float* A_log, const void* B,

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "vmscan.h")
 LIB = os.path.join(ROOT, "selective_state_space_41_amd", "libvmscan.so")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP, ERR_SCRATCH = range(8)
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP, ERR_SCRATCH, ERR_WAIT = range(9)
 
 
 def declared_functions():
@@ -49,7 +49,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for s in range(8):
+    for s in range(9):
         txt = lib.vmscan_status_string(s).decode()
         assert txt.startswith("VMSCAN_")
     assert lib.vmscan_status_string(99).decode() == "VMSCAN_ERR_UNKNOWN"
@@ -58,6 +58,7 @@ def test_status_strings(lib):
 
 I64 = ctypes.c_int64
 VP = ctypes.c_void_p
+STATUS = 256  # every workspace starts with the 256-byte wait status region
 
 
 def _fwd(lib, ptrs, nb=2, nd=16, L=8, ds=16, dt=1, ws=None, wsb=0, chunk=0):
@@ -138,12 +139,13 @@ def agg_bytes(nb, nd, L, K, ns=16):
 
 
 def test_fwd_workspace(lib):
-    # the workspace holds the fp32 B/C copy and, for chunked plans, the chunk carries
+    # the workspace holds the wait status word, the fp32 B/C copy and, for chunked plans, the chunk carries
     need = lib.vmscan_fwd_bidir_workspace_bytes_ex(I64(2), I64(16), I64(100), 16, 1, I64(16))
-    assert need == bct_bytes(2, 100) + agg_bytes(2, 16, 100, 16)
-    assert lib.vmscan_fwd_bidir_workspace_bytes_ex(I64(2), I64(16), I64(100), 16, 1, I64(100)) == bct_bytes(2, 100)
+    assert need == STATUS + bct_bytes(2, 100) + agg_bytes(2, 16, 100, 16)
+    assert lib.vmscan_fwd_bidir_workspace_bytes_ex(I64(2), I64(16), I64(100), 16, 1, I64(100)) == \
+        STATUS + bct_bytes(2, 100)
     need32 = lib.vmscan_fwd_bidir_workspace_bytes_ex(I64(2), I64(16), I64(100), 32, 1, I64(16))
-    assert need32 == bct_bytes(2, 100, 32) + agg_bytes(2, 16, 100, 16, 32)
+    assert need32 == STATUS + bct_bytes(2, 100, 32) + agg_bytes(2, 16, 100, 16, 32)
     assert _fwd(lib, _good_ptrs(), L=100, chunk=16, ds=32, ws=0x80000, wsb=need32 - 1) == ERR_WORKSPACE
     assert _fwd(lib, _good_ptrs(), L=100, chunk=16, ds=32, ws=0x80008, wsb=need32) == ERR_ALIGN
     assert lib.vmscan_fwd_bidir_workspace_bytes_ex(I64(2), I64(16), I64(100), 24, 1, I64(16)) == 0
@@ -155,12 +157,12 @@ def test_fwd_workspace(lib):
 
 def test_workspace_queries(lib):
     assert lib.vmscan_fwd_bidir_chunk_len(I64(128), I64(384), I64(197), 16) == 197
-    assert lib.vmscan_fwd_bidir_workspace_bytes(I64(128), I64(384), I64(197), 16, 1) == bct_bytes(128, 197)
+    assert lib.vmscan_fwd_bidir_workspace_bytes(I64(128), I64(384), I64(197), 16, 1) == STATUS + bct_bytes(128, 197)
     assert lib.vmscan_fwd_bidir_workspace_bytes(I64(0), I64(384), I64(197), 16, 1) == 0
     K = lib.vmscan_fwd_bidir_chunk_len(I64(8), I64(384), I64(6085), 16)
     assert 32 <= K <= 206
     assert lib.vmscan_fwd_bidir_workspace_bytes(I64(8), I64(384), I64(6085), 16, 1) == \
-        bct_bytes(8, 6085) + agg_bytes(8, 384, 6085, K)
+        STATUS + bct_bytes(8, 6085) + agg_bytes(8, 384, 6085, K)
     # split plans use LDS rows of at most 159 floats, so that four workgroups fit one CU's 160 KiB
     for nb, nd, L in [(8, 384, 6085), (32, 512, 3136), (1, 384, 197), (2, 64, 1000), (4, 768, 4097), (16, 384, 207)]:
         K = lib.vmscan_fwd_bidir_chunk_len(I64(nb), I64(nd), I64(L), 16)
