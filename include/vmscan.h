@@ -299,9 +299,9 @@ size_t ss2d_cross_scan_workspace_bytes_ex(int64_t batch, int64_t dim, int64_t H,
  * H*W must be < 2^31.  Sequences are either cut into chunks of at most 206 positions (an LDS row),
  * whose entering states come from a chunk pass and a carry prefix, or walked whole, each pair's
  * two directions meeting in float32 rows in the workspace that a merge kernel then sums per
- * pixel.  The library walks whole when H*W > 206 and batch * ceil(dim / 64) * (d_state / 16) >=
- * 256 (enough (batch, channel-group) tiles to fill the GPU without chunks); chunk_len >= H*W
- * asks for the whole walk, 0 < chunk_len < H*W for chunks of that length (at most 206).
+ * pixel.  The library walks whole when H*W > 206 and batch * ceil(dim / 64) >= 256 (enough
+ * (batch, channel-group) tiles to fill the GPU without chunks); chunk_len >= H*W asks for the
+ * whole walk, 0 < chunk_len < H*W for chunks of that length (at most 206).
  */
 vmscan_status ss2d_cross_scan_fwd(const void *x, const void *delta_raw, const float *A_log,
                                   const void *B, const void *C, const float *D,

@@ -244,7 +244,7 @@ enum { kModeVim = 0, kModeFirstPair = 1, kModeSecondPair = 2, kModeVimSum = 3, k
 // B/C transpose: for state part q, bct[b][dir][q][s][0..7] = B_dir[b][8q + 0..7, si(s)] ln 2 and
 // bct[b][dir][q][s][8..15] = C_dir[b][8q + 0..7, si(s)].
 
-template <typename T>
+template <typename T, int KH = kH>
 __global__ __launch_bounds__(kTransThreads) void bc_transpose_kernel(ScanArgs a) {
   const int64_t ntile = (a.L + kTransThreads - 1) / kTransThreads;
   const int64_t blk = blockIdx.x;
@@ -258,16 +258,17 @@ __global__ __launch_bounds__(kTransThreads) void bc_transpose_kernel(ScanArgs a)
   const int64_t si = da.rev ? a.L - 1 - s : s;
   const T* bb = static_cast<const T*>(da.B) + static_cast<int64_t>(b) * da.bc_bs + si;
   const T* cb = static_cast<const T*>(da.C) + static_cast<int64_t>(b) * da.bc_bs + si;
+  constexpr int NB = 2 * KH;
   for (int q = 0; q < a.parts; ++q) {
-    float v[kBC];
+    float v[NB];
 #pragma unroll
-    for (int k = 0; k < kH; ++k) {
-      v[k] = ld_act(bb, static_cast<int64_t>(kH * q + k) * a.L) * kLn2;  // B ln 2: Δ2 u (B ln 2) = Δ u B
-      v[kH + k] = ld_act(cb, static_cast<int64_t>(kH * q + k) * a.L);
+    for (int k = 0; k < KH; ++k) {
+      v[k] = ld_act(bb, static_cast<int64_t>(KH * q + k) * a.L) * kLn2;  // B ln 2: Δ2 u (B ln 2) = Δ u B
+      v[KH + k] = ld_act(cb, static_cast<int64_t>(KH * q + k) * a.L);
     }
-    float4* dst = reinterpret_cast<float4*>(a.bct + (((static_cast<int64_t>(b) * 2 + dir) * a.parts + q) * a.L + s) * kBC);
+    float4* dst = reinterpret_cast<float4*>(a.bct + (((static_cast<int64_t>(b) * 2 + dir) * a.parts + q) * a.L + s) * NB);
 #pragma unroll
-    for (int k = 0; k < kBC / 4; ++k) dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+    for (int k = 0; k < NB / 4; ++k) dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
   }
 }
 
@@ -474,47 +475,52 @@ struct Window {
   }
 };
 
-// A = -exp(A_log) for the wave's 8 states (the decay of a step is exp2(Δ2 A)); ns = d_state.
-__device__ __forceinline__ void load_a2(const DirArgs& da, const Lane& l, int ns, float (&A2)[kH]) {
+// A = -exp(A_log) for the wave's KH states (the decay of a step is exp2(Δ2 A)); ns = d_state.
+template <int KH>
+__device__ __forceinline__ void load_a2(const DirArgs& da, const Lane& l, int ns, float (&A2)[KH]) {
 #pragma unroll
-  for (int k = 0; k < kH; ++k) A2[k] = -expf(da.A_log[static_cast<int64_t>(l.dd) * ns + kH * l.part + k]);
+  for (int k = 0; k < KH; ++k) A2[k] = -expf(da.A_log[static_cast<int64_t>(l.dd) * ns + KH * l.part + k]);
 }
 
-// B/C of one position for the wave's state part: 8 + 8 wave-uniform floats (one s_load_dwordx16).
-__device__ __forceinline__ void load_bc(scalar_fp p, float (&bc)[kBC]) {
+// B/C of one position for the wave's state part: KH + KH wave-uniform floats (one s_load_dwordx16
+// for 8 states, s_load_dwordx8 for 4).
+template <int NB>
+__device__ __forceinline__ void load_bc(scalar_fp p, float (&bc)[NB]) {
 #pragma unroll
-  for (int q = 0; q < kBC; ++q) bc[q] = p[q];
+  for (int q = 0; q < NB; ++q) bc[q] = p[q];
 }
 
-// The wave's row of the B/C copy.
-template <int DIR>
+// The wave's row of the B/C copy (2 KH floats per position and part of KH states).
+template <int DIR, int KH = kH>
 __device__ __forceinline__ scalar_fp bc_row(const ScanArgs& a, const Lane& l) {
-  return (scalar_fp)(a.bct) + (((static_cast<int64_t>(l.b) * 2 + DIR) * a.parts + l.part) * a.L) * kBC;
+  return (scalar_fp)(a.bct) + (((static_cast<int64_t>(l.b) * 2 + DIR) * a.parts + l.part) * a.L) * (2 * KH);
 }
 
-// One token for the wave's 8 states, h = exp2(Δ2 A) h + (Δ2 u)(B ln 2); returns yi + Σ C h.  Scalar
-// loads may return out of order, so any wait for one covers every scalar load in flight: the token
-// first waits for its own B/C (requested a token ago), then requests the next token's (nxt), which
-// so has this whole token's work to arrive before the next token waits for it.  32 SGPRs hold B/C.
-__device__ __forceinline__ float scan_token(float dl, float du, float yi, const float (&A2)[kH], float (&h)[kH],
-                                           const float (&cur)[kBC], float (&nxt)[kBC], scalar_fp nxt_p) {
+// One token for the wave's KH states, h = exp2(Δ2 A) h + (Δ2 u)(B ln 2); returns yi + Σ C h.
+// Scalar loads may return out of order, so any wait for one covers every scalar load in flight: the
+// token first waits for its own B/C (requested a token ago), then requests the next token's (nxt),
+// which so has this whole token's work to arrive before the next token waits for it.  4 KH SGPRs
+// hold B/C.
+template <int KH>
+__device__ __forceinline__ float scan_token(float dl, float du, float yi, const float (&A2)[KH], float (&h)[KH],
+                                           const float (&cur)[2 * KH], float (&nxt)[2 * KH], scalar_fp nxt_p) {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited for
   __builtin_amdgcn_sched_barrier(0);
   load_bc(nxt_p, nxt);
   __builtin_amdgcn_sched_barrier(0);
-  float an[kH];
+  float an[KH];
 #pragma unroll
-  for (int n = 0; n < kH; ++n) an[n] = __builtin_amdgcn_exp2f(dl * A2[n]);
+  for (int n = 0; n < KH; ++n) an[n] = __builtin_amdgcn_exp2f(dl * A2[n]);
 #pragma unroll
-  for (int n = 0; n < kH; ++n) {
+  for (int n = 0; n < KH; ++n) {
     h[n] = h[n] * an[n];
     h[n] = __builtin_fmaf(du, cur[n], h[n]);
   }
   float y0 = yi, y1 = 0.0f;
 #pragma unroll
-  for (int n = 0; n < kH; n += 2) {
-    y0 = __builtin_fmaf(cur[kH + n], h[n], y0);
-    y1 = __builtin_fmaf(cur[kH + n + 1], h[n + 1], y1);
+  for (int n = 0; n < KH; n += 2) {
+    y0 = __builtin_fmaf(cur[KH + n], h[n], y0);
+    y1 = __builtin_fmaf(cur[KH + n + 1], h[n + 1], y1);
   }
   return y0 + y1;
 }
@@ -523,19 +529,21 @@ __device__ __forceinline__ float scan_token(float dl, float du, float yi, const 
 // holds the B/C of step i0 + kWin.  The buffers alternate between the steps, so no register
 // copies are needed.  The one-past-the-end prefetch of a row's last step stays inside the B/C
 // copy: forward rows are followed by another row, and backward rows follow another row.
-template <int MODE, int DIR>
+template <int MODE, int DIR, int KH>
 __device__ __forceinline__ void run_steps(const Lane& l, int i0, const float (&dl)[kWin], const float (&du)[kWin],
-                                          const float (&yi)[kWin], const float (&A2)[kH], float (&h)[kH],
-                                          float (&bcA)[kBC], float (&bcB)[kBC], scalar_fp bct, float (&y)[kWin]) {
+                                          const float (&yi)[kWin], const float (&A2)[KH], float (&h)[KH],
+                                          float (&bcA)[2 * KH], float (&bcB)[2 * KH], scalar_fp bct,
+                                          float (&y)[kWin]) {
   using Dr = Dir<MODE, DIR>;
+  constexpr int NB = 2 * KH;  // B/C floats per position
   // Address of step i0 + k as a window base plus an immediate offset.
   const int64_t p0 = Dr::pos(l, i0);
-  scalar_fp base = DIR == 0 ? bct + p0 * kBC : bct + (p0 - kWin) * kBC;
+  scalar_fp base = DIR == 0 ? bct + p0 * NB : bct + (p0 - kWin) * NB;
 #pragma unroll
   for (int j = 0; j < kWin; j += 2) {
-    y[j] = scan_token(dl[j], du[j], yi[j], A2, h, bcA, bcB, base + (DIR == 0 ? j + 1 : kWin - j - 1) * kBC);
+    y[j] = scan_token(dl[j], du[j], yi[j], A2, h, bcA, bcB, base + (DIR == 0 ? j + 1 : kWin - j - 1) * NB);
     y[j + 1] = scan_token(dl[j + 1], du[j + 1], yi[j + 1], A2, h, bcB, bcA,
-                          base + (DIR == 0 ? j + 2 : kWin - j - 2) * kBC);
+                          base + (DIR == 0 ? j + 2 : kWin - j - 2) * NB);
   }
 }
 
@@ -554,19 +562,19 @@ __device__ __forceinline__ void prep_window(const float (&uu)[kWin], const float
 // One step i outside the full windows (chunk tails): raw loads, Δ, the token update and the B/C
 // prefetch of step i + 1 into bcA.  Returns the wave's partial y (with its D·u share) and sets
 // *dl_out = Δ2.
-template <typename T, int MODE, int DIR>
+template <typename T, int MODE, int DIR, int KH>
 __device__ __forceinline__ float single_step(const ScanArgs& a, const Lane& l, const DirArgs& da, float bias, float Dh,
-                                             int i, const float (&A2)[kH], float (&h)[kH], scalar_fp bct,
-                                             float (&bcA)[kBC], float* dl_out) {
+                                             int i, const float (&A2)[KH], float (&h)[KH], scalar_fp bct,
+                                             float (&bcA)[2 * KH], float* dl_out) {
   using Dr = Dir<MODE, DIR>;
   const T* ub = static_cast<const T*>(da.u) + static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(l.dd) * a.L;
   const T* db = static_cast<const T*>(da.draw) + static_cast<int64_t>(l.b) * da.draw_bs + static_cast<int64_t>(l.dd) * a.L;
   const float uu = ld_act(ub, Dr::pos(l, i));
   const float dl = delta2(ld_act(db, Dr::sidx(a, l, i)), bias);
-  float bcB[kBC];
-  const float y = scan_token(dl, dl * uu, Dh * uu, A2, h, bcA, bcB, bct + Dr::pos(l, i + 1) * kBC);
+  float bcB[2 * KH];
+  const float y = scan_token(dl, dl * uu, Dh * uu, A2, h, bcA, bcB, bct + Dr::pos(l, i + 1) * (2 * KH));
 #pragma unroll
-  for (int q = 0; q < kBC; ++q) bcA[q] = bcB[q];
+  for (int q = 0; q < 2 * KH; ++q) bcA[q] = bcB[q];
   *dl_out = dl;
   return y;
 }
@@ -1160,10 +1168,10 @@ __device__ __forceinline__ void walk_combine(WalkShared<NP>& sh, const Lane& l, 
   }
 }
 
-template <typename T, int DIR, int PHASE, int NP>
+template <typename T, int DIR, int PHASE, int NP, int KH>
 __device__ __forceinline__ void walk_phase(const ScanArgs& a, const Lane& l, const DirArgs& da, float bias, float Dh,
-                                           int i_begin, int n_win, int i_end, int keep_step, const float (&A2)[kH],
-                                           float (&h)[kH], scalar_fp bct, float (&bcA)[kBC], float (&bcB)[kBC],
+                                           int i_begin, int n_win, int i_end, int keep_step, const float (&A2)[KH],
+                                           float (&h)[KH], scalar_fp bct, float (&bcA)[2 * KH], float (&bcB)[2 * KH],
                                            float* G, WalkShared<NP>& sh, int& unit, float* vkeep) {
   constexpr int MODE = kModeFirstPair;  // pair semantics: the backward direction's inputs are stored reversed
   Window<T, MODE, DIR> win;
@@ -1198,38 +1206,42 @@ __device__ __forceinline__ void walk_phase(const ScanArgs& a, const Lane& l, con
   }
 }
 
-template <typename T, int DIR, int NP>
+template <typename T, int DIR, int NP, int KH>
 __device__ __forceinline__ void walk_dir(const ScanArgs& a, const Lane& l, WalkShared<NP>& sh) {
   using Dr = Dir<kModeFirstPair, DIR>;
   const DirArgs& da = DIR == 0 ? a.d0 : a.d1;
   const int L = l.Kc;
   const int M = (L + 1) >> 1;  // steps of the first half
   const bool odd = (L & 1) != 0;
-  float A2[kH], h[kH];
+  float A2[KH], h[KH];
   load_a2(da, l, a.ns, A2);
 #pragma unroll
-  for (int n = 0; n < kH; ++n) h[n] = 0.0f;
+  for (int n = 0; n < KH; ++n) h[n] = 0.0f;
   const float bias = da.bias[l.dd] * kLog2e;
   const float Dh = l.part == 0 ? da.Dp[l.dd] : 0.0f;
-  const scalar_fp bct = bc_row<DIR>(a, l);
+  const scalar_fp bct = bc_row<DIR, KH>(a, l);
   float* G = a.wsy + ((static_cast<int64_t>(l.b) * a.ngroups + l.d / kW) * a.L) * kW;
-  float bcA[kBC], bcB[kBC];
-  load_bc(bct + Dr::pos(l, 0) * kBC, bcA);
+  float bcA[2 * KH], bcB[2 * KH];
+  load_bc(bct + Dr::pos(l, 0) * (2 * KH), bcA);
   const int nw0 = (odd ? M - 1 : M) / kWin;
   // In an odd sequence both directions reach the middle token at step M - 1: the forward one
   // stores it, the backward one adds its value after the phase barrier.
   const int keep = (DIR == 1 && odd) ? M - 1 : -1;
   float vmid = 0.0f;
   int unit = 0;
-  walk_phase<T, DIR, 0, NP>(a, l, da, bias, Dh, 0, nw0, M, keep, A2, h, bct, bcA, bcB, G, sh, unit, &vmid);
+  walk_phase<T, DIR, 0, NP, KH>(a, l, da, bias, Dh, 0, nw0, M, keep, A2, h, bct, bcA, bcB, G, sh, unit, &vmid);
   __syncthreads();  // first halves of both directions stored (global memory, workgroup scope)
   if (keep >= 0 && l.part == NP - 1) G[static_cast<int64_t>(M - 1) * kW + l.lane] += vmid;
-  walk_phase<T, DIR, 1, NP>(a, l, da, bias, Dh, M, (L - M) / kWin, L, -1, A2, h, bct, bcA, bcB, G, sh, unit, &vmid);
+  walk_phase<T, DIR, 1, NP, KH>(a, l, da, bias, Dh, M, (L - M) / kWin, L, -1, A2, h, bct, bcA, bcB, G, sh, unit,
+                                &vmid);
 }
 
 // Workgroup: 2 NP waves on one (batch, channel group) tile of one pair, wave w on direction w & 1
-// and state part w >> 1.  Two pairs (argument sets) per launch, the first set's tiles first.
-template <typename T, int NP>
+// and state part w >> 1 (KH states each; d_state = NP KH).  Two pairs (argument sets) per launch,
+// the first set's tiles first.  A whole-sequence walk has no chunks to add parallelism, so the
+// state is cut into four parts whatever d_state is: at d_state 16 four parts of 4 states give the
+// 56 x 56 workload four waves per SIMD, which outweighs the per-token work shared by fewer states.
+template <typename T, int NP, int KH>
 __global__ __launch_bounds__(2 * kW * NP) void walk_pair_kernel(ScanArgs a0, ScanArgs a1) {
   __shared__ WalkShared<NP> sh;
   const int nb = a0.batch * a0.ngroups, bid = static_cast<int>(blockIdx.x);
@@ -1240,8 +1252,8 @@ __global__ __launch_bounds__(2 * kW * NP) void walk_pair_kernel(ScanArgs a0, Sca
   if (threadIdx.x < 2 * NP) sh.prod[threadIdx.x / NP][threadIdx.x % NP] = 0;
   if (threadIdx.x < 2) sh.cons[threadIdx.x] = 0;
   __syncthreads();
-  if ((__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6) & 1) == 0) walk_dir<T, 0, NP>(a, l, sh);
-  else walk_dir<T, 1, NP>(a, l, sh);
+  if ((__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6) & 1) == 0) walk_dir<T, 0, NP, KH>(a, l, sh);
+  else walk_dir<T, 1, NP, KH>(a, l, sh);
 }
 
 // Cross-merge of the two pairs' sums: out[b][d][h][w] = (R[h W + w] + C[w H + h]) (times
@@ -1785,12 +1797,15 @@ Ss2dLayout ss2d_layout(int64_t batch, int64_t dim, int64_t L, int64_t K, size_t 
 }
 
 // SS2D whole-sequence walk (walk_pair_kernel): chosen for sequences longer than an LDS row when
-// the (batch, channel-group) tiles of both pairs give at least two waves per SIMD
-// (kWalkTiles four-wave units), or forced by a chunk length of at least the sequence.
+// the (batch, channel-group) tiles give both pairs together at least four waves per SIMD
+// (kWalkTiles tiles of two eight-wave workgroups), or forced by a chunk length of at least the
+// sequence.
 constexpr int64_t kWalkTiles = 256;
+constexpr int kWalkParts = 4;  // state parts per direction in the walk: 4 states each at d_state 16, 8 at 32
 bool ss2d_walk(int64_t batch, int64_t dim, int64_t L, int ns, int64_t chunk_len) {
   if (chunk_len > 0) return chunk_len >= L;
-  return L > kKMax && batch * groups(dim) * (ns / kN) >= kWalkTiles;
+  (void)ns;  // the walk's workgroups have kWalkParts parts whatever d_state is
+  return L > kKMax && batch * groups(dim) >= kWalkTiles;
 }
 
 // Walk workspace: the two pairs' float32 rows [batch][group][L][64], the transposed x, and each
@@ -3214,7 +3229,7 @@ vmscan_status ss2d_walk_fwd(const void* x, const void* xT, const void* delta_raw
   for (int k = 0; k < 2; ++k) {  // 0: column pair (directions 1, 3) over x^T; 1: row pair (0, 2) over x
     ScanArgs& s = a[k];
     s.ns = ns;
-    s.parts = ns / kH;
+    s.parts = kWalkParts;  // of ns / kWalkParts states each
     s.u_bs = dim * L;
     s.L = L;
     s.dim = static_cast<int>(dim);
@@ -3228,25 +3243,34 @@ vmscan_status ss2d_walk_fwd(const void* x, const void* xT, const void* delta_raw
     s.bct = reinterpret_cast<float*>(wsp + (k == 0 ? lay.bct_c : lay.bct_r));
     s.d0 = k == 0 ? dir_args(xT, 1, 0) : dir_args(x, 0, 0);
     s.d1 = k == 0 ? dir_args(xT, 3, 1) : dir_args(x, 2, 1);
-    if (dtype == VMSCAN_F32)
-      hipLaunchKernelGGL(bc_transpose_kernel<float>, dim3(static_cast<unsigned>(tblocks)), dim3(kTransThreads), 0,
-                         stream, s);
-    else
-      hipLaunchKernelGGL(bc_transpose_kernel<uint16_t>, dim3(static_cast<unsigned>(tblocks)), dim3(kTransThreads), 0,
-                         stream, s);
+    if (dtype == VMSCAN_F32) {
+      if (ns == 16)
+        hipLaunchKernelGGL((bc_transpose_kernel<float, 4>), dim3(static_cast<unsigned>(tblocks)), dim3(kTransThreads),
+                           0, stream, s);
+      else
+        hipLaunchKernelGGL((bc_transpose_kernel<float, 8>), dim3(static_cast<unsigned>(tblocks)), dim3(kTransThreads),
+                           0, stream, s);
+    } else {
+      if (ns == 16)
+        hipLaunchKernelGGL((bc_transpose_kernel<uint16_t, 4>), dim3(static_cast<unsigned>(tblocks)),
+                           dim3(kTransThreads), 0, stream, s);
+      else
+        hipLaunchKernelGGL((bc_transpose_kernel<uint16_t, 8>), dim3(static_cast<unsigned>(tblocks)),
+                           dim3(kTransThreads), 0, stream, s);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return launch_failed(e);
   }
-  const dim3 grid(static_cast<unsigned>(2 * nb));
+  const dim3 grid(static_cast<unsigned>(2 * nb)), block(2 * kW * kWalkParts);
   if (dtype == VMSCAN_F32) {
-    if (ns == 16) hipLaunchKernelGGL((walk_pair_kernel<float, 2>), grid, dim3(2 * kW * 2), 0, stream, a[0], a[1]);
-    else hipLaunchKernelGGL((walk_pair_kernel<float, 4>), grid, dim3(2 * kW * 4), 0, stream, a[0], a[1]);
+    if (ns == 16) hipLaunchKernelGGL((walk_pair_kernel<float, kWalkParts, 4>), grid, block, 0, stream, a[0], a[1]);
+    else hipLaunchKernelGGL((walk_pair_kernel<float, kWalkParts, 8>), grid, block, 0, stream, a[0], a[1]);
     hipLaunchKernelGGL(walk_merge_kernel<float>, dim3(static_cast<unsigned>(mblocks)), dim3(256), 0, stream,
                        a[1].wsy, a[0].wsy, static_cast<const float*>(z), static_cast<float*>(out),
                        static_cast<int>(dim), static_cast<int>(H), static_cast<int>(W), static_cast<int>(ngr));
   } else {
-    if (ns == 16) hipLaunchKernelGGL((walk_pair_kernel<uint16_t, 2>), grid, dim3(2 * kW * 2), 0, stream, a[0], a[1]);
-    else hipLaunchKernelGGL((walk_pair_kernel<uint16_t, 4>), grid, dim3(2 * kW * 4), 0, stream, a[0], a[1]);
+    if (ns == 16) hipLaunchKernelGGL((walk_pair_kernel<uint16_t, kWalkParts, 4>), grid, block, 0, stream, a[0], a[1]);
+    else hipLaunchKernelGGL((walk_pair_kernel<uint16_t, kWalkParts, 8>), grid, block, 0, stream, a[0], a[1]);
     hipLaunchKernelGGL(walk_merge_kernel<uint16_t>, dim3(static_cast<unsigned>(mblocks)), dim3(256), 0, stream,
                        a[1].wsy, a[0].wsy, static_cast<const uint16_t*>(z), static_cast<uint16_t*>(out),
                        static_cast<int>(dim), static_cast<int>(H), static_cast<int>(W), static_cast<int>(ngr));
