@@ -1979,13 +1979,24 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(const T* __restrict__ dou
   }
 }
 
-// Column sums over the wave's 64 lanes of the 32 values each lane stored in its LDS row: lane c
-// (c < 32) returns the sum of column c; lanes 32-63 return the same sums.
-__device__ __forceinline__ float wave_column_sum(const float* rows, int lane) {
+// Weighted column sums over the wave's 64 lanes of the 32 values each lane stored in its LDS row:
+// lane c (c < 32) returns the sum over rows r of rows[r][c] * wts[c / 8][r], lanes 32-63 the same
+// sums.  Each weight row holds one weight per lane (channel), kWtStride floats apart, so that the
+// four rows a 16-byte read touches start in different banks.
+constexpr int kWtStride = kW + 4;
+constexpr int kWtFloats = 4 * kWtStride;
+__device__ __forceinline__ float wave_column_dot(const float* rows, const float* wts, int lane) {
   const int c = lane & 31, r0 = (lane >> 5) * 32;
-  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // four chains, so the adds overlap the LDS reads
+  const float* wr = wts + (c >> 3) * kWtStride + r0;
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // four chains, so the FMAs overlap the LDS reads
 #pragma unroll
-  for (int r = 0; r < 32; ++r) acc[r & 3] += rows[(r0 + r) * kRedStride + c];
+  for (int r = 0; r < 32; r += 4) {
+    const float4 wv = *reinterpret_cast<const float4*>(wr + r);
+    acc[0] = __builtin_fmaf(rows[(r0 + r) * kRedStride + c], wv.x, acc[0]);
+    acc[1] = __builtin_fmaf(rows[(r0 + r + 1) * kRedStride + c], wv.y, acc[1]);
+    acc[2] = __builtin_fmaf(rows[(r0 + r + 2) * kRedStride + c], wv.z, acc[2]);
+    acc[3] = __builtin_fmaf(rows[(r0 + r + 3) * kRedStride + c], wv.w, acc[3]);
+  }
   const float s = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   return s + __shfl_xor(s, 32);
 }
@@ -2254,19 +2265,20 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
   float* dbcw = ba.dbc + ((static_cast<int64_t>(DIR) * a.ngroups + group) * a.batch + l.b) * 2 * a.ns * a.L;
   // The walk starts after the chunk's last step with a λ = μ, passed back by the chunks after it
   // (zero for the last chunk in scan order and for an unsplit sequence).
-  float lam[kH], anext[kH], dA[kH];
-  const float* mu = ba.adj ? ba.adj + ((((static_cast<int64_t>(l.b) * a.dim + l.dd) * 2 + DIR) * a.nch) + l.c) * (a.ns + 1) +
-                                 kH * l.part
-                           : nullptr;
+  // mu = a_{t+1} λ_{t+1}, the part of λ_t that comes from the later steps
+  float mu[kH], dA[kH];
+  const float* mu0 = ba.adj ? ba.adj + ((((static_cast<int64_t>(l.b) * a.dim + l.dd) * 2 + DIR) * a.nch) + l.c) * (a.ns + 1) +
+                                  kH * l.part
+                            : nullptr;
 #pragma unroll
   for (int n = 0; n < kH; ++n) {
-    lam[n] = mu ? mu[n] : 0.0f;
-    anext[n] = 1.0f;
+    mu[n] = mu0 ? mu0[n] : 0.0f;
     dA[n] = 0.0f;
   }
   float dD = 0.0f, dbias = 0.0f;
   int nstaged = 0;  // windows staged so far
   float* myrow = rows + l.lane * kRedStride;
+  float* wts = rows + kW * kRedStride;  // the column sums' weight rows: [step & 1][B, C][lane]
   RevWin<T, MODE, DIR> rw;
   const WinSched sched = win_sched(ba.msched, L);
   const int nwin = sched.n;
@@ -2311,12 +2323,19 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
     }
     auto bc_at = [&](int j) { return bct + Dr::pos(l, i0 + (j < ns ? j : ns - 1)) * kBC; };
     // The window is walked in two halves (steps 7..4, then 3..0).  Each half first rebuilds its
-    // four states from the checkpoint (the upper half runs through steps 0..3 without keeping
-    // them), so only five states per lane are held at a time.
+    // four states and decays from the checkpoint (the upper half runs through steps 0..3 without
+    // keeping them), so only five states and four decays per lane are held at a time.
 #pragma unroll
     for (int hf = 1; hf >= 0; --hf) {
       const int j0 = 4 * hf;
+      // hiding Δ2 of the lower half's steps from the compiler stops it from keeping the upper
+      // half's rebuild decays of those steps through the upper walk (more registers)
+      if (hf == 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(d2[j]));
+      }
       float hq[5][kH];  // hq[0] = state before step j0, hq[1 + k] = state after step j0 + k
+      float aq[4][kH];  // aq[k] = decay of step j0 + k
       {
         float hcur[kH], bc0[kBC], bc1[kBC];
 #pragma unroll
@@ -2335,17 +2354,17 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
           }
           const float du2 = d2[j] * uu[j];
 #pragma unroll
-          for (int n = 0; n < kH; ++n) hcur[n] = __builtin_fmaf(du2, cur[n], __builtin_amdgcn_exp2f(d2[j] * A[n]) * hcur[n]);
+          for (int n = 0; n < kH; ++n) {
+            const float an = __builtin_amdgcn_exp2f(d2[j] * A[n]);
+            if (j >= j0) aq[j - j0][n] = an;
+            hcur[n] = __builtin_fmaf(du2, cur[n], an * hcur[n]);
+          }
           if (j >= j0) {
 #pragma unroll
             for (int n = 0; n < kH; ++n) hq[1 + j - j0][n] = hcur[n];
           }
         }
       }
-      // The decays are recomputed in the walk rather than kept from the rebuild (more registers);
-      // hiding Δ2 from the compiler stops it from reusing the earlier values.
-#pragma unroll
-      for (int j = j0; j < j0 + 4; ++j) asm volatile("" : "+v"(d2[j]));
       // the upper part's staging area is free once the lower part has read the previous window
       if (hf == 1 && (l.part & 1)) unit_wait(&pf[1], nstaged, a.werr);
       float bc0[kBC], bc1[kBC];
@@ -2358,20 +2377,16 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
           const int k = 2 * r + jj, j = j0 + k;
           float (&cur)[kBC] = (j & 1) ? bc1 : bc0;
           float (&nxt)[kBC] = (j & 1) ? bc0 : bc1;
-          float vb[kH], vc[kH];
+          float lam[kH];
           float P[2] = {0.0f, 0.0f}, Q[2] = {0.0f, 0.0f};  // two chains each
-          const float mdu = vmask * d2[j] * uu[j], mg = vmask * gg[j];
 #pragma unroll
           for (int n = 0; n < kH; ++n) {
-            const float an = __builtin_amdgcn_exp2f(d2[j] * A[n]);
-            lam[n] = __builtin_fmaf(gg[j], cur[kH + n], anext[n] * lam[n]);
-            const float wv = lam[n] * (an * hq[k][n]);
+            lam[n] = __builtin_fmaf(gg[j], cur[kH + n], mu[n]);  // λ_t = g_t C_t + a_{t+1} λ_{t+1}
+            mu[n] = aq[k][n] * lam[n];
+            const float wv = mu[n] * hq[k][n];  // λ_t a_t h_{t-1}
             Q[n & 1] = __builtin_fmaf(A[n], wv, Q[n & 1]);
             dA[n] = __builtin_fmaf(d2[j], wv, dA[n]);
             P[n & 1] = __builtin_fmaf(lam[n], cur[n], P[n & 1]);
-            vb[n] = lam[n] * mdu;
-            vc[n] = mg * hq[k + 1][n];
-            anext[n] = an;
           }
           __builtin_amdgcn_sched_barrier(0);
           if (j > j0) load_bc(bc_at(j - 1), nxt);
@@ -2383,16 +2398,20 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
           dD = __builtin_fmaf(gg[j], uu[j], dD);
           stage[j * kW + l.lane] = __builtin_fmaf(d2[j], Ps, Dh * gg[j]);  // du share
           stage[(kWin + j) * kW + l.lane] = gx;                           // dΔ_raw share
+          // dB_t and dC_t are channel sums of λ_t Δ2_t u_t and g_t h_t: the lane's λ_t and h_t go to
+          // its row, its Δ2_t u_t and g_t to the weight rows (zero past the last channel)
           float4* dst = reinterpret_cast<float4*>(myrow + jj * 2 * kH);
-          dst[0] = make_float4(vb[0], vb[1], vb[2], vb[3]);
-          dst[1] = make_float4(vb[4], vb[5], vb[6], vb[7]);
-          dst[2] = make_float4(vc[0], vc[1], vc[2], vc[3]);
-          dst[3] = make_float4(vc[4], vc[5], vc[6], vc[7]);
+          dst[0] = make_float4(lam[0], lam[1], lam[2], lam[3]);
+          dst[1] = make_float4(lam[4], lam[5], lam[6], lam[7]);
+          dst[2] = make_float4(hq[k + 1][0], hq[k + 1][1], hq[k + 1][2], hq[k + 1][3]);
+          dst[3] = make_float4(hq[k + 1][4], hq[k + 1][5], hq[k + 1][6], hq[k + 1][7]);
+          wts[(2 * jj) * kWtStride + l.lane] = vmask * d2[j] * uu[j];
+          wts[(2 * jj + 1) * kWtStride + l.lane] = vmask * gg[j];
         }
         // A wave's LDS accesses execute in order, so every lane's row is written before it is
         // read and read before the next round overwrites it; the compiler barriers keep that order.
         asm volatile("" ::: "memory");
-        const float sum = wave_column_sum(rows, l.lane);
+        const float sum = wave_column_dot(rows, wts, l.lane);
         asm volatile("" ::: "memory");
         if (l.lane < kRedCols) {
           const int jj = l.lane >> 4, tk = l.lane & 15;  // tk = (B or C) * 8 + state
@@ -2455,7 +2474,7 @@ __device__ __forceinline__ void bwd_scan_block(const BwdArgs& ba, int bid, float
 
 template <typename T, int MODE, int SETS>
 __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(BwdArgs b0, BwdArgs b1) {
-  __shared__ __attribute__((aligned(16))) float rows[4][kW * kRedStride];
+  __shared__ __attribute__((aligned(16))) float rows[4][kW * kRedStride + kWtFloats];
   __shared__ __attribute__((aligned(16))) float stage[4][kStageFloats];
   __shared__ int pflag[2][2];  // per direction: windows staged by the upper part, consumed by the lower
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
