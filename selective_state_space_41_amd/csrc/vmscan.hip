@@ -502,12 +502,8 @@ __device__ __forceinline__ scalar_fp bc_row(const ScanArgs& a, const Lane& l) {
 // which so has this whole token's work to arrive before the next token waits for it.  4 KH SGPRs
 // hold B/C.
 template <int KH>
-__device__ __forceinline__ float scan_token(float dl, float du, float yi, const float (&A2)[KH], float (&h)[KH],
-                                           const float (&cur)[2 * KH], float (&nxt)[2 * KH], scalar_fp nxt_p) {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited for
-  __builtin_amdgcn_sched_barrier(0);
-  load_bc(nxt_p, nxt);
-  __builtin_amdgcn_sched_barrier(0);
+__device__ __forceinline__ float token_update(float dl, float du, float yi, const float (&A2)[KH], float (&h)[KH],
+                                             const float* cur) {
   float an[KH];
 #pragma unroll
   for (int n = 0; n < KH; ++n) an[n] = __builtin_amdgcn_exp2f(dl * A2[n]);
@@ -523,6 +519,16 @@ __device__ __forceinline__ float scan_token(float dl, float du, float yi, const 
     y1 = __builtin_fmaf(cur[KH + n + 1], h[n + 1], y1);
   }
   return y0 + y1;
+}
+
+template <int KH>
+__device__ __forceinline__ float scan_token(float dl, float du, float yi, const float (&A2)[KH], float (&h)[KH],
+                                           const float (&cur)[2 * KH], float (&nxt)[2 * KH], scalar_fp nxt_p) {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited for
+  __builtin_amdgcn_sched_barrier(0);
+  load_bc(nxt_p, nxt);
+  __builtin_amdgcn_sched_barrier(0);
+  return token_update(dl, du, yi, A2, h, cur);
 }
 
 // Steps [i0, i0 + kWin) of one direction.  On entry bcA holds the B/C of step i0; on exit bcA
@@ -544,6 +550,40 @@ __device__ __forceinline__ void run_steps(const Lane& l, int i0, const float (&d
     y[j] = scan_token(dl[j], du[j], yi[j], A2, h, bcA, bcB, base + (DIR == 0 ? j + 1 : kWin - j - 1) * NB);
     y[j + 1] = scan_token(dl[j + 1], du[j + 1], yi[j + 1], A2, h, bcB, bcA,
                           base + (DIR == 0 ? j + 2 : kWin - j - 2) * NB);
+  }
+}
+
+// Steps [i0, i0 + kWin) of a wave of 4 states.  Two adjacent steps' B/C (8 floats each) are
+// adjacent in the B/C copy, so a pair comes with one 64-byte scalar load and is requested two steps
+// before it is used: a wave's token is too short to cover a scalar load's latency on its own.  A
+// pair buffer holds its two positions in address order: the first step's values first in the
+// forward direction, second in the backward one.  On entry pA holds the pair of steps i0, i0 + 1;
+// on exit that of i0 + kWin, i0 + kWin + 1 (the read past a row's end stays inside the copy, as in
+// run_steps).
+template <int MODE, int DIR>
+__device__ __forceinline__ void run_steps2(const Lane& l, int i0, const float (&dl)[kWin], const float (&du)[kWin],
+                                           const float (&yi)[kWin], const float (&A2)[4], float (&h)[4],
+                                           float (&pA)[16], float (&pB)[16], scalar_fp bct, float (&y)[kWin]) {
+  using Dr = Dir<MODE, DIR>;
+  constexpr int NB = 8;
+  const int64_t p0 = Dr::pos(l, i0);
+  // the pair of steps s, s + 1 starts at window base + s (forward) or + kWin - 1 - s (backward)
+  scalar_fp base = DIR == 0 ? bct + p0 * NB : bct + (p0 - kWin) * NB;
+  constexpr int kF = DIR == 0 ? 0 : NB, kS = DIR == 0 ? NB : 0;  // offsets of the first and second step
+#pragma unroll
+  for (int j = 0; j < kWin; j += 4) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): pA, requested two steps ago
+    __builtin_amdgcn_sched_barrier(0);
+    load_bc(base + (DIR == 0 ? j + 2 : kWin - 3 - j) * NB, pB);
+    __builtin_amdgcn_sched_barrier(0);
+    y[j] = token_update(dl[j], du[j], yi[j], A2, h, pA + kF);
+    y[j + 1] = token_update(dl[j + 1], du[j + 1], yi[j + 1], A2, h, pA + kS);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // pB
+    __builtin_amdgcn_sched_barrier(0);
+    load_bc(base + (DIR == 0 ? j + 4 : kWin - 5 - j) * NB, pA);
+    __builtin_amdgcn_sched_barrier(0);
+    y[j + 2] = token_update(dl[j + 2], du[j + 2], yi[j + 2], A2, h, pB + kF);
+    y[j + 3] = token_update(dl[j + 3], du[j + 3], yi[j + 3], A2, h, pB + kS);
   }
 }
 
@@ -1120,14 +1160,24 @@ __global__ __launch_bounds__(2 * kW * NP) void scan_pair_kernel(ScanArgs a) {
 // last part adds its own and does the global store or, in the second half, the read-add of the
 // other direction's value); the first part reuses a ring slot only after the last part has
 // consumed it.  The fp32 sums of both directions are what the merge kernel then reads.
+//
+// Δ2 = softplus(Δ_raw + bias) log2 e and Δ2 u are the same for every state part of a direction,
+// so each part computes them for kWin / NP steps of a window and publishes them in a second LDS
+// ring, from which all parts read the whole window.  A part publishes its share of window w + 1
+// (from raw inputs loaded two windows ahead) before it waits for the shares of window w, so the
+// parts exchange without waiting as long as none is a window behind.
 
-constexpr int kRing = 2;  // windows in flight between the first and the last state part
+constexpr int kRing = 2;   // windows in flight between the first and the last state part
+constexpr int kXRing = 4;  // windows of shared Δ2, Δ2 u: at most three in use (w - 1 .. w + 1)
 
 template <int NP>
 struct WalkShared {
-  float ring[2][kRing][kWin][kW];  // [dir][slot][step][lane]: partial y of a window, parts so far
-  int prod[2][NP];                 // [dir][part]: units the part has added to its ring slot
-  int cons[2];                     // [dir]: units the last part has consumed
+  static constexpr int kX = kWin / NP;  // steps per part and window
+  float ring[2][kRing][kWin][kW];       // [dir][slot][step][lane]: partial y of a window, parts so far
+  int prod[2][NP];                      // [dir][part]: units the part has added to its ring slot
+  int cons[2];                          // [dir]: units the last part has consumed
+  float xv[2][kXRing][NP][2][kW][kX];   // [dir][window % kXRing][part][Δ2, Δ2 u][lane][step]
+  int xprod[2][NP];                     // [dir][part]: windows whose share the part has published
 };
 
 // One window (len steps at positions p0 + kStep j) of partial readouts y: combined over the state
@@ -1168,35 +1218,87 @@ __device__ __forceinline__ void walk_combine(WalkShared<NP>& sh, const Lane& l, 
   }
 }
 
-template <typename T, int DIR, int PHASE, int NP, int KH>
+template <typename T, int DIR, int PHASE, int NP, int KH, int PART>
 __device__ __forceinline__ void walk_phase(const ScanArgs& a, const Lane& l, const DirArgs& da, float bias, float Dh,
                                            int i_begin, int n_win, int i_end, int keep_step, const float (&A2)[KH],
                                            float (&h)[KH], scalar_fp bct, float (&bcA)[2 * KH], float (&bcB)[2 * KH],
-                                           float* G, WalkShared<NP>& sh, int& unit, float* vkeep) {
+                                           float* G, WalkShared<NP>& sh, int& unit, int& xw, float* vkeep) {
   constexpr int MODE = kModeFirstPair;  // pair semantics: the backward direction's inputs are stored reversed
+  constexpr int kX = WalkShared<NP>::kX;
+  static_assert(kWin % NP == 0, "a window's steps split evenly over the state parts");
   Window<T, MODE, DIR> win;
-  const int full_end = i_begin + n_win * kWin;
   constexpr int kStep = DIR == 0 ? 1 : -1;
-  const bool last = l.part == NP - 1;
-  if (full_end > i_begin) win.load(a, l, da, i_begin);
-  for (int i0 = i_begin; i0 < full_end; i0 += kWin) {
-    float uu[kWin], xr[kWin], dl[kWin], du[kWin], yi[kWin], y[kWin], r[kWin];
-    rotate_priority(i0 / kWin);
+  constexpr bool last = PART == NP - 1;
+  float yn[kWin];  // part 0: D u of the window whose share was published last
+  // This part's share of window wi (raw inputs uu, xr): Δ2 and Δ2 u of steps kX PART .. + kX - 1.
+  auto publish = [&](const float (&uu)[kWin], const float (&xr)[kWin], int wi) {
+    float (&mine)[2][kW][kX] = sh.xv[DIR][wi % kXRing][PART];
+#pragma unroll
+    for (int k = 0; k < kX; ++k) {
+      const int j = kX * PART + k;
+      const float d = delta2(xr[j], bias);
+      mine[0][l.lane][k] = d;
+      mine[1][l.lane][k] = d * uu[j];
+    }
+    if (PART == 0) {
+#pragma unroll
+      for (int j = 0; j < kWin; ++j) yn[j] = Dh * uu[j];
+    }
+    unit_signal(&sh.xprod[DIR][PART], wi + 1);
+  };
+  using Dr = Dir<MODE, DIR>;
+  constexpr bool kPairs = KH == 4;  // B/C two steps at a time (run_steps2)
+  float pA[16], pB[16];
+  if (kPairs && n_win > 0) load_bc(bct + (DIR == 0 ? Dr::pos(l, i_begin) : Dr::pos(l, i_begin) - 1) * 8, pA);
+  if (n_win > 0) {
+    float uu[kWin], xr[kWin];
+    win.load(a, l, da, i_begin);
     win.unpack(uu, xr);
-    __builtin_amdgcn_sched_barrier(0);  // see chunk_state_dir
-    win.load(a, l, da, i0 + kWin < full_end ? i0 + kWin : i0);
+    __builtin_amdgcn_sched_barrier(0);
+    win.load(a, l, da, n_win > 1 ? i_begin + kWin : i_begin);
+    publish(uu, xr, xw);
+  }
+  for (int k = 0; k < n_win; ++k, ++xw) {
+    const int i0 = i_begin + k * kWin;
+    float dl[kWin], du[kWin], yi[kWin], y[kWin], r[kWin];
+    rotate_priority(i0 / kWin);
+#pragma unroll
+    for (int j = 0; j < kWin; ++j) yi[j] = PART == 0 ? yn[j] : 0.0f;
+    {
+      // raw inputs of window k + 1 (window k again at the last, unused): the window registers
+      // are loop-carried, so the next load is unconditional and stays after the unpack
+      float uu[kWin], xr[kWin];
+      win.unpack(uu, xr);
+      __builtin_amdgcn_sched_barrier(0);
+      win.load(a, l, da, k + 2 < n_win ? i0 + 2 * kWin : i0);
+      if (k + 1 < n_win) publish(uu, xr, xw + 1);
+    }
+#pragma unroll
+    for (int q = 0; q < NP; ++q)
+      if (q != PART) unit_wait(&sh.xprod[DIR][q], xw + 1, a.werr);
+    const float (&xs)[NP][2][kW][kX] = sh.xv[DIR][xw % kXRing];
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+#pragma unroll
+      for (int kk = 0; kk < kX; ++kk) {
+        dl[kX * q + kk] = xs[q][0][l.lane][kk];
+        du[kX * q + kk] = xs[q][1][l.lane][kk];
+      }
+    }
     const int64_t p0 = DIR == 0 ? i0 : l.Kc - 1 - i0;
     if (PHASE == 1 && last) {
       // the other direction's values, requested a window's work before they are added
 #pragma unroll
       for (int j = 0; j < kWin; ++j) r[j] = G[(p0 + kStep * j) * kW + l.lane];
     }
-    prep_window(uu, xr, bias, Dh, dl, du, yi);
-    run_steps<MODE, DIR>(l, i0, dl, du, yi, A2, h, bcA, bcB, bct, y);
+    if constexpr (kPairs) run_steps2<MODE, DIR>(l, i0, dl, du, yi, A2, h, pA, pB, bct, y);
+    else run_steps<MODE, DIR>(l, i0, dl, du, yi, A2, h, bcA, bcB, bct, y);
     walk_combine<DIR, PHASE, NP, kWin>(sh, l, unit, y, r, G, p0, kStep, -1, vkeep, a.werr);
     ++unit;
   }
-  for (int i = full_end; i < i_end; ++i) {
+  // single steps take their B/C one at a time in bcA
+  if (kPairs && i_begin + n_win * kWin < i_end) load_bc(bct + Dr::pos(l, i_begin + n_win * kWin) * 8, bcA);
+  for (int i = i_begin + n_win * kWin; i < i_end; ++i) {
     float dl, y[1], r[1];
     const int64_t pos = DIR == 0 ? i : l.Kc - 1 - i;
     if (PHASE == 1 && last) r[0] = G[pos * kW + l.lane];
@@ -1206,7 +1308,7 @@ __device__ __forceinline__ void walk_phase(const ScanArgs& a, const Lane& l, con
   }
 }
 
-template <typename T, int DIR, int NP, int KH>
+template <typename T, int DIR, int NP, int KH, int PART>
 __device__ __forceinline__ void walk_dir(const ScanArgs& a, const Lane& l, WalkShared<NP>& sh) {
   using Dr = Dir<kModeFirstPair, DIR>;
   const DirArgs& da = DIR == 0 ? a.d0 : a.d1;
@@ -1228,12 +1330,13 @@ __device__ __forceinline__ void walk_dir(const ScanArgs& a, const Lane& l, WalkS
   // stores it, the backward one adds its value after the phase barrier.
   const int keep = (DIR == 1 && odd) ? M - 1 : -1;
   float vmid = 0.0f;
-  int unit = 0;
-  walk_phase<T, DIR, 0, NP, KH>(a, l, da, bias, Dh, 0, nw0, M, keep, A2, h, bct, bcA, bcB, G, sh, unit, &vmid);
+  int unit = 0, xw = 0;
+  walk_phase<T, DIR, 0, NP, KH, PART>(a, l, da, bias, Dh, 0, nw0, M, keep, A2, h, bct, bcA, bcB, G, sh, unit, xw,
+                                      &vmid);
   __syncthreads();  // first halves of both directions stored (global memory, workgroup scope)
   if (keep >= 0 && l.part == NP - 1) G[static_cast<int64_t>(M - 1) * kW + l.lane] += vmid;
-  walk_phase<T, DIR, 1, NP, KH>(a, l, da, bias, Dh, M, (L - M) / kWin, L, -1, A2, h, bct, bcA, bcB, G, sh, unit,
-                                &vmid);
+  walk_phase<T, DIR, 1, NP, KH, PART>(a, l, da, bias, Dh, M, (L - M) / kWin, L, -1, A2, h, bct, bcA, bcB, G, sh,
+                                      unit, xw, &vmid);
 }
 
 // Workgroup: 2 NP waves on one (batch, channel group) tile of one pair, wave w on direction w & 1
@@ -1249,11 +1352,24 @@ __global__ __launch_bounds__(2 * kW * NP) void walk_pair_kernel(ScanArgs a0, Sca
   const ScanArgs* ap = first ? &a0 : &a1;
   const ScanArgs& a = *ap;
   const Lane l = lane_at(a, logical_block(first ? bid : bid - nb, nb));
-  if (threadIdx.x < 2 * NP) sh.prod[threadIdx.x / NP][threadIdx.x % NP] = 0;
+  if (threadIdx.x < 2 * NP) {
+    sh.prod[threadIdx.x / NP][threadIdx.x % NP] = 0;
+    sh.xprod[threadIdx.x / NP][threadIdx.x % NP] = 0;
+  }
   if (threadIdx.x < 2) sh.cons[threadIdx.x] = 0;
   __syncthreads();
-  if ((__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6) & 1) == 0) walk_dir<T, 0, NP, KH>(a, l, sh);
-  else walk_dir<T, 1, NP, KH>(a, l, sh);
+  static_assert(NP == 4, "one instantiation per state part");
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);  // direction w & 1, part w >> 1
+  switch (w) {
+    case 0: walk_dir<T, 0, NP, KH, 0>(a, l, sh); break;
+    case 1: walk_dir<T, 1, NP, KH, 0>(a, l, sh); break;
+    case 2: walk_dir<T, 0, NP, KH, 1>(a, l, sh); break;
+    case 3: walk_dir<T, 1, NP, KH, 1>(a, l, sh); break;
+    case 4: walk_dir<T, 0, NP, KH, 2>(a, l, sh); break;
+    case 5: walk_dir<T, 1, NP, KH, 2>(a, l, sh); break;
+    case 6: walk_dir<T, 0, NP, KH, 3>(a, l, sh); break;
+    default: walk_dir<T, 1, NP, KH, 3>(a, l, sh); break;
+  }
 }
 
 // Cross-merge of the two pairs' sums: out[b][d][h][w] = (R[h W + w] + C[w H + h]) (times
