@@ -2136,6 +2136,56 @@ struct RevWin {
   }
 };
 
+// Steps [i0, i0 + kWin) of the checkpoint walk: the state only, so only B is read.  A step is too
+// short to cover a scalar load's latency at the two waves per SIMD this pass gets, so B comes two
+// steps at a time, requested two steps before use (one wait per pair: scalar loads may return out
+// of order).  On entry bA holds B of steps i0, i0 + 1; on exit that of i0 + kWin, i0 + kWin + 1
+// (reads past a row's end stay inside the B/C copy, as in run_steps).
+// Steps j, j + 1 (of the window at i0) of the checkpoint walk: the state only, so only B is read.
+// A step is too short to cover a scalar load's latency at the two waves per SIMD this pass gets,
+// so B comes two steps at a time: the pair waits for its own B (requested two steps ago), then
+// requests that of steps j + 2, j + 3 into nxt (one wait per pair: scalar loads may return out of
+// order).  Reads past a row's end stay inside the B/C copy, as in run_steps.
+template <int MODE, int DIR>
+__device__ __forceinline__ void ckpt_pair(const Lane& l, int i0, int j, const float (&dl)[kWin], const float (&du)[kWin],
+                                          const float (&A2)[kH], float (&h)[kH], const float (&cur)[2 * kH],
+                                          float (&nxt)[2 * kH], scalar_fp bct) {
+  using Dr = Dir<MODE, DIR>;
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_sched_barrier(0);
+  const scalar_fp p0 = bct + Dr::pos(l, i0 + j + 2) * kBC, p1 = bct + Dr::pos(l, i0 + j + 3) * kBC;
+#pragma unroll
+  for (int q = 0; q < kH; ++q) {
+    nxt[q] = p0[q];
+    nxt[kH + q] = p1[q];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    float an[kH];
+#pragma unroll
+    for (int n = 0; n < kH; ++n) an[n] = __builtin_amdgcn_exp2f(dl[j + k] * A2[n]);
+#pragma unroll
+    for (int n = 0; n < kH; ++n) {
+      h[n] = h[n] * an[n];
+      h[n] = __builtin_fmaf(du[j + k], cur[kH * k + n], h[n]);
+    }
+  }
+}
+
+// Steps [i0, i0 + kWin) of the checkpoint walk.  On entry bA holds B of steps i0, i0 + 1 (kH floats
+// each, in step order); on exit that of i0 + kWin, i0 + kWin + 1.
+template <int MODE, int DIR>
+__device__ __forceinline__ void ckpt_steps(const Lane& l, int i0, const float (&dl)[kWin], const float (&du)[kWin],
+                                           const float (&A2)[kH], float (&h)[kH], float (&bA)[2 * kH],
+                                           float (&bB)[2 * kH], scalar_fp bct) {
+#pragma unroll
+  for (int j = 0; j < kWin; j += 4) {
+    ckpt_pair<MODE, DIR>(l, i0, j, dl, du, A2, h, bA, bB, bct);
+    ckpt_pair<MODE, DIR>(l, i0, j + 2, dl, du, A2, h, bB, bA, bct);
+  }
+}
+
 // Forward over the sequence, storing the state entering each 8-step window (the steps of a last,
 // partial window are not needed: nothing follows them).  Its own kernel: it needs few registers
 // and so runs at full occupancy.
@@ -2154,7 +2204,7 @@ __device__ __forceinline__ void bwd_ckpt_dir(const BwdArgs& ba, const Lane& l) {
     return ckw + ((static_cast<int64_t>(l.c) * ba.wpc + w) * a.dim + l.dd) * kH;
   };
   const int full_end = (L / kWin) * kWin;
-  float h[kH], bcA[kBC], bcB[kBC];
+  float h[kH];
   if (ba.fnch > 1) {
     // the state entering the chunk, left by the forward's carry prefix for its forward chunk
     // where this direction enters: the first, or (backward direction) the last of the chunk's
@@ -2168,16 +2218,23 @@ __device__ __forceinline__ void bwd_ckpt_dir(const BwdArgs& ba, const Lane& l) {
     for (int n = 0; n < kH; ++n) h[n] = 0.0f;
   }
   Window<T, MODE, DIR> win;
-  load_bc(bct + Dr::pos(l, 0) * kBC, bcA);
-  if (full_end > 0) win.load(a, l, da, 0);
+  float bA[2 * kH], bB[2 * kH];
+  if (full_end > 0) {
+#pragma unroll
+    for (int q = 0; q < kH; ++q) {
+      bA[q] = bct[Dr::pos(l, 0) * kBC + q];
+      bA[kH + q] = bct[Dr::pos(l, 1) * kBC + q];
+    }
+    win.load(a, l, da, 0);
+  }
   for (int i0 = 0; i0 < full_end; i0 += kWin) {
     if (l.valid) store8(ck_at(i0 / kWin), h);
-    float uu[kWin], xr[kWin], dl[kWin], du[kWin], yi[kWin], y[kWin];
+    float uu[kWin], xr[kWin], dl[kWin], du[kWin], yi[kWin];
     win.unpack(uu, xr);
     __builtin_amdgcn_sched_barrier(0);  // see chunk_state_dir
     win.load(a, l, da, i0 + kWin < full_end ? i0 + kWin : i0);
     prep_window(uu, xr, bias2, 0.0f, dl, du, yi);
-    run_steps<MODE, DIR>(l, i0, dl, du, yi, A, h, bcA, bcB, bct, y);
+    ckpt_steps<MODE, DIR>(l, i0, dl, du, A, h, bA, bB, bct);
   }
   if (full_end < L && l.valid) store8(ck_at(full_end / kWin), h);
 }
