@@ -587,6 +587,52 @@ __device__ __forceinline__ void run_steps2(const Lane& l, int i0, const float (&
   }
 }
 
+// Steps j, j + 1 (of the window at i0) of a walk that needs the state only (the chunk pass, the
+// backward's checkpoint pass), so only B is read.  A step is too short to cover a scalar load's
+// latency at the two or three waves per SIMD these passes get, so B comes two steps at a time: the
+// pair waits for its own B (requested two steps ago), then requests that of steps j + 2, j + 3 into
+// nxt (one wait per pair: scalar loads may return out of order).  Reads past a row's end stay
+// inside the B/C copy, as in run_steps.
+template <int MODE, int DIR>
+__device__ __forceinline__ void ckpt_pair(const Lane& l, int i0, int j, const float (&dl)[kWin], const float (&du)[kWin],
+                                          const float (&A2)[kH], float (&h)[kH], const float (&cur)[2 * kH],
+                                          float (&nxt)[2 * kH], scalar_fp bct) {
+  using Dr = Dir<MODE, DIR>;
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_sched_barrier(0);
+  const scalar_fp p0 = bct + Dr::pos(l, i0 + j + 2) * kBC, p1 = bct + Dr::pos(l, i0 + j + 3) * kBC;
+#pragma unroll
+  for (int q = 0; q < kH; ++q) {
+    nxt[q] = p0[q];
+    nxt[kH + q] = p1[q];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    float an[kH];
+#pragma unroll
+    for (int n = 0; n < kH; ++n) an[n] = __builtin_amdgcn_exp2f(dl[j + k] * A2[n]);
+#pragma unroll
+    for (int n = 0; n < kH; ++n) {
+      h[n] = h[n] * an[n];
+      h[n] = __builtin_fmaf(du[j + k], cur[kH * k + n], h[n]);
+    }
+  }
+}
+
+// Steps [i0, i0 + kWin) of a state-only walk.  On entry bA holds B of steps i0, i0 + 1 (kH floats
+// each, in step order); on exit that of i0 + kWin, i0 + kWin + 1.
+template <int MODE, int DIR>
+__device__ __forceinline__ void ckpt_steps(const Lane& l, int i0, const float (&dl)[kWin], const float (&du)[kWin],
+                                           const float (&A2)[kH], float (&h)[kH], float (&bA)[2 * kH],
+                                           float (&bB)[2 * kH], scalar_fp bct) {
+#pragma unroll
+  for (int j = 0; j < kWin; j += 4) {
+    ckpt_pair<MODE, DIR>(l, i0, j, dl, du, A2, h, bA, bB, bct);
+    ckpt_pair<MODE, DIR>(l, i0, j + 2, dl, du, A2, h, bB, bA, bct);
+  }
+}
+
 // Δ2 and Δ2·u of a window from its raw u and Δ_raw (bias2 = bias log2 e); yi = the lane's D·u
 // share (state part 0 only).
 __device__ __forceinline__ void prep_window(const float (&uu)[kWin], const float (&xr)[kWin], float bias2, float Dh,
@@ -673,15 +719,22 @@ __device__ __forceinline__ void chunk_state_dir(const ScanArgs& a, const Lane& l
   const float bias = da.bias[l.dd] * kLog2e;  // base-2 units
   const scalar_fp bct = bc_row<DIR>(a, l);
   float S = 0.0f;
-  float bcA[kBC], bcB[kBC];
+  using Dr = Dir<MODE, DIR>;
+  float bcA[kBC], bA[2 * kH], bB[2 * kH];  // bA, bB: B of two steps (ckpt_steps)
   Window<T, MODE, DIR> win;
   const int full_end = (l.Kc / kWin) * kWin;
   constexpr int me = PART, kX = ChunkXchg<NP>::kX;
-  load_bc(bct + Dir<MODE, DIR>::pos(l, 0) * kBC, bcA);
-  if (full_end > 0) win.load(a, l, da, 0);
+  if (full_end > 0) {
+#pragma unroll
+    for (int q = 0; q < kH; ++q) {
+      bA[q] = bct[Dr::pos(l, 0) * kBC + q];
+      bA[kH + q] = bct[Dr::pos(l, 1) * kBC + q];
+    }
+    win.load(a, l, da, 0);
+  }
   int w = 0;
   for (int i0 = 0; i0 < full_end; i0 += kWin, ++w) {
-    float uu[kWin], xr[kWin], dl[kWin], du[kWin], y[kWin];
+    float uu[kWin], xr[kWin], dl[kWin], du[kWin];
     win.unpack(uu, xr);
     // The prefetch must not be hoisted above the unpack: the window registers are loop-carried,
     // and a load into other registers would need a copy (and so a wait) at the loop back edge.
@@ -712,9 +765,9 @@ __device__ __forceinline__ void chunk_state_dir(const ScanArgs& a, const Lane& l
     }
 #pragma unroll
     for (int j = 0; j < kWin; ++j) S += dl[j];
-    const float yi[kWin] = {};
-    run_steps<MODE, DIR>(l, i0, dl, du, yi, A2, h, bcA, bcB, bct, y);
+    ckpt_steps<MODE, DIR>(l, i0, dl, du, A2, h, bA, bB, bct);
   }
+  if (full_end < l.Kc) load_bc(bct + Dr::pos(l, full_end) * kBC, bcA);  // single steps: one B/C at a time
   for (int i = full_end; i < l.Kc; ++i) {
     float dl;
     single_step<T, MODE, DIR>(a, l, da, bias, 0.0f, i, A2, h, bct, bcA, &dl);
@@ -2141,51 +2194,6 @@ struct RevWin {
 // steps at a time, requested two steps before use (one wait per pair: scalar loads may return out
 // of order).  On entry bA holds B of steps i0, i0 + 1; on exit that of i0 + kWin, i0 + kWin + 1
 // (reads past a row's end stay inside the B/C copy, as in run_steps).
-// Steps j, j + 1 (of the window at i0) of the checkpoint walk: the state only, so only B is read.
-// A step is too short to cover a scalar load's latency at the two waves per SIMD this pass gets,
-// so B comes two steps at a time: the pair waits for its own B (requested two steps ago), then
-// requests that of steps j + 2, j + 3 into nxt (one wait per pair: scalar loads may return out of
-// order).  Reads past a row's end stay inside the B/C copy, as in run_steps.
-template <int MODE, int DIR>
-__device__ __forceinline__ void ckpt_pair(const Lane& l, int i0, int j, const float (&dl)[kWin], const float (&du)[kWin],
-                                          const float (&A2)[kH], float (&h)[kH], const float (&cur)[2 * kH],
-                                          float (&nxt)[2 * kH], scalar_fp bct) {
-  using Dr = Dir<MODE, DIR>;
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __builtin_amdgcn_sched_barrier(0);
-  const scalar_fp p0 = bct + Dr::pos(l, i0 + j + 2) * kBC, p1 = bct + Dr::pos(l, i0 + j + 3) * kBC;
-#pragma unroll
-  for (int q = 0; q < kH; ++q) {
-    nxt[q] = p0[q];
-    nxt[kH + q] = p1[q];
-  }
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    float an[kH];
-#pragma unroll
-    for (int n = 0; n < kH; ++n) an[n] = __builtin_amdgcn_exp2f(dl[j + k] * A2[n]);
-#pragma unroll
-    for (int n = 0; n < kH; ++n) {
-      h[n] = h[n] * an[n];
-      h[n] = __builtin_fmaf(du[j + k], cur[kH * k + n], h[n]);
-    }
-  }
-}
-
-// Steps [i0, i0 + kWin) of the checkpoint walk.  On entry bA holds B of steps i0, i0 + 1 (kH floats
-// each, in step order); on exit that of i0 + kWin, i0 + kWin + 1.
-template <int MODE, int DIR>
-__device__ __forceinline__ void ckpt_steps(const Lane& l, int i0, const float (&dl)[kWin], const float (&du)[kWin],
-                                           const float (&A2)[kH], float (&h)[kH], float (&bA)[2 * kH],
-                                           float (&bB)[2 * kH], scalar_fp bct) {
-#pragma unroll
-  for (int j = 0; j < kWin; j += 4) {
-    ckpt_pair<MODE, DIR>(l, i0, j, dl, du, A2, h, bA, bB, bct);
-    ckpt_pair<MODE, DIR>(l, i0, j + 2, dl, du, A2, h, bB, bA, bct);
-  }
-}
-
 // Forward over the sequence, storing the state entering each 8-step window (the steps of a last,
 // partial window are not needed: nothing follows them).  Its own kernel: it needs few registers
 // and so runs at full occupancy.
@@ -2276,6 +2284,38 @@ __global__ __launch_bounds__(kThreads) void bwd_ckpt_kernel(BwdArgs b0, BwdArgs 
 // the records (X, Σ Δ2) gives every chunk its μ.  This pass computes the records: per direction and
 // state part, the walk from zero over the chunk's steps, last first (windows of 8 with the previous
 // window's loads in flight).  It needs no forward state.
+// Steps j, j - 1 (of the window at i0) of the adjoint-record walk, which runs against the scan
+// order: λ = g C + a λ' with a the later step's decay.  Only C is read, two steps at a time as in
+// ckpt_pair: the pair waits for its own C (cur, requested two steps ago) and requests that of steps
+// j - 2, j - 3 into nxt.  This walk runs towards a row's other end, so the request is clamped to
+// the chunk's first step (the last pair re-reads it) instead of reading past the row.
+template <int MODE, int DIR>
+__device__ __forceinline__ void adj_pair(const Lane& l, int i0, int j, const float (&xr)[kWin], const float (&gg)[kWin],
+                                         float bias2, const float (&A)[kH], float (&lam)[kH], float (&anext)[kH],
+                                         float& S, const float (&cur)[2 * kH], float (&nxt)[2 * kH], scalar_fp bct) {
+  using Dr = Dir<MODE, DIR>;
+  const int i2 = i0 + j - 2 > 0 ? i0 + j - 2 : 0, i3 = i0 + j - 3 > 0 ? i0 + j - 3 : 0;
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_sched_barrier(0);
+  const scalar_fp p2 = bct + Dr::pos(l, i2) * kBC + kH, p3 = bct + Dr::pos(l, i3) * kBC + kH;
+#pragma unroll
+  for (int q = 0; q < kH; ++q) {
+    nxt[q] = p2[q];
+    nxt[kH + q] = p3[q];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const float d2 = delta2(xr[j - k], bias2);
+#pragma unroll
+    for (int n = 0; n < kH; ++n) {
+      lam[n] = __builtin_fmaf(gg[j - k], cur[kH * k + n], anext[n] * lam[n]);
+      anext[n] = __builtin_amdgcn_exp2f(d2 * A[n]);
+    }
+    S += d2;
+  }
+}
+
 template <typename T, int MODE, int DIR>
 __device__ __forceinline__ void adj_state_dir(const BwdArgs& ba, const Lane& l) {
   const ScanArgs& a = ba.s;
@@ -2316,7 +2356,15 @@ __device__ __forceinline__ void adj_state_dir(const BwdArgs& ba, const Lane& l) 
     xw.load(xb + (Dr::kSidxSgn > 0 ? si : si - (kWin - 1)));
     gw.load(gb + (Dr::kPosSgn > 0 ? p : p - (kWin - 1)));
   };
-  if (full_end > 0) wload(full_end - kWin);
+  float cA[2 * kH], cB[2 * kH];  // C of two steps, the later one first
+  if (full_end > 0) {
+    wload(full_end - kWin);
+#pragma unroll
+    for (int q = 0; q < kH; ++q) {
+      cA[q] = bct[Dr::pos(l, full_end - 1) * kBC + kH + q];
+      cA[kH + q] = bct[Dr::pos(l, full_end - 2) * kBC + kH + q];
+    }
+  }
   for (int i0 = full_end - kWin; i0 >= 0; i0 -= kWin) {
     float xr[kWin], gg[kWin];
     xw.template unpack<(Dr::kSidxSgn < 0)>(xr);
@@ -2324,7 +2372,10 @@ __device__ __forceinline__ void adj_state_dir(const BwdArgs& ba, const Lane& l) 
     __builtin_amdgcn_sched_barrier(0);
     wload(i0 > 0 ? i0 - kWin : i0);
 #pragma unroll
-    for (int j = kWin - 1; j >= 0; --j) step(delta2(xr[j], bias2), gg[j], bct + Dr::pos(l, i0 + j) * kBC);
+    for (int j = kWin - 1; j >= 0; j -= 4) {
+      adj_pair<MODE, DIR>(l, i0, j, xr, gg, bias2, A, lam, anext, S, cA, cB, bct);
+      adj_pair<MODE, DIR>(l, i0, j - 2, xr, gg, bias2, A, lam, anext, S, cB, cA, bct);
+    }
   }
   if (l.valid) {
     float* rec = ba.adj + ((((static_cast<int64_t>(l.b) * a.dim + l.d) * 2 + DIR) * a.nch) + l.c) * (a.ns + 1);
