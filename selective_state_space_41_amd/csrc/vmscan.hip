@@ -1283,6 +1283,11 @@ __device__ __forceinline__ void walk_phase(const ScanArgs& a, const Lane& l, con
   constexpr int kStep = DIR == 0 ? 1 : -1;
   constexpr bool last = PART == NP - 1;
   float yn[kWin];  // part 0: D u of the window whose share was published last
+  // Parts above 0 add a window's readout to the ring at the start of the next window, after the
+  // lower part has had that window's work to publish its own: the wait then rarely stalls.
+  float yd[kWin], rd[kWin];  // the pending window's readout (and, last part, second half: the other direction's)
+  int64_t pd = -1;           // its first position, -1 when none
+  int ud = 0;                // its unit
   // This part's share of window wi (raw inputs uu, xr): Δ2 and Δ2 u of steps kX PART .. + kX - 1.
   auto publish = [&](const float (&uu)[kWin], const float (&xr)[kWin], int wi) {
     float (&mine)[2][kW][kX] = sh.xv[DIR][wi % kXRing][PART];
@@ -1339,6 +1344,10 @@ __device__ __forceinline__ void walk_phase(const ScanArgs& a, const Lane& l, con
       }
     }
     const int64_t p0 = DIR == 0 ? i0 : l.Kc - 1 - i0;
+    if (PART > 0 && pd >= 0) {
+      walk_combine<DIR, PHASE, NP, kWin>(sh, l, ud, yd, rd, G, pd, kStep, -1, vkeep, a.werr);
+      pd = -1;
+    }
     if (PHASE == 1 && last) {
       // the other direction's values, requested a window's work before they are added
 #pragma unroll
@@ -1346,9 +1355,20 @@ __device__ __forceinline__ void walk_phase(const ScanArgs& a, const Lane& l, con
     }
     if constexpr (kPairs) run_steps2<MODE, DIR>(l, i0, dl, du, yi, A2, h, pA, pB, bct, y);
     else run_steps<MODE, DIR>(l, i0, dl, du, yi, A2, h, bcA, bcB, bct, y);
-    walk_combine<DIR, PHASE, NP, kWin>(sh, l, unit, y, r, G, p0, kStep, -1, vkeep, a.werr);
+    if (PART == 0) {
+      walk_combine<DIR, PHASE, NP, kWin>(sh, l, unit, y, r, G, p0, kStep, -1, vkeep, a.werr);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kWin; ++j) {
+        yd[j] = y[j];
+        rd[j] = r[j];
+      }
+      pd = p0;
+      ud = unit;
+    }
     ++unit;
   }
+  if (PART > 0 && pd >= 0) walk_combine<DIR, PHASE, NP, kWin>(sh, l, ud, yd, rd, G, pd, kStep, -1, vkeep, a.werr);
   // single steps take their B/C one at a time in bcA
   if (kPairs && i_begin + n_win * kWin < i_end) load_bc(bct + Dr::pos(l, i_begin + n_win * kWin) * 8, bcA);
   for (int i = i_begin + n_win * kWin; i < i_end; ++i) {
