@@ -308,7 +308,7 @@ def make_sets(cfg_id, cfg, nsets, torch, v2=False):
     return sets
 
 
-def bench_config(cfg_id, steps, warmup, with_cpu, torch, V, v2=False, d_state=None):
+def bench_config(cfg_id, steps, warmup, with_cpu, torch, V, v2=False, d_state=None, lane_scan=False):
     import synth
     cfg = with_d_state(cfg_id, d_state)
     v2 = v2 and cfg["kind"] == "vim"
@@ -333,9 +333,11 @@ def bench_config(cfg_id, steps, warmup, with_cpu, torch, V, v2=False, d_state=No
         sets = make_sets(cfg_id, cfg, nsets, torch, v2)
     dev = torch.device("cuda", 0)
     ws = None
+    lane_scan = lane_scan and cfg["kind"] == "vim"
+    chunk_len = V.CHUNK_LANE_SCAN if lane_scan else 0
     if cfg["kind"] == "vim":
-        wsb = V.lib.vmscan_fwd_bidir_workspace_bytes(cfg["batch"], cfg["dim"], cfg["seqlen"], cfg["d_state"],
-                                                     1 if cfg["dtype"] == "bf16" else 0)
+        wsb = V.lib.vmscan_fwd_bidir_workspace_bytes_ex(cfg["batch"], cfg["dim"], cfg["seqlen"], cfg["d_state"],
+                                                        1 if cfg["dtype"] == "bf16" else 0, chunk_len)
     else:
         wsb = V.lib.ss2d_cross_scan_workspace_bytes(cfg["batch"], cfg["dim"], cfg["H"], cfg["W"], cfg["d_state"],
                                                     1 if cfg["dtype"] == "bf16" else 0)
@@ -349,11 +351,11 @@ def bench_config(cfg_id, steps, warmup, with_cpu, torch, V, v2=False, d_state=No
             return V.vmscan_fwd_bidir_v2(act["u"], act["delta_raw"], par["delta_bias"], act["u_b"], act["delta_raw_b"],
                                          par["delta_bias_b"], act["z"], par["A_log"], par["A_b_log"], act["B"],
                                          act["C"], act["B_b"], act["C_b"], par["D"], par["D_b"], out=act["out"],
-                                         workspace=ws, stage=stage, prepare=True)
+                                         workspace=ws, stage=stage, prepare=True, chunk_len=chunk_len)
         if cfg["kind"] == "vim":
             return V.vmscan_fwd_bidir(act["u"], act["delta_raw"], act["z"], par["A_log"], par["A_b_log"], act["B"],
                                       act["C"], act["B_b"], act["C_b"], par["D"], par["D_b"], par["delta_bias"],
-                                      out=act["out"], workspace=ws, stage=stage, prepare=True)
+                                      out=act["out"], workspace=ws, stage=stage, prepare=True, chunk_len=chunk_len)
         return V.ss2d_cross_scan_fwd(act["x"], act["delta_raw"], par["A_log"], act["B"], act["C"], par["D"],
                                      par["delta_bias"], out=act["out"], workspace=ws, prepare=True)
 
@@ -399,7 +401,8 @@ def bench_config(cfg_id, steps, warmup, with_cpu, torch, V, v2=False, d_state=No
     is_default = cfg_id == 1 and cfg["d_state"] == synth.CONFIGS[cfg_id]["d_state"]
     roof = {"bound": "alu", "achieved": round(alu / 1e9, 1), "peak": round(ALU_PEAK_UPD_S / 1e9, 1), "unit": "Gupd/s",
             "frac": round(alu / ALU_PEAK_UPD_S, 4), "traffic": traffic_record(cfg["name"]),
-            "kernel": (("scan_pair_kernel<bf16, vim> (scan stage of vmscan_fwd_bidir" + ("_v2)" if v2 else ")")) if split else
+            "kernel": ((("lane_scan_kernel<bf16> (vmscan_fwd_bidir" if lane_scan else "scan_pair_kernel<bf16, vim> (scan stage of vmscan_fwd_bidir") +
+                        ("_v2)" if v2 else ")")) if split else
                        "all kernels of the call (transpose, chunk states, both SS2D pairs)"),
             "kernel_avg_us": round(kern_ms * 1000, 2),
             "updates_per_launch": upd,
@@ -419,7 +422,8 @@ def bench_config(cfg_id, steps, warmup, with_cpu, torch, V, v2=False, d_state=No
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": cfg["name"] + ("_sepbwd" if v2 else ""), "batch": cfg["batch"], "dim": cfg["dim"],
+        "config": {"workload": cfg["name"] + ("_sepbwd" if v2 else "") + ("_lanescan" if lane_scan else ""),
+                   "batch": cfg["batch"], "dim": cfg["dim"],
                    "seqlen": cfg.get("seqlen", cfg.get("H", 0) * cfg.get("W", 0)), "d_state": cfg["d_state"],
                    "io_dtype": cfg["dtype"], "rotation_sets": len(sets),
                    "step_ms_p10_p50_p90": [step_ms[len(step_ms) // 10], step_ms[len(step_ms) // 2],
@@ -689,6 +693,8 @@ def main():
     ap.add_argument("--bwd", action="store_true", help="time the backward pass of the Vim workloads")
     ap.add_argument("--front", action="store_true",
                     help="time the front convolution (conv1d / conv2d + SiLU) followed by the scan")
+    ap.add_argument("--lane-scan", action="store_true",
+                    help="Vim workloads through the lane-scan path (associative scan over positions, no chunk pass)")
     ap.add_argument("--d-state", type=int, default=None, choices=(16, 32),
                     help="state size of the workloads, forward or backward (default: the workload's own, 16)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -743,7 +749,8 @@ def main():
             if rec is None:
                 continue
         else:
-            rec = bench_config(c, args.steps, args.warmup, not args.no_cpu, torch, V, args.v2, args.d_state)
+            rec = bench_config(c, args.steps, args.warmup, not args.no_cpu, torch, V, args.v2, args.d_state,
+                               args.lane_scan)
         print(json.dumps(rec), flush=True)
 
 

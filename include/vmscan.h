@@ -83,6 +83,14 @@ int vmscan_last_hip_error(void);
 
 /* Chunk length (tokens) the library uses for a bidirectional scan of this shape when
  * chunk_len = 0 is passed to the _ex entry points; a value >= seqlen means one chunk. */
+/* chunk_len = VMSCAN_CHUNK_LANE_SCAN selects, for seqlen <= 8192, the scan that spreads each
+ * sequence over the lanes instead of splitting it into chunks: one workgroup per (batch, channel),
+ * a run of 16 positions per lane, and the state carried between lanes by an associative scan of
+ * (decay, state) pairs within each 1024-position wave segment ([P4] §3.2, the parallel cumulative
+ * form; [P3] §3, the selective-scan kernel's block scan), so no chunk end state is recomputed.
+ * Same results as the other paths up to rounding order; its workspace is the status word only.
+ * Longer sequences return VMSCAN_ERR_UNSUPPORTED. */
+#define VMSCAN_CHUNK_LANE_SCAN (-1)
 int64_t vmscan_fwd_bidir_chunk_len(int64_t batch, int64_t dim, int64_t seqlen, int d_state);
 
 /* Workspace bytes for vmscan_fwd_bidir / vmscan_fwd_bidir_ex (chunk_len 0 = library choice).

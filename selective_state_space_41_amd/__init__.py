@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libvmscan.so")
 
 VMSCAN_F32 = 0
 VMSCAN_BF16 = 1
+CHUNK_LANE_SCAN = -1  # VMSCAN_CHUNK_LANE_SCAN: chunk_len that selects the lane-scan path (seqlen <= 8192)
 D_STATE = 16          # the usual state size; the forward entry points also take 32
 D_STATES_FWD = (16, 32)
 
@@ -185,7 +186,8 @@ def vmscan_fwd_bidir(u, delta_raw, z, A_log, A_b_log, B, C, B_b, C_b, D, D_b, de
     u, delta_raw, z: [batch, dim, L]; A_log, A_b_log: [dim, N] float32 (d_state N = 16 or 32,
     taken from A_log); B, C, B_b, C_b: [batch, N, L] (original token order); D, D_b, delta_bias:
     [dim] float32.  Activations are
-    float32 or bfloat16 (all the same).  ``chunk_len`` 0 lets the library choose.  ``stage``
+    float32 or bfloat16 (all the same).  ``chunk_len`` 0 lets the library choose;
+    ``CHUNK_LANE_SCAN`` selects the lane-scan path (no chunks, seqlen <= 8192).  ``stage``
     1 / 2 runs only the preparation (B/C copy, chunk carries) / the fused scan
     (vmscan_fwd_bidir_stage); 3 runs both.  ``prepare=True`` validates once and returns a callable
     that repeats the call on the same tensors and stream."""

@@ -62,6 +62,7 @@
 #include <cstddef>
 #include <cstdint>
 #include <mutex>
+#include <type_traits>
 
 #include "vmscan.h"
 
@@ -112,6 +113,16 @@ template <>
 struct Run8<uint16_t> {
   uint4 r;
   __device__ __forceinline__ void load(const uint16_t* p) { __builtin_memcpy(&r, p, sizeof(r)); }
+  // elements 0 .. n - 1 only (n may be <= 0); the others read as zero
+  __device__ __forceinline__ void load_part(const uint16_t* p, int n) {
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t lo = 2 * q < n ? p[2 * q] : 0u, hi = 2 * q + 1 < n ? p[2 * q + 1] : 0u;
+      w[q] = lo | (hi << 16);
+    }
+    r = make_uint4(w[0], w[1], w[2], w[3]);
+  }
   template <bool REV>
   __device__ __forceinline__ void unpack(float (&v)[kWin]) const {
     const uint32_t w[4] = {r.x, r.y, r.z, r.w};
@@ -128,6 +139,13 @@ struct Run8<float> {
   __device__ __forceinline__ void load(const float* p) {
     __builtin_memcpy(&r0, p, sizeof(r0));
     __builtin_memcpy(&r1, p + 4, sizeof(r1));
+  }
+  __device__ __forceinline__ void load_part(const float* p, int n) {
+    float t[kWin];
+#pragma unroll
+    for (int j = 0; j < kWin; ++j) t[j] = j < n ? p[j] : 0.0f;
+    r0 = make_float4(t[0], t[1], t[2], t[3]);
+    r1 = make_float4(t[4], t[5], t[6], t[7]);
   }
   template <bool REV>
   __device__ __forceinline__ void unpack(float (&v)[kWin]) const {
@@ -232,6 +250,7 @@ struct ScanArgs {
   // wait for another state part gave up; cleared by the call's first B/C copy (werr_clear).
   int* werr;
   int werr_clear;
+  int lane_path;   // kModeVim: run lane_scan_kernel instead of the chunked pair kernels
 };
 
 // kModeVimSum: Vim order, but the epilogue turns the un-gated sum y_f + y_b into the gate's
@@ -512,13 +531,12 @@ __device__ __forceinline__ float token_update(float dl, float du, float yi, cons
     h[n] = h[n] * an[n];
     h[n] = __builtin_fmaf(du, cur[n], h[n]);
   }
-  float y0 = yi, y1 = 0.0f;
+  // one accumulator: the readout chain is not on the critical path (the next token's decays do
+  // not depend on it), and a second accumulator costs a final add per token (measured 3% slower)
+  float y = yi;
 #pragma unroll
-  for (int n = 0; n < KH; n += 2) {
-    y0 = __builtin_fmaf(cur[KH + n], h[n], y0);
-    y1 = __builtin_fmaf(cur[KH + n + 1], h[n + 1], y1);
-  }
-  return y0 + y1;
+  for (int n = 0; n < KH; ++n) y = __builtin_fmaf(cur[KH + n], h[n], y);
+  return y;
 }
 
 template <int KH>
@@ -1515,6 +1533,238 @@ __global__ __launch_bounds__(256) void walk_merge_kernel(const float* __restrict
 }
 
 // ---------------------------------------------------------------------------------------------
+// Long Vim sequences: lanes over positions, with an associative scan of (decay, state) pairs.
+//
+// A sequence longer than an LDS row is otherwise split into chunks whose end states a chunk pass
+// recomputes from a zero start: a second exp2 per (position, state, direction) for almost the
+// whole sequence.  Here one workgroup of two waves takes one (batch, channel): wave 0 the forward
+// direction, wave 1 the backward one.  A lane owns a run of kRun consecutive positions, so a wave
+// covers a segment of kSeg positions, and the segments are walked in scan order with the state
+// carried between them.  Per state n and segment each lane
+//  * computes its run's decays a_t = exp2(Δ2_t A_n) and inputs b_t = Δ_t u_t B_t,n once and
+//    keeps them in registers, folding them into the run's transform h -> P h + H from a zero
+//    state (P = exp2(A_n Σ Δ2) is the run's total decay);
+//  * combines the transforms of the earlier lanes with an inclusive DPP scan across the wave
+//    (row_shr 1, 2, 4, 8 within rows of 16 lanes, then row_bcast 15 and 31 across rows), the
+//    pair (P1, H1) followed by (P2, H2) composing to (P1 P2, P2 H1 + H2);
+//  * shifts that scan by one lane (wave_shr 1) for the state entering its run, applies it to the
+//    state entering the segment, and walks the run again from there with the kept a_t, b_t,
+//    accumulating y_t += C_t,n h_t.
+// So the carry between lanes costs the scan's few operations per run and state, not a second
+// exp2.  The backward wave takes the runs of a segment in reverse lane order (lane k the run
+// 63 - k, walked backwards), so its scan also runs up the lanes.  Positions past the sequence end
+// have Δ = 0 and input 0, the identity transform.
+//
+// The two directions meet in the middle through an LDS row of the whole sequence: in the first
+// phase the forward wave takes the first half of the segments and the backward wave the second
+// half, each storing its y (with D u) in the row; after a barrier each takes the other half, adds
+// the stored value, applies the gate 0.5 (y_f + y_b) silu(z) and stores the outputs.  A lane's
+// run is contiguous in memory, so a wave's loads and stores are whole contiguous segments.
+// B and C are read directly from the inputs ([batch][state][position]): every lane of a segment
+// reads a different run, so no copy would be shared.
+
+constexpr int kRun = 16;              // positions per lane
+constexpr int kSeg = kW * kRun;       // positions per wave segment
+constexpr int kLaneMaxL = 8192;       // longest sequence taken (its LDS row is 32 KB)
+constexpr int kNMax = 32;             // largest d_state
+
+// N consecutive elements of a row, any alignment; past n (n <= 0: all) they read as zero and are
+// not accessed.
+template <typename T, int N>
+struct RunN {
+  Run8<T> r[N / kWin];
+  __device__ __forceinline__ void load(const T* p, int n) {
+    if (n >= N) {
+#pragma unroll
+      for (int k = 0; k < N / kWin; ++k) r[k].load(p + kWin * k);
+    } else {
+#pragma unroll
+      for (int k = 0; k < N / kWin; ++k) r[k].load_part(p + kWin * k, n - kWin * k);
+    }
+  }
+  // v[i] = element i (REV: element N - 1 - i)
+  template <bool REV>
+  __device__ __forceinline__ void unpack(float (&v)[N]) const {
+#pragma unroll
+    for (int k = 0; k < N / kWin; ++k) {
+      float t[kWin];
+      r[k].template unpack<REV>(t);
+#pragma unroll
+      for (int j = 0; j < kWin; ++j) v[REV ? N - kWin * (k + 1) + j : kWin * k + j] = t[j];
+    }
+  }
+};
+
+// One DPP step of the inclusive scan: each lane composes the transform of the lane the control
+// selects (earlier in the wave) before its own, H += P H_src, P *= P_src.  Both are single VOP2
+// instructions with the shifted operand read through DPP; a lane without a source (row_shr past its
+// row's start) or outside the row mask is not written, which is the identity (1, 0) for free.  A
+// DPP operand must not be read within two wait states of the VALU write that produced it, so each
+// DPP instruction is preceded by s_nop 1.
+#define VMSCAN_SCAN_STEP(CTRL)                                                                    \
+  asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %0, %1 " CTRL " bank_mask:0xf\n\t"                 \
+               "s_nop 1\n\tv_mul_f32_dpp %1, %1, %1 " CTRL " bank_mask:0xf"                        \
+               : "+v"(H), "+v"(P))
+
+// Inclusive scan of the lanes' transforms over the wave (lane 0 first), then shifted by one lane:
+// on return (P, H) is the composition of the transforms of lanes 0 .. lane - 1 (lane 0: identity).
+__device__ __forceinline__ void wave_exclusive_scan(float& P, float& H) {
+  VMSCAN_SCAN_STEP("row_shr:1 row_mask:0xf");
+  VMSCAN_SCAN_STEP("row_shr:2 row_mask:0xf");
+  VMSCAN_SCAN_STEP("row_shr:4 row_mask:0xf");
+  VMSCAN_SCAN_STEP("row_shr:8 row_mask:0xf");
+  VMSCAN_SCAN_STEP("row_bcast:15 row_mask:0xa");  // lane 15 of rows 0 and 2 into rows 1 and 3
+  VMSCAN_SCAN_STEP("row_bcast:31 row_mask:0xc");  // lane 31 into rows 2 and 3
+  asm volatile("s_nop 1" ::: "memory");            // the shift below reads P and H through DPP too
+  P = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(P), 0x138, 0xf, 0xf, false));
+  H = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(H), 0x138, 0xf, 0xf, false));  // wave_shr:1
+}
+#undef VMSCAN_SCAN_STEP
+
+// One segment of one direction: the lane's run, every state, and its half of the combination.
+// FULL: the whole segment lies inside the sequence (every segment but possibly the last), so no
+// lane needs bound checks.
+template <typename T, int DIR, int PHASE, bool FULL>
+__device__ __forceinline__ void lane_segment(const ScanArgs& a, const DirArgs& da, int b, int d, int s, int lane,
+                                             float* row, float* carry) {
+  const int L = static_cast<int>(a.L);
+  const int ns = a.ns;
+  const int p0 = s * kSeg + kRun * (DIR == 0 ? lane : kW - 1 - lane);  // the run's first position
+  const int nv = FULL ? kRun : L - p0;                                   // positions of it in the sequence
+  constexpr bool kRev = DIR == 1;  // index i of the run in scan order: position p0 + i, or p0 + kRun - 1 - i
+  const int64_t rbase = static_cast<int64_t>(b) * a.u_bs + static_cast<int64_t>(d) * L + p0;
+  float dl[kRun], du[kRun], y[kRun];
+  float S = 0.0f;
+  {
+    RunN<T, kRun> ur, xr;
+    ur.load(static_cast<const T*>(da.u) + rbase, nv);
+    xr.load(static_cast<const T*>(da.draw) + static_cast<int64_t>(b) * da.draw_bs + static_cast<int64_t>(d) * L + p0, nv);
+    float uu[kRun], xx[kRun];
+    ur.template unpack<kRev>(uu);
+    xr.template unpack<kRev>(xx);
+    const float bias2 = da.bias[d] * kLog2e;
+    const float Dd = da.Dp[d];
+#pragma unroll
+    for (int i = 0; i < kRun; ++i) {
+      const bool in = (kRev ? kRun - 1 - i : i) < nv;
+      dl[i] = in ? delta2(xx[i], bias2) : 0.0f;
+      du[i] = dl[i] * uu[i] * kLn2;  // Δ u = Δ2 u ln 2
+      y[i] = Dd * uu[i];
+      S += dl[i];
+    }
+  }
+  const T* Bp = static_cast<const T*>(da.B) + static_cast<int64_t>(b) * da.bc_bs + p0;
+  const T* Cp = static_cast<const T*>(da.C) + static_cast<int64_t>(b) * da.bc_bs + p0;
+  const float* Al = da.A_log + static_cast<int64_t>(d) * ns;
+  RunN<T, kRun> br, cr;
+  br.load(Bp, nv);
+  cr.load(Cp, nv);
+  for (int n = 0; n < ns; ++n) {
+    const float A = -expf(Al[n]);
+    const int64_t nxt = static_cast<int64_t>(n + 1 < ns ? n + 1 : n) * L;  // the next state's rows (the last: again)
+    float bv[kRun], av[kRun];
+    br.template unpack<kRev>(bv);
+    br.load(Bp + nxt, nv);
+    float h = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kRun; ++i) {
+      av[i] = __builtin_amdgcn_exp2f(dl[i] * A);
+      bv[i] *= du[i];
+      h = __builtin_fmaf(av[i], h, bv[i]);
+    }
+    float P = __builtin_amdgcn_exp2f(A * S), H = h;
+    wave_exclusive_scan(P, H);
+    h = __builtin_fmaf(P, carry[n], H);  // the state entering the run
+    float cv[kRun];
+    cr.template unpack<kRev>(cv);
+    cr.load(Cp + nxt, nv);
+#pragma unroll
+    for (int i = 0; i < kRun; ++i) {
+      h = __builtin_fmaf(av[i], h, bv[i]);
+      y[i] = __builtin_fmaf(cv[i], h, y[i]);
+    }
+    // the state leaving the segment: the last lane's (positions past the end leave it unchanged)
+    const float hl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(h), kW - 1));
+    if (lane == 0) carry[n] = hl;  // read by this wave only, in order
+  }
+  if (PHASE == 0) {
+#pragma unroll
+    for (int i = 0; i < kRun; ++i) {
+      const int q = kRev ? kRun - 1 - i : i;
+      if (q < nv) row[p0 + q] = y[i];
+    }
+    return;
+  }
+  RunN<T, kRun> zr;
+  zr.load(static_cast<const T*>(a.z) + rbase, nv);
+  float zz[kRun], o[kRun];
+  zr.template unpack<false>(zz);
+#pragma unroll
+  for (int i = 0; i < kRun; ++i) {
+    const int q = kRev ? kRun - 1 - i : i;  // o and zz in position order
+    o[q] = 0.5f * (y[i] + (q < nv ? row[p0 + q] : 0.0f)) * silu_f(zz[q]);
+  }
+  T* op = static_cast<T*>(a.out) + rbase;
+  if (nv >= kRun) {
+#pragma unroll
+    for (int k = 0; k < kRun / kWin; ++k) {
+      float w[kWin];
+#pragma unroll
+      for (int j = 0; j < kWin; ++j) w[j] = o[kWin * k + j];
+      store8(op + kWin * k, w);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < kRun; ++q)
+      if (q < nv) st_act(op, q, o[q]);
+  }
+}
+
+template <typename T, int DIR>
+__device__ __forceinline__ void lane_dir(const ScanArgs& a, int b, int d, int lane, float* row, float* carry) {
+  const DirArgs& da = DIR == 0 ? a.d0 : a.d1;
+  const int nseg = static_cast<int>((a.L + kSeg - 1) / kSeg);
+  const int mid = nseg / 2;  // forward: segments [0, mid) first; backward: [mid, nseg) first
+  if (lane < a.ns) carry[lane] = 0.0f;
+  const int L = static_cast<int>(a.L);
+  // segment s with or without bound checks (only the last one can reach past the sequence)
+  auto seg = [&](int s, auto phase) {
+    constexpr int PH = decltype(phase)::value;
+    if ((s + 1) * kSeg <= L) lane_segment<T, DIR, PH, true>(a, da, b, d, s, lane, row, carry);
+    else lane_segment<T, DIR, PH, false>(a, da, b, d, s, lane, row, carry);
+  };
+  using Ph0 = std::integral_constant<int, 0>;
+  using Ph1 = std::integral_constant<int, 1>;
+  if (DIR == 0) {
+    for (int s = 0; s < mid; ++s) seg(s, Ph0{});
+  } else {
+    for (int s = nseg - 1; s >= mid; --s) seg(s, Ph0{});
+  }
+  __syncthreads();  // the first phase's values are in the row
+  if (DIR == 0) {
+    for (int s = mid; s < nseg; ++s) seg(s, Ph1{});
+  } else {
+    for (int s = mid - 1; s >= 0; --s) seg(s, Ph1{});
+  }
+}
+
+// Workgroup: two waves on one (batch, channel), wave 0 forward, wave 1 backward.
+template <typename T>
+__global__ __launch_bounds__(2 * kW) void lane_scan_kernel(ScanArgs a) {
+  extern __shared__ float lrow[];           // [L]: the first phase's y
+  __shared__ float carry[2][kNMax];         // per direction: the state entering the next segment
+  const int nblk = a.batch * a.dim;
+  const int lb = logical_block(static_cast<int>(blockIdx.x), nblk);  // one XCD: consecutive channels of a batch row
+  const int b = lb / a.dim, d = lb - b * a.dim;
+  const int lane = threadIdx.x & (kW - 1);
+  if (a.werr_clear && blockIdx.x == 0 && threadIdx.x == 0) *a.werr = 0;  // no bounded waits here
+  if (__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6) == 0)
+    lane_dir<T, 0>(a, b, d, lane, lrow, carry[0]);
+  else
+    lane_dir<T, 1>(a, b, d, lane, lrow, carry[1]);
+}
+
+// ---------------------------------------------------------------------------------------------
 // Front convolutions: the local mixing that produces the scan input.  Both are streaming kernels
 // bound by HBM: the scans are bound by the vector ALU, so recomputing the convolution and SiLU
 // in every wave of a scan would cost more issue slots than one pass over the activations, and the
@@ -1967,6 +2217,23 @@ vmscan_status run_pair_dtype(const ScanArgs& a, vmscan_dtype dtype, hipStream_t 
                              : run_pair<uint16_t, MODE>(a, stream, stages);
 }
 
+// The long-sequence Vim forward: one launch, nothing to prepare (stage kStagePrepare is empty).
+template <typename T>
+vmscan_status run_lane(const ScanArgs& a, hipStream_t stream, int stages) {
+  if (!(stages & kStageScan)) return VMSCAN_OK;
+  const int64_t nblocks = static_cast<int64_t>(a.batch) * a.dim;
+  if (nblocks >= (int64_t{1} << 31) || a.L > kLaneMaxL || a.ns > kNMax) return VMSCAN_ERR_SHAPE;
+  hipLaunchKernelGGL(lane_scan_kernel<T>, dim3(static_cast<unsigned>(nblocks)), dim3(2 * kW),
+                     sizeof(float) * static_cast<size_t>(a.L), stream, a);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? VMSCAN_OK : launch_failed(e);
+}
+
+vmscan_status run_vim(const ScanArgs& a, vmscan_dtype dtype, hipStream_t stream, int stages) {
+  if (a.lane_path) return dtype == VMSCAN_F32 ? run_lane<float>(a, stream, stages) : run_lane<uint16_t>(a, stream, stages);
+  return run_pair_dtype<kModeVim>(a, dtype, stream, stages);
+}
+
 // SS2D workspace: the column pair's fp32 image, its transpose, the transposed x, then the B/C copy
 // and the chunk carries shared by both pairs.
 struct Ss2dLayout {
@@ -2048,14 +2315,17 @@ vmscan_status vim_args(ScanArgs& a, const void* u, const void* delta_raw, const 
                         D, D_b, out};
   for (const void* p : ptrs)
     if (!p) return VMSCAN_ERR_NULL;
-  if (!shape_ok(batch, dim, seqlen) || chunk_len < 0) return VMSCAN_ERR_SHAPE;
+  if (!shape_ok(batch, dim, seqlen) || (chunk_len < 0 && chunk_len != VMSCAN_CHUNK_LANE_SCAN)) return VMSCAN_ERR_SHAPE;
   if (!d_state_ok(d_state) || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16)) return VMSCAN_ERR_UNSUPPORTED;
+  if (chunk_len == VMSCAN_CHUNK_LANE_SCAN && seqlen > kLaneMaxL) return VMSCAN_ERR_UNSUPPORTED;
   for (const void* p : ptrs)
     if (!aligned16(p)) return VMSCAN_ERR_ALIGN;
   const int ns = d_state;
-  const int64_t K = plan_chunk(plan_base(batch, dim, ns), seqlen, chunk_len);
-  const vmscan_status ws = check_workspace(workspace, workspace_bytes,
-                                           kStatusBytes + bct_bytes(batch, seqlen, ns) + agg_bytes(batch, dim, seqlen, K, ns));
+  const int64_t K = plan_chunk(plan_base(batch, dim, ns), seqlen, chunk_len > 0 ? chunk_len : 0);
+  const bool lane = chunk_len == VMSCAN_CHUNK_LANE_SCAN;  // the status word is all that path uses
+  const vmscan_status ws = check_workspace(
+      workspace, workspace_bytes,
+      kStatusBytes + (lane ? 0 : bct_bytes(batch, seqlen, ns) + agg_bytes(batch, dim, seqlen, K, ns)));
   if (ws != VMSCAN_OK) return ws;
   a.u_bs = dim * seqlen;
   a.z = z;
@@ -2075,6 +2345,7 @@ vmscan_status vim_args(ScanArgs& a, const void* u, const void* delta_raw, const 
   a.K = static_cast<int>(K);
   a.nch = static_cast<int>(ceil_div(seqlen, K));
   a.ngroups = static_cast<int>(groups(dim));
+  a.lane_path = lane;
   return VMSCAN_OK;
 }
 
@@ -3304,8 +3575,9 @@ int64_t vmscan_fwd_bidir_chunk_len(int64_t batch, int64_t dim, int64_t seqlen, i
 size_t vmscan_fwd_bidir_workspace_bytes_ex(int64_t batch, int64_t dim, int64_t seqlen, int d_state,
                                            vmscan_dtype dtype, int64_t chunk_len) {
   if (!shape_ok(batch, dim, seqlen) || !d_state_ok(d_state) || (dtype != VMSCAN_F32 && dtype != VMSCAN_BF16) ||
-      chunk_len < 0)
+      (chunk_len < 0 && chunk_len != VMSCAN_CHUNK_LANE_SCAN))
     return 0;
+  if (chunk_len == VMSCAN_CHUNK_LANE_SCAN) return seqlen <= kLaneMaxL ? kStatusBytes : 0;  // the status word only
   const int64_t K = plan_chunk(plan_base(batch, dim, d_state), seqlen, chunk_len);
   return kStatusBytes + bct_bytes(batch, seqlen, d_state) + agg_bytes(batch, dim, seqlen, K, d_state);
 }
@@ -3382,7 +3654,7 @@ vmscan_status vmscan_fwd_bidir_v2_stage(const void* u, const void* delta_raw, co
       vim_args(a, u, delta_raw, delta_bias, u_b, delta_raw_b, delta_bias_b, z, A_log, A_b_log, B, C, B_b, C_b, D, D_b,
                out, batch, dim, seqlen, d_state, dtype, workspace, workspace_bytes, chunk_len);
   if (st != VMSCAN_OK) return st;
-  return finish_call(run_pair_dtype<kModeVim>(a, dtype, stream, stage), workspace, stream);
+  return finish_call(run_vim(a, dtype, stream, stage), workspace, stream);
 }
 
 vmscan_status vmscan_fwd_bidir_v2(const void* u, const void* delta_raw, const float* delta_bias, const void* u_b,

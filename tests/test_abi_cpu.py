@@ -104,7 +104,17 @@ def test_fwd_v2_errors(lib):
 def test_fwd_bad_shapes(lib):
     for nb, nd, L in ((0, 16, 8), (2, 0, 8), (2, 16, 0), (-1, 16, 8), (1, 1, 1 << 31)):
         assert _fwd(lib, _good_ptrs(), nb=nb, nd=nd, L=L) == ERR_SHAPE
-    assert _fwd(lib, _good_ptrs(), chunk=-1) == ERR_SHAPE
+    assert _fwd(lib, _good_ptrs(), chunk=-2) == ERR_SHAPE
+
+
+def test_fwd_lane_scan_selector(lib):
+    # chunk_len -1 (VMSCAN_CHUNK_LANE_SCAN) selects the lane-scan path: validation goes on to the
+    # workspace (the status word), and sequences past 8192 positions are refused
+    assert _fwd(lib, _good_ptrs(), chunk=-1) == ERR_WORKSPACE
+    assert _fwd(lib, _good_ptrs(), L=8193, chunk=-1) == ERR_UNSUPPORTED
+    assert lib.vmscan_fwd_bidir_workspace_bytes_ex(I64(2), I64(16), I64(8192), 16, 1, I64(-1)) == 256
+    assert lib.vmscan_fwd_bidir_workspace_bytes_ex(I64(2), I64(16), I64(8193), 16, 1, I64(-1)) == 0
+    assert lib.vmscan_fwd_bidir_workspace_bytes_ex(I64(2), I64(16), I64(100), 16, 1, I64(-2)) == 0
 
 
 def test_fwd_unsupported(lib):

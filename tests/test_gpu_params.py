@@ -181,7 +181,7 @@ def _limit_vim(kind, dtype, L, nb=2, nd=40, layer=0):
 LIMITS = ["delta0", "delta_large", "bias_sweep", "z0"]
 
 
-@pytest.mark.parametrize("L,K", [(197, 0), (150, 32)], ids=["whole", "split"])
+@pytest.mark.parametrize("L,K", [(197, 0), (150, 32), (1100, -1)], ids=["whole", "split", "lanescan"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("kind", LIMITS)
 def test_vim_limits(kind, dtype, L, K):
