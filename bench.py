@@ -618,7 +618,7 @@ def bench_front(cfg_id, steps, warmup, torch, V, with_cpu=False):
                    "front": "conv1d d_conv 4 + SiLU, both branches" if vim else "conv2d 3x3 + SiLU, row-major and transposed"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "conv1d_front_kernel" if vim else "conv2d_front_kernel",
+                     "kernel": "conv1d_flat_kernel" if vim else "conv2d_front_kernel",
                      "kernel_avg_us": round(front_ms * 1000, 2), "algorithmic_bytes_per_launch": fb,
                      "scan": {"bound": "alu", "achieved": round(alu / 1e9, 1), "peak": round(ALU_PEAK_UPD_S / 1e9, 1),
                               "unit": "Gupd/s", "frac": round(alu / ALU_PEAK_UPD_S, 4),

@@ -841,24 +841,36 @@ __global__ __launch_bounds__(256) void carry_prefix_kernel(ScanArgs a, float* re
   float* rec = recs + (bd * 2 + dir) * a.nch * stride;
   const bool up = (dir == 0) != (reverse != 0);  // the walk visits chunks in increasing order
   float h = 0.0f;
-  // eight chunks at a time: all their loads are in flight before the dependent updates
-  for (int k0 = 0; k0 < a.nch; k0 += 8) {
-    float hend[8], S[8];
+  // kPB chunks at a time, the next group's records requested before this group's dependent
+  // updates run: the walk waits for memory about once per sequence instead of once per group
+  constexpr int kPB = 16;
+  auto fetch = [&](int k0, float (&hend)[kPB], float (&S)[kPB]) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < kPB; ++j) {
       const int k = k0 + j < a.nch ? k0 + j : a.nch - 1;
       const float* e = rec + (up ? k : a.nch - 1 - k) * stride;
       hend[j] = e[n];
       S[j] = e[ns];
     }
+  };
+  auto walk = [&](int k0, const float (&hend)[kPB], const float (&S)[kPB]) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < kPB; ++j) {
       const int k = k0 + j;
       if (k < a.nch) {
         rec[(up ? k : a.nch - 1 - k) * stride + n] = h;
         if (k + 1 < a.nch) h = __builtin_fmaf(__builtin_amdgcn_exp2f(A2 * S[j]), h, hend[j]);
       }
     }
+  };
+  float hA[kPB], SA[kPB], hB[kPB], SB[kPB];
+  fetch(0, hA, SA);
+  for (int k0 = 0; k0 < a.nch; k0 += 2 * kPB) {
+    fetch(k0 + kPB < a.nch ? k0 + kPB : k0, hB, SB);
+    walk(k0, hA, SA);
+    if (k0 + kPB >= a.nch) break;
+    fetch(k0 + 2 * kPB < a.nch ? k0 + 2 * kPB : k0, hA, SA);
+    walk(k0 + kPB, hB, SB);
   }
 }
 
@@ -1794,134 +1806,108 @@ __device__ __forceinline__ void conv_taps(const float* w, int64_t d, int K, bool
 // u_b = silu(b_b + Σ_k w_b[k] x[t + (K-1) - k]) (the flipped branch's causal convolution, in
 // original token order), depthwise, from one read of x.
 //
-// A workgroup owns a contiguous span of the flat [rows][L] tensor: whole rows when a row has at
-// most 256 runs of 8 positions (kRowsPerBlock rows), else 256 runs of one row.  The span and
-// 3 positions on each side are staged in LDS with aligned 16-byte loads; each thread then
-// computes one run of 8 positions of one row from LDS (positions outside its row read as zero, so
-// the taps need no masks and a run has one channel), writes its results back to LDS, and the
-// span is stored with aligned 16-byte stores (element stores only in the span's first and last
-// 8-element blocks).  Every global access of a wave is thus full-width and aligned; the run
-// arithmetic is 4 FMAs and a SiLU per output.
-constexpr int kFrontRuns = 256;                      // runs per workgroup
-constexpr int kFrontSpan = kFrontRuns * kWin;        // positions per workgroup, at most
-constexpr int kFrontIn = kFrontSpan + 2 * kWin + 8;  // staged input, aligned start, both halos
-
+// Vim front, flat form: thread k computes the 8 outputs at flat positions f = 8k .. 8k + 7 of the
+// [rows][L] tensors (both branches) from the three aligned 16-byte blocks x[f - 8, f + 16): no
+// staging and no barrier, so every wave goes from its loads to its stores on its own, and the
+// neighbours' reads of the same blocks hit in L1.  (The LDS-staged form this replaced and a
+// grid-stride form that keeps the next run's loads in flight took the same time on the Vim-Ti
+// front, 21-22 us: the write-heavy stream, one read for two outputs, sets it, not the structure.)  A run of 8 can cross one row boundary (rows of
+// at least 8 positions): positions of the window are masked per row (the previous row, the run's
+// first row r0, the next row r0 + 1), and each output takes the convolution of its own row, with
+// its row's taps.  Rows shorter than 8 positions go element by element.
 template <typename T>
-__global__ __launch_bounds__(kFrontRuns) void conv1d_front_kernel(
-    const T* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
-    const float* __restrict__ w_b, const float* __restrict__ bias_b, T* __restrict__ u, T* __restrict__ u_b, int rows,
-    int dim, int L, int K, int rpr, int rows_per_block, int blocks_per_row, float inv_rpr) {
+__global__ __launch_bounds__(256) void conv1d_flat_kernel(const T* __restrict__ x, const float* __restrict__ w,
+                                                          const float* __restrict__ bias,
+                                                          const float* __restrict__ w_b,
+                                                          const float* __restrict__ bias_b, T* __restrict__ u,
+                                                          T* __restrict__ u_b, int64_t total, int dim, int L, int K) {
   constexpr int kHalo = kConvMax - 1;
-  __shared__ __attribute__((aligned(16))) float xin[kFrontIn];
-  __shared__ __attribute__((aligned(16))) T yout[2][kFrontSpan + 2 * kWin];
-  const int tid = threadIdx.x;
-  const int64_t total = static_cast<int64_t>(rows) * L;
-  // this workgroup's rows / runs and this thread's run
-  int row, t0;
-  int64_t S, E;  // flat span [S, E)
-  bool active;
-  if (rows_per_block > 0) {
-    const int r0 = static_cast<int>(blockIdx.x) * rows_per_block;
-    const int nr = rows - r0 < rows_per_block ? rows - r0 : rows_per_block;
-    // tid / rpr for tid < 256: the float quotient is within 1e-5 of (tid + 0.5) / rpr, at least
-    // 0.5 / rpr from an integer
-    const int lr = static_cast<int>((static_cast<float>(tid) + 0.5f) * inv_rpr);
-    row = r0 + lr;
-    t0 = (tid - lr * rpr) * kWin;
-    active = lr < nr;
-    S = static_cast<int64_t>(r0) * L;
-    E = static_cast<int64_t>(r0 + nr) * L;
-  } else {
-    row = static_cast<int>(blockIdx.x) / blocks_per_row;
-    const int seg = static_cast<int>(blockIdx.x) - row * blocks_per_row;
-    t0 = (seg * kFrontRuns + tid) * kWin;
-    active = t0 < L;
-    S = static_cast<int64_t>(row) * L + static_cast<int64_t>(seg) * kFrontSpan;
-    const int64_t seg_end = static_cast<int64_t>(seg + 1) * kFrontSpan;
-    E = static_cast<int64_t>(row) * L + (seg_end < L ? seg_end : L);
-  }
-  // the run's filter taps and biases, requested together with the staged input
-  const int d = (active ? row : 0) % dim;
-  float tap[2][kConvMax], b0[2];
-  conv_taps(w, d, K, false, tap[0]);
-  b0[0] = bias[d];
-  if (u_b) {
-    conv_taps(w_b, d, K, true, tap[1]);
-    b0[1] = bias_b[d];
-  }
-  // stage x[A, A + 8 nchunk) with A = S - 3 rounded down to a multiple of 8
-  const int64_t A = (S - kHalo) & ~static_cast<int64_t>(kWin - 1);
-  const int nchunk = static_cast<int>((E + kHalo - A + kWin - 1) / kWin);
-  for (int c = tid; c < nchunk; c += kFrontRuns) {
-    const int64_t f = A + static_cast<int64_t>(c) * kWin;
-    float v[kWin];
-    if (f >= 0 && f + kWin <= total) {
-      Run8<T> r;
-      r.load(x + f);
-      r.template unpack<false>(v);
-    } else {
-#pragma unroll
-      for (int j = 0; j < kWin; ++j) v[j] = f + j >= 0 && f + j < total ? ld_act(x, f + j) : 0.0f;
-    }
-    float4* dst = reinterpret_cast<float4*>(xin + c * kWin);
-    dst[0] = make_float4(v[0], v[1], v[2], v[3]);
-    dst[1] = make_float4(v[4], v[5], v[6], v[7]);
-  }
-  __syncthreads();
-  const int64_t B = S & ~static_cast<int64_t>(kWin - 1);  // aligned start of the output blocks
-  if (active) {
-    const int n = L - t0 < kWin ? L - t0 : kWin;
-    const int64_t f = static_cast<int64_t>(row) * L + t0;
-    const int o = static_cast<int>(f - kHalo - A);
-    // xs[i] = x at row position t0 - 3 + i, zero outside the row
-    float xs[kWin + 2 * kHalo];
-#pragma unroll
-    for (int i = 0; i < kWin + 2 * kHalo; ++i) {
-      const int t = t0 - kHalo + i;
-      xs[i] = t >= 0 && t < L ? xin[o + i] : 0.0f;
-    }
-    const int oy = static_cast<int>(f - B);
-#pragma unroll
-    for (int br = 0; br < 2; ++br) {
-      if (br == 1 && !u_b) break;
-#pragma unroll
-      for (int j = 0; j < kWin; ++j) {
-        float acc = b0[br];
-#pragma unroll
-        for (int k = 0; k < kConvMax; ++k) acc = __builtin_fmaf(tap[br][k], xs[br == 0 ? j + k : kHalo + j + k], acc);
-        if (j < n) {
-          const float y = silu_f(acc);
-          if constexpr (sizeof(T) == 2) yout[br][oy + j] = f32_to_bf16_rne(y);
-          else yout[br][oy + j] = y;
+  const int64_t f = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * kWin;
+  if (f >= total) return;
+  const int nbr = u_b ? 2 : 1;
+  if (L < kWin) {
+    for (int j = 0; j < kWin && f + j < total; ++j) {
+      const int64_t p = f + j, r = p / L;
+      const int t = static_cast<int>(p - r * L);
+      const int d = static_cast<int>(r % dim);
+      for (int br = 0; br < nbr; ++br) {
+        float tap[kConvMax];
+        conv_taps(br == 0 ? w : w_b, d, K, br == 1, tap);
+        float acc = (br == 0 ? bias : bias_b)[d];
+        for (int k = 0; k < kConvMax; ++k) {
+          const int tt = br == 0 ? t - kHalo + k : t + k;
+          if (tt >= 0 && tt < L) acc = __builtin_fmaf(tap[k], ld_act(x, r * L + tt), acc);
         }
+        st_act(br == 0 ? u : u_b, p, silu_f(acc));
       }
     }
+    return;
   }
-  __syncthreads();
-  // store [S, E) in aligned blocks of 8; the first and last block may be partly outside
-  const int nout = static_cast<int>((E - B + kWin - 1) / kWin);
+  // xs[i] = x at flat position f - 3 + i, i = 0 .. 13 (past either end of the tensor: 0)
+  float xs[kWin + 2 * kHalo];
+  {
+    float pv[kWin], cv[kWin], nv[kWin];
+    Run8<T> rp, rc, rn;
+    if (f >= kWin) rp.load(x + f - kWin);
+    else rp.load_part(x, 0);
+    if (f + kWin <= total) rc.load(x + f);
+    else rc.load_part(x + f, static_cast<int>(total - f));
+    if (f + 2 * kWin <= total) rn.load(x + f + kWin);
+    else rn.load_part(x + f + kWin, static_cast<int>(total - f - kWin));
+    rp.template unpack<false>(pv);
+    rc.template unpack<false>(cv);
+    rn.template unpack<false>(nv);
+#pragma unroll
+    for (int i = 0; i < kHalo; ++i) xs[i] = pv[kWin - kHalo + i];
+#pragma unroll
+    for (int i = 0; i < kWin; ++i) xs[kHalo + i] = cv[i];
+#pragma unroll
+    for (int i = 0; i < kHalo; ++i) xs[kHalo + kWin + i] = nv[i];
+  }
+  const int64_t r0 = f / L;
+  const int t0 = static_cast<int>(f - r0 * L);
+  const int q = L - t0;  // outputs j < q are in row r0, the others in row r0 + 1 (q >= 1)
+  // the window masked to row r0 (x0) and to row r0 + 1 (x1): window position i is at row
+  // position t0 - 3 + i
+  float x0[kWin + 2 * kHalo], x1[kWin + 2 * kHalo];
+#pragma unroll
+  for (int i = 0; i < kWin + 2 * kHalo; ++i) {
+    const int tt = t0 - kHalo + i;
+    x0[i] = tt >= 0 && tt < L ? xs[i] : 0.0f;
+    x1[i] = tt >= L && tt < 2 * L ? xs[i] : 0.0f;
+  }
+  const int d0 = static_cast<int>(r0 % dim), d1 = d0 + 1 < dim ? d0 + 1 : 0;
+  float o[2][kWin];
+#pragma unroll
+  for (int br = 0; br < 2; ++br) {
+    if (br == 1 && !u_b) break;
+    const float* wp = br == 0 ? w : w_b;
+    const float* bp = br == 0 ? bias : bias_b;
+    float ta[kConvMax], tb[kConvMax];
+    conv_taps(wp, d0, K, br == 1, ta);
+    conv_taps(wp, d1, K, br == 1, tb);
+    const float ba = bp[d0], bb = bp[d1];
+#pragma unroll
+    for (int j = 0; j < kWin; ++j) {
+      float aa = ba, ab = bb;
+#pragma unroll
+      for (int k = 0; k < kConvMax; ++k) {
+        const int i = br == 0 ? j + k : kHalo + j + k;  // causal: x[t - 3 + k]; reversed: x[t + k]
+        aa = __builtin_fmaf(ta[k], x0[i], aa);
+        ab = __builtin_fmaf(tb[k], x1[i], ab);
+      }
+      o[br][j] = silu_f(j < q ? aa : ab);
+    }
+  }
+#pragma unroll
   for (int br = 0; br < 2; ++br) {
     if (br == 1 && !u_b) break;
     T* out = br == 0 ? u : u_b;
-    for (int c = tid; c < nout; c += kFrontRuns) {
-      const int64_t f = B + static_cast<int64_t>(c) * kWin;
-      const T* src = &yout[br][c * kWin];
-      if (f >= S && f + kWin <= E) {
-        if constexpr (sizeof(T) == 2) {
-          uint4 r;
-          __builtin_memcpy(&r, src, sizeof(r));
-          __builtin_memcpy(out + f, &r, sizeof(r));
-        } else {
-          float4 r0, r1;
-          __builtin_memcpy(&r0, src, sizeof(r0));
-          __builtin_memcpy(&r1, src + 4, sizeof(r1));
-          __builtin_memcpy(out + f, &r0, sizeof(r0));
-          __builtin_memcpy(out + f + 4, &r1, sizeof(r1));
-        }
-      } else {
-        for (int j = 0; j < kWin; ++j)
-          if (f + j >= S && f + j < E) out[f + j] = src[j];
-      }
+    if (f + kWin <= total) {
+      store8(out + f, o[br]);
+    } else {
+      for (int j = 0; j < kWin; ++j)
+        if (f + j < total) st_act(out, f + j, o[br][j]);
     }
   }
 }
@@ -3931,30 +3917,20 @@ vmscan_status vmscan_conv1d_silu_fwd(const void* x, const float* conv_w, const f
   const void* ptrs[] = {x, conv_w, conv_b, conv_w_b, conv_b_b, u, u_b};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return VMSCAN_ERR_ALIGN;
-  // a workgroup per kFrontRuns runs: whole rows when a row has at most kFrontRuns runs
-  if (batch * dim >= (int64_t{1} << 31) || seqlen >= (int64_t{1} << 30)) return VMSCAN_ERR_SHAPE;
-  const int rows = static_cast<int>(batch * dim), Li = static_cast<int>(seqlen), di = static_cast<int>(dim);
-  const int rpr = static_cast<int>(ceil_div(seqlen, kWin));
-  int rows_per_block = 0, blocks_per_row = 0;
-  int64_t blocks;
-  if (rpr <= kFrontRuns) {
-    rows_per_block = kFrontRuns / rpr;
-    blocks = ceil_div(rows, rows_per_block);
-  } else {
-    blocks_per_row = static_cast<int>(ceil_div(rpr, kFrontRuns));
-    blocks = static_cast<int64_t>(rows) * blocks_per_row;
-  }
-  if (blocks >= (int64_t{1} << 31)) return VMSCAN_ERR_SHAPE;
+  const int64_t total = batch * dim * seqlen;
+  const int64_t blocks = ceil_div(ceil_div(total, kWin), 256);  // a thread per 8 outputs
+  if (dim >= (int64_t{1} << 31) || seqlen >= (int64_t{1} << 30) || blocks >= (int64_t{1} << 31))
+    return VMSCAN_ERR_SHAPE;
   const dim3 grid(static_cast<unsigned>(blocks));
-  const float inv = 1.0f / static_cast<float>(rpr);
+  const int di = static_cast<int>(dim), Li = static_cast<int>(seqlen);
   if (dtype == VMSCAN_F32)
-    hipLaunchKernelGGL(conv1d_front_kernel<float>, grid, dim3(kFrontRuns), 0, stream, static_cast<const float*>(x),
-                       conv_w, conv_b, conv_w_b, conv_b_b, static_cast<float*>(u), static_cast<float*>(u_b), rows, di,
-                       Li, d_conv, rpr, rows_per_block, blocks_per_row, inv);
+    hipLaunchKernelGGL(conv1d_flat_kernel<float>, grid, dim3(256), 0, stream, static_cast<const float*>(x), conv_w,
+                       conv_b, conv_w_b, conv_b_b, static_cast<float*>(u), static_cast<float*>(u_b), total, di, Li,
+                       d_conv);
   else
-    hipLaunchKernelGGL(conv1d_front_kernel<uint16_t>, grid, dim3(kFrontRuns), 0, stream,
-                       static_cast<const uint16_t*>(x), conv_w, conv_b, conv_w_b, conv_b_b, static_cast<uint16_t*>(u),
-                       static_cast<uint16_t*>(u_b), rows, di, Li, d_conv, rpr, rows_per_block, blocks_per_row, inv);
+    hipLaunchKernelGGL(conv1d_flat_kernel<uint16_t>, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(x),
+                       conv_w, conv_b, conv_w_b, conv_b_b, static_cast<uint16_t*>(u), static_cast<uint16_t*>(u_b),
+                       total, di, Li, d_conv);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? VMSCAN_OK : launch_failed(e);
 }

@@ -49,9 +49,11 @@ def oracle_conv1d(p, batches=None, alias_v1=False):
     return O.conv1d_silu(x, p["conv_w"], p["conv_b"]), O.conv1d_silu(x, wb, bb, reverse=True)
 
 
-# rows of at most 256 runs of 8 share a workgroup; longer rows (the last two) are split over several
-CONV1D = [(1, 1, 1), (1, 3, 2), (2, 5, 7), (1, 16, 8), (2, 17, 9), (1, 16, 197), (3, 40, 100), (1, 7, 1000),
-          (1, 300, 3), (1, 3, 2049), (1, 2, 4100)]
+# a thread takes 8 consecutive elements of the flat [rows][L] tensor: rows shorter than 8 go element
+# by element (the first three and (1, 300, 3)); 8 and 9 put the window's far end two rows on; the
+# others put row boundaries at every offset inside a run
+CONV1D = [(1, 1, 1), (1, 3, 2), (2, 5, 7), (1, 16, 8), (2, 17, 9), (1, 6, 10), (1, 16, 197), (3, 40, 100),
+          (1, 7, 1000), (1, 300, 3), (1, 3, 2049), (1, 2, 4100)]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
