@@ -1809,9 +1809,9 @@ __device__ __forceinline__ void conv_taps(const float* w, int64_t d, int K, bool
 // Vim front, flat form: thread k computes the 8 outputs at flat positions f = 8k .. 8k + 7 of the
 // [rows][L] tensors (both branches) from the three aligned 16-byte blocks x[f - 8, f + 16): no
 // staging and no barrier, so every wave goes from its loads to its stores on its own, and the
-// neighbours' reads of the same blocks hit in L1.  (The LDS-staged form this replaced and a
-// grid-stride form that keeps the next run's loads in flight took the same time on the Vim-Ti
-// front, 21-22 us: the write-heavy stream, one read for two outputs, sets it, not the structure.)  A run of 8 can cross one row boundary (rows of
+// neighbours' reads of the same blocks hit in L1.  (A form that stages each span of rows in LDS
+// and a grid-stride form that keeps the next run's loads in flight take the same time on the
+// Vim-Ti front, 21-22 us: the write-heavy stream, one read for two outputs, sets it.)  A run of 8 can cross one row boundary (rows of
 // at least 8 positions): positions of the window are masked per row (the previous row, the run's
 // first row r0, the next row r0 + 1), and each output takes the convolution of its own row, with
 // its row's taps.  Rows shorter than 8 positions go element by element.
