@@ -651,15 +651,13 @@ __device__ __forceinline__ void ckpt_steps(const Lane& l, int i0, const float (&
   }
 }
 
-// Δ2 and Δ2·u of a window from its raw u and Δ_raw (bias2 = bias log2 e); yi = the lane's D·u
-// share (state part 0 only).
-__device__ __forceinline__ void prep_window(const float (&uu)[kWin], const float (&xr)[kWin], float bias2, float Dh,
-                                            float (&dl)[kWin], float (&du)[kWin], float (&yi)[kWin]) {
+// Δ2 and Δ2·u of a window from its raw u and Δ_raw (bias2 = bias log2 e).
+__device__ __forceinline__ void prep_window(const float (&uu)[kWin], const float (&xr)[kWin], float bias2,
+                                            float (&dl)[kWin], float (&du)[kWin]) {
 #pragma unroll
   for (int j = 0; j < kWin; ++j) {
     dl[j] = delta2(xr[j], bias2);
     du[j] = dl[j] * uu[j];
-    yi[j] = Dh * uu[j];
   }
 }
 
@@ -940,8 +938,13 @@ __device__ __forceinline__ void run_phase(const ScanArgs& a, const Lane& l, cons
   const bool relay = NP > 2 && !lo && l.part < NP - 1;  // a middle part publishes its own adds
   float yp[kWin];
   int pp = -1;  // parts above 0: chunk position of the pending window's first step, -1 when none
+  // The readout's starting value: the lane's D·u share in part 0, zero in the other parts (which so
+  // skip the product).
+  float yi[kWin];
+#pragma unroll
+  for (int j = 0; j < kWin; ++j) yi[j] = 0.0f;
   for (int i0 = i_begin; i0 < full_end; i0 += kWin) {
-    float uu[kWin], xr[kWin], dl[kWin], du[kWin], yi[kWin], y[kWin], r[kWin];
+    float uu[kWin], xr[kWin], dl[kWin], du[kWin], y[kWin], r[kWin];
     rotate_priority(i0 / kWin);
     win.unpack(uu, xr);
     __builtin_amdgcn_sched_barrier(0);  // see chunk_state_dir
@@ -957,7 +960,11 @@ __device__ __forceinline__ void run_phase(const ScanArgs& a, const Lane& l, cons
 #pragma unroll
       for (int j = 0; j < kWin; ++j) r[j] = myY[pp + kStep * j];
     }
-    prep_window(uu, xr, bias, Dh, dl, du, yi);
+    prep_window(uu, xr, bias, dl, du);
+    if (lo) {
+#pragma unroll
+      for (int j = 0; j < kWin; ++j) yi[j] = Dh * uu[j];
+    }
     if (!lo && pp >= 0) {
 #pragma unroll
       for (int j = 0; j < kWin; ++j) myY[pp + kStep * j] = r[j] + yp[j];
@@ -2514,11 +2521,11 @@ __device__ __forceinline__ void bwd_ckpt_dir(const BwdArgs& ba, const Lane& l) {
   }
   for (int i0 = 0; i0 < full_end; i0 += kWin) {
     if (l.valid) store8(ck_at(i0 / kWin), h);
-    float uu[kWin], xr[kWin], dl[kWin], du[kWin], yi[kWin];
+    float uu[kWin], xr[kWin], dl[kWin], du[kWin];
     win.unpack(uu, xr);
     __builtin_amdgcn_sched_barrier(0);  // see chunk_state_dir
     win.load(a, l, da, i0 + kWin < full_end ? i0 + kWin : i0);
-    prep_window(uu, xr, bias2, 0.0f, dl, du, yi);
+    prep_window(uu, xr, bias2, dl, du);
     ckpt_steps<MODE, DIR>(l, i0, dl, du, A, h, bA, bB, bct);
   }
   if (full_end < L && l.valid) store8(ck_at(full_end / kWin), h);
