@@ -2085,8 +2085,11 @@ int64_t plan_chunk(int64_t base, int64_t L, int64_t forced) {
   if (fill > nch && ceil_div(L, fill) >= kMinChunk) nch = fill;
   int64_t K = ceil_div(L, nch);
   if (K < kMinChunk) K = kMinChunk;
-  // whole windows of 8 steps: no chunk but the last has a ragged window
-  K = ceil_div(K, kWin) * kWin;
+  // Whole windows of 8 steps, so that no chunk but the last has a ragged window.  Rounded down: the
+  // extra chunk that leaves is a short tail, whereas rounding up drops the chunk count below the
+  // one chosen to fill the last round (measured 1-7% slower on split shapes, 5% on the 1248-pixel
+  // Vim-Ti workload).
+  K = (K / kWin) * kWin;
   if (K > kKSplit) K = (kKSplit / kWin) * kWin;
   return K < L ? K : L;
 }
