@@ -2098,10 +2098,12 @@ int64_t plan_chunk(int64_t base, int64_t L, int64_t forced) {
 // records), which only pays when the unsplit walk would leave CUs idle: with at least one
 // workgroup per CU (kBwdSplitBelow) the sequence stays whole.  Otherwise the chunks are whole
 // multiples m of the forward's chunks Kf, so that the forward carries give the state entering
-// each, and as few as still give kBwdTargetBlocks workgroups (measured best on the 1248-pixel
-// Vim and 56 x 56 SS2D workloads among 512, 1024, 2048 and the forward's own chunks).
+// each, and as few as still give kBwdTargetBlocks workgroups: three rounds of two per CU.  On the
+// 1248-pixel Vim workload (forward chunks of 144) that is m = 1 at d_state 16 and m = 2 at d_state
+// 32, the best of m = 1, 2, 3, 4, 6, 8 at both (a target of 1024 gave m = 3 at d_state 32: 2.86
+// against 2.70 ms).
 constexpr int64_t kBwdSplitBelow = 256;
-constexpr int64_t kBwdTargetBlocks = 1024;
+constexpr int64_t kBwdTargetBlocks = 1536;
 int64_t bwd_chunk(int64_t base, int64_t L, int64_t Kf) {
   const int64_t nch_f = ceil_div(L, Kf);
   if (nch_f <= 1 || base >= kBwdSplitBelow) return L;
