@@ -2250,16 +2250,29 @@ Ss2dLayout ss2d_layout(int64_t batch, int64_t dim, int64_t L, int64_t K, size_t 
   return w;
 }
 
-// SS2D whole-sequence walk (walk_pair_kernel): chosen for sequences longer than an LDS row when
-// the (batch, channel-group) tiles give both pairs together at least four waves per SIMD
-// (kWalkTiles tiles of two eight-wave workgroups), or forced by a chunk length of at least the
-// sequence.
-constexpr int64_t kWalkTiles = 256;
+// SS2D whole-sequence walk (walk_pair_kernel) or chunked pairs, for sequences longer than an LDS row
+// (a chunk length of at least the sequence forces the walk, a shorter one the chunks).  The walk
+// runs one wave per state part along the whole sequence, so with fewer (batch, channel-group) tiles
+// it fills fewer SIMDs and its time grows with L; the chunked path fills the GPU at any tile count but
+// pays the chunk pass.  Measured at d_state 16 (bf16, d_inner 512, walk against the chunked default):
+// the walk wins at every L from 160 tiles up (192 tiles, 56x56: 1075 against 1287 us); at 128 tiles
+// up to L = 1936 (44x44: 568 against 586 us) but not at 2304 or 3136 (671 against 619 us at 48x48);
+// at 96 tiles up to L = 900 (30x30: 243 against 279 us); at 64 tiles nowhere.  d_state 32 keeps the
+// threshold its walk was measured at (256 tiles).
+constexpr int64_t kWalkTiles = 256;        // d_state 32
+constexpr int64_t kWalkTilesAnyL = 160;    // d_state 16: the walk at any L
+constexpr int64_t kWalkTilesMid = 128;     // ... for L <= kWalkMidL
+constexpr int64_t kWalkMidL = 2048;
+constexpr int64_t kWalkTilesShort = 96;    // ... for L <= kWalkShortL
+constexpr int64_t kWalkShortL = 1024;
 constexpr int kWalkParts = 4;  // state parts per direction in the walk: 4 states each at d_state 16, 8 at 32
 bool ss2d_walk(int64_t batch, int64_t dim, int64_t L, int ns, int64_t chunk_len) {
   if (chunk_len > 0) return chunk_len >= L;
-  (void)ns;  // the walk's workgroups have kWalkParts parts whatever d_state is
-  return L > kKMax && batch * groups(dim) >= kWalkTiles;
+  if (L <= kKMax) return false;
+  const int64_t tiles = batch * groups(dim);
+  if (ns != kN) return tiles >= kWalkTiles;
+  return tiles >= kWalkTilesAnyL || (tiles >= kWalkTilesMid && L <= kWalkMidL) ||
+         (tiles >= kWalkTilesShort && L <= kWalkShortL);
 }
 
 // Walk workspace: the two pairs' float32 rows [batch][group][L][64], the transposed x, and each
