@@ -2072,10 +2072,14 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Chunk length for a pair scan over L tokens with `base` = batch * channel-groups workgroups per
 // chunk: one chunk when it fits an LDS row and there are enough workgroups, else enough chunks
-// of at most kKMax tokens to reach kTargetBlocks workgroups.
+// of at most kKMax tokens to reach kTargetBlocks workgroups.  "Enough" is a quarter of a round: a
+// wave of the unsplit scan runs at its own latency-bound pace, so below a round the unsplit call
+// takes about the same time whatever the batch (Vim, d_inner 384, L 197, bf16: 69-73 us from 48 to
+// 288 workgroups), while the split call grows with it (37, 61, 78, 94 us at 48, 144, 192, 288).
+constexpr int64_t kWholeFrom = kTargetBlocks / 4;
 int64_t plan_chunk(int64_t base, int64_t L, int64_t forced) {
   if (forced > 0) return forced < kKMax ? (forced < L ? forced : L) : (kKMax < L ? kKMax : L);
-  if (L <= kKMax && (base >= kTargetBlocks / 2 || L <= kMinChunk)) return L;
+  if (L <= kKMax && (base >= kWholeFrom || L <= kMinChunk)) return L;
   // Split: chunks of at most kKSplit positions (four workgroups per CU), at least one full round of
   // kSplitSlots workgroups, and the chunk count raised to fill the last round.
   int64_t nch = ceil_div(L, kKSplit);

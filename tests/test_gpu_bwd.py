@@ -280,10 +280,10 @@ def test_bwd_unsplit_walk_chunked_forward(dtype):
 @pytest.mark.parametrize("dtype,gated", [("f32", False), ("bf16", True)])
 def test_ss2d_bwd_unsplit_walk_chunked_forward(dtype, gated):
     """SS2D with 256 (batch, channel-group) tiles, so the backward walk is unsplit, over a forward
-    cut into chunks of 48 pixels (8 x 24 images)."""
+    cut into chunks of 56 pixels (8 x 28 images: longer than an LDS row, so the forward splits)."""
     import selective_state_space_41_amd as V
-    assert V.fwd_bidir_chunk_len(32, 512, 192) == 48
-    p = synth.make_ss2d_inputs(4, layer=1800, batch=32, dim=512, H=8, W=24, dtype=dtype, with_z=gated)
+    assert V.fwd_bidir_chunk_len(32, 512, 224) == 56
+    p = synth.make_ss2d_inputs(4, layer=1800, batch=32, dim=512, H=8, W=28, dtype=dtype, with_z=gated)
     dout = _dout(dict(u=p["x"], dtype=dtype), 17)
     got, ref = run_ss2d_bwd(p, dout), oracle_ss2d_bwd(p, dout)
     for k in SS2D_GRADS:
