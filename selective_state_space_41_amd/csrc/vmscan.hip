@@ -2099,18 +2099,22 @@ int64_t plan_chunk(int64_t base, int64_t L, int64_t forced) {
 }
 
 // Backward chunks.  A split adds two passes over the sequence (the forward carries and the adjoint
-// records), which only pays when the unsplit walk would leave CUs idle: with at least one
-// workgroup per CU (kBwdSplitBelow) the sequence stays whole.  Otherwise the chunks are whole
+// records), which only pays when the unsplit walk would leave CUs idle: from kBwdSplitBelow
+// workgroups in the walk's launch (`launch_base`: SS2D runs both pairs in one launch) the sequence
+// stays whole.  Measured (Vim, d_inner 384, bf16, split against whole): 258 tiles, L 232: 345
+// against 367 us; 288 tiles, L 1000 / 3000: 1.42 / 4.16 against 1.57 / 4.75 ms; 384 tiles, L 400 /
+// 1000: 742 / 1875 against 695 / 1773 us; SS2D 56x56 (2 x 256 workgroups): 6.61 against 4.99 ms.
+// Otherwise the chunks are whole
 // multiples m of the forward's chunks Kf, so that the forward carries give the state entering
 // each, and as few as still give kBwdTargetBlocks workgroups: three rounds of two per CU.  On the
 // 1248-pixel Vim workload (forward chunks of 144) that is m = 1 at d_state 16 and m = 2 at d_state
 // 32, the best of m = 1, 2, 3, 4, 6, 8 at both (a target of 1024 gave m = 3 at d_state 32: 2.86
 // against 2.70 ms).
-constexpr int64_t kBwdSplitBelow = 256;
+constexpr int64_t kBwdSplitBelow = 320;
 constexpr int64_t kBwdTargetBlocks = 1536;
-int64_t bwd_chunk(int64_t base, int64_t L, int64_t Kf) {
+int64_t bwd_chunk(int64_t base, int64_t L, int64_t Kf, int64_t launch_base = -1) {
   const int64_t nch_f = ceil_div(L, Kf);
-  if (nch_f <= 1 || base >= kBwdSplitBelow) return L;
+  if (nch_f <= 1 || (launch_base < 0 ? base : launch_base) >= kBwdSplitBelow) return L;
   int64_t m = nch_f / ceil_div(kBwdTargetBlocks, base);
   if (m < 1) m = 1;
   return m * Kf;
@@ -3344,7 +3348,7 @@ Ss2dBwdLayout ss2d_bwd_layout(int64_t batch, int64_t dim, int64_t L, int64_t Kf,
   w.f = ss2d_layout(batch, dim, L, Kf, esz, ns);
   const size_t plane = round256(static_cast<size_t>(batch) * dim * L * sizeof(float));
   const size_t planes = round256(static_cast<size_t>(2) * (ns / kH / 2) * batch * dim * L * sizeof(float));
-  const int64_t Kb = bwd_chunk(plan_base(batch, dim, ns), L, Kf);
+  const int64_t Kb = bwd_chunk(plan_base(batch, dim, ns), L, Kf, 2 * plan_base(batch, dim, ns));
   w.ysum = round256(w.f.total);
   w.g = w.ysum + plane;
   w.gcol = w.g + plane;
@@ -3480,7 +3484,7 @@ vmscan_status run_ss2d_bwd(const void* x, const void* delta_raw, const float* A_
   // own buffers: the column pair (directions 1 and 3 over x^T, g in column order) and the row
   // pair (directions 0 and 2 over x, g in row order).
   BwdArgs bp[2];
-  const int64_t Kb = bwd_chunk(plan_base(batch, dim, ns), L, Kf);
+  const int64_t Kb = bwd_chunk(plan_base(batch, dim, ns), L, Kf, 2 * plan_base(batch, dim, ns));
   for (int k = 0; k < 2; ++k) {
     BwdArgs& ba = bp[k];
     const PairBufs& q = lay.p[k];
