@@ -2404,6 +2404,11 @@ struct BwdArgs {
   float* gx;        // [dir][part / 2][batch][dim][L]: the share of dΔ_raw of a pair of state parts
   float* dbc;       // [dir][group][batch][2][ns][L]: sums over the group's channels of λ Δ2 u (dB / ln2), g h (dC)
   float* dpar;      // [dir][part][dim][kParStride][batch * nch]
+  // SS2D with one share per direction (d_state 16), or null: the walk stores dΔ_raw itself, rounded
+  // once to the activation dtype; element (b, d, idx) of direction DIR at
+  // gx_out + DIR * gx_out_dir + b * gx_out_bs + d * L + idx (else the gx planes and a sum pass).
+  void* gx_out;
+  int64_t gx_out_dir, gx_out_bs;
   int wpc;          // checkpoint slots per chunk (at least the windows of the schedule)
   int msched;       // 1: windows of the forward's two-phase walk, whose checkpoints it stored
   int fnch, fm;     // the forward's chunk count, and forward chunks per backward chunk
@@ -2717,8 +2722,8 @@ constexpr int kStageFloats = 2 * kWin * kW + 2 * kH * kWin;
 
 // Store a window's 8 values v[j] (step j) at the 8 consecutive indices lo..lo+7 that the steps
 // occupy in ascending (ASC) or descending order; only the first ns steps when ns < 8.
-template <bool ASC>
-__device__ __forceinline__ void store_window(float* base, int64_t lo, const float (&v)[kWin], int ns) {
+template <bool ASC, typename O>
+__device__ __forceinline__ void store_window(O* base, int64_t lo, const float (&v)[kWin], int ns) {
   if (ns == kWin) {
     float o[kWin];
 #pragma unroll
@@ -2726,7 +2731,7 @@ __device__ __forceinline__ void store_window(float* base, int64_t lo, const floa
     store8(base + lo, o);
     return;
   }
-  for (int j = 0; j < ns; ++j) base[ASC ? lo + j : lo + kWin - 1 - j] = v[j];
+  for (int j = 0; j < ns; ++j) st_act(base, ASC ? lo + j : lo + kWin - 1 - j, v[j]);
 }
 
 // Windows of a chunk of Kc steps in the walk's step order: uniform windows of kWin steps from step 0
@@ -2973,7 +2978,13 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
 #pragma unroll
       for (int j = 0; j < kWin; ++j) v[j] = stage[(kWin + j) * kW + l.lane] + up[(kWin + j) * kW + l.lane];
       const int64_t slo = Dr::kSidxSgn > 0 ? Dr::sidx(a, l, i0) : Dr::sidx(a, l, i0) - (kWin - 1);
-      store_window<(Dr::kSidxSgn > 0)>(gxw, slo, v, ns);  // Δ_raw's own storage order
+      if (ba.gx_out) {
+        T* gxo = static_cast<T*>(ba.gx_out) + DIR * ba.gx_out_dir + static_cast<int64_t>(l.b) * ba.gx_out_bs +
+                 static_cast<int64_t>(l.dd) * a.L;
+        store_window<(Dr::kSidxSgn > 0)>(gxo, slo, v, ns);
+      } else {
+        store_window<(Dr::kSidxSgn > 0)>(gxw, slo, v, ns);  // Δ_raw's own storage order
+      }
     }
     if (l.lane < 2 * kH) {
       const int ty = l.lane >> 3, kk = l.lane & 7;
@@ -3402,8 +3413,10 @@ vmscan_status ss2d_pair_post(const BwdArgs& ba, int k0, int k1, void* ddelta_raw
   const int64_t plane = n;
   T* ddr = static_cast<T*>(ddelta_raw);
   const int np = a.parts / 2;  // planes per direction
-  launch_sum_planes<T>(ba.gx, np, plane, nullptr, ddr + k0 * DL, DL, a.batch, 4 * DL, stream);
-  launch_sum_planes<T>(ba.gx + np * plane, np, plane, nullptr, ddr + k1 * DL, DL, a.batch, 4 * DL, stream);
+  if (!ba.gx_out) {  // else the walk stored dΔ_raw
+    launch_sum_planes<T>(ba.gx, np, plane, nullptr, ddr + k0 * DL, DL, a.batch, 4 * DL, stream);
+    launch_sum_planes<T>(ba.gx + np * plane, np, plane, nullptr, ddr + k1 * DL, DL, a.batch, 4 * DL, stream);
+  }
   const int ns = a.ns;
   const int64_t NL = static_cast<int64_t>(ns) * a.L;
   launch_bwd_bc<T>(ba.dbc, static_cast<T*>(dB) + k0 * NL, static_cast<T*>(dC) + k0 * NL, static_cast<T*>(dB) + k1 * NL,
@@ -3506,6 +3519,11 @@ vmscan_status run_ss2d_bwd(const void* x, const void* delta_raw, const float* A_
     ba.g = k == 0 ? gcol : g;
     ba.s.d0 = k == 0 ? dir_args(xt, 1, 0) : dir_args(x, 0, 0);
     ba.s.d1 = k == 0 ? dir_args(xt, 3, 1) : dir_args(x, 2, 1);
+    if (a.parts == 2) {  // one dΔ_raw share per direction: the walk rounds and stores it
+      ba.gx_out = static_cast<unsigned char*>(ddelta_raw) + (k == 0 ? 1 : 0) * dim * L * static_cast<int64_t>(esz);
+      ba.gx_out_dir = 2 * dim * L;  // directions (1, 3) and (0, 2): two planes apart
+      ba.gx_out_bs = 4 * dim * L;
+    }
     st = ss2d_pair_prepare<T>(ba, stream);
     if (st != VMSCAN_OK) return st;
     a.werr_clear = 0;
