@@ -3207,6 +3207,93 @@ void launch_sum_planes(const float* base, int np, int64_t pstride, const float* 
                      out_bstride);
 }
 
+// dx of the SS2D backward in one pass.  The column pair's du shares (np float32 planes in the
+// transposed images' order, [img][R = W][Cc = H]) are summed and transposed through an LDS tile, the
+// row pair's shares (np planes, [img][H][W]) are summed and added, and the result is rounded once:
+// dx = (0 + row_0 + row_1 ...) + (0 + col_0 + col_1 ...)^T, the same sums in the same order as
+// summing, transposing and summing again in three passes.
+template <typename O>
+__device__ __forceinline__ void store4(O* p, const float (&v)[4]);
+template <>
+__device__ __forceinline__ void store4(float* p, const float (&v)[4]) {
+  const float4 r = make_float4(v[0], v[1], v[2], v[3]);
+  __builtin_memcpy(p, &r, sizeof(r));
+}
+template <>
+__device__ __forceinline__ void store4(uint16_t* p, const float (&v)[4]) {
+  const uint2 r = make_uint2(static_cast<uint32_t>(f32_to_bf16_rne(v[0])) | (static_cast<uint32_t>(f32_to_bf16_rne(v[1])) << 16),
+                             static_cast<uint32_t>(f32_to_bf16_rne(v[2])) | (static_cast<uint32_t>(f32_to_bf16_rne(v[3])) << 16));
+  __builtin_memcpy(p, &r, sizeof(r));
+}
+
+template <typename O>
+__global__ __launch_bounds__(256) void dx_merge_kernel(const float* __restrict__ colp, const float* __restrict__ rowp,
+                                                       int np, int64_t pstride, O* __restrict__ out, int R, int Cc,
+                                                       int tiles_r, int tiles_c) {
+  __shared__ float tile[kTile][kTile + 1];
+  const int64_t blk = blockIdx.x;
+  const int tc = static_cast<int>(blk % tiles_c);
+  const int tr = static_cast<int>((blk / tiles_c) % tiles_r);
+  const int64_t img = blk / (static_cast<int64_t>(tiles_c) * tiles_r);
+  const int64_t ioff = img * R * Cc;
+  const int r0 = tr * kTile, c0 = tc * kTile;
+  if ((R & 3) == 0 && (Cc & 3) == 0) {
+    // both sides multiples of 4: runs of 4 as single 16-byte accesses on both sides
+    const int tq = threadIdx.x & 15, tw = threadIdx.x >> 4;
+    for (int i = tw; i < kTile; i += 16) {
+      const int r = r0 + i, c = c0 + 4 * tq;
+      if (r < R && c < Cc) {
+        float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int k = 0; k < np; ++k) {
+          float v[4];
+          __builtin_memcpy(v, colp + k * pstride + ioff + static_cast<int64_t>(r) * Cc + c, sizeof(v));
+#pragma unroll
+          for (int q = 0; q < 4; ++q) sum[q] += v[q];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) tile[i][4 * tq + q] = sum[q];
+      }
+    }
+    __syncthreads();
+    for (int i = tw; i < kTile; i += 16) {
+      const int c = c0 + i, r = r0 + 4 * tq;
+      if (c < Cc && r < R) {
+        const int64_t o = ioff + static_cast<int64_t>(c) * R + r;
+        float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int k = 0; k < np; ++k) {
+          float v[4];
+          __builtin_memcpy(v, rowp + k * pstride + o, sizeof(v));
+#pragma unroll
+          for (int q = 0; q < 4; ++q) sum[q] += v[q];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sum[q] += tile[4 * tq + q][i];
+        store4(out + o, sum);
+      }
+    }
+    return;
+  }
+  const int tx = threadIdx.x & (kTile - 1), ty = threadIdx.x >> 6;
+  for (int i = ty; i < kTile; i += 4) {
+    const int r = r0 + i, c = c0 + tx;
+    if (r < R && c < Cc) {
+      float sum = 0.0f;
+      for (int k = 0; k < np; ++k) sum += colp[k * pstride + ioff + static_cast<int64_t>(r) * Cc + c];
+      tile[i][tx] = sum;
+    }
+  }
+  __syncthreads();
+  for (int i = ty; i < kTile; i += 4) {
+    const int c = c0 + i, r = r0 + tx;
+    if (c < Cc && r < R) {
+      const int64_t o = ioff + static_cast<int64_t>(c) * R + r;
+      float sum = 0.0f;
+      for (int k = 0; k < np; ++k) sum += rowp[k * pstride + o];
+      st_act(out, o, sum + tile[tx][i]);
+    }
+  }
+}
+
 // Backward buffers that depend on the chunking (the forward's: chunks of Kf): checkpoints of every
 // window of every chunk, the adjoint records (split sequences only) and the per-chunk parameter sums.
 // Checkpoint slots per chunk: its windows, one more for the forward's two-phase schedule.
@@ -3533,17 +3620,18 @@ vmscan_status run_ss2d_bwd(const void* x, const void* delta_raw, const float* A_
   const BwdArgs& ba = bp[0];
   st = ss2d_pair_post<T>(bp[0], 1, 3, ddelta_raw, dB, dC, dA_log, A_log, dD, ddelta_bias, stream);
   if (st != VMSCAN_OK) return st;
-  // its du back to row-major pixels: sum the partial planes (column order), transpose
-  float* col = reinterpret_cast<float*>(wsp + lay.f.col_img);
-  float* rowp = reinterpret_cast<float*>(wsp + lay.f.row_img);
-  launch_sum_planes<float>(ba.gu, a.parts, n, nullptr, col, n, 1, n, stream);
-  st = launch_transpose(col, rowp, nimg, static_cast<int>(W), static_cast<int>(H), 4, stream);
-  if (st != VMSCAN_OK) return st;
-  // the row pair's gradients, and dx = its du plus the column pair's, transposed
+  // the row pair's gradients, and dx = its du plus the column pair's, transposed (one pass)
   const BwdArgs& br = bp[1];
   st = ss2d_pair_post<T>(br, 0, 2, ddelta_raw, dB, dC, dA_log, A_log, dD, ddelta_bias, stream);
   if (st != VMSCAN_OK) return st;
-  launch_sum_planes<T>(br.gu, a.parts, n, rowp, static_cast<T*>(dx), n, 1, n, stream);
+  {
+    const int R = static_cast<int>(W), Cc = static_cast<int>(H);
+    const int tr = static_cast<int>(ceil_div(R, kTile)), tc = static_cast<int>(ceil_div(Cc, kTile));
+    const int64_t blocks = nimg * tr * tc;
+    if (blocks >= (int64_t{1} << 31)) return VMSCAN_ERR_SHAPE;
+    hipLaunchKernelGGL(dx_merge_kernel<T>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, ba.gu, br.gu,
+                       a.parts, n, static_cast<T*>(dx), R, Cc, tr, tc);
+  }
   e = hipGetLastError();
   return e == hipSuccess ? VMSCAN_OK : launch_failed(e);
 }
