@@ -2398,6 +2398,8 @@ struct BwdArgs {
                     // chunking (K, nch) and, for split sequences, the forward carries (agg: the state
                     // entering each chunk)
   const float* g;   // [batch][dim][L]: dout silu(z) / 2
+  const void* gt;   // ungated SS2D with bf16 activations and unsplit walks, or null: g in the activation
+                    // dtype (dout itself, or its transpose for the column pair), read instead of g
   float* ck;        // [batch][dir][part][nch * wpc][dim][8]: state entering each window of each chunk
   float* adj;       // split sequences: [batch][dim][dir][nch][ns + 1] adjoint records, then carries
   float* gu;        // [dir][part / 2][batch][dim][L]: the share of du of a pair of state parts
@@ -2486,13 +2488,15 @@ __device__ __forceinline__ float wave_column_dot(const float* rows, const float*
 }
 
 // Raw inputs of one full 8-step window of the backward walk, loaded one window ahead: u and
-// Δ_raw (activation dtype), g (float32) and the checkpoint state entering the window.
-template <typename T, int MODE, int DIR>
+// Δ_raw (activation dtype), g (GT: float32, or the activation dtype when it is dout itself) and the
+// checkpoint state entering the window.
+template <typename T, int MODE, int DIR, typename GT = float>
 struct RevWin {
   using Dr = Dir<MODE, DIR>;
   Run8<T> u, x;
-  Run8<float> g, ck;
-  __device__ __forceinline__ void load(const ScanArgs& a, const T* ub, const T* xb, const float* gb, const float* ckp,
+  Run8<GT> g;
+  Run8<float> ck;
+  __device__ __forceinline__ void load(const ScanArgs& a, const T* ub, const T* xb, const GT* gb, const float* ckp,
                                        const Lane& l, int i0) {
     const int64_t p = Dr::pos(l, i0);
     const int64_t lo = Dr::kPosSgn > 0 ? p : p - (kWin - 1);  // lowest position of the window
@@ -2773,16 +2777,18 @@ __device__ __forceinline__ void win_at(const WinSched& w, int s, int& i0, int& l
 }
 
 // The adjoint walk of one direction and state part over one chunk, window by window from the last.
-template <typename T, int MODE, int DIR>
+template <typename T, int MODE, int DIR, bool GACT = false>
 __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float* rows, float* stage, int* pf) {
   const ScanArgs& a = ba.s;
   using Dr = Dir<MODE, DIR>;
+  using GT = typename std::conditional<GACT, T, float>::type;  // g as stored
   constexpr bool kRevOrder = Dr::kPosSgn < 0;  // window positions descend with the step
   const DirArgs& da = DIR == 0 ? a.d0 : a.d1;
   const int L = l.Kc;  // steps of this chunk
   const T* ub = static_cast<const T*>(da.u) + static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(l.dd) * a.L;
   const T* xb = static_cast<const T*>(da.draw) + static_cast<int64_t>(l.b) * da.draw_bs + static_cast<int64_t>(l.dd) * a.L;
-  const float* gb = ba.g + static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(l.dd) * a.L;
+  const GT* gb = (GACT ? static_cast<const GT*>(ba.gt) : reinterpret_cast<const GT*>(ba.g)) +
+                 static_cast<int64_t>(l.b) * a.u_bs + static_cast<int64_t>(l.dd) * a.L;
   float A[kH];
   load_a2(da, l, a.ns, A);
   const float bias2 = da.bias[l.dd] * kLog2e;
@@ -2818,7 +2824,7 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
   int nstaged = 0;  // windows staged so far
   float* myrow = rows + l.lane * kRedStride;
   float* wts = rows + kW * kRedStride;  // the column sums' weight rows: [step & 1][B, C][lane]
-  RevWin<T, MODE, DIR> rw;
+  RevWin<T, MODE, DIR, GT> rw;
   const WinSched sched = win_sched(ba.msched, L);
   const int nwin = sched.n;
   {
@@ -2851,7 +2857,7 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
         const int64_t p = Dr::pos(l, ij);
         xr[j] = ld_act(xb, Dr::sidx(a, l, ij));
         uu[j] = ld_act(ub, p);
-        gg[j] = j < ns ? gb[p] : 0.0f;
+        gg[j] = j < ns ? ld_act(gb, p) : 0.0f;
       }
       if (nsn == kWin) rw.load(a, ub, xb, gb, ck_at(w - 1), l, i0n);
     }
@@ -2978,7 +2984,9 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
 #pragma unroll
       for (int j = 0; j < kWin; ++j) v[j] = stage[(kWin + j) * kW + l.lane] + up[(kWin + j) * kW + l.lane];
       const int64_t slo = Dr::kSidxSgn > 0 ? Dr::sidx(a, l, i0) : Dr::sidx(a, l, i0) - (kWin - 1);
-      if (ba.gx_out) {
+      bool direct = false;  // SS2D only: the Vim walk would carry the branch's registers too
+      if constexpr (MODE == kModeSecondPair) direct = ba.gx_out != nullptr;
+      if (direct) {
         T* gxo = static_cast<T*>(ba.gx_out) + DIR * ba.gx_out_dir + static_cast<int64_t>(l.b) * ba.gx_out_bs +
                  static_cast<int64_t>(l.dd) * a.L;
         store_window<(Dr::kSidxSgn > 0)>(gxo, slo, v, ns);
@@ -3009,18 +3017,18 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
   }
 }
 
-template <typename T, int MODE>
+template <typename T, int MODE, bool GACT>
 __device__ __forceinline__ void bwd_scan_block(const BwdArgs& ba, int bid, float* rows, float* stage, int (*pflag)[2]) {
   const Lane l = bwd_lane(ba.s, bid);
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-  if ((w & 1) == 0) bwd_dir<T, MODE, 0>(ba, l, rows, stage, pflag[0]);
-  else bwd_dir<T, MODE, 1>(ba, l, rows, stage, pflag[1]);
+  if ((w & 1) == 0) bwd_dir<T, MODE, 0, GACT>(ba, l, rows, stage, pflag[0]);
+  else bwd_dir<T, MODE, 1, GACT>(ba, l, rows, stage, pflag[1]);
 }
 
 // Float32 inputs make the window prefetch 8 registers larger, which takes the walk past 256 registers
 // and so to one wave per SIMD; asking for two costs a few bytes of spills and is faster (the SS2D
 // walk by about 9%).  The bf16 walk fits two waves without the request and is slower with it.
-template <typename T, int MODE, int SETS>
+template <typename T, int MODE, int SETS, bool GACT = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(std::is_same<T, float>::value ? 2 : 1)))
 void bwd_scan_kernel(BwdArgs b0, BwdArgs b1) {
   __shared__ __attribute__((aligned(16))) float rows[4][kW * kRedStride + kWtFloats];
@@ -3034,7 +3042,7 @@ void bwd_scan_kernel(BwdArgs b0, BwdArgs b1) {
   // argument segment)
   const bool first = SETS == 1 || bid < nb;
   const BwdArgs* ba = first ? &b0 : &b1;
-  bwd_scan_block<T, MODE>(*ba, first ? bid : bid - nb, rows[w], stage[w], pflag);
+  bwd_scan_block<T, MODE, GACT>(*ba, first ? bid : bid - nb, rows[w], stage[w], pflag);
 }
 
 // du, dΔ_raw (and the backward branch's, or their sums when the branches share inputs):
@@ -3361,6 +3369,13 @@ vmscan_status launch_bwd_scans(const BwdArgs& b0, const BwdArgs& b1, hipStream_t
       if (e != hipSuccess) return launch_failed(e);
     }
   }
+  if constexpr (MODE == kModeSecondPair && std::is_same<T, uint16_t>::value) {
+    if (b0.gt) {  // g in the activation dtype (both sets)
+      hipLaunchKernelGGL((bwd_scan_kernel<T, MODE, SETS, true>), grid, dim3(kThreads), 0, stream, b0, b1);
+      e = hipGetLastError();
+      return e == hipSuccess ? VMSCAN_OK : launch_failed(e);
+    }
+  }
   hipLaunchKernelGGL((bwd_scan_kernel<T, MODE, SETS>), grid, dim3(kThreads), 0, stream, b0, b1);
   e = hipGetLastError();
   return e == hipSuccess ? VMSCAN_OK : launch_failed(e);
@@ -3573,18 +3588,27 @@ vmscan_status run_ss2d_bwd(const void* x, const void* delta_raw, const float* A_
     st = run_pair<T, kModeSecondPairSum>(a, stream, kStageAll);
     if (st != VMSCAN_OK) return st;
   }
-  hipLaunchKernelGGL(gate_bwd_kernel<T>, dim3(static_cast<unsigned>(ceil_div(n, 256 * kWin))), dim3(256), 0, stream,
-                     static_cast<const T*>(dout), static_cast<const T*>(z), ysum, g, static_cast<T*>(dz), n, 1.0f);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return launch_failed(e);
-  // g in column-major order for the column pair
-  st = launch_transpose(g, gcol, nimg, static_cast<int>(H), static_cast<int>(W), 4, stream);
-  if (st != VMSCAN_OK) return st;
+  const int64_t Kb = bwd_chunk(plan_base(batch, dim, ns), L, Kf, 2 * plan_base(batch, dim, ns));
+  // Without a gate g is dout itself.  With bf16 activations and unsplit walks, the walks read it (and
+  // its transpose, for the column pair) as it is instead of a float32 copy; the values are the same.
+  const bool gact = !z && sizeof(T) == 2 && ceil_div(L, Kb) == 1;
+  hipError_t e;
+  if (gact) {
+    st = launch_transpose(dout, gcol, nimg, static_cast<int>(H), static_cast<int>(W), esz, stream);
+    if (st != VMSCAN_OK) return st;
+  } else {
+    hipLaunchKernelGGL(gate_bwd_kernel<T>, dim3(static_cast<unsigned>(ceil_div(n, 256 * kWin))), dim3(256), 0, stream,
+                       static_cast<const T*>(dout), static_cast<const T*>(z), ysum, g, static_cast<T*>(dz), n, 1.0f);
+    e = hipGetLastError();
+    if (e != hipSuccess) return launch_failed(e);
+    // g in column-major order for the column pair
+    st = launch_transpose(g, gcol, nimg, static_cast<int>(H), static_cast<int>(W), 4, stream);
+    if (st != VMSCAN_OK) return st;
+  }
   // Both pairs' adjoint walks in the same launches (twice the workgroups of one pair), each with its
   // own buffers: the column pair (directions 1 and 3 over x^T, g in column order) and the row
   // pair (directions 0 and 2 over x, g in row order).
   BwdArgs bp[2];
-  const int64_t Kb = bwd_chunk(plan_base(batch, dim, ns), L, Kf, 2 * plan_base(batch, dim, ns));
   for (int k = 0; k < 2; ++k) {
     BwdArgs& ba = bp[k];
     const PairBufs& q = lay.p[k];
@@ -3604,6 +3628,7 @@ vmscan_status run_ss2d_bwd(const void* x, const void* delta_raw, const float* A_
     ba.dpar = reinterpret_cast<float*>(wsp + q.dpar);
     ba.wpc = static_cast<int>(ck_slots(Kb));
     ba.g = k == 0 ? gcol : g;
+    ba.gt = gact ? (k == 0 ? static_cast<const void*>(gcol) : dout) : nullptr;
     ba.s.d0 = k == 0 ? dir_args(xt, 1, 0) : dir_args(x, 0, 0);
     ba.s.d1 = k == 0 ? dir_args(xt, 3, 1) : dir_args(x, 2, 1);
     if (a.parts == 2) {  // one dΔ_raw share per direction: the walk rounds and stores it
