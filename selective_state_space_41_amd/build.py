@@ -6,6 +6,7 @@
 microbenchmark (``csrc/probe.hip`` -> ``vmscan_probe``), which is not part of the library.
 """
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -36,15 +37,68 @@ def _run(cmd):
     return out
 
 
+# The hot kernels' occupancy is part of their design: each launch shape assumes that many waves per
+# SIMD fit the registers (the Vim scan three, so that a Vim-Ti call is one round; the backward walk
+# two; the SS2D walk four, two eight-wave workgroups per CU; the state-only passes many).  A change
+# that costs a kernel a wave shows up only as a slower call, so the build reads the compiler's
+# per-kernel resource report and fails when a kernel falls below its floor or spills where it should
+# not (only the float32 backward walk is allowed a few bytes of scratch).
+OCCUPANCY_FLOORS = [  # (kernel name fragment, minimum waves per SIMD)
+    ("scan_pair_kernel", 3),
+    ("bwd_scan_kernel", 2),
+    ("walk_pair_kernel", 4),
+    ("chunk_state_kernel", 6),
+    ("bwd_ckpt_kernel", 6),
+    ("adj_state_kernel", 6),
+    ("lane_scan_kernel", 2),
+]
+SCRATCH_ALLOWED = [("bwd_scan_kernelIf", 64)]  # bytes per lane
+
+
+def kernel_resources(report):
+    """Per-kernel {VGPRs, AGPRs, ScratchSize, Occupancy} from -Rpass-analysis=kernel-resource-usage."""
+    res, cur = {}, None
+    for line in report.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            cur = m.group(1)
+            res[cur] = {}
+            continue
+        m = re.search(r"remark:\s+(VGPRs|AGPRs|ScratchSize \[bytes/lane\]|Occupancy \[waves/SIMD\]): (\d+)", line)
+        if m and cur:
+            res[cur][m.group(1).split()[0]] = int(m.group(2))
+    return res
+
+
+def check_resources(res):
+    """Problems with the hot kernels' occupancy or scratch (empty when all is well)."""
+    bad = []
+    for name, r in res.items():
+        for frag, floor in OCCUPANCY_FLOORS:
+            if frag in name and r.get("Occupancy", 0) < floor:
+                bad.append(f"{name}: {r.get('Occupancy')} waves per SIMD (VGPRs {r.get('VGPRs')}, AGPRs "
+                           f"{r.get('AGPRs')}), needs {floor}")
+        allowed = next((b for frag, b in SCRATCH_ALLOWED if frag in name), 0)
+        if any(frag in name for frag, _ in OCCUPANCY_FLOORS) and r.get("ScratchSize", 0) > allowed:
+            bad.append(f"{name}: {r.get('ScratchSize')} bytes of scratch per lane, at most {allowed}")
+    return bad
+
+
 def build(verbose=False):
-    """Compile libvmscan.so."""
+    """Compile libvmscan.so and check the hot kernels' occupancy."""
     hipcc = _hipcc()
     tmp = LIB + ".tmp"
-    out = _run([hipcc, *HIP_FLAGS, "-shared", "-I", os.path.join(ROOT, "include"),
-                "-o", tmp, os.path.join(PKG, "csrc", "vmscan.hip")])
+    out = _run([hipcc, *HIP_FLAGS, "-Rpass-analysis=kernel-resource-usage", "-shared", "-I",
+                os.path.join(ROOT, "include"), "-o", tmp, os.path.join(PKG, "csrc", "vmscan.hip")])
+    res = kernel_resources(out)
+    if not any(frag in name for name in res for frag, _ in OCCUPANCY_FLOORS):
+        raise RuntimeError("build: the compiler printed no kernel resource report")
+    bad = check_resources(res)
+    if bad:
+        raise RuntimeError("build: kernels below their occupancy floor:\n  " + "\n  ".join(bad))
     os.replace(tmp, LIB)
-    if verbose and out.strip():
-        print(out)
+    if verbose:
+        print("\n".join(l for l in out.splitlines() if "kernel-resource-usage" not in l and l.strip()))
     return LIB
 
 
