@@ -2411,6 +2411,10 @@ struct BwdArgs {
   // gx_out + DIR * gx_out_dir + b * gx_out_bs + d * L + idx (else the gx planes and a sum pass).
   void* gx_out;
   int64_t gx_out_dir, gx_out_bs;
+  // Vim with separate branches at d_state 16 (one share per direction), or null: the walk rounds and
+  // stores direction DIR's du and dΔ_raw itself, [batch][dim][L] each (else the planes and a combine pass).
+  void* du_out[2];
+  void* dx_out[2];
   int wpc;          // checkpoint slots per chunk (at least the windows of the schedule)
   int msched;       // 1: windows of the forward's two-phase walk, whose checkpoints it stored
   int fnch, fm;     // the forward's chunk count, and forward chunks per backward chunk
@@ -2777,7 +2781,7 @@ __device__ __forceinline__ void win_at(const WinSched& w, int s, int& i0, int& l
 }
 
 // The adjoint walk of one direction and state part over one chunk, window by window from the last.
-template <typename T, int MODE, int DIR, bool GACT = false>
+template <typename T, int MODE, int DIR, bool GACT = false, bool VDIRECT = false>
 __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float* rows, float* stage, int* pf) {
   const ScanArgs& a = ba.s;
   using Dr = Dir<MODE, DIR>;
@@ -2979,14 +2983,17 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
 #pragma unroll
       for (int j = 0; j < kWin; ++j) v[j] = stage[j * kW + l.lane] + up[j * kW + l.lane];
       const int64_t plo = Dr::kPosSgn > 0 ? Dr::pos(l, i0) : Dr::pos(l, i0) - (kWin - 1);
-      store_window<(Dr::kPosSgn > 0)>(guw, plo, v, ns);
+      if constexpr (VDIRECT) store_window<(Dr::kPosSgn > 0)>(static_cast<T*>(ba.du_out[DIR]) + row, plo, v, ns);
+      else store_window<(Dr::kPosSgn > 0)>(guw, plo, v, ns);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < kWin; ++j) v[j] = stage[(kWin + j) * kW + l.lane] + up[(kWin + j) * kW + l.lane];
       const int64_t slo = Dr::kSidxSgn > 0 ? Dr::sidx(a, l, i0) : Dr::sidx(a, l, i0) - (kWin - 1);
       bool direct = false;  // SS2D only: the Vim walk would carry the branch's registers too
       if constexpr (MODE == kModeSecondPair) direct = ba.gx_out != nullptr;
-      if (direct) {
+      if constexpr (VDIRECT) {
+        store_window<(Dr::kSidxSgn > 0)>(static_cast<T*>(ba.dx_out[DIR]) + row, slo, v, ns);
+      } else if (direct) {
         T* gxo = static_cast<T*>(ba.gx_out) + DIR * ba.gx_out_dir + static_cast<int64_t>(l.b) * ba.gx_out_bs +
                  static_cast<int64_t>(l.dd) * a.L;
         store_window<(Dr::kSidxSgn > 0)>(gxo, slo, v, ns);
@@ -3017,18 +3024,18 @@ __device__ __forceinline__ void bwd_dir(const BwdArgs& ba, const Lane& l, float*
   }
 }
 
-template <typename T, int MODE, bool GACT>
+template <typename T, int MODE, bool GACT, bool VDIRECT>
 __device__ __forceinline__ void bwd_scan_block(const BwdArgs& ba, int bid, float* rows, float* stage, int (*pflag)[2]) {
   const Lane l = bwd_lane(ba.s, bid);
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-  if ((w & 1) == 0) bwd_dir<T, MODE, 0, GACT>(ba, l, rows, stage, pflag[0]);
-  else bwd_dir<T, MODE, 1, GACT>(ba, l, rows, stage, pflag[1]);
+  if ((w & 1) == 0) bwd_dir<T, MODE, 0, GACT, VDIRECT>(ba, l, rows, stage, pflag[0]);
+  else bwd_dir<T, MODE, 1, GACT, VDIRECT>(ba, l, rows, stage, pflag[1]);
 }
 
 // Float32 inputs make the window prefetch 8 registers larger, which takes the walk past 256 registers
 // and so to one wave per SIMD; asking for two costs a few bytes of spills and is faster (the SS2D
 // walk by about 9%).  The bf16 walk fits two waves without the request and is slower with it.
-template <typename T, int MODE, int SETS, bool GACT = false>
+template <typename T, int MODE, int SETS, bool GACT = false, bool VDIRECT = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(std::is_same<T, float>::value ? 2 : 1)))
 void bwd_scan_kernel(BwdArgs b0, BwdArgs b1) {
   __shared__ __attribute__((aligned(16))) float rows[4][kW * kRedStride + kWtFloats];
@@ -3042,7 +3049,7 @@ void bwd_scan_kernel(BwdArgs b0, BwdArgs b1) {
   // argument segment)
   const bool first = SETS == 1 || bid < nb;
   const BwdArgs* ba = first ? &b0 : &b1;
-  bwd_scan_block<T, MODE, GACT>(*ba, first ? bid : bid - nb, rows[w], stage[w], pflag);
+  bwd_scan_block<T, MODE, GACT, VDIRECT>(*ba, first ? bid : bid - nb, rows[w], stage[w], pflag);
 }
 
 // du, dΔ_raw (and the backward branch's, or their sums when the branches share inputs):
@@ -3369,6 +3376,13 @@ vmscan_status launch_bwd_scans(const BwdArgs& b0, const BwdArgs& b1, hipStream_t
       if (e != hipSuccess) return launch_failed(e);
     }
   }
+  if constexpr (MODE == kModeVim) {
+    if (b0.du_out[0]) {  // separate branches: the walk stores du and dΔ_raw
+      hipLaunchKernelGGL((bwd_scan_kernel<T, MODE, SETS, false, true>), grid, dim3(kThreads), 0, stream, b0, b1);
+      e = hipGetLastError();
+      return e == hipSuccess ? VMSCAN_OK : launch_failed(e);
+    }
+  }
   if constexpr (MODE == kModeSecondPair && std::is_same<T, uint16_t>::value) {
     if (b0.gt) {  // g in the activation dtype (both sets)
       hipLaunchKernelGGL((bwd_scan_kernel<T, MODE, SETS, true>), grid, dim3(kThreads), 0, stream, b0, b1);
@@ -3425,11 +3439,20 @@ vmscan_status run_bwd(const ScanArgs& fwd, const BwdLayout& lay, unsigned char* 
   if (st != VMSCAN_OK) return st;
   ba.s.werr_clear = 0;
   hipError_t e;
+  // Separate branches at d_state 16: one share per direction, which the walk rounds and stores itself.
+  const bool vdirect = du_b && dx_b && fwd.parts == 2;
+  if (vdirect) {
+    ba.du_out[0] = du;
+    ba.du_out[1] = du_b;
+    ba.dx_out[0] = dx;
+    ba.dx_out[1] = dx_b;
+  }
   st = launch_bwd_scans<T, kModeVim, 1>(ba, ba, stream);
   if (st != VMSCAN_OK) return st;
-  hipLaunchKernelGGL(bwd_combine_kernel<T>, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, stream,
-                     ba.gu, ba.gx, static_cast<T*>(du), static_cast<T*>(dx), static_cast<T*>(du_b),
-                     static_cast<T*>(dx_b), n, fwd.parts / 2);
+  if (!vdirect)
+    hipLaunchKernelGGL(bwd_combine_kernel<T>, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, stream,
+                       ba.gu, ba.gx, static_cast<T*>(du), static_cast<T*>(dx), static_cast<T*>(du_b),
+                       static_cast<T*>(dx_b), n, fwd.parts / 2);
   launch_bwd_bc<T>(ba.dbc, static_cast<T*>(dB), static_cast<T*>(dC), static_cast<T*>(dB_b), static_cast<T*>(dC_b),
                    fwd.batch, fwd.ngroups, fwd.L, static_cast<int64_t>(ns) * fwd.L, ns, stream);
   hipLaunchKernelGGL(bwd_param_kernel, dim3(static_cast<unsigned>(ceil_div(2 * fwd.dim * ns + 4 * fwd.dim, 4))),
