@@ -291,3 +291,24 @@ def test_ss2d_bwd_unsplit_walk_chunked_forward(dtype, gated):
             assert got[k] is None
             continue
         _report(f"ss2d bwd unsplit walk, chunked forward {dtype} gated={gated} {k}", grad_err(got[k], ref, k, TOL[dtype]), TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype,gated", [("bf16", False), ("bf16", True), ("f32", False)])
+def test_ss2d_bwd_unsplit_walk_ungated_dout(dtype, gated):
+    """SS2D with 160 (batch, channel-group) tiles per pair (2 x 160 workgroups in the walk's launch),
+    so the backward walks are unsplit over a forward in chunks of 32.  Without a gate and with bf16
+    activations the walks read dout itself (and, for the column pair, its transpose) as g; the
+    non-square 8 x 12 image makes a wrong transpose visible.  The gated and float32 cases take the
+    float32 g on the same shape."""
+    import selective_state_space_41_amd as V
+    assert V.fwd_bidir_chunk_len(20, 512, 96) == 32
+    p = synth.make_ss2d_inputs(4, layer=1850, batch=20, dim=512, H=8, W=12, dtype=dtype, with_z=gated,
+                               params="indep")
+    dout = _dout(dict(u=p["x"], dtype=dtype), 19)
+    got, ref = run_ss2d_bwd(p, dout), oracle_ss2d_bwd(p, dout)
+    for k in SS2D_GRADS:
+        if ref[k] is None:
+            assert got[k] is None
+            continue
+        _report(f"ss2d bwd unsplit walk, dout as g {dtype} gated={gated} {k}", grad_err(got[k], ref, k, TOL[dtype]),
+                TOL[dtype])
