@@ -690,7 +690,7 @@ def main():
     ap.add_argument("--all", action="store_true", help="one line per workload (configs 0-4)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--v2", action="store_true", help="Vim workloads with a separate backward branch (u_b, delta_raw_b, bias_b)")
-    ap.add_argument("--bwd", action="store_true", help="time the backward pass of the Vim workloads")
+    ap.add_argument("--bwd", action="store_true", help="time the backward pass (every gradient) of the workloads")
     ap.add_argument("--front", action="store_true",
                     help="time the front convolution (conv1d / conv2d + SiLU) followed by the scan")
     ap.add_argument("--lane-scan", action="store_true",
