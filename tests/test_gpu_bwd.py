@@ -85,6 +85,32 @@ def test_bwd_config1_full():
         _report(f"bwd config 1 {k} (all batches)", O.rel_err(got[k], v), 2e-2)
 
 
+def test_bwd_config1_shared_sampled():
+    """The Vim-Ti workload with shared inputs (both branches read u, Δ_raw and the bias), as the
+    bench's default backward leg runs it: the two branches' du, dΔ_raw and dbias come out summed.
+    Per-batch gradients on sampled batches; the batch-summed parameter gradients on those batches
+    run as a batch of their own."""
+    p = synth.make_vim_v2_inputs(1)
+    dout = _dout(p, 8)
+    got = run_bwd(p, dout, shared=True)
+    bsel = np.array([0, 50, 127])
+    ref = oracle_bwd(p, dout, batches=bsel, shared=True)
+    assert got["du_b"] is None and got["ddelta_raw_b"] is None and got["ddelta_bias_b"] is None
+    for k, rk in (("du", ("du", "du_b")), ("ddelta_raw", ("ddelta_raw", "ddelta_raw_b"))):
+        _report(f"bwd config 1 shared {k} (batches 0,50,127)", grad_err(got[k][bsel], shared_ref(ref, k, rk), k, 2e-2),
+                2e-2)
+    for k in ("dz", "dB", "dC", "dB_b", "dC_b"):
+        _report(f"bwd config 1 shared {k} (batches 0,50,127)", grad_err(got[k][bsel], ref, k, 2e-2), 2e-2)
+    per = ("u", "delta_raw", "u_b", "delta_raw_b", "z", "B", "C", "B_b", "C_b")
+    sub = {k: (v[bsel] if k in per else v) for k, v in p.items()}
+    gsub = run_bwd(sub, np.ascontiguousarray(dout[bsel]), shared=True)
+    _report("bwd config 1 shared, batches 0,50,127 as a batch: ddelta_bias",
+            grad_err(gsub["ddelta_bias"], shared_ref(ref, "ddelta_bias", ("ddelta_bias", "ddelta_bias_b")),
+                     "ddelta_bias", 2e-2), 2e-2)
+    for k in ("dA_log", "dA_b_log", "dD", "dD_b"):
+        _report(f"bwd config 1 shared, batches 0,50,127 as a batch: {k}", grad_err(gsub[k], ref, k, 2e-2), 2e-2)
+
+
 def test_bwd_config3_chunked():
     """The 1248-pixel Vim-Ti workload (B8 D384 L6085 bf16), whose sequence the backward pass splits
     into the forward's chunks (checkpoints from the forward carries, adjoint carries passed back):
@@ -180,6 +206,24 @@ def test_ss2d_bwd_config4_sampled():
     gsub = run_ss2d_bwd(sub, np.ascontiguousarray(dout[bsel]))
     for k in ("dA_log", "dD", "ddelta_bias"):
         _report(f"ss2d bwd config 4 shape, batches 0,31 as a batch: {k}", grad_err(gsub[k], ref, k, 2e-2), 2e-2)
+
+
+def test_ss2d_bwd_d_state32_config4_sampled():
+    """The 56x56 VMamba stage at d_state 32 (B32 D512 bf16, no gate), as the bench's d_state-32
+    backward leg runs it (four state parts in two workgroups per tile, their dΔ_raw planes summed
+    afterwards): per-batch gradients on two sampled batches; the parameter gradients on those
+    batches run as a batch of their own."""
+    p = synth.make_ss2d_inputs(4, d_state=32)
+    dout = _dout(dict(u=p["x"], dtype=p["dtype"]), 9)
+    got = run_ss2d_bwd(p, dout)
+    bsel = np.array([0, 31])
+    ref = oracle_ss2d_bwd(p, dout, batches=bsel)
+    for k in ("dx", "ddelta_raw", "dB", "dC"):
+        _report(f"ss2d bwd n32 config 4 {k} (batches 0,31)", grad_err(got[k][bsel], ref, k, 2e-2), 2e-2)
+    sub = {k: (v[bsel] if k in ("x", "delta_raw", "B", "C") else v) for k, v in p.items()}
+    gsub = run_ss2d_bwd(sub, np.ascontiguousarray(dout[bsel]))
+    for k in ("dA_log", "dD", "ddelta_bias"):
+        _report(f"ss2d bwd n32 config 4 shape, batches 0,31 as a batch: {k}", grad_err(gsub[k], ref, k, 2e-2), 2e-2)
 
 
 def test_bwd_very_long_sequence():
