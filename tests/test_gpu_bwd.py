@@ -111,6 +111,40 @@ def test_bwd_config1_shared_sampled():
         _report(f"bwd config 1 shared, batches 0,50,127 as a batch: {k}", grad_err(gsub[k], ref, k, 2e-2), 2e-2)
 
 
+@pytest.mark.parametrize("shared", [True, False], ids=["shared", "separate"])
+@pytest.mark.parametrize("cfg", [0, 2])
+def test_bwd_config_sampled(cfg, shared):
+    """The float32 B1 D384 L197 and Vim-S (bf16 B128 D768 L197) backward legs of the bench, with
+    shared inputs and with separate branches: per-batch gradients on the first and last batch; the
+    batch-summed parameter gradients on those batches run as a batch of their own."""
+    p = synth.make_vim_v2_inputs(cfg)
+    dout = _dout(p, 20 + cfg)
+    got = run_bwd(p, dout, shared=shared)
+    nb = p["u"].shape[0]
+    bsel = np.array(sorted({0, nb - 1}))
+    ref = oracle_bwd(p, dout, batches=bsel, shared=shared)
+    tol = TOL[p["dtype"]]
+    sums = (("du", ("du", "du_b")), ("ddelta_raw", ("ddelta_raw", "ddelta_raw_b")),
+            ("ddelta_bias", ("ddelta_bias", "ddelta_bias_b")))
+    per = [(k, shared_ref(ref, k, rk)) for k, rk in sums[:2]] if shared else [(k, ref) for k in ("du", "ddelta_raw",
+                                                                                                   "du_b", "ddelta_raw_b")]
+    per += [(k, ref) for k in ("dz", "dB", "dC", "dB_b", "dC_b")]
+    for k, r in per:
+        _report(f"bwd config {cfg} {'shared' if shared else 'separate'} {k} (batches {list(bsel)})",
+                grad_err(got[k][bsel], r, k, tol), tol)
+    if nb == len(bsel):
+        gsub = got
+    else:
+        act = ("u", "delta_raw", "u_b", "delta_raw_b", "z", "B", "C", "B_b", "C_b")
+        sub = {k: (v[bsel] if k in act else v) for k, v in p.items()}
+        gsub = run_bwd(sub, np.ascontiguousarray(dout[bsel]), shared=shared)
+    params = [("ddelta_bias", shared_ref(ref, *sums[2]))] if shared else [("ddelta_bias", ref), ("ddelta_bias_b", ref)]
+    params += [(k, ref) for k in ("dA_log", "dA_b_log", "dD", "dD_b")]
+    for k, r in params:
+        _report(f"bwd config {cfg} {'shared' if shared else 'separate'}, batches {list(bsel)} as a batch: {k}",
+                grad_err(gsub[k], r, k, tol), tol)
+
+
 def test_bwd_config3_chunked():
     """The 1248-pixel Vim-Ti workload (B8 D384 L6085 bf16), whose sequence the backward pass splits
     into the forward's chunks (checkpoints from the forward carries, adjoint carries passed back):

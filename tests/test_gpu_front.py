@@ -81,14 +81,18 @@ def test_conv1d_front_one_branch_and_v1():
     _report("conv1d v1 u_b", O.rel_err(ub, rub), 1e-5)
 
 
-def test_conv1d_front_config1_sampled():
-    """The Vim-Ti front (bf16, batch 128, 384 channels, 197 tokens, d_conv 4), batches 0 and 127."""
-    p = synth.make_conv1d_inputs(1)
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3])
+def test_conv1d_front_config_sampled(cfg):
+    """The Vim fronts of the bench's workloads (d_conv 4): float32 B1 D384 L197, Vim-Ti bf16 B128
+    D384 L197, Vim-S bf16 B128 D768 L197 and 1248-pixel bf16 B8 D384 L6085; first and last batch."""
+    p = synth.make_conv1d_inputs(cfg)
     u, ub = run_conv1d(p)
-    bsel = np.array([0, 127])
+    nb = p["x"].shape[0]
+    bsel = np.array(sorted({0, nb - 1}))
     ru, rub = oracle_conv1d(p, batches=bsel)
-    _report("conv1d config 1 u (batches 0,127)", O.rel_err(u[bsel], ru), 2e-2)
-    _report("conv1d config 1 u_b (batches 0,127)", O.rel_err(ub[bsel], rub), 2e-2)
+    tol = TOL[p["dtype"]]
+    _report(f"conv1d config {cfg} u (batches {list(bsel)})", O.rel_err(u[bsel], ru), tol)
+    _report(f"conv1d config {cfg} u_b (batches {list(bsel)})", O.rel_err(ub[bsel], rub), tol)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
