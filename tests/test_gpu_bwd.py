@@ -111,14 +111,20 @@ def test_bwd_config1_shared_sampled():
         _report(f"bwd config 1 shared, batches 0,50,127 as a batch: {k}", grad_err(gsub[k], ref, k, 2e-2), 2e-2)
 
 
-@pytest.mark.parametrize("shared", [True, False], ids=["shared", "separate"])
-@pytest.mark.parametrize("cfg", [0, 2])
-def test_bwd_config_sampled(cfg, shared):
-    """The float32 B1 D384 L197 and Vim-S (bf16 B128 D768 L197) backward legs of the bench, with
-    shared inputs and with separate branches: per-batch gradients on the first and last batch; the
-    batch-summed parameter gradients on those batches run as a batch of their own."""
-    p = synth.make_vim_v2_inputs(cfg)
-    dout = _dout(p, 20 + cfg)
+BWD_LEGS = [(0, True, 16), (0, False, 16), (2, True, 16), (2, False, 16), (3, True, 16), (0, True, 32), (2, True, 32),
+            (3, True, 32)]
+
+
+@pytest.mark.parametrize("leg", BWD_LEGS, ids=[f"c{c}-{'shared' if s else 'separate'}-n{n}" for c, s, n in BWD_LEGS])
+def test_bwd_config_sampled(leg):
+    """The bench's backward legs not covered above, each at its full workload: float32 B1 D384 L197,
+    Vim-S (bf16 B128 D768 L197) and 1248-pixel (bf16 B8 D384 L6085, split sequences), with shared
+    inputs (the default legs, also at d_state 32) or separate branches.  Per-batch gradients on the
+    first and last batch; the batch-summed parameter gradients on those batches run as a batch of
+    their own."""
+    cfg, shared, N = leg
+    p = synth.make_vim_v2_inputs(cfg, d_state=N)
+    dout = _dout(p, 20 + cfg + N)
     got = run_bwd(p, dout, shared=shared)
     nb = p["u"].shape[0]
     bsel = np.array(sorted({0, nb - 1}))
@@ -130,7 +136,7 @@ def test_bwd_config_sampled(cfg, shared):
                                                                                                    "du_b", "ddelta_raw_b")]
     per += [(k, ref) for k in ("dz", "dB", "dC", "dB_b", "dC_b")]
     for k, r in per:
-        _report(f"bwd config {cfg} {'shared' if shared else 'separate'} {k} (batches {list(bsel)})",
+        _report(f"bwd config {cfg} N={N} {'shared' if shared else 'separate'} {k} (batches {bsel.tolist()})",
                 grad_err(got[k][bsel], r, k, tol), tol)
     if nb == len(bsel):
         gsub = got
@@ -141,7 +147,7 @@ def test_bwd_config_sampled(cfg, shared):
     params = [("ddelta_bias", shared_ref(ref, *sums[2]))] if shared else [("ddelta_bias", ref), ("ddelta_bias_b", ref)]
     params += [(k, ref) for k in ("dA_log", "dA_b_log", "dD", "dD_b")]
     for k, r in params:
-        _report(f"bwd config {cfg} {'shared' if shared else 'separate'}, batches {list(bsel)} as a batch: {k}",
+        _report(f"bwd config {cfg} N={N} {'shared' if shared else 'separate'}, batches {bsel.tolist()} as a batch: {k}",
                 grad_err(gsub[k], r, k, tol), tol)
 
 

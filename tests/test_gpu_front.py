@@ -91,8 +91,8 @@ def test_conv1d_front_config_sampled(cfg):
     bsel = np.array(sorted({0, nb - 1}))
     ru, rub = oracle_conv1d(p, batches=bsel)
     tol = TOL[p["dtype"]]
-    _report(f"conv1d config {cfg} u (batches {list(bsel)})", O.rel_err(u[bsel], ru), tol)
-    _report(f"conv1d config {cfg} u_b (batches {list(bsel)})", O.rel_err(ub[bsel], rub), tol)
+    _report(f"conv1d config {cfg} u (batches {bsel.tolist()})", O.rel_err(u[bsel], ru), tol)
+    _report(f"conv1d config {cfg} u_b (batches {bsel.tolist()})", O.rel_err(ub[bsel], rub), tol)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

@@ -236,6 +236,17 @@ def test_config1_d_state32_sampled():
     _report("config 1 N=32 (batches 0,77,127)", O.rel_err(run_vim(p)[bsel], oracle_vim(p, batches=bsel)), 2e-2)
 
 
+@pytest.mark.parametrize("cfg", [0, 2])
+def test_config_d_state32_sampled(cfg):
+    """The float32 B1 D384 L197 and Vim-S (bf16 B128 D768 L197) workloads with d_state 32, as the
+    bench's d_state-32 legs run them; first and last batch."""
+    p = synth.make_vim_inputs(cfg, d_state=32)
+    nb = p["u"].shape[0]
+    bsel = np.array(sorted({0, nb - 1}))
+    tol = TOL[p["dtype"]]
+    _report(f"config {cfg} N=32 (batches {bsel.tolist()})", O.rel_err(run_vim(p)[bsel], oracle_vim(p, batches=bsel)), tol)
+
+
 def test_config3_d_state32_sampled():
     """1248-pixel Vim-Ti (6085 tokens, split into chunks) with d_state 32."""
     p = synth.make_vim_inputs(3, d_state=32)
