@@ -141,6 +141,17 @@ def test_config1_v2_full_sampled():
             O.rel_err(run_vim_v2(p)[bsel], oracle_vim_v2(p, batches=bsel)), 2e-2)
 
 
+@pytest.mark.parametrize("cfg", [0, 2])
+def test_config_v2_sampled(cfg):
+    """The float32 B1 D384 L197 and Vim-S (bf16 B128 D768 L197) workloads with a separate backward
+    branch, as the bench's separate-branch legs run them; first and last batch."""
+    p = synth.make_vim_v2_inputs(cfg)
+    nb = p["u"].shape[0]
+    bsel = np.array(sorted({0, nb - 1}))
+    _report(f"config {cfg} v2 (batches {bsel.tolist()})", O.rel_err(run_vim_v2(p)[bsel], oracle_vim_v2(p, batches=bsel)),
+            TOL[p["dtype"]])
+
+
 def test_config3_v2_sampled():
     p = synth.make_vim_v2_inputs(3)
     bsel = np.array([3])
