@@ -111,17 +111,17 @@ def test_bwd_config1_shared_sampled():
         _report(f"bwd config 1 shared, batches 0,50,127 as a batch: {k}", grad_err(gsub[k], ref, k, 2e-2), 2e-2)
 
 
-BWD_LEGS = [(0, True, 16), (0, False, 16), (2, True, 16), (2, False, 16), (3, True, 16), (0, True, 32), (2, True, 32),
-            (3, True, 32)]
+BWD_LEGS = [(0, True, 16), (0, False, 16), (2, True, 16), (2, False, 16), (3, True, 16),
+            (0, True, 32), (1, True, 32), (2, True, 32), (3, True, 32)]
 
 
 @pytest.mark.parametrize("leg", BWD_LEGS, ids=[f"c{c}-{'shared' if s else 'separate'}-n{n}" for c, s, n in BWD_LEGS])
 def test_bwd_config_sampled(leg):
     """The bench's backward legs not covered above, each at its full workload: float32 B1 D384 L197,
-    Vim-S (bf16 B128 D768 L197) and 1248-pixel (bf16 B8 D384 L6085, split sequences), with shared
-    inputs (the default legs, also at d_state 32) or separate branches.  Per-batch gradients on the
-    first and last batch; the batch-summed parameter gradients on those batches run as a batch of
-    their own."""
+    Vim-Ti at d_state 32, Vim-S (bf16 B128 D768 L197) and 1248-pixel (bf16 B8 D384 L6085, split
+    sequences), with shared inputs (the default legs, also at d_state 32) or separate branches.
+    Per-batch gradients on the first and last batch; the batch-summed parameter gradients on those
+    batches run as a batch of their own."""
     cfg, shared, N = leg
     p = synth.make_vim_v2_inputs(cfg, d_state=N)
     dout = _dout(p, 20 + cfg + N)
