@@ -1813,27 +1813,33 @@ __device__ __forceinline__ void conv_taps(const float* w, int64_t d, int K, bool
 // u_b = silu(b_b + Σ_k w_b[k] x[t + (K-1) - k]) (the flipped branch's causal convolution, in
 // original token order), depthwise, from one read of x.
 //
-// Vim front, flat form: thread k computes the 8 outputs at flat positions f = 8k .. 8k + 7 of the
-// [rows][L] tensors (both branches) from the three aligned 16-byte blocks x[f - 8, f + 16): no
+// Vim front, flat form: thread k computes the E outputs at flat positions f = E k .. E k + E - 1 of
+// the [rows][L] tensors (both branches) from the aligned 16-byte blocks x[f - 8, f + E + 8): no
 // staging and no barrier, so every wave goes from its loads to its stores on its own, and the
 // neighbours' reads of the same blocks hit in L1.  (A form that stages each span of rows in LDS
 // and a grid-stride form that keeps the next run's loads in flight take the same time on the
-// Vim-Ti front, 21-22 us: the write-heavy stream, one read for two outputs, sets it.)  A run of 8 can cross one row boundary (rows of
-// at least 8 positions): positions of the window are masked per row (the previous row, the run's
+// Vim-Ti front, 21-22 us: the write-heavy stream, one read for two outputs, sets it.)  With E = 16
+// the halo blocks are a third of the loads instead of two thirds, and the fronts take 1.5-4% less
+// time than with 8 (32 costs registers and is slower).  A run can cross one row boundary (rows of
+// at least E positions): positions of the window are masked per row (the previous row, the run's
 // first row r0, the next row r0 + 1), and each output takes the convolution of its own row, with
-// its row's taps.  Rows shorter than 8 positions go element by element.
-template <typename T>
+// its row's taps.  Rows shorter than E positions go element by element.
+constexpr int kConvRun = 16;  // outputs per thread of the Vim front (E)
+
+template <typename T, int E>
 __global__ __launch_bounds__(256) void conv1d_flat_kernel(const T* __restrict__ x, const float* __restrict__ w,
                                                           const float* __restrict__ bias,
                                                           const float* __restrict__ w_b,
                                                           const float* __restrict__ bias_b, T* __restrict__ u,
                                                           T* __restrict__ u_b, int64_t total, int dim, int L, int K) {
+  static_assert(E % kWin == 0, "whole 8-element runs per thread");
   constexpr int kHalo = kConvMax - 1;
-  const int64_t f = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * kWin;
+  constexpr int kR = E / kWin;  // runs of 8 per thread
+  const int64_t f = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * E;
   if (f >= total) return;
   const int nbr = u_b ? 2 : 1;
-  if (L < kWin) {
-    for (int j = 0; j < kWin && f + j < total; ++j) {
+  if (L < E) {
+    for (int j = 0; j < E && f + j < total; ++j) {
       const int64_t p = f + j, r = p / L;
       const int t = static_cast<int>(p - r * L);
       const int d = static_cast<int>(r % dim);
@@ -1850,41 +1856,48 @@ __global__ __launch_bounds__(256) void conv1d_flat_kernel(const T* __restrict__ 
     }
     return;
   }
-  // xs[i] = x at flat position f - 3 + i, i = 0 .. 13 (past either end of the tensor: 0)
-  float xs[kWin + 2 * kHalo];
+  // xs[i] = x at flat position f - 3 + i, i = 0 .. E + 5 (past either end of the tensor: 0)
+  float xs[E + 2 * kHalo];
   {
-    float pv[kWin], cv[kWin], nv[kWin];
-    Run8<T> rp, rc, rn;
+    float pv[kWin], cv[kR][kWin], nv[kWin];
+    Run8<T> rp, rc[kR], rn;
     if (f >= kWin) rp.load(x + f - kWin);
     else rp.load_part(x, 0);
-    if (f + kWin <= total) rc.load(x + f);
-    else rc.load_part(x + f, static_cast<int>(total - f));
-    if (f + 2 * kWin <= total) rn.load(x + f + kWin);
-    else rn.load_part(x + f + kWin, static_cast<int>(total - f - kWin));
+#pragma unroll
+    for (int c = 0; c < kR; ++c) {
+      const int64_t o = f + kWin * c;
+      if (o + kWin <= total) rc[c].load(x + o);
+      else rc[c].load_part(x + o, static_cast<int>(total - o > 0 ? total - o : 0));
+    }
+    if (f + E + kWin <= total) rn.load(x + f + E);
+    else rn.load_part(x + f + E, static_cast<int>(total - f - E > 0 ? total - f - E : 0));
     rp.template unpack<false>(pv);
-    rc.template unpack<false>(cv);
+#pragma unroll
+    for (int c = 0; c < kR; ++c) rc[c].template unpack<false>(cv[c]);
     rn.template unpack<false>(nv);
 #pragma unroll
     for (int i = 0; i < kHalo; ++i) xs[i] = pv[kWin - kHalo + i];
 #pragma unroll
-    for (int i = 0; i < kWin; ++i) xs[kHalo + i] = cv[i];
+    for (int c = 0; c < kR; ++c)
 #pragma unroll
-    for (int i = 0; i < kHalo; ++i) xs[kHalo + kWin + i] = nv[i];
+      for (int i = 0; i < kWin; ++i) xs[kHalo + kWin * c + i] = cv[c][i];
+#pragma unroll
+    for (int i = 0; i < kHalo; ++i) xs[kHalo + E + i] = nv[i];
   }
   const int64_t r0 = f / L;
   const int t0 = static_cast<int>(f - r0 * L);
-  const int q = L - t0;  // outputs j < q are in row r0, the others in row r0 + 1 (q >= 1)
+  const int q = L - t0;  // outputs j < q are in row r0, the others in row r0 + 1 (q >= 1, E <= L)
   // the window masked to row r0 (x0) and to row r0 + 1 (x1): window position i is at row
   // position t0 - 3 + i
-  float x0[kWin + 2 * kHalo], x1[kWin + 2 * kHalo];
+  float x0[E + 2 * kHalo], x1[E + 2 * kHalo];
 #pragma unroll
-  for (int i = 0; i < kWin + 2 * kHalo; ++i) {
+  for (int i = 0; i < E + 2 * kHalo; ++i) {
     const int tt = t0 - kHalo + i;
     x0[i] = tt >= 0 && tt < L ? xs[i] : 0.0f;
     x1[i] = tt >= L && tt < 2 * L ? xs[i] : 0.0f;
   }
   const int d0 = static_cast<int>(r0 % dim), d1 = d0 + 1 < dim ? d0 + 1 : 0;
-  float o[2][kWin];
+  float o[2][E];
 #pragma unroll
   for (int br = 0; br < 2; ++br) {
     if (br == 1 && !u_b) break;
@@ -1895,7 +1908,7 @@ __global__ __launch_bounds__(256) void conv1d_flat_kernel(const T* __restrict__ 
     conv_taps(wp, d1, K, br == 1, tb);
     const float ba = bp[d0], bb = bp[d1];
 #pragma unroll
-    for (int j = 0; j < kWin; ++j) {
+    for (int j = 0; j < E; ++j) {
       float aa = ba, ab = bb;
 #pragma unroll
       for (int k = 0; k < kConvMax; ++k) {
@@ -1910,11 +1923,18 @@ __global__ __launch_bounds__(256) void conv1d_flat_kernel(const T* __restrict__ 
   for (int br = 0; br < 2; ++br) {
     if (br == 1 && !u_b) break;
     T* out = br == 0 ? u : u_b;
-    if (f + kWin <= total) {
-      store8(out + f, o[br]);
-    } else {
-      for (int j = 0; j < kWin; ++j)
-        if (f + j < total) st_act(out, f + j, o[br][j]);
+#pragma unroll
+    for (int c = 0; c < kR; ++c) {
+      const int64_t oo = f + kWin * c;
+      float v[kWin];
+#pragma unroll
+      for (int j = 0; j < kWin; ++j) v[j] = o[br][kWin * c + j];
+      if (oo + kWin <= total) {
+        store8(out + oo, v);
+      } else {
+        for (int j = 0; j < kWin; ++j)
+          if (oo + j < total) st_act(out, oo + j, v[j]);
+      }
     }
   }
 }
@@ -4109,17 +4129,17 @@ vmscan_status vmscan_conv1d_silu_fwd(const void* x, const float* conv_w, const f
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return VMSCAN_ERR_ALIGN;
   const int64_t total = batch * dim * seqlen;
-  const int64_t blocks = ceil_div(ceil_div(total, kWin), 256);  // a thread per 8 outputs
+  const int64_t blocks = ceil_div(ceil_div(total, kConvRun), 256);  // a thread per kConvRun outputs
   if (dim >= (int64_t{1} << 31) || seqlen >= (int64_t{1} << 30) || blocks >= (int64_t{1} << 31))
     return VMSCAN_ERR_SHAPE;
   const dim3 grid(static_cast<unsigned>(blocks));
   const int di = static_cast<int>(dim), Li = static_cast<int>(seqlen);
   if (dtype == VMSCAN_F32)
-    hipLaunchKernelGGL(conv1d_flat_kernel<float>, grid, dim3(256), 0, stream, static_cast<const float*>(x), conv_w,
+    hipLaunchKernelGGL((conv1d_flat_kernel<float, kConvRun>), grid, dim3(256), 0, stream, static_cast<const float*>(x), conv_w,
                        conv_b, conv_w_b, conv_b_b, static_cast<float*>(u), static_cast<float*>(u_b), total, di, Li,
                        d_conv);
   else
-    hipLaunchKernelGGL(conv1d_flat_kernel<uint16_t>, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(x),
+    hipLaunchKernelGGL((conv1d_flat_kernel<uint16_t, kConvRun>), grid, dim3(256), 0, stream, static_cast<const uint16_t*>(x),
                        conv_w, conv_b, conv_w_b, conv_b_b, static_cast<uint16_t*>(u), static_cast<uint16_t*>(u_b),
                        total, di, Li, d_conv);
   const hipError_t e = hipGetLastError();

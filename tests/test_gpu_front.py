@@ -52,8 +52,8 @@ def oracle_conv1d(p, batches=None, alias_v1=False):
 # a thread takes 8 consecutive elements of the flat [rows][L] tensor: rows shorter than 8 go element
 # by element (the first three and (1, 300, 3)); 8 and 9 put the window's far end two rows on; the
 # others put row boundaries at every offset inside a run
-CONV1D = [(1, 1, 1), (1, 3, 2), (2, 5, 7), (1, 16, 8), (2, 17, 9), (1, 6, 10), (1, 16, 197), (3, 40, 100),
-          (1, 7, 1000), (1, 300, 3), (1, 3, 2049), (1, 2, 4100)]
+CONV1D = [(1, 1, 1), (1, 3, 2), (2, 5, 7), (1, 16, 8), (2, 17, 9), (1, 6, 10), (2, 9, 16), (1, 5, 17), (2, 3, 23),
+          (1, 16, 197), (3, 40, 100), (1, 7, 1000), (1, 300, 3), (1, 3, 2049), (1, 2, 4100)]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
